@@ -1,0 +1,316 @@
+"""CPU oracle for piecewise (exact-or-approximate) block-sparse attention.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the bench's CPU
+baseline leg may import this module. The product path (the HIP library and its Python
+binding) never imports, calls or links anything here, and this module imports nothing
+from the product package.
+
+Plain float64 numpy, one head at a time. Each function follows one passage of the
+pages and names it. There is no blocking, fusion or reordering beyond what those
+definitions state; library primitives (matmul, sort) serve as single steps.
+
+Notation (Sparse Linear Attention blog, notation paragraph; PISA paper §3.2
+Formulation): q_t, k_i, v_i are rows in R^d with 1/sqrt(d) already folded into q.
+Tokens are cut into blocks B_j of (at most) B tokens; block j holds n_j valid tokens
+in its first n_j slots. k̄_j is the key centroid, ΣV_j the value sum,
+H_j = sum_i v_i (k_i - k̄_j)^T the key-value cross statistic, C_j the within-block
+key covariance, σ²_j its diagonal, H̄ the average of H_j over all blocks.
+α_{t,j} = exp(q_t·k̄_j). S_i / U_i are the selected / unselected key blocks of
+query tile i (every row of a tile shares them: PISA paper §3.2).
+
+Readings taken where the pages are silent or garbled (each is listed with its
+reason in the design notes of the repository):
+  * ragged blocks: B is replaced by n_j in the centroid, the virtual-token weight
+    n_j·α and the ln n_j gate; H̄ = (1/nb) sum_j H_j over all blocks of the head;
+  * C_j uses the population normalisation 1/n_j;
+  * the second-order factor multiplies the zeroth-order numerator, the first-order
+    weight and the denominator alike (blog, PWT section: all three share the
+    corrected logit);
+  * the garbled k̄_t in the paper's global first-order formula is read as k̄_j and
+    the coefficient as sum_{j in U} α_{t,j} (blog, Sparse Linear Attention section);
+  * selection ties go to the lower block index; a row with no key support
+    (empty selection and no virtual tokens) outputs 0 with lse = -inf; padded query
+    rows output 0 with lse = -inf.
+
+Every function here has at least one pin in tests/test_oracle_*.py against closed
+forms, reductions to dense attention, invariants or the paper's error bound.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# Mode presets. The GPU exposes DROP, PISA, PWT and LITERAL; PISA0 and the keyword
+# overrides below exist for the ablation pins only.
+PRESETS = {
+    # keep-or-drop block-sparse attention: unselected blocks contribute nothing
+    "drop": dict(virtual=False, first="none", w_kind="none"),
+    # zeroth-order virtual tokens only (PISA paper Table 8 "Zeroth order")
+    "pisa0": dict(virtual=True, first="none", w_kind="none"),
+    # PISA hybrid order: block-wise zeroth order + global first order (PISA paper §3.3)
+    "pisa": dict(virtual=True, first="global", w_kind="none"),
+    # PWT: PISA + diagonal, query-pooled, gated second-order mass term (blog, PWT section)
+    "pwt": dict(virtual=True, first="global", w_kind="pooled", w_map="exp", guard="gate",
+                pooling="sqmean"),
+    # block-wise first order H_j q and per-row w = ½ qᵀC_j q, with 1+w (blog, PWT derivation)
+    "literal": dict(virtual=True, first="block", w_kind="row", w_map="linear", guard="gate"),
+}
+
+
+# ----------------------------------------------------------------------------- blocks
+def block_ranges(L_pad: int, B: int, block_len=None):
+    """(start, n_j) of every block: tokens cut in order into blocks of size B
+    (blog, notation); ragged blocks keep their n_j valid tokens first."""
+    nb = L_pad // B
+    if L_pad % B:
+        raise ValueError("L_pad must be a multiple of B")
+    if block_len is None:
+        return [(j * B, B) for j in range(nb)]
+    bl = np.asarray(block_len)
+    if bl.shape != (nb,) or (bl < 1).any() or (bl > B).any():
+        raise ValueError("block_len must hold nb values in [1, B]")
+    return [(j * B, int(bl[j])) for j in range(nb)]
+
+
+# ----------------------------------------------------------------------------- statistics
+def block_stats(K: np.ndarray, V: np.ndarray, B: int, block_len=None) -> dict:
+    """Per-block statistics of one head.
+
+    k̄_j = (1/n_j) sum_i k_i                       (blog, notation; MoBA centroid)
+    ΣV_j = sum_i v_i                                (PISA paper §3.2 "Practical Challenge"; Fig. 3 V̂)
+    H_j = sum_i v_i (k_i - k̄_j)^T, stored [e, c]    (blog, Sparse Linear Attention section)
+    C_j = (1/n_j) sum_i (k_i - k̄_j)(k_i - k̄_j)^T   (blog, PWT section: within-block key covariance)
+    σ²_j = diag C_j                                 (blog, PWT section: diagonal approximation)
+    H̄ = (1/nb) sum_j H_j                            (blog: H̄ = (B/L) sum_j H_j with L = nb·B)
+    """
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    L_pad, d = K.shape
+    rng = block_ranges(L_pad, B, block_len)
+    nb = len(rng)
+    kbar = np.zeros((nb, d))
+    vsum = np.zeros((nb, d))
+    Hj = np.zeros((nb, d, d))
+    Cj = np.zeros((nb, d, d))
+    n = np.zeros(nb)
+    for j, (s, nj) in enumerate(rng):
+        k = K[s:s + nj]
+        v = V[s:s + nj]
+        kbar[j] = k.mean(axis=0)
+        vsum[j] = v.sum(axis=0)
+        dev = k - kbar[j]
+        Hj[j] = v.T @ dev
+        Cj[j] = dev.T @ dev / nj
+        n[j] = nj
+    sig2 = np.einsum("jcc->jc", Cj).copy()
+    hbar = Hj.mean(axis=0)
+    return dict(kbar=kbar, vsum=vsum, H=Hj, C=Cj, sig2=sig2, hbar=hbar, n=n)
+
+
+def pool_queries(Q: np.ndarray, B: int, block_len=None) -> dict:
+    """Per query tile: q̄_i (mean of the valid rows; PISA paper Fig. 3 Q̄) and
+    mean of squares  \\overline{q²}_i (blog, PWT section: square first, then average),
+    plus the square of the mean q̄_i² kept only for the pooling ablation."""
+    Q = np.asarray(Q, dtype=np.float64)
+    rng = block_ranges(Q.shape[0], B, block_len)
+    d = Q.shape[1]
+    qbar = np.zeros((len(rng), d))
+    qsq = np.zeros((len(rng), d))
+    for i, (s, ni) in enumerate(rng):
+        qbar[i] = Q[s:s + ni].mean(axis=0)
+        qsq[i] = (Q[s:s + ni] ** 2).mean(axis=0)
+    return dict(qbar=qbar, qsq=qsq, qbar_sq=qbar ** 2)
+
+
+# ----------------------------------------------------------------------------- selection
+def block_scores(qbar: np.ndarray, kbar: np.ndarray) -> np.ndarray:
+    """s_{i,j} = q̄_i · k̄_j: MoBA-style block-mean scoring with the pooled query of
+    each tile (blog, Sparse Attention section; PISA paper Fig. 3 prepare phase)."""
+    return np.asarray(qbar, dtype=np.float64) @ np.asarray(kbar, dtype=np.float64).T
+
+
+def select_topk(scores: np.ndarray, K_sel: int) -> np.ndarray:
+    """S_i = the K_sel largest scores of row i, ties to the lower block index; returned
+    in ascending block order, shape [nq, K_sel] int64."""
+    scores = np.asarray(scores)
+    nq, nb = scores.shape
+    if not 0 <= K_sel <= nb:
+        raise ValueError("K_sel out of range")
+    out = np.zeros((nq, K_sel), dtype=np.int64)
+    j = np.arange(nb)
+    for i in range(nq):
+        order = np.lexsort((j, -scores[i]))        # primary: score desc, secondary: index asc
+        out[i] = np.sort(order[:K_sel])
+    return out
+
+
+# ----------------------------------------------------------------------------- second order
+def _guard_and_map(w: np.ndarray, n: np.ndarray, guard: str, w_map: str) -> np.ndarray:
+    """Validity gate of the second-order term and its placement in the logit (blog, PWT
+    section): w > ln n_j is zeroed (gate) or held at ln n_j (clamp, the rejected first
+    attempt); then φ = w (the implementation's e^w) or φ = ln(1 + w) (the 1 + w form)."""
+    lim = np.log(n)
+    if guard == "gate":
+        w = np.where(w > lim, 0.0, w)
+    elif guard == "clamp":
+        w = np.minimum(w, lim)
+    elif guard != "none":
+        raise ValueError(guard)
+    if w_map == "exp":
+        return w
+    if w_map == "linear":
+        return np.log1p(w)
+    raise ValueError(w_map)
+
+
+# ----------------------------------------------------------------------------- attention
+def attention_head(Q, K, V, B: int, block_len=None, K_sel: int = 0, mode: str = "pwt",
+                   idx=None, tiles=None, stats=None, **overrides) -> dict:
+    """Piecewise sparse attention of one head (non-causal self-attention, Q/K/V share
+    the block partition).
+
+    o_t = N_t / D_t with, for query t in tile i (PISA paper §3.2 Eq. (3.2); blog,
+    Sparse Linear Attention and PWT sections):
+      D_t = sum_{j in S_i} sum_n exp(q_t·k_{j,n}) + sum_{j in U_i} n_j exp(q_t·k̄_j + φ_{t,j})
+      N_t = sum_{j in S_i} sum_n exp(q_t·k_{j,n}) v_{j,n}
+            + sum_{j in U_i} exp(q_t·k̄_j + φ_{t,j}) ΣV_j                  (zeroth order)
+            + first-order term:
+                global: (sum_{j in U_i} exp(q_t·k̄_j + φ_{t,j})) H̄ q_t    (PISA paper §3.3)
+                block:  sum_{j in U_i} exp(q_t·k̄_j + φ_{t,j}) H_j q_t      (blog; paper Eq. (3.2))
+    φ comes from w: pooled w̃_{i,j} = ½ sum_c \\overline{q²}_{i,c} σ²_{j,c} (PWT's diagonal
+    + pooled form), or per row ½ q_tᵀ C_j q_t, then gated and mapped (see _guard_and_map).
+
+    The sums are evaluated with one shift c_t = max over every logit of the row
+    (exact and virtual, including ln n_j), which leaves N/D unchanged.
+
+    Returns dict(O [L_pad, d], lse [L_pad], idx [nb, K_sel], D_log (= lse)).
+    ``idx`` overrides the selection; ``tiles`` restricts the computed query tiles
+    (other rows stay 0 / -inf); ``stats`` reuses block_stats output.
+    """
+    opts = dict(PRESETS[mode])
+    opts.update(overrides)
+    virtual = opts.get("virtual", True)
+    first = opts.get("first", "none")
+    w_kind = opts.get("w_kind", "none")
+    w_map = opts.get("w_map", "exp")
+    guard = opts.get("guard", "gate")
+    pooling = opts.get("pooling", "sqmean")
+    numerator_w = opts.get("numerator_w", True)
+
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    L_pad, d = Q.shape
+    rng = block_ranges(L_pad, B, block_len)
+    nb = len(rng)
+    st = stats if stats is not None else block_stats(K, V, B, block_len)
+    pq = pool_queries(Q, B, block_len)
+    if idx is None:
+        idx = select_topk(block_scores(pq["qbar"], st["kbar"]), K_sel)
+    idx = np.asarray(idx, dtype=np.int64).reshape(nb, -1)
+    n = st["n"]
+
+    O = np.zeros((L_pad, d))
+    lse = np.full(L_pad, -np.inf)
+    tile_list = range(nb) if tiles is None else tiles
+    for i in tile_list:
+        s0, ni = rng[i]
+        q = Q[s0:s0 + ni]                                     # [m, d]
+        sel = np.zeros(nb, dtype=bool)
+        sel[idx[i]] = True
+        S = np.flatnonzero(sel)
+        U = np.flatnonzero(~sel) if virtual else np.zeros(0, dtype=np.int64)
+
+        # exact branch over the valid tokens of the selected blocks
+        ks = np.concatenate([K[rng[j][0]:rng[j][0] + rng[j][1]] for j in S]) if S.size else np.zeros((0, d))
+        vs = np.concatenate([V[rng[j][0]:rng[j][0] + rng[j][1]] for j in S]) if S.size else np.zeros((0, d))
+        x = q @ ks.T                                          # [m, |tokens|]
+
+        # virtual tokens of the unselected blocks
+        s = q @ st["kbar"][U].T                               # q_t·k̄_j, [m, |U|]
+        if w_kind == "none":
+            w = np.zeros_like(s)
+        elif w_kind == "pooled":
+            pool = pq["qsq"][i] if pooling == "sqmean" else pq["qbar_sq"][i]
+            w = np.broadcast_to(0.5 * (st["sig2"][U] @ pool), s.shape)
+        elif w_kind == "rowdiag":
+            w = 0.5 * (q ** 2) @ st["sig2"][U].T
+        elif w_kind == "row":
+            w = 0.5 * np.einsum("tc,jce,te->tj", q, st["C"][U], q)
+        else:
+            raise ValueError(w_kind)
+        phi = _guard_and_map(np.asarray(w, dtype=np.float64), n[U][None, :], guard, w_map)
+        ell = s + phi + np.log(n[U])[None, :]                 # log of the weight n_j e^{s+φ}
+
+        allmax = np.full(ni, -np.inf)
+        if x.shape[1]:
+            allmax = np.maximum(allmax, x.max(axis=1))
+        if ell.shape[1]:
+            allmax = np.maximum(allmax, ell.max(axis=1))
+        empty = ~np.isfinite(allmax)
+        c = np.where(empty, 0.0, allmax)[:, None]
+
+        ex = np.exp(x - c)
+        ev = np.exp(ell - c)
+        D = ex.sum(axis=1) + ev.sum(axis=1)
+        a = np.exp(s + phi - c) if numerator_w else np.exp(s - c)   # coefficient of ΣV_j and H_j q
+        N = ex @ vs + a @ st["vsum"][U]
+        if first == "global":
+            N = N + a.sum(axis=1)[:, None] * (q @ st["hbar"].T)
+        elif first == "block":
+            N = N + np.einsum("tj,jec,tc->te", a, st["H"][U], q)
+        elif first != "none":
+            raise ValueError(first)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            o = np.where(empty[:, None], 0.0, N / np.where(D > 0, D, 1.0)[:, None])
+            l = np.where(empty, -np.inf, c[:, 0] + np.log(np.where(D > 0, D, 1.0)))
+        O[s0:s0 + ni] = o
+        lse[s0:s0 + ni] = l
+    return dict(O=O, lse=lse, idx=idx)
+
+
+def dense_attention_head(Q, K, V, B: int, block_len=None) -> dict:
+    """Dense softmax attention o_t = sum_i e^{q_t·k_i} v_i / sum_i e^{q_t·k_i} over the
+    valid keys (PISA paper §3.1), one max shift per row; padded query rows output 0."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    L_pad, d = Q.shape
+    rng = block_ranges(L_pad, B, block_len)
+    valid = np.zeros(L_pad, dtype=bool)
+    for s0, nj in rng:
+        valid[s0:s0 + nj] = True
+    x = Q[valid] @ K[valid].T
+    c = x.max(axis=1, keepdims=True)
+    e = np.exp(x - c)
+    D = e.sum(axis=1)
+    O = np.zeros((L_pad, d))
+    lse = np.full(L_pad, -np.inf)
+    O[valid] = (e @ V[valid]) / D[:, None]
+    lse[valid] = c[:, 0] + np.log(D)
+    return dict(O=O, lse=lse)
+
+
+# ----------------------------------------------------------------------------- multi-head
+def run(Q, K, V, B: int, block_len=None, K_sel: int = 0, mode: str = "pwt", heads=None,
+        tiles=None, idx=None, **overrides) -> dict:
+    """Every head of [H, L_pad, d] float64 inputs; ``idx`` may be [H, nb, K_sel]."""
+    H = Q.shape[0]
+    hs = range(H) if heads is None else heads
+    O = np.zeros(Q.shape)
+    lse = np.full(Q.shape[:2], -np.inf)
+    sel = {}
+    for h in hs:
+        r = attention_head(Q[h], K[h], V[h], B, block_len, K_sel, mode,
+                           idx=None if idx is None else idx[h], tiles=tiles, **overrides)
+        O[h] = r["O"]
+        lse[h] = r["lse"]
+        sel[h] = r["idx"]
+    return dict(O=O, lse=lse, idx=sel)
+
+
+def pooled_w(qsq: np.ndarray, sig2: np.ndarray) -> np.ndarray:
+    """w̃_{i,j} = ½ sum_c \\overline{q²}_{i,c} σ²_{j,c}, the [query tile x key block] matrix
+    of the diagonal + pooled second-order term (blog, PWT section), before the gate."""
+    return 0.5 * np.asarray(qsq, dtype=np.float64) @ np.asarray(sig2, dtype=np.float64).T
