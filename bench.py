@@ -1,0 +1,273 @@
+"""Benchmark of the piecewise sparse attention forward pass on one MI355X.
+
+A step is one pass of the whole path over one batch of resident synthetic input:
+pisa_block_stats -> pisa_select_topk -> pisa_attention_fwd (PWT mode by default).
+Default workload: the Wan2.1-like video config (40 heads, latent grid 21x30x52 =
+32,760 tokens in 4x4x4 cubes, d = 128, bf16, keep 10% of key blocks per query cube).
+
+Prints ONE JSON line with the effective throughput (exact + compensation FLOPs over
+valid tokens only, divided by the measured step time), the per-call split, the dense
+baselines, the attention kernel's roofline and the CPU oracle's time on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms/call + effective TFLOP/s (% bf16 MFMA peak), Wan2.1-like L=32760 H=40 d=128"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA peaks
+PEAK_HBM_GBS = 8000.0
+
+
+def flop_counts(idx: np.ndarray, block_len: np.ndarray, d: int, mode: str) -> dict:
+    """Algorithmic FLOPs of one step over valid tokens only.
+
+    exact    4d per (valid query, valid key of a selected block)      (QKᵀ and PV)
+    virtual  4d per (valid query, unselected block)                   (PISA/PWT)
+             4d per (valid query, valid key of an unselected block)   (LITERAL)
+    first    2d² per valid query                                      (A_t H̄ q_t, PISA/PWT)
+    prepare  2d² per valid key (H̄ cross term) + 2d·nb² per head for the block scores,
+             and another 2d·nb² per head for w̃ (PWT)
+    """
+    H, nb, K_sel = idx.shape
+    bl = block_len.astype(np.int64)
+    sel_tokens = bl[idx].sum(axis=-1) if K_sel else np.zeros((H, nb), dtype=np.int64)   # [H, nb]
+    rows = bl[None, :]
+    exact = int((4 * d * rows * sel_tokens).sum())
+    unsel_blocks = nb - K_sel
+    virtual = first = 0
+    if mode in ("pisa", "pwt"):
+        virtual = int(4 * d * rows.sum() * unsel_blocks * H)
+        first = int(2 * d * d * rows.sum() * H)
+    elif mode == "literal":
+        virtual = int((4 * d * rows * (bl.sum() - sel_tokens)).sum())
+    prepare = int(2 * d * d * bl.sum() * H + 2 * d * nb * nb * H * (2 if mode == "pwt" else 1))
+    return dict(exact=exact, virtual=virtual, first=first, prepare=prepare,
+                attention=exact + virtual + first, total=exact + virtual + first + prepare)
+
+
+def kernel_source_hash() -> str:
+    p = os.path.join(ROOT, "block_sparse_attention_43_amd", "csrc", "attention_fwd.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per attention launch measured with rocprofv3 counters, if they were taken
+    on the current kernel source (profiles/attention_fwd_<workload>_traffic.json)."""
+    p = os.path.join(ROOT, "profiles", f"attention_fwd_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, mode: str, tiles: int, seed: int = 0) -> dict:
+    """The oracle as it stands, on one head and a few query tiles of the same workload."""
+    from oracle import pisa_oracle as orc
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = 1
+    rng = np.random.default_rng(seed)
+    nb = inp.nb
+    tl = sorted(rng.choice(nb, size=min(tiles, nb), replace=False).tolist())
+    bl = inp.layout.block_len
+    Q, K, V = inp.f64("Q", 0), inp.f64("K", 0), inp.f64("V", 0)
+    t0 = time.perf_counter()
+    res = orc.attention_head(Q, K, V, 64, bl, inp.K_sel, mode, tiles=tl)
+    dt = time.perf_counter() - t0
+    idx = res["idx"][tl][None]
+    sub_bl = bl.copy()
+    # FLOPs of the sampled tiles (exact/virtual/first for those rows) + the head's prepare work
+    fc = flop_counts(res["idx"][None], bl, inp.d, mode)
+    per_tile = {k: 0 for k in ("exact", "virtual", "first")}
+    rows = bl[tl].astype(np.int64)
+    sel_tok = bl[idx[0]].sum(axis=-1) if inp.K_sel else np.zeros(len(tl), dtype=np.int64)
+    per_tile["exact"] = int((4 * inp.d * rows * sel_tok).sum())
+    if mode in ("pisa", "pwt"):
+        per_tile["virtual"] = int(4 * inp.d * rows.sum() * (nb - inp.K_sel))
+        per_tile["first"] = int(2 * inp.d * inp.d * rows.sum())
+    elif mode == "literal":
+        per_tile["virtual"] = int((4 * inp.d * rows * (bl.sum() - sel_tok)).sum())
+    flops = sum(per_tile.values()) + fc["prepare"] // inp.H
+    del sub_bl
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"head 0, {len(tl)} of {nb} query tiles, {mode}, float64 numpy "
+                      f"(per-head statistics included), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="wan", help="tiny | flux | wan | hunyuan | long")
+    ap.add_argument("--mode", default="pwt", help="drop | pisa | pwt | literal")
+    ap.add_argument("--cpu-tiles", type=int, default=8, help="query tiles in the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU: every workload fits one "
+                                   "MI355X and the path has no multi-GPU mode; run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    from block_sparse_attention_43_amd import pisa, synth
+
+    torch.cuda.set_device(0)
+    pisa.load()
+    inp = synth.make(args.config)
+    cfg = inp.cfg
+    K_sel = inp.K_sel
+    mode = args.mode
+    base = pisa.MODES[mode]
+
+    def dev(x):
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        return (t.view(torch.bfloat16) if cfg.dtype == "bf16" else t).cuda()
+
+    Q, K, V = dev(inp.Q), dev(inp.K), dev(inp.V)
+    bl = inp.layout.block_len
+    blt = None if (bl == 64).all() else torch.from_numpy(bl.astype(np.int32)).cuda()
+    H, L, d = Q.shape
+    nb = L // 64
+
+    # every buffer allocated once, outside the timed region
+    st = pisa.alloc_stats(K)
+    ws_stats = torch.empty(max(pisa.load().pisa_block_stats_workspace_bytes(H, L, d, 64), 16),
+                           dtype=torch.uint8, device="cuda")
+    ws_sel = torch.empty(pisa.load().pisa_select_workspace_bytes(H, L, d, 64), dtype=torch.uint8, device="cuda")
+    idx = torch.empty(H, nb, max(K_sel, 1), dtype=torch.int32, device="cuda")[:, :, :K_sel]
+    mask = torch.empty(H, nb, (nb + 31) // 32, dtype=torch.int32, device="cuda")
+    wt = torch.empty(H, nb, nb, dtype=torch.float32, device="cuda") if base == pisa.MODE_PWT else None
+    O = torch.empty_like(Q)
+    lse = torch.empty(H, L, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        pisa.block_stats(K, V, blt, out=st, workspace=ws_stats)
+        if ev is not None:
+            ev[1].record(stream)
+        pisa.select_topk(Q, st, K_sel, blt, out=(idx, mask, wt), workspace=ws_sel)
+        if ev is not None:
+            ev[2].record(stream)
+        pisa.attention_fwd(Q, K, V, st, idx, mask, wt, K_sel, mode, blt, out=O, lse=lse)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_stats = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_sel = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    fc = flop_counts(idx.cpu().numpy(), bl, d, mode)
+    value = fc["total"] / (ms_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[cfg.dtype]
+    attn_tflops = fc["attention"] / (ms_attn * 1e-3) / 1e12
+    traffic = load_traffic(args.config)
+
+    # exact branch alone: DROP on the same selection (phase 1 only)
+    def timed(fn, n=5):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    ms_exact = timed(lambda: pisa.attention_fwd(Q, K, V, st, idx, mask, None, K_sel, "drop", blt, out=O))
+    exact_tflops = fc["exact"] / (ms_exact * 1e-3) / 1e12
+
+    dense = {}
+    if not args.no_dense:
+        idx_all = torch.arange(nb, dtype=torch.int32, device="cuda").expand(H, nb, nb).contiguous()
+        ms_drop_all = timed(lambda: pisa.attention_fwd(Q, K, V, st, idx_all, None, None, nb, "drop", blt, out=O), 3)
+        del idx_all
+        ok = torch.from_numpy(inp.layout.perm >= 0).cuda()
+        q = Q[:, ok].unsqueeze(0).contiguous()
+        k = K[:, ok].unsqueeze(0).contiguous()
+        v = V[:, ok].unsqueeze(0).contiguous()
+        try:
+            ms_sdpa = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=1.0), 3)
+        except Exception as e:  # pragma: no cover - backend dependent
+            ms_sdpa = None
+            dense["sdpa_error"] = str(e)[:200]
+        del q, k, v
+        best = min(x for x in (ms_drop_all, ms_sdpa) if x is not None)
+        dense.update(dense_ours_ms=round(ms_drop_all, 4),
+                     dense_sdpa_ms=None if ms_sdpa is None else round(ms_sdpa, 4),
+                     dense_best_ms=round(best, 4), speedup_vs_dense=round(best / ms_step, 3))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, mode, args.cpu_tiles)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded smooth 3D field + noise, cube layout; no model activations)",
+        "config": {"workload": f"{cfg.name}: H={H} L={inp.layout.L} (padded {L}) d={d} B=64 "
+                               f"K_sel={K_sel}/{nb} mode={mode}",
+                   "heads": H, "seq_len": inp.layout.L, "head_dim": d, "block": 64,
+                   "k_sel": K_sel, "n_blocks": nb, "mode": mode},
+        "ms_stats": round(ms_stats, 4),
+        "ms_select": round(ms_sel, 4),
+        "ms_attention": round(ms_attn, 4),
+        "frac_of_peak_total": round(value / peak, 4),
+        "exact_branch": {"ms": round(ms_exact, 4), "tflops": round(exact_tflops, 2),
+                         "frac": round(exact_tflops / peak, 4)},
+        "flops": fc,
+        **dense,
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4), "traffic": traffic,
+                     "kernel": "attention_kernel (pisa_attention_fwd)",
+                     "algorithmic_flops_per_launch": fc["attention"]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,235 @@
+// C ABI: argument validation, workspace sizing and dispatch onto the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "internal.hpp"
+#include "pisa.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+pisa_status fail(pisa_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pisa_status fail(pisa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+pisa_status ok() {
+  g_err.clear();
+  return PISA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(pisa_dtype dt) { return dt == PISA_BF16 ? 2 : 4; }
+
+// Shape checks common to every call. Returns PISA_OK or an error with the message set.
+pisa_status check_shape(int H, int L, int d, int B) {
+  if (H < 1) return fail(PISA_ERR_INVALID_ARG, "H must be >= 1 (got %d)", H);
+  if (L < 1) return fail(PISA_ERR_INVALID_ARG, "L must be >= 1 (got %d)", L);
+  if (B != pisa::kB) return fail(PISA_ERR_UNSUPPORTED, "only B == 64 is supported (got %d)", B);
+  if (L % B) return fail(PISA_ERR_INVALID_ARG, "L (%d) must be a multiple of B (%d)", L, B);
+  if (d != 64 && d != 128) return fail(PISA_ERR_UNSUPPORTED, "d must be 64 or 128 (got %d)", d);
+  if (L / B > 32768) return fail(PISA_ERR_UNSUPPORTED, "at most 32768 blocks are supported (got %d)", L / B);
+  if (static_cast<long long>(H) * (L / B) >= (1LL << 31))
+    return fail(PISA_ERR_UNSUPPORTED, "H * nb must fit a 31-bit grid");
+  return PISA_OK;
+}
+
+pisa_status check_dtype(pisa_dtype dt) {
+  if (dt != PISA_F32 && dt != PISA_BF16) return fail(PISA_ERR_UNSUPPORTED, "unknown dtype %d", int(dt));
+  return PISA_OK;
+}
+
+pisa_status check_ptr(const void* p, const char* name, bool need_align = true) {
+  if (!p) return fail(PISA_ERR_INVALID_ARG, "%s must not be NULL", name);
+  if (need_align && !aligned16(p)) return fail(PISA_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+  return PISA_OK;
+}
+
+pisa_status hip_fail(hipError_t e, const char* what) {
+  return fail(PISA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define PISA_TRY(x)                  \
+  do {                               \
+    pisa_status _s = (x);            \
+    if (_s != PISA_OK) return _s;    \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t pisa_packed_bytes(pisa_dtype dt, int H, int L, int d, int B) {
+  if (check_dtype(dt) != PISA_OK || check_shape(H, L, d, B) != PISA_OK) return 0;
+  return pisa::packed_layout(elem_size(dt), H, L, d).total;
+}
+
+size_t pisa_block_stats_workspace_bytes(int H, int L, int d, int B) {
+  if (check_shape(H, L, d, B) != PISA_OK) return 0;
+  const int nb = L / B;
+  const int G = pisa::stats_group(H, nb);
+  const int ng = (nb + G - 1) / G;
+  return size_t(H) * ng * d * d * sizeof(float);
+}
+
+pisa_status pisa_block_stats(pisa_dtype dt, const void* K, const void* V, int H, int L, int d,
+                             int B, const int32_t* block_len, unsigned flags,
+                             const pisa_stats* out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  PISA_TRY(check_dtype(dt));
+  PISA_TRY(check_shape(H, L, d, B));
+  PISA_TRY(check_ptr(K, "K"));
+  PISA_TRY(check_ptr(V, "V"));
+  PISA_TRY(check_ptr(out, "out", false));
+  if (flags & ~3u) return fail(PISA_ERR_INVALID_ARG, "unknown stats flags 0x%x", flags);
+  PISA_TRY(check_ptr(out->kbar, "out->kbar"));
+  PISA_TRY(check_ptr(out->vsum, "out->vsum"));
+  PISA_TRY(check_ptr(out->ksig2, "out->ksig2"));
+  PISA_TRY(check_ptr(out->hbarT, "out->hbarT"));
+  PISA_TRY(check_ptr(out->packed, "out->packed"));
+  if (flags & PISA_STATS_BLOCK_H) PISA_TRY(check_ptr(out->hblk, "out->hblk"));
+  if (flags & PISA_STATS_BLOCK_C) PISA_TRY(check_ptr(out->cblk, "out->cblk"));
+  const size_t need = pisa_block_stats_workspace_bytes(H, L, d, B);
+  if (!workspace || workspace_bytes < need)
+    return fail(PISA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(PISA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+  pisa::StatsArgs a{};
+  a.K = K;
+  a.V = V;
+  a.block_len = block_len;
+  a.kbar = out->kbar;
+  a.vsum = out->vsum;
+  a.ksig2 = out->ksig2;
+  a.hbarT = out->hbarT;
+  a.hblk = out->hblk;
+  a.cblk = out->cblk;
+  a.packed = static_cast<char*>(out->packed);
+  a.part = static_cast<float*>(workspace);
+  a.H = H;
+  a.L = L;
+  a.d = d;
+  a.pl = pisa::packed_layout(elem_size(dt), H, L, d);
+  a.nb = a.pl.nb;
+  a.nbp = a.pl.nbp;
+  a.G = pisa::stats_group(H, a.nb);
+  a.ngroups = (a.nb + a.G - 1) / a.G;
+  hipError_t e = pisa::launch_block_stats(dt == PISA_BF16, a, flags, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pisa_block_stats launch");
+  return ok();
+}
+
+size_t pisa_select_workspace_bytes(int H, int L, int d, int B) {
+  if (check_shape(H, L, d, B) != PISA_OK) return 0;
+  const size_t nb = size_t(L / B);
+  return pisa::align256(2 * size_t(H) * nb * d * sizeof(float)) + size_t(H) * nb * nb * sizeof(float);
+}
+
+pisa_status pisa_select_topk(pisa_dtype dt, const void* Q, const pisa_stats* st, int H, int L,
+                             int d, int B, const int32_t* block_len, int K_sel, int32_t* idx,
+                             uint32_t* mask, float* wt, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  PISA_TRY(check_dtype(dt));
+  PISA_TRY(check_shape(H, L, d, B));
+  PISA_TRY(check_ptr(Q, "Q"));
+  PISA_TRY(check_ptr(st, "st", false));
+  PISA_TRY(check_ptr(st->kbar, "st->kbar"));
+  PISA_TRY(check_ptr(st->ksig2, "st->ksig2"));
+  const int nb = L / B;
+  if (K_sel < 0 || K_sel > nb) return fail(PISA_ERR_INVALID_ARG, "K_sel must be in [0, %d] (got %d)", nb, K_sel);
+  if (K_sel > 0) PISA_TRY(check_ptr(idx, "idx", false));
+  const size_t need = pisa_select_workspace_bytes(H, L, d, B);
+  if (!workspace || workspace_bytes < need)
+    return fail(PISA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(PISA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+  pisa::SelectArgs a{};
+  a.Q = Q;
+  a.kbar = st->kbar;
+  a.ksig2 = st->ksig2;
+  a.block_len = block_len;
+  a.qbar = static_cast<float*>(workspace);
+  a.qsq = a.qbar + size_t(H) * nb * d;
+  a.scores = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      pisa::align256(2 * size_t(H) * nb * d * sizeof(float)));
+  a.wt = wt;
+  a.idx = idx;
+  a.mask = mask;
+  a.H = H;
+  a.L = L;
+  a.d = d;
+  a.nb = nb;
+  a.K_sel = K_sel;
+  a.nw = (nb + 31) / 32;
+  hipError_t e = pisa::launch_select(dt == PISA_BF16, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pisa_select_topk launch");
+  return ok();
+}
+
+pisa_status pisa_attention_fwd(pisa_dtype dt, const void* Q, const void* K, const void* V,
+                               const pisa_stats* st, const int32_t* idx, const uint32_t* mask,
+                               const float* wt, int H, int L, int d, int B,
+                               const int32_t* block_len, int K_sel, unsigned mode, void* O,
+                               float* lse, void* stream) {
+  PISA_TRY(check_dtype(dt));
+  PISA_TRY(check_shape(H, L, d, B));
+  PISA_TRY(check_ptr(Q, "Q"));
+  PISA_TRY(check_ptr(K, "K"));
+  PISA_TRY(check_ptr(V, "V"));
+  PISA_TRY(check_ptr(O, "O"));
+  PISA_TRY(check_ptr(st, "st", false));
+  PISA_TRY(check_ptr(st->packed, "st->packed"));
+  const int nb = L / B;
+  if (K_sel < 0 || K_sel > nb) return fail(PISA_ERR_INVALID_ARG, "K_sel must be in [0, %d] (got %d)", nb, K_sel);
+  if (K_sel > 0) PISA_TRY(check_ptr(idx, "idx", false));
+  const unsigned base = mode & 15u;
+  if (base > PISA_MODE_LITERAL) return fail(PISA_ERR_INVALID_ARG, "unknown mode %u", base);
+  if (mode & ~(15u | PISA_W_LINEAR | PISA_W_EXP | PISA_W_NOGATE))
+    return fail(PISA_ERR_INVALID_ARG, "unknown mode bits 0x%x", mode);
+  if ((mode & PISA_W_LINEAR) && (mode & PISA_W_EXP))
+    return fail(PISA_ERR_INVALID_ARG, "PISA_W_LINEAR and PISA_W_EXP are exclusive");
+  if (base != PISA_MODE_DROP) PISA_TRY(check_ptr(mask, "mask", false));
+  if (base == PISA_MODE_PWT) PISA_TRY(check_ptr(wt, "wt", false));
+
+  pisa::AttnArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.packed = static_cast<const char*>(st->packed);
+  a.block_len = block_len;
+  a.idx = idx;
+  a.mask = mask;
+  a.wt = wt;
+  a.O = O;
+  a.lse = lse;
+  a.H = H;
+  a.L = L;
+  a.d = d;
+  a.pl = pisa::packed_layout(elem_size(dt), H, L, d);
+  a.nb = a.pl.nb;
+  a.nbp = a.pl.nbp;
+  a.K_sel = K_sel;
+  a.nw = (nb + 31) / 32;
+  a.w_linear = base == PISA_MODE_LITERAL ? !(mode & PISA_W_EXP) : !!(mode & PISA_W_LINEAR);
+  a.gate = !(mode & PISA_W_NOGATE);
+  (void)V;  // V enters through its per-block transpose in st->packed
+  hipError_t e = pisa::launch_attention(dt == PISA_BF16, int(base), a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pisa_attention_fwd launch");
+  return ok();
+}
+
+const char* pisa_last_error(void) { return g_err.c_str(); }
+
+const char* pisa_version(void) { return "pisa-mi355x 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,224 @@
+// Prepare phase, part 1: per-block key/value statistics of every head.
+//
+// For key block j with n_j valid tokens (PISA paper §3.4 prepare phase and Fig. 3;
+// Sparse Linear Attention blog, notation and PWT sections):
+//   k̄_j = (1/n_j) Σ k_i,   ΣV_j = Σ v_i,   σ²_{j,c} = (1/n_j) Σ (k_{i,c} - k̄_{j,c})²,
+//   H̄ᵀ = (1/nb) Σ_j Σ_i (k_i - k̄_j) v_iᵀ,
+// optionally H_j (stored [e][c]) and C_j = (1/n_j) Σ (k_i - k̄_j)(k_i - k̄_j)ᵀ.
+//
+// One pass over K and V (HBM-bound). A workgroup of 4 waves streams G consecutive
+// blocks through LDS; the d x d cross term K_jᵀV_j runs on MFMA with exact bf16
+// products and fp32 accumulation, and the per-block centring k̄_j ΣV_jᵀ is removed in
+// fp32 before the block is added to the workgroup's partial sum. Partials are reduced
+// in a fixed order by a second kernel, so repeated runs are bit-identical.
+// The same pass writes the attention kernel's operand layouts: Vᵀ per block,
+// centroids and mean values (ΣV_j / n_j, transposed per group of 64 blocks) in the
+// storage type, and H̄[e][c].
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace pisa {
+
+template <class T, int D>
+__global__ __launch_bounds__(256) void block_stats_kernel(StatsArgs a, unsigned flags) {
+  using M = typename MmaFor<T>::type;
+  constexpr int KI = M::KI, KH = M::KH;
+  constexpr int EPC = 16 / sizeof(T);      // elements per 16-byte chunk
+  constexpr int LDR = D + EPC;             // LDS row stride (elements), padded against bank conflicts
+  constexpr int CPR = D / EPC;             // chunks per token row
+  constexpr int NT = D / 32;               // 32-wide output tiles per side of d x d
+  constexpr int TPW = NT * NT / 4;         // output tiles per wave
+  __shared__ __align__(16) T sK[kB * LDR];
+  __shared__ __align__(16) T sV[kB * LDR];
+  __shared__ float sKbar[D], sVsum[D];
+
+  const int h = blockIdx.y, grp = blockIdx.x;
+  const int j0 = grp * a.G;
+  const int j1 = min(a.nb, j0 + a.G);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int ct = (wave * TPW) / NT;        // row tile (c) of this wave; its tiles share it
+
+  const T* Kh = static_cast<const T*>(a.K) + size_t(h) * a.L * D;
+  const T* Vh = static_cast<const T*>(a.V) + size_t(h) * a.L * D;
+  T* vt = reinterpret_cast<T*>(a.packed + a.pl.vt) + size_t(h) * a.nb * D * kB;
+  T* kbp = reinterpret_cast<T*>(a.packed + a.pl.kbar) + size_t(h) * a.nbp * D;
+  T* vbp = reinterpret_cast<T*>(a.packed + a.pl.vbar) + size_t(h) * a.nbp * D;
+
+  f32x16 run[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) run[u] = zero16();
+
+  for (int j = j0; j < j1; ++j) {
+    int n = a.block_len ? a.block_len[j] : kB;
+    n = min(max(n, 1), kB);
+    const float invn = 1.f / float(n);
+
+    // Stage K_j and V_j (rows >= n_j zeroed) in LDS.
+    for (int c = tid; c < kB * CPR; c += 256) {
+      const int row = c / CPR, col = (c % CPR) * EPC;
+      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (row < n) {
+        kv = *reinterpret_cast<const uint4*>(Kh + size_t(j * kB + row) * D + col);
+        vv = *reinterpret_cast<const uint4*>(Vh + size_t(j * kB + row) * D + col);
+      }
+      *reinterpret_cast<uint4*>(sK + row * LDR + col) = kv;
+      *reinterpret_cast<uint4*>(sV + row * LDR + col) = vv;
+    }
+    __syncthreads();
+
+    // Column statistics: threads [0, D) own key columns, [128, 128 + D) value columns.
+    if (tid < D) {
+      float s = 0.f;
+      for (int r = 0; r < kB; ++r) s += to_f32(sK[r * LDR + tid]);
+      const float mean = s * invn;
+      float ss = 0.f;
+      for (int r = 0; r < n; ++r) {
+        const float dv = to_f32(sK[r * LDR + tid]) - mean;
+        ss += dv * dv;
+      }
+      const size_t o = (size_t(h) * a.nb + j) * D + tid;
+      a.kbar[o] = mean;
+      a.ksig2[o] = ss * invn;
+      sKbar[tid] = mean;
+      kbp[size_t(j) * D + tid] = from_f32<T>(mean);
+    } else if (tid >= 128 && tid < 128 + D) {
+      const int c = tid - 128;
+      float s = 0.f;
+      for (int r = 0; r < kB; ++r) s += to_f32(sV[r * LDR + c]);
+      a.vsum[(size_t(h) * a.nb + j) * D + c] = s;
+      sVsum[c] = s;
+      vbp[(size_t(j / kB) * D + c) * kB + (j % kB)] = from_f32<T>(s * invn);
+    }
+
+    // Vᵀ of the block: vt[j][e][i], 16-byte chunks of consecutive keys, coalesced stores.
+    for (int c = tid; c < D * (kB / EPC); c += 256) {
+      const int e = c / (kB / EPC), i0 = (c % (kB / EPC)) * EPC;
+      __align__(16) T tmp[EPC];
+#pragma unroll
+      for (int u = 0; u < EPC; ++u) tmp[u] = sV[(i0 + u) * LDR + e];
+      *reinterpret_cast<uint4*>(vt + (size_t(j) * D + e) * kB + i0) = *reinterpret_cast<uint4*>(tmp);
+    }
+    __syncthreads();   // sKbar / sVsum visible
+
+    // Cross term on MFMA: blk[c][e] = Σ_i K[i][c] V[i][e] (A = Kᵀ, B = V, k = token).
+    f32x16 blk[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) blk[u] = zero16();
+#pragma unroll
+    for (int ks = 0; ks < kB / KI; ++ks) {
+      float av[KH];
+#pragma unroll
+      for (int u = 0; u < KH; ++u) av[u] = to_f32(sK[(KI * ks + KH * g + u) * LDR + 32 * ct + l32]);
+      const typename M::AB A = M::pack(av);
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const int et = (wave * TPW + u) % NT;
+        float bv[KH];
+#pragma unroll
+        for (int q = 0; q < KH; ++q) bv[q] = to_f32(sV[(KI * ks + KH * g + q) * LDR + 32 * et + l32]);
+        blk[u] = M::mma(A, M::pack(bv), blk[u]);
+      }
+    }
+    // H_j[c][e]ᵀ = blk - k̄_j ΣV_jᵀ ; accumulate and optionally store H_j as [e][c].
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int et = (wave * TPW + u) % NT;
+      const int e = 32 * et + l32;
+      const float ve = sVsum[e];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = 32 * ct + acc_row(r, g);
+        const float hv = blk[u][r] - sKbar[c] * ve;
+        run[u][r] += hv;
+        if (flags & 1u) a.hblk[((size_t(h) * a.nb + j) * D + e) * D + c] = hv;
+      }
+    }
+    if (flags & 2u) {
+      // C_j[c][c'] = (1/n) Σ_i K[i][c] K[i][c'] - k̄_c k̄_c'
+      f32x16 cb[TPW];
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) cb[u] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < kB / KI; ++ks) {
+        float av[KH];
+#pragma unroll
+        for (int u = 0; u < KH; ++u) av[u] = to_f32(sK[(KI * ks + KH * g + u) * LDR + 32 * ct + l32]);
+        const typename M::AB A = M::pack(av);
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+          const int et = (wave * TPW + u) % NT;
+          float bv[KH];
+#pragma unroll
+          for (int q = 0; q < KH; ++q) bv[q] = to_f32(sK[(KI * ks + KH * g + q) * LDR + 32 * et + l32]);
+          cb[u] = M::mma(A, M::pack(bv), cb[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const int et = (wave * TPW + u) % NT;
+        const int c2 = 32 * et + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 32 * ct + acc_row(r, g);
+          a.cblk[((size_t(h) * a.nb + j) * D + c) * D + c2] = cb[u][r] * invn - sKbar[c] * sKbar[c2];
+        }
+      }
+    }
+    __syncthreads();   // LDS reused by the next block
+  }
+
+  float* part = a.part + (size_t(h) * a.ngroups + grp) * D * D;
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int et = (wave * TPW + u) % NT;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int c = 32 * ct + acc_row(r, g);
+      part[size_t(c) * D + 32 * et + l32] = run[u][r];
+    }
+  }
+}
+
+// Fixed-order reduction of the per-workgroup partials into H̄ᵀ (fp32) and H̄[e][c]
+// (storage type); also zeroes the padding rows of the packed centroid / mean-value
+// tiles beyond nb so the attention kernel reads finite zeros there.
+template <class T, int D>
+__global__ __launch_bounds__(256) void hbar_reduce_kernel(StatsArgs a) {
+  const int h = blockIdx.y;
+  const int x = blockIdx.x * 256 + threadIdx.x;
+  if (x >= D * D) return;
+  const int c = x / D, e = x % D;
+  const float* part = a.part + size_t(h) * a.ngroups * D * D;
+  float s = 0.f;
+  for (int q = 0; q < a.ngroups; ++q) s += part[size_t(q) * D * D + x];
+  const float hb = s / float(a.nb);
+  a.hbarT[size_t(h) * D * D + x] = hb;
+  T* hbp = reinterpret_cast<T*>(a.packed + a.pl.hbar) + size_t(h) * D * D;
+  hbp[size_t(e) * D + c] = from_f32<T>(hb);
+
+  const int pad = a.nbp - a.nb;
+  if (pad > 0 && x < pad * D) {
+    T* kbp = reinterpret_cast<T*>(a.packed + a.pl.kbar) + size_t(h) * a.nbp * D;
+    kbp[size_t(a.nb) * D + x] = from_f32<T>(0.f);
+    T* vbp = reinterpret_cast<T*>(a.packed + a.pl.vbar) + size_t(h) * a.nbp * D;
+    const int ee = x / pad, k = a.nb % kB + x % pad;
+    vbp[(size_t(a.nb / kB) * D + ee) * kB + k] = from_f32<T>(0.f);
+  }
+}
+
+template <class T, int D>
+static hipError_t launch_stats_t(const StatsArgs& a, unsigned flags, hipStream_t s) {
+  dim3 g1(a.ngroups, a.H), g2((D * D + 255) / 256, a.H);
+  hipLaunchKernelGGL((block_stats_kernel<T, D>), g1, dim3(256), 0, s, a, flags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((hbar_reduce_kernel<T, D>), g2, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_stats(int bf16, const StatsArgs& a, unsigned flags, hipStream_t s) {
+  if (bf16) return a.d == 64 ? launch_stats_t<uint16_t, 64>(a, flags, s) : launch_stats_t<uint16_t, 128>(a, flags, s);
+  return a.d == 64 ? launch_stats_t<float, 64>(a, flags, s) : launch_stats_t<float, 128>(a, flags, s);
+}
+
+}  // namespace pisa

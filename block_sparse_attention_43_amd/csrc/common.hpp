@@ -1,0 +1,143 @@
+// Device-side helpers shared by the gfx950 kernels: element types, MFMA operand
+// traits, wave reductions and the XCD-aware workgroup remap.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pisa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+  return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  __bf16 b = static_cast<__bf16>(x);  // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// Storage element <-> float.
+template <class T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) { return bf16_to_f32(v); }
+template <class T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) { return f32_to_bf16(v); }
+
+// ---------------------------------------------------------------------------
+// MFMA operand traits for the 32x32 output shape.
+//
+// For v_mfma_f32_32x32x{KI}: lane l supplies KH = KI/2 consecutive k-values of
+// row (l % 32) of A and of column (l % 32) of B, at k = KH*(l/32) + [0, KH).
+// Accumulator register r of lane l holds D[8*(r/4) + 4*(l/32) + r%4][l % 32].
+// ---------------------------------------------------------------------------
+struct MmaBF16 {
+  using T = uint16_t;                // storage element
+  using AB = bf16x8;                 // one lane's operand
+  static constexpr int KI = 16;      // k per instruction
+  static constexpr int KH = 8;       // k per lane
+  __device__ __forceinline__ static AB load(const T* p) {
+    return *reinterpret_cast<const AB*>(p);         // 16 bytes, 16-byte aligned
+  }
+  __device__ __forceinline__ static AB pack(const float* v) {
+    AB r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = static_cast<__bf16>(v[i]);
+    return r;
+  }
+  __device__ __forceinline__ static AB zero() {
+    AB r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = static_cast<__bf16>(0.f);
+    return r;
+  }
+  __device__ __forceinline__ static void unpack(AB a, float* v) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = static_cast<float>(a[i]);
+  }
+  __device__ __forceinline__ static f32x16 mma(AB a, AB b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+struct MmaF32 {
+  using T = float;
+  using AB = float;
+  static constexpr int KI = 2;
+  static constexpr int KH = 1;
+  __device__ __forceinline__ static AB load(const T* p) { return *p; }
+  __device__ __forceinline__ static AB pack(const float* v) { return v[0]; }
+  __device__ __forceinline__ static AB zero() { return 0.f; }
+  __device__ __forceinline__ static void unpack(AB a, float* v) { v[0] = a; }
+  __device__ __forceinline__ static f32x16 mma(AB a, AB b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+template <class T> struct MmaFor;
+template <> struct MmaFor<uint16_t> { using type = MmaBF16; };
+template <> struct MmaFor<float> { using type = MmaF32; };
+
+// Row index -> accumulator row of the 32x32 output:  row(r, g) = 8*(r/4) + 4*g + r%4.
+__device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Combine a value with the one held by lane l ^ 32 (the other half of the wave).
+// v_permlane32_swap with the same register as both operands returns the low half's
+// values in one result and the high half's in the other, on every lane; combining the
+// two is symmetric, so both halves end with bit-identical results.
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroups are dealt round-robin to the 8 XCDs; remap so that consecutive logical
+// ids (neighbouring query tiles of one head) run on the same XCD and share its L2.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t n) {
+  constexpr uint32_t kX = 8;
+  uint32_t q = n / kX, rmd = n % kX;
+  uint32_t x = b % kX, slot = b / kX;
+  uint32_t base = x < rmd ? x * (q + 1) : rmd * (q + 1) + (x - rmd) * q;
+  return base + slot;
+}
+
+// Block-wide exclusive scan of one int per thread (blockDim.x = 256).
+__device__ __forceinline__ int block_exclusive_scan_256(int v, int* sh /*[8]*/, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    int s = sh[w];
+    if (w < wave) off += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + x - v;
+}
+
+}  // namespace pisa

@@ -1,0 +1,90 @@
+// Host-side interface between the C ABI (abi.hip) and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pisa {
+
+constexpr int kB = 64;  // block / tile size handled by the kernels
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Byte offsets inside the packed (kernel-layout) statistics buffer.
+struct PackedLayout {
+  size_t vt, kbar, vbar, hbar, total;
+  int nb, nbp;
+};
+
+inline PackedLayout packed_layout(size_t elem, int H, int L, int d) {
+  PackedLayout p;
+  p.nb = L / kB;
+  p.nbp = (p.nb + kB - 1) / kB * kB;
+  size_t o = 0;
+  p.vt = o;   o = align256(o + size_t(H) * p.nb * d * kB * elem);    // [H][nb][d][64]   V^T per block
+  p.kbar = o; o = align256(o + size_t(H) * p.nbp * d * elem);        // [H][nbp][d]      centroids
+  p.vbar = o; o = align256(o + size_t(H) * p.nbp * d * elem);        // [H][nbp/64][d][64] (ΣV/n)^T
+  p.hbar = o; o = align256(o + size_t(H) * d * d * elem);            // [H][d][d]        H̄[e][c]
+  p.total = o;
+  return p;
+}
+
+// Blocks reduced per workgroup in the statistics kernel (sets its workspace size).
+inline int stats_group(int H, int nb) {
+  long long g = (static_cast<long long>(H) * nb + 1023) / 1024;
+  if (g < 1) g = 1;
+  if (g > 64) g = 64;
+  return static_cast<int>(g);
+}
+
+struct StatsArgs {
+  const void* K;
+  const void* V;
+  const int32_t* block_len;
+  float* kbar;
+  float* vsum;
+  float* ksig2;
+  float* hbarT;
+  float* hblk;
+  float* cblk;
+  char* packed;
+  float* part;     // [H][ngroups][d][d]
+  int H, L, d, nb, nbp, G, ngroups;
+  PackedLayout pl;
+};
+
+struct SelectArgs {
+  const void* Q;
+  const float* kbar;
+  const float* ksig2;
+  const int32_t* block_len;
+  float* qbar;     // [H][nb][d]   workspace
+  float* qsq;      // [H][nb][d]   workspace
+  float* scores;   // [H][nb][nb]  workspace
+  float* wt;       // [H][nb][nb]  or null
+  int32_t* idx;    // [H][nb][K_sel]
+  uint32_t* mask;  // [H][nb][nw]  or null
+  int H, L, d, nb, K_sel, nw;
+};
+
+struct AttnArgs {
+  const void* Q;
+  const void* K;
+  const char* packed;
+  const int32_t* block_len;
+  const int32_t* idx;
+  const uint32_t* mask;
+  const float* wt;
+  void* O;
+  float* lse;
+  int H, L, d, nb, nbp, K_sel, nw;
+  int w_linear;    // phi(w) = ln(1 + w) instead of w
+  int gate;        // zero w when w > ln n_j
+  PackedLayout pl;
+};
+
+hipError_t launch_block_stats(int bf16, const StatsArgs& a, unsigned flags, hipStream_t s);
+hipError_t launch_select(int bf16, const SelectArgs& a, hipStream_t s);
+hipError_t launch_attention(int bf16, int mode, const AttnArgs& a, hipStream_t s);
+
+}  // namespace pisa

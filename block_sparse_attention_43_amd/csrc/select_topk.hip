@@ -1,0 +1,254 @@
+// Prepare phase, part 2: pooled-query block scores, the second-order matrix and
+// block-wise top-K selection.
+//
+// q̄_i = mean of the valid rows of query tile i, \overline{q²}_i = mean of their squares
+// (PISA paper Fig. 3 prepare phase; Sparse Linear Attention blog, PWT section: square
+// first, then average). Scores s_{i,j} = q̄_i·k̄_j (MoBA-style block-mean scoring,
+// blog Sparse Attention section) and w̃_{i,j} = ½ Σ_c \overline{q²}_{i,c} σ²_{j,c}, the
+// [query block x key block] matrix that PWT computes once before the attention kernel.
+// S_i keeps the K_sel largest scores, ties to the lower block index, emitted in
+// ascending block order plus a bitmask of the selected blocks.
+//
+// Scores are fp32 with one fixed summation order per element, so identical centroids
+// score identically. Top-K is an exact radix select on order-preserving 32-bit keys
+// held in registers (256 threads, up to 128 keys each), with the tie rule resolved by
+// block-wide prefix counts in index order.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace pisa {
+
+template <class T, int D>
+__global__ __launch_bounds__(256) void pool_kernel(SelectArgs a) {
+  constexpr int PARTS = 256 / D;           // row groups
+  constexpr int RPP = kB / PARTS;          // rows per group
+  __shared__ float s1[256], s2[256];
+  const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  int n = a.block_len ? a.block_len[i] : kB;
+  n = min(max(n, 1), kB);
+  const int c = tid % D, part = tid / D;
+  const T* Qt = static_cast<const T*>(a.Q) + (size_t(h) * a.L + size_t(i) * kB) * D;
+  float s = 0.f, q2 = 0.f;
+  for (int r = part * RPP; r < (part + 1) * RPP; ++r) {
+    if (r < n) {
+      const float x = to_f32(Qt[size_t(r) * D + c]);
+      s += x;
+      q2 += x * x;
+    }
+  }
+  s1[tid] = s;
+  s2[tid] = q2;
+  __syncthreads();
+  if (tid < D) {
+    float t1 = 0.f, t2 = 0.f;
+    for (int p = 0; p < PARTS; ++p) {
+      t1 += s1[p * D + tid];
+      t2 += s2[p * D + tid];
+    }
+    const float invn = 1.f / float(n);
+    a.qbar[(size_t(h) * a.nb + i) * D + tid] = t1 * invn;
+    a.qsq[(size_t(h) * a.nb + i) * D + tid] = t2 * invn;
+  }
+}
+
+// S = Q̄ K̄ᵀ and W = ½ Q̄² Σ²ᵀ per head; 64x64 output tile per workgroup, 4x4 per thread.
+template <int D>
+__global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
+  constexpr int KC = 16;
+  __shared__ float sA[KC][68], sB[KC][68], sA2[KC][68], sB2[KC][68];
+  const int h = blockIdx.z;
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const int tid = threadIdx.x, ti = tid / 16, tj = tid % 16;
+  const bool want_w = a.wt != nullptr;
+  const float* qb = a.qbar + size_t(h) * a.nb * D;
+  const float* q2 = a.qsq + size_t(h) * a.nb * D;
+  const float* kb = a.kbar + size_t(h) * a.nb * D;
+  const float* ks = a.ksig2 + size_t(h) * a.nb * D;
+  float acc[4][4], acw[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = acw[x][y] = 0.f;
+
+  for (int c0 = 0; c0 < D; c0 += KC) {
+    // 64 rows x 16 columns of each operand, stored transposed [c][row]
+    for (int e = tid; e < 64 * KC; e += 256) {
+      const int row = e / KC, c = e % KC;
+      const int ii = i0 + row, jj = j0 + row;
+      sA[c][row] = ii < a.nb ? qb[size_t(ii) * D + c0 + c] : 0.f;
+      sB[c][row] = jj < a.nb ? kb[size_t(jj) * D + c0 + c] : 0.f;
+      if (want_w) {
+        sA2[c][row] = ii < a.nb ? q2[size_t(ii) * D + c0 + c] : 0.f;
+        sB2[c][row] = jj < a.nb ? ks[size_t(jj) * D + c0 + c] : 0.f;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        av[x] = sA[c][ti * 4 + x];
+        bv[x] = sB[c][tj * 4 + x];
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(av[x], bv[y], acc[x][y]);
+      if (want_w) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          av[x] = sA2[c][ti * 4 + x];
+          bv[x] = sB2[c][tj * 4 + x];
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int y = 0; y < 4; ++y) acw[x][y] = fmaf(av[x], bv[y], acw[x][y]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int ii = i0 + ti * 4 + x;
+    if (ii >= a.nb) continue;
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int jj = j0 + tj * 4 + y;
+      if (jj >= a.nb) continue;
+      const size_t o = (size_t(h) * a.nb + ii) * a.nb + jj;
+      a.scores[o] = acc[x][y];
+      if (want_w) a.wt[o] = 0.5f * acw[x][y];
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t order_key(float s) {
+  s = s + 0.0f;                                   // -0 -> +0 so equal scores tie
+  const uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One workgroup per (query tile, head). Thread t owns block indices [t*P, t*P + P).
+template <int P>
+__global__ __launch_bounds__(256) void topk_kernel(SelectArgs a) {
+  __shared__ int hist[256];
+  __shared__ int scan_sh[8];
+  __shared__ uint32_t s_digit;
+  __shared__ int s_rem;
+  __shared__ uint32_t smask[1024];
+  const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int nb = a.nb, K = a.K_sel;
+  const float* row = a.scores + (size_t(h) * nb + i) * nb;
+  const int base = tid * P;
+
+  uint32_t key[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) key[p] = (base + p < nb) ? order_key(row[base + p]) : 0u;
+
+  // Threshold key T (the K-th largest) and how many keys equal to T are taken.
+  uint32_t T = 0u;
+  int take_eq = 0;
+  bool all = (K >= nb);
+  if (K > 0 && !all) {
+    uint32_t prefix = 0u, pmask = 0u;
+    int rem = K;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      hist[tid] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+        if (base + p < nb && (key[p] & pmask) == prefix) atomicAdd(&hist[(key[p] >> shift) & 255u], 1);
+      __syncthreads();
+      const int b = 255 - tid;                 // scan from the highest digit down
+      const int v = hist[b];
+      int tot;
+      const int excl = block_exclusive_scan_256(v, scan_sh, &tot);
+      if (excl < rem && excl + v >= rem) {
+        s_digit = uint32_t(b);
+        s_rem = rem - excl;
+      }
+      __syncthreads();
+      prefix |= s_digit << shift;
+      pmask |= 0xFFu << shift;
+      rem = s_rem;
+      __syncthreads();
+    }
+    T = prefix;
+    take_eq = rem;
+  }
+
+  // Selected flags in index order: key > T, or key == T among the first take_eq such.
+  int eq_local = 0;
+#pragma unroll
+  for (int p = 0; p < P; ++p) eq_local += (base + p < nb && key[p] == T) ? 1 : 0;
+  int tot;
+  const int eq_start = block_exclusive_scan_256(eq_local, scan_sh, &tot);
+  auto selected = [&](int p, int& eqc) -> bool {
+    if (base + p >= nb) return false;
+    if (all) return true;
+    if (K == 0) return false;
+    if (key[p] > T) return true;
+    if (key[p] == T) return eqc++ < take_eq;
+    return false;
+  };
+  int cnt = 0;
+  {
+    int eqc = eq_start;
+#pragma unroll
+    for (int p = 0; p < P; ++p) cnt += selected(p, eqc) ? 1 : 0;
+  }
+  int pos = block_exclusive_scan_256(cnt, scan_sh, &tot);
+  int32_t* out = a.idx + (size_t(h) * nb + i) * K;
+  if (a.mask) {
+    for (int w = tid; w < a.nw; w += 256) smask[w] = 0u;
+    __syncthreads();
+  }
+  {
+    int eqc = eq_start;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      if (selected(p, eqc)) {
+        if (pos < K) out[pos] = base + p;   // bound holds by construction; kept as a guard
+        ++pos;
+        if (a.mask) atomicOr(&smask[(base + p) >> 5], 1u << ((base + p) & 31));
+      }
+    }
+  }
+  if (a.mask) {
+    __syncthreads();
+    uint32_t* mo = a.mask + (size_t(h) * nb + i) * a.nw;
+    for (int w = tid; w < a.nw; w += 256) mo[w] = smask[w];
+  }
+}
+
+template <class T, int D>
+static hipError_t launch_select_t(const SelectArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((pool_kernel<T, D>), dim3(a.nb, a.H), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nt = (a.nb + 63) / 64;
+  hipLaunchKernelGGL((score_kernel<D>), dim3(nt, nt, a.H), dim3(256), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int per = (a.nb + 255) / 256;
+  const dim3 g(a.nb, a.H);
+  if (per <= 1) hipLaunchKernelGGL((topk_kernel<1>), g, dim3(256), 0, s, a);
+  else if (per <= 2) hipLaunchKernelGGL((topk_kernel<2>), g, dim3(256), 0, s, a);
+  else if (per <= 4) hipLaunchKernelGGL((topk_kernel<4>), g, dim3(256), 0, s, a);
+  else if (per <= 8) hipLaunchKernelGGL((topk_kernel<8>), g, dim3(256), 0, s, a);
+  else if (per <= 16) hipLaunchKernelGGL((topk_kernel<16>), g, dim3(256), 0, s, a);
+  else if (per <= 32) hipLaunchKernelGGL((topk_kernel<32>), g, dim3(256), 0, s, a);
+  else if (per <= 64) hipLaunchKernelGGL((topk_kernel<64>), g, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((topk_kernel<128>), g, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(int bf16, const SelectArgs& a, hipStream_t s) {
+  if (bf16) return a.d == 64 ? launch_select_t<uint16_t, 64>(a, s) : launch_select_t<uint16_t, 128>(a, s);
+  return a.d == 64 ? launch_select_t<float, 64>(a, s) : launch_select_t<float, 128>(a, s);
+}
+
+}  // namespace pisa

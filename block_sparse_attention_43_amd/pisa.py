@@ -1,0 +1,203 @@
+"""Python binding of the C ABI in include/pisa.h (argument marshalling only).
+
+PyTorch provides device memory and the current HIP stream; every step of the forward
+pass runs in the library's HIP kernels. Loading fails loudly if ``libpisa.so`` is
+missing: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpisa.so")
+
+PISA_F32, PISA_BF16 = 0, 1
+MODE_DROP, MODE_PISA, MODE_PWT, MODE_LITERAL = 0, 1, 2, 3
+W_LINEAR, W_EXP, W_NOGATE = 1 << 4, 1 << 5, 1 << 6
+STATS_BLOCK_H, STATS_BLOCK_C = 1 << 0, 1 << 1
+MODES = {"drop": MODE_DROP, "pisa": MODE_PISA, "pwt": MODE_PWT, "literal": MODE_LITERAL}
+B = 64
+
+# Every symbol include/pisa.h declares.
+EXPORTS = ("pisa_packed_bytes", "pisa_block_stats_workspace_bytes", "pisa_block_stats",
+           "pisa_select_workspace_bytes", "pisa_select_topk", "pisa_attention_fwd",
+           "pisa_last_error", "pisa_version")
+
+
+class PisaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"pisa status {status}: {msg}")
+        self.status = status
+
+
+class _Stats(ctypes.Structure):
+    _fields_ = [("kbar", ctypes.c_void_p), ("vsum", ctypes.c_void_p), ("ksig2", ctypes.c_void_p),
+                ("hbarT", ctypes.c_void_p), ("hblk", ctypes.c_void_p), ("cblk", ctypes.c_void_p),
+                ("packed", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m block_sparse_attention_43_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_uint
+    sp = ctypes.POINTER(_Stats)
+    lib.pisa_packed_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.pisa_packed_bytes.restype = sz
+    lib.pisa_block_stats_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.pisa_block_stats_workspace_bytes.restype = sz
+    lib.pisa_select_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.pisa_select_workspace_bytes.restype = sz
+    lib.pisa_block_stats.argtypes = [i32, vp, vp, i32, i32, i32, i32, vp, u32, sp, vp, sz, vp]
+    lib.pisa_block_stats.restype = i32
+    lib.pisa_select_topk.argtypes = [i32, vp, sp, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, sz, vp]
+    lib.pisa_select_topk.restype = i32
+    lib.pisa_attention_fwd.argtypes = [i32, vp, vp, vp, sp, vp, vp, vp, i32, i32, i32, i32, vp, i32,
+                                       u32, vp, vp, vp]
+    lib.pisa_attention_fwd.restype = i32
+    lib.pisa_last_error.argtypes = []
+    lib.pisa_last_error.restype = ctypes.c_char_p
+    lib.pisa_version.argtypes = []
+    lib.pisa_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise PisaError(status, load().pisa_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PISA_F32
+    if t.dtype == torch.bfloat16:
+        return PISA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _shape(Q: torch.Tensor):
+    if Q.dim() != 3 or not Q.is_contiguous():
+        raise ValueError("tensors must be contiguous [H, L, d]")
+    H, L, d = Q.shape
+    return H, L, d
+
+
+@dataclass
+class Stats:
+    """Device buffers of pisa_stats (see include/pisa.h)."""
+    kbar: torch.Tensor
+    vsum: torch.Tensor
+    ksig2: torch.Tensor
+    hbarT: torch.Tensor
+    packed: torch.Tensor
+    hblk: torch.Tensor | None = None
+    cblk: torch.Tensor | None = None
+
+    def struct(self) -> _Stats:
+        return _Stats(self.kbar.data_ptr(), self.vsum.data_ptr(), self.ksig2.data_ptr(),
+                      self.hbarT.data_ptr(), _ptr(self.hblk), _ptr(self.cblk), self.packed.data_ptr())
+
+
+def packed_bytes(dtype: torch.dtype, H: int, L: int, d: int) -> int:
+    code = PISA_BF16 if dtype == torch.bfloat16 else PISA_F32
+    return load().pisa_packed_bytes(code, H, L, d, B)
+
+
+def alloc_stats(K: torch.Tensor, flags: int = 0) -> Stats:
+    H, L, d = _shape(K)
+    nb = L // B
+    dev = K.device
+    f = dict(dtype=torch.float32, device=dev)
+    return Stats(kbar=torch.empty(H, nb, d, **f), vsum=torch.empty(H, nb, d, **f),
+                 ksig2=torch.empty(H, nb, d, **f), hbarT=torch.empty(H, d, d, **f),
+                 packed=torch.empty(packed_bytes(K.dtype, H, L, d), dtype=torch.uint8, device=dev),
+                 hblk=torch.empty(H, nb, d, d, **f) if flags & STATS_BLOCK_H else None,
+                 cblk=torch.empty(H, nb, d, d, **f) if flags & STATS_BLOCK_C else None)
+
+
+def block_stats(K, V, block_len=None, flags: int = 0, out: Stats | None = None, workspace=None,
+                stream=None) -> Stats:
+    lib = load()
+    H, L, d = _shape(K)
+    st = out if out is not None else alloc_stats(K, flags)
+    need = lib.pisa_block_stats_workspace_bytes(H, L, d, B)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=K.device)
+    s = st.struct()
+    _check(lib.pisa_block_stats(_dtype_code(K), _ptr(K), _ptr(V), H, L, d, B, _ptr(block_len), flags,
+                                ctypes.byref(s), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return st
+
+
+def select_topk(Q, st: Stats, K_sel: int, block_len=None, want_wt: bool = True, want_mask: bool = True,
+                out=None, workspace=None, stream=None):
+    """Returns (idx [H, nb, K_sel] int32, mask [H, nb, nw] int32 bit pattern or None,
+    wt [H, nb, nb] float32 or None)."""
+    lib = load()
+    H, L, d = _shape(Q)
+    nb = L // B
+    nw = (nb + 31) // 32
+    if out is None:
+        idx = torch.empty(H, nb, max(K_sel, 1), dtype=torch.int32, device=Q.device)[:, :, :K_sel]
+        mask = torch.empty(H, nb, nw, dtype=torch.int32, device=Q.device) if want_mask else None
+        wt = torch.empty(H, nb, nb, dtype=torch.float32, device=Q.device) if want_wt else None
+    else:
+        idx, mask, wt = out
+    need = lib.pisa_select_workspace_bytes(H, L, d, B)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    s = st.struct()
+    _check(lib.pisa_select_topk(_dtype_code(Q), _ptr(Q), ctypes.byref(s), H, L, d, B, _ptr(block_len),
+                                K_sel, _ptr(idx), _ptr(mask), _ptr(wt), _ptr(workspace),
+                                workspace.numel(), _stream(stream)))
+    return idx, mask, wt
+
+
+def attention_fwd(Q, K, V, st: Stats, idx, mask, wt, K_sel: int, mode="pwt", block_len=None,
+                  out=None, lse=None, want_lse: bool = True, stream=None):
+    lib = load()
+    H, L, d = _shape(Q)
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    if out is None:
+        out = torch.empty_like(Q)
+    if lse is None and want_lse:
+        lse = torch.empty(H, L, dtype=torch.float32, device=Q.device)
+    s = st.struct()
+    _check(lib.pisa_attention_fwd(_dtype_code(Q), _ptr(Q), _ptr(K), _ptr(V), ctypes.byref(s), _ptr(idx),
+                                  _ptr(mask), _ptr(wt), H, L, d, B, _ptr(block_len), K_sel, m, _ptr(out),
+                                  _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def forward(Q, K, V, K_sel: int, mode="pwt", block_len=None, flags: int = 0, stream=None):
+    """One full pass: statistics, selection, fused attention. Returns (O, lse, idx, stats)."""
+    base = (MODES[mode] if isinstance(mode, str) else int(mode)) & 15
+    st = block_stats(K, V, block_len, stream=stream)
+    idx, mask, wt = select_topk(Q, st, K_sel, block_len, want_wt=(base == MODE_PWT), stream=stream)
+    O, lse = attention_fwd(Q, K, V, st, idx, mask, wt, K_sel, mode, block_len, stream=stream)
+    return O, lse, idx, st
+
+
+def version() -> str:
+    return load().pisa_version().decode()

@@ -1,0 +1,192 @@
+/*
+ * pisa.h — C ABI of the piecewise (exact-or-approximate) block-sparse attention
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * The method (PISA paper "PISA: Piecewise Sparse Attention Is Wiser for Efficient
+ * Diffusion Transformers", §3.2 Formulation Eq. (3.2), §3.3 Hybrid Approximation,
+ * §3.4 Hardware-aware Kernel Implementation and Fig. 3; blog "Sparse Linear Attention",
+ * sections "Sparse Linear Attention" and "Going Further: Adding the Second-Order Term
+ * (PWT)"): keys are cut into blocks of B tokens; each query tile of B rows attends
+ * exactly to its K_sel best-scoring key blocks, and every other block enters the same
+ * softmax as one Taylor "virtual token" built from the block's statistics.
+ *
+ * Three stream-ordered calls make one forward pass:
+ *   pisa_block_stats    prepare phase: per-block statistics of K and V
+ *   pisa_select_topk    prepare phase: pooled-query scores, second-order matrix, top-K
+ *   pisa_attention_fwd  fused kernel: exact phase, virtual-token phase, first-order phase
+ *
+ * Conventions shared by every call
+ *   Layout     Q, K, V, O are contiguous row-major [H][L][d] (d fastest); a batch is
+ *              folded into H. L is the padded length, a multiple of B. Q, K, V share one
+ *              block partition (non-causal self-attention; the PISA paper's appendix on
+ *              sparse attention for DiTs covers the bidirectional case only).
+ *   Scale      Q already carries the 1/sqrt(d) factor (the pages absorb it into q).
+ *   Blocks     block_len is a DEVICE int32[nb] (nb = L / B), shared by all heads, or NULL
+ *              when every block is full. Block j's n_j valid tokens occupy its first n_j
+ *              slots; values are clamped to [1, B] by the kernels. Padded slots may hold
+ *              any finite values: they are masked. Padded query rows produce O = 0 and
+ *              lse = -inf.
+ *   Supported  B == 64, d in {64, 128}, 1 <= nb <= 32768, dtype PISA_F32 or PISA_BF16
+ *              (bfloat16 storage; fp32 accumulation everywhere). Every tensor pointer
+ *              must be 16-byte aligned.
+ *   Ownership  The caller allocates every buffer (device memory), including the
+ *              workspaces, and keeps them alive until the stream work completes. The
+ *              library allocates nothing and keeps no state besides the thread-local
+ *              error string.
+ *   Streams    `stream` is a hipStream_t passed as void* (NULL = default stream). Every
+ *              call only enqueues work and returns.
+ *   Errors     Argument errors return synchronously, with a message from
+ *              pisa_last_error() and nothing enqueued. Unsupported shapes or dtypes give
+ *              PISA_ERR_UNSUPPORTED, a short workspace PISA_ERR_WORKSPACE, a failed launch
+ *              PISA_ERR_HIP (with hipGetErrorString). Faults inside kernels surface at the
+ *              caller's next synchronisation. Inputs are not scanned for NaN/Inf.
+ *              Nothing throws or aborts across the ABI.
+ */
+#ifndef PISA_H
+#define PISA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PISA_OK = 0,
+  PISA_ERR_INVALID_ARG = 1,
+  PISA_ERR_UNSUPPORTED = 2,
+  PISA_ERR_WORKSPACE = 3,
+  PISA_ERR_HIP = 4
+} pisa_status;
+
+typedef enum { PISA_F32 = 0, PISA_BF16 = 1 } pisa_dtype;
+
+/* Attention modes (low 4 bits of `mode`). */
+enum {
+  /* Keep-or-drop block-sparse attention: only the selected blocks (Phase 1).
+     With K_sel = nb this is dense attention. */
+  PISA_MODE_DROP = 0,
+  /* PISA hybrid order: block-wise zeroth-order virtual tokens + global first order
+     (A_t H̄ q_t), PISA paper §3.3 and §3.4. */
+  PISA_MODE_PISA = 1,
+  /* PWT: PISA plus the diagonal, query-pooled, gated second-order mass term
+     w̃_{i,j} = ½ Σ_c mean_tile(q_c²) σ²_{j,c} on the virtual-token logit
+     (blog, PWT section). */
+  PISA_MODE_PWT = 2,
+  /* Block-wise first order H_j q_t and per-row w = ½ q_tᵀ C_j q_t with weight 1 + w,
+     computed from the raw unselected blocks (blog, PWT derivation; PISA paper Eq. (3.2)
+     exact first-order variant). Costs about as much as dense attention. */
+  PISA_MODE_LITERAL = 3
+};
+
+/* Modifier bits of `mode`. */
+enum {
+  PISA_W_LINEAR = 1u << 4,  /* φ(w) = ln(1 + w) (the 1 + w form); default for LITERAL */
+  PISA_W_EXP = 1u << 5,     /* φ(w) = w (the e^w form); default for PWT */
+  PISA_W_NOGATE = 1u << 6   /* disable the validity gate (w > ln n_j => w = 0) */
+};
+
+/* Flags of pisa_block_stats. */
+enum {
+  PISA_STATS_BLOCK_H = 1u << 0, /* also write every H_j to pisa_stats.hblk */
+  PISA_STATS_BLOCK_C = 1u << 1  /* also write every C_j to pisa_stats.cblk */
+};
+
+/*
+ * Block statistics (device buffers, caller-allocated, row-major). For block j of head h
+ * with valid tokens I_j, n_j = |I_j| (blog, notation and PWT sections; PISA paper
+ * Fig. 3 prepare phase):
+ *   kbar  [H][nb][d]   k̄_j = (1/n_j) Σ_{I_j} k_i
+ *   vsum  [H][nb][d]   ΣV_j = Σ_{I_j} v_i
+ *   ksig2 [H][nb][d]   σ²_{j,c} = (1/n_j) Σ_{I_j} (k_{i,c} - k̄_{j,c})²
+ *   hbarT [H][d][d]    H̄ᵀ[c][e] with H̄ = (1/nb) Σ_j H_j, H_j = Σ_{I_j} v_i (k_i - k̄_j)ᵀ
+ *   hblk  [H][nb][d][d] H_j[e][c]              (NULL unless PISA_STATS_BLOCK_H)
+ *   cblk  [H][nb][d][d] C_j = (1/n_j) Σ (k_i - k̄_j)(k_i - k̄_j)ᵀ (NULL unless PISA_STATS_BLOCK_C)
+ *   packed             pisa_packed_bytes() bytes: the same statistics re-laid for the
+ *                      attention kernel's operands (plus Vᵀ per block); opaque, written
+ *                      by pisa_block_stats and read by pisa_attention_fwd.
+ */
+typedef struct {
+  float* kbar;
+  float* vsum;
+  float* ksig2;
+  float* hbarT;
+  float* hblk;
+  float* cblk;
+  void* packed;
+} pisa_stats;
+
+/* Bytes of pisa_stats.packed for these sizes (0 if unsupported). */
+size_t pisa_packed_bytes(pisa_dtype dt, int H, int L, int d, int B);
+
+/* Workspace bytes of pisa_block_stats (fp32 partial sums of H̄; 0 if unsupported). */
+size_t pisa_block_stats_workspace_bytes(int H, int L, int d, int B);
+
+/*
+ * Prepare phase, part 1 (PISA paper §3.4 "Prepare Phase": block centroids, value sums
+ * and the global statistic H̄ in a single pass; blog, PWT section: σ²_j).
+ * K, V: [H][L][d] device tensors of dtype `dt`. Writes every field of *out (hblk / cblk
+ * only when flagged). `out` is a host pointer to a struct of device pointers.
+ * Repeated calls on the same inputs give bit-identical results.
+ */
+pisa_status pisa_block_stats(pisa_dtype dt, const void* K, const void* V, int H, int L, int d,
+                             int B, const int32_t* block_len, unsigned flags,
+                             const pisa_stats* out, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Workspace bytes of pisa_select_topk (pooled queries and the fp32 score matrix). */
+size_t pisa_select_workspace_bytes(int H, int L, int d, int B);
+
+/*
+ * Prepare phase, part 2 (PISA paper Fig. 3 and §3.4: block-wise top-K selection;
+ * blog, Sparse Attention section: MoBA block-mean scoring; blog, PWT section: the
+ * [query block x key block] matrix w̃).
+ * For query tile i: q̄_i = mean of its valid Q rows, \overline{q²}_i = mean of their
+ * squares; s_{i,j} = q̄_i·k̄_j in fp32; S_i = the K_sel largest s_{i,j}, ties to the lower
+ * block index.
+ *   Q      [H][L][d] dtype `dt`
+ *   st     reads st->kbar and st->ksig2 (from pisa_block_stats)
+ *   idx    [H][nb][K_sel] int32 out: S_i in ascending block order
+ *   mask   [H][nb][ceil(nb/32)] uint32 out or NULL: bit j set iff j in S_i
+ *   wt     [H][nb][nb] float out or NULL: w̃_{i,j} = ½ Σ_c \overline{q²}_{i,c} σ²_{j,c}
+ *          before the gate (needed by PISA_MODE_PWT)
+ * 0 <= K_sel <= nb.
+ */
+pisa_status pisa_select_topk(pisa_dtype dt, const void* Q, const pisa_stats* st, int H, int L,
+                             int d, int B, const int32_t* block_len, int K_sel, int32_t* idx,
+                             uint32_t* mask, float* wt, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * Fused kernel (PISA paper §3.4 phases 1-3; Eq. (3.2); blog, PWT section).
+ * For valid query t of tile i, o_t = N_t / D_t with one running max and denominator:
+ *   D_t = Σ_{j∈S_i} Σ_{n<n_j} e^{q_t·k_{j,n}} + Σ_{j∉S_i} n_j e^{q_t·k̄_j + φ_{t,j}}
+ *   N_t = Σ_{j∈S_i} Σ_{n<n_j} e^{q_t·k_{j,n}} v_{j,n} + Σ_{j∉S_i} e^{q_t·k̄_j + φ_{t,j}} ΣV_j
+ *         + first order: (Σ_{j∉S_i} e^{q_t·k̄_j + φ_{t,j}}) H̄ q_t      (PISA, PWT)
+ *                        Σ_{j∉S_i} e^{q_t·k̄_j + φ_{t,j}} H_j q_t        (LITERAL)
+ *   φ = 0 (PISA); φ = w̃_{i,j} (PWT); per-row w = ½ q_tᵀC_j q_t mapped to ln(1 + w)
+ *   (LITERAL); w is zeroed when w > ln n_j unless PISA_W_NOGATE. DROP keeps S_i only.
+ * Inputs: Q, K, V [H][L][d] dtype `dt`; st->packed from pisa_block_stats on the same K, V;
+ * idx from pisa_select_topk with the same K_sel; mask (required unless DROP); wt
+ * (required for PWT). Outputs: O [H][L][d] dtype `dt`; lse [H][L] float or NULL
+ * (natural-log log-sum-exp of every row's logits, -inf for padded rows and rows with no
+ * support). Out-of-range entries of idx are treated as empty blocks.
+ */
+pisa_status pisa_attention_fwd(pisa_dtype dt, const void* Q, const void* K, const void* V,
+                               const pisa_stats* st, const int32_t* idx, const uint32_t* mask,
+                               const float* wt, int H, int L, int d, int B,
+                               const int32_t* block_len, int K_sel, unsigned mode, void* O,
+                               float* lse, void* stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* pisa_last_error(void);
+
+/* Library version string. */
+const char* pisa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PISA_H */

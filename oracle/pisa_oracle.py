@@ -74,7 +74,7 @@ def block_ranges(L_pad: int, B: int, block_len=None):
 
 
 # ----------------------------------------------------------------------------- statistics
-def block_stats(K: np.ndarray, V: np.ndarray, B: int, block_len=None) -> dict:
+def block_stats(K: np.ndarray, V: np.ndarray, B: int, block_len=None, per_block: bool = True) -> dict:
     """Per-block statistics of one head.
 
     k̄_j = (1/n_j) sum_i k_i                       (blog, notation; MoBA centroid)
@@ -83,6 +83,9 @@ def block_stats(K: np.ndarray, V: np.ndarray, B: int, block_len=None) -> dict:
     C_j = (1/n_j) sum_i (k_i - k̄_j)(k_i - k̄_j)^T   (blog, PWT section: within-block key covariance)
     σ²_j = diag C_j                                 (blog, PWT section: diagonal approximation)
     H̄ = (1/nb) sum_j H_j                            (blog: H̄ = (B/L) sum_j H_j with L = nb·B)
+
+    per_block=False keeps only H̄ and σ² (H and C are None): the same sums, without
+    storing the nb d x d matrices of long sequences.
     """
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
@@ -91,8 +94,10 @@ def block_stats(K: np.ndarray, V: np.ndarray, B: int, block_len=None) -> dict:
     nb = len(rng)
     kbar = np.zeros((nb, d))
     vsum = np.zeros((nb, d))
-    Hj = np.zeros((nb, d, d))
-    Cj = np.zeros((nb, d, d))
+    sig2 = np.zeros((nb, d))
+    Hj = np.zeros((nb, d, d)) if per_block else None
+    Cj = np.zeros((nb, d, d)) if per_block else None
+    hsum = np.zeros((d, d))
     n = np.zeros(nb)
     for j, (s, nj) in enumerate(rng):
         k = K[s:s + nj]
@@ -100,11 +105,14 @@ def block_stats(K: np.ndarray, V: np.ndarray, B: int, block_len=None) -> dict:
         kbar[j] = k.mean(axis=0)
         vsum[j] = v.sum(axis=0)
         dev = k - kbar[j]
-        Hj[j] = v.T @ dev
-        Cj[j] = dev.T @ dev / nj
+        h = v.T @ dev
+        hsum += h
+        sig2[j] = (dev ** 2).mean(axis=0)
+        if per_block:
+            Hj[j] = h
+            Cj[j] = dev.T @ dev / nj
         n[j] = nj
-    sig2 = np.einsum("jcc->jc", Cj).copy()
-    hbar = Hj.mean(axis=0)
+    hbar = hsum / nb
     return dict(kbar=kbar, vsum=vsum, H=Hj, C=Cj, sig2=sig2, hbar=hbar, n=n)
 
 
@@ -204,16 +212,19 @@ def attention_head(Q, K, V, B: int, block_len=None, K_sel: int = 0, mode: str = 
     L_pad, d = Q.shape
     rng = block_ranges(L_pad, B, block_len)
     nb = len(rng)
-    st = stats if stats is not None else block_stats(K, V, B, block_len)
+    st = stats if stats is not None else block_stats(
+        K, V, B, block_len, per_block=(first == "block" or w_kind == "row"))
     pq = pool_queries(Q, B, block_len)
+    tile_list = list(range(nb)) if tiles is None else list(tiles)
     if idx is None:
-        idx = select_topk(block_scores(pq["qbar"], st["kbar"]), K_sel)
+        # selection rows of the evaluated tiles only (other rows stay -1)
+        idx = np.full((nb, K_sel), -1, dtype=np.int64)
+        idx[tile_list] = select_topk(block_scores(pq["qbar"][tile_list], st["kbar"]), K_sel)
     idx = np.asarray(idx, dtype=np.int64).reshape(nb, -1)
     n = st["n"]
 
     O = np.zeros((L_pad, d))
     lse = np.full(L_pad, -np.inf)
-    tile_list = range(nb) if tiles is None else tiles
     for i in tile_list:
         s0, ni = rng[i]
         q = Q[s0:s0 + ni]                                     # [m, d]

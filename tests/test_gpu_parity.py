@@ -1,0 +1,222 @@
+"""GPU parity of the three library calls against the oracle on small seeded cases that
+span several tiles, ragged blocks and a partial centroid group.
+
+Bar: selection bit-exact wherever the fp32 score gap exceeds its rounding bound; outputs
+rel-L2 <= 1e-4 for fp32 inputs and <= 2e-2 for bf16 inputs against the oracle on its own
+selection (the tighter comparison on the GPU's selection is asserted too).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_43_amd import synth
+from oracle import pisa_oracle as orc
+from helpers import (MODE_NAMES, check_selection, gpu_run, mask_to_sets, rel_l2, to_device,
+                     valid_rows)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+# tighter arithmetic bound when both sides use the same selection
+TOL_SAME_SEL = {"f32": 1e-4, "bf16": 1e-2}
+
+
+def _case(name):
+    if name == "tiny":
+        return synth.make("tiny"), 4
+    if name == "bf16_d128_ragged":
+        bl = [64, 64, 17, 64, 1, 64, 40, 64, 64, 33]
+        return synth.random_blocks(101, H=2, nb=10, d=128, dtype="bf16", block_len=bl, smooth=2.0), 3
+    if name == "bf16_d64":
+        return synth.random_blocks(102, H=3, nb=7, d=64, dtype="bf16", smooth=2.0), 2
+    if name == "f32_d128_ragged":
+        bl = [64, 8, 64, 64, 50, 64, 64, 2, 64]
+        return synth.random_blocks(103, H=2, nb=9, d=128, dtype="f32", block_len=bl, smooth=2.0), 4
+    if name == "bf16_nb70":
+        return synth.random_blocks(104, H=1, nb=70, d=128, dtype="bf16", smooth=2.0), 9
+    if name == "f32_d64_ragged_nb130":
+        bl = np.full(130, 64)
+        bl[[3, 64, 129]] = [5, 63, 1]
+        return synth.random_blocks(105, H=1, nb=130, d=64, dtype="f32", block_len=bl, smooth=1.0), 13
+    raise KeyError(name)
+
+
+CASES = ["tiny", "bf16_d128_ragged", "bf16_d64", "f32_d128_ragged", "bf16_nb70", "f32_d64_ragged_nb130"]
+
+
+def _oracle(inp, h, mode, K_sel, idx=None, **kw):
+    return orc.attention_head(inp.f64("Q", h), inp.f64("K", h), inp.f64("V", h), 64,
+                              inp.layout.block_len, K_sel, mode, idx=idx, **kw)
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_block_stats_parity(gpu_lib, case):
+    inp, _ = _case(case)
+    g = gpu_run(gpu_lib, inp, "drop", 0, flags=gpu_lib.STATS_BLOCK_H | gpu_lib.STATS_BLOCK_C)
+    for h in range(inp.H):
+        st = orc.block_stats(inp.f64("K", h), inp.f64("V", h), 64, inp.layout.block_len)
+        assert rel_l2(g["kbar"][h], st["kbar"]) < 1e-6
+        assert rel_l2(g["vsum"][h], st["vsum"]) < 1e-6
+        assert rel_l2(g["ksig2"][h], st["sig2"]) < 1e-5
+        assert rel_l2(g["hbarT"][h], st["hbar"].T) < 1e-5
+        assert rel_l2(g["hblk"][h], st["H"]) < 1e-5
+        assert rel_l2(g["cblk"][h], st["C"]) < 1e-5
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_selection_parity(gpu_lib, case):
+    inp, K_sel = _case(case)
+    g = gpu_run(gpu_lib, inp, "pwt", K_sel)
+    bl = inp.layout.block_len
+    for h in range(inp.H):
+        Q, K, V = inp.f64("Q", h), inp.f64("K", h), inp.f64("V", h)
+        st = orc.block_stats(K, V, 64, bl, per_block=False)
+        pq = orc.pool_queries(Q, 64, bl)
+        scores = orc.block_scores(pq["qbar"], st["kbar"])
+        exact, near, gap = check_selection(g["idx"][h], scores, K_sel)
+        print(f"{case} h{h}: {exact} tiles bit-exact, {near} near ties, min gap {gap:.3e}")
+        if inp.cfg.dtype == "f32":
+            assert near == 0, "fp32 selection must be bit-exact"
+        sets = mask_to_sets(g["mask"][h], inp.nb)
+        for i in range(inp.nb):
+            assert set(np.flatnonzero(sets[i])) == set(g["idx"][h][i])
+        assert rel_l2(g["wt"][h], orc.pooled_w(pq["qsq"], st["sig2"])) < 1e-5
+
+
+@pytest.mark.parametrize("mode", MODE_NAMES)
+@pytest.mark.parametrize("case", CASES)
+def test_attention_parity(gpu_lib, case, mode):
+    inp, K_sel = _case(case)
+    g = gpu_run(gpu_lib, inp, mode, K_sel)
+    ok = valid_rows(inp)
+    worst_own = worst_same = 0.0
+    for h in range(inp.H):
+        own = _oracle(inp, h, mode, K_sel)
+        same = _oracle(inp, h, mode, K_sel, idx=g["idx"][h])
+        e_own = rel_l2(g["O"][h][ok], own["O"][ok])
+        e_same = rel_l2(g["O"][h][ok], same["O"][ok])
+        worst_own, worst_same = max(worst_own, e_own), max(worst_same, e_same)
+        assert np.all(g["O"][h][~ok] == 0)
+        assert np.all(np.isneginf(g["lse"][h][~ok]))
+        lse_err = np.abs(g["lse"][h][ok] - same["lse"][ok]).max()
+        assert lse_err < (1e-4 if inp.cfg.dtype == "f32" else 2e-2)
+    print(f"{case} {mode}: rel-L2 vs oracle own sel {worst_own:.2e}, same sel {worst_same:.2e}")
+    assert worst_own <= TOL[inp.cfg.dtype]
+    assert worst_same <= TOL_SAME_SEL[inp.cfg.dtype]
+
+
+@pytest.mark.parametrize("mode", MODE_NAMES)
+@pytest.mark.parametrize("which", ["zero", "all"])
+def test_selection_extremes(gpu_lib, mode, which):
+    """K_sel = 0 (pure virtual attention; DROP gives an empty support: O = 0, lse = -inf)
+    and K_sel = nb (every mode is dense attention)."""
+    inp, _ = _case("bf16_d128_ragged")
+    K_sel = 0 if which == "zero" else inp.nb
+    g = gpu_run(gpu_lib, inp, mode, K_sel)
+    ok = valid_rows(inp)
+    for h in range(inp.H):
+        ref = _oracle(inp, h, mode, K_sel)
+        if which == "zero" and mode == "drop":
+            assert np.all(g["O"][h] == 0) and np.all(np.isneginf(g["lse"][h]))
+            continue
+        assert rel_l2(g["O"][h][ok], ref["O"][ok]) < 1e-2
+        if which == "all":
+            dense = orc.dense_attention_head(inp.f64("Q", h), inp.f64("K", h), inp.f64("V", h), 64,
+                                             inp.layout.block_len)
+            assert rel_l2(g["O"][h][ok], dense["O"][ok]) < 1e-2
+
+
+@pytest.mark.parametrize("bits,mode,kw", [
+    ("W_LINEAR", "pwt", dict(w_map="linear")),
+    ("W_NOGATE", "pwt", dict(guard="none")),
+    ("W_EXP", "literal", dict(w_map="exp")),
+    ("W_NOGATE", "literal", dict(guard="none")),
+])
+def test_mode_modifiers(gpu_lib, bits, mode, kw):
+    inp, K_sel = _case("f32_d128_ragged")
+    g = gpu_run(gpu_lib, inp, mode, K_sel, mode_bits=getattr(gpu_lib, bits))
+    ok = valid_rows(inp)
+    for h in range(inp.H):
+        ref = _oracle(inp, h, mode, K_sel, idx=g["idx"][h], **kw)
+        assert rel_l2(g["O"][h][ok], ref["O"][ok]) < 1e-4
+
+
+def test_gate_fires_on_outliers(gpu_lib):
+    """Outlier key/query dimensions make w̃ exceed ln n_j; the gate must zero it so PWT
+    equals PISA, and the output stays finite (blog, PWT section)."""
+    inp, K_sel = _case("f32_d128_ragged")
+    for name in ("Q", "K"):
+        x = getattr(inp, name)
+        x[:, :, [3, 77]] *= 40.0
+    t = to_device(inp)
+    pwt = gpu_run(gpu_lib, inp, "pwt", K_sel, tensors=t)
+    pisa = gpu_run(gpu_lib, inp, "pisa", K_sel, tensors=t)
+    ok = valid_rows(inp)
+    assert np.all(np.isfinite(pwt["O"]))
+    for h in range(inp.H):
+        ref = _oracle(inp, h, "pwt", K_sel, idx=pwt["idx"][h])
+        assert rel_l2(pwt["O"][h][ok], ref["O"][ok]) < 1e-4
+    gated = pwt["wt"] > np.log(inp.layout.block_len)[None, None, :]
+    assert gated.mean() > 0.5
+    if gated.all():
+        assert rel_l2(pwt["O"][:, ok], pisa["O"][:, ok]) < 1e-6
+
+
+def test_deterministic(gpu_lib):
+    inp, K_sel = _case("bf16_nb70")
+    t = to_device(inp)
+    a = gpu_run(gpu_lib, inp, "pwt", K_sel, tensors=t)
+    b = gpu_run(gpu_lib, inp, "pwt", K_sel, tensors=t)
+    for k in ("O", "lse", "idx", "hbarT", "kbar", "wt"):
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+
+
+def test_padding_content_is_ignored(gpu_lib):
+    """Garbage in the padded slots of Q, K and V leaves every valid output unchanged."""
+    inp, K_sel = _case("bf16_d128_ragged")
+    ok = valid_rows(inp)
+    clean = gpu_run(gpu_lib, inp, "pwt", K_sel)
+    rng = np.random.default_rng(5)
+    for name in ("Q", "K", "V"):
+        x = getattr(inp, name)
+        junk = rng.standard_normal((inp.H, int((~ok).sum()), inp.d)) * 30
+        x[:, ~ok, :] = synth.f32_to_bf16_bits(junk)
+    dirty = gpu_run(gpu_lib, inp, "pwt", K_sel)
+    assert np.array_equal(clean["idx"], dirty["idx"])
+    assert np.array_equal(clean["O"][:, ok], dirty["O"][:, ok])
+
+
+def test_out_of_range_indices_are_empty_blocks(gpu_lib):
+    """The kernel bounds-checks idx: entries outside [0, nb) contribute nothing."""
+    pisa = gpu_lib
+    inp, K_sel = _case("tiny")
+    Q, K, V, blt = to_device(inp)
+    st = pisa.block_stats(K, V, blt)
+    idx, mask, wt = pisa.select_topk(Q, st, K_sel, blt)
+    bad = idx.clone()
+    bad[0, :, 0] = -7
+    bad[0, :, 1] = inp.nb + 3
+    O, _ = pisa.attention_fwd(Q, K, V, st, bad, mask, wt, K_sel, "drop", blt)
+    torch.cuda.synchronize()
+    keep = idx[0, :, 2:].cpu().numpy()
+    ref = orc.attention_head(inp.f64("Q", 0), inp.f64("K", 0), inp.f64("V", 0), 64, None, K_sel - 2,
+                             "drop", idx=keep)
+    assert rel_l2(O[0].cpu().numpy().astype(np.float64), ref["O"]) < 1e-4
+
+
+def test_abi_errors_launch_nothing(gpu_lib):
+    """Invalid arguments return an error status and leave outputs untouched."""
+    pisa = gpu_lib
+    inp, K_sel = _case("tiny")
+    Q, K, V, blt = to_device(inp)
+    st = pisa.block_stats(K, V, blt)
+    idx, mask, wt = pisa.select_topk(Q, st, K_sel, blt)
+    O = torch.full_like(Q, 7.0)
+    with pytest.raises(pisa.PisaError):
+        pisa.attention_fwd(Q, K, V, st, idx, mask, None, K_sel, "pwt", blt, out=O)   # PWT needs wt
+    with pytest.raises(pisa.PisaError):
+        pisa.attention_fwd(Q, K, V, st, idx, mask, wt, inp.nb + 1, "pwt", blt, out=O)
+    torch.cuda.synchronize()
+    assert bool((O == 7.0).all())

@@ -289,6 +289,9 @@ def test_block_statistics_definitions():
     # covariance against numpy's population covariance
     for j in range(nb):
         assert np.abs(np.cov(K[j * B:(j + 1) * B].T, bias=True) - st["C"][j]).max() < 1e-13
+        assert np.abs(np.var(K[j * B:(j + 1) * B], axis=0) - st["sig2"][j]).max() < 1e-13
+    lean = orc.block_stats(K, V, B, per_block=False)
+    assert lean["H"] is None and np.abs(lean["hbar"] - st["hbar"]).max() < 1e-13
 
 
 def test_theorem_error_bound():
