@@ -43,6 +43,27 @@ __device__ __forceinline__ int acc_key(int mt, int r, int g) {
   return 32 * mt + M::KI * (r / M::KH) + M::KH * g + (r % M::KH);
 }
 
+// Running-max update shared by every phase (log2 domain). The max only moves when a
+// logit exceeds it by more than kTau (lazy rescaling): exponentials stay <= 2^kTau and
+// the accumulators are rescaled on few tiles. All state is scaled by 2^-m.
+constexpr float kTau = 8.f;
+
+template <int NET>
+__device__ __forceinline__ void raise_max(float cand, float& m, float& lsum, float& asum, f32x16 (&acc)[NET]) {
+  const bool up = cand > m + kTau;
+  if (__any(up)) {
+    const float m_new = up ? cand : m;
+    const float alpha = fast_exp2(m - m_new);   // 1 where unchanged, 0 from -inf
+    m = m_new;
+    lsum *= alpha;
+    asum *= alpha;
+#pragma unroll
+    for (int et = 0; et < NET; ++et)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[et][r] *= alpha;
+  }
+}
+
 template <class T, int D, int MODE>
 __global__ __launch_bounds__(128) void attention_kernel(AttnArgs a) {
   using M = typename MmaFor<T>::type;
@@ -61,24 +82,26 @@ __global__ __launch_bounds__(128) void attention_kernel(AttnArgs a) {
   constexpr bool VIRT = (MODE == MODE_PISA || MODE == MODE_PWT);
   constexpr float NEG_INF = -__builtin_huge_valf();
 
-  __shared__ __align__(16) T sK[kB * LDK];
-  __shared__ __align__(16) T sV[D * LDV];
-  __shared__ float sBias[kB], sInvN[kB];
+  __shared__ __align__(16) T sK[2][kB * LDK];
+  __shared__ __align__(16) T sV[2][D * LDV];
+  __shared__ float sBias[2][kB], sInvN[2][kB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const uint32_t lin = xcd_remap(blockIdx.x, gridDim.x);
   const int h = int(lin / uint32_t(a.nb)), i = int(lin % uint32_t(a.nb));
+  const int nb = a.nb;
   int ni = a.block_len ? a.block_len[i] : kB;
   ni = min(max(ni, 1), kB);
 
   const T* Qh = static_cast<const T*>(a.Q) + size_t(h) * a.L * D;
   const T* Kh = static_cast<const T*>(a.K) + size_t(h) * a.L * D;
-  const T* vt = reinterpret_cast<const T*>(a.packed + a.pl.vt) + size_t(h) * a.nb * D * kB;
+  const T* vt = reinterpret_cast<const T*>(a.packed + a.pl.vt) + size_t(h) * nb * D * kB;
   const T* kbp = reinterpret_cast<const T*>(a.packed + a.pl.kbar) + size_t(h) * a.nbp * D;
   const T* vbp = reinterpret_cast<const T*>(a.packed + a.pl.vbar) + size_t(h) * a.nbp * D;
   const T* hbp = reinterpret_cast<const T*>(a.packed + a.pl.hbar) + size_t(h) * D * D;
-  const uint32_t* mrow = a.mask ? a.mask + (size_t(h) * a.nb + i) * a.nw : nullptr;
-  const int32_t* irow = a.idx + (size_t(h) * a.nb + i) * a.K_sel;
+  const uint32_t* mrow = a.mask ? a.mask + (size_t(h) * nb + i) * a.nw : nullptr;
+  const int32_t* irow = a.idx + (size_t(h) * nb + i) * a.K_sel;
+  const float* wrow = a.wt ? a.wt + (size_t(h) * nb + i) * nb : nullptr;
 
   // This lane's query row and its Q fragments (B operand of Sᵀ = K Qᵀ), kept in registers.
   const int qrow = 32 * wave + l32;
@@ -91,191 +114,226 @@ __global__ __launch_bounds__(128) void attention_kernel(AttnArgs a) {
   f32x16 acc[NET];
 #pragma unroll
   for (int et = 0; et < NET; ++et) acc[et] = zero16();
-  float m = NEG_INF, lsum = 0.f, asum = 0.f;   // running max (log2 units), partial sums
+  float m = NEG_INF, lsum = 0.f, asum = 0.f;
 
   const int n1 = a.K_sel;
-  const int n2 = VIRT ? a.nbp / kB : (MODE == MODE_LITERAL ? a.nb - a.K_sel : 0);
+  const int n2 = VIRT ? a.nbp / kB : (MODE == MODE_LITERAL ? nb - a.K_sel : 0);
   const int N = n1 + n2;
-
   int lit_cursor = 0;
-  auto source = [&](int n) -> int {
+
+  // Source of tile n: block index (exact / literal) or centroid-group index (virtual);
+  // -1 past the end. Called once per tile, in order.
+  auto next_source = [&](int n) -> int {
+    if (n >= N) return -1;
     if (n < n1) return irow[n];
     if (VIRT) return n - n1;
-    int j = lit_cursor;                       // next block whose mask bit is clear
-    while (j < a.nb && ((mrow[j >> 5] >> (j & 31)) & 1u)) ++j;
+    int j = lit_cursor;                        // next block whose mask bit is clear
+    while (j < nb && ((mrow[j >> 5] >> (j & 31)) & 1u)) ++j;
     lit_cursor = j + 1;
     return j;
   };
-  auto block_n = [&](int j) -> int {          // valid tokens of block j; 0 if j is out of range
-    if (j < 0 || j >= a.nb) return 0;
-    const int n = a.block_len ? a.block_len[j] : kB;
-    return min(max(n, 1), kB);
+  // Valid keys of tile n with source j: n_j for a block (0 if j is out of range), 64 for
+  // a centroid group (its padding is masked through the bias).
+  auto tile_keys = [&](int n, int j) -> int {
+    if (n >= N) return 0;
+    if (VIRT && n >= n1) return kB;
+    if (j < 0 || j >= nb) return 0;
+    const int v = a.block_len ? a.block_len[j] : kB;
+    return min(max(v, 1), kB);
   };
 
-  uint4 rk[PF], rv[PF];
-  auto prefetch = [&](int n, int src) {
-    const T* pk;
-    const T* pv;
-    if (VIRT && n >= n1) {
-      pk = kbp + size_t(src) * kB * D;
-      pv = vbp + size_t(src) * D * kB;
-    } else {
-      const int j = (src >= 0 && src < a.nb) ? src : 0;
-      pk = Kh + size_t(j) * kB * D;
-      pv = vt + size_t(j) * D * kB;
-    }
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int c = tid + 128 * p;
-      rk[p] = *reinterpret_cast<const uint4*>(pk + (c / CPRK) * D + (c % CPRK) * EPC);
-      rv[p] = *reinterpret_cast<const uint4*>(pv + (c / CPRV) * kB + (c % CPRV) * EPC);
+  u32x4 rk[PF], rv[PF];
+#define PISA_LOAD_TILE(n_, j_)                                                        \
+  do {                                                                               \
+    const T* pk_;                                                                    \
+    const T* pv_;                                                                    \
+    if (VIRT && (n_) >= n1) {                                                        \
+      pk_ = kbp + size_t(j_) * kB * D;                                               \
+      pv_ = vbp + size_t(j_) * D * kB;                                               \
+    } else {                                                                         \
+      const int jj_ = ((j_) >= 0 && (j_) < nb) ? (j_) : 0;                           \
+      pk_ = Kh + size_t(jj_) * kB * D;                                               \
+      pv_ = vt + size_t(jj_) * D * kB;                                               \
+    }                                                                                \
+    static_for<0, PF>([&](auto pc) {                                                 \
+      constexpr int p = decltype(pc)::value;                                         \
+      const int c = tid + 128 * p;                                                   \
+      rk[p] = *reinterpret_cast<const u32x4*>(pk_ + (c / CPRK) * D + (c % CPRK) * EPC); \
+      rv[p] = *reinterpret_cast<const u32x4*>(pv_ + (c / CPRV) * kB + (c % CPRV) * EPC); \
+    });                                                                              \
+  } while (0)
+#define PISA_STORE_TILE(buf_)                                                         \
+  do {                                                                               \
+    static_for<0, PF>([&](auto pc) {                                                 \
+      constexpr int p = decltype(pc)::value;                                         \
+      const int c = tid + 128 * p;                                                   \
+      *reinterpret_cast<u32x4*>(&sK[buf_][(c / CPRK) * LDK + (c % CPRK) * EPC]) = rk[p]; \
+      *reinterpret_cast<u32x4*>(&sV[buf_][(c / CPRV) * LDV + (c % CPRV) * EPC]) = rv[p]; \
+    });                                                                              \
+  } while (0)
+
+  // Raw inputs of one centroid group's bias (threads < 64, centroid 64*grp + tid),
+  // loaded one tile ahead; the bias itself is formed when the group is staged.
+  uint32_t bw_mask = 0u;
+  int bw_len = kB;
+  float bw_w = 0.f;
+  auto load_bias_raw = [&](int grp) {
+    if (tid < kB) {
+      const int jj = min(grp * kB + tid, nb - 1);
+      bw_mask = mrow[jj >> 5];
+      bw_len = a.block_len ? a.block_len[jj] : kB;
+      if (MODE == MODE_PWT) bw_w = wrow[jj];
     }
   };
-
-  int src = 0;
-  if (N > 0) {
-    src = source(0);
-    prefetch(0, src);
-  }
-  for (int n = 0; n < N; ++n) {
-    const int cur = src;
-    const bool second = n >= n1;
-    __syncthreads();                          // previous tile fully consumed
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int c = tid + 128 * p;
-      *reinterpret_cast<uint4*>(sK + (c / CPRK) * LDK + (c % CPRK) * EPC) = rk[p];
-      *reinterpret_cast<uint4*>(sV + (c / CPRV) * LDV + (c % CPRV) * EPC) = rv[p];
-    }
-    if (VIRT && second && tid < kB) {
-      // log2-domain bias ln n_j + φ_{i,j} of the 64 centroids of this group;
-      // -inf for selected blocks and for the padding beyond nb.
-      const int jj = cur * kB + tid;
+  // log2-domain bias ln n_j + φ_{i,j}; -inf for selected blocks and the padding beyond nb.
+  auto store_bias = [&](int buf, int grp) {
+    if (tid < kB) {
+      const int jj = grp * kB + tid;
       float b = NEG_INF, invn = 0.f;
-      if (jj < a.nb && !((mrow[jj >> 5] >> (jj & 31)) & 1u)) {
-        const int nj = block_n(jj);
+      if (jj < nb && !((bw_mask >> (jj & 31)) & 1u)) {
+        const int nj = min(max(bw_len, 1), kB);
         const float lnn = logf(float(nj));
         float phi = 0.f;
         if (MODE == MODE_PWT) {
-          float w = a.wt[(size_t(h) * a.nb + i) * a.nb + jj];
+          float w = bw_w;
           if (a.gate && w > lnn) w = 0.f;
           phi = a.w_linear ? log1pf(w) : w;
         }
         b = (lnn + phi) * kLog2e;
         invn = 1.f / float(nj);
       }
-      sBias[tid] = b;
-      sInvN[tid] = invn;
+      sBias[buf][tid] = b;
+      sInvN[buf][tid] = invn;
     }
-    __syncthreads();
-    if (n + 1 < N) {
-      src = source(n + 1);
-      prefetch(n + 1, src);
+  };
+
+  // Descriptor pipeline: sources of tiles n, n+1, n+2 and key counts of n, n+1 are in
+  // registers at the top of iteration n, so no per-tile metadata load is on the
+  // critical path.
+  int j_c = next_source(0), j_n = next_source(1), j_n2 = next_source(2);
+  int k_c = tile_keys(0, j_c), k_n = tile_keys(1, j_n);
+  if (N > 0) {
+    PISA_LOAD_TILE(0, j_c);
+    PISA_STORE_TILE(0);
+    if (VIRT && n1 == 0) {
+      load_bias_raw(j_c);
+      store_bias(0, j_c);
+    }
+    if (N > 1) {
+      PISA_LOAD_TILE(1, j_n);
+      if (VIRT && 1 >= n1) load_bias_raw(j_n);
+    }
+  }
+  __syncthreads();
+
+  for (int n = 0; n < N; ++n) {
+    const int buf = n & 1;
+    const bool second = n >= n1;
+    const T* sKb = sK[buf];
+    const T* sVb = sV[buf];
+    const int nj = k_c;
+
+    // Sᵀ[key][q] for the two 32-key halves of the tile (independent MFMA chains).
+    f32x16 s0 = zero16(), s1 = zero16();
+    {
+      const T* kr0 = sKb + feed_row<M>(l32) * LDK + KH * g;
+      const T* kr1 = kr0 + 32 * LDK;
+#pragma unroll
+      for (int ks = 0; ks < NKD; ++ks) {
+        s0 = M::mma(M::load(kr0 + KI * ks), qf[ks], s0);
+        s1 = M::mma(M::load(kr1 + KI * ks), qf[ks], s1);
+      }
     }
 
-    // Sᵀ[key][q] for the two 32-key halves of the tile.
-    f32x16 s[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      s[mt] = zero16();
-      const T* krow = sK + (32 * mt + feed_row<M>(l32)) * LDK + KH * g;
-#pragma unroll
-      for (int ks = 0; ks < NKD; ++ks) s[mt] = M::mma(M::load(krow + KI * ks), qf[ks], s[mt]);
-    }
-
-    float pr[2][16];
-    float mx = NEG_INF;
     if (!second || VIRT) {
-      const int nj = second ? kB : block_n(cur);
+      float mx = NEG_INF;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = acc_key<M>(mt, r, g);
-          float t;
-          if (second) t = s[mt][r] * kLog2e + sBias[key];
-          else t = key < nj ? s[mt][r] * kLog2e : NEG_INF;
-          pr[mt][r] = t;
-          mx = fmaxf(mx, t);
+      for (int r = 0; r < 16; ++r) {
+        const int k0 = acc_key<M>(0, r, g), k1 = acc_key<M>(1, r, g);
+        if (second) {
+          s0[r] = s0[r] * kLog2e + sBias[buf][k0];
+          s1[r] = s1[r] * kLog2e + sBias[buf][k1];
+        } else {
+          s0[r] = k0 < nj ? s0[r] * kLog2e : NEG_INF;
+          s1[r] = k1 < nj ? s1[r] * kLog2e : NEG_INF;
         }
+        mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+      }
       mx = max_halves(mx);
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == NEG_INF ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      m = m_new;
+      raise_max<NET>(mx, m, lsum, asum, acc);
+      const float mu = m == NEG_INF ? 0.f : m;
       float ps = 0.f, pa = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(pr[mt][r] - m_use);
-          pr[mt][r] = p;
-          ps += p;
-          if (VIRT && second) pa += p * sInvN[acc_key<M>(mt, r, g)];
-        }
-      lsum = lsum * alpha + ps;
-      if (VIRT) asum = asum * alpha + pa;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int et = 0; et < NET; ++et)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[et][r] *= alpha;
+      for (int r = 0; r < 16; ++r) {
+        s0[r] = fast_exp2(s0[r] - mu);
+        s1[r] = fast_exp2(s1[r] - mu);
+        ps += s0[r] + s1[r];
+        if (VIRT && second)
+          pa += s0[r] * sInvN[buf][acc_key<M>(0, r, g)] + s1[r] * sInvN[buf][acc_key<M>(1, r, g)];
       }
+      lsum += ps;
+      if (VIRT) asum += pa;
     } else {
       // LITERAL: block-wise first-order weights with the per-row second-order factor.
-      const int nj = block_n(cur);
       const float invn = nj > 0 ? 1.f / float(nj) : 0.f;
       float ssum = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (acc_key<M>(mt, r, g) < nj) ssum += s[mt][r];
-      ssum = sum_halves(ssum);
-      const float mean = ssum * invn;
+      for (int r = 0; r < 16; ++r) {
+        if (acc_key<M>(0, r, g) < nj) ssum += s0[r];
+        if (acc_key<M>(1, r, g) < nj) ssum += s1[r];
+      }
+      const float mean = sum_halves(ssum) * invn;
       float y2 = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (acc_key<M>(mt, r, g) < nj) {
-            const float y = s[mt][r] - mean;
-            y2 += y * y;
-          }
-      y2 = sum_halves(y2);
-      float w = 0.5f * y2 * invn;
+      for (int r = 0; r < 16; ++r) {
+        const float y0 = s0[r] - mean, y1 = s1[r] - mean;
+        if (acc_key<M>(0, r, g) < nj) y2 += y0 * y0;
+        if (acc_key<M>(1, r, g) < nj) y2 += y1 * y1;
+      }
+      float w = 0.5f * sum_halves(y2) * invn;
       const float lnn = nj > 0 ? logf(float(nj)) : 0.f;
       if (a.gate && w > lnn) w = 0.f;
       const float phi = a.w_linear ? log1pf(w) : w;
-      const float ell = nj > 0 ? (mean + phi + lnn) * kLog2e : NEG_INF;
-      const float m_new = fmaxf(m, ell);
-      const float m_use = m_new == NEG_INF ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      m = m_new;
-      const float cw = nj > 0 ? fast_exp2((mean + phi) * kLog2e - m_use) : 0.f;
+      raise_max<NET>(nj > 0 ? (mean + phi + lnn) * kLog2e : NEG_INF, m, lsum, asum, acc);
+      const float mu = m == NEG_INF ? 0.f : m;
+      const float cw = nj > 0 ? fast_exp2((mean + phi) * kLog2e - mu) : 0.f;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          pr[mt][r] = acc_key<M>(mt, r, g) < nj ? cw * (1.f + (s[mt][r] - mean)) : 0.f;
-      lsum = lsum * alpha + (g == 0 ? float(nj) * cw : 0.f);
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int et = 0; et < NET; ++et)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[et][r] *= alpha;
+      for (int r = 0; r < 16; ++r) {
+        s0[r] = acc_key<M>(0, r, g) < nj ? cw * (1.f + (s0[r] - mean)) : 0.f;
+        s1[r] = acc_key<M>(1, r, g) < nj ? cw * (1.f + (s1[r] - mean)) : 0.f;
       }
+      lsum += g == 0 ? float(nj) * cw : 0.f;
     }
 
     // Oᵀ += Vᵀ Pᵀ : the B operand of k-step ks is registers [(ks % KPM) * KH, +KH) of m-tile ks / KPM.
-#pragma unroll
-    for (int ks = 0; ks < NKB; ++ks) {
-      const AB b = M::pack(&pr[ks / KPM][(ks % KPM) * KH]);
+    static_for<0, NKB>([&](auto ksc) {
+      constexpr int ks = decltype(ksc)::value;
+      const AB b = (ks / KPM == 0) ? M::template packv<(ks % KPM) * KH>(s0)
+                                   : M::template packv<(ks % KPM) * KH>(s1);
 #pragma unroll
       for (int et = 0; et < NET; ++et)
-        acc[et] = M::mma(M::load(sV + (32 * et + l32) * LDV + KI * ks + KH * g), b, acc[et]);
+        acc[et] = M::mma(M::load(sVb + (32 * et + l32) * LDV + KI * ks + KH * g), b, acc[et]);
+    });
+
+    // Stage tile n + 1 into the other buffer, start loading tile n + 2, advance the
+    // descriptor pipeline.
+    if (n + 1 < N) {
+      PISA_STORE_TILE(buf ^ 1);
+      if (VIRT && n + 1 >= n1) store_bias(buf ^ 1, j_n);
+      if (n + 2 < N) {
+        PISA_LOAD_TILE(n + 2, j_n2);
+        if (VIRT && n + 2 >= n1) load_bias_raw(j_n2);
+      }
     }
+    j_c = j_n;
+    k_c = k_n;
+    j_n = j_n2;
+    k_n = tile_keys(n + 2, j_n2);
+    j_n2 = next_source(n + 3);
+    __syncthreads();
   }
+#undef PISA_LOAD_TILE
+#undef PISA_STORE_TILE
 
   if (VIRT) {
     // Phase 3: Oᵀ += H̄ (A_t q_t)ᵀ with H̄[e][c] as the A operand.
@@ -295,12 +353,12 @@ __global__ __launch_bounds__(128) void attention_kernel(AttnArgs a) {
 
   const float lt = sum_halves(lsum);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  __syncthreads();
+  T* sO = sK[0];
 #pragma unroll
   for (int et = 0; et < NET; ++et)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      sK[qrow * LDK + 32 * et + acc_row(r, g)] = from_f32<T>(qvalid ? acc[et][r] * inv : 0.f);
+      sO[qrow * LDK + 32 * et + acc_row(r, g)] = from_f32<T>(qvalid ? acc[et][r] * inv : 0.f);
   if (a.lse && g == 0)
     a.lse[size_t(h) * a.L + size_t(i) * kB + qrow] = (qvalid && lt > 0.f) ? m * kLn2 + logf(lt) : NEG_INF;
   __syncthreads();
@@ -308,8 +366,8 @@ __global__ __launch_bounds__(128) void attention_kernel(AttnArgs a) {
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
     const int c = tid + 128 * p;
-    *reinterpret_cast<uint4*>(Oh + (c / CPRK) * D + (c % CPRK) * EPC) =
-        *reinterpret_cast<const uint4*>(sK + (c / CPRK) * LDK + (c % CPRK) * EPC);
+    *reinterpret_cast<u32x4*>(Oh + (c / CPRK) * D + (c % CPRK) * EPC) =
+        *reinterpret_cast<const u32x4*>(sO + (c / CPRK) * LDK + (c % CPRK) * EPC);
   }
 }
 

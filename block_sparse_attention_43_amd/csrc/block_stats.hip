@@ -56,13 +56,13 @@ __global__ __launch_bounds__(256) void block_stats_kernel(StatsArgs a, unsigned 
     // Stage K_j and V_j (rows >= n_j zeroed) in LDS.
     for (int c = tid; c < kB * CPR; c += 256) {
       const int row = c / CPR, col = (c % CPR) * EPC;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
       if (row < n) {
-        kv = *reinterpret_cast<const uint4*>(Kh + size_t(j * kB + row) * D + col);
-        vv = *reinterpret_cast<const uint4*>(Vh + size_t(j * kB + row) * D + col);
+        kv = *reinterpret_cast<const u32x4*>(Kh + size_t(j * kB + row) * D + col);
+        vv = *reinterpret_cast<const u32x4*>(Vh + size_t(j * kB + row) * D + col);
       }
-      *reinterpret_cast<uint4*>(sK + row * LDR + col) = kv;
-      *reinterpret_cast<uint4*>(sV + row * LDR + col) = vv;
+      *reinterpret_cast<u32x4*>(sK + row * LDR + col) = kv;
+      *reinterpret_cast<u32x4*>(sV + row * LDR + col) = vv;
     }
     __syncthreads();
 
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void block_stats_kernel(StatsArgs a, unsigned 
       __align__(16) T tmp[EPC];
 #pragma unroll
       for (int u = 0; u < EPC; ++u) tmp[u] = sV[(i0 + u) * LDR + e];
-      *reinterpret_cast<uint4*>(vt + (size_t(j) * D + e) * kB + i0) = *reinterpret_cast<uint4*>(tmp);
+      *reinterpret_cast<u32x4*>(vt + (size_t(j) * D + e) * kB + i0) = *reinterpret_cast<u32x4*>(tmp);
     }
     __syncthreads();   // sKbar / sVsum visible
 

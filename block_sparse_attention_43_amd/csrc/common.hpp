@@ -4,10 +4,22 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace pisa {
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [I0, N).
+template <int I0, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I0 < N) {
+    f(std::integral_constant<int, I0>{});
+    static_for<I0 + 1, N>(f);
+  }
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // one 16-byte chunk
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -62,6 +74,14 @@ struct MmaBF16 {
   __device__ __forceinline__ static f32x16 mma(AB a, AB b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
+  // Operand from 8 consecutive accumulator registers [OFF, OFF + 8).
+  template <int OFF>
+  __device__ __forceinline__ static AB packv(const f32x16& v) {
+    AB r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = static_cast<__bf16>(v[OFF + i]);
+    return r;
+  }
 };
 
 struct MmaF32 {
@@ -76,6 +96,8 @@ struct MmaF32 {
   __device__ __forceinline__ static f32x16 mma(AB a, AB b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
+  template <int OFF>
+  __device__ __forceinline__ static AB packv(const f32x16& v) { return v[OFF]; }
 };
 
 template <class T> struct MmaFor;
