@@ -177,13 +177,11 @@ __global__ __launch_bounds__(128) void attention_kernel(AttnArgs a) {
   uint32_t bw_mask = 0u;
   int bw_len = kB;
   float bw_w = 0.f;
-  auto load_bias_raw = [&](int grp) {
-    if (tid < kB) {
-      const int jj = min(grp * kB + tid, nb - 1);
-      bw_mask = mrow[jj >> 5];
-      bw_len = a.block_len ? a.block_len[jj] : kB;
-      if (MODE == MODE_PWT) bw_w = wrow[jj];
-    }
+  auto load_bias_raw = [&](int grp) {          // every lane loads (no branch); lanes < 64 use it
+    const int jj = min(grp * kB + (tid & 63), nb - 1);
+    bw_mask = mrow[jj >> 5];
+    bw_len = a.block_len ? a.block_len[jj] : kB;
+    if (MODE == MODE_PWT) bw_w = wrow[jj];
   };
   // log2-domain bias ln n_j + φ_{i,j}; -inf for selected blocks and the padding beyond nb.
   auto store_bias = [&](int buf, int grp) {
@@ -371,14 +369,367 @@ __global__ __launch_bounds__(128) void attention_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split-key kernel for DROP / PISA / PWT (the timed path).
+//
+// One 64-row query tile per workgroup of four waves. Wave w owns query rows
+// 32*(w & 1) + [0, 32) and the key half 32*(w >> 1) + [0, 32) of every tile it visits,
+// with its own running max / sums; the two key halves of each query half are merged
+// at the end (flash-decoding style). This keeps 16 score registers and 64 output
+// accumulators per lane, so two workgroups (eight waves) fit on a CU and the softmax of
+// one wave overlaps the MFMA work of another. Tiles arrive by direct global->LDS loads
+// into two stages of swizzled LDS; one barrier per tile.
+// ---------------------------------------------------------------------------
+template <class T, int D, int MODE>
+__global__ __launch_bounds__(256, 2) void attention_split_kernel(AttnArgs a) {
+  using M = typename MmaFor<T>::type;
+  using AB = typename M::AB;
+  constexpr int KI = M::KI, KH = M::KH;
+  constexpr int ES = sizeof(T);
+  constexpr int KROW = D * ES;                 // bytes per key row
+  constexpr int VROW = kB * ES;                // bytes per Vᵀ row (64 keys)
+  constexpr int TB = kB * KROW;                // bytes per operand tile
+  constexpr int NDMA = TB / 1024;              // 1 KB loads per operand tile
+  constexpr int DPW = NDMA / 4;                // ... per wave
+  constexpr int NKD = D / KI;                  // k-steps over the head dimension
+  constexpr int NKH = 32 / KI;                 // k-steps over a 32-key half
+  constexpr int NET = D / 32;                  // 32-row tiles of Oᵀ
+  constexpr bool VIRT = (MODE == MODE_PISA || MODE == MODE_PWT);
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  using KT = SwizzledTile<KROW>;
+  using VT = SwizzledTile<VROW>;
+  static_assert(NDMA % 4 == 0 && 1024 % KROW == 0 && 1024 % VROW == 0, "tile shape");
+
+  constexpr int DCH = 512;                       // descriptor chunk (exact tiles)
+  // Separate objects per stage and operand, so the compiler can see that reading one
+  // stage does not depend on the direct loads still landing in the other.
+  __shared__ __align__(1024) char sK0[TB], sV0[TB], sK1[TB], sV1[TB];
+  __shared__ float sBias[2][kB], sInvN[2][kB];
+  __shared__ uint32_t sDesc[2][DCH];             // exact tile -> block | keys << 16
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int qh = wave & 1, kh = wave >> 1;
+  const uint32_t lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = int(lin / uint32_t(a.nb)), i = int(lin % uint32_t(a.nb));
+  const int nb = a.nb;
+  int ni = a.block_len ? a.block_len[i] : kB;
+  ni = min(max(ni, 1), kB);
+
+  const T* Qh = static_cast<const T*>(a.Q) + size_t(h) * a.L * D;
+  const char* Kh = reinterpret_cast<const char*>(static_cast<const T*>(a.K) + size_t(h) * a.L * D);
+  const char* vt = a.packed + a.pl.vt + size_t(h) * nb * TB;
+  const char* kbp = a.packed + a.pl.kbar + size_t(h) * a.nbp * KROW;
+  const char* vbp = a.packed + a.pl.vbar + size_t(h) * a.nbp * KROW;
+  const T* hbp = reinterpret_cast<const T*>(a.packed + a.pl.hbar) + size_t(h) * D * D;
+  const uint32_t* mrow = a.mask ? a.mask + (size_t(h) * nb + i) * a.nw : nullptr;
+  const int32_t* irow = a.idx + (size_t(h) * nb + i) * a.K_sel;
+  const float* wrow = a.wt ? a.wt + (size_t(h) * nb + i) * nb : nullptr;
+
+  const int qrow = 32 * qh + l32;
+  const bool qvalid = qrow < ni;
+  AB qf[NKD];
+#pragma unroll
+  for (int ks = 0; ks < NKD; ++ks)
+    qf[ks] = qvalid ? M::load(Qh + (size_t(i) * kB + qrow) * D + KI * ks + KH * g) : M::zero();
+
+  f32x16 acc[NET];
+#pragma unroll
+  for (int et = 0; et < NET; ++et) acc[et] = zero16();
+  float m = NEG_INF, lsum = 0.f, asum = 0.f;
+
+  const int n1 = a.K_sel;
+  const int N = n1 + (VIRT ? a.nbp / kB : 0);
+
+  // Descriptor of exact tile n: its block (out-of-range indices become block 0 with no
+  // valid keys) and the block's valid key count, staged in LDS in chunks of DCH tiles.
+  auto fill_desc = [&](int chunk) {
+    for (int e = tid; e < DCH; e += 256) {
+      const int n = chunk * DCH + e;
+      uint32_t d = 0u;
+      if (n < n1) {
+        const int j = irow[n];
+        if (j >= 0 && j < nb) {
+          const int v = a.block_len ? a.block_len[j] : kB;
+          d = uint32_t(j) | (uint32_t(min(max(v, 1), kB)) << 16);
+        }
+      }
+      sDesc[chunk & 1][e] = d;
+    }
+  };
+  // (source, keys) of tile n: block and n_j for exact tiles, group and 64 for virtual ones.
+  auto desc = [&](int n, int& j, int& k) {
+    if (n < n1) {
+      const uint32_t d = sDesc[(n / DCH) & 1][n % DCH];
+      j = int(d & 0xFFFFu);
+      k = int(d >> 16);
+    } else {
+      j = n - n1;
+      k = kB;
+    }
+  };
+  // Direct loads of tile n (source j) into stage ST; this wave's share of both operands.
+  auto issue_tile = [&](int n, int j, auto stc) {
+    constexpr int ST = decltype(stc)::value;
+    char* dk = ST ? sK1 : sK0;
+    char* dv = ST ? sV1 : sV0;
+    const char* gk;
+    const char* gv;
+    if (VIRT && n >= n1) {
+      gk = kbp + size_t(j) * TB;
+      gv = vbp + size_t(j) * TB;
+    } else {
+      const int jj = (j >= 0 && j < nb) ? j : 0;
+      gk = Kh + size_t(jj) * TB;
+      gv = vt + size_t(jj) * TB;
+    }
+#pragma unroll
+    for (int u = 0; u < DPW; ++u) {
+      const int ins = wave * DPW + u;
+      const int b = ins * 1024 + lane * 16;    // byte of the LDS tile this lane fills
+      {
+        const int r = b / KROW, pos = (b % KROW) >> 4;
+        const int c = pos ^ KT::swz(r);
+        dma16(gk + r * KROW + c * 16, dk + ins * 1024);
+      }
+      {
+        const int r = b / VROW, pos = (b % VROW) >> 4;
+        const int c = pos ^ VT::swz(r);
+        dma16(gv + r * VROW + c * 16, dv + ins * 1024);
+      }
+    }
+  };
+
+  // Raw inputs of a centroid group's bias (threads < 64), loaded one tile ahead.
+  uint32_t bw_mask = 0u;
+  int bw_len = kB;
+  float bw_w = 0.f;
+  auto load_bias_raw = [&](int grp) {          // every lane loads (no branch); lanes < 64 use it
+    const int jj = min(grp * kB + (tid & 63), nb - 1);
+    bw_mask = mrow[jj >> 5];
+    bw_len = a.block_len ? a.block_len[jj] : kB;
+    if (MODE == MODE_PWT) bw_w = wrow[jj];
+  };
+  auto store_bias = [&](int st, int grp) {     // log2-domain ln n_j + φ_{i,j}; -inf if excluded
+    if (tid < kB) {
+      const int jj = grp * kB + tid;
+      float b = NEG_INF, invn = 0.f;
+      if (jj < nb && !((bw_mask >> (jj & 31)) & 1u)) {
+        const int nj = min(max(bw_len, 1), kB);
+        const float lnn = logf(float(nj));
+        float phi = 0.f;
+        if (MODE == MODE_PWT) {
+          float w = bw_w;
+          if (a.gate && w > lnn) w = 0.f;
+          phi = a.w_linear ? log1pf(w) : w;
+        }
+        b = (lnn + phi) * kLog2e;
+        invn = 1.f / float(nj);
+      }
+      sBias[st][tid] = b;
+      sInvN[st][tid] = invn;
+    }
+  };
+
+  // One tile: Sᵀ for this wave's 32 keys, online softmax, Oᵀ += Vᵀ Pᵀ.
+  auto compute = [&](auto stc, bool second, int nj) {
+    constexpr int st = decltype(stc)::value;
+    const char* sk = st ? sK1 : sK0;
+    const char* sv = st ? sV1 : sV0;
+    f32x16 s = zero16();
+    {
+      const int R = 32 * kh + feed_row<M>(l32);
+      AB kf[NKD];
+#pragma unroll
+      for (int ks = 0; ks < NKD; ++ks)
+        kf[ks] = M::load(reinterpret_cast<const T*>(sk + KT::offset(R, (KI * ks + KH * g) * ES)));
+#pragma unroll
+      for (int ks = 0; ks < NKD; ++ks) s = M::mma(kf[ks], qf[ks], s);
+    }
+    // Logits in log2 units: t = s * log2(e) + bias. The max is taken on the same values
+    // the exponentials use, so every p <= 2^kTau.
+    float mx = NEG_INF;
+    if (VIRT && second) {
+      // per-key bias / (1 / n_j): keys 32*kh + acc_key(0, r, g) are runs of KH consecutive keys
+#pragma unroll
+      for (int r = 0; r < 16; r += KH) {
+        const int key = 32 * kh + acc_key<M>(0, r, g);
+#pragma unroll
+        for (int u = 0; u < KH; ++u) s[r + u] = fmaf(s[r + u], kLog2e, sBias[st][key + u]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    } else if (nj >= kB) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx *= kLog2e;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (32 * kh + acc_key<M>(0, r, g) >= nj) s[r] = NEG_INF;
+        mx = fmaxf(mx, s[r]);
+      }
+      mx *= kLog2e;
+    }
+    mx = max_halves(mx);
+    raise_max<NET>(mx, m, lsum, asum, acc);
+    const float mu = m == NEG_INF ? 0.f : m;
+    float ps = 0.f, pa = 0.f;
+    if (VIRT && second) {
+#pragma unroll
+      for (int r = 0; r < 16; r += KH) {
+        const int key = 32 * kh + acc_key<M>(0, r, g);
+#pragma unroll
+        for (int u = 0; u < KH; ++u) {
+          const float p = fast_exp2(s[r + u] - mu);
+          s[r + u] = p;
+          ps += p;
+          pa = fmaf(p, sInvN[st][key + u], pa);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(s[r], kLog2e, -mu));
+        s[r] = p;
+        ps += p;
+      }
+    }
+    lsum += ps;
+    if (VIRT) asum += pa;
+    static_for<0, NKH>([&](auto ksc) {
+      constexpr int ks = decltype(ksc)::value;
+      const AB b = M::template packv<ks * KH>(s);
+      const int kb = (32 * kh + KI * ks + KH * g) * ES;     // byte of this lane's keys in a Vᵀ row
+#pragma unroll
+      for (int et = 0; et < NET; ++et)
+        acc[et] = M::mma(M::load(reinterpret_cast<const T*>(sv + VT::offset(32 * et + l32, kb))), b, acc[et]);
+    });
+  };
+
+  if (n1 > 0) fill_desc(0);
+  if (n1 > DCH) fill_desc(1);
+  __syncthreads();
+  if (N > 0) {
+    int j0, k0;
+    desc(0, j0, k0);
+    issue_tile(0, j0, std::integral_constant<int, 0>{});
+    if (VIRT && n1 == 0) {
+      load_bias_raw(j0);
+      store_bias(0, j0);
+    }
+    if (VIRT && N > 1 && 1 >= n1) load_bias_raw(1 - n1);
+  }
+  // Two stages: even tiles use stage 0, odd tiles stage 1 (unrolled so each LDS read
+  // names one stage).
+  for (int n = 0; n < N; n += 2) {
+    static_for<0, 2>([&](auto hc) {
+      constexpr int half = decltype(hc)::value;
+      const int t = n + half;
+      if (t < N) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): this wave's loads of tile t landed
+        __syncthreads();                         // ... everyone's; stage half ^ 1 is free
+        // Refill the descriptor chunk that the tiles just finished used (before any
+        // direct load is in flight, so its own waits cost nothing extra).
+        if (t % DCH == 0 && t >= DCH && t + DCH < n1) fill_desc(t / DCH + 1);
+        if (t + 1 < N) {
+          int j1, k1;
+          desc(t + 1, j1, k1);
+          issue_tile(t + 1, j1, std::integral_constant<int, half ^ 1>{});
+          if (VIRT && t + 1 >= n1) store_bias(half ^ 1, j1);
+          if (VIRT && t + 2 < N && t + 2 >= n1) load_bias_raw(t + 2 - n1);
+        }
+        int jc, kc;
+        desc(t, jc, kc);
+        compute(hc, t >= n1, kc);
+      }
+    });
+  }
+
+  // Merge the two key halves of each query half. Wave (qh, kh) finishes Oᵀ tiles
+  // [kh * NET/2, (kh + 1) * NET/2) and hands the other half of its accumulators over.
+  constexpr int HE = NET / 2;
+  constexpr int XS = HE * 16 + 3;              // floats per lane handed over
+  __syncthreads();
+  static_assert(XS * 64 * 4 <= TB, "hand-over buffer must fit one stage array");
+  auto xbuf = [&](int q, int k) -> float* {      // one array per wave
+    char* b = q ? (k ? sV1 : sK1) : (k ? sV0 : sK0);
+    return reinterpret_cast<float*>(b);
+  };
+  {
+    float* mine = xbuf(qh, kh) + lane;
+#pragma unroll
+    for (int u = 0; u < HE; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mine[(u * 16 + r) * 64] = kh ? acc[u][r] : acc[HE + u][r];
+    mine[(HE * 16 + 0) * 64] = m;
+    mine[(HE * 16 + 1) * 64] = lsum;
+    mine[(HE * 16 + 2) * 64] = asum;
+  }
+  __syncthreads();
+  f32x16 res[HE];
+  float mt, lt_part, at_part;
+  {
+    const float* other = xbuf(qh, 1 - kh) + lane;
+    const float mo = other[(HE * 16 + 0) * 64];
+    mt = fmaxf(m, mo);
+    const float mu = mt == NEG_INF ? 0.f : mt;
+    const float f = fast_exp2(m - mu), fo = fast_exp2(mo - mu);
+#pragma unroll
+    for (int u = 0; u < HE; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) res[u][r] = (kh ? acc[HE + u][r] : acc[u][r]) * f + other[(u * 16 + r) * 64] * fo;
+    lt_part = lsum * f + other[(HE * 16 + 1) * 64] * fo;
+    at_part = asum * f + other[(HE * 16 + 2) * 64] * fo;
+  }
+  if (VIRT) {
+    // Phase 3: Oᵀ += H̄ (A_t q_t)ᵀ for this wave's Oᵀ tiles, H̄[e][c] as the A operand.
+    const float at = sum_halves(at_part);
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks) {
+      float qv[KH];
+      M::unpack(qf[ks], qv);
+#pragma unroll
+      for (int u = 0; u < KH; ++u) qv[u] *= at;
+      const AB b = M::pack(qv);
+#pragma unroll
+      for (int u = 0; u < HE; ++u)
+        res[u] = M::mma(M::load(hbp + size_t(32 * (kh * HE + u) + l32) * D + KI * ks + KH * g), b, res[u]);
+    }
+  }
+  const float lt = sum_halves(lt_part);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (a.lse && kh == 0 && g == 0)
+    a.lse[size_t(h) * a.L + size_t(i) * kB + qrow] = (qvalid && lt > 0.f) ? mt * kLn2 + logf(lt) : NEG_INF;
+  __syncthreads();                               // hand-over buffer consumed
+  // Output tile staged in LDS (swizzled like a key tile) for coalesced 16-byte stores.
+  char* sO = sK1;
+#pragma unroll
+  for (int u = 0; u < HE; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int e = 32 * (kh * HE + u) + acc_row(r, g);
+      *reinterpret_cast<T*>(sO + KT::offset(qrow, e * ES)) = from_f32<T>(qvalid ? res[u][r] * inv : 0.f);
+    }
+  __syncthreads();
+  char* Oh = reinterpret_cast<char*>(static_cast<T*>(a.O) + (size_t(h) * a.L + size_t(i) * kB) * D);
+  constexpr int OCH = kB * KROW / 16;            // 16-byte chunks of the output tile
+#pragma unroll
+  for (int p = 0; p < OCH / 256; ++p) {
+    const int c = tid + 256 * p;
+    const int row = c / (KROW / 16), cb = (c % (KROW / 16)) * 16;
+    *reinterpret_cast<u32x4*>(Oh + size_t(row) * KROW + cb) =
+        *reinterpret_cast<const u32x4*>(sO + KT::offset(row, cb));
+  }
+}
+
 template <class T, int D>
 static hipError_t launch_attn_t(int mode, const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(unsigned(a.H) * unsigned(a.nb)), block(128);
+  const dim3 grid(unsigned(a.H) * unsigned(a.nb));
   switch (mode) {
-    case MODE_DROP: hipLaunchKernelGGL((attention_kernel<T, D, MODE_DROP>), grid, block, 0, s, a); break;
-    case MODE_PISA: hipLaunchKernelGGL((attention_kernel<T, D, MODE_PISA>), grid, block, 0, s, a); break;
-    case MODE_PWT: hipLaunchKernelGGL((attention_kernel<T, D, MODE_PWT>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((attention_kernel<T, D, MODE_LITERAL>), grid, block, 0, s, a); break;
+    case MODE_DROP: hipLaunchKernelGGL((attention_split_kernel<T, D, MODE_DROP>), grid, dim3(256), 0, s, a); break;
+    case MODE_PISA: hipLaunchKernelGGL((attention_split_kernel<T, D, MODE_PISA>), grid, dim3(256), 0, s, a); break;
+    case MODE_PWT: hipLaunchKernelGGL((attention_split_kernel<T, D, MODE_PWT>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((attention_kernel<T, D, MODE_LITERAL>), grid, dim3(128), 0, s, a); break;
   }
   return hipGetLastError();
 }

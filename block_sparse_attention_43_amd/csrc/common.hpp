@@ -129,6 +129,32 @@ __device__ __forceinline__ float max_halves(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------------------
+// LDS tiles staged by direct global->LDS loads (global_load_lds_dwordx4).
+//
+// One such load writes 16 bytes per lane at (LDS base + 16 * lane), i.e. a wave fills
+// 1 KB of LDS contiguously. A tile of `rows` rows of ROW bytes is kept unpadded; the
+// 16-byte chunks of row r are stored in XOR-permuted order (chunk c at position
+// c ^ swz(r)) so that the MFMA operand reads, which take the same logical chunk from
+// many rows, spread over all banks.
+// ---------------------------------------------------------------------------
+template <int ROW>
+struct SwizzledTile {
+  static constexpr int kChunks = ROW / 16;                          // chunks per row
+  static constexpr int kRowsPerLine = ROW >= 256 ? 1 : 256 / ROW;   // rows sharing 256 bytes
+  static constexpr int kMask = (kChunks < 16 ? kChunks : 16) - 1;
+  __device__ __forceinline__ static int swz(int r) { return (r / kRowsPerLine) & kMask; }
+  // byte offset of (row r, byte b within the logical row)
+  __device__ __forceinline__ static int offset(int r, int b) {
+    return r * ROW + (((b >> 4) ^ swz(r)) << 4) + (b & 15);
+  }
+};
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src,
+      (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
+}
+
 // Workgroups are dealt round-robin to the 8 XCDs; remap so that consecutive logical
 // ids (neighbouring query tiles of one head) run on the same XCD and share its L2.
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t n) {
