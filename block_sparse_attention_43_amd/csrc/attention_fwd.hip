@@ -467,34 +467,38 @@ __global__ __launch_bounds__(256, 2) void attention_split_kernel(AttnArgs a) {
       k = kB;
     }
   };
+  // Buffer resources of this head's key tiles, Vᵀ tiles, centroid and mean-value groups;
+  // per-lane byte offsets inside a tile are loop-invariant.
+  int koff[DPW], voff[DPW];
+#pragma unroll
+  for (int u = 0; u < DPW; ++u) {
+    const int b = (wave * DPW + u) * 1024 + lane * 16;   // byte of the LDS tile this lane fills
+    const int rk = b / KROW, rv = b / VROW;
+    koff[u] = rk * KROW + ((((b % KROW) >> 4) ^ KT::swz(rk)) << 4);
+    voff[u] = rv * VROW + ((((b % VROW) >> 4) ^ VT::swz(rv)) << 4);
+  }
   // Direct loads of tile n (source j) into stage ST; this wave's share of both operands.
   auto issue_tile = [&](int n, int j, auto stc) {
     constexpr int ST = decltype(stc)::value;
     char* dk = ST ? sK1 : sK0;
     char* dv = ST ? sV1 : sV0;
-    const char* gk;
-    const char* gv;
-    if (VIRT && n >= n1) {
-      gk = kbp + size_t(j) * TB;
-      gv = vbp + size_t(j) * TB;
-    } else {
-      const int jj = (j >= 0 && j < nb) ? j : 0;
-      gk = Kh + size_t(jj) * TB;
-      gv = vt + size_t(jj) * TB;
-    }
+    const bool virt = VIRT && n >= n1;
+    const int base = __builtin_amdgcn_readfirstlane(((j >= 0 && j < nb) || virt ? j : 0) * TB);
+    if (virt) {
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbp, uint32_t(a.nbp) * KROW);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbp, uint32_t(a.nbp) * KROW);
 #pragma unroll
-    for (int u = 0; u < DPW; ++u) {
-      const int ins = wave * DPW + u;
-      const int b = ins * 1024 + lane * 16;    // byte of the LDS tile this lane fills
-      {
-        const int r = b / KROW, pos = (b % KROW) >> 4;
-        const int c = pos ^ KT::swz(r);
-        dma16(gk + r * KROW + c * 16, dk + ins * 1024);
+      for (int u = 0; u < DPW; ++u) {
+        buf_dma16(rk, koff[u], base, dk + (wave * DPW + u) * 1024);
+        buf_dma16(rv, voff[u], base, dv + (wave * DPW + u) * 1024);
       }
-      {
-        const int r = b / VROW, pos = (b % VROW) >> 4;
-        const int c = pos ^ VT::swz(r);
-        dma16(gv + r * VROW + c * 16, dv + ins * 1024);
+    } else {
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh, uint32_t(nb) * TB);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vt, uint32_t(nb) * TB);
+#pragma unroll
+      for (int u = 0; u < DPW; ++u) {
+        buf_dma16(rk, koff[u], base, dk + (wave * DPW + u) * 1024);
+        buf_dma16(rv, voff[u], base, dv + (wave * DPW + u) * 1024);
       }
     }
   };
@@ -531,8 +535,12 @@ __global__ __launch_bounds__(256, 2) void attention_split_kernel(AttnArgs a) {
   };
 
   // One tile: Sᵀ for this wave's 32 keys, online softmax, Oᵀ += Vᵀ Pᵀ.
+  const bool wave_has_rows = 32 * qh < ni;        // some of this wave's query rows are valid
   auto compute = [&](auto stc, bool second, int nj) {
     constexpr int st = decltype(stc)::value;
+    // Nothing to do when all of this wave's rows, or all keys of its half of an exact
+    // block, are padding (ragged edge cubes hold 8..32 tokens).
+    if (!wave_has_rows || (!second && nj <= 32 * kh)) return;
     const char* sk = st ? sK1 : sK0;
     const char* sv = st ? sV1 : sV0;
     f32x16 s = zero16();

@@ -155,6 +155,16 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
       (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
 }
 
+// Buffer-addressed variant: byte address = base(rsrc) + soff (scalar) + voff (per lane);
+// reads past `bytes` of the resource return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
+}
+__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, int voff, int soff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_wave_base),
+                                           16, voff, soff, 0, 0);
+}
+
 // Workgroups are dealt round-robin to the 8 XCDs; remap so that consecutive logical
 // ids (neighbouring query tiles of one head) run on the same XCD and share its L2.
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t n) {
