@@ -107,7 +107,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="wan", help="tiny | flux | wan | hunyuan | long")
     ap.add_argument("--mode", default="pwt", help="drop | pisa | pwt | literal")
-    ap.add_argument("--cpu-heads", type=int, default=8, help="heads in the oracle sample")
+    ap.add_argument("--cpu-heads", type=int, default=12, help="heads in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     args = ap.parse_args()
