@@ -110,6 +110,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--traffic-driver", action="store_true",
+                    help="counter-collection driver: a 512 MiB device copy (calibration) x3, then "
+                         "statistics + selection once and three attention launches; prints one line")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -137,6 +140,21 @@ def main():
     blt = None if (bl == 64).all() else torch.from_numpy(bl.astype(np.int32)).cuda()
     H, L, d = Q.shape
     nb = L // 64
+
+    if args.traffic_driver:
+        src = torch.ones(512 * 2**20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        st = pisa.block_stats(K, V, blt)
+        idx, mask, wt = pisa.select_topk(Q, st, K_sel, blt, want_wt=(base == pisa.MODE_PWT))
+        O = torch.empty_like(Q)
+        for _ in range(3):
+            pisa.attention_fwd(Q, K, V, st, idx, mask, wt, K_sel, mode, blt, out=O)
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_driver": cfg.name, "mode": mode, "copy_bytes": 512 * 2**20,
+                          "kernel_sha256_16": kernel_source_hash()}))
+        return
 
     # every buffer allocated once, outside the timed region
     st = pisa.alloc_stats(K)

@@ -19,13 +19,14 @@
 
 namespace pisa {
 
-template <class T, int D>
+template <class T, int D, bool PER_BLOCK>
 __global__ __launch_bounds__(256) void block_stats_kernel(StatsArgs a, unsigned flags) {
   using M = typename MmaFor<T>::type;
   constexpr int KI = M::KI, KH = M::KH;
   constexpr int EPC = 16 / sizeof(T);      // elements per 16-byte chunk
   constexpr int LDR = D + EPC;             // LDS row stride (elements), padded against bank conflicts
   constexpr int CPR = D / EPC;             // chunks per token row
+  constexpr int CPT = kB * CPR / 256;      // chunks per thread per operand
   constexpr int NT = D / 32;               // 32-wide output tiles per side of d x d
   constexpr int TPW = NT * NT / 4;         // output tiles per wave
   __shared__ __align__(16) T sK[kB * LDR];
@@ -44,26 +45,39 @@ __global__ __launch_bounds__(256) void block_stats_kernel(StatsArgs a, unsigned 
   T* kbp = reinterpret_cast<T*>(a.packed + a.pl.kbar) + size_t(h) * a.nbp * D;
   T* vbp = reinterpret_cast<T*>(a.packed + a.pl.vbar) + size_t(h) * a.nbp * D;
 
+  // Running Σ_j Σ_i (k_i - k̄_j) v_iᵀ of this workgroup's blocks, as [c][e] MFMA tiles.
   f32x16 run[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) run[u] = zero16();
+
+  // Block j's K and V rows, 16-byte chunks, held in registers one block ahead.
+  u32x4 rk[CPT], rv[CPT];
+  auto load_block = [&](int j) {
+#pragma unroll
+    for (int p = 0; p < CPT; ++p) {
+      const int c = tid + 256 * p;
+      const int row = c / CPR, col = (c % CPR) * EPC;
+      rk[p] = *reinterpret_cast<const u32x4*>(Kh + size_t(j * kB + row) * D + col);
+      rv[p] = *reinterpret_cast<const u32x4*>(Vh + size_t(j * kB + row) * D + col);
+    }
+  };
+  if (j0 < j1) load_block(j0);
 
   for (int j = j0; j < j1; ++j) {
     int n = a.block_len ? a.block_len[j] : kB;
     n = min(max(n, 1), kB);
     const float invn = 1.f / float(n);
 
-    // Stage K_j and V_j (rows >= n_j zeroed) in LDS.
-    for (int c = tid; c < kB * CPR; c += 256) {
+    __syncthreads();                       // previous block's LDS reads done
+#pragma unroll
+    for (int p = 0; p < CPT; ++p) {        // stage K_j, V_j; rows >= n_j as zeros
+      const int c = tid + 256 * p;
       const int row = c / CPR, col = (c % CPR) * EPC;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (row < n) {
-        kv = *reinterpret_cast<const u32x4*>(Kh + size_t(j * kB + row) * D + col);
-        vv = *reinterpret_cast<const u32x4*>(Vh + size_t(j * kB + row) * D + col);
-      }
-      *reinterpret_cast<u32x4*>(sK + row * LDR + col) = kv;
-      *reinterpret_cast<u32x4*>(sV + row * LDR + col) = vv;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sK + row * LDR + col) = row < n ? rk[p] : z;
+      *reinterpret_cast<u32x4*>(sV + row * LDR + col) = row < n ? rv[p] : z;
     }
+    if (j + 1 < j1) load_block(j + 1);     // in flight while this block is reduced
     __syncthreads();
 
     // Column statistics: threads [0, D) own key columns, [128, 128 + D) value columns.
@@ -98,12 +112,14 @@ __global__ __launch_bounds__(256) void block_stats_kernel(StatsArgs a, unsigned 
       for (int u = 0; u < EPC; ++u) tmp[u] = sV[(i0 + u) * LDR + e];
       *reinterpret_cast<u32x4*>(vt + (size_t(j) * D + e) * kB + i0) = *reinterpret_cast<u32x4*>(tmp);
     }
-    __syncthreads();   // sKbar / sVsum visible
+    __syncthreads();                       // sKbar / sVsum visible
 
-    // Cross term on MFMA: blk[c][e] = Σ_i K[i][c] V[i][e] (A = Kᵀ, B = V, k = token).
-    f32x16 blk[TPW];
+    // Cross term on MFMA, accumulated straight into the running sum:
+    // run[c][e] += Σ_i K[i][c] V[i][e] (A = Kᵀ, B = V, k = token), then the centring
+    // term k̄_j[c] ΣV_j[e] is removed for this block.
+    f32x16 blk[PER_BLOCK ? TPW : 1];
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) blk[u] = zero16();
+    for (int u = 0; u < (PER_BLOCK ? TPW : 1); ++u) blk[u] = zero16();
 #pragma unroll
     for (int ks = 0; ks < kB / KI; ++ks) {
       float av[KH];
@@ -116,10 +132,10 @@ __global__ __launch_bounds__(256) void block_stats_kernel(StatsArgs a, unsigned 
         float bv[KH];
 #pragma unroll
         for (int q = 0; q < KH; ++q) bv[q] = to_f32(sV[(KI * ks + KH * g + q) * LDR + 32 * et + l32]);
-        blk[u] = M::mma(A, M::pack(bv), blk[u]);
+        if constexpr (PER_BLOCK) blk[u] = M::mma(A, M::pack(bv), blk[u]);
+        else run[u] = M::mma(A, M::pack(bv), run[u]);
       }
     }
-    // H_j[c][e]ᵀ = blk - k̄_j ΣV_jᵀ ; accumulate and optionally store H_j as [e][c].
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int et = (wave * TPW + u) % NT;
@@ -128,43 +144,48 @@ __global__ __launch_bounds__(256) void block_stats_kernel(StatsArgs a, unsigned 
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int c = 32 * ct + acc_row(r, g);
-        const float hv = blk[u][r] - sKbar[c] * ve;
-        run[u][r] += hv;
-        if (flags & 1u) a.hblk[((size_t(h) * a.nb + j) * D + e) * D + c] = hv;
+        if constexpr (PER_BLOCK) {
+          const float hv = blk[u][r] - sKbar[c] * ve;
+          run[u][r] += hv;
+          if (flags & 1u) a.hblk[((size_t(h) * a.nb + j) * D + e) * D + c] = hv;
+        } else {
+          run[u][r] = fmaf(-sKbar[c], ve, run[u][r]);
+        }
       }
     }
-    if (flags & 2u) {
-      // C_j[c][c'] = (1/n) Σ_i K[i][c] K[i][c'] - k̄_c k̄_c'
-      f32x16 cb[TPW];
+    if constexpr (PER_BLOCK) {
+      if (flags & 2u) {
+        // C_j[c][c'] = (1/n) Σ_i K[i][c] K[i][c'] - k̄_c k̄_c'
+        f32x16 cb[TPW];
 #pragma unroll
-      for (int u = 0; u < TPW; ++u) cb[u] = zero16();
+        for (int u = 0; u < TPW; ++u) cb[u] = zero16();
 #pragma unroll
-      for (int ks = 0; ks < kB / KI; ++ks) {
-        float av[KH];
+        for (int ks = 0; ks < kB / KI; ++ks) {
+          float av[KH];
 #pragma unroll
-        for (int u = 0; u < KH; ++u) av[u] = to_f32(sK[(KI * ks + KH * g + u) * LDR + 32 * ct + l32]);
-        const typename M::AB A = M::pack(av);
+          for (int u = 0; u < KH; ++u) av[u] = to_f32(sK[(KI * ks + KH * g + u) * LDR + 32 * ct + l32]);
+          const typename M::AB A = M::pack(av);
+#pragma unroll
+          for (int u = 0; u < TPW; ++u) {
+            const int et = (wave * TPW + u) % NT;
+            float bv[KH];
+#pragma unroll
+            for (int q = 0; q < KH; ++q) bv[q] = to_f32(sK[(KI * ks + KH * g + q) * LDR + 32 * et + l32]);
+            cb[u] = M::mma(A, M::pack(bv), cb[u]);
+          }
+        }
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
           const int et = (wave * TPW + u) % NT;
-          float bv[KH];
+          const int c2 = 32 * et + l32;
 #pragma unroll
-          for (int q = 0; q < KH; ++q) bv[q] = to_f32(sK[(KI * ks + KH * g + q) * LDR + 32 * et + l32]);
-          cb[u] = M::mma(A, M::pack(bv), cb[u]);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < TPW; ++u) {
-        const int et = (wave * TPW + u) % NT;
-        const int c2 = 32 * et + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = 32 * ct + acc_row(r, g);
-          a.cblk[((size_t(h) * a.nb + j) * D + c) * D + c2] = cb[u][r] * invn - sKbar[c] * sKbar[c2];
+          for (int r = 0; r < 16; ++r) {
+            const int c = 32 * ct + acc_row(r, g);
+            a.cblk[((size_t(h) * a.nb + j) * D + c) * D + c2] = cb[u][r] * invn - sKbar[c] * sKbar[c2];
+          }
         }
       }
     }
-    __syncthreads();   // LDS reused by the next block
   }
 
   float* part = a.part + (size_t(h) * a.ngroups + grp) * D * D;
@@ -209,7 +230,8 @@ __global__ __launch_bounds__(256) void hbar_reduce_kernel(StatsArgs a) {
 template <class T, int D>
 static hipError_t launch_stats_t(const StatsArgs& a, unsigned flags, hipStream_t s) {
   dim3 g1(a.ngroups, a.H), g2((D * D + 255) / 256, a.H);
-  hipLaunchKernelGGL((block_stats_kernel<T, D>), g1, dim3(256), 0, s, a, flags);
+  if (flags) hipLaunchKernelGGL((block_stats_kernel<T, D, true>), g1, dim3(256), 0, s, a, flags);
+  else hipLaunchKernelGGL((block_stats_kernel<T, D, false>), g1, dim3(256), 0, s, a, flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((hbar_reduce_kernel<T, D>), g2, dim3(256), 0, s, a);

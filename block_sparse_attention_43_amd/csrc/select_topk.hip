@@ -20,30 +20,45 @@ namespace pisa {
 
 template <class T, int D>
 __global__ __launch_bounds__(256) void pool_kernel(SelectArgs a) {
-  constexpr int PARTS = 256 / D;           // row groups
-  constexpr int RPP = kB / PARTS;          // rows per group
-  __shared__ float s1[256], s2[256];
+  // Thread t reads 16-byte chunks (EPC columns) of rows t / CPR + RG * p; column sums and
+  // sums of squares are reduced over the RG row groups through LDS.
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int CPR = D / EPC;             // chunks per row
+  constexpr int RG = 256 / CPR;            // row groups
+  __shared__ float s1[RG][D], s2[RG][D];
   const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   int n = a.block_len ? a.block_len[i] : kB;
   n = min(max(n, 1), kB);
-  const int c = tid % D, part = tid / D;
+  const int ch = tid % CPR, rg = tid / CPR;
   const T* Qt = static_cast<const T*>(a.Q) + (size_t(h) * a.L + size_t(i) * kB) * D;
-  float s = 0.f, q2 = 0.f;
-  for (int r = part * RPP; r < (part + 1) * RPP; ++r) {
+  float sum[EPC], sq[EPC];
+#pragma unroll
+  for (int u = 0; u < EPC; ++u) sum[u] = sq[u] = 0.f;
+#pragma unroll
+  for (int p = 0; p < kB / RG; ++p) {
+    const int r = rg + RG * p;
     if (r < n) {
-      const float x = to_f32(Qt[size_t(r) * D + c]);
-      s += x;
-      q2 += x * x;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(Qt + size_t(r) * D + ch * EPC);
+      const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+      for (int u = 0; u < EPC; ++u) {
+        const float x = to_f32(e[u]);
+        sum[u] += x;
+        sq[u] += x * x;
+      }
     }
   }
-  s1[tid] = s;
-  s2[tid] = q2;
+#pragma unroll
+  for (int u = 0; u < EPC; ++u) {
+    s1[rg][ch * EPC + u] = sum[u];
+    s2[rg][ch * EPC + u] = sq[u];
+  }
   __syncthreads();
   if (tid < D) {
     float t1 = 0.f, t2 = 0.f;
-    for (int p = 0; p < PARTS; ++p) {
-      t1 += s1[p * D + tid];
-      t2 += s2[p * D + tid];
+    for (int q = 0; q < RG; ++q) {
+      t1 += s1[q][tid];
+      t2 += s2[q][tid];
     }
     const float invn = 1.f / float(n);
     a.qbar[(size_t(h) * a.nb + i) * D + tid] = t1 * invn;
@@ -51,11 +66,12 @@ __global__ __launch_bounds__(256) void pool_kernel(SelectArgs a) {
   }
 }
 
-// S = Q̄ K̄ᵀ and W = ½ Q̄² Σ²ᵀ per head; 64x64 output tile per workgroup, 4x4 per thread.
+// S = Q̄ K̄ᵀ and W = ½ Q̄² Σ²ᵀ per head; 64x64 output tile per workgroup, 4x4 per thread,
+// operands staged transposed in LDS in chunks of 32 of the head dimension.
 template <int D>
 __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
-  constexpr int KC = 16;
-  __shared__ float sA[KC][68], sB[KC][68], sA2[KC][68], sB2[KC][68];
+  constexpr int KC = 32;
+  __shared__ __align__(16) float sA[KC][64], sB[KC][64], sA2[KC][64], sB2[KC][64];
   const int h = blockIdx.z;
   const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
   const int tid = threadIdx.x, ti = tid / 16, tj = tid % 16;
@@ -71,40 +87,36 @@ __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
     for (int y = 0; y < 4; ++y) acc[x][y] = acw[x][y] = 0.f;
 
   for (int c0 = 0; c0 < D; c0 += KC) {
-    // 64 rows x 16 columns of each operand, stored transposed [c][row]
-    for (int e = tid; e < 64 * KC; e += 256) {
-      const int row = e / KC, c = e % KC;
-      const int ii = i0 + row, jj = j0 + row;
-      sA[c][row] = ii < a.nb ? qb[size_t(ii) * D + c0 + c] : 0.f;
-      sB[c][row] = jj < a.nb ? kb[size_t(jj) * D + c0 + c] : 0.f;
+    // 64 rows x 32 columns of each operand (8 threads per row, 4 columns each), stored [c][row]
+    const int row = tid / 4, cq = (tid % 4) * 8;
+    const int ii = i0 + row, jj = j0 + row;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      sA[cq + u][row] = ii < a.nb ? qb[size_t(ii) * D + c0 + cq + u] : 0.f;
+      sB[cq + u][row] = jj < a.nb ? kb[size_t(jj) * D + c0 + cq + u] : 0.f;
       if (want_w) {
-        sA2[c][row] = ii < a.nb ? q2[size_t(ii) * D + c0 + c] : 0.f;
-        sB2[c][row] = jj < a.nb ? ks[size_t(jj) * D + c0 + c] : 0.f;
+        sA2[cq + u][row] = ii < a.nb ? q2[size_t(ii) * D + c0 + cq + u] : 0.f;
+        sB2[cq + u][row] = jj < a.nb ? ks[size_t(jj) * D + c0 + cq + u] : 0.f;
       }
     }
     __syncthreads();
-#pragma unroll
+#pragma unroll 8
     for (int c = 0; c < KC; ++c) {
-      float av[4], bv[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        av[x] = sA[c][ti * 4 + x];
-        bv[x] = sB[c][tj * 4 + x];
-      }
+      const float4 av = *reinterpret_cast<const float4*>(&sA[c][ti * 4]);
+      const float4 bv = *reinterpret_cast<const float4*>(&sB[c][tj * 4]);
+      const float ax[4] = {av.x, av.y, av.z, av.w}, bx[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
       for (int x = 0; x < 4; ++x)
 #pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(av[x], bv[y], acc[x][y]);
+        for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(ax[x], bx[y], acc[x][y]);
       if (want_w) {
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          av[x] = sA2[c][ti * 4 + x];
-          bv[x] = sB2[c][tj * 4 + x];
-        }
+        const float4 aw = *reinterpret_cast<const float4*>(&sA2[c][ti * 4]);
+        const float4 bw = *reinterpret_cast<const float4*>(&sB2[c][tj * 4]);
+        const float ay[4] = {aw.x, aw.y, aw.z, aw.w}, by[4] = {bw.x, bw.y, bw.z, bw.w};
 #pragma unroll
         for (int x = 0; x < 4; ++x)
 #pragma unroll
-          for (int y = 0; y < 4; ++y) acw[x][y] = fmaf(av[x], bv[y], acw[x][y]);
+          for (int y = 0; y < 4; ++y) acw[x][y] = fmaf(ay[x], by[y], acw[x][y]);
       }
     }
     __syncthreads();
