@@ -269,7 +269,7 @@ def main():
         **dense,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4), "traffic": traffic,
-                     "kernel": "attention_kernel (pisa_attention_fwd)",
+                     "kernel": "attention_split_kernel (pisa_attention_fwd)",
                      "algorithmic_flops_per_launch": fc["attention"]},
         "cpu_baseline": cpu,
     }
