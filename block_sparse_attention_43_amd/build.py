@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpisa.so")
-SOURCES = ["abi.hip", "block_stats.hip", "select_topk.hip", "attention_fwd.hip"]
+SOURCES = ["abi.hip", "block_stats.hip", "select_topk.hip", "attention_fwd.hip", "attention_frag.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU forms are disabled for all device code (hipcc emits them from plain
 # float code otherwise); the host pass warns that it does not know the feature.
@@ -42,12 +42,18 @@ def _run(cmd):
     return out
 
 
+# Per-source extra flags. The register-streamed attention kernel keeps its MFMA results
+# in VGPRs (the VALU reads every score tile); operands still come from AGPRs.
+EXTRA = {"attention_frag.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"]}
+
+
 def build(verbose: bool = False, jobs: int = 4) -> str:
     hipcc = _hipcc()
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
-    cmds = [[hipcc, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    cmds = [[hipcc, *FLAGS, *EXTRA.get(s, []), "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():

@@ -1,0 +1,515 @@
+// Register-streamed attention forward for bf16 inputs, modes DROP / PISA / PWT.
+//
+// Same computation as the LDS-staged kernels of attention_fwd.hip (PISA paper §3.2
+// Eq. (3.2), §3.3 and §3.4 phases 1-3; Sparse Linear Attention blog, Sparse Linear
+// Attention and PWT sections): exact softmax terms of every key of the selected blocks,
+// one virtual token per unselected block (logit q·k̄_j + ln n_j + φ_ij, value ΣV_j / n_j,
+// its weight e^{q·k̄_j + φ} also summed into A_t), then N_t += A_t H̄ q_t and
+// o_t = N_t / D_t, all under one online softmax.
+//
+// Organisation, chosen for gfx950:
+// * One workgroup of two waves per 64-row query tile. Wave w takes key half w (32 keys)
+//   of every tile, for all 64 queries: the scores Sᵀ (32 keys x 64 queries, two
+//   v_mfma_f32_32x32x16_bf16 output tiles) and the output Oᵀ (D x 64) are each computed
+//   once, and the two halves' softmax states are merged at the end.
+// * K, Vᵀ, centroid and mean-value tiles are stored in MFMA operand order (TileLayout),
+//   so a wave streams its 8 KB + 8 KB of a tile with 1 KB buffer loads straight into
+//   operand registers, about one tile ahead of use. The main loop has no barrier and
+//   touches LDS only for the bias of virtual tiles.
+// * One wave per SIMD holds Q (both query halves), the D x 64 accumulators and two tiles
+//   of operands. MFMA and VALU work overlap inside the wave by software pipelining over
+//   units u = (tile u / 2, query half u % 2): step k issues the score MFMAs of unit k + 1
+//   and the PV MFMAs of unit k - 1 while the VALU runs the softmax of unit k.
+// * Exact-tile descriptors (block index, valid keys) are staged in LDS per wave and read
+//   one issue ahead of use.
+// * No rescaling inside the loop: each row's exponentials are taken against a fixed
+//   reference, the first finite unit max of that row (the sums are still zero then).
+//   A row whose later logits exceed the reference by more than kSpan (log2 units) could
+//   overflow; the wave then runs its tiles again with the row's true max as reference,
+//   which bounds every exponential by 1. The accumulators are therefore touched by MFMA
+//   only and stay in accumulation registers for the whole loop.
+#include "attention.hpp"
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace pisa {
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Key (within the 32-key half) held by Sᵀ accumulator register r of lane half g.
+__device__ __forceinline__ constexpr int half_key(int r, int g) { return 16 * (r >> 3) + 8 * g + (r & 7); }
+
+__device__ __forceinline__ bf16x8 ld_frag(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ bf16x8 pack8(const f32x16& v, int off) {
+  bf16x8 r;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) r[u] = static_cast<__bf16>(v[off + u]);
+  return r;
+}
+
+// acc + Σ of the 8 bf16 values (v_dot2 against (1, 1), fp32 accumulation).
+__device__ __forceinline__ float sum8(bf16x8 v, float acc) {
+  const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+}
+
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+// Largest logit excess over the reference (log2 units) accepted without a second pass:
+// exponentials stay <= 2^32, so sums over up to 2^21 keys of values below 2^70 are finite.
+constexpr float kSpan = 32.f;
+
+}  // namespace
+
+template <int D, int MODE>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attention_frag_kernel(AttnArgs a) {
+  constexpr int NKD = D / 16;            // K fragments per half tile (score k-steps)
+  constexpr int NET = D / 32;            // 32-row tiles of Oᵀ
+  constexpr int NVF = 2 * NET;           // Vᵀ fragments per half tile
+  constexpr int HE = NET / 2;            // Oᵀ tiles finalised by each wave
+  constexpr int TB = kB * D * 2;         // bytes per tile
+  constexpr int HB = TB / 2;             // bytes per half tile
+  constexpr bool VIRT = MODE == MODE_PISA || MODE == MODE_PWT;
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  constexpr int kDead = 0x40000000;      // tile offset past every buffer: loads return zeros
+  constexpr int XS = HE * 32 + 8;        // floats per lane handed over in the merge
+  // Tiles of K / Vᵀ operands held in registers (loads run NS - 1 tiles ahead); the
+  // modes with virtual tiles need more registers elsewhere and keep two.
+  constexpr int NS = (D == 128 && VIRT) ? 2 : 3;
+  using KT = SwizzledTile<D * 2>;
+  static_assert(2 * XS * 64 * 4 >= kB * D * 2, "output staging must fit the hand-over buffer");
+
+  __shared__ __align__(16) float sX[2 * XS * 64];
+  __shared__ __align__(16) float sBias[2][32], sInvN[2][32];
+
+  const int lane = threadIdx.x & 63, kh = threadIdx.x >> 6, g = lane >> 5, l32 = lane & 31;
+  const int nb = a.nb, ngrp = a.nbp / kB;
+  const uint32_t lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = int(lin / uint32_t(nb)), i = int(lin % uint32_t(nb));
+  int ni = a.block_len ? a.block_len[i] : kB;
+  ni = min(max(ni, 1), kB);
+
+  const uint16_t* Qh = static_cast<const uint16_t*>(a.Q) + size_t(h) * a.L * D;
+  const char* kfh = a.packed + a.pl.kf + size_t(h) * nb * TB;
+  const char* vth = a.packed + a.pl.vt + size_t(h) * nb * TB;
+  const char* kbh = a.packed + a.pl.kbar + size_t(h) * ngrp * TB;
+  const char* vbh = a.packed + a.pl.vbar + size_t(h) * ngrp * TB;
+  const uint16_t* hbp = reinterpret_cast<const uint16_t*>(a.packed + a.pl.hbar) + size_t(h) * D * D;
+  const uint32_t* mrow = VIRT ? a.mask + (size_t(h) * nb + i) * a.nw : nullptr;
+  const float* wrow = MODE == MODE_PWT ? a.wt + (size_t(h) * nb + i) * nb : nullptr;
+
+  // Q fragments, B operand of Sᵀ = K Qᵀ, for query halves 0 and 1; padding rows are zero.
+  bf16x8 qf[2][NKD];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int row = 32 * qt + l32;
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks) {
+      bf16x8 v = {};
+      if (row < ni) v = *reinterpret_cast<const bf16x8*>(Qh + (size_t(i) * kB + row) * D + 16 * ks + 8 * g);
+      qf[qt][ks] = v;
+    }
+  }
+
+  f32x16 acc[NET][2];
+  float m[2] = {NEG_INF, NEG_INF}, mtop[2] = {NEG_INF, NEG_INF}, lsum[2], asum[2];
+  bool over = false;
+
+  const int n1 = a.K_sel;
+  const int N = n1 + (VIRT ? ngrp : 0);
+
+  // Exact-tile descriptors (block index | valid keys << 16; 0 for an out-of-range index)
+  // are staged in a wave-private LDS table, DCAP tiles at a time. The table lives in this
+  // wave's own hand-over region, which the wave writes only after its loop. Each issue
+  // reads the next tile's descriptor one issue ahead, so the loop never waits on memory
+  // for descriptors; tables are refilled (waiting on memory) only every DCAP tiles.
+  constexpr int DCAP = XS * 64;
+  uint32_t* dtab = reinterpret_cast<uint32_t*>(sX + kh * XS * 64);
+  const int32_t* irow = a.idx + (size_t(h) * nb + i) * a.K_sel;
+  int dbase = 0;
+  auto fill = [&](int t0) {              // descriptors of exact tiles [t0, t0 + DCAP)
+    const int cnt = min(DCAP, n1 - t0);
+    for (int e = lane; e < cnt; e += 64) {
+      const int j = irow[t0 + e];
+      uint32_t d = 0u;
+      if (j >= 0 && j < nb) {
+        const int v = a.block_len ? a.block_len[j] : kB;
+        d = uint32_t(j) | (uint32_t(min(max(v, 1), kB)) << 16);
+      }
+      dtab[e] = d;
+    }
+    dbase = t0;
+  };
+  auto read_desc = [&](int t) -> uint32_t {   // t < n1, t >= dbase
+    if (t - dbase >= DCAP) fill(t);
+    return dtab[t - dbase];
+  };
+  uint32_t dnext = 0u;                   // descriptor of the next exact tile to issue
+  // Operand ring: the K and Vᵀ registers of NS tiles. Stage s holds tiles t with t % NS == s.
+  bf16x8 kst[NS][NKD], vst[NS][NVF];
+  int toff[NS], njs[NS];
+  uint32_t bwm[NS];
+  int bwl[NS];
+  float bww[NS];
+
+  // Tile t's source (stage P = t % NS): offset and valid-key count from its descriptor,
+  // the descriptor pipeline advanced, and for virtual tiles the raw inputs of this
+  // wave's 32 biases. The fragment loads themselves are spread over the step.
+  auto issue_desc = [&](int t, auto pc) {
+    constexpr int P = decltype(pc)::value;
+    const bool virt = VIRT && t >= n1;
+    int off = kDead, nk = 0;
+    if (t < N) {
+      if (virt) {
+        off = (t - n1) * TB;
+        nk = kB;
+      } else {
+        const uint32_t d = __builtin_amdgcn_readfirstlane(dnext);
+        nk = int(d >> 16);
+        off = int(d & 0xFFFFu) * TB;
+        if (t + 1 < n1) dnext = read_desc(t + 1);
+      }
+    }
+    toff[P] = off;
+    njs[P] = nk;
+    if constexpr (VIRT) {
+      const int grp = min(max(t - n1, 0), ngrp - 1);
+      const int jj = min(grp * kB + 32 * kh + l32, nb - 1);
+      bwm[P] = mrow[jj >> 5];
+      bwl[P] = a.block_len ? a.block_len[jj] : kB;
+      if constexpr (MODE == MODE_PWT) bww[P] = wrow[jj];
+    }
+    // These loads stay ahead of the step's tile loads, so that reading them at the next
+    // issue waits only for older loads.
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Buffer resource and lane offset of tile t's K (or Vᵀ) fragments in stage P.
+  auto krsrc = [&](int t) { return VIRT && t >= n1 ? make_rsrc(kbh, uint32_t(ngrp) * TB) : make_rsrc(kfh, uint32_t(nb) * TB); };
+  auto vrsrc = [&](int t) { return VIRT && t >= n1 ? make_rsrc(vbh, uint32_t(ngrp) * TB) : make_rsrc(vth, uint32_t(nb) * TB); };
+  auto frag_at = [&](__amdgpu_buffer_rsrc_t r, int vo, int f) { return ld_frag(r, vo + (f & 3) * 1024, (f >> 2) * 4096); };
+  auto issue_k = [&](int t, auto pc) {   // whole tile at once (prologue)
+    constexpr int P = decltype(pc)::value;
+    issue_desc(t, pc);
+    const __amdgpu_buffer_rsrc_t r = krsrc(t);
+    const int vo = lane * 16 + toff[P] + kh * HB;
+    static_for<0, NKD>([&](auto fc) { kst[P][decltype(fc)::value] = frag_at(r, vo, decltype(fc)::value); });
+  };
+  auto issue_v = [&](int t, auto pc) {
+    constexpr int P = decltype(pc)::value;
+    const __amdgpu_buffer_rsrc_t r = vrsrc(t);
+    const int vo = lane * 16 + toff[P] + kh * HB;
+    static_for<0, NVF>([&](auto fc) { vst[P][decltype(fc)::value] = frag_at(r, vo, decltype(fc)::value); });
+  };
+
+  // Scores of unit (tile n, stage P, query half QT) in log2 units or raw: virtual tiles
+  // get their bias (-inf for selected blocks and padding) and return scale 1; ragged
+  // exact blocks mask their padding keys and return scale log2(e).
+  auto prep = [&](f32x16& s, int n, auto pc, auto qc) -> float {
+    constexpr int P = decltype(pc)::value, QT = decltype(qc)::value;
+    if (VIRT && n >= n1) {
+      if constexpr (QT == 0) {
+        const int jj = (n - n1) * kB + 32 * kh + l32;
+        float b = NEG_INF, inv = 0.f;
+        if (jj < nb && !((bwm[P] >> (jj & 31)) & 1u)) {
+          const int nj = min(max(bwl[P], 1), kB);
+          const float lnn = logf(float(nj));
+          float phi = 0.f;
+          if constexpr (MODE == MODE_PWT) {
+            float w = bww[P];
+            if (a.gate && w > lnn) w = 0.f;
+            phi = a.w_linear ? log1pf(w) : w;
+          }
+          b = (lnn + phi) * kLog2e;
+          inv = 1.f / float(nj);
+        }
+        if (g == 0) {
+          sBias[kh][l32] = b;
+          sInvN[kh][l32] = inv;
+        }
+      }
+      const float4* bp = reinterpret_cast<const float4*>(&sBias[kh][8 * g]);
+      const float4 b0 = bp[0], b1 = bp[1], b2 = bp[4], b3 = bp[5];
+      const float bb[16] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w,
+                            b2.x, b2.y, b2.z, b2.w, b3.x, b3.y, b3.z, b3.w};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], kLog2e, bb[r]);
+      return 1.f;
+    }
+    const int nk = njs[P];
+    if (nk < kB) {
+      const int lim = nk - 32 * kh - 8 * g;    // register r holds key 32 kh + 8 g + half_key(r, 0)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (half_key(r, 0) >= lim) s[r] = NEG_INF;
+    }
+    return kLog2e;
+  };
+
+  f32x16 sb[2];
+  bf16x8 pb[2][2];
+
+  // One pipeline step k (unit k = tile k / 2, query half k % 2), ST = k % (2 NS).
+  //
+  // The step's matrix work (score MFMAs of unit k + 1, PV MFMAs of unit k - 1,
+  // alternating) and its VALU work (softmax of unit k) are laid out as NM groups: MFMA c,
+  // then one fragment load (odd steps) and a slice of the softmax, fenced so that the
+  // in-order wave always has VALU work to issue while an MFMA runs.
+  constexpr int NM = NKD + NVF;                  // MFMAs per step
+  auto step = [&](int k, auto stc) {
+    constexpr int ST = decltype(stc)::value;
+    constexpr int QT = ST & 1, QO = QT ^ 1;        // query half of unit k; of units k -+ 1
+    constexpr int TP = (ST >> 1) % NS;                  // stage of unit k's tile
+    constexpr int SK = ((ST + 1) >> 1) % NS;            // K stage read by the scores of unit k + 1
+    constexpr int SV = ((ST + 2 * NS - 1) >> 1) % NS;   // V stage read by the PV of unit k - 1
+    constexpr int LV = (TP + NS - 1) % NS;              // stage receiving Vᵀ on odd steps
+    const int n = k >> 1;
+    f32x16& sc = sb[QT];
+    f32x16& sn = sb[QO];
+    const float scl = prep(sc, n, ic<TP>{}, ic<QT>{});
+    // Odd steps stream operands NS - 1 tiles ahead of use: K of tile n + NS into the
+    // stage that tile n just left, Vᵀ of tile n + NS - 1 into the one tile n - 1 left.
+    if constexpr (ST & 1) issue_desc(n + NS, ic<TP>{});
+    const __amdgpu_buffer_rsrc_t rk = krsrc(n + NS), rv = vrsrc(n + NS - 1);   // used on odd steps
+    const int vok = lane * 16 + toff[TP] + kh * HB, vov = lane * 16 + toff[LV] + kh * HB;
+    float t0 = 0.f, t1 = 0.f, mx = 0.f, mu = 0.f;
+    // Softmax of unit k in 16 slices against the row's fixed reference.
+    auto slice = [&](auto vc) {
+      constexpr int v = decltype(vc)::value;
+      if constexpr (v == 0) {
+        t0 = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+      } else if constexpr (v == 1) {
+        t1 = fmaxf(fmaxf(fmaxf(sc[8], sc[9]), fmaxf(sc[10], sc[11])), fmaxf(fmaxf(sc[12], sc[13]), fmaxf(sc[14], sc[15])));
+      } else if constexpr (v == 2) {
+        mx = max_halves(fmaxf(t0, t1)) * scl;
+      } else if constexpr (v == 3) {
+        const float mn = m[QT] == NEG_INF ? mx : m[QT];
+        m[QT] = mn;
+        mtop[QT] = fmaxf(mtop[QT], mx);
+        over |= mx > mn + kSpan;
+        mu = mn == NEG_INF ? 0.f : mn;
+      } else if constexpr (v < 12) {
+        constexpr int r = 2 * (v - 4);
+        sc[r] = fast_exp2(fmaf(sc[r], scl, -mu));
+        sc[r + 1] = fast_exp2(fmaf(sc[r + 1], scl, -mu));
+      } else if constexpr (v == 12) {
+        pb[QT][0] = pack8(sc, 0);
+      } else if constexpr (v == 13) {
+        lsum[QT] = sum8(pb[QT][0], lsum[QT]);
+      } else if constexpr (v == 14) {
+        pb[QT][1] = pack8(sc, 8);
+      } else {
+        lsum[QT] = sum8(pb[QT][1], lsum[QT]);
+      }
+    };
+    static_for<0, NM>([&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      if constexpr (c & 1) {                     // score MFMA f of unit k + 1
+        constexpr int f = c >> 1;
+        sn = MmaBF16::mma(kst[SK][f], qf[QO][f], f == 0 ? zero16() : sn);
+      } else {                                   // PV MFMA v of unit k - 1
+        constexpr int v = c >> 1, et = v % NET, ks = v / NET;
+        acc[et][QO] = MmaBF16::mma(vst[SV][2 * et + ks], pb[QO][ks], acc[et][QO]);
+      }
+      if constexpr (ST & 1) {
+        if constexpr (c < NKD) kst[TP][c] = frag_at(rk, vok, c);
+        else vst[LV][c - NKD] = frag_at(rv, vov, c - NKD);
+      }
+      static_for<c * 16 / NM, (c + 1) * 16 / NM>(slice);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // P of unit k is used by the next step's MFMAs and the sums only after the loop;
+    // keep them computed here rather than sunk next to those uses.
+    asm volatile("" ::"v"(pb[QT][0]), "v"(pb[QT][1]), "v"(lsum[QT]), "v"(mtop[QT]));
+
+    if (VIRT && n >= n1) {            // A_t: Σ p / n_j over this lane's virtual tokens
+      const float4* ip = reinterpret_cast<const float4*>(&sInvN[kh][8 * g]);
+      const float4 c0 = ip[0], c1 = ip[1], c2 = ip[4], c3 = ip[5];
+      const float cc[16] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w,
+                            c2.x, c2.y, c2.z, c2.w, c3.x, c3.y, c3.z, c3.w};
+      float pa = asum[QT];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pa = fmaf(sc[r], cc[r], pa);
+      asum[QT] = pa;
+    }
+  };
+  // After the last step: PV of the last unit (query half 1, V stage SV).
+  auto finish = [&](auto svc) {
+    constexpr int SV = decltype(svc)::value;
+    static_for<0, 2>([&](auto kc) {
+      constexpr int ks = decltype(kc)::value;
+#pragma unroll
+      for (int et = 0; et < NET; ++et) acc[et][1] = MmaBF16::mma(vst[SV][2 * et + ks], pb[1][ks], acc[et][1]);
+    });
+  };
+
+  for (int pass = 0;; ++pass) {
+#pragma unroll
+    for (int et = 0; et < NET; ++et) acc[et][0] = acc[et][1] = zero16();
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) lsum[qt] = asum[qt] = 0.f;
+    if (N == 0) break;
+    // Prologue: descriptors, K of tiles [0, NS), Vᵀ of tiles [0, NS - 1), scores of
+    // unit 0. Vᵀ stage NS - 1 and P of "unit -1" are zero, so step 0's PV adds nothing.
+    if (n1 > 0) {
+      fill(0);
+      dnext = read_desc(0);
+    }
+#pragma unroll
+    for (int f = 0; f < NVF; ++f) vst[NS - 1][f] = bf16x8{};
+    pb[1][0] = pb[1][1] = bf16x8{};
+    static_for<0, NS>([&](auto tc) { issue_k(decltype(tc)::value, tc); });
+    static_for<0, NS - 1>([&](auto tc) { issue_v(decltype(tc)::value, tc); });
+    sb[0] = MmaBF16::mma(kst[0][0], qf[0][0], zero16());
+    static_for<1, NKD>([&](auto fc) {
+      constexpr int f = decltype(fc)::value;
+      sb[0] = MmaBF16::mma(kst[0][f], qf[0][f], sb[0]);
+    });
+
+    // 2 NS steps (NS tiles) per iteration so every stage index is static; the last
+    // N % NS tiles run after the loop (a single loop exit keeps the register assignment
+    // simple), then the PV of the last unit.
+    const int last = 2 * N;
+    int k = 0;
+    for (; k + 2 * NS <= last; k += 2 * NS)
+      static_for<0, 2 * NS>([&](auto sc) { step(k + decltype(sc)::value, sc); });
+    static_for<0, NS>([&](auto rc) {
+      constexpr int R = decltype(rc)::value;              // tiles left
+      if (last - k == 2 * R) {
+        static_for<0, 2 * R>([&](auto sc) { step(k + decltype(sc)::value, sc); });
+        finish(ic<(R + NS - 1) % NS>{});
+      }
+    });
+    // Some row may have overflowed: run again with every row's true max as reference.
+    if (pass > 0 || !__any(over)) break;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) m[qt] = mtop[qt];
+    over = false;
+  }
+
+  // Merge the two key halves. Each lane's sums cover its own 16 keys; both lane halves
+  // hold the same max. Wave kh finalises Oᵀ tiles [kh HE, kh HE + HE) of both query
+  // halves and hands the partner's tiles over through LDS.
+  {
+    float* mine = sX + kh * XS * 64 + lane;
+    auto hand_over = [&](auto oc) {
+      constexpr int O = decltype(oc)::value;      // first tile the partner finalises
+#pragma unroll
+      for (int u = 0; u < HE; ++u)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mine[((u * 2 + qt) * 16 + r) * 64] = acc[O + u][qt][r];
+    };
+    if (kh == 0) hand_over(ic<HE>{});
+    else hand_over(ic<0>{});
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      mine[(HE * 32 + qt) * 64] = m[qt];
+      mine[(HE * 32 + 2 + qt) * 64] = lsum[qt];
+      mine[(HE * 32 + 4 + qt) * 64] = asum[qt];
+    }
+  }
+  __syncthreads();
+  f32x16 res[HE][2];
+  float mt[2], lt[2], at[2];
+  {
+    const float* oth = sX + (1 - kh) * XS * 64 + lane;
+    auto combine = [&](auto oc) {
+      constexpr int O = decltype(oc)::value;      // first tile this wave finalises
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const float mo = oth[(HE * 32 + qt) * 64];
+        mt[qt] = fmaxf(m[qt], mo);
+        const float mu = mt[qt] == NEG_INF ? 0.f : mt[qt];
+        const float f = fast_exp2(m[qt] - mu), fo = fast_exp2(mo - mu);
+#pragma unroll
+        for (int u = 0; u < HE; ++u)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) res[u][qt][r] = acc[O + u][qt][r] * f + oth[((u * 2 + qt) * 16 + r) * 64] * fo;
+        lt[qt] = lsum[qt] * f + oth[(HE * 32 + 2 + qt) * 64] * fo;
+        at[qt] = asum[qt] * f + oth[(HE * 32 + 4 + qt) * 64] * fo;
+      }
+    };
+    if (kh == 0) combine(ic<0>{});
+    else combine(ic<HE>{});
+  }
+  if constexpr (VIRT) {
+    // Phase 3: Oᵀ += H̄ (A_t q_t)ᵀ for this wave's Oᵀ tiles, H̄[e][c] as the A operand.
+    bf16x8 hf[HE][NKD];
+#pragma unroll
+    for (int u = 0; u < HE; ++u)
+#pragma unroll
+      for (int ks = 0; ks < NKD; ++ks)
+        hf[u][ks] = *reinterpret_cast<const bf16x8*>(hbp + size_t(32 * (kh * HE + u) + l32) * D + 16 * ks + 8 * g);
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const float A = sum_halves(at[qt]);
+#pragma unroll
+      for (int ks = 0; ks < NKD; ++ks) {
+        bf16x8 b;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) b[u] = static_cast<__bf16>(static_cast<float>(qf[qt][ks][u]) * A);
+#pragma unroll
+        for (int u = 0; u < HE; ++u) res[u][qt] = MmaBF16::mma(hf[u][ks], b, res[u][qt]);
+      }
+    }
+  }
+  float inv[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float l = sum_halves(lt[qt]);
+    inv[qt] = l > 0.f ? 1.f / l : 0.f;
+    const int q = 32 * qt + l32;
+    if (a.lse && kh == 0 && g == 0)
+      a.lse[size_t(h) * a.L + size_t(i) * kB + q] = (q < ni && l > 0.f) ? mt[qt] * kLn2 + logf(l) : NEG_INF;
+  }
+  __syncthreads();                                  // hand-over buffers consumed
+  // Output tile staged in LDS (swizzled rows) for coalesced 16-byte stores.
+  char* so = reinterpret_cast<char*>(sX);
+#pragma unroll
+  for (int u = 0; u < HE; ++u)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int q = 32 * qt + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int e = 32 * (kh * HE + u) + acc_row(r, g);
+        *reinterpret_cast<uint16_t*>(so + KT::offset(q, e * 2)) = f32_to_bf16(q < ni ? res[u][qt][r] * inv[qt] : 0.f);
+      }
+    }
+  __syncthreads();
+  char* Oh = reinterpret_cast<char*>(static_cast<uint16_t*>(a.O) + (size_t(h) * a.L + size_t(i) * kB) * D);
+  constexpr int OCH = kB * D * 2 / 16;             // 16-byte chunks of the output tile
+#pragma unroll
+  for (int p = 0; p < OCH / 128; ++p) {
+    const int c = threadIdx.x + 128 * p;
+    const int row = c / (D * 2 / 16), cb = (c % (D * 2 / 16)) * 16;
+    *reinterpret_cast<u32x4*>(Oh + size_t(row) * D * 2 + cb) = *reinterpret_cast<const u32x4*>(so + KT::offset(row, cb));
+  }
+}
+
+template <int D>
+static hipError_t launch_frag_d(int mode, const AttnArgs& a, hipStream_t s) {
+  const dim3 grid(unsigned(a.H) * unsigned(a.nb));
+  switch (mode) {
+    case MODE_DROP: hipLaunchKernelGGL((attention_frag_kernel<D, MODE_DROP>), grid, dim3(128), 0, s, a); break;
+    case MODE_PISA: hipLaunchKernelGGL((attention_frag_kernel<D, MODE_PISA>), grid, dim3(128), 0, s, a); break;
+    default: hipLaunchKernelGGL((attention_frag_kernel<D, MODE_PWT>), grid, dim3(128), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_frag(int mode, const AttnArgs& a, hipStream_t s) {
+  return a.d == 64 ? launch_frag_d<64>(mode, a, s) : launch_frag_d<128>(mode, a, s);
+}
+
+}  // namespace pisa

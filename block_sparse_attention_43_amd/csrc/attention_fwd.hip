@@ -24,12 +24,11 @@
 // pass). K / Vᵀ tiles are staged through padded LDS; the next tile's global loads are
 // issued before the current tile is computed. Workgroup ids are remapped so that
 // neighbouring tiles of one head share an XCD (and its L2).
+#include "attention.hpp"
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace pisa {
-
-enum { MODE_DROP = 0, MODE_PISA = 1, MODE_PWT = 2, MODE_LITERAL = 3 };
 
 // Key row (within a 32-key m-tile) that the lane with A-row R loads.
 template <class M>
@@ -43,11 +42,7 @@ __device__ __forceinline__ int acc_key(int mt, int r, int g) {
   return 32 * mt + M::KI * (r / M::KH) + M::KH * g + (r % M::KH);
 }
 
-// Running-max update shared by every phase (log2 domain). The max only moves when a
-// logit exceeds it by more than kTau (lazy rescaling): exponentials stay <= 2^kTau and
-// the accumulators are rescaled on few tiles. All state is scaled by 2^-m.
-constexpr float kTau = 8.f;
-
+// Running-max update shared by every phase (log2 domain), lazy by kTau.
 template <int NET>
 __device__ __forceinline__ void raise_max(float cand, float& m, float& lsum, float& asum, f32x16 (&acc)[NET]) {
   const bool up = cand > m + kTau;
@@ -142,12 +137,16 @@ __global__ __launch_bounds__(128) void attention_kernel(AttnArgs a) {
     return min(max(v, 1), kB);
   };
 
+  // Packed tiles are in TileLayout order; chunk c below is the natural-order chunk
+  // (row c / CPRK of K, row c / CPRV of Vᵀ) that lands in the padded LDS tile.
+  using TL = TileLayout<T, D>;
   u32x4 rk[PF], rv[PF];
 #define PISA_LOAD_TILE(n_, j_)                                                        \
   do {                                                                               \
+    const bool virt_ = VIRT && (n_) >= n1;                                           \
     const T* pk_;                                                                    \
     const T* pv_;                                                                    \
-    if (VIRT && (n_) >= n1) {                                                        \
+    if (virt_) {                                                                     \
       pk_ = kbp + size_t(j_) * kB * D;                                               \
       pv_ = vbp + size_t(j_) * D * kB;                                               \
     } else {                                                                         \
@@ -158,8 +157,9 @@ __global__ __launch_bounds__(128) void attention_kernel(AttnArgs a) {
     static_for<0, PF>([&](auto pc) {                                                 \
       constexpr int p = decltype(pc)::value;                                         \
       const int c = tid + 128 * p;                                                   \
-      rk[p] = *reinterpret_cast<const u32x4*>(pk_ + (c / CPRK) * D + (c % CPRK) * EPC); \
-      rv[p] = *reinterpret_cast<const u32x4*>(pv_ + (c / CPRV) * kB + (c % CPRV) * EPC); \
+      const int kr_ = c / CPRK, kc_ = (c % CPRK) * EPC;                              \
+      rk[p] = *reinterpret_cast<const u32x4*>(pk_ + (virt_ ? TL::k(kr_, kc_) : kr_ * D + kc_)); \
+      rv[p] = *reinterpret_cast<const u32x4*>(pv_ + TL::v((c % CPRV) * EPC, c / CPRV)); \
     });                                                                              \
   } while (0)
 #define PISA_STORE_TILE(buf_)                                                         \
@@ -733,16 +733,20 @@ __global__ __launch_bounds__(256, 2) void attention_split_kernel(AttnArgs a) {
 template <class T, int D>
 static hipError_t launch_attn_t(int mode, const AttnArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.H) * unsigned(a.nb));
-  switch (mode) {
-    case MODE_DROP: hipLaunchKernelGGL((attention_split_kernel<T, D, MODE_DROP>), grid, dim3(256), 0, s, a); break;
-    case MODE_PISA: hipLaunchKernelGGL((attention_split_kernel<T, D, MODE_PISA>), grid, dim3(256), 0, s, a); break;
-    case MODE_PWT: hipLaunchKernelGGL((attention_split_kernel<T, D, MODE_PWT>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((attention_kernel<T, D, MODE_LITERAL>), grid, dim3(128), 0, s, a); break;
+  if (mode == MODE_LITERAL) {
+    hipLaunchKernelGGL((attention_kernel<T, D, MODE_LITERAL>), grid, dim3(128), 0, s, a);
+  } else if constexpr (std::is_same<T, float>::value) {   // fp32 DROP / PISA / PWT
+    switch (mode) {
+      case MODE_DROP: hipLaunchKernelGGL((attention_split_kernel<T, D, MODE_DROP>), grid, dim3(256), 0, s, a); break;
+      case MODE_PISA: hipLaunchKernelGGL((attention_split_kernel<T, D, MODE_PISA>), grid, dim3(256), 0, s, a); break;
+      default: hipLaunchKernelGGL((attention_split_kernel<T, D, MODE_PWT>), grid, dim3(256), 0, s, a); break;
+    }
   }
   return hipGetLastError();
 }
 
 hipError_t launch_attention(int bf16, int mode, const AttnArgs& a, hipStream_t s) {
+  if (bf16 && mode != MODE_LITERAL) return launch_attention_frag(mode, a, s);
   if (bf16) return a.d == 64 ? launch_attn_t<uint16_t, 64>(mode, a, s) : launch_attn_t<uint16_t, 128>(mode, a, s);
   return a.d == 64 ? launch_attn_t<float, 64>(mode, a, s) : launch_attn_t<float, 128>(mode, a, s);
 }

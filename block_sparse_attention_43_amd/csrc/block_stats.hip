@@ -11,9 +11,10 @@
 // products and fp32 accumulation, and the per-block centring k̄_j ΣV_jᵀ is removed in
 // fp32 before the block is added to the workgroup's partial sum. Partials are reduced
 // in a fixed order by a second kernel, so repeated runs are bit-identical.
-// The same pass writes the attention kernel's operand layouts: Vᵀ per block,
-// centroids and mean values (ΣV_j / n_j, transposed per group of 64 blocks) in the
-// storage type, and H̄[e][c].
+// The same pass writes the attention kernel's operands in the storage type, as 64-key
+// tiles in TileLayout order: Vᵀ per block (and, for bf16, K per block, so that the
+// attention kernel streams both straight into MFMA operand registers), centroids and
+// mean values ΣV_j / n_j per group of 64 blocks, and H̄[e][c]. Padding keys are zero.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -41,7 +42,10 @@ __global__ __launch_bounds__(256) void block_stats_kernel(StatsArgs a, unsigned 
 
   const T* Kh = static_cast<const T*>(a.K) + size_t(h) * a.L * D;
   const T* Vh = static_cast<const T*>(a.V) + size_t(h) * a.L * D;
-  T* vt = reinterpret_cast<T*>(a.packed + a.pl.vt) + size_t(h) * a.nb * D * kB;
+  using TL = TileLayout<T, D>;
+  constexpr int TE = kB * D;               // elements per 64-key tile
+  T* vt = reinterpret_cast<T*>(a.packed + a.pl.vt) + size_t(h) * a.nb * TE;
+  T* kf = reinterpret_cast<T*>(a.packed + a.pl.kf) + size_t(h) * a.nb * TE;
   T* kbp = reinterpret_cast<T*>(a.packed + a.pl.kbar) + size_t(h) * a.nbp * D;
   T* vbp = reinterpret_cast<T*>(a.packed + a.pl.vbar) + size_t(h) * a.nbp * D;
 
@@ -94,23 +98,31 @@ __global__ __launch_bounds__(256) void block_stats_kernel(StatsArgs a, unsigned 
       a.kbar[o] = mean;
       a.ksig2[o] = ss * invn;
       sKbar[tid] = mean;
-      kbp[size_t(j) * D + tid] = from_f32<T>(mean);
+      kbp[size_t(j / kB) * TE + TL::k(j % kB, tid)] = from_f32<T>(mean);
     } else if (tid >= 128 && tid < 128 + D) {
       const int c = tid - 128;
       float s = 0.f;
       for (int r = 0; r < kB; ++r) s += to_f32(sV[r * LDR + c]);
       a.vsum[(size_t(h) * a.nb + j) * D + c] = s;
       sVsum[c] = s;
-      vbp[(size_t(j / kB) * D + c) * kB + (j % kB)] = from_f32<T>(s * invn);
+      vbp[size_t(j / kB) * TE + TL::v(j % kB, c)] = from_f32<T>(s * invn);
     }
 
-    // Vᵀ of the block: vt[j][e][i], 16-byte chunks of consecutive keys, coalesced stores.
-    for (int c = tid; c < D * (kB / EPC); c += 256) {
-      const int e = c / (kB / EPC), i0 = (c % (kB / EPC)) * EPC;
+    // Vᵀ tile of the block (and the K tile for bf16), one 16-byte chunk per thread and
+    // step in storage order, so the stores are coalesced.
+    for (int x = tid; x < TE / EPC; x += 256) {
+      int i0 = 0, e = 0;
+      TL::vchunk(x, i0, e);
       __align__(16) T tmp[EPC];
 #pragma unroll
       for (int u = 0; u < EPC; ++u) tmp[u] = sV[(i0 + u) * LDR + e];
-      *reinterpret_cast<u32x4*>(vt + (size_t(j) * D + e) * kB + i0) = *reinterpret_cast<u32x4*>(tmp);
+      *reinterpret_cast<u32x4*>(vt + size_t(j) * TE + x * EPC) = *reinterpret_cast<u32x4*>(tmp);
+      if constexpr (sizeof(T) == 2) {
+        int key = 0, c0 = 0;
+        TL::kchunk(x, key, c0);
+        *reinterpret_cast<u32x4*>(kf + size_t(j) * TE + x * EPC) =
+            *reinterpret_cast<const u32x4*>(sK + key * LDR + c0);
+      }
     }
     __syncthreads();                       // sKbar / sVsum visible
 
@@ -219,11 +231,13 @@ __global__ __launch_bounds__(256) void hbar_reduce_kernel(StatsArgs a) {
 
   const int pad = a.nbp - a.nb;
   if (pad > 0 && x < pad * D) {
+    using TL = TileLayout<T, D>;
+    const size_t last = size_t(a.nb / kB) * kB * D;       // first element of the last group
+    const int key = a.nb % kB + x / D, col = x % D;
     T* kbp = reinterpret_cast<T*>(a.packed + a.pl.kbar) + size_t(h) * a.nbp * D;
-    kbp[size_t(a.nb) * D + x] = from_f32<T>(0.f);
     T* vbp = reinterpret_cast<T*>(a.packed + a.pl.vbar) + size_t(h) * a.nbp * D;
-    const int ee = x / pad, k = a.nb % kB + x % pad;
-    vbp[(size_t(a.nb / kB) * D + ee) * kB + k] = from_f32<T>(0.f);
+    kbp[last + TL::k(key, col)] = from_f32<T>(0.f);
+    vbp[last + TL::v(key, col)] = from_f32<T>(0.f);
   }
 }
 

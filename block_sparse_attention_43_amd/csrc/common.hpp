@@ -104,6 +104,61 @@ template <class T> struct MmaFor;
 template <> struct MmaFor<uint16_t> { using type = MmaBF16; };
 template <> struct MmaFor<float> { using type = MmaF32; };
 
+// ---------------------------------------------------------------------------
+// Element order of a 64-key tile (64 keys x D columns) in the packed buffers.
+//
+// fp32: K-type tiles are plain rows [key][c], V-type tiles plain Vᵀ rows [e][key].
+// bf16: MFMA operand order for v_mfma_f32_32x32x16_bf16, so that one 16-byte load per
+// lane, 1 KB per wave, is exactly one operand. The tile is two 32-key halves; in a half,
+//   K-type (A operand of Sᵀ = K Qᵀ), fragment ks < D/16: lane 32g + R holds
+//     K[key_of_row(R)][16 ks + 8 g + u], u < 8;
+//   V-type (A operand of Oᵀ += Vᵀ Pᵀ), fragment (et < D/32, ks < 2): lane 32g + l holds
+//     V[16 ks + 8 g + u][32 et + l], u < 8.
+// key_of_row permutes the 32 keys of a half so that Sᵀ accumulator register r of lane
+// half g holds key 16 (r / 8) + 8 g + r % 8: registers [8 ks, 8 ks + 8) are then the
+// B operand (P) of k-step ks of Oᵀ += Vᵀ Pᵀ without any data movement.
+// In both layouts the fastest index runs over 16 bytes of consecutive c (K-type) or
+// consecutive keys (V-type), so a 16-byte chunk is contiguous in either.
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int key_of_row(int R) {        // A row R -> key within the half
+  return 16 * ((4 * (R >> 3) + (R & 3)) >> 3) + 8 * ((R >> 2) & 1) + ((4 * (R >> 3) + (R & 3)) & 7);
+}
+__host__ __device__ constexpr int row_of_key(int k) {        // inverse of key_of_row
+  return 8 * ((8 * (k >> 4) + (k & 7)) >> 2) + 4 * ((k >> 3) & 1) + ((8 * (k >> 4) + (k & 7)) & 3);
+}
+
+template <class T, int D> struct TileLayout;
+template <int D> struct TileLayout<float, D> {
+  __host__ __device__ static constexpr int k(int key, int c) { return key * D + c; }
+  __host__ __device__ static constexpr int v(int key, int e) { return e * 64 + key; }
+  // 16-byte chunk x of a V-type tile in storage order -> (first key, e) it holds
+  __host__ __device__ static constexpr void vchunk(int x, int& key0, int& e) {
+    e = x / 16;
+    key0 = (x % 16) * 4;
+  }
+};
+template <int D> struct TileLayout<uint16_t, D> {
+  __host__ __device__ static constexpr int k(int key, int c) {
+    return ((((key >> 5) * (D / 16) + (c >> 4)) * 64 + 32 * ((c >> 3) & 1) + row_of_key(key & 31)) << 3) + (c & 7);
+  }
+  __host__ __device__ static constexpr int v(int key, int e) {
+    return (((((key >> 5) * (D / 32) + (e >> 5)) * 2 + ((key >> 4) & 1)) * 64 + 32 * ((key >> 3) & 1) + (e & 31)) << 3) +
+           (key & 7);
+  }
+  __host__ __device__ static constexpr void vchunk(int x, int& key0, int& e) {
+    const int lane = x & 63, f = x >> 6;
+    const int half = f / (D / 16), et = (f % (D / 16)) >> 1, ks = f & 1;
+    e = 32 * et + (lane & 31);
+    key0 = 32 * half + 16 * ks + 8 * (lane >> 5);
+  }
+  // 16-byte chunk x of a K-type tile in storage order -> (key, first c) it holds
+  __host__ __device__ static constexpr void kchunk(int x, int& key, int& c0) {
+    const int lane = x & 63, f = x >> 6;
+    key = 32 * (f / (D / 16)) + key_of_row(lane & 31);
+    c0 = 16 * (f % (D / 16)) + 8 * (lane >> 5);
+  }
+};
+
 // Row index -> accumulator row of the 32x32 output:  row(r, g) = 8*(r/4) + 4*g + r%4.
 __device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 

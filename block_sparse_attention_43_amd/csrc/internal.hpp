@@ -10,9 +10,12 @@ constexpr int kB = 64;  // block / tile size handled by the kernels
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Byte offsets inside the packed (kernel-layout) statistics buffer.
+// Byte offsets inside the packed (kernel-layout) statistics buffer. Every region but
+// H̄ is a sequence of 64-key tiles of 64 * d elements; the element order inside a tile
+// is TileLayout<T, d> (common.hpp): plain K rows / Vᵀ rows for fp32, MFMA operand order
+// for bf16. The bf16 layout also carries an operand-order copy of K per block.
 struct PackedLayout {
-  size_t vt, kbar, vbar, hbar, total;
+  size_t kf, vt, kbar, vbar, hbar, total;
   int nb, nbp;
 };
 
@@ -20,11 +23,13 @@ inline PackedLayout packed_layout(size_t elem, int H, int L, int d) {
   PackedLayout p;
   p.nb = L / kB;
   p.nbp = (p.nb + kB - 1) / kB * kB;
+  const size_t tile = size_t(kB) * d * elem;
   size_t o = 0;
-  p.vt = o;   o = align256(o + size_t(H) * p.nb * d * kB * elem);    // [H][nb][d][64]   V^T per block
-  p.kbar = o; o = align256(o + size_t(H) * p.nbp * d * elem);        // [H][nbp][d]      centroids
-  p.vbar = o; o = align256(o + size_t(H) * p.nbp * d * elem);        // [H][nbp/64][d][64] (ΣV/n)^T
-  p.hbar = o; o = align256(o + size_t(H) * d * d * elem);            // [H][d][d]        H̄[e][c]
+  p.kf = o;   o = align256(o + (elem == 2 ? size_t(H) * p.nb * tile : 0));  // [H][nb] K tiles (bf16)
+  p.vt = o;   o = align256(o + size_t(H) * p.nb * tile);                    // [H][nb] Vᵀ tiles
+  p.kbar = o; o = align256(o + size_t(H) * (p.nbp / kB) * tile);            // [H][nbp/64] centroid tiles
+  p.vbar = o; o = align256(o + size_t(H) * (p.nbp / kB) * tile);            // [H][nbp/64] (ΣV/n)ᵀ tiles
+  p.hbar = o; o = align256(o + size_t(H) * d * d * elem);                   // [H][d][d]   H̄[e][c]
   p.total = o;
   return p;
 }
