@@ -124,33 +124,57 @@ void attention_frag_kernel(AttnArgs a) {
   float m[2] = {NEG_INF, NEG_INF}, mtop[2] = {NEG_INF, NEG_INF}, lsum[2], asum[2];
   bool over = false;
 
-  const int n1 = a.K_sel;
-  const int N = n1 + (VIRT ? ngrp : 0);
-
-  // Exact-tile descriptors (block index | valid keys << 16; 0 for an out-of-range index)
-  // are staged in a wave-private LDS table, DCAP tiles at a time. The table lives in this
-  // wave's own hand-over region, which the wave writes only after its loop. Each issue
-  // reads the next tile's descriptor one issue ahead, so the loop never waits on memory
-  // for descriptors; tables are refilled (waiting on memory) only every DCAP tiles.
+  // Exact tiles of this wave. Descriptors (block j | key half << 16 | valid keys << 17)
+  // are staged in a wave-private LDS table that lives in this wave's own hand-over
+  // region (written only after its loop); each issue reads the next descriptor one issue
+  // ahead, so the loop never waits on memory for them.
+  //
+  // When the whole selection fits the table, each wave keeps only useful work: its own
+  // key half of every full block, and half 0 of every other block of at most 32 tokens
+  // (ragged blocks alternate between the waves); out-of-range indices are dropped. The
+  // two partial softmax states are merged at the end, so any split of the keys is exact.
+  // Larger selections are staged DCAP tiles at a time, every block with half kh.
   constexpr int DCAP = XS * 64;
   uint32_t* dtab = reinterpret_cast<uint32_t*>(sX + kh * XS * 64);
   const int32_t* irow = a.idx + (size_t(h) * nb + i) * a.K_sel;
+  const bool compact = a.K_sel <= DCAP;
+  int n1 = a.K_sel;                      // exact tiles of this wave
+  int N = n1 + (VIRT ? ngrp : 0);        // all tiles of this wave
   int dbase = 0;
-  auto fill = [&](int t0) {              // descriptors of exact tiles [t0, t0 + DCAP)
+  auto block_keys = [&](int j) -> int { return a.block_len ? min(max(a.block_len[j], 1), kB) : kB; };
+  auto build_list = [&]() -> int {       // compact table; returns its length
+    const uint64_t below = (uint64_t(1) << lane) - 1u;
+    int written = 0, ragged = 0;
+    for (int s0 = 0; s0 < a.K_sel; s0 += 64) {
+      const int e = s0 + lane;
+      const int j = e < a.K_sel ? irow[e] : -1;
+      const bool valid = j >= 0 && j < nb;
+      const int v = valid ? block_keys(j) : 0;
+      const bool rag = valid && v <= 32;
+      const uint64_t rmask = __ballot(rag);
+      const int rank = ragged + __popcll(rmask & below);
+      const bool mine = valid && (!rag || (rank & 1) == kh);
+      const uint64_t mmask = __ballot(mine);
+      if (mine) {
+        const uint32_t half = rag ? 0u : uint32_t(kh);
+        dtab[written + __popcll(mmask & below)] = uint32_t(j) | (half << 16) | (uint32_t(v) << 17);
+      }
+      written += __popcll(mmask);
+      ragged += __popcll(rmask);
+    }
+    return written;
+  };
+  auto fill = [&](int t0) {              // uncompacted table of tiles [t0, t0 + DCAP)
     const int cnt = min(DCAP, n1 - t0);
     for (int e = lane; e < cnt; e += 64) {
       const int j = irow[t0 + e];
-      uint32_t d = 0u;
-      if (j >= 0 && j < nb) {
-        const int v = a.block_len ? a.block_len[j] : kB;
-        d = uint32_t(j) | (uint32_t(min(max(v, 1), kB)) << 16);
-      }
-      dtab[e] = d;
+      const bool valid = j >= 0 && j < nb;
+      dtab[e] = valid ? uint32_t(j) | (uint32_t(kh) << 16) | (uint32_t(block_keys(j)) << 17) : uint32_t(kh) << 16;
     }
     dbase = t0;
   };
   auto read_desc = [&](int t) -> uint32_t {   // t < n1, t >= dbase
-    if (t - dbase >= DCAP) fill(t);
+    if (!compact && t - dbase >= DCAP) fill(t);
     return dtab[t - dbase];
   };
   uint32_t dnext = 0u;                   // descriptor of the next exact tile to issue
@@ -170,12 +194,13 @@ void attention_frag_kernel(AttnArgs a) {
     int off = kDead, nk = 0;
     if (t < N) {
       if (virt) {
-        off = (t - n1) * TB;
+        off = (t - n1) * TB + kh * HB;
         nk = kB;
       } else {
         const uint32_t d = __builtin_amdgcn_readfirstlane(dnext);
-        nk = int(d >> 16);
-        off = int(d & 0xFFFFu) * TB;
+        const int half = int((d >> 16) & 1u);
+        nk = int(d >> 17) - 32 * half;     // valid keys counted from this half's first key
+        off = int(d & 0xFFFFu) * TB + half * HB;
         if (t + 1 < n1) dnext = read_desc(t + 1);
       }
     }
@@ -200,13 +225,13 @@ void attention_frag_kernel(AttnArgs a) {
     constexpr int P = decltype(pc)::value;
     issue_desc(t, pc);
     const __amdgpu_buffer_rsrc_t r = krsrc(t);
-    const int vo = lane * 16 + toff[P] + kh * HB;
+    const int vo = lane * 16 + toff[P];
     static_for<0, NKD>([&](auto fc) { kst[P][decltype(fc)::value] = frag_at(r, vo, decltype(fc)::value); });
   };
   auto issue_v = [&](int t, auto pc) {
     constexpr int P = decltype(pc)::value;
     const __amdgpu_buffer_rsrc_t r = vrsrc(t);
-    const int vo = lane * 16 + toff[P] + kh * HB;
+    const int vo = lane * 16 + toff[P];
     static_for<0, NVF>([&](auto fc) { vst[P][decltype(fc)::value] = frag_at(r, vo, decltype(fc)::value); });
   };
 
@@ -244,9 +269,9 @@ void attention_frag_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], kLog2e, bb[r]);
       return 1.f;
     }
-    const int nk = njs[P];
-    if (nk < kB) {
-      const int lim = nk - 32 * kh - 8 * g;    // register r holds key 32 kh + 8 g + half_key(r, 0)
+    const int nk = njs[P];                     // valid keys from the first key of this half
+    if (nk < 32) {
+      const int lim = nk - 8 * g;              // register r holds key 8 g + half_key(r, 0) of the half
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (half_key(r, 0) >= lim) s[r] = NEG_INF;
@@ -279,7 +304,7 @@ void attention_frag_kernel(AttnArgs a) {
     // stage that tile n just left, Vᵀ of tile n + NS - 1 into the one tile n - 1 left.
     if constexpr (ST & 1) issue_desc(n + NS, ic<TP>{});
     const __amdgpu_buffer_rsrc_t rk = krsrc(n + NS), rv = vrsrc(n + NS - 1);   // used on odd steps
-    const int vok = lane * 16 + toff[TP] + kh * HB, vov = lane * 16 + toff[LV] + kh * HB;
+    const int vok = lane * 16 + toff[TP], vov = lane * 16 + toff[LV];
     float t0 = 0.f, t1 = 0.f, mx = 0.f, mu = 0.f;
     // Softmax of unit k in 16 slices against the row's fixed reference.
     auto slice = [&](auto vc) {
@@ -359,10 +384,16 @@ void attention_frag_kernel(AttnArgs a) {
     if (N == 0) break;
     // Prologue: descriptors, K of tiles [0, NS), Vᵀ of tiles [0, NS - 1), scores of
     // unit 0. Vᵀ stage NS - 1 and P of "unit -1" are zero, so step 0's PV adds nothing.
-    if (n1 > 0) {
-      fill(0);
-      dnext = read_desc(0);
+    if (a.K_sel > 0) {
+      if (compact) {
+        n1 = build_list();
+        N = n1 + (VIRT ? ngrp : 0);
+      } else {
+        fill(0);
+      }
+      if (n1 > 0) dnext = read_desc(0);
     }
+    if (N == 0) break;
 #pragma unroll
     for (int f = 0; f < NVF; ++f) vst[NS - 1][f] = bf16x8{};
     pb[1][0] = pb[1][1] = bf16x8{};
