@@ -69,7 +69,7 @@ constexpr float kSpan = 32.f;
 
 }  // namespace
 
-template <int D, int MODE>
+template <int D, int MODE, int UPT>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attention_frag_kernel(AttnArgs a) {
   constexpr int NKD = D / 16;            // K fragments per half tile (score k-steps)
@@ -82,9 +82,9 @@ void attention_frag_kernel(AttnArgs a) {
   constexpr float NEG_INF = -__builtin_huge_valf();
   constexpr int kDead = 0x40000000;      // tile offset past every buffer: loads return zeros
   constexpr int XS = HE * 32 + 8;        // floats per lane handed over in the merge
-  // Tiles of K / Vᵀ operands held in registers (loads run NS - 1 tiles ahead); the
-  // modes with virtual tiles need more registers elsewhere and keep two.
-  constexpr int NS = (D == 128 && VIRT) ? 2 : 3;
+  // Tiles of K / Vᵀ operands held in registers (loads run NS - 1 tiles ahead); d = 128
+  // has room for two.
+  constexpr int NS = D == 128 ? 2 : 3;
   using KT = SwizzledTile<D * 2>;
   static_assert(2 * XS * 64 * 4 >= kB * D * 2, "output staging must fit the hand-over buffer");
 
@@ -97,6 +97,9 @@ void attention_frag_kernel(AttnArgs a) {
   const int h = int(lin / uint32_t(nb)), i = int(lin % uint32_t(nb));
   int ni = a.block_len ? a.block_len[i] : kB;
   ni = min(max(ni, 1), kB);
+  // Query tiles of more than 32 rows run with two units per tile, the others with one
+  // (their second query half is all padding); each kind has its own launch.
+  if ((ni > 32) != (UPT == 2)) return;
 
   const uint16_t* Qh = static_cast<const uint16_t*>(a.Q) + size_t(h) * a.L * D;
   const char* kfh = a.packed + a.pl.kf + size_t(h) * nb * TB;
@@ -245,13 +248,16 @@ void attention_frag_kernel(AttnArgs a) {
         const int jj = (n - n1) * kB + 32 * kh + l32;
         float b = NEG_INF, inv = 0.f;
         if (jj < nb && !((bwm[P] >> (jj & 31)) & 1u)) {
+          // Hardware log (v_log_f32, within 1 ulp): the library forms are calls once the
+          // bias code is replicated in every step, and w >= 0 keeps ln(1 + w) accurate
+          // to ~1e-7 absolute, far below the logit's own rounding.
           const int nj = min(max(bwl[P], 1), kB);
-          const float lnn = logf(float(nj));
+          const float lnn = __logf(float(nj));
           float phi = 0.f;
           if constexpr (MODE == MODE_PWT) {
             float w = bww[P];
             if (a.gate && w > lnn) w = 0.f;
-            phi = a.w_linear ? log1pf(w) : w;
+            phi = a.w_linear ? __logf(1.f + w) : w;
           }
           b = (lnn + phi) * kLog2e;
           inv = 1.f / float(nj);
@@ -282,29 +288,35 @@ void attention_frag_kernel(AttnArgs a) {
   f32x16 sb[2];
   bf16x8 pb[2][2];
 
-  // One pipeline step k (unit k = tile k / 2, query half k % 2), ST = k % (2 NS).
+  // One pipeline step k, ST = k % (2 NS). With UPT = 2 units per tile, unit k is
+  // (tile k / 2, query half k % 2); query tiles of at most 32 rows use UPT = 1, one unit
+  // (query half 0) per tile, and skip the all-padding half.
   //
   // The step's matrix work (score MFMAs of unit k + 1, PV MFMAs of unit k - 1,
   // alternating) and its VALU work (softmax of unit k) are laid out as NM groups: MFMA c,
-  // then one fragment load (odd steps) and a slice of the softmax, fenced so that the
-  // in-order wave always has VALU work to issue while an MFMA runs.
+  // then one fragment load (steps that start a tile's loads) and a slice of the softmax,
+  // fenced so that the in-order wave always has VALU work to issue while an MFMA runs.
   constexpr int NM = NKD + NVF;                  // MFMAs per step
-  auto step = [&](int k, auto stc) {
+  auto step = [&](int k, auto uc, auto stc) {
     constexpr int ST = decltype(stc)::value;
-    constexpr int QT = ST & 1, QO = QT ^ 1;        // query half of unit k; of units k -+ 1
-    constexpr int TP = (ST >> 1) % NS;                  // stage of unit k's tile
-    constexpr int SK = ((ST + 1) >> 1) % NS;            // K stage read by the scores of unit k + 1
-    constexpr int SV = ((ST + 2 * NS - 1) >> 1) % NS;   // V stage read by the PV of unit k - 1
-    constexpr int LV = (TP + NS - 1) % NS;              // stage receiving Vᵀ on odd steps
-    const int n = k >> 1;
-    f32x16& sc = sb[QT];
-    f32x16& sn = sb[QO];
+    constexpr int BP = ST & 1, BO = BP ^ 1;                  // buffer of unit k; of units k -+ 1
+    constexpr int QT = UPT == 2 ? BP : 0, QO = UPT == 2 ? BO : 0;   // query halves of the same
+    constexpr int TP = (ST / UPT) % NS;                      // stage of unit k's tile
+    constexpr int SK = ((ST + 1) / UPT) % NS;                // K stage read by the scores of unit k + 1
+    constexpr int SV = ((ST + UPT * NS - 1) / UPT) % NS;     // V stage read by the PV of unit k - 1
+    constexpr bool LOADS = UPT == 1 || (ST & 1);             // steps that stream a tile's operands
+    constexpr int VL = UPT == 2 ? NS - 1 : NS - 2;           // Vᵀ runs VL tiles ahead, K NS
+    constexpr int LV = (TP + VL) % NS;                       // stage receiving Vᵀ
+    const int n = k / UPT;
+    f32x16& sc = sb[BP];
+    f32x16& sn = sb[BO];
     const float scl = prep(sc, n, ic<TP>{}, ic<QT>{});
-    // Odd steps stream operands NS - 1 tiles ahead of use: K of tile n + NS into the
-    // stage that tile n just left, Vᵀ of tile n + NS - 1 into the one tile n - 1 left.
-    if constexpr (ST & 1) issue_desc(n + NS, ic<TP>{});
-    const __amdgpu_buffer_rsrc_t rk = krsrc(n + NS), rv = vrsrc(n + NS - 1);   // used on odd steps
-    const int vok = lane * 16 + toff[TP], vov = lane * 16 + toff[LV];
+    // K of tile n + NS goes into the stage that tile n just left, Vᵀ of tile n + VL into
+    // the one that tile n + VL - NS left.
+    const int vov = lane * 16 + toff[LV];       // read before the K issue may reuse the slot
+    if constexpr (LOADS) issue_desc(n + NS, ic<TP>{});
+    const __amdgpu_buffer_rsrc_t rk = krsrc(n + NS), rv = vrsrc(n + VL);   // used when LOADS
+    const int vok = lane * 16 + toff[TP];
     float t0 = 0.f, t1 = 0.f, mx = 0.f, mu = 0.f;
     // Softmax of unit k in 16 slices against the row's fixed reference.
     auto slice = [&](auto vc) {
@@ -326,13 +338,13 @@ void attention_frag_kernel(AttnArgs a) {
         sc[r] = fast_exp2(fmaf(sc[r], scl, -mu));
         sc[r + 1] = fast_exp2(fmaf(sc[r + 1], scl, -mu));
       } else if constexpr (v == 12) {
-        pb[QT][0] = pack8(sc, 0);
+        pb[BP][0] = pack8(sc, 0);
       } else if constexpr (v == 13) {
-        lsum[QT] = sum8(pb[QT][0], lsum[QT]);
+        lsum[QT] = sum8(pb[BP][0], lsum[QT]);
       } else if constexpr (v == 14) {
-        pb[QT][1] = pack8(sc, 8);
+        pb[BP][1] = pack8(sc, 8);
       } else {
-        lsum[QT] = sum8(pb[QT][1], lsum[QT]);
+        lsum[QT] = sum8(pb[BP][1], lsum[QT]);
       }
     };
     static_for<0, NM>([&](auto cc) {
@@ -342,9 +354,9 @@ void attention_frag_kernel(AttnArgs a) {
         sn = MmaBF16::mma(kst[SK][f], qf[QO][f], f == 0 ? zero16() : sn);
       } else {                                   // PV MFMA v of unit k - 1
         constexpr int v = c >> 1, et = v % NET, ks = v / NET;
-        acc[et][QO] = MmaBF16::mma(vst[SV][2 * et + ks], pb[QO][ks], acc[et][QO]);
+        acc[et][QO] = MmaBF16::mma(vst[SV][2 * et + ks], pb[BO][ks], acc[et][QO]);
       }
-      if constexpr (ST & 1) {
+      if constexpr (LOADS) {
         if constexpr (c < NKD) kst[TP][c] = frag_at(rk, vok, c);
         else vst[LV][c - NKD] = frag_at(rv, vov, c - NKD);
       }
@@ -353,7 +365,7 @@ void attention_frag_kernel(AttnArgs a) {
     });
     // P of unit k is used by the next step's MFMAs and the sums only after the loop;
     // keep them computed here rather than sunk next to those uses.
-    asm volatile("" ::"v"(pb[QT][0]), "v"(pb[QT][1]), "v"(lsum[QT]), "v"(mtop[QT]));
+    asm volatile("" ::"v"(pb[BP][0]), "v"(pb[BP][1]), "v"(lsum[QT]), "v"(mtop[QT]));
 
     if (VIRT && n >= n1) {            // A_t: Σ p / n_j over this lane's virtual tokens
       const float4* ip = reinterpret_cast<const float4*>(&sInvN[kh][8 * g]);
@@ -366,65 +378,71 @@ void attention_frag_kernel(AttnArgs a) {
       asum[QT] = pa;
     }
   };
-  // After the last step: PV of the last unit (query half 1, V stage SV).
-  auto finish = [&](auto svc) {
-    constexpr int SV = decltype(svc)::value;
+  // After the last step: PV of the last unit (its step index mod 2 NS is STL).
+  auto finish = [&](auto uc, auto stlc) {
+    constexpr int STL = decltype(stlc)::value;
+    constexpr int SV = (STL / UPT) % NS, BL = STL & 1, QL = UPT == 2 ? BL : 0;
     static_for<0, 2>([&](auto kc) {
       constexpr int ks = decltype(kc)::value;
 #pragma unroll
-      for (int et = 0; et < NET; ++et) acc[et][1] = MmaBF16::mma(vst[SV][2 * et + ks], pb[1][ks], acc[et][1]);
+      for (int et = 0; et < NET; ++et) acc[et][QL] = MmaBF16::mma(vst[SV][2 * et + ks], pb[BL][ks], acc[et][QL]);
     });
   };
 
-  for (int pass = 0;; ++pass) {
+  // The tile loop for UPT units per tile, run again if some row overflowed its reference.
+  auto run = [&](auto uc) {
+    constexpr int VL = UPT == 2 ? NS - 1 : NS - 2;
+    for (int pass = 0;; ++pass) {
 #pragma unroll
-    for (int et = 0; et < NET; ++et) acc[et][0] = acc[et][1] = zero16();
+      for (int et = 0; et < NET; ++et) acc[et][0] = acc[et][1] = zero16();
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) lsum[qt] = asum[qt] = 0.f;
-    if (N == 0) break;
-    // Prologue: descriptors, K of tiles [0, NS), Vᵀ of tiles [0, NS - 1), scores of
-    // unit 0. Vᵀ stage NS - 1 and P of "unit -1" are zero, so step 0's PV adds nothing.
-    if (a.K_sel > 0) {
-      if (compact) {
-        n1 = build_list();
-        N = n1 + (VIRT ? ngrp : 0);
-      } else {
-        fill(0);
+      for (int qt = 0; qt < 2; ++qt) lsum[qt] = asum[qt] = 0.f;
+      if (N == 0) break;
+      // Prologue: descriptors, K of tiles [0, NS), Vᵀ of tiles [0, VL), scores of unit 0.
+      // Vᵀ stage NS - 1 and P of "unit -1" are zero, so step 0's PV adds nothing.
+      if (a.K_sel > 0) {
+        if (compact) {
+          n1 = build_list();
+          N = n1 + (VIRT ? ngrp : 0);
+        } else {
+          fill(0);
+        }
+        if (n1 > 0) dnext = read_desc(0);
       }
-      if (n1 > 0) dnext = read_desc(0);
-    }
-    if (N == 0) break;
+      if (N == 0) break;
 #pragma unroll
-    for (int f = 0; f < NVF; ++f) vst[NS - 1][f] = bf16x8{};
-    pb[1][0] = pb[1][1] = bf16x8{};
-    static_for<0, NS>([&](auto tc) { issue_k(decltype(tc)::value, tc); });
-    static_for<0, NS - 1>([&](auto tc) { issue_v(decltype(tc)::value, tc); });
-    sb[0] = MmaBF16::mma(kst[0][0], qf[0][0], zero16());
-    static_for<1, NKD>([&](auto fc) {
-      constexpr int f = decltype(fc)::value;
-      sb[0] = MmaBF16::mma(kst[0][f], qf[0][f], sb[0]);
-    });
+      for (int f = 0; f < NVF; ++f) vst[NS - 1][f] = bf16x8{};
+      pb[1][0] = pb[1][1] = bf16x8{};
+      static_for<0, NS>([&](auto tc) { issue_k(decltype(tc)::value, tc); });
+      static_for<0, VL>([&](auto tc) { issue_v(decltype(tc)::value, tc); });
+      sb[0] = MmaBF16::mma(kst[0][0], qf[0][0], zero16());
+      static_for<1, NKD>([&](auto fc) {
+        constexpr int f = decltype(fc)::value;
+        sb[0] = MmaBF16::mma(kst[0][f], qf[0][f], sb[0]);
+      });
 
-    // 2 NS steps (NS tiles) per iteration so every stage index is static; the last
-    // N % NS tiles run after the loop (a single loop exit keeps the register assignment
-    // simple), then the PV of the last unit.
-    const int last = 2 * N;
-    int k = 0;
-    for (; k + 2 * NS <= last; k += 2 * NS)
-      static_for<0, 2 * NS>([&](auto sc) { step(k + decltype(sc)::value, sc); });
-    static_for<0, NS>([&](auto rc) {
-      constexpr int R = decltype(rc)::value;              // tiles left
-      if (last - k == 2 * R) {
-        static_for<0, 2 * R>([&](auto sc) { step(k + decltype(sc)::value, sc); });
-        finish(ic<(R + NS - 1) % NS>{});
-      }
-    });
-    // Some row may have overflowed: run again with every row's true max as reference.
-    if (pass > 0 || !__any(over)) break;
+      // 2 NS steps per iteration so every stage and buffer index is static; the last
+      // steps run after the loop (a single loop exit keeps the register assignment
+      // simple), then the PV of the last unit.
+      const int last = UPT * N;
+      int k = 0;
+      for (; k + 2 * NS <= last; k += 2 * NS)
+        static_for<0, 2 * NS>([&](auto sc) { step(k + decltype(sc)::value, uc, sc); });
+      static_for<0, 2 * NS / UPT>([&](auto rc) {
+        constexpr int R = decltype(rc)::value * UPT;       // steps left
+        if (last - k == R) {
+          static_for<0, R>([&](auto sc) { step(k + decltype(sc)::value, uc, sc); });
+          finish(uc, ic<(R + 2 * NS - 1) % (2 * NS)>{});
+        }
+      });
+      // Some row may have overflowed: run again with every row's true max as reference.
+      if (pass > 0 || !__any(over)) break;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) m[qt] = mtop[qt];
-    over = false;
-  }
+      for (int qt = 0; qt < 2; ++qt) m[qt] = mtop[qt];
+      over = false;
+    }
+  };
+  run(ic<UPT>{});
 
   // Merge the two key halves. Each lane's sums cover its own 16 keys; both lane halves
   // hold the same max. Wave kh finalises Oᵀ tiles [kh HE, kh HE + HE) of both query
@@ -528,15 +546,22 @@ void attention_frag_kernel(AttnArgs a) {
   }
 }
 
+template <int D, int MODE>
+static hipError_t launch_frag_m(const AttnArgs& a, hipStream_t s) {
+  const dim3 grid(unsigned(a.H) * unsigned(a.nb));
+  hipLaunchKernelGGL((attention_frag_kernel<D, MODE, 2>), grid, dim3(128), 0, s, a);
+  // Without block lengths every query tile is full and the second launch would be empty.
+  if (a.block_len) hipLaunchKernelGGL((attention_frag_kernel<D, MODE, 1>), grid, dim3(128), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_frag_d(int mode, const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(unsigned(a.H) * unsigned(a.nb));
   switch (mode) {
-    case MODE_DROP: hipLaunchKernelGGL((attention_frag_kernel<D, MODE_DROP>), grid, dim3(128), 0, s, a); break;
-    case MODE_PISA: hipLaunchKernelGGL((attention_frag_kernel<D, MODE_PISA>), grid, dim3(128), 0, s, a); break;
-    default: hipLaunchKernelGGL((attention_frag_kernel<D, MODE_PWT>), grid, dim3(128), 0, s, a); break;
+    case MODE_DROP: return launch_frag_m<D, MODE_DROP>(a, s);
+    case MODE_PISA: return launch_frag_m<D, MODE_PISA>(a, s);
+    default: return launch_frag_m<D, MODE_PWT>(a, s);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_attention_frag(int mode, const AttnArgs& a, hipStream_t s) {
