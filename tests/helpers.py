@@ -44,6 +44,50 @@ def gpu_run(pisa, inp: synth.Inputs, mode: str, K_sel: int, flags: int = 0, mode
                 cblk=None if st.cblk is None else to_f64(st.cblk))
 
 
+def oracle_selection(inp: synth.Inputs, K_sel: int):
+    """The oracle's own selection and PWT weights for every head, from the seeded inputs
+    only: idx [H, nb, K_sel] (ascending) and w [H, nb, nb] (before the gate)."""
+    from oracle import pisa_oracle as orc
+    bl = inp.layout.block_len
+    idx = np.zeros((inp.H, inp.nb, K_sel), dtype=np.int64)
+    w = np.zeros((inp.H, inp.nb, inp.nb))
+    for h in range(inp.H):
+        st = orc.block_stats(inp.f64("K", h), inp.f64("V", h), 64, bl, per_block=False)
+        pq = orc.pool_queries(inp.f64("Q", h), 64, bl)
+        idx[h] = orc.select_topk(orc.block_scores(pq["qbar"], st["kbar"]), K_sel)
+        w[h] = orc.pooled_w(pq["qsq"], st["sig2"])
+    return idx, w
+
+
+def selection_to_device(idx: np.ndarray, w: np.ndarray, nb: int):
+    """Host selection -> the device tensors the attention call takes: idx int32, the
+    membership bitmask [H, nb, ceil(nb / 32)] and fp32 weights."""
+    H, nq, K_sel = idx.shape
+    nw = (nb + 31) // 32
+    member = np.zeros((H, nq, nw * 32), dtype=bool)
+    hh, ii, kk = np.nonzero((idx >= 0) & (idx < nb))
+    member[hh, ii, idx[hh, ii, kk]] = True
+    mask = np.packbits(member, axis=-1, bitorder="little").view(np.uint32).reshape(H, nq, nw)
+    di = torch.zeros(H, nq, max(K_sel, 1), dtype=torch.int32)
+    di[:, :, :K_sel] = torch.from_numpy(idx.astype(np.int32))
+    return (di.cuda()[:, :, :K_sel],
+            torch.from_numpy(mask.view(np.int32)).cuda(),
+            torch.from_numpy(w.astype(np.float32)).cuda())
+
+
+def gpu_attention_on(pisa, inp: synth.Inputs, K_sel: int, mode: str, idx: np.ndarray, w: np.ndarray,
+                     mode_bits: int = 0, tensors=None, flags: int = 0):
+    """GPU statistics and attention on a given (oracle) selection."""
+    Q, K, V, blt = tensors if tensors is not None else to_device(inp)
+    base = pisa.MODES[mode]
+    st = pisa.block_stats(K, V, blt, flags=flags)
+    di, dm, dw = selection_to_device(idx, w, inp.nb)
+    O, lse = pisa.attention_fwd(Q, K, V, st, di, dm, dw if base == pisa.MODE_PWT else None, K_sel,
+                                base | mode_bits, blt)
+    torch.cuda.synchronize()
+    return dict(O=to_f64(O), lse=to_f64(lse))
+
+
 def rel_l2(a: np.ndarray, b: np.ndarray) -> float:
     den = np.linalg.norm(b)
     return float(np.linalg.norm(a - b) / (den if den > 0 else 1.0))
