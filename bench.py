@@ -56,9 +56,12 @@ def flop_counts(idx: np.ndarray, block_len: np.ndarray, d: int, mode: str) -> di
 
 
 def kernel_source_hash() -> str:
-    p = os.path.join(ROOT, "block_sparse_attention_43_amd", "csrc", "attention_fwd.hip")
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the sources of the bf16 attention kernels (the measured kernel)."""
+    h = hashlib.sha256()
+    for name in ("attention_frag.hip", "common.hpp", "attention.hpp"):
+        with open(os.path.join(ROOT, "block_sparse_attention_43_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload: str):
@@ -269,7 +272,8 @@ def main():
         **dense,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4), "traffic": traffic,
-                     "kernel": "attention_split_kernel (pisa_attention_fwd)",
+                     "kernel": "pisa_attention_fwd: attention_frag_kernel, one launch for query "
+                               "tiles of more than 32 rows and one for the rest",
                      "algorithmic_flops_per_launch": fc["attention"]},
         "cpu_baseline": cpu,
     }
