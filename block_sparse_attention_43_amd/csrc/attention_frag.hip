@@ -224,19 +224,6 @@ void attention_frag_kernel(AttnArgs a) {
   auto krsrc = [&](int t) { return VIRT && t >= n1 ? make_rsrc(kbh, uint32_t(ngrp) * TB) : make_rsrc(kfh, uint32_t(nb) * TB); };
   auto vrsrc = [&](int t) { return VIRT && t >= n1 ? make_rsrc(vbh, uint32_t(ngrp) * TB) : make_rsrc(vth, uint32_t(nb) * TB); };
   auto frag_at = [&](__amdgpu_buffer_rsrc_t r, int vo, int f) { return ld_frag(r, vo + (f & 3) * 1024, (f >> 2) * 4096); };
-  auto issue_k = [&](int t, auto pc) {   // whole tile at once (prologue)
-    constexpr int P = decltype(pc)::value;
-    issue_desc(t, pc);
-    const __amdgpu_buffer_rsrc_t r = krsrc(t);
-    const int vo = lane * 16 + toff[P];
-    static_for<0, NKD>([&](auto fc) { kst[P][decltype(fc)::value] = frag_at(r, vo, decltype(fc)::value); });
-  };
-  auto issue_v = [&](int t, auto pc) {
-    constexpr int P = decltype(pc)::value;
-    const __amdgpu_buffer_rsrc_t r = vrsrc(t);
-    const int vo = lane * 16 + toff[P];
-    static_for<0, NVF>([&](auto fc) { vst[P][decltype(fc)::value] = frag_at(r, vo, decltype(fc)::value); });
-  };
 
   // Scores of unit (tile n, stage P, query half QT) in log2 units or raw: virtual tiles
   // get their bias (-inf for selected blocks and padding) and return scale 1; ragged
@@ -297,6 +284,8 @@ void attention_frag_kernel(AttnArgs a) {
   // then one fragment load (steps that start a tile's loads) and a slice of the softmax,
   // fenced so that the in-order wave always has VALU work to issue while an MFMA runs.
   constexpr int NM = NKD + NVF;                  // MFMAs per step
+  // Vᵀ fragment read by the PV MFMA of group 2 v.
+  auto vfrag = [](int v) constexpr { return 2 * (v % NET) + v / NET; };
   auto step = [&](int k, auto uc, auto stc) {
     constexpr int ST = decltype(stc)::value;
     constexpr int BP = ST & 1, BO = BP ^ 1;                  // buffer of unit k; of units k -+ 1
@@ -356,9 +345,11 @@ void attention_frag_kernel(AttnArgs a) {
         constexpr int v = c >> 1, et = v % NET, ks = v / NET;
         acc[et][QO] = MmaBF16::mma(vst[SV][2 * et + ks], pb[BO][ks], acc[et][QO]);
       }
+      // Each group loads the fragment that the same group of a later step consumes, so
+      // every fragment has the same lead.
       if constexpr (LOADS) {
-        if constexpr (c < NKD) kst[TP][c] = frag_at(rk, vok, c);
-        else vst[LV][c - NKD] = frag_at(rv, vov, c - NKD);
+        if constexpr (c & 1) kst[TP][c >> 1] = frag_at(rk, vok, c >> 1);
+        else vst[LV][vfrag(c >> 1)] = frag_at(rv, vov, vfrag(c >> 1));
       }
       static_for<c * 16 / NM, (c + 1) * 16 / NM>(slice);
       __builtin_amdgcn_sched_barrier(0);
@@ -398,8 +389,10 @@ void attention_frag_kernel(AttnArgs a) {
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) lsum[qt] = asum[qt] = 0.f;
       if (N == 0) break;
-      // Prologue: descriptors, K of tiles [0, NS), Vᵀ of tiles [0, VL), scores of unit 0.
-      // Vᵀ stage NS - 1 and P of "unit -1" are zero, so step 0's PV adds nothing.
+      // Prologue: descriptors, K of tiles [0, NS), Vᵀ of tiles [0, VL), scores of unit 0,
+      // issued as the loading steps of tiles -NS .. -1 would issue them (the loop's
+      // memory waits then hold from its first step on). Vᵀ stage NS - 1 and P of
+      // "unit -1" are zero, so step 0's PV adds nothing.
       if (a.K_sel > 0) {
         if (compact) {
           n1 = build_list();
@@ -410,11 +403,20 @@ void attention_frag_kernel(AttnArgs a) {
         if (n1 > 0) dnext = read_desc(0);
       }
       if (N == 0) break;
-#pragma unroll
-      for (int f = 0; f < NVF; ++f) vst[NS - 1][f] = bf16x8{};
       pb[1][0] = pb[1][1] = bf16x8{};
-      static_for<0, NS>([&](auto tc) { issue_k(decltype(tc)::value, tc); });
-      static_for<0, VL>([&](auto tc) { issue_v(decltype(tc)::value, tc); });
+      static_for<0, NS>([&](auto pc) {
+        constexpr int P = decltype(pc)::value, TV = P - NS + VL, LVP = (P + VL) % NS;
+        issue_desc(P, pc);
+        const __amdgpu_buffer_rsrc_t rk = krsrc(P), rv = vrsrc(TV < 0 ? 0 : TV);
+        const int vok = lane * 16 + toff[P];
+        const int vov = lane * 16 + (TV < 0 ? kDead : toff[TV < 0 ? 0 : TV % NS]);   // tile < 0: zeros
+        static_for<0, NM>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          if constexpr (c & 1) kst[P][c >> 1] = frag_at(rk, vok, c >> 1);
+          else vst[LVP][vfrag(c >> 1)] = frag_at(rv, vov, vfrag(c >> 1));
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      });
       sb[0] = MmaBF16::mma(kst[0][0], qf[0][0], zero16());
       static_for<1, NKD>([&](auto fc) {
         constexpr int f = decltype(fc)::value;
