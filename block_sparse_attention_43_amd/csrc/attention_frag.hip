@@ -5,7 +5,7 @@
 // Attention and PWT sections): exact softmax terms of every key of the selected blocks,
 // one virtual token per unselected block (logit q·k̄_j + ln n_j + φ_ij, value ΣV_j / n_j,
 // its weight e^{q·k̄_j + φ} also summed into A_t), then N_t += A_t H̄ q_t and
-// o_t = N_t / D_t, all under one online softmax.
+// o_t = N_t / D_t, all under one softmax.
 //
 // Organisation, chosen for gfx950:
 // * One workgroup of two waves per 64-row query tile. Wave w takes key half w (32 keys)
@@ -14,20 +14,25 @@
 //   once, and the two halves' softmax states are merged at the end.
 // * K, Vᵀ, centroid and mean-value tiles are stored in MFMA operand order (TileLayout),
 //   so a wave streams its 8 KB + 8 KB of a tile with 1 KB buffer loads straight into
-//   operand registers, about one tile ahead of use. The main loop has no barrier and
-//   touches LDS only for the bias of virtual tiles.
+//   operand registers, two steps ahead of use. The main loop has no barrier.
 // * One wave per SIMD holds Q (both query halves), the D x 64 accumulators and two tiles
 //   of operands. MFMA and VALU work overlap inside the wave by software pipelining over
 //   units u = (tile u / 2, query half u % 2): step k issues the score MFMAs of unit k + 1
 //   and the PV MFMAs of unit k - 1 while the VALU runs the softmax of unit k.
+// * Everything that depends on the key alone enters the scores through the accumulator
+//   input of the first score MFMA: 0 / -inf for the valid / padding keys of exact tiles,
+//   ln n_j + φ_ij (or -inf for selected blocks) for virtual tokens. These 32-key rows
+//   live in LDS (a fixed table of masks, and per wave a ring of virtual-tile rows filled
+//   ahead of use) and are read one step before the scores that add them, so the softmax
+//   is the same short sequence of exp2, bf16 packing and v_dot2 sums for every tile.
 // * Exact-tile descriptors (block index, valid keys) are staged in LDS per wave and read
 //   one issue ahead of use.
-// * No rescaling inside the loop: each row's exponentials are taken against a fixed
-//   reference, the first finite unit max of that row (the sums are still zero then).
-//   A row whose later logits exceed the reference by more than kSpan (log2 units) could
-//   overflow; the wave then runs its tiles again with the row's true max as reference,
-//   which bounds every exponential by 1. The accumulators are therefore touched by MFMA
-//   only and stay in accumulation registers for the whole loop.
+// * No rescaling and no running max inside the loop: each row's exponentials are taken
+//   against a fixed reference, the max of the row's first unit (each wave its own). Any
+//   exponential above 2^60 leaves the row's sum above 2^60; a wave with such a row (or
+//   one whose first unit had no valid key and whose sum fell below 2^-60) computes the
+//   true row max in a score-only pass and runs its tiles again against it, which bounds
+//   every exponential by 1. The accumulators are therefore touched by MFMA only.
 #include "attention.hpp"
 #include "common.hpp"
 #include "internal.hpp"
@@ -37,35 +42,15 @@ namespace {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Key (within the 32-key half) held by Sᵀ accumulator register r of lane half g.
-__device__ __forceinline__ constexpr int half_key(int r, int g) { return 16 * (r >> 3) + 8 * g + (r & 7); }
-
 __device__ __forceinline__ bf16x8 ld_frag(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-
-__device__ __forceinline__ bf16x8 pack8(const f32x16& v, int off) {
-  bf16x8 r;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) r[u] = static_cast<__bf16>(v[off + u]);
-  return r;
-}
-
-// acc + Σ of the 8 bf16 values (v_dot2 against (1, 1), fp32 accumulation).
-__device__ __forceinline__ float sum8(bf16x8 v, float acc) {
-  const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
 }
 
 template <int I>
 using ic = std::integral_constant<int, I>;
 
-// Largest logit excess over the reference (log2 units) accepted without a second pass:
-// exponentials stay <= 2^32, so sums over up to 2^21 keys of values below 2^70 are finite.
-constexpr float kSpan = 32.f;
+// Sums beyond these bounds send a wave to the second pass (see above).
+constexpr float kSumHi = 0x1p60f, kSumLo = 0x1p-60f;
 
 }  // namespace
 
@@ -85,13 +70,18 @@ void attention_frag_kernel(AttnArgs a) {
   // Tiles of K / Vᵀ operands held in registers (loads run NS - 1 tiles ahead); d = 128
   // has room for two.
   constexpr int NS = D == 128 ? 2 : 3;
+  // Bias rows: 33 mask rows (row nk: keys < nk get 0, the others -inf), then per wave a
+  // ring of VR virtual-tile rows (32 fp32 biases ln n_j + φ, then 32 bf16 weights 1 / n_j),
+  // refilled VH tiles at a time.
+  constexpr int VR = 32, VH = 16, MROWS = 33;
   using KT = SwizzledTile<D * 2>;
   static_assert(2 * XS * 64 * 4 >= kB * D * 2, "output staging must fit the hand-over buffer");
 
   __shared__ __align__(16) float sX[2 * XS * 64];
-  __shared__ __align__(16) float sBias[2][32], sInvN[2][32];
+  __shared__ __align__(16) float sRow[MROWS + (VIRT ? 2 * VR : 0)][64];
 
-  const int lane = threadIdx.x & 63, kh = threadIdx.x >> 6, g = lane >> 5, l32 = lane & 31;
+  const int lane = threadIdx.x & 63, g = lane >> 5, l32 = lane & 31;
+  const int kh = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, kept scalar
   const int nb = a.nb, ngrp = a.nbp / kB;
   const uint32_t lin = xcd_remap(blockIdx.x, gridDim.x);
   const int h = int(lin / uint32_t(nb)), i = int(lin % uint32_t(nb));
@@ -123,9 +113,13 @@ void attention_frag_kernel(AttnArgs a) {
     }
   }
 
+  // Mask rows, written in full by each wave (the same values), so no barrier is needed.
+  for (int e = lane; e < MROWS * 32; e += 64) sRow[e >> 5][e & 31] = (e & 31) < (e >> 5) ? 0.f : NEG_INF;
+
   f32x16 acc[NET][2];
-  float m[2] = {NEG_INF, NEG_INF}, mtop[2] = {NEG_INF, NEG_INF}, lsum[2], asum[2];
-  bool over = false;
+  // Per query half: the exponent reference (log2 units), Σ p and Σ p / n_j over virtual
+  // tokens (A_t), each over this lane's 16 keys.
+  float mu[2] = {0.f, 0.f}, lsum[2], asum[2];
 
   // Exact tiles of this wave. Descriptors (block j | key half << 16 | valid keys << 17)
   // are staged in a wave-private LDS table that lives in this wave's own hand-over
@@ -180,100 +174,98 @@ void attention_frag_kernel(AttnArgs a) {
     if (!compact && t - dbase >= DCAP) fill(t);
     return dtab[t - dbase];
   };
+
+  // Virtual-tile rows of tiles [t0, t0 + cnt) into the ring (slot (t - n1) mod VR): lane
+  // half g takes every other tile, lane l32 one key of this wave's half of the group.
+  auto vrow = [&](int t) { return MROWS + kh * VR + ((t - n1) & (VR - 1)); };
+  auto vfill = [&](int t0, int cnt) {
+    for (int u0 = 0; u0 < cnt; u0 += 2) {
+      const int u = u0 + g, t = t0 + u;
+      const int jj = (t - n1) * kB + 32 * kh + l32;
+      float bias = NEG_INF, inv = 0.f;
+      if (u < cnt && jj < nb && !((mrow[jj >> 5] >> (jj & 31)) & 1u)) {
+        // Hardware log (v_log_f32, within 1 ulp): w >= 0 keeps ln(1 + w) accurate to
+        // ~1e-7 absolute, far below the logit's own rounding.
+        const int nj = block_keys(jj);
+        const float lnn = __logf(float(nj));
+        float phi = 0.f;
+        if constexpr (MODE == MODE_PWT) {
+          float w = wrow[jj];
+          if (a.gate && w > lnn) w = 0.f;
+          phi = a.w_linear ? __logf(1.f + w) : w;
+        }
+        bias = lnn + phi;
+        inv = __builtin_amdgcn_rcpf(float(nj));
+      }
+      if (u < cnt) {
+        sRow[vrow(t)][l32] = bias;
+        reinterpret_cast<__bf16*>(&sRow[vrow(t)][32])[l32] = static_cast<__bf16>(inv);
+      }
+    }
+  };
+  // The 16 biases of a row this lane adds, in Sᵀ accumulator order: register r of lane
+  // half g holds key 16 (r / 8) + 8 g + r % 8.
+  auto read_row = [&](int row) -> f32x16 {
+    const float4* p = reinterpret_cast<const float4*>(&sRow[row][8 * g]);
+    const float4 x0 = p[0], x1 = p[1], x2 = p[4], x3 = p[5];
+    f32x16 c;
+    c[0] = x0.x; c[1] = x0.y; c[2] = x0.z; c[3] = x0.w;
+    c[4] = x1.x; c[5] = x1.y; c[6] = x1.z; c[7] = x1.w;
+    c[8] = x2.x; c[9] = x2.y; c[10] = x2.z; c[11] = x2.w;
+    c[12] = x3.x; c[13] = x3.y; c[14] = x3.z; c[15] = x3.w;
+    return c;
+  };
+  // The matching 1 / n_j weights of a virtual row, as the bf16 pairs of P.
+  auto read_inv = [&](int row, bf16x8 (&w)[2]) {
+    const bf16x8* p = reinterpret_cast<const bf16x8*>(&sRow[row][32 + 4 * g]);
+    w[0] = p[0];
+    w[1] = p[2];
+  };
+
   uint32_t dnext = 0u;                   // descriptor of the next exact tile to issue
   // Operand ring: the K and Vᵀ registers of NS tiles. Stage s holds tiles t with t % NS == s.
   bf16x8 kst[NS][NKD], vst[NS][NVF];
-  int toff[NS], njs[NS];
-  uint32_t bwm[NS];
-  int bwl[NS];
-  float bww[NS];
+  int toff[NS], crow[NS];
 
-  // Tile t's source (stage P = t % NS): offset and valid-key count from its descriptor,
-  // the descriptor pipeline advanced, and for virtual tiles the raw inputs of this
-  // wave's 32 biases. The fragment loads themselves are spread over the step.
+  // Tile t's source (stage P = t % NS): fragment offset and bias row from its descriptor,
+  // and the descriptor pipeline advanced. The fragment loads themselves are spread over
+  // the step.
   auto issue_desc = [&](int t, auto pc) {
     constexpr int P = decltype(pc)::value;
-    const bool virt = VIRT && t >= n1;
-    int off = kDead, nk = 0;
+    int off = kDead, row = 0;
     if (t < N) {
-      if (virt) {
+      if (VIRT && t >= n1) {
         off = (t - n1) * TB + kh * HB;
-        nk = kB;
+        row = vrow(t);
       } else {
         const uint32_t d = __builtin_amdgcn_readfirstlane(dnext);
         const int half = int((d >> 16) & 1u);
-        nk = int(d >> 17) - 32 * half;     // valid keys counted from this half's first key
         off = int(d & 0xFFFFu) * TB + half * HB;
+        row = min(max(int(d >> 17) - 32 * half, 0), 32);   // valid keys from this half's first
         if (t + 1 < n1) dnext = read_desc(t + 1);
       }
     }
     toff[P] = off;
-    njs[P] = nk;
-    if constexpr (VIRT) {
-      const int grp = min(max(t - n1, 0), ngrp - 1);
-      const int jj = min(grp * kB + 32 * kh + l32, nb - 1);
-      bwm[P] = mrow[jj >> 5];
-      bwl[P] = a.block_len ? a.block_len[jj] : kB;
-      if constexpr (MODE == MODE_PWT) bww[P] = wrow[jj];
-    }
-    // These loads stay ahead of the step's tile loads, so that reading them at the next
-    // issue waits only for older loads.
+    crow[P] = row;
     __builtin_amdgcn_sched_barrier(0);
   };
   // Buffer resource and lane offset of tile t's K (or Vᵀ) fragments in stage P.
   auto krsrc = [&](int t) { return VIRT && t >= n1 ? make_rsrc(kbh, uint32_t(ngrp) * TB) : make_rsrc(kfh, uint32_t(nb) * TB); };
   auto vrsrc = [&](int t) { return VIRT && t >= n1 ? make_rsrc(vbh, uint32_t(ngrp) * TB) : make_rsrc(vth, uint32_t(nb) * TB); };
   auto frag_at = [&](__amdgpu_buffer_rsrc_t r, int vo, int f) { return ld_frag(r, vo + (f & 3) * 1024, (f >> 2) * 4096); };
-
-  // Scores of unit (tile n, stage P, query half QT) in log2 units or raw: virtual tiles
-  // get their bias (-inf for selected blocks and padding) and return scale 1; ragged
-  // exact blocks mask their padding keys and return scale log2(e).
-  auto prep = [&](f32x16& s, int n, auto pc, auto qc) -> float {
-    constexpr int P = decltype(pc)::value, QT = decltype(qc)::value;
-    if (VIRT && n >= n1) {
-      if constexpr (QT == 0) {
-        const int jj = (n - n1) * kB + 32 * kh + l32;
-        float b = NEG_INF, inv = 0.f;
-        if (jj < nb && !((bwm[P] >> (jj & 31)) & 1u)) {
-          // Hardware log (v_log_f32, within 1 ulp): the library forms are calls once the
-          // bias code is replicated in every step, and w >= 0 keeps ln(1 + w) accurate
-          // to ~1e-7 absolute, far below the logit's own rounding.
-          const int nj = min(max(bwl[P], 1), kB);
-          const float lnn = __logf(float(nj));
-          float phi = 0.f;
-          if constexpr (MODE == MODE_PWT) {
-            float w = bww[P];
-            if (a.gate && w > lnn) w = 0.f;
-            phi = a.w_linear ? __logf(1.f + w) : w;
-          }
-          b = (lnn + phi) * kLog2e;
-          inv = 1.f / float(nj);
-        }
-        if (g == 0) {
-          sBias[kh][l32] = b;
-          sInvN[kh][l32] = inv;
-        }
-      }
-      const float4* bp = reinterpret_cast<const float4*>(&sBias[kh][8 * g]);
-      const float4 b0 = bp[0], b1 = bp[1], b2 = bp[4], b3 = bp[5];
-      const float bb[16] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w,
-                            b2.x, b2.y, b2.z, b2.w, b3.x, b3.y, b3.z, b3.w};
+  // Exponent reference from one unit's scores: its row max in log2 units, 0 if empty.
+  auto ref_of = [&](const f32x16& s) -> float {
+    float x = s[0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], kLog2e, bb[r]);
-      return 1.f;
-    }
-    const int nk = njs[P];                     // valid keys from the first key of this half
-    if (nk < 32) {
-      const int lim = nk - 8 * g;              // register r holds key 8 g + half_key(r, 0) of the half
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (half_key(r, 0) >= lim) s[r] = NEG_INF;
-    }
-    return kLog2e;
+    for (int r = 1; r < 16; ++r) x = fmaxf(x, s[r]);
+    x = max_halves(x);
+    return x > NEG_INF ? x * kLog2e : 0.f;
   };
 
   f32x16 sb[2];
+  f32x16 c0;                             // bias row of the tile whose scores come next
   bf16x8 pb[2][2];
+  const bf16x2 one2 = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
   // One pipeline step k, ST = k % (2 NS). With UPT = 2 units per tile, unit k is
   // (tile k / 2, query half k % 2); query tiles of at most 32 rows use UPT = 1, one unit
@@ -286,7 +278,7 @@ void attention_frag_kernel(AttnArgs a) {
   constexpr int NM = NKD + NVF;                  // MFMAs per step
   // Vᵀ fragment read by the PV MFMA of group 2 v.
   auto vfrag = [](int v) constexpr { return 2 * (v % NET) + v / NET; };
-  auto step = [&](int k, auto uc, auto stc) {
+  auto step = [&](int k, auto stc) {
     constexpr int ST = decltype(stc)::value;
     constexpr int BP = ST & 1, BO = BP ^ 1;                  // buffer of unit k; of units k -+ 1
     constexpr int QT = UPT == 2 ? BP : 0, QO = UPT == 2 ? BO : 0;   // query halves of the same
@@ -296,51 +288,44 @@ void attention_frag_kernel(AttnArgs a) {
     constexpr bool LOADS = UPT == 1 || (ST & 1);             // steps that stream a tile's operands
     constexpr int VL = UPT == 2 ? NS - 1 : NS - 2;           // Vᵀ runs VL tiles ahead, K NS
     constexpr int LV = (TP + VL) % NS;                       // stage receiving Vᵀ
+    // Steps whose score MFMAs are the last to add the current bias row load the next one
+    // (tile n + 1, or n + 2 with one unit per tile) once the first score MFMA has read it.
+    constexpr bool CLOAD = UPT == 1 || (ST & 1) == 0;
+    constexpr int CT = UPT == 2 ? 1 : 2;
+    constexpr int CS = (ST / UPT + CT) % NS;
     const int n = k / UPT;
     f32x16& sc = sb[BP];
     f32x16& sn = sb[BO];
-    const float scl = prep(sc, n, ic<TP>{}, ic<QT>{});
     // K of tile n + NS goes into the stage that tile n just left, Vᵀ of tile n + VL into
     // the one that tile n + VL - NS left.
     const int vov = lane * 16 + toff[LV];       // read before the K issue may reuse the slot
     if constexpr (LOADS) issue_desc(n + NS, ic<TP>{});
+    if constexpr (VIRT && CLOAD) {
+      const int tc = n + CT;                    // refill the ring half that tile tc opens
+      if (tc < N && tc - n1 >= VR && ((tc - n1) & (VH - 1)) == 0) vfill(tc, min(VH, N - tc));
+    }
+    const int crw = crow[CS];
     const __amdgpu_buffer_rsrc_t rk = krsrc(n + NS), rv = vrsrc(n + VL);   // used when LOADS
     const int vok = lane * 16 + toff[TP];
-    float t0 = 0.f, t1 = 0.f, mx = 0.f, mu = 0.f;
-    // Softmax of unit k in 16 slices against the row's fixed reference.
-    auto slice = [&](auto vc) {
-      constexpr int v = decltype(vc)::value;
-      if constexpr (v == 0) {
-        t0 = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-      } else if constexpr (v == 1) {
-        t1 = fmaxf(fmaxf(fmaxf(sc[8], sc[9]), fmaxf(sc[10], sc[11])), fmaxf(fmaxf(sc[12], sc[13]), fmaxf(sc[14], sc[15])));
-      } else if constexpr (v == 2) {
-        mx = max_halves(fmaxf(t0, t1)) * scl;
-      } else if constexpr (v == 3) {
-        const float mn = m[QT] == NEG_INF ? mx : m[QT];
-        m[QT] = mn;
-        mtop[QT] = fmaxf(mtop[QT], mx);
-        over |= mx > mn + kSpan;
-        mu = mn == NEG_INF ? 0.f : mn;
-      } else if constexpr (v < 12) {
-        constexpr int r = 2 * (v - 4);
-        sc[r] = fast_exp2(fmaf(sc[r], scl, -mu));
-        sc[r + 1] = fast_exp2(fmaf(sc[r + 1], scl, -mu));
-      } else if constexpr (v == 12) {
-        pb[BP][0] = pack8(sc, 0);
-      } else if constexpr (v == 13) {
-        lsum[QT] = sum8(pb[BP][0], lsum[QT]);
-      } else if constexpr (v == 14) {
-        pb[BP][1] = pack8(sc, 8);
-      } else {
-        lsum[QT] = sum8(pb[BP][1], lsum[QT]);
-      }
+    const float nmu = -mu[QT];
+    // Softmax of unit k against the row's fixed reference: element r's exponential at
+    // group r NM / 16, each pair packed to bf16 two slots later and summed (v_dot2, the
+    // same bf16 values the PV MFMA reads) one slot after that.
+    auto pack = [&](auto dc) {
+      constexpr int dd = decltype(dc)::value;
+      pb[BP][dd >> 2][2 * (dd & 3)] = static_cast<__bf16>(sc[2 * dd]);
+      pb[BP][dd >> 2][2 * (dd & 3) + 1] = static_cast<__bf16>(sc[2 * dd + 1]);
+    };
+    auto total = [&](auto dc) {
+      constexpr int dd = decltype(dc)::value;
+      const bf16x2 pr = {pb[BP][dd >> 2][2 * (dd & 3)], pb[BP][dd >> 2][2 * (dd & 3) + 1]};
+      lsum[QT] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, lsum[QT], false);
     };
     static_for<0, NM>([&](auto cc) {
       constexpr int c = decltype(cc)::value;
       if constexpr (c & 1) {                     // score MFMA f of unit k + 1
         constexpr int f = c >> 1;
-        sn = MmaBF16::mma(kst[SK][f], qf[QO][f], f == 0 ? zero16() : sn);
+        sn = MmaBF16::mma(kst[SK][f], qf[QO][f], f == 0 ? c0 : sn);
       } else {                                   // PV MFMA v of unit k - 1
         constexpr int v = c >> 1, et = v % NET, ks = v / NET;
         acc[et][QO] = MmaBF16::mma(vst[SV][2 * et + ks], pb[BO][ks], acc[et][QO]);
@@ -351,26 +336,41 @@ void attention_frag_kernel(AttnArgs a) {
         if constexpr (c & 1) kst[TP][c >> 1] = frag_at(rk, vok, c >> 1);
         else vst[LV][vfrag(c >> 1)] = frag_at(rv, vov, vfrag(c >> 1));
       }
-      static_for<c * 16 / NM, (c + 1) * 16 / NM>(slice);
+      if constexpr (CLOAD && c == 4) c0 = read_row(crw);
+      static_for<0, 16>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        if constexpr (r * NM / 16 == c) sc[r] = fast_exp2(fmaf(sc[r], kLog2e, nmu));
+      });
+      static_for<0, 8>([&](auto dc) {
+        constexpr int dd = decltype(dc)::value;
+        if constexpr ((2 * dd + 2) * NM / 16 == c) pack(dc);
+        if constexpr ((2 * dd + 3) * NM / 16 == c) total(dc);
+      });
       __builtin_amdgcn_sched_barrier(0);
+    });
+    static_for<0, 8>([&](auto dc) {
+      constexpr int dd = decltype(dc)::value;
+      if constexpr ((2 * dd + 2) * NM / 16 >= NM) pack(dc);
+      if constexpr ((2 * dd + 3) * NM / 16 >= NM) total(dc);
     });
     // P of unit k is used by the next step's MFMAs and the sums only after the loop;
     // keep them computed here rather than sunk next to those uses.
-    asm volatile("" ::"v"(pb[BP][0]), "v"(pb[BP][1]), "v"(lsum[QT]), "v"(mtop[QT]));
+    asm volatile("" ::"v"(pb[BP][0]), "v"(pb[BP][1]), "v"(lsum[QT]));
 
     if (VIRT && n >= n1) {            // A_t: Σ p / n_j over this lane's virtual tokens
-      const float4* ip = reinterpret_cast<const float4*>(&sInvN[kh][8 * g]);
-      const float4 c0 = ip[0], c1 = ip[1], c2 = ip[4], c3 = ip[5];
-      const float cc[16] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w,
-                            c2.x, c2.y, c2.z, c2.w, c3.x, c3.y, c3.z, c3.w};
+      bf16x8 iw[2];
+      read_inv(vrow(n), iw);
       float pa = asum[QT];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) pa = fmaf(sc[r], cc[r], pa);
+      static_for<0, 8>([&](auto dc) {
+        constexpr int dd = decltype(dc)::value, x = dd >> 2, y = 2 * (dd & 3);
+        const bf16x2 pr = {pb[BP][x][y], pb[BP][x][y + 1]}, wr = {iw[x][y], iw[x][y + 1]};
+        pa = __builtin_amdgcn_fdot2_f32_bf16(pr, wr, pa, false);
+      });
       asum[QT] = pa;
     }
   };
   // After the last step: PV of the last unit (its step index mod 2 NS is STL).
-  auto finish = [&](auto uc, auto stlc) {
+  auto finish = [&](auto stlc) {
     constexpr int STL = decltype(stlc)::value;
     constexpr int SV = (STL / UPT) % NS, BL = STL & 1, QL = UPT == 2 ? BL : 0;
     static_for<0, 2>([&](auto kc) {
@@ -380,8 +380,48 @@ void attention_frag_kernel(AttnArgs a) {
     });
   };
 
-  // The tile loop for UPT units per tile, run again if some row overflowed its reference.
-  auto run = [&](auto uc) {
+  // Score-only pass over this wave's tiles: the true max of every row (log2 units) as the
+  // new reference. Taken only after an out-of-range sum, so it is kept simple.
+  auto max_pass = [&]() {
+    float mt[2] = {NEG_INF, NEG_INF};
+    if (!compact && n1 > 0) fill(0);
+    for (int t = 0; t < N; ++t) {
+      int off, row;
+      __amdgpu_buffer_rsrc_t r;
+      if (VIRT && t >= n1) {
+        if (((t - n1) & (VH - 1)) == 0) vfill(t, min(VH, N - t));
+        off = (t - n1) * TB + kh * HB;
+        row = vrow(t);
+        r = make_rsrc(kbh, uint32_t(ngrp) * TB);
+      } else {
+        const uint32_t d = __builtin_amdgcn_readfirstlane(read_desc(t));
+        const int half = int((d >> 16) & 1u);
+        off = int(d & 0xFFFFu) * TB + half * HB;
+        row = min(max(int(d >> 17) - 32 * half, 0), 32);
+        r = make_rsrc(kfh, uint32_t(nb) * TB);
+      }
+      bf16x8 kk[NKD];
+#pragma unroll
+      for (int f = 0; f < NKD; ++f) kk[f] = frag_at(r, lane * 16 + off, f);
+      const f32x16 cb = read_row(row);
+#pragma unroll
+      for (int qt = 0; qt < UPT; ++qt) {
+        f32x16 s = cb;
+#pragma unroll
+        for (int f = 0; f < NKD; ++f) s = MmaBF16::mma(kk[f], qf[qt][f], s);
+        float x = s[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) x = fmaxf(x, s[e]);
+        mt[qt] = fmaxf(mt[qt], max_halves(x));
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) mu[qt] = mt[qt] > NEG_INF ? mt[qt] * kLog2e : 0.f;
+  };
+
+  // The tile loop for UPT units per tile; a wave with an out-of-range row sum runs it
+  // again against the rows' true maxima.
+  auto run = [&]() {
     constexpr int VL = UPT == 2 ? NS - 1 : NS - 2;
     for (int pass = 0;; ++pass) {
 #pragma unroll
@@ -389,10 +429,10 @@ void attention_frag_kernel(AttnArgs a) {
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) lsum[qt] = asum[qt] = 0.f;
       if (N == 0) break;
-      // Prologue: descriptors, K of tiles [0, NS), Vᵀ of tiles [0, VL), scores of unit 0,
-      // issued as the loading steps of tiles -NS .. -1 would issue them (the loop's
-      // memory waits then hold from its first step on). Vᵀ stage NS - 1 and P of
-      // "unit -1" are zero, so step 0's PV adds nothing.
+      // Prologue: descriptors, virtual rows, K of tiles [0, NS), Vᵀ of tiles [0, VL),
+      // scores of unit 0, issued as the loading steps of tiles -NS .. -1 would issue them
+      // (the loop's memory waits then hold from its first step on). Vᵀ stage NS - 1 and
+      // P of "unit -1" are zero, so step 0's PV adds nothing.
       if (a.K_sel > 0) {
         if (compact) {
           n1 = build_list();
@@ -403,6 +443,9 @@ void attention_frag_kernel(AttnArgs a) {
         if (n1 > 0) dnext = read_desc(0);
       }
       if (N == 0) break;
+      if constexpr (VIRT) {
+        if (N > n1) vfill(n1, min(VR, N - n1));
+      }
       pb[1][0] = pb[1][1] = bf16x8{};
       static_for<0, NS>([&](auto pc) {
         constexpr int P = decltype(pc)::value, TV = P - NS + VL, LVP = (P + VL) % NS;
@@ -417,11 +460,24 @@ void attention_frag_kernel(AttnArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         });
       });
-      sb[0] = MmaBF16::mma(kst[0][0], qf[0][0], zero16());
+      c0 = read_row(crow[0]);
+      sb[0] = MmaBF16::mma(kst[0][0], qf[0][0], c0);
       static_for<1, NKD>([&](auto fc) {
         constexpr int f = decltype(fc)::value;
         sb[0] = MmaBF16::mma(kst[0][f], qf[0][f], sb[0]);
       });
+      if (pass == 0) {
+        mu[0] = ref_of(sb[0]);
+        if constexpr (UPT == 2) {
+          f32x16 s1 = MmaBF16::mma(kst[0][0], qf[1][0], c0);
+          static_for<1, NKD>([&](auto fc) {
+            constexpr int f = decltype(fc)::value;
+            s1 = MmaBF16::mma(kst[0][f], qf[1][f], s1);
+          });
+          mu[1] = ref_of(s1);
+        }
+      }
+      if constexpr (UPT == 1) c0 = read_row(crow[1]);
 
       // 2 NS steps per iteration so every stage and buffer index is static; the last
       // steps run after the loop (a single loop exit keeps the register assignment
@@ -429,25 +485,30 @@ void attention_frag_kernel(AttnArgs a) {
       const int last = UPT * N;
       int k = 0;
       for (; k + 2 * NS <= last; k += 2 * NS)
-        static_for<0, 2 * NS>([&](auto sc) { step(k + decltype(sc)::value, uc, sc); });
+        static_for<0, 2 * NS>([&](auto sc) { step(k + decltype(sc)::value, sc); });
       static_for<0, 2 * NS / UPT>([&](auto rc) {
         constexpr int R = decltype(rc)::value * UPT;       // steps left
         if (last - k == R) {
-          static_for<0, R>([&](auto sc) { step(k + decltype(sc)::value, uc, sc); });
-          finish(uc, ic<(R + 2 * NS - 1) % (2 * NS)>{});
+          static_for<0, R>([&](auto sc) { step(k + decltype(sc)::value, sc); });
+          finish(ic<(R + 2 * NS - 1) % (2 * NS)>{});
         }
       });
-      // Some row may have overflowed: run again with every row's true max as reference.
-      if (pass > 0 || !__any(over)) break;
+      if (pass > 0) break;
+      bool over = false;
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) m[qt] = mtop[qt];
-      over = false;
+      for (int qt = 0; qt < UPT; ++qt) {
+        const float l = sum_halves(lsum[qt]);
+        over |= !(l >= kSumLo && l <= kSumHi);
+      }
+      if (!__any(over)) break;
+      max_pass();
     }
   };
-  run(ic<UPT>{});
+  run();
+
 
   // Merge the two key halves. Each lane's sums cover its own 16 keys; both lane halves
-  // hold the same max. Wave kh finalises Oᵀ tiles [kh HE, kh HE + HE) of both query
+  // hold the same reference. Wave kh finalises Oᵀ tiles [kh HE, kh HE + HE) of both query
   // halves and hands the partner's tiles over through LDS.
   {
     float* mine = sX + kh * XS * 64 + lane;
@@ -464,7 +525,7 @@ void attention_frag_kernel(AttnArgs a) {
     else hand_over(ic<0>{});
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      mine[(HE * 32 + qt) * 64] = m[qt];
+      mine[(HE * 32 + qt) * 64] = mu[qt];
       mine[(HE * 32 + 2 + qt) * 64] = lsum[qt];
       mine[(HE * 32 + 4 + qt) * 64] = asum[qt];
     }
@@ -479,9 +540,8 @@ void attention_frag_kernel(AttnArgs a) {
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
         const float mo = oth[(HE * 32 + qt) * 64];
-        mt[qt] = fmaxf(m[qt], mo);
-        const float mu = mt[qt] == NEG_INF ? 0.f : mt[qt];
-        const float f = fast_exp2(m[qt] - mu), fo = fast_exp2(mo - mu);
+        mt[qt] = fmaxf(mu[qt], mo);
+        const float f = fast_exp2(mu[qt] - mt[qt]), fo = fast_exp2(mo - mt[qt]);
 #pragma unroll
         for (int u = 0; u < HE; ++u)
 #pragma unroll
