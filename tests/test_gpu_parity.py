@@ -246,3 +246,35 @@ def test_selection_larger_than_descriptor_table(gpu_lib, d, nb, K_sel, mode):
     err = rel_l2(g["O"][0][rows], ref["O"][rows])
     print(f"d={d} nb={nb} K_sel={K_sel} {mode}: rel-L2 {err:.2e}")
     assert err <= TOL_SAME_SEL["bf16"]
+
+
+@pytest.mark.parametrize("mode", MODE_NAMES)
+def test_late_logits_far_above_the_first_unit(gpu_lib, mode):
+    """Query tiles 0 and 6 (full and ragged) meet a block whose logits exceed those of
+    their first selected block by about 100 nats: exponentials taken against the first
+    block's max would overflow fp32, so the kernel must detect it and recompute against
+    the true row max. Ragged key blocks included."""
+    bl = [64, 64, 40, 64, 64, 64, 17, 64]
+    inp = synth.random_blocks(121, H=1, nb=8, d=128, dtype="bf16", block_len=bl)
+    ok = valid_rows(inp)
+    q = synth.bf16_bits_to_f32(inp.Q)
+    k = synth.bf16_bits_to_f32(inp.K)
+    q[0, :64, 0] += 10.0                               # full query tile 0
+    q[0, 6 * 64:7 * 64, 0] += 10.0                     # ragged query tile 6 (17 rows)
+    k[0, 5 * 64:6 * 64, 0] += 10.0
+    q[:, ~ok, :] = 0.0
+    k[:, ~ok, :] = 0.0
+    inp.Q[...] = synth.f32_to_bf16_bits(q)
+    inp.K[...] = synth.f32_to_bf16_bits(k)
+    K_sel = 4
+    sel, w = oracle_selection(inp, K_sel)
+    for t in (0, 6):                                   # the big block comes after the first one
+        assert 5 in sel[0, t] and sel[0, t, 0] < 5
+    g = gpu_attention_on(gpu_lib, inp, K_sel, mode, sel, w)
+    ref = _oracle(inp, 0, mode, K_sel, idx=sel[0])
+    assert np.all(np.isfinite(g["O"][0][ok]))
+    err = rel_l2(g["O"][0][ok], ref["O"][ok])
+    lse_err = float(np.max(np.abs(g["lse"][0][ok] - ref["lse"][ok])))
+    print(f"{mode}: rel-L2 {err:.2e}, max |lse diff| {lse_err:.2e}")
+    assert err <= TOL_SAME_SEL["bf16"]
+    assert lse_err < 5e-2
