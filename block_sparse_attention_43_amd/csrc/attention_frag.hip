@@ -100,7 +100,8 @@ void attention_frag_kernel(AttnArgs a) {
   const uint32_t* mrow = VIRT ? a.mask + (size_t(h) * nb + i) * a.nw : nullptr;
   const float* wrow = MODE == MODE_PWT ? a.wt + (size_t(h) * nb + i) * nb : nullptr;
 
-  // Q fragments, B operand of Sᵀ = K Qᵀ, for query halves 0 and 1; padding rows are zero.
+  // Q fragments, B operand of Sᵀ = K Qᵀ, for query halves 0 and 1; padding rows (all of
+  // half 1 with one unit per tile) are zero.
   bf16x8 qf[2][NKD];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
@@ -108,7 +109,7 @@ void attention_frag_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks) {
       bf16x8 v = {};
-      if (row < ni) v = *reinterpret_cast<const bf16x8*>(Qh + (size_t(i) * kB + row) * D + 16 * ks + 8 * g);
+      if ((UPT == 2 || qt == 0) && row < ni) v = *reinterpret_cast<const bf16x8*>(Qh + (size_t(i) * kB + row) * D + 16 * ks + 8 * g);
       qf[qt][ks] = v;
     }
   }
@@ -562,7 +563,7 @@ void attention_frag_kernel(AttnArgs a) {
       for (int ks = 0; ks < NKD; ++ks)
         hf[u][ks] = *reinterpret_cast<const bf16x8*>(hbp + size_t(32 * (kh * HE + u) + l32) * D + 16 * ks + 8 * g);
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < UPT; ++qt) {
       const float A = sum_halves(at[qt]);
 #pragma unroll
       for (int ks = 0; ks < NKD; ++ks) {

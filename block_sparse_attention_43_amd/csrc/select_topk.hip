@@ -9,10 +9,10 @@
 // S_i keeps the K_sel largest scores, ties to the lower block index, emitted in
 // ascending block order plus a bitmask of the selected blocks.
 //
-// Scores are fp32 with one fixed summation order per element, so identical centroids
-// score identically. Top-K is an exact radix select on order-preserving 32-bit keys
-// held in registers (256 threads, up to 128 keys each), with the tie rule resolved by
-// block-wide prefix counts in index order.
+// Scores are fp32 (matrix-core fp32 products and sums) with one fixed summation order per
+// element, so identical centroids score identically. Top-K is an exact radix select on
+// order-preserving 32-bit keys held in registers (256 threads, up to 128 keys each), with
+// the tie rule resolved by block-wide prefix counts in index order.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -66,74 +66,47 @@ __global__ __launch_bounds__(256) void pool_kernel(SelectArgs a) {
   }
 }
 
-// S = Q̄ K̄ᵀ and W = ½ Q̄² Σ²ᵀ per head; 64x64 output tile per workgroup, 4x4 per thread,
-// operands staged transposed in LDS in chunks of 32 of the head dimension.
+// S = Q̄ K̄ᵀ and W = ½ Q̄² Σ²ᵀ per head on the fp32 matrix cores: one wave per 32x32 output
+// tile, v_mfma_f32_32x32x2f32 over the head dimension. MFMA step m pairs column m (lane
+// half 0) with column m + D/2 (lane half 1), so every lane streams one contiguous half
+// row of its query (A) and key (B) block straight from memory. Each output element is
+// accumulated in the same order whatever its position, so identical centroids still
+// score identically.
 template <int D>
-__global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
-  constexpr int KC = 32;
-  __shared__ __align__(16) float sA[KC][64], sB[KC][64], sA2[KC][64], sB2[KC][64];
-  const int h = blockIdx.z;
-  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
-  const int tid = threadIdx.x, ti = tid / 16, tj = tid % 16;
-  const bool want_w = a.wt != nullptr;
-  const float* qb = a.qbar + size_t(h) * a.nb * D;
-  const float* q2 = a.qsq + size_t(h) * a.nb * D;
-  const float* kb = a.kbar + size_t(h) * a.nb * D;
-  const float* ks = a.ksig2 + size_t(h) * a.nb * D;
-  float acc[4][4], acw[4][4];
+__global__ __launch_bounds__(64) void score_kernel(SelectArgs a) {
+  constexpr int KH = D / 2;                // MFMA steps
+  const int lane = threadIdx.x, g = lane >> 5, c = lane & 31;
+  const int h = blockIdx.z, i0 = blockIdx.y * 32, j0 = blockIdx.x * 32, nb = a.nb;
+  auto tile = [&](const float* A, const float* B, float* out, float scale) {
+    const int ra = i0 + c, rb = j0 + c;
+    const float4* ap = reinterpret_cast<const float4*>(A + (size_t(h) * nb + min(ra, nb - 1)) * D + KH * g);
+    const float4* bp = reinterpret_cast<const float4*>(B + (size_t(h) * nb + min(rb, nb - 1)) * D + KH * g);
+    float4 av[KH / 4], bv[KH / 4];
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+    for (int u = 0; u < KH / 4; ++u) {
+      av[u] = ap[u];
+      bv[u] = bp[u];
+    }
+    f32x16 acc = zero16();
 #pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = acw[x][y] = 0.f;
-
-  for (int c0 = 0; c0 < D; c0 += KC) {
-    // 64 rows x 32 columns of each operand (8 threads per row, 4 columns each), stored [c][row]
-    const int row = tid / 4, cq = (tid % 4) * 8;
-    const int ii = i0 + row, jj = j0 + row;
+    for (int u = 0; u < KH / 4; ++u) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u].x, bv[u].x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u].y, bv[u].y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u].z, bv[u].z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u].w, bv[u].w, acc, 0, 0, 0);
+    }
+    // Rows / columns past nb read a valid row (clamped) and are not stored.
+    const int col = j0 + c;
+    if (col < nb) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      sA[cq + u][row] = ii < a.nb ? qb[size_t(ii) * D + c0 + cq + u] : 0.f;
-      sB[cq + u][row] = jj < a.nb ? kb[size_t(jj) * D + c0 + cq + u] : 0.f;
-      if (want_w) {
-        sA2[cq + u][row] = ii < a.nb ? q2[size_t(ii) * D + c0 + cq + u] : 0.f;
-        sB2[cq + u][row] = jj < a.nb ? ks[size_t(jj) * D + c0 + cq + u] : 0.f;
+      for (int r = 0; r < 16; ++r) {
+        const int row = i0 + acc_row(r, g);
+        if (row < nb) out[(size_t(h) * nb + row) * nb + col] = acc[r] * scale;
       }
     }
-    __syncthreads();
-#pragma unroll 8
-    for (int c = 0; c < KC; ++c) {
-      const float4 av = *reinterpret_cast<const float4*>(&sA[c][ti * 4]);
-      const float4 bv = *reinterpret_cast<const float4*>(&sB[c][tj * 4]);
-      const float ax[4] = {av.x, av.y, av.z, av.w}, bx[4] = {bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(ax[x], bx[y], acc[x][y]);
-      if (want_w) {
-        const float4 aw = *reinterpret_cast<const float4*>(&sA2[c][ti * 4]);
-        const float4 bw = *reinterpret_cast<const float4*>(&sB2[c][tj * 4]);
-        const float ay[4] = {aw.x, aw.y, aw.z, aw.w}, by[4] = {bw.x, bw.y, bw.z, bw.w};
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-          for (int y = 0; y < 4; ++y) acw[x][y] = fmaf(ay[x], by[y], acw[x][y]);
-      }
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int ii = i0 + ti * 4 + x;
-    if (ii >= a.nb) continue;
-#pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int jj = j0 + tj * 4 + y;
-      if (jj >= a.nb) continue;
-      const size_t o = (size_t(h) * a.nb + ii) * a.nb + jj;
-      a.scores[o] = acc[x][y];
-      if (want_w) a.wt[o] = 0.5f * acw[x][y];
-    }
-  }
+  };
+  tile(a.qbar, a.kbar, a.scores, 1.f);
+  if (a.wt) tile(a.qsq, a.ksig2, a.wt, 0.5f);
 }
 
 __device__ __forceinline__ uint32_t order_key(float s) {
@@ -241,8 +214,8 @@ static hipError_t launch_select_t(const SelectArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((pool_kernel<T, D>), dim3(a.nb, a.H), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nt = (a.nb + 63) / 64;
-  hipLaunchKernelGGL((score_kernel<D>), dim3(nt, nt, a.H), dim3(256), 0, s, a);
+  const int nt = (a.nb + 31) / 32;
+  hipLaunchKernelGGL((score_kernel<D>), dim3(nt, nt, a.H), dim3(64), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int per = (a.nb + 255) / 256;
