@@ -71,8 +71,8 @@ void attention_frag_kernel(AttnArgs a) {
   // has room for two.
   constexpr int NS = D == 128 ? 2 : 3;
   // Bias rows: 33 mask rows (row nk: keys < nk get 0, the others -inf), then per wave a
-  // ring of VR virtual-tile rows (32 fp32 biases ln n_j + φ, then 32 bf16 weights 1 / n_j),
-  // refilled VH tiles at a time.
+  // ring of VR virtual-tile rows (32 fp32 biases ln n_j + φ, then 32 bf16 weights 1 / n_j):
+  // the first VR filled before the loop, VH at a time, later ones one per loading step.
   constexpr int VR = 32, VH = 16, MROWS = 33;
   using KT = SwizzledTile<D * 2>;
   static_assert(2 * XS * 64 * 4 >= kB * D * 2, "output staging must fit the hand-over buffer");
@@ -179,30 +179,47 @@ void attention_frag_kernel(AttnArgs a) {
   // Virtual-tile rows of tiles [t0, t0 + cnt) into the ring (slot (t - n1) mod VR): lane
   // half g takes every other tile, lane l32 one key of this wave's half of the group.
   auto vrow = [&](int t) { return MROWS + kh * VR + ((t - n1) & (VR - 1)); };
-  auto vfill = [&](int t0, int cnt) {
-    for (int u0 = 0; u0 < cnt; u0 += 2) {
-      const int u = u0 + g, t = t0 + u;
-      const int jj = (t - n1) * kB + 32 * kh + l32;
-      float bias = NEG_INF, inv = 0.f;
-      if (u < cnt && jj < nb && !((mrow[jj >> 5] >> (jj & 31)) & 1u)) {
-        // Hardware log (v_log_f32, within 1 ulp): w >= 0 keeps ln(1 + w) accurate to
-        // ~1e-7 absolute, far below the logit's own rounding.
-        const int nj = block_keys(jj);
-        const float lnn = __logf(float(nj));
-        float phi = 0.f;
-        if constexpr (MODE == MODE_PWT) {
-          float w = wrow[jj];
-          if (a.gate && w > lnn) w = 0.f;
-          phi = a.w_linear ? __logf(1.f + w) : w;
-        }
-        bias = lnn + phi;
-        inv = __builtin_amdgcn_rcpf(float(nj));
+  // Row of virtual tile t from this lane's inputs (mask word, block length, w̃ of key jj =
+  // its key of the group): lane l32 writes key l32 of this wave's half.
+  auto write_vrow = [&](int t, uint32_t mw, int blv, float wv) {
+    const int jj = (t - n1) * kB + 32 * kh + l32;
+    float bias = NEG_INF, inv = 0.f;
+    if (jj < nb && !((mw >> (jj & 31)) & 1u)) {
+      // Hardware log (v_log_f32, within 1 ulp): w >= 0 keeps ln(1 + w) accurate to
+      // ~1e-7 absolute, far below the logit's own rounding.
+      const int nj = min(max(blv, 1), kB);
+      const float lnn = __logf(float(nj));
+      float phi = 0.f;
+      if constexpr (MODE == MODE_PWT) {
+        float w = wv;
+        if (a.gate && w > lnn) w = 0.f;
+        phi = a.w_linear ? __logf(1.f + w) : w;
       }
-      if (u < cnt) {
-        sRow[vrow(t)][l32] = bias;
-        reinterpret_cast<__bf16*>(&sRow[vrow(t)][32])[l32] = static_cast<__bf16>(inv);
-      }
+      bias = lnn + phi;
+      inv = __builtin_amdgcn_rcpf(float(nj));
     }
+    sRow[vrow(t)][l32] = bias;
+    reinterpret_cast<__bf16*>(&sRow[vrow(t)][32])[l32] = static_cast<__bf16>(inv);
+  };
+  // Inputs of key l32 of virtual tile t (clamped in bounds; unused past the last tile).
+  auto vin_jj = [&](int t) { return min((t - n1) * kB + 32 * kh + l32, nb - 1); };
+  // Rows of tiles [t0, t0 + cnt), cnt <= VH, lane half g taking every other tile; all
+  // inputs are loaded first, so one memory latency covers the fill.
+  auto vfill = [&](int t0, int cnt) {
+    constexpr int VI = VH / 2;
+    uint32_t mw[VI];
+    int bl[VI];
+    float wv[VI];
+#pragma unroll
+    for (int q = 0; q < VI; ++q) {
+      const int jj = vin_jj(t0 + 2 * q + g);
+      mw[q] = mrow[jj >> 5];
+      bl[q] = a.block_len ? a.block_len[jj] : kB;
+      wv[q] = MODE == MODE_PWT ? wrow[jj] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < VI; ++q)
+      if (2 * q + g < cnt) write_vrow(t0 + 2 * q + g, mw[q], bl[q], wv[q]);
   };
   // The 16 biases of a row this lane adds, in Sᵀ accumulator order: register r of lane
   // half g holds key 16 (r / 8) + 8 g + r % 8.
@@ -227,6 +244,9 @@ void attention_frag_kernel(AttnArgs a) {
   // Operand ring: the K and Vᵀ registers of NS tiles. Stage s holds tiles t with t % NS == s.
   bf16x8 kst[NS][NKD], vst[NS][NVF];
   int toff[NS], crow[NS];
+  uint32_t pv_m = 0u;                    // inputs of the next progressively written virtual row
+  int pv_b = 0;
+  float pv_w = 0.f;
 
   // Tile t's source (stage P = t % NS): fragment offset and bias row from its descriptor,
   // and the descriptor pipeline advanced. The fragment loads themselves are spread over
@@ -301,9 +321,18 @@ void attention_frag_kernel(AttnArgs a) {
     // the one that tile n + VL - NS left.
     const int vov = lane * 16 + toff[LV];       // read before the K issue may reuse the slot
     if constexpr (LOADS) issue_desc(n + NS, ic<TP>{});
-    if constexpr (VIRT && CLOAD) {
-      const int tc = n + CT;                    // refill the ring half that tile tc opens
-      if (tc < N && tc - n1 >= VR && ((tc - n1) & (VH - 1)) == 0) vfill(tc, min(VH, N - tc));
+    if constexpr (VIRT && LOADS) {
+      // Virtual rows past the prologue's VR: the inputs of tile n + NS + 2 are loaded here
+      // and its row written at the next loading step, a step or more before its bias
+      // row is read (tile n + NS + 1, loaded at the previous one, is written now).
+      const int tp = n + NS + 1, tq = n + NS + 2;
+      if (tp < N && tp - n1 >= VR) write_vrow(tp, pv_m, pv_b, pv_w);
+      if (tq < N && tq - n1 >= VR) {
+        const int jj = vin_jj(tq);
+        pv_m = mrow[jj >> 5];
+        pv_b = a.block_len ? a.block_len[jj] : kB;
+        pv_w = MODE == MODE_PWT ? wrow[jj] : 0.f;
+      }
     }
     const int crw = crow[CS];
     const __amdgpu_buffer_rsrc_t rk = krsrc(n + NS), rv = vrsrc(n + VL);   // used when LOADS
@@ -445,7 +474,8 @@ void attention_frag_kernel(AttnArgs a) {
       }
       if (N == 0) break;
       if constexpr (VIRT) {
-        if (N > n1) vfill(n1, min(VR, N - n1));
+        if (N > n1) vfill(n1, min(VH, N - n1));
+        if (N > n1 + VH) vfill(n1 + VH, min(VH, N - n1 - VH));
       }
       pb[1][0] = pb[1][1] = bf16x8{};
       static_for<0, NS>([&](auto pc) {
