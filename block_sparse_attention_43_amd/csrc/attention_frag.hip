@@ -83,13 +83,17 @@ void attention_frag_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63, g = lane >> 5, l32 = lane & 31;
   const int kh = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, kept scalar
   const int nb = a.nb, ngrp = a.nbp / kB;
-  const uint32_t lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = int(lin / uint32_t(nb)), i = int(lin % uint32_t(nb));
-  int ni = a.block_len ? a.block_len[i] : kB;
-  ni = min(max(ni, 1), kB);
   // Query tiles of more than 32 rows run with two units per tile, the others with one
-  // (their second query half is all padding); each kind has its own launch.
-  if ((ni > 32) != (UPT == 2)) return;
+  // (their second query half is all padding); each kind has its own launch over the
+  // statistics call's tile order (that kind's tiles first), and the workgroups past the
+  // kind's count leave at once.
+  const int32_t* order = reinterpret_cast<const int32_t*>(a.packed + a.pl.tiles);
+  const uint32_t cnt = uint32_t(order[UPT == 2 ? 0 : 1]), work = uint32_t(a.H) * cnt;
+  if (blockIdx.x >= work) return;
+  const uint32_t lin = xcd_remap(blockIdx.x, work);
+  const int h = int(lin / cnt);
+  const int ent = order[2 + (UPT == 2 ? 0 : order[0]) + int(lin % cnt)];
+  const int i = ent >> 7, ni = ent & 127;
 
   const uint16_t* Qh = static_cast<const uint16_t*>(a.Q) + size_t(h) * a.L * D;
   const char* kfh = a.packed + a.pl.kf + size_t(h) * nb * TB;

@@ -241,6 +241,29 @@ __global__ __launch_bounds__(256) void hbar_reduce_kernel(StatsArgs a) {
   }
 }
 
+// Launch order of the query tiles for the bf16 attention kernels: tiles of more than 32
+// valid rows (two query halves per tile), then the others, each ascending. Entry
+// tile * 128 + rows after the two counts; one workgroup, each thread a contiguous chunk.
+__global__ __launch_bounds__(256) void tile_order_kernel(StatsArgs a) {
+  __shared__ int sh[8];
+  int32_t* out = reinterpret_cast<int32_t*>(a.packed + a.pl.tiles);
+  const int nb = a.nb, C = (nb + 255) / 256, t0 = min(int(threadIdx.x) * C, nb), t1 = min(t0 + C, nb);
+  auto rows = [&](int t) { return a.block_len ? min(max(a.block_len[t], 1), kB) : kB; };
+  int full = 0;
+  for (int t = t0; t < t1; ++t) full += rows(t) > 32;
+  int total;
+  const int before = block_exclusive_scan_256(full, sh, &total);
+  int pf = before, pr = total + (t0 - before);
+  for (int t = t0; t < t1; ++t) {
+    const int r = rows(t);
+    out[2 + (r > 32 ? pf++ : pr++)] = t * 128 + r;
+  }
+  if (threadIdx.x == 0) {
+    out[0] = total;
+    out[1] = nb - total;
+  }
+}
+
 template <class T, int D>
 static hipError_t launch_stats_t(const StatsArgs& a, unsigned flags, hipStream_t s) {
   dim3 g1(a.ngroups, a.H), g2((D * D + 255) / 256, a.H);
@@ -249,6 +272,9 @@ static hipError_t launch_stats_t(const StatsArgs& a, unsigned flags, hipStream_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((hbar_reduce_kernel<T, D>), g2, dim3(256), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(tile_order_kernel, dim3(1), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -15,7 +15,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // is TileLayout<T, d> (common.hpp): plain K rows / Vᵀ rows for fp32, MFMA operand order
 // for bf16. The bf16 layout also carries an operand-order copy of K per block.
 struct PackedLayout {
-  size_t kf, vt, kbar, vbar, hbar, total;
+  size_t kf, vt, kbar, vbar, hbar, tiles, total;
   int nb, nbp;
 };
 
@@ -30,6 +30,7 @@ inline PackedLayout packed_layout(size_t elem, int H, int L, int d) {
   p.kbar = o; o = align256(o + size_t(H) * (p.nbp / kB) * tile);            // [H][nbp/64] centroid tiles
   p.vbar = o; o = align256(o + size_t(H) * (p.nbp / kB) * tile);            // [H][nbp/64] (ΣV/n)ᵀ tiles
   p.hbar = o; o = align256(o + size_t(H) * d * d * elem);                   // [H][d][d]   H̄[e][c]
+  p.tiles = o; o = align256(o + (2 + size_t(p.nb)) * 4);                    // query-tile order
   p.total = o;
   return p;
 }

@@ -66,44 +66,52 @@ __global__ __launch_bounds__(256) void pool_kernel(SelectArgs a) {
   }
 }
 
-// S = Q̄ K̄ᵀ and W = ½ Q̄² Σ²ᵀ per head on the fp32 matrix cores: one wave per 32x32 output
-// tile, v_mfma_f32_32x32x2f32 over the head dimension. MFMA step m pairs column m (lane
-// half 0) with column m + D/2 (lane half 1), so every lane streams one contiguous half
-// row of its query (A) and key (B) block straight from memory. Each output element is
-// accumulated in the same order whatever its position, so identical centroids still
-// score identically.
+// S = Q̄ K̄ᵀ and W = ½ Q̄² Σ²ᵀ per head on the fp32 matrix cores: a 64x64 output tile per
+// workgroup, each of its four waves a 32x32 quarter (v_mfma_f32_32x32x2f32 over the head
+// dimension). The 64 query and 64 key rows are staged in LDS with coalesced 16-byte loads.
+// MFMA step m pairs column m (lane half 0) with column m + D/2 (lane half 1), so each
+// lane reads one contiguous half row per operand. Every output element is accumulated
+// in the same order whatever its position, so identical centroids score identically.
 template <int D>
-__global__ __launch_bounds__(64) void score_kernel(SelectArgs a) {
+__global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
   constexpr int KH = D / 2;                // MFMA steps
-  const int lane = threadIdx.x, g = lane >> 5, c = lane & 31;
-  const int h = blockIdx.z, i0 = blockIdx.y * 32, j0 = blockIdx.x * 32, nb = a.nb;
+  constexpr int RS = D + 4;                // LDS row stride in floats (staggers the banks)
+  constexpr int CPR = D / 4, NCH = 64 * CPR / 256;
+  __shared__ __align__(16) float sA[64 * RS], sB[64 * RS];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int h = blockIdx.z, i0 = blockIdx.y * 64, j0 = blockIdx.x * 64, nb = a.nb;
+  const int wi = (wave >> 1) * 32, wj = (wave & 1) * 32;
   auto tile = [&](const float* A, const float* B, float* out, float scale) {
-    const int ra = i0 + c, rb = j0 + c;
-    const float4* ap = reinterpret_cast<const float4*>(A + (size_t(h) * nb + min(ra, nb - 1)) * D + KH * g);
-    const float4* bp = reinterpret_cast<const float4*>(B + (size_t(h) * nb + min(rb, nb - 1)) * D + KH * g);
-    float4 av[KH / 4], bv[KH / 4];
 #pragma unroll
-    for (int u = 0; u < KH / 4; ++u) {
-      av[u] = ap[u];
-      bv[u] = bp[u];
+    for (int p = 0; p < NCH; ++p) {          // rows past nb read a valid row, not stored
+      const int q = tid + 256 * p, r = q / CPR, col = 4 * (q % CPR);
+      const float4 va = *reinterpret_cast<const float4*>(A + (size_t(h) * nb + min(i0 + r, nb - 1)) * D + col);
+      const float4 vb = *reinterpret_cast<const float4*>(B + (size_t(h) * nb + min(j0 + r, nb - 1)) * D + col);
+      *reinterpret_cast<float4*>(&sA[r * RS + col]) = va;
+      *reinterpret_cast<float4*>(&sB[r * RS + col]) = vb;
     }
+    __syncthreads();
+    const float* pa = &sA[(wi + c) * RS + KH * g];
+    const float* pb = &sB[(wj + c) * RS + KH * g];
     f32x16 acc = zero16();
 #pragma unroll
     for (int u = 0; u < KH / 4; ++u) {
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u].x, bv[u].x, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u].y, bv[u].y, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u].z, bv[u].z, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u].w, bv[u].w, acc, 0, 0, 0);
+      const float4 x = *reinterpret_cast<const float4*>(pa + 4 * u);
+      const float4 y = *reinterpret_cast<const float4*>(pb + 4 * u);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, y.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, y.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, y.w, acc, 0, 0, 0);
     }
-    // Rows / columns past nb read a valid row (clamped) and are not stored.
-    const int col = j0 + c;
+    const int col = j0 + wj + c;
     if (col < nb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = i0 + acc_row(r, g);
+        const int row = i0 + wi + acc_row(r, g);
         if (row < nb) out[(size_t(h) * nb + row) * nb + col] = acc[r] * scale;
       }
     }
+    __syncthreads();                         // LDS reused by the next product
   };
   tile(a.qbar, a.kbar, a.scores, 1.f);
   if (a.wt) tile(a.qsq, a.ksig2, a.wt, 0.5f);
@@ -214,8 +222,8 @@ static hipError_t launch_select_t(const SelectArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((pool_kernel<T, D>), dim3(a.nb, a.H), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nt = (a.nb + 31) / 32;
-  hipLaunchKernelGGL((score_kernel<D>), dim3(nt, nt, a.H), dim3(64), 0, s, a);
+  const int nt = (a.nb + 63) / 64;
+  hipLaunchKernelGGL((score_kernel<D>), dim3(nt, nt, a.H), dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int per = (a.nb + 255) / 256;

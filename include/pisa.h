@@ -104,8 +104,9 @@ enum {
  *   hblk  [H][nb][d][d] H_j[e][c]              (NULL unless PISA_STATS_BLOCK_H)
  *   cblk  [H][nb][d][d] C_j = (1/n_j) Σ (k_i - k̄_j)(k_i - k̄_j)ᵀ (NULL unless PISA_STATS_BLOCK_C)
  *   packed             pisa_packed_bytes() bytes: the same statistics re-laid for the
- *                      attention kernel's operands (plus Vᵀ per block); opaque, written
- *                      by pisa_block_stats and read by pisa_attention_fwd.
+ *                      attention kernel's operands (plus Vᵀ per block) and the order in
+ *                      which it visits query tiles; opaque, written by pisa_block_stats
+ *                      and read by pisa_attention_fwd.
  */
 typedef struct {
   float* kbar;
