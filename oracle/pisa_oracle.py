@@ -138,6 +138,31 @@ def block_scores(qbar: np.ndarray, kbar: np.ndarray) -> np.ndarray:
     return np.asarray(qbar, dtype=np.float64) @ np.asarray(kbar, dtype=np.float64).T
 
 
+# Offset inside log(M_j + ε) of the covariance-aware score. The paper leaves ε unstated;
+# it only keeps the log finite when a block matches the global statistic exactly.
+ROUTE_EPS = 1e-6
+
+
+def block_heterogeneity(st: dict) -> np.ndarray:
+    """M_j = ||H_j - H̄||_F per block: the heterogeneity whose norm bounds the error of
+    replacing H_j by the global H̄ (PISA paper §3.3 Error Analysis, Theorem 3.1 with
+    M_t = max_j ||H_j - H̄||_2, and Covariance-Aware Block Selection). The Frobenius norm
+    is the computable choice; it bounds the spectral norm from above. Needs the per-block
+    H_j (block_stats with per_block=True)."""
+    H = st["H"]
+    if H is None:
+        raise ValueError("block_heterogeneity needs per-block H_j")
+    return np.sqrt(((H - st["hbar"][None, :, :]) ** 2).sum(axis=(1, 2)))
+
+
+def routed_scores(qbar: np.ndarray, kbar: np.ndarray, hnorm: np.ndarray, eps: float = ROUTE_EPS) -> np.ndarray:
+    """Covariance-aware selection score (PISA paper §3.3 Eq. (7)):
+    q̄_i·k̄_j + log(M_j + ε). The softmax of Eq. (7) is monotone along each row, so the
+    top-K is taken on its argument; the pooled q̄_i stands for q_t, as in block-mean
+    scoring, and 1/sqrt(d) is already folded into Q."""
+    return block_scores(qbar, kbar) + np.log(np.asarray(hnorm, dtype=np.float64) + eps)[None, :]
+
+
 def select_topk(scores: np.ndarray, K_sel: int) -> np.ndarray:
     """S_i = the K_sel largest scores of row i, ties to the lower block index; returned
     in ascending block order, shape [nq, K_sel] int64."""

@@ -429,6 +429,52 @@ def test_duplicated_blocks_tie_to_lower_index():
     assert np.all(idx[:, 0] == 1)
 
 
+def test_heterogeneity_two_token_closed_form():
+    """For a block of two tokens H_j = ½ (v_1 - v_2)(k_1 - k_2)ᵀ, a rank-one matrix, so
+    with two blocks H̄ = ½ (H_1 + H_2) and M_1 = M_2 = ½ ||H_1 - H_2||_F; with identical
+    blocks M_j = 0 (PISA paper §3.3 Theorem 3.1, M = ||H_j - H̄||)."""
+    r = np.random.default_rng(21)
+    d = 3
+    K = r.standard_normal((4, d))
+    V = r.standard_normal((4, d))
+    st = orc.block_stats(K, V, 2)
+    H1 = 0.5 * np.outer(V[0] - V[1], K[0] - K[1])
+    H2 = 0.5 * np.outer(V[2] - V[3], K[2] - K[3])
+    m = orc.block_heterogeneity(st)
+    want = 0.5 * math.sqrt(float(((H1 - H2) ** 2).sum()))
+    assert abs(m[0] - want) < 1e-12 and abs(m[1] - want) < 1e-12
+    same = orc.block_stats(np.tile(K[:2], (3, 1)), np.tile(V[:2], (3, 1)), 2)
+    assert np.all(orc.block_heterogeneity(same) < 1e-14)
+
+
+def test_covariance_routing_prefers_heterogeneous_blocks():
+    """With equal centroid scores the covariance-aware score (PISA paper Eq. (7)) picks
+    the block whose H_j is farthest from H̄; with every M_j equal it selects exactly what
+    plain block-mean scoring selects."""
+    r = np.random.default_rng(22)
+    B, nb, d = 4, 5, 6
+    K = np.zeros((B * nb, d))
+    V = np.zeros((B * nb, d))
+    base = r.standard_normal((B, d))
+    for j in range(nb):                       # same centroid everywhere, spread grows with j
+        K[j * B:(j + 1) * B] = 1.0 + (j + 1) * 0.1 * (base - base.mean(axis=0))
+        V[j * B:(j + 1) * B] = r.standard_normal((B, d))
+    V[3 * B:4 * B] *= 10.0                    # block 3: by far the largest H_j
+    st = orc.block_stats(K, V, B)
+    pq = orc.pool_queries(r.standard_normal((B * nb, d)), B)
+    plain = orc.block_scores(pq["qbar"], st["kbar"])
+    assert np.allclose(plain, plain[:, :1])   # all blocks tie on the centroid score
+    m = orc.block_heterogeneity(st)
+    routed = orc.routed_scores(pq["qbar"], st["kbar"], m)
+    assert int(np.argmax(m)) == 3
+    assert np.all(orc.select_topk(routed, 1)[:, 0] == 3)
+    pq2 = orc.pool_queries(r.standard_normal((B * nb, d)), B)
+    st2 = orc.block_stats(r.standard_normal((B * nb, d)), V, B)
+    a = orc.select_topk(orc.routed_scores(pq2["qbar"], st2["kbar"], np.full(nb, 2.0)), 2)
+    b = orc.select_topk(orc.block_scores(pq2["qbar"], st2["kbar"]), 2)
+    assert np.array_equal(a, b)
+
+
 def test_pooled_query_is_valid_row_mean():
     """q̄_i averages only the n_i valid rows of a ragged tile (PISA paper Fig. 3 Q̄)."""
     Q = np.arange(16, dtype=np.float64).reshape(8, 2)
