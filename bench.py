@@ -142,6 +142,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="wan", help="tiny | flux | wan | hunyuan | long")
     ap.add_argument("--mode", default="pwt", help="drop | pisa | pwt | literal")
+    ap.add_argument("--route", default="mean", help="mean | covariance (block selection score)")
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -192,7 +193,9 @@ def main():
         return
 
     # every buffer allocated once, outside the timed region
-    st = pisa.alloc_stats(K)
+    route = args.route
+    sflags = pisa.STATS_HNORM if route == "covariance" else 0
+    st = pisa.alloc_stats(K, sflags)
     ws_stats = torch.empty(max(pisa.load().pisa_block_stats_workspace_bytes(H, L, d, 64), 16),
                            dtype=torch.uint8, device="cuda")
     ws_sel = torch.empty(pisa.load().pisa_select_workspace_bytes(H, L, d, 64), dtype=torch.uint8, device="cuda")
@@ -206,10 +209,10 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        pisa.block_stats(K, V, blt, out=st, workspace=ws_stats)
+        pisa.block_stats(K, V, blt, flags=sflags, out=st, workspace=ws_stats)
         if ev is not None:
             ev[1].record(stream)
-        pisa.select_topk(Q, st, K_sel, blt, out=(idx, mask, wt), workspace=ws_sel)
+        pisa.select_topk(Q, st, K_sel, blt, out=(idx, mask, wt), workspace=ws_sel, route=route)
         if ev is not None:
             ev[2].record(stream)
         pisa.attention_fwd(Q, K, V, st, idx, mask, wt, K_sel, mode, blt, out=O, lse=lse)
@@ -252,6 +255,26 @@ def main():
 
     ms_exact = timed(lambda: pisa.attention_fwd(Q, K, V, st, idx, mask, None, K_sel, "drop", blt, out=O))
     exact_tflops = fc["exact"] / (ms_exact * 1e-3) / 1e12
+
+    # covariance-aware routing, the optional selection rule: its prepare-phase cost (second
+    # statistics pass for M_j + routed scores) and how many tiles change their selection
+    routing = None
+    if route == "mean":
+        st_r = pisa.alloc_stats(K, pisa.STATS_HNORM)
+        idx_r, mask_r = torch.empty_like(idx), torch.empty_like(mask)
+        wt_r = None if wt is None else torch.empty_like(wt)
+
+        def prep_routed():
+            pisa.block_stats(K, V, blt, flags=pisa.STATS_HNORM, out=st_r, workspace=ws_stats)
+            pisa.select_topk(Q, st_r, K_sel, blt, out=(idx_r, mask_r, wt_r), workspace=ws_sel,
+                             route="covariance")
+
+        ms_prep_r = timed(prep_routed)
+        changed = float((idx_r != idx).any(dim=-1).float().mean().item()) if K_sel else 0.0
+        routing = {"ms_prepare_covariance": round(ms_prep_r, 4),
+                   "ms_prepare_mean": round(ms_stats + ms_sel, 4),
+                   "tiles_with_changed_selection": round(changed, 4)}
+        del st_r, idx_r, mask_r, wt_r
 
     # cold cache: a 512 MiB fill between runs evicts L2 and the Infinity Cache
     flush = torch.empty(512 * 2**20, dtype=torch.uint8, device="cuda")
@@ -320,9 +343,9 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic (seeded smooth 3D field + noise, cube layout; no model activations)",
         "config": {"workload": f"{cfg.name}: H={H} L={inp.layout.L} (padded {L}) d={d} B=64 "
-                               f"K_sel={K_sel}/{nb} mode={mode}",
+                               f"K_sel={K_sel}/{nb} mode={mode}" + (f" route={route}" if route != "mean" else ""),
                    "heads": H, "seq_len": inp.layout.L, "head_dim": d, "block": 64,
-                   "k_sel": K_sel, "n_blocks": nb, "mode": mode},
+                   "k_sel": K_sel, "n_blocks": nb, "mode": mode, "route": route},
         "ms_stats": round(ms_stats, 4),
         "ms_select": round(ms_sel, 4),
         "ms_attention": round(ms_attn, 4),
@@ -334,6 +357,7 @@ def main():
                        "runs": len(cold_step), "flush_bytes": 512 * 2**20},
         "layout_permutation_ms": round(ms_perm, 4),
         "literal": literal,
+        "covariance_routing": routing,
         "flops": fc,
         **dense,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,

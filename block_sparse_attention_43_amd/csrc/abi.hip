@@ -92,7 +92,7 @@ pisa_status pisa_block_stats(pisa_dtype dt, const void* K, const void* V, int H,
   PISA_TRY(check_ptr(K, "K"));
   PISA_TRY(check_ptr(V, "V"));
   PISA_TRY(check_ptr(out, "out", false));
-  if (flags & ~3u) return fail(PISA_ERR_INVALID_ARG, "unknown stats flags 0x%x", flags);
+  if (flags & ~7u) return fail(PISA_ERR_INVALID_ARG, "unknown stats flags 0x%x", flags);
   PISA_TRY(check_ptr(out->kbar, "out->kbar"));
   PISA_TRY(check_ptr(out->vsum, "out->vsum"));
   PISA_TRY(check_ptr(out->ksig2, "out->ksig2"));
@@ -100,6 +100,7 @@ pisa_status pisa_block_stats(pisa_dtype dt, const void* K, const void* V, int H,
   PISA_TRY(check_ptr(out->packed, "out->packed"));
   if (flags & PISA_STATS_BLOCK_H) PISA_TRY(check_ptr(out->hblk, "out->hblk"));
   if (flags & PISA_STATS_BLOCK_C) PISA_TRY(check_ptr(out->cblk, "out->cblk"));
+  if (flags & PISA_STATS_HNORM) PISA_TRY(check_ptr(out->hnorm, "out->hnorm", false));
   const size_t need = pisa_block_stats_workspace_bytes(H, L, d, B);
   if (!workspace || workspace_bytes < need)
     return fail(PISA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
@@ -115,6 +116,7 @@ pisa_status pisa_block_stats(pisa_dtype dt, const void* K, const void* V, int H,
   a.hbarT = out->hbarT;
   a.hblk = out->hblk;
   a.cblk = out->cblk;
+  a.hnorm = out->hnorm;
   a.packed = static_cast<char*>(out->packed);
   a.part = static_cast<float*>(workspace);
   a.H = H;
@@ -136,16 +138,22 @@ size_t pisa_select_workspace_bytes(int H, int L, int d, int B) {
   return pisa::align256(2 * size_t(H) * nb * d * sizeof(float)) + size_t(H) * nb * nb * sizeof(float);
 }
 
-pisa_status pisa_select_topk(pisa_dtype dt, const void* Q, const pisa_stats* st, int H, int L,
-                             int d, int B, const int32_t* block_len, int K_sel, int32_t* idx,
-                             uint32_t* mask, float* wt, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+pisa_status pisa_select_topk_routed(pisa_dtype dt, const void* Q, const pisa_stats* st, int H,
+                                    int L, int d, int B, const int32_t* block_len, int K_sel,
+                                    unsigned route, float eps, int32_t* idx, uint32_t* mask,
+                                    float* wt, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
   PISA_TRY(check_dtype(dt));
   PISA_TRY(check_shape(H, L, d, B));
   PISA_TRY(check_ptr(Q, "Q"));
   PISA_TRY(check_ptr(st, "st", false));
   PISA_TRY(check_ptr(st->kbar, "st->kbar"));
   PISA_TRY(check_ptr(st->ksig2, "st->ksig2"));
+  if (route > PISA_ROUTE_COVARIANCE) return fail(PISA_ERR_INVALID_ARG, "unknown route %u", route);
+  if (route == PISA_ROUTE_COVARIANCE) {
+    PISA_TRY(check_ptr(st->hnorm, "st->hnorm", false));
+    if (!(eps > 0.f) || eps > 3.0e38f) return fail(PISA_ERR_INVALID_ARG, "eps must be finite and > 0 (got %g)", double(eps));
+  }
   const int nb = L / B;
   if (K_sel < 0 || K_sel > nb) return fail(PISA_ERR_INVALID_ARG, "K_sel must be in [0, %d] (got %d)", nb, K_sel);
   if (K_sel > 0) PISA_TRY(check_ptr(idx, "idx", false));
@@ -158,6 +166,8 @@ pisa_status pisa_select_topk(pisa_dtype dt, const void* Q, const pisa_stats* st,
   a.Q = Q;
   a.kbar = st->kbar;
   a.ksig2 = st->ksig2;
+  a.hnorm = route == PISA_ROUTE_COVARIANCE ? st->hnorm : nullptr;
+  a.route_eps = eps;
   a.block_len = block_len;
   a.qbar = static_cast<float*>(workspace);
   a.qsq = a.qbar + size_t(H) * nb * d;
@@ -175,6 +185,14 @@ pisa_status pisa_select_topk(pisa_dtype dt, const void* Q, const pisa_stats* st,
   hipError_t e = pisa::launch_select(dt == PISA_BF16, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "pisa_select_topk launch");
   return ok();
+}
+
+pisa_status pisa_select_topk(pisa_dtype dt, const void* Q, const pisa_stats* st, int H, int L,
+                             int d, int B, const int32_t* block_len, int K_sel, int32_t* idx,
+                             uint32_t* mask, float* wt, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return pisa_select_topk_routed(dt, Q, st, H, L, d, B, block_len, K_sel, PISA_ROUTE_MEAN, 1.f, idx,
+                                 mask, wt, workspace, workspace_bytes, stream);
 }
 
 pisa_status pisa_attention_fwd(pisa_dtype dt, const void* Q, const void* K, const void* V,

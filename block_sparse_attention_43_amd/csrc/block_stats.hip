@@ -241,6 +241,101 @@ __global__ __launch_bounds__(256) void hbar_reduce_kernel(StatsArgs a) {
   }
 }
 
+// Block heterogeneity M_j = ||H_j - H̄||_F (PISA paper §3.3: the error bound of replacing
+// every H_j by the global H̄ grows with max_j ||H_j - H̄||, and covariance-aware selection
+// takes its log as a routing prior; the Frobenius norm bounds the spectral one). H̄ is
+// only known once every block has been reduced, so this is a second pass over K and V
+// with the first pass's layout: G blocks per workgroup through LDS, K_jᵀV_j on MFMA,
+// centring with the first pass's k̄_j and ΣV_j, H̄ᵀ held in registers in accumulator
+// order. Squares are summed per lane, then across lanes and waves in a fixed order.
+template <class T, int D>
+__global__ __launch_bounds__(256) void heterogeneity_kernel(StatsArgs a) {
+  using M = typename MmaFor<T>::type;
+  constexpr int KI = M::KI, KH = M::KH;
+  constexpr int EPC = 16 / sizeof(T), LDR = D + EPC, CPR = D / EPC, CPT = kB * CPR / 256;
+  constexpr int NT = D / 32, TPW = NT * NT / 4;
+  __shared__ __align__(16) T sK[kB * LDR];
+  __shared__ __align__(16) T sV[kB * LDR];
+  __shared__ float sKbar[D], sVsum[D], sPart[4];
+
+  const int h = blockIdx.y, j0 = blockIdx.x * a.G, j1 = min(a.nb, j0 + a.G);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int ct = (wave * TPW) / NT;
+  const T* Kh = static_cast<const T*>(a.K) + size_t(h) * a.L * D;
+  const T* Vh = static_cast<const T*>(a.V) + size_t(h) * a.L * D;
+
+  f32x16 hb[TPW];                          // H̄ᵀ[c][e] at this lane's accumulator slots
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int e = 32 * ((wave * TPW + u) % NT) + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) hb[u][r] = a.hbarT[(size_t(h) * D + 32 * ct + acc_row(r, g)) * D + e];
+  }
+
+  u32x4 rk[CPT], rv[CPT];
+  auto load_block = [&](int j) {
+#pragma unroll
+    for (int p = 0; p < CPT; ++p) {
+      const int c = tid + 256 * p, row = c / CPR, col = (c % CPR) * EPC;
+      rk[p] = *reinterpret_cast<const u32x4*>(Kh + size_t(j * kB + row) * D + col);
+      rv[p] = *reinterpret_cast<const u32x4*>(Vh + size_t(j * kB + row) * D + col);
+    }
+  };
+  if (j0 < j1) load_block(j0);
+
+  for (int j = j0; j < j1; ++j) {
+    int n = a.block_len ? a.block_len[j] : kB;
+    n = min(max(n, 1), kB);
+    __syncthreads();                       // previous block's LDS reads done
+#pragma unroll
+    for (int p = 0; p < CPT; ++p) {
+      const int c = tid + 256 * p, row = c / CPR, col = (c % CPR) * EPC;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sK + row * LDR + col) = row < n ? rk[p] : z;
+      *reinterpret_cast<u32x4*>(sV + row * LDR + col) = row < n ? rv[p] : z;
+    }
+    const size_t o = (size_t(h) * a.nb + j) * D;
+    if (tid < D) sKbar[tid] = a.kbar[o + tid];
+    else if (tid >= 128 && tid < 128 + D) sVsum[tid - 128] = a.vsum[o + tid - 128];
+    if (j + 1 < j1) load_block(j + 1);
+    __syncthreads();
+
+    f32x16 blk[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) blk[u] = zero16();
+#pragma unroll
+    for (int ks = 0; ks < kB / KI; ++ks) {
+      float av[KH];
+#pragma unroll
+      for (int u = 0; u < KH; ++u) av[u] = to_f32(sK[(KI * ks + KH * g + u) * LDR + 32 * ct + l32]);
+      const typename M::AB A = M::pack(av);
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const int et = (wave * TPW + u) % NT;
+        float bv[KH];
+#pragma unroll
+        for (int q = 0; q < KH; ++q) bv[q] = to_f32(sV[(KI * ks + KH * g + q) * LDR + 32 * et + l32]);
+        blk[u] = M::mma(A, M::pack(bv), blk[u]);
+      }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const float ve = sVsum[32 * ((wave * TPW + u) % NT) + l32];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float dv = blk[u][r] - sKbar[32 * ct + acc_row(r, g)] * ve - hb[u][r];
+        ss = fmaf(dv, dv, ss);
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+    if (lane == 0) sPart[wave] = ss;
+    __syncthreads();
+    if (tid == 0) a.hnorm[size_t(h) * a.nb + j] = sqrtf((sPart[0] + sPart[1]) + (sPart[2] + sPart[3]));
+  }
+}
+
 // Launch order of the query tiles for the bf16 attention kernels: tiles of more than 32
 // valid rows (two query halves per tile), then the others, each ascending. Entry
 // tile * 128 + rows after the two counts; one workgroup, each thread a contiguous chunk.
@@ -267,13 +362,18 @@ __global__ __launch_bounds__(256) void tile_order_kernel(StatsArgs a) {
 template <class T, int D>
 static hipError_t launch_stats_t(const StatsArgs& a, unsigned flags, hipStream_t s) {
   dim3 g1(a.ngroups, a.H), g2((D * D + 255) / 256, a.H);
-  if (flags) hipLaunchKernelGGL((block_stats_kernel<T, D, true>), g1, dim3(256), 0, s, a, flags);
+  if (flags & 3u) hipLaunchKernelGGL((block_stats_kernel<T, D, true>), g1, dim3(256), 0, s, a, flags);
   else hipLaunchKernelGGL((block_stats_kernel<T, D, false>), g1, dim3(256), 0, s, a, flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((hbar_reduce_kernel<T, D>), g2, dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (flags & 4u) {
+    hipLaunchKernelGGL((heterogeneity_kernel<T, D>), g1, dim3(256), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(tile_order_kernel, dim3(1), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -53,6 +53,7 @@ struct StatsArgs {
   float* hbarT;
   float* hblk;
   float* cblk;
+  float* hnorm;    // [H][nb] or null
   char* packed;
   float* part;     // [H][ngroups][d][d]
   int H, L, d, nb, nbp, G, ngroups;
@@ -63,6 +64,8 @@ struct SelectArgs {
   const void* Q;
   const float* kbar;
   const float* ksig2;
+  const float* hnorm;  // [H][nb] M_j, or null for block-mean scoring
+  float route_eps;
   const int32_t* block_len;
   float* qbar;     // [H][nb][d]   workspace
   float* qsq;      // [H][nb][d]   workspace

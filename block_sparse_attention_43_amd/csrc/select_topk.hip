@@ -7,7 +7,10 @@
 // blog Sparse Attention section) and w̃_{i,j} = ½ Σ_c \overline{q²}_{i,c} σ²_{j,c}, the
 // [query block x key block] matrix that PWT computes once before the attention kernel.
 // S_i keeps the K_sel largest scores, ties to the lower block index, emitted in
-// ascending block order plus a bitmask of the selected blocks.
+// ascending block order plus a bitmask of the selected blocks. Covariance-aware routing
+// (PISA paper §3.3, Eq. (7)) adds ln(M_j + eps) of the block heterogeneity to every score
+// of key block j; the row softmax of Eq. (7) keeps the order, so the top-K is taken on
+// the sum.
 //
 // Scores are fp32 (matrix-core fp32 products and sums) with one fixed summation order per
 // element, so identical centroids score identically. Top-K is an exact radix select on
@@ -81,7 +84,8 @@ __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int h = blockIdx.z, i0 = blockIdx.y * 64, j0 = blockIdx.x * 64, nb = a.nb;
   const int wi = (wave >> 1) * 32, wj = (wave & 1) * 32;
-  auto tile = [&](const float* A, const float* B, float* out, float scale) {
+  // bias: per key block ln(M_j + eps) added to the product (covariance-aware scores), or null.
+  auto tile = [&](const float* A, const float* B, float* out, float scale, const float* bias) {
 #pragma unroll
     for (int p = 0; p < NCH; ++p) {          // rows past nb read a valid row, not stored
       const int q = tid + 256 * p, r = q / CPR, col = 4 * (q % CPR);
@@ -105,16 +109,17 @@ __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
     }
     const int col = j0 + wj + c;
     if (col < nb) {
+      const float lb = bias ? logf(bias[size_t(h) * nb + col] + a.route_eps) : 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = i0 + wi + acc_row(r, g);
-        if (row < nb) out[(size_t(h) * nb + row) * nb + col] = acc[r] * scale;
+        if (row < nb) out[(size_t(h) * nb + row) * nb + col] = bias ? acc[r] * scale + lb : acc[r] * scale;
       }
     }
     __syncthreads();                         // LDS reused by the next product
   };
-  tile(a.qbar, a.kbar, a.scores, 1.f);
-  if (a.wt) tile(a.qsq, a.ksig2, a.wt, 0.5f);
+  tile(a.qbar, a.kbar, a.scores, 1.f, a.hnorm);
+  if (a.wt) tile(a.qsq, a.ksig2, a.wt, 0.5f, nullptr);
 }
 
 __device__ __forceinline__ uint32_t order_key(float s) {

@@ -18,13 +18,17 @@ LIB_PATH = os.path.join(_HERE, "libpisa.so")
 PISA_F32, PISA_BF16 = 0, 1
 MODE_DROP, MODE_PISA, MODE_PWT, MODE_LITERAL = 0, 1, 2, 3
 W_LINEAR, W_EXP, W_NOGATE = 1 << 4, 1 << 5, 1 << 6
-STATS_BLOCK_H, STATS_BLOCK_C = 1 << 0, 1 << 1
+STATS_BLOCK_H, STATS_BLOCK_C, STATS_HNORM = 1 << 0, 1 << 1, 1 << 2
+ROUTE_MEAN, ROUTE_COVARIANCE = 0, 1
+ROUTES = {"mean": ROUTE_MEAN, "covariance": ROUTE_COVARIANCE}
+ROUTE_EPS = 1e-6          # ε of ln(M_j + ε) in covariance-aware scores
 MODES = {"drop": MODE_DROP, "pisa": MODE_PISA, "pwt": MODE_PWT, "literal": MODE_LITERAL}
 B = 64
 
 # Every symbol include/pisa.h declares.
 EXPORTS = ("pisa_packed_bytes", "pisa_block_stats_workspace_bytes", "pisa_block_stats",
-           "pisa_select_workspace_bytes", "pisa_select_topk", "pisa_attention_fwd",
+           "pisa_select_workspace_bytes", "pisa_select_topk", "pisa_select_topk_routed",
+           "pisa_attention_fwd",
            "pisa_last_error", "pisa_version")
 
 
@@ -37,7 +41,7 @@ class PisaError(RuntimeError):
 class _Stats(ctypes.Structure):
     _fields_ = [("kbar", ctypes.c_void_p), ("vsum", ctypes.c_void_p), ("ksig2", ctypes.c_void_p),
                 ("hbarT", ctypes.c_void_p), ("hblk", ctypes.c_void_p), ("cblk", ctypes.c_void_p),
-                ("packed", ctypes.c_void_p)]
+                ("packed", ctypes.c_void_p), ("hnorm", ctypes.c_void_p)]
 
 
 _lib = None
@@ -63,6 +67,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pisa_block_stats.restype = i32
     lib.pisa_select_topk.argtypes = [i32, vp, sp, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.pisa_select_topk.restype = i32
+    lib.pisa_select_topk_routed.argtypes = [i32, vp, sp, i32, i32, i32, i32, vp, i32, u32, ctypes.c_float,
+                                            vp, vp, vp, vp, sz, vp]
+    lib.pisa_select_topk_routed.restype = i32
     lib.pisa_attention_fwd.argtypes = [i32, vp, vp, vp, sp, vp, vp, vp, i32, i32, i32, i32, vp, i32,
                                        u32, vp, vp, vp]
     lib.pisa_attention_fwd.restype = i32
@@ -113,10 +120,12 @@ class Stats:
     packed: torch.Tensor
     hblk: torch.Tensor | None = None
     cblk: torch.Tensor | None = None
+    hnorm: torch.Tensor | None = None
 
     def struct(self) -> _Stats:
         return _Stats(self.kbar.data_ptr(), self.vsum.data_ptr(), self.ksig2.data_ptr(),
-                      self.hbarT.data_ptr(), _ptr(self.hblk), _ptr(self.cblk), self.packed.data_ptr())
+                      self.hbarT.data_ptr(), _ptr(self.hblk), _ptr(self.cblk), self.packed.data_ptr(),
+                      _ptr(self.hnorm))
 
 
 def packed_bytes(dtype: torch.dtype, H: int, L: int, d: int) -> int:
@@ -133,7 +142,8 @@ def alloc_stats(K: torch.Tensor, flags: int = 0) -> Stats:
                  ksig2=torch.empty(H, nb, d, **f), hbarT=torch.empty(H, d, d, **f),
                  packed=torch.empty(packed_bytes(K.dtype, H, L, d), dtype=torch.uint8, device=dev),
                  hblk=torch.empty(H, nb, d, d, **f) if flags & STATS_BLOCK_H else None,
-                 cblk=torch.empty(H, nb, d, d, **f) if flags & STATS_BLOCK_C else None)
+                 cblk=torch.empty(H, nb, d, d, **f) if flags & STATS_BLOCK_C else None,
+                 hnorm=torch.empty(H, nb, **f) if flags & STATS_HNORM else None)
 
 
 def block_stats(K, V, block_len=None, flags: int = 0, out: Stats | None = None, workspace=None,
@@ -151,9 +161,10 @@ def block_stats(K, V, block_len=None, flags: int = 0, out: Stats | None = None, 
 
 
 def select_topk(Q, st: Stats, K_sel: int, block_len=None, want_wt: bool = True, want_mask: bool = True,
-                out=None, workspace=None, stream=None):
+                out=None, workspace=None, stream=None, route="mean", eps: float = ROUTE_EPS):
     """Returns (idx [H, nb, K_sel] int32, mask [H, nb, nw] int32 bit pattern or None,
-    wt [H, nb, nb] float32 or None)."""
+    wt [H, nb, nb] float32 or None). route="covariance" needs st.hnorm (block_stats with
+    STATS_HNORM)."""
     lib = load()
     H, L, d = _shape(Q)
     nb = L // B
@@ -167,10 +178,11 @@ def select_topk(Q, st: Stats, K_sel: int, block_len=None, want_wt: bool = True, 
     need = lib.pisa_select_workspace_bytes(H, L, d, B)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    r = ROUTES[route] if isinstance(route, str) else int(route)
     s = st.struct()
-    _check(lib.pisa_select_topk(_dtype_code(Q), _ptr(Q), ctypes.byref(s), H, L, d, B, _ptr(block_len),
-                                K_sel, _ptr(idx), _ptr(mask), _ptr(wt), _ptr(workspace),
-                                workspace.numel(), _stream(stream)))
+    _check(lib.pisa_select_topk_routed(_dtype_code(Q), _ptr(Q), ctypes.byref(s), H, L, d, B,
+                                       _ptr(block_len), K_sel, r, eps, _ptr(idx), _ptr(mask), _ptr(wt),
+                                       _ptr(workspace), workspace.numel(), _stream(stream)))
     return idx, mask, wt
 
 
@@ -190,11 +202,14 @@ def attention_fwd(Q, K, V, st: Stats, idx, mask, wt, K_sel: int, mode="pwt", blo
     return out, lse
 
 
-def forward(Q, K, V, K_sel: int, mode="pwt", block_len=None, flags: int = 0, stream=None):
+def forward(Q, K, V, K_sel: int, mode="pwt", block_len=None, flags: int = 0, stream=None, route="mean"):
     """One full pass: statistics, selection, fused attention. Returns (O, lse, idx, stats)."""
     base = (MODES[mode] if isinstance(mode, str) else int(mode)) & 15
-    st = block_stats(K, V, block_len, stream=stream)
-    idx, mask, wt = select_topk(Q, st, K_sel, block_len, want_wt=(base == MODE_PWT), stream=stream)
+    r = ROUTES[route] if isinstance(route, str) else int(route)
+    st = block_stats(K, V, block_len, flags=flags | (STATS_HNORM if r == ROUTE_COVARIANCE else 0),
+                     stream=stream)
+    idx, mask, wt = select_topk(Q, st, K_sel, block_len, want_wt=(base == MODE_PWT), stream=stream,
+                                route=r)
     O, lse = attention_fwd(Q, K, V, st, idx, mask, wt, K_sel, mode, block_len, stream=stream)
     return O, lse, idx, st
 

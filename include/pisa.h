@@ -90,7 +90,15 @@ enum {
 /* Flags of pisa_block_stats. */
 enum {
   PISA_STATS_BLOCK_H = 1u << 0, /* also write every H_j to pisa_stats.hblk */
-  PISA_STATS_BLOCK_C = 1u << 1  /* also write every C_j to pisa_stats.cblk */
+  PISA_STATS_BLOCK_C = 1u << 1, /* also write every C_j to pisa_stats.cblk */
+  PISA_STATS_HNORM = 1u << 2    /* also write M_j = ||H_j - H̄||_F to pisa_stats.hnorm
+                                   (a second pass over K and V) */
+};
+
+/* Selection rules of pisa_select_topk_routed. */
+enum {
+  PISA_ROUTE_MEAN = 0,       /* s_{i,j} = q̄_i·k̄_j (block-mean scoring) */
+  PISA_ROUTE_COVARIANCE = 1  /* s_{i,j} = q̄_i·k̄_j + ln(M_j + eps) (covariance-aware) */
 };
 
 /*
@@ -103,6 +111,9 @@ enum {
  *   hbarT [H][d][d]    H̄ᵀ[c][e] with H̄ = (1/nb) Σ_j H_j, H_j = Σ_{I_j} v_i (k_i - k̄_j)ᵀ
  *   hblk  [H][nb][d][d] H_j[e][c]              (NULL unless PISA_STATS_BLOCK_H)
  *   cblk  [H][nb][d][d] C_j = (1/n_j) Σ (k_i - k̄_j)(k_i - k̄_j)ᵀ (NULL unless PISA_STATS_BLOCK_C)
+ *   hnorm [H][nb]      M_j = ||H_j - H̄||_F, the block's heterogeneity against the global
+ *                      first-order statistic (PISA paper §3.3, Error Analysis and
+ *                      Covariance-Aware Block Selection; NULL unless PISA_STATS_HNORM)
  *   packed             pisa_packed_bytes() bytes: the same statistics re-laid for the
  *                      attention kernel's operands (plus Vᵀ per block) and the order in
  *                      which it visits query tiles; opaque, written by pisa_block_stats
@@ -116,6 +127,7 @@ typedef struct {
   float* hblk;
   float* cblk;
   void* packed;
+  float* hnorm;
 } pisa_stats;
 
 /* Bytes of pisa_stats.packed for these sizes (0 if unsupported). */
@@ -127,8 +139,8 @@ size_t pisa_block_stats_workspace_bytes(int H, int L, int d, int B);
 /*
  * Prepare phase, part 1 (PISA paper §3.4 "Prepare Phase": block centroids, value sums
  * and the global statistic H̄ in a single pass; blog, PWT section: σ²_j).
- * K, V: [H][L][d] device tensors of dtype `dt`. Writes every field of *out (hblk / cblk
- * only when flagged). `out` is a host pointer to a struct of device pointers.
+ * K, V: [H][L][d] device tensors of dtype `dt`. Writes every field of *out (hblk / cblk /
+ * hnorm only when flagged). `out` is a host pointer to a struct of device pointers.
  * Repeated calls on the same inputs give bit-identical results.
  */
 pisa_status pisa_block_stats(pisa_dtype dt, const void* K, const void* V, int H, int L, int d,
@@ -158,6 +170,22 @@ pisa_status pisa_select_topk(pisa_dtype dt, const void* Q, const pisa_stats* st,
                              int d, int B, const int32_t* block_len, int K_sel, int32_t* idx,
                              uint32_t* mask, float* wt, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/*
+ * pisa_select_topk with a choice of block score (PISA paper §3.3, Covariance-Aware Block
+ * Selection, Eq. (7)). PISA_ROUTE_COVARIANCE ranks key block j for query tile i by
+ * q̄_i·k̄_j + ln(M_j + eps), with M_j read from st->hnorm (pisa_block_stats with
+ * PISA_STATS_HNORM on the same K, V). Eq. (7) normalises this score with a softmax over
+ * the blocks, which leaves the order within a row, and so the top-K set, unchanged; the
+ * pooled q̄_i stands for the query as in block-mean scoring. eps must be finite and > 0.
+ * wt is w̃ as in pisa_select_topk (the routing term does not enter it).
+ * PISA_ROUTE_MEAN gives exactly pisa_select_topk.
+ */
+pisa_status pisa_select_topk_routed(pisa_dtype dt, const void* Q, const pisa_stats* st, int H,
+                                    int L, int d, int B, const int32_t* block_len, int K_sel,
+                                    unsigned route, float eps, int32_t* idx, uint32_t* mask,
+                                    float* wt, void* workspace, size_t workspace_bytes,
+                                    void* stream);
 
 /*
  * Fused kernel (PISA paper §3.4 phases 1-3; Eq. (3.2); blog, PWT section).

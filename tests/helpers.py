@@ -28,11 +28,13 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 
 
 def gpu_run(pisa, inp: synth.Inputs, mode: str, K_sel: int, flags: int = 0, mode_bits: int = 0,
-            tensors=None):
+            tensors=None, route: str = "mean"):
     Q, K, V, blt = tensors if tensors is not None else to_device(inp)
     base = pisa.MODES[mode]
+    if route == "covariance":
+        flags |= pisa.STATS_HNORM
     st = pisa.block_stats(K, V, blt, flags=flags)
-    idx, mask, wt = pisa.select_topk(Q, st, K_sel, blt, want_wt=True)
+    idx, mask, wt = pisa.select_topk(Q, st, K_sel, blt, want_wt=True, route=route)
     O, lse = pisa.attention_fwd(Q, K, V, st, idx, mask, wt if base == pisa.MODE_PWT else None, K_sel,
                                 base | mode_bits, blt)
     torch.cuda.synchronize()
@@ -41,21 +43,33 @@ def gpu_run(pisa, inp: synth.Inputs, mode: str, K_sel: int, flags: int = 0, mode
                 kbar=to_f64(st.kbar), vsum=to_f64(st.vsum), ksig2=to_f64(st.ksig2),
                 hbarT=to_f64(st.hbarT),
                 hblk=None if st.hblk is None else to_f64(st.hblk),
-                cblk=None if st.cblk is None else to_f64(st.cblk))
+                cblk=None if st.cblk is None else to_f64(st.cblk),
+                hnorm=None if st.hnorm is None else to_f64(st.hnorm))
 
 
-def oracle_selection(inp: synth.Inputs, K_sel: int):
+def oracle_scores(inp: synth.Inputs, h: int, route: str = "mean"):
+    """The oracle's block scores of head h (block-mean, or covariance-aware with its own
+    M_j) and its PWT weights, from the seeded inputs only."""
+    from oracle import pisa_oracle as orc
+    bl = inp.layout.block_len
+    st = orc.block_stats(inp.f64("K", h), inp.f64("V", h), 64, bl, per_block=(route == "covariance"))
+    pq = orc.pool_queries(inp.f64("Q", h), 64, bl)
+    if route == "covariance":
+        s = orc.routed_scores(pq["qbar"], st["kbar"], orc.block_heterogeneity(st))
+    else:
+        s = orc.block_scores(pq["qbar"], st["kbar"])
+    return s, orc.pooled_w(pq["qsq"], st["sig2"])
+
+
+def oracle_selection(inp: synth.Inputs, K_sel: int, route: str = "mean"):
     """The oracle's own selection and PWT weights for every head, from the seeded inputs
     only: idx [H, nb, K_sel] (ascending) and w [H, nb, nb] (before the gate)."""
     from oracle import pisa_oracle as orc
-    bl = inp.layout.block_len
     idx = np.zeros((inp.H, inp.nb, K_sel), dtype=np.int64)
     w = np.zeros((inp.H, inp.nb, inp.nb))
     for h in range(inp.H):
-        st = orc.block_stats(inp.f64("K", h), inp.f64("V", h), 64, bl, per_block=False)
-        pq = orc.pool_queries(inp.f64("Q", h), 64, bl)
-        idx[h] = orc.select_topk(orc.block_scores(pq["qbar"], st["kbar"]), K_sel)
-        w[h] = orc.pooled_w(pq["qsq"], st["sig2"])
+        s, w[h] = oracle_scores(inp, h, route)
+        idx[h] = orc.select_topk(s, K_sel)
     return idx, w
 
 
@@ -136,3 +150,28 @@ def check_selection(gpu_idx: np.ndarray, scores: np.ndarray, K_sel: int, rtol: f
             assert all(j in got for j in range(nb) if s[j] > kth + tol), f"tile {i}: missed a clear winner"
             near += 1
     return exact, near, min_gap
+
+
+def small_case(name):
+    """Seeded parity case by name: (inputs, K_sel). Several tiles, ragged blocks, both
+    dtypes and head sizes, a partial centroid group (nb = 70, 130)."""
+    if name == "tiny":
+        return synth.make("tiny"), 4
+    if name == "bf16_d128_ragged":
+        bl = [64, 64, 17, 64, 1, 64, 40, 64, 64, 33]
+        return synth.random_blocks(101, H=2, nb=10, d=128, dtype="bf16", block_len=bl, smooth=2.0), 3
+    if name == "bf16_d64":
+        return synth.random_blocks(102, H=3, nb=7, d=64, dtype="bf16", smooth=2.0), 2
+    if name == "f32_d128_ragged":
+        bl = [64, 8, 64, 64, 50, 64, 64, 2, 64]
+        return synth.random_blocks(103, H=2, nb=9, d=128, dtype="f32", block_len=bl, smooth=2.0), 4
+    if name == "bf16_nb70":
+        return synth.random_blocks(104, H=1, nb=70, d=128, dtype="bf16", smooth=2.0), 9
+    if name == "f32_d64_ragged_nb130":
+        bl = np.full(130, 64)
+        bl[[3, 64, 129]] = [5, 63, 1]
+        return synth.random_blocks(105, H=1, nb=130, d=64, dtype="f32", block_len=bl, smooth=1.0), 13
+    raise KeyError(name)
+
+
+CASES = ["tiny", "bf16_d128_ragged", "bf16_d64", "f32_d128_ragged", "bf16_nb70", "f32_d64_ragged_nb130"]

@@ -15,8 +15,8 @@ import torch
 
 from block_sparse_attention_43_amd import synth
 from oracle import pisa_oracle as orc
-from helpers import (MODE_NAMES, check_selection, gpu_attention_on, gpu_run, mask_to_sets,
-                     oracle_selection, rel_l2, to_device, valid_rows)
+from helpers import (CASES, MODE_NAMES, check_selection, gpu_attention_on, gpu_run, mask_to_sets,
+                     oracle_selection, rel_l2, small_case, to_device, valid_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,27 +25,7 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}
 TOL_SAME_SEL = {"f32": 1e-4, "bf16": 1e-2}
 
 
-def _case(name):
-    if name == "tiny":
-        return synth.make("tiny"), 4
-    if name == "bf16_d128_ragged":
-        bl = [64, 64, 17, 64, 1, 64, 40, 64, 64, 33]
-        return synth.random_blocks(101, H=2, nb=10, d=128, dtype="bf16", block_len=bl, smooth=2.0), 3
-    if name == "bf16_d64":
-        return synth.random_blocks(102, H=3, nb=7, d=64, dtype="bf16", smooth=2.0), 2
-    if name == "f32_d128_ragged":
-        bl = [64, 8, 64, 64, 50, 64, 64, 2, 64]
-        return synth.random_blocks(103, H=2, nb=9, d=128, dtype="f32", block_len=bl, smooth=2.0), 4
-    if name == "bf16_nb70":
-        return synth.random_blocks(104, H=1, nb=70, d=128, dtype="bf16", smooth=2.0), 9
-    if name == "f32_d64_ragged_nb130":
-        bl = np.full(130, 64)
-        bl[[3, 64, 129]] = [5, 63, 1]
-        return synth.random_blocks(105, H=1, nb=130, d=64, dtype="f32", block_len=bl, smooth=1.0), 13
-    raise KeyError(name)
-
-
-CASES = ["tiny", "bf16_d128_ragged", "bf16_d64", "f32_d128_ragged", "bf16_nb70", "f32_d64_ragged_nb130"]
+_case = small_case
 
 
 def _oracle(inp, h, mode, K_sel, idx=None, **kw):
