@@ -163,6 +163,21 @@ def routed_scores(qbar: np.ndarray, kbar: np.ndarray, hnorm: np.ndarray, eps: fl
     return block_scores(qbar, kbar) + np.log(np.asarray(hnorm, dtype=np.float64) + eps)[None, :]
 
 
+def error_routed_scores(qbar: np.ndarray, kbar: np.ndarray, w: np.ndarray, n: np.ndarray,
+                        hnorm: np.ndarray, eps: float = ROUTE_EPS) -> np.ndarray:
+    """Routing by predicted truncation error (blog, PWT section: a block's truncation error
+    is roughly its mass times its within-block heterogeneity, so the log of the block's
+    virtual-token mass n_j e^{q·k̄_j + w} plus the log of its heterogeneity ranks the
+    blocks; the PISA paper's covariance-aware selection is this view of routing).
+    Score: q̄_i·k̄_j + w̃_{i,j} + ln n_j + ln(M_j + ε), with the pooled q̄_i and w̃_{i,j}
+    of the tile (before the gate: a block whose expansion fails is the one to keep
+    exact), n_j the valid count (B for a full block) and M_j = ||H_j - H̄||_F as in
+    Eq. (7) of the PISA paper."""
+    n = np.asarray(n, dtype=np.float64)
+    return (block_scores(qbar, kbar) + np.asarray(w, dtype=np.float64) + np.log(n)[None, :]
+            + np.log(np.asarray(hnorm, dtype=np.float64) + eps)[None, :])
+
+
 def select_topk(scores: np.ndarray, K_sel: int) -> np.ndarray:
     """S_i = the K_sel largest scores of row i, ties to the lower block index; returned
     in ascending block order, shape [nq, K_sel] int64."""

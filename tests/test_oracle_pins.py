@@ -540,3 +540,51 @@ def test_error_ordering_on_gaussian_inputs():
     assert e["drop"] > e["pisa0"] > e["pisa"] > e["literal"]
     assert e["pwt"] < e["pisa"]
     assert e["pwt"] < e["pwt_meansq"]
+
+
+def test_error_routing_mass_term_prefers_larger_blocks():
+    """Blocks of one repeated token (k0, v0) but different valid counts: centroids,
+    w̃ = 0 and M_j = 0 all tie, so routing by predicted truncation error (blog, PWT
+    section) ranks the blocks by their mass n_j alone, ties to the lower index, while
+    block-mean scores agree up to rounding."""
+    r = np.random.default_rng(23)
+    B, d = 8, 5
+    bl = np.array([2, 8, 3, 8, 1, 5])
+    nb = len(bl)
+    k0, v0 = r.standard_normal(d), r.standard_normal(d)
+    K = np.tile(k0, (B * nb, 1))
+    V = np.tile(v0, (B * nb, 1))
+    st = orc.block_stats(K, V, B, bl)
+    m = orc.block_heterogeneity(st)
+    assert np.all(m < 1e-12)
+    pq = orc.pool_queries(r.standard_normal((B * nb, d)), B, bl)
+    w = orc.pooled_w(pq["qsq"], st["sig2"])
+    assert np.all(np.abs(w) < 1e-12)
+    s = orc.error_routed_scores(pq["qbar"], st["kbar"], w, bl, m)
+    assert np.all(orc.select_topk(s, 1)[:, 0] == 1)
+    assert np.all(orc.select_topk(s, 3) == [1, 3, 5])
+    plain = orc.block_scores(pq["qbar"], st["kbar"])
+    assert np.allclose(plain, plain[:, :1], rtol=1e-12, atol=1e-12)
+
+
+def test_error_routing_second_order_term_prefers_wider_blocks():
+    """V = 0 makes every H_j and M_j zero; keys share one centroid with a spread growing
+    with j, so the second-order mass w̃_{i,j} = ½ Σ_c mean(q_c²) σ²_{j,c} grows with j and
+    alone decides the routing: the widest blocks win, in every tile."""
+    r = np.random.default_rng(24)
+    B, nb, d = 4, 6, 5
+    c = r.standard_normal(d)
+    u = r.standard_normal((B, d))
+    u -= u.mean(axis=0)
+    K = np.concatenate([c + 0.2 * (j + 1) * u for j in range(nb)])
+    V = np.zeros((B * nb, d))
+    st = orc.block_stats(K, V, B)
+    m = orc.block_heterogeneity(st)
+    assert np.all(m == 0.0)
+    pq = orc.pool_queries(r.standard_normal((B * nb, d)), B)
+    w = orc.pooled_w(pq["qsq"], st["sig2"])
+    assert np.all(np.diff(w, axis=1) > 0)
+    s = orc.error_routed_scores(pq["qbar"], st["kbar"], w, np.full(nb, B), m)
+    assert np.all(orc.select_topk(s, 2) == [nb - 2, nb - 1])
+    # the same blocks under Eq. (7)'s score tie (equal centroids, equal M_j): lowest indices
+    assert np.all(orc.select_topk(orc.routed_scores(pq["qbar"], st["kbar"], m), 2) == [0, 1])
