@@ -142,7 +142,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="wan", help="tiny | flux | wan | hunyuan | long")
     ap.add_argument("--mode", default="pwt", help="drop | pisa | pwt | literal")
-    ap.add_argument("--route", default="mean", help="mean | covariance (block selection score)")
+    ap.add_argument("--route", default="mean", help="mean | covariance | error (block selection score)")
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -194,7 +194,7 @@ def main():
 
     # every buffer allocated once, outside the timed region
     route = args.route
-    sflags = pisa.STATS_HNORM if route == "covariance" else 0
+    sflags = pisa.STATS_HNORM if route != "mean" else 0
     st = pisa.alloc_stats(K, sflags)
     ws_stats = torch.empty(max(pisa.load().pisa_block_stats_workspace_bytes(H, L, d, 64), 16),
                            dtype=torch.uint8, device="cuda")

@@ -149,8 +149,8 @@ pisa_status pisa_select_topk_routed(pisa_dtype dt, const void* Q, const pisa_sta
   PISA_TRY(check_ptr(st, "st", false));
   PISA_TRY(check_ptr(st->kbar, "st->kbar"));
   PISA_TRY(check_ptr(st->ksig2, "st->ksig2"));
-  if (route > PISA_ROUTE_COVARIANCE) return fail(PISA_ERR_INVALID_ARG, "unknown route %u", route);
-  if (route == PISA_ROUTE_COVARIANCE) {
+  if (route > PISA_ROUTE_ERROR) return fail(PISA_ERR_INVALID_ARG, "unknown route %u", route);
+  if (route != PISA_ROUTE_MEAN) {
     PISA_TRY(check_ptr(st->hnorm, "st->hnorm", false));
     if (!(eps > 0.f) || eps > 3.0e38f) return fail(PISA_ERR_INVALID_ARG, "eps must be finite and > 0 (got %g)", double(eps));
   }
@@ -166,8 +166,9 @@ pisa_status pisa_select_topk_routed(pisa_dtype dt, const void* Q, const pisa_sta
   a.Q = Q;
   a.kbar = st->kbar;
   a.ksig2 = st->ksig2;
-  a.hnorm = route == PISA_ROUTE_COVARIANCE ? st->hnorm : nullptr;
+  a.hnorm = route != PISA_ROUTE_MEAN ? st->hnorm : nullptr;
   a.route_eps = eps;
+  a.route = int(route);
   a.block_len = block_len;
   a.qbar = static_cast<float*>(workspace);
   a.qsq = a.qbar + size_t(H) * nb * d;

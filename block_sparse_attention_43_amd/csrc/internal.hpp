@@ -64,8 +64,9 @@ struct SelectArgs {
   const void* Q;
   const float* kbar;
   const float* ksig2;
-  const float* hnorm;  // [H][nb] M_j, or null for block-mean scoring
+  const float* hnorm;  // [H][nb] M_j (routes 1, 2)
   float route_eps;
+  int route;           // 0 block mean, 1 + ln(M_j + eps), 2 + w̃ + ln n_j + ln(M_j + eps)
   const int32_t* block_len;
   float* qbar;     // [H][nb][d]   workspace
   float* qsq;      // [H][nb][d]   workspace

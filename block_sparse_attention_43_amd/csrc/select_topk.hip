@@ -10,7 +10,8 @@
 // ascending block order plus a bitmask of the selected blocks. Covariance-aware routing
 // (PISA paper §3.3, Eq. (7)) adds ln(M_j + eps) of the block heterogeneity to every score
 // of key block j; the row softmax of Eq. (7) keeps the order, so the top-K is taken on
-// the sum.
+// the sum. Routing by predicted truncation error (Sparse Linear Attention blog, PWT
+// section: mass times heterogeneity) adds w̃_{i,j} + ln n_j on top.
 //
 // Scores are fp32 (matrix-core fp32 products and sums) with one fixed summation order per
 // element, so identical centroids score identically. Top-K is an exact radix select on
@@ -84,15 +85,15 @@ __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int h = blockIdx.z, i0 = blockIdx.y * 64, j0 = blockIdx.x * 64, nb = a.nb;
   const int wi = (wave >> 1) * 32, wj = (wave & 1) * 32;
-  // bias: per key block ln(M_j + eps) added to the product (covariance-aware scores), or null.
-  auto tile = [&](const float* A, const float* B, float* out, float scale, const float* bias) {
+  const int col = j0 + wj + c;
+  auto product = [&](const float* A, const float* B) {
 #pragma unroll
     for (int p = 0; p < NCH; ++p) {          // rows past nb read a valid row, not stored
-      const int q = tid + 256 * p, r = q / CPR, col = 4 * (q % CPR);
-      const float4 va = *reinterpret_cast<const float4*>(A + (size_t(h) * nb + min(i0 + r, nb - 1)) * D + col);
-      const float4 vb = *reinterpret_cast<const float4*>(B + (size_t(h) * nb + min(j0 + r, nb - 1)) * D + col);
-      *reinterpret_cast<float4*>(&sA[r * RS + col]) = va;
-      *reinterpret_cast<float4*>(&sB[r * RS + col]) = vb;
+      const int q = tid + 256 * p, r = q / CPR, cc = 4 * (q % CPR);
+      const float4 va = *reinterpret_cast<const float4*>(A + (size_t(h) * nb + min(i0 + r, nb - 1)) * D + cc);
+      const float4 vb = *reinterpret_cast<const float4*>(B + (size_t(h) * nb + min(j0 + r, nb - 1)) * D + cc);
+      *reinterpret_cast<float4*>(&sA[r * RS + cc]) = va;
+      *reinterpret_cast<float4*>(&sB[r * RS + cc]) = vb;
     }
     __syncthreads();
     const float* pa = &sA[(wi + c) * RS + KH * g];
@@ -107,19 +108,36 @@ __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y.z, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, y.w, acc, 0, 0, 0);
     }
-    const int col = j0 + wj + c;
-    if (col < nb) {
-      const float lb = bias ? logf(bias[size_t(h) * nb + col] + a.route_eps) : 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = i0 + wi + acc_row(r, g);
-        if (row < nb) out[(size_t(h) * nb + row) * nb + col] = bias ? acc[r] * scale + lb : acc[r] * scale;
-      }
-    }
     __syncthreads();                         // LDS reused by the next product
+    return acc;
   };
-  tile(a.qbar, a.kbar, a.scores, 1.f, a.hnorm);
-  if (a.wt) tile(a.qsq, a.ksig2, a.wt, 0.5f, nullptr);
+  auto store = [&](float* out, const f32x16& v) {
+    if (col >= nb) return;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = i0 + wi + acc_row(r, g);
+      if (row < nb) out[(size_t(h) * nb + row) * nb + col] = v[r];
+    }
+  };
+  f32x16 w = zero16();
+  if (a.wt || a.route == 2) {
+    w = product(a.qsq, a.ksig2);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) w[r] *= 0.5f;
+    if (a.wt) store(a.wt, w);
+  }
+  f32x16 s = product(a.qbar, a.kbar);
+  if (a.route != 0 && col < nb) {
+    // per key block: ln(M_j + eps) (Eq. (7)), plus ln n_j and w̃ for the predicted-error route
+    float bias = logf(a.hnorm[size_t(h) * nb + col] + a.route_eps);
+    if (a.route == 2) {
+      const int n = a.block_len ? min(max(a.block_len[col], 1), kB) : kB;
+      bias += logf(float(n));
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = (a.route == 2 ? s[r] + w[r] : s[r]) + bias;
+  }
+  store(a.scores, s);
 }
 
 __device__ __forceinline__ uint32_t order_key(float s) {

@@ -19,8 +19,8 @@ PISA_F32, PISA_BF16 = 0, 1
 MODE_DROP, MODE_PISA, MODE_PWT, MODE_LITERAL = 0, 1, 2, 3
 W_LINEAR, W_EXP, W_NOGATE = 1 << 4, 1 << 5, 1 << 6
 STATS_BLOCK_H, STATS_BLOCK_C, STATS_HNORM = 1 << 0, 1 << 1, 1 << 2
-ROUTE_MEAN, ROUTE_COVARIANCE = 0, 1
-ROUTES = {"mean": ROUTE_MEAN, "covariance": ROUTE_COVARIANCE}
+ROUTE_MEAN, ROUTE_COVARIANCE, ROUTE_ERROR = 0, 1, 2
+ROUTES = {"mean": ROUTE_MEAN, "covariance": ROUTE_COVARIANCE, "error": ROUTE_ERROR}
 ROUTE_EPS = 1e-6          # ε of ln(M_j + ε) in covariance-aware scores
 MODES = {"drop": MODE_DROP, "pisa": MODE_PISA, "pwt": MODE_PWT, "literal": MODE_LITERAL}
 B = 64
@@ -163,8 +163,8 @@ def block_stats(K, V, block_len=None, flags: int = 0, out: Stats | None = None, 
 def select_topk(Q, st: Stats, K_sel: int, block_len=None, want_wt: bool = True, want_mask: bool = True,
                 out=None, workspace=None, stream=None, route="mean", eps: float = ROUTE_EPS):
     """Returns (idx [H, nb, K_sel] int32, mask [H, nb, nw] int32 bit pattern or None,
-    wt [H, nb, nb] float32 or None). route="covariance" needs st.hnorm (block_stats with
-    STATS_HNORM)."""
+    wt [H, nb, nb] float32 or None). route="covariance" or "error" needs st.hnorm
+    (block_stats with STATS_HNORM)."""
     lib = load()
     H, L, d = _shape(Q)
     nb = L // B
@@ -206,7 +206,7 @@ def forward(Q, K, V, K_sel: int, mode="pwt", block_len=None, flags: int = 0, str
     """One full pass: statistics, selection, fused attention. Returns (O, lse, idx, stats)."""
     base = (MODES[mode] if isinstance(mode, str) else int(mode)) & 15
     r = ROUTES[route] if isinstance(route, str) else int(route)
-    st = block_stats(K, V, block_len, flags=flags | (STATS_HNORM if r == ROUTE_COVARIANCE else 0),
+    st = block_stats(K, V, block_len, flags=flags | (STATS_HNORM if r != ROUTE_MEAN else 0),
                      stream=stream)
     idx, mask, wt = select_topk(Q, st, K_sel, block_len, want_wt=(base == MODE_PWT), stream=stream,
                                 route=r)

@@ -97,8 +97,10 @@ enum {
 
 /* Selection rules of pisa_select_topk_routed. */
 enum {
-  PISA_ROUTE_MEAN = 0,       /* s_{i,j} = q̄_i·k̄_j (block-mean scoring) */
-  PISA_ROUTE_COVARIANCE = 1  /* s_{i,j} = q̄_i·k̄_j + ln(M_j + eps) (covariance-aware) */
+  PISA_ROUTE_MEAN = 0,        /* s_{i,j} = q̄_i·k̄_j (block-mean scoring) */
+  PISA_ROUTE_COVARIANCE = 1,  /* s_{i,j} = q̄_i·k̄_j + ln(M_j + eps) (covariance-aware) */
+  PISA_ROUTE_ERROR = 2        /* s_{i,j} = q̄_i·k̄_j + w̃_{i,j} + ln n_j + ln(M_j + eps)
+                                 (predicted truncation error: mass times heterogeneity) */
 };
 
 /*
@@ -177,9 +179,11 @@ pisa_status pisa_select_topk(pisa_dtype dt, const void* Q, const pisa_stats* st,
  * q̄_i·k̄_j + ln(M_j + eps), with M_j read from st->hnorm (pisa_block_stats with
  * PISA_STATS_HNORM on the same K, V). Eq. (7) normalises this score with a softmax over
  * the blocks, which leaves the order within a row, and so the top-K set, unchanged; the
- * pooled q̄_i stands for the query as in block-mean scoring. eps must be finite and > 0.
- * wt is w̃ as in pisa_select_topk (the routing term does not enter it).
- * PISA_ROUTE_MEAN gives exactly pisa_select_topk.
+ * pooled q̄_i stands for the query as in block-mean scoring. PISA_ROUTE_ERROR ranks by
+ * the log of the predicted truncation error, virtual-token mass n_j e^{q̄_i·k̄_j + w̃_{i,j}}
+ * times heterogeneity M_j + eps (blog, PWT section), with w̃ before the gate and n_j from
+ * block_len. eps must be finite and > 0. wt is w̃ as in pisa_select_topk (the routing
+ * terms do not enter it). PISA_ROUTE_MEAN gives exactly pisa_select_topk.
  */
 pisa_status pisa_select_topk_routed(pisa_dtype dt, const void* Q, const pisa_stats* st, int H,
                                     int L, int d, int B, const int32_t* block_len, int K_sel,

@@ -31,7 +31,7 @@ def gpu_run(pisa, inp: synth.Inputs, mode: str, K_sel: int, flags: int = 0, mode
             tensors=None, route: str = "mean"):
     Q, K, V, blt = tensors if tensors is not None else to_device(inp)
     base = pisa.MODES[mode]
-    if route == "covariance":
+    if route != "mean":
         flags |= pisa.STATS_HNORM
     st = pisa.block_stats(K, V, blt, flags=flags)
     idx, mask, wt = pisa.select_topk(Q, st, K_sel, blt, want_wt=True, route=route)
@@ -48,17 +48,20 @@ def gpu_run(pisa, inp: synth.Inputs, mode: str, K_sel: int, flags: int = 0, mode
 
 
 def oracle_scores(inp: synth.Inputs, h: int, route: str = "mean"):
-    """The oracle's block scores of head h (block-mean, or covariance-aware with its own
-    M_j) and its PWT weights, from the seeded inputs only."""
+    """The oracle's block scores of head h (block-mean, covariance-aware or predicted
+    error, with its own M_j) and its PWT weights, from the seeded inputs only."""
     from oracle import pisa_oracle as orc
     bl = inp.layout.block_len
-    st = orc.block_stats(inp.f64("K", h), inp.f64("V", h), 64, bl, per_block=(route == "covariance"))
+    st = orc.block_stats(inp.f64("K", h), inp.f64("V", h), 64, bl, per_block=(route != "mean"))
     pq = orc.pool_queries(inp.f64("Q", h), 64, bl)
+    w = orc.pooled_w(pq["qsq"], st["sig2"])
     if route == "covariance":
         s = orc.routed_scores(pq["qbar"], st["kbar"], orc.block_heterogeneity(st))
+    elif route == "error":
+        s = orc.error_routed_scores(pq["qbar"], st["kbar"], w, bl, orc.block_heterogeneity(st))
     else:
         s = orc.block_scores(pq["qbar"], st["kbar"])
-    return s, orc.pooled_w(pq["qsq"], st["sig2"])
+    return s, w
 
 
 def oracle_selection(inp: synth.Inputs, K_sel: int, route: str = "mean"):

@@ -111,7 +111,8 @@ def test_stats_and_select_argument_errors(lib):
 
 
 @pytest.mark.parametrize("route,eps,hnorm,msg", [
-    (2, 1e-6, 16, "unknown route"),
+    (3, 1e-6, 16, "unknown route"),
+    (2, 1e-6, None, "st->hnorm must not be NULL"),
     (1, 1e-6, None, "st->hnorm must not be NULL"),
     (1, 0.0, 16, "eps must be finite"),
     (1, -1.0, 16, "eps must be finite"),

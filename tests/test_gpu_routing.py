@@ -1,5 +1,6 @@
 """GPU parity of covariance-aware routing (PISA paper §3.3, Covariance-Aware Block
-Selection, Eq. (7)): the block heterogeneity M_j = ||H_j - H̄||_F from the statistics
+Selection, Eq. (7)) and of routing by predicted truncation error (Sparse Linear Attention
+blog, PWT section): the block heterogeneity M_j = ||H_j - H̄||_F from the statistics
 call, the routed top-K and attention on the routed selection, against the oracle.
 
 Bars: M_j within rel-L2 1e-5 of the oracle (fp32 sums of fp32 products); selection as in
@@ -25,6 +26,7 @@ ROUTED_RTOL = 1e-5
 
 
 HOT = (1, 5, 9)
+ROUTES = ["covariance", "error"]
 
 
 def _hetero_case(seed=131):
@@ -70,13 +72,14 @@ def test_heterogeneity_of_identical_blocks_vanishes(gpu_lib):
     assert g["hnorm"][0].max() <= 1e-5 * scale
 
 
+@pytest.mark.parametrize("route", ROUTES)
 @pytest.mark.parametrize("case", CASES + ["hetero"])
-def test_routed_selection_parity(gpu_lib, case):
+def test_routed_selection_parity(gpu_lib, case, route):
     inp, K_sel = _hetero_case() if case == "hetero" else small_case(case)
-    g = gpu_run(gpu_lib, inp, "pwt", K_sel, route="covariance")
+    g = gpu_run(gpu_lib, inp, "pwt", K_sel, route=route)
     differs = 0
     for h in range(inp.H):
-        scores, w = oracle_scores(inp, h, "covariance")
+        scores, w = oracle_scores(inp, h, route)
         exact, near, gap = check_selection(g["idx"][h], scores, K_sel, rtol=ROUTED_RTOL)
         print(f"{case} h{h}: {exact} tiles bit-exact, {near} near ties, min gap {gap:.3e}")
         sets = mask_to_sets(g["mask"][h], inp.nb)
@@ -99,14 +102,15 @@ def test_routed_selection_prefers_heterogeneous_blocks(gpu_lib):
     assert frac["covariance"] > 0.5 and frac["mean"] < 0.1
 
 
+@pytest.mark.parametrize("route", ROUTES)
 @pytest.mark.parametrize("mode", ["pisa", "pwt"])
 @pytest.mark.parametrize("case", ["bf16_d128_ragged", "f32_d128_ragged", "hetero"])
-def test_routed_attention_parity(gpu_lib, case, mode):
+def test_routed_attention_parity(gpu_lib, case, mode, route):
     """End to end on the routed selection: the GPU's own routing against the oracle's, and
     the GPU attention on the oracle's routed selection."""
     inp, K_sel = _hetero_case() if case == "hetero" else small_case(case)
-    g = gpu_run(gpu_lib, inp, mode, K_sel, route="covariance")
-    sel, w = oracle_selection(inp, K_sel, route="covariance")
+    g = gpu_run(gpu_lib, inp, mode, K_sel, route=route)
+    sel, w = oracle_selection(inp, K_sel, route=route)
     s = gpu_attention_on(gpu_lib, inp, K_sel, mode, sel, w)
     ok = valid_rows(inp)
     for h in range(inp.H):
@@ -114,7 +118,7 @@ def test_routed_attention_parity(gpu_lib, case, mode):
                                  K_sel, mode, idx=sel[h])
         e_own = rel_l2(g["O"][h][ok], ref["O"][ok])
         e_same = rel_l2(s["O"][h][ok], ref["O"][ok])
-        print(f"{case} {mode} h{h}: rel-L2 end to end {e_own:.2e}, on the oracle's selection {e_same:.2e}")
+        print(f"{case} {mode} {route} h{h}: rel-L2 end to end {e_own:.2e}, on the oracle's selection {e_same:.2e}")
         assert e_own <= TOL[inp.cfg.dtype]
         assert e_same <= TOL_SAME_SEL[inp.cfg.dtype]
 
