@@ -54,6 +54,7 @@ class Config:
     keep: float = 0.0          # fraction of key blocks kept per query tile
     keep_blocks: int = 0       # explicit K_sel (tiny)
     rope: bool = False
+    rope_split: tuple = ()     # dims per (t, h, w) axis; () = ROPE_SPLIT
     cube: tuple = (4, 4, 4)
     n_modes: int = 0
     noise_var: float = 1.0
@@ -204,14 +205,14 @@ def _grid_coords(grid: tuple) -> list:
     return [t.ravel().astype(np.float64), h.ravel().astype(np.float64), w.ravel().astype(np.float64)]
 
 
-def _rope_3d(x: np.ndarray, grid: tuple) -> np.ndarray:
-    """Rotary embedding over (t, h, w): dims split ROPE_SPLIT, adjacent pairs rotated."""
+def _rope_3d(x: np.ndarray, grid: tuple, split: tuple = ROPE_SPLIT, base: float = ROPE_BASE) -> np.ndarray:
+    """Rotary embedding over (t, h, w): dims split ``split``, adjacent pairs rotated."""
     coords = _grid_coords(grid)
     out = x.copy()
     off = 0
-    for axis, width in enumerate(ROPE_SPLIT):
+    for axis, width in enumerate(split):
         k = np.arange(width // 2, dtype=np.float64)
-        theta = ROPE_BASE ** (-2.0 * k / width)
+        theta = base ** (-2.0 * k / width)
         ang = np.outer(coords[axis], theta)                 # [L, width/2]
         c, s = np.cos(ang), np.sin(ang)
         x0 = x[:, off:off + width:2]
@@ -258,8 +259,20 @@ class Inputs:
         return to_float64(x, self.cfg.dtype)
 
 
-def make_head(cfg: Config, h: int, rng: np.random.Generator, layout: Layout):
-    """Natural-order float64 (q, k, v) for one head, consuming rng in the documented order."""
+def rope_split_for(cfg: Config) -> tuple:
+    return cfg.rope_split or ROPE_SPLIT
+
+
+def positions(cfg: Config, layout: Layout) -> np.ndarray:
+    """[L_pad, 3] float32 (t, h, w) grid position of every slot in block order (0 for padding):
+    the positions the rotary embedding of a rope config used."""
+    coords = np.stack(_grid_coords(cfg.grid), axis=1)
+    return to_blocks(coords, layout).astype(np.float32)
+
+
+def make_head(cfg: Config, h: int, rng: np.random.Generator, layout: Layout, pre: dict | None = None):
+    """Natural-order float64 (q, k, v) for one head, consuming rng in the documented order.
+    For a rope config, ``pre`` (if given) receives q and k before the rotation."""
     d = cfg.d
     if cfg.kind == "iid":
         raise ValueError("iid draws whole tensors, not heads")
@@ -274,13 +287,18 @@ def make_head(cfg: Config, h: int, rng: np.random.Generator, layout: Layout):
     v = F + sd * rng.standard_normal((L, d))
     q *= 1.0 / math.sqrt(d)
     if cfg.rope:
-        q = _rope_3d(q, cfg.grid)
-        k = _rope_3d(k, cfg.grid)
+        if pre is not None:
+            pre["q"], pre["k"] = q, k
+        q = _rope_3d(q, cfg.grid, rope_split_for(cfg))
+        k = _rope_3d(k, cfg.grid, rope_split_for(cfg))
     return q, k, v
 
 
-def make(name: str | Config, heads: int | None = None) -> Inputs:
-    """Canonical inputs of a named workload, in block layout. ``heads`` truncates H (tests)."""
+def make(name: str | Config, heads: int | None = None, keep_pre_rope: bool = False) -> Inputs:
+    """Canonical inputs of a named workload, in block layout. ``heads`` truncates H (tests).
+    keep_pre_rope (rope configs): also return Q and K before the rotary embedding, each
+    rounded to the dtype on its own (as a model holds them), and the token positions, in
+    ``extra`` under "Q_pre", "K_pre" and "pos"."""
     cfg = CONFIGS[name] if isinstance(name, str) else name
     layout = layout_for(cfg)
     H = cfg.H if heads is None else min(heads, cfg.H)
@@ -316,11 +334,20 @@ def make(name: str | Config, heads: int | None = None) -> Inputs:
             K[h] = to_blocks(_round(k, cfg.dtype), layout)
             V[h] = to_blocks(_round(v, cfg.dtype), layout)
     else:
+        keep = keep_pre_rope and cfg.rope
+        if keep:
+            extra = dict(Q_pre=np.zeros_like(Q), K_pre=np.zeros_like(K), pos=positions(cfg, layout))
         for h in range(H):
-            q, k, v = make_head(cfg, h, rng, layout)
+            pre = {} if keep else None
+            q, k, v = make_head(cfg, h, rng, layout, pre)
             Q[h] = to_blocks(_round(q, cfg.dtype), layout)
             K[h] = to_blocks(_round(k, cfg.dtype), layout)
             V[h] = to_blocks(_round(v, cfg.dtype), layout)
+            if keep:
+                extra["Q_pre"][h] = to_blocks(_round(pre["q"], cfg.dtype), layout)
+                extra["K_pre"][h] = to_blocks(_round(pre["k"], cfg.dtype), layout)
+        if keep:
+            return Inputs(cfg, layout, Q, K, V, k_sel_for(cfg, layout.nb), extra)
     return Inputs(cfg, layout, Q, K, V, k_sel_for(cfg, layout.nb))
 
 

@@ -178,6 +178,55 @@ def error_routed_scores(qbar: np.ndarray, kbar: np.ndarray, w: np.ndarray, n: np
             + np.log(np.asarray(hnorm, dtype=np.float64) + eps)[None, :])
 
 
+def rope_rotate(x: np.ndarray, pos: np.ndarray, widths, base: float, pairs: str = "adjacent") -> np.ndarray:
+    """Rotary position embedding R_p x of rows x [n, d] at positions pos [n, n_axes]
+    (Sparse Linear Attention (2) blog, Selection Error: a position-dependent rotation R_i
+    with R_mᵀR_n = R_{n-m}). The head dimension is cut into consecutive slices of
+    widths[a] dims, one per position axis a; inside slice a, pair f (dims 2f, 2f+1 for
+    "adjacent", f, f + widths[a]/2 for "half") turns by the angle pos_a · base^(-2f/widths[a])."""
+    x = np.asarray(x, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.float64).reshape(x.shape[0], -1)
+    out = x.copy()
+    off = 0
+    for a, wdt in enumerate(widths):
+        f = np.arange(wdt // 2, dtype=np.float64)
+        ang = np.outer(pos[:, a], base ** (-2.0 * f / wdt))
+        c, s = np.cos(ang), np.sin(ang)
+        if pairs == "adjacent":
+            i0 = off + 2 * np.arange(wdt // 2)
+            i1 = i0 + 1
+        elif pairs == "half":
+            i0 = off + np.arange(wdt // 2)
+            i1 = i0 + wdt // 2
+        else:
+            raise ValueError(pairs)
+        out[:, i0] = x[:, i0] * c - x[:, i1] * s
+        out[:, i1] = x[:, i0] * s + x[:, i1] * c
+        off += wdt
+    if off != x.shape[1]:
+        raise ValueError("rotary widths must cover the head dimension")
+    return out
+
+
+def rope_block_scores(Q_pre: np.ndarray, K_pre: np.ndarray, pos: np.ndarray, B: int, block_len,
+                      widths, base: float, pairs: str = "adjacent") -> np.ndarray:
+    """Block scores with RoPE-aware centroids (Sparse Linear Attention (2) blog, Selection
+    Error): average the rows before the rotary embedding, then rotate the average at the
+    block centre c_j, so that the score is an inner product that depends on the relative
+    position only. Every tile does the same on the query side: q̄_i is the mean of its
+    valid pre-rotation rows, turned at its own centre c_i; c is the mean position of the
+    valid tokens (tiles and blocks share one partition).
+    s_{i,j} = (R_{c_i} q̄_i)·(R_{c_j} k̄_j). pos: [L_pad, n_axes] in block order."""
+    pos = np.asarray(pos, dtype=np.float64)
+    pos = pos.reshape(pos.shape[0], -1)
+    rng = block_ranges(np.asarray(K_pre).shape[0], B, block_len)
+    qbar = pool_queries(Q_pre, B, block_len)["qbar"]
+    kbar = np.stack([np.asarray(K_pre, dtype=np.float64)[s:s + n].mean(axis=0) for s, n in rng])
+    centre = np.stack([pos[s:s + n].mean(axis=0) for s, n in rng])
+    return block_scores(rope_rotate(qbar, centre, widths, base, pairs),
+                        rope_rotate(kbar, centre, widths, base, pairs))
+
+
 def select_topk(scores: np.ndarray, K_sel: int) -> np.ndarray:
     """S_i = the K_sel largest scores of row i, ties to the lower block index; returned
     in ascending block order, shape [nq, K_sel] int64."""
