@@ -66,6 +66,84 @@ pisa_status hip_fail(hipError_t e, const char* what) {
     if (_s != PISA_OK) return _s;    \
   } while (0)
 
+pisa_status select_impl(pisa_dtype dt, const void* Q, const void* Q_pre, const void* K_pre,
+                        const float* pos, const pisa_rope* rope, const pisa_stats* st, int H,
+                        int L, int d, int B, const int32_t* block_len, int K_sel,
+                        unsigned route, float eps, int32_t* idx, uint32_t* mask,
+                        float* wt, void* workspace, size_t workspace_bytes, void* stream) {
+  PISA_TRY(check_dtype(dt));
+  PISA_TRY(check_shape(H, L, d, B));
+  if (!rope || wt) PISA_TRY(check_ptr(Q, "Q"));
+  PISA_TRY(check_ptr(st, "st", false));
+  if (!rope) PISA_TRY(check_ptr(st->kbar, "st->kbar"));
+  if (wt) PISA_TRY(check_ptr(st->ksig2, "st->ksig2"));
+  if (rope) {
+    PISA_TRY(check_ptr(Q_pre, "Q_pre"));
+    PISA_TRY(check_ptr(K_pre, "K_pre"));
+    PISA_TRY(check_ptr(pos, "pos", false));
+    if (rope->n_axes < 1 || rope->n_axes > 3)
+      return fail(PISA_ERR_INVALID_ARG, "rope->n_axes must be 1, 2 or 3 (got %d)", rope->n_axes);
+    int sum = 0;
+    for (int x = 0; x < rope->n_axes; ++x) {
+      if (rope->width[x] < 2 || rope->width[x] % 2)
+        return fail(PISA_ERR_INVALID_ARG, "rope->width[%d] must be even and >= 2 (got %d)", x, rope->width[x]);
+      sum += rope->width[x];
+    }
+    if (sum != d) return fail(PISA_ERR_INVALID_ARG, "rope widths must sum to d = %d (got %d)", d, sum);
+    if (!(rope->base > 0.f) || rope->base > 3.0e38f)
+      return fail(PISA_ERR_INVALID_ARG, "rope->base must be finite and > 0");
+    if (rope->pairs != PISA_ROPE_ADJACENT && rope->pairs != PISA_ROPE_HALF)
+      return fail(PISA_ERR_INVALID_ARG, "unknown rope->pairs %d", rope->pairs);
+  }
+  if (route > PISA_ROUTE_ERROR) return fail(PISA_ERR_INVALID_ARG, "unknown route %u", route);
+  if (route != PISA_ROUTE_MEAN) {
+    PISA_TRY(check_ptr(st->hnorm, "st->hnorm", false));
+    if (!(eps > 0.f) || eps > 3.0e38f) return fail(PISA_ERR_INVALID_ARG, "eps must be finite and > 0 (got %g)", double(eps));
+  }
+  const int nb = L / B;
+  if (K_sel < 0 || K_sel > nb) return fail(PISA_ERR_INVALID_ARG, "K_sel must be in [0, %d] (got %d)", nb, K_sel);
+  if (K_sel > 0) PISA_TRY(check_ptr(idx, "idx", false));
+  const size_t need = pisa_select_workspace_bytes(H, L, d, B);
+  if (!workspace || workspace_bytes < need)
+    return fail(PISA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(PISA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+  pisa::SelectArgs a{};
+  a.Q = Q;
+  a.kbar = st->kbar;
+  a.ksig2 = st->ksig2;
+  a.hnorm = route != PISA_ROUTE_MEAN ? st->hnorm : nullptr;
+  a.route_eps = eps;
+  a.route = int(route);
+  if (rope) {
+    a.Q_pre = Q_pre;
+    a.K_pre = K_pre;
+    a.pos = pos;
+    a.rope_axes = rope->n_axes;
+    a.rope_pairs = rope->pairs;
+    for (int x = 0; x < 3; ++x) a.rope_width[x] = x < rope->n_axes ? rope->width[x] : 0;
+    a.rope_base = rope->base;
+  }
+  a.block_len = block_len;
+  a.qbar = static_cast<float*>(workspace);
+  a.qsq = a.qbar + size_t(H) * nb * d;
+  a.krot = a.qsq + size_t(H) * nb * d;
+  a.scores = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      pisa::align256(3 * size_t(H) * nb * d * sizeof(float)));
+  a.wt = wt;
+  a.idx = idx;
+  a.mask = mask;
+  a.H = H;
+  a.L = L;
+  a.d = d;
+  a.nb = nb;
+  a.K_sel = K_sel;
+  a.nw = (nb + 31) / 32;
+  hipError_t e = pisa::launch_select(dt == PISA_BF16, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pisa_select_topk launch");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -135,7 +213,7 @@ pisa_status pisa_block_stats(pisa_dtype dt, const void* K, const void* V, int H,
 size_t pisa_select_workspace_bytes(int H, int L, int d, int B) {
   if (check_shape(H, L, d, B) != PISA_OK) return 0;
   const size_t nb = size_t(L / B);
-  return pisa::align256(2 * size_t(H) * nb * d * sizeof(float)) + size_t(H) * nb * nb * sizeof(float);
+  return pisa::align256(3 * size_t(H) * nb * d * sizeof(float)) + size_t(H) * nb * nb * sizeof(float);
 }
 
 pisa_status pisa_select_topk_routed(pisa_dtype dt, const void* Q, const pisa_stats* st, int H,
@@ -143,49 +221,18 @@ pisa_status pisa_select_topk_routed(pisa_dtype dt, const void* Q, const pisa_sta
                                     unsigned route, float eps, int32_t* idx, uint32_t* mask,
                                     float* wt, void* workspace, size_t workspace_bytes,
                                     void* stream) {
-  PISA_TRY(check_dtype(dt));
-  PISA_TRY(check_shape(H, L, d, B));
-  PISA_TRY(check_ptr(Q, "Q"));
-  PISA_TRY(check_ptr(st, "st", false));
-  PISA_TRY(check_ptr(st->kbar, "st->kbar"));
-  PISA_TRY(check_ptr(st->ksig2, "st->ksig2"));
-  if (route > PISA_ROUTE_ERROR) return fail(PISA_ERR_INVALID_ARG, "unknown route %u", route);
-  if (route != PISA_ROUTE_MEAN) {
-    PISA_TRY(check_ptr(st->hnorm, "st->hnorm", false));
-    if (!(eps > 0.f) || eps > 3.0e38f) return fail(PISA_ERR_INVALID_ARG, "eps must be finite and > 0 (got %g)", double(eps));
-  }
-  const int nb = L / B;
-  if (K_sel < 0 || K_sel > nb) return fail(PISA_ERR_INVALID_ARG, "K_sel must be in [0, %d] (got %d)", nb, K_sel);
-  if (K_sel > 0) PISA_TRY(check_ptr(idx, "idx", false));
-  const size_t need = pisa_select_workspace_bytes(H, L, d, B);
-  if (!workspace || workspace_bytes < need)
-    return fail(PISA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
-  if (!aligned16(workspace)) return fail(PISA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return select_impl(dt, Q, nullptr, nullptr, nullptr, nullptr, st, H, L, d, B, block_len, K_sel,
+                     route, eps, idx, mask, wt, workspace, workspace_bytes, stream);
+}
 
-  pisa::SelectArgs a{};
-  a.Q = Q;
-  a.kbar = st->kbar;
-  a.ksig2 = st->ksig2;
-  a.hnorm = route != PISA_ROUTE_MEAN ? st->hnorm : nullptr;
-  a.route_eps = eps;
-  a.route = int(route);
-  a.block_len = block_len;
-  a.qbar = static_cast<float*>(workspace);
-  a.qsq = a.qbar + size_t(H) * nb * d;
-  a.scores = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                      pisa::align256(2 * size_t(H) * nb * d * sizeof(float)));
-  a.wt = wt;
-  a.idx = idx;
-  a.mask = mask;
-  a.H = H;
-  a.L = L;
-  a.d = d;
-  a.nb = nb;
-  a.K_sel = K_sel;
-  a.nw = (nb + 31) / 32;
-  hipError_t e = pisa::launch_select(dt == PISA_BF16, a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "pisa_select_topk launch");
-  return ok();
+pisa_status pisa_select_topk_rope(pisa_dtype dt, const void* Q, const void* Q_pre, const void* K_pre,
+                                  const float* pos, const pisa_rope* rope, const pisa_stats* st,
+                                  int H, int L, int d, int B, const int32_t* block_len, int K_sel,
+                                  int32_t* idx, uint32_t* mask, float* wt, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  PISA_TRY(check_ptr(rope, "rope", false));
+  return select_impl(dt, Q, Q_pre, K_pre, pos, rope, st, H, L, d, B, block_len, K_sel,
+                     PISA_ROUTE_MEAN, 1.f, idx, mask, wt, workspace, workspace_bytes, stream);
 }
 
 pisa_status pisa_select_topk(pisa_dtype dt, const void* Q, const pisa_stats* st, int H, int L,

@@ -67,6 +67,15 @@ struct SelectArgs {
   const float* hnorm;  // [H][nb] M_j (routes 1, 2)
   float route_eps;
   int route;           // 0 block mean, 1 + ln(M_j + eps), 2 + w̃ + ln n_j + ln(M_j + eps)
+  // RoPE-aware centroids (rope_axes > 0): pre-rotation Q and K pooled per block and turned
+  // at the block centre; the turned key centroids go to krot (workspace), queries to qbar.
+  const void* Q_pre;
+  const void* K_pre;
+  const float* pos;    // [L][rope_axes]
+  float* krot;         // [H][nb][d] workspace
+  int rope_axes, rope_pairs;
+  int rope_width[3];
+  float rope_base;
   const int32_t* block_len;
   float* qbar;     // [H][nb][d]   workspace
   float* qsq;      // [H][nb][d]   workspace

@@ -70,6 +70,69 @@ __global__ __launch_bounds__(256) void pool_kernel(SelectArgs a) {
   }
 }
 
+// RoPE-aware centroids (Sparse Linear Attention (2) blog, Selection Error): the mean of
+// the valid pre-rotation rows of block i (queries for blockIdx.z = 0, keys for 1), turned
+// by the rotary embedding at the block centre c_i = mean position of its valid tokens, so
+// that q̄·k̄ of two turned means depends on c_j - c_i only. Column means as in pool_kernel;
+// the centre and the angles c_a · base^(-2f/width_a) are taken in fp64, the turn in fp32.
+template <class T, int D>
+__global__ __launch_bounds__(256) void rope_pool_kernel(SelectArgs a) {
+  constexpr int EPC = 16 / sizeof(T), CPR = D / EPC, RG = 256 / CPR;
+  __shared__ float s1[RG][D];
+  __shared__ float mean[D];
+  __shared__ double centre[3];
+  const int i = blockIdx.x, h = blockIdx.y, keys = blockIdx.z, tid = threadIdx.x;
+  int n = a.block_len ? a.block_len[i] : kB;
+  n = min(max(n, 1), kB);
+  const int ch = tid % CPR, rg = tid / CPR;
+  const T* X = static_cast<const T*>(keys ? a.K_pre : a.Q_pre) + (size_t(h) * a.L + size_t(i) * kB) * D;
+  float sum[EPC];
+#pragma unroll
+  for (int u = 0; u < EPC; ++u) sum[u] = 0.f;
+#pragma unroll
+  for (int p = 0; p < kB / RG; ++p) {
+    const int r = rg + RG * p;
+    if (r < n) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(X + size_t(r) * D + ch * EPC);
+      const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+      for (int u = 0; u < EPC; ++u) sum[u] += to_f32(e[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < EPC; ++u) s1[rg][ch * EPC + u] = sum[u];
+  if (tid < a.rope_axes) {
+    double c = 0.0;
+    for (int r = 0; r < n; ++r) c += double(a.pos[(size_t(i) * kB + r) * a.rope_axes + tid]);
+    centre[tid] = c / double(n);
+  }
+  __syncthreads();
+  if (tid < D) {
+    float t = 0.f;
+    for (int q = 0; q < RG; ++q) t += s1[q][tid];
+    mean[tid] = t * (1.f / float(n));
+  }
+  __syncthreads();
+  if (tid < D / 2) {                         // pair tid: axis ax, frequency f
+    int ax = 0, off = 0, f = tid;
+    while (ax + 1 < a.rope_axes && f >= a.rope_width[ax] / 2) {
+      f -= a.rope_width[ax] / 2;
+      off += a.rope_width[ax];
+      ++ax;
+    }
+    const int w = a.rope_width[ax];
+    const int i0 = a.rope_pairs ? off + f : off + 2 * f;
+    const int i1 = a.rope_pairs ? i0 + w / 2 : i0 + 1;
+    const double ang = centre[ax] * pow(double(a.rope_base), -2.0 * f / w);
+    double sd, cd;
+    sincos(ang, &sd, &cd);
+    const float cs = float(cd), sn = float(sd), x0 = mean[i0], x1 = mean[i1];
+    float* out = (keys ? a.krot : a.qbar) + (size_t(h) * a.nb + i) * D;
+    out[i0] = x0 * cs - x1 * sn;
+    out[i1] = x0 * sn + x1 * cs;
+  }
+}
+
 // S = Q̄ K̄ᵀ and W = ½ Q̄² Σ²ᵀ per head on the fp32 matrix cores: a 64x64 output tile per
 // workgroup, each of its four waves a 32x32 quarter (v_mfma_f32_32x32x2f32 over the head
 // dimension). The 64 query and 64 key rows are staged in LDS with coalesced 16-byte loads.
@@ -126,7 +189,7 @@ __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
     for (int r = 0; r < 16; ++r) w[r] *= 0.5f;
     if (a.wt) store(a.wt, w);
   }
-  f32x16 s = product(a.qbar, a.kbar);
+  f32x16 s = product(a.qbar, a.rope_axes ? a.krot : a.kbar);
   if (a.route != 0 && col < nb) {
     // per key block: ln(M_j + eps) (Eq. (7)), plus ln n_j and w̃ for the predicted-error route
     float bias = logf(a.hnorm[size_t(h) * nb + col] + a.route_eps);
@@ -242,9 +305,17 @@ __global__ __launch_bounds__(256) void topk_kernel(SelectArgs a) {
 
 template <class T, int D>
 static hipError_t launch_select_t(const SelectArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((pool_kernel<T, D>), dim3(a.nb, a.H), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (a.rope_axes == 0 || a.wt) {            // RoPE-aware scores read Q only for w̃
+    hipLaunchKernelGGL((pool_kernel<T, D>), dim3(a.nb, a.H), dim3(256), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.rope_axes > 0) {                     // after pool_kernel: replaces q̄
+    hipLaunchKernelGGL((rope_pool_kernel<T, D>), dim3(a.nb, a.H, 2), dim3(256), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int nt = (a.nb + 63) / 64;
   hipLaunchKernelGGL((score_kernel<D>), dim3(nt, nt, a.H), dim3(256), 0, s, a);
   e = hipGetLastError();

@@ -28,6 +28,7 @@ B = 64
 # Every symbol include/pisa.h declares.
 EXPORTS = ("pisa_packed_bytes", "pisa_block_stats_workspace_bytes", "pisa_block_stats",
            "pisa_select_workspace_bytes", "pisa_select_topk", "pisa_select_topk_routed",
+           "pisa_select_topk_rope",
            "pisa_attention_fwd",
            "pisa_last_error", "pisa_version")
 
@@ -42,6 +43,14 @@ class _Stats(ctypes.Structure):
     _fields_ = [("kbar", ctypes.c_void_p), ("vsum", ctypes.c_void_p), ("ksig2", ctypes.c_void_p),
                 ("hbarT", ctypes.c_void_p), ("hblk", ctypes.c_void_p), ("cblk", ctypes.c_void_p),
                 ("packed", ctypes.c_void_p), ("hnorm", ctypes.c_void_p)]
+
+
+ROPE_PAIRS = {"adjacent": 0, "half": 1}
+
+
+class _Rope(ctypes.Structure):
+    _fields_ = [("n_axes", ctypes.c_int), ("width", ctypes.c_int * 3), ("base", ctypes.c_float),
+                ("pairs", ctypes.c_int)]
 
 
 _lib = None
@@ -70,6 +79,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pisa_select_topk_routed.argtypes = [i32, vp, sp, i32, i32, i32, i32, vp, i32, u32, ctypes.c_float,
                                             vp, vp, vp, vp, sz, vp]
     lib.pisa_select_topk_routed.restype = i32
+    lib.pisa_select_topk_rope.argtypes = [i32, vp, vp, vp, vp, ctypes.POINTER(_Rope), sp, i32, i32, i32, i32,
+                                          vp, i32, vp, vp, vp, vp, sz, vp]
+    lib.pisa_select_topk_rope.restype = i32
     lib.pisa_attention_fwd.argtypes = [i32, vp, vp, vp, sp, vp, vp, vp, i32, i32, i32, i32, vp, i32,
                                        u32, vp, vp, vp]
     lib.pisa_attention_fwd.restype = i32
@@ -183,6 +195,37 @@ def select_topk(Q, st: Stats, K_sel: int, block_len=None, want_wt: bool = True, 
     _check(lib.pisa_select_topk_routed(_dtype_code(Q), _ptr(Q), ctypes.byref(s), H, L, d, B,
                                        _ptr(block_len), K_sel, r, eps, _ptr(idx), _ptr(mask), _ptr(wt),
                                        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return idx, mask, wt
+
+
+def select_topk_rope(Q, Q_pre, K_pre, pos, widths, base: float, st: Stats, K_sel: int, block_len=None,
+                     pairs: str = "adjacent", want_wt: bool = True, want_mask: bool = True, out=None,
+                     workspace=None, stream=None):
+    """pisa_select_topk with RoPE-aware centroids. Q_pre, K_pre: [H, L, d] before the rotary
+    embedding; pos: [L, n_axes] float32 device positions in block order; widths: dims per
+    axis. Q (rotated) is read only for wt and may be None when want_wt is False."""
+    lib = load()
+    H, L, d = _shape(Q_pre)
+    nb = L // B
+    nw = (nb + 31) // 32
+    if out is None:
+        idx = torch.empty(H, nb, max(K_sel, 1), dtype=torch.int32, device=Q_pre.device)[:, :, :K_sel]
+        mask = torch.empty(H, nb, nw, dtype=torch.int32, device=Q_pre.device) if want_mask else None
+        wt = torch.empty(H, nb, nb, dtype=torch.float32, device=Q_pre.device) if want_wt else None
+    else:
+        idx, mask, wt = out
+    if pos.dtype != torch.float32 or not pos.is_contiguous() or pos.shape[0] != L:
+        raise ValueError("pos must be a contiguous float32 [L, n_axes] tensor")
+    w = list(widths) + [0] * (3 - len(widths))
+    rope = _Rope(len(widths), (ctypes.c_int * 3)(*w), base, ROPE_PAIRS[pairs])
+    if workspace is None:
+        workspace = torch.empty(lib.pisa_select_workspace_bytes(H, L, d, B), dtype=torch.uint8,
+                                device=Q_pre.device)
+    s = st.struct()
+    _check(lib.pisa_select_topk_rope(_dtype_code(Q_pre), _ptr(Q), _ptr(Q_pre), _ptr(K_pre), _ptr(pos),
+                                     ctypes.byref(rope), ctypes.byref(s), H, L, d, B, _ptr(block_len), K_sel,
+                                     _ptr(idx), _ptr(mask), _ptr(wt), _ptr(workspace), workspace.numel(),
+                                     _stream(stream)))
     return idx, mask, wt
 
 

@@ -150,7 +150,8 @@ pisa_status pisa_block_stats(pisa_dtype dt, const void* K, const void* V, int H,
                              const pisa_stats* out, void* workspace, size_t workspace_bytes,
                              void* stream);
 
-/* Workspace bytes of pisa_select_topk (pooled queries and the fp32 score matrix). */
+/* Workspace bytes of pisa_select_topk, pisa_select_topk_routed and pisa_select_topk_rope
+ * (pooled queries, rotated key centroids and the fp32 score matrix). */
 size_t pisa_select_workspace_bytes(int H, int L, int d, int B);
 
 /*
@@ -190,6 +191,43 @@ pisa_status pisa_select_topk_routed(pisa_dtype dt, const void* Q, const pisa_sta
                                     unsigned route, float eps, int32_t* idx, uint32_t* mask,
                                     float* wt, void* workspace, size_t workspace_bytes,
                                     void* stream);
+
+/* Pairing of dims inside each rotary slice of pisa_rope. */
+enum {
+  PISA_ROPE_ADJACENT = 0, /* pair f of a slice is dims (2f, 2f + 1) */
+  PISA_ROPE_HALF = 1      /* pair f of a slice of width w is dims (f, f + w/2) */
+};
+
+/* Rotary position embedding as the caller applied it to Q and K: the head dimension is cut
+ * into n_axes consecutive slices of width[a] dims (axis a of the token position, e.g.
+ * t, h, w); pair f of slice a turns by the angle pos_a · base^(-2f/width[a]). */
+typedef struct {
+  int n_axes;     /* 1..3 */
+  int width[3];   /* even, >= 2, summing to d (entries past n_axes ignored) */
+  float base;     /* finite, > 0 */
+  int pairs;      /* PISA_ROPE_ADJACENT or PISA_ROPE_HALF */
+} pisa_rope;
+
+/*
+ * pisa_select_topk with RoPE-aware centroids (blog "Sparse Linear Attention (2)", section
+ * Selection Error): block means of rotated keys mix B different rotations and lose the
+ * relative-position form of the score; instead the block is averaged before the rotation
+ * and the mean is turned at the block centre c_j. Queries are pooled per tile the same
+ * way, so s_{i,j} = (R_{c_i} q̄_i)·(R_{c_j} k̄_j), which depends on c_j - c_i only.
+ *   Q_pre, K_pre  [H][L][d] dtype `dt`: Q (with 1/sqrt(d)) and K before the rotation
+ *   pos           DEVICE float [L][rope->n_axes]: position of every slot in block order;
+ *                 c_j = mean position of block j's valid tokens (padded slots ignored)
+ *   Q             the rotated Q of the attention call; read only for wt (may be NULL when
+ *                 wt is NULL); st->ksig2 is read for wt, st->kbar is not read
+ * Selection, idx, mask and wt as in pisa_select_topk. The attention call itself takes the
+ * rotated Q, K, V and the statistics of the rotated K as usual.
+ */
+pisa_status pisa_select_topk_rope(pisa_dtype dt, const void* Q, const void* Q_pre,
+                                  const void* K_pre, const float* pos, const pisa_rope* rope,
+                                  const pisa_stats* st, int H, int L, int d, int B,
+                                  const int32_t* block_len, int K_sel, int32_t* idx,
+                                  uint32_t* mask, float* wt, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /*
  * Fused kernel (PISA paper §3.4 phases 1-3; Eq. (3.2); blog, PWT section).

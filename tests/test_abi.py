@@ -126,3 +126,26 @@ def test_routed_select_argument_errors(lib, route, eps, hnorm, msg):
     r = lib.pisa_select_topk_routed(1, 16, ctypes.byref(st), 1, 1024, 64, 64, None, 4, route, eps, 16, None,
                                     None, 16, 1 << 20, None)
     assert r == 1 and msg in lib.pisa_last_error().decode()
+
+
+@pytest.mark.parametrize("rope,msg", [
+    (dict(n_axes=0), "n_axes"),
+    (dict(n_axes=4), "n_axes"),
+    (dict(width=(16, 23, 25)), "even"),
+    (dict(width=(16, 24, 26)), "sum to d"),
+    (dict(base=0.0), "base"),
+    (dict(pairs=2), "pairs"),
+])
+def test_rope_select_argument_errors(lib, rope, msg):
+    from block_sparse_attention_43_amd import pisa
+    st = _stats(pisa)
+    a = dict(n_axes=3, width=(16, 24, 24), base=10000.0, pairs=0)
+    a.update(rope)
+    r = pisa._Rope(a["n_axes"], (ctypes.c_int * 3)(*a["width"]), a["base"], a["pairs"])
+    s = lib.pisa_select_topk_rope(1, 16, 16, 16, 16, ctypes.byref(r), ctypes.byref(st), 1, 1024, 64, 64, None,
+                                  4, 16, None, 16, 16, 1 << 20, None)
+    assert s == 1 and msg in lib.pisa_last_error().decode()
+    r = pisa._Rope(3, (ctypes.c_int * 3)(16, 24, 24), 10000.0, 0)
+    s = lib.pisa_select_topk_rope(1, None, 16, 16, 16, ctypes.byref(r), ctypes.byref(st), 1, 1024, 64, 64, None,
+                                  4, 16, None, 16, 16, 1 << 20, None)
+    assert s == 1 and "Q must not be NULL" in lib.pisa_last_error().decode()   # wt needs Q
