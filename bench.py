@@ -143,6 +143,8 @@ def main():
     ap.add_argument("--config", default="wan", help="tiny | flux | wan | hunyuan | long")
     ap.add_argument("--mode", default="pwt", help="drop | pisa | pwt | literal")
     ap.add_argument("--route", default="mean", help="mean | covariance | error (block selection score)")
+    ap.add_argument("--rope-select", action="store_true",
+                    help="rotary workloads: select with RoPE-aware centroids in the timed step")
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -161,7 +163,7 @@ def main():
 
     torch.cuda.set_device(0)
     pisa.load()
-    inp = synth.make(args.config)
+    inp = synth.make(args.config, keep_pre_rope=True)
     cfg = inp.cfg
     K_sel = inp.K_sel
     mode = args.mode
@@ -194,6 +196,14 @@ def main():
 
     # every buffer allocated once, outside the timed region
     route = args.route
+    rope_select = args.rope_select
+    if rope_select and (not cfg.rope or route != "mean"):
+        print(json.dumps({"error": "--rope-select needs a rotary workload (hunyuan) and the mean route"}))
+        sys.exit(2)
+    if cfg.rope:
+        Qp, Kp = dev(inp.extra["Q_pre"]), dev(inp.extra["K_pre"])
+        pos = torch.from_numpy(inp.extra["pos"]).cuda()
+        widths = synth.rope_split_for(cfg)
     sflags = pisa.STATS_HNORM if route != "mean" else 0
     st = pisa.alloc_stats(K, sflags)
     ws_stats = torch.empty(max(pisa.load().pisa_block_stats_workspace_bytes(H, L, d, 64), 16),
@@ -212,7 +222,11 @@ def main():
         pisa.block_stats(K, V, blt, flags=sflags, out=st, workspace=ws_stats)
         if ev is not None:
             ev[1].record(stream)
-        pisa.select_topk(Q, st, K_sel, blt, out=(idx, mask, wt), workspace=ws_sel, route=route)
+        if rope_select:
+            pisa.select_topk_rope(Q, Qp, Kp, pos, widths, synth.ROPE_BASE, st, K_sel, blt,
+                                  out=(idx, mask, wt), workspace=ws_sel)
+        else:
+            pisa.select_topk(Q, st, K_sel, blt, out=(idx, mask, wt), workspace=ws_sel, route=route)
         if ev is not None:
             ev[2].record(stream)
         pisa.attention_fwd(Q, K, V, st, idx, mask, wt, K_sel, mode, blt, out=O, lse=lse)
@@ -259,6 +273,7 @@ def main():
     # covariance-aware routing, the optional selection rule: its prepare-phase cost (second
     # statistics pass for M_j + routed scores) and how many tiles change their selection
     routing = None
+    rules = {("rope" if rope_select else route): (idx.clone(), mask.clone())}
     if route == "mean":
         st_r = pisa.alloc_stats(K, pisa.STATS_HNORM)
         idx_r, mask_r = torch.empty_like(idx), torch.empty_like(mask)
@@ -274,7 +289,23 @@ def main():
         routing = {"ms_prepare_covariance": round(ms_prep_r, 4),
                    "ms_prepare_mean": round(ms_stats + ms_sel, 4),
                    "tiles_with_changed_selection": round(changed, 4)}
+        rules["covariance"] = (idx_r.clone(), mask_r.clone())
+        pisa.select_topk(Q, st_r, K_sel, blt, out=(idx_r, mask_r, wt_r), workspace=ws_sel, route="error")
+        rules["error"] = (idx_r.clone(), mask_r.clone())
         del st_r, idx_r, mask_r, wt_r
+
+    # RoPE-aware centroids on rotary workloads: selection cost and how many tiles change
+    rope_leg = None
+    if cfg.rope and not rope_select:
+        idx_p, mask_p = torch.empty_like(idx), torch.empty_like(mask)
+        wt_p = None if wt is None else torch.empty_like(wt)
+        ms_sel_rope = timed(lambda: pisa.select_topk_rope(Q, Qp, Kp, pos, widths, synth.ROPE_BASE, st, K_sel,
+                                                          blt, out=(idx_p, mask_p, wt_p), workspace=ws_sel))
+        changed = float((idx_p != idx).any(dim=-1).float().mean().item()) if K_sel else 0.0
+        rope_leg = {"ms_select_rope": round(ms_sel_rope, 4), "ms_select_mean": round(ms_sel, 4),
+                    "tiles_with_changed_selection": round(changed, 4)}
+        rules["rope"] = (idx_p.clone(), mask_p.clone())
+        del idx_p, mask_p, wt_p
 
     # cold cache: a 512 MiB fill between runs evicts L2 and the Infinity Cache
     flush = torch.empty(512 * 2**20, dtype=torch.uint8, device="cuda")
@@ -309,7 +340,18 @@ def main():
     if not args.no_dense:
         idx_all = torch.arange(nb, dtype=torch.int32, device="cuda").expand(H, nb, nb).contiguous()
         ms_drop_all = timed(lambda: pisa.attention_fwd(Q, K, V, st, idx_all, None, None, nb, "drop", blt, out=O), 3)
-        del idx_all
+        # selection quality: the share of each row's dense softmax mass that the selected
+        # blocks hold, exp(lse over the selected keys - lse over all keys), mean over valid rows
+        lse_all = torch.empty(H, L, dtype=torch.float32, device="cuda")
+        lse_sel = torch.empty_like(lse_all)
+        pisa.attention_fwd(Q, K, V, st, idx_all, None, None, nb, "drop", blt, out=O, lse=lse_all)
+        valid = torch.from_numpy((np.arange(64)[None, :] < bl[:, None]).reshape(-1)).cuda()
+        recall = {}
+        for name_r, (idx_x, mask_x) in rules.items():
+            pisa.attention_fwd(Q, K, V, st, idx_x, mask_x, None, K_sel, "drop", blt, out=O, lse=lse_sel)
+            recall[name_r] = round(float(torch.exp(lse_sel - lse_all)[:, valid].mean().item()), 5)
+        dense["selection_mass_recall"] = recall
+        del idx_all, lse_all, lse_sel
         ok = torch.from_numpy(inp.layout.perm >= 0).cuda()
         q = Q[:, ok].unsqueeze(0).contiguous()
         k = K[:, ok].unsqueeze(0).contiguous()
@@ -343,9 +385,10 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic (seeded smooth 3D field + noise, cube layout; no model activations)",
         "config": {"workload": f"{cfg.name}: H={H} L={inp.layout.L} (padded {L}) d={d} B=64 "
-                               f"K_sel={K_sel}/{nb} mode={mode}" + (f" route={route}" if route != "mean" else ""),
+                               f"K_sel={K_sel}/{nb} mode={mode}" + (f" route={route}" if route != "mean" else "")
+                               + (" rope-aware selection" if rope_select else ""),
                    "heads": H, "seq_len": inp.layout.L, "head_dim": d, "block": 64,
-                   "k_sel": K_sel, "n_blocks": nb, "mode": mode, "route": route},
+                   "k_sel": K_sel, "n_blocks": nb, "mode": mode, "route": route, "rope_select": rope_select},
         "ms_stats": round(ms_stats, 4),
         "ms_select": round(ms_sel, 4),
         "ms_attention": round(ms_attn, 4),
@@ -358,6 +401,7 @@ def main():
         "layout_permutation_ms": round(ms_perm, 4),
         "literal": literal,
         "covariance_routing": routing,
+        "rope_selection": rope_leg,
         "flops": fc,
         **dense,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
