@@ -53,6 +53,9 @@ PRESETS = {
     # PWT: PISA + diagonal, query-pooled, gated second-order mass term (blog, PWT section)
     "pwt": dict(virtual=True, first="global", w_kind="pooled", w_map="exp", guard="gate",
                 pooling="sqmean"),
+    # PWT with the per-row diagonal w_{t,j} = ½ Σ_c q_{t,c}² σ²_{j,c} instead of the tile-pooled
+    # w̃ (blog, PWT section: the accuracy / speed ablation of the pooling)
+    "pwt_row": dict(virtual=True, first="global", w_kind="rowdiag", w_map="exp", guard="gate"),
     # block-wise first order H_j q and per-row w = ½ qᵀC_j q, with 1+w (blog, PWT derivation)
     "literal": dict(virtual=True, first="block", w_kind="row", w_map="linear", guard="gate"),
 }

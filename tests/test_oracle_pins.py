@@ -653,3 +653,28 @@ def test_rope_centroid_undoes_the_rotation_mixture():
     post = orc.block_scores(orc.rope_rotate(Q, pos, widths, 10.0).reshape(nb, B, d).mean(axis=1),
                             orc.rope_rotate(K, pos, widths, 10.0).reshape(nb, B, d).mean(axis=1))
     assert np.abs(post - s).max() > 1e-3
+
+
+def test_per_row_diagonal_w_reduces_to_pooled_and_to_full_quadratic_form():
+    """Per-row diagonal w_{t,j} = ½ Σ_c q_{t,c}² σ²_{j,c} (blog, PWT section ablation):
+    (1) tiles whose rows are ±q share q² row by row, so it equals the tile-pooled w̃ (PWT);
+    (2) blocks whose keys deviate along one coordinate only have a diagonal C_j, so it
+    equals the full per-row form ½ q_tᵀ C_j q_t (used with the same global first order)."""
+    r = np.random.default_rng(28)
+    B, nb, d = 4, 6, 6
+    q = r.standard_normal((nb, d))
+    Q = np.concatenate([np.stack([q[i], -q[i], q[i], -q[i]]) for i in range(nb)]) * 0.7
+    K = r.standard_normal((B * nb, d))
+    V = r.standard_normal((B * nb, d))
+    a = orc.attention_head(Q, K, V, B, None, 2, "pwt_row")
+    b = orc.attention_head(Q, K, V, B, None, 2, "pwt")
+    assert np.allclose(a["O"], b["O"], rtol=1e-12, atol=1e-12)
+    Kd = np.repeat(r.standard_normal((nb, d)), B, axis=0)
+    for j in range(nb):                               # block j varies along coordinate j % d
+        Kd[j * B:(j + 1) * B, j % d] += r.standard_normal(B) * 0.8
+    Q2 = r.standard_normal((B * nb, d)) * 0.7
+    c = orc.attention_head(Q2, Kd, V, B, None, 2, "pwt_row")
+    e = orc.attention_head(Q2, Kd, V, B, None, 2, "pwt", w_kind="row")
+    assert np.allclose(c["O"], e["O"], rtol=1e-12, atol=1e-12)
+    f = orc.attention_head(Q2, Kd, V, B, None, 2, "pwt")          # pooled differs here
+    assert np.abs(f["O"] - c["O"]).max() > 1e-6
