@@ -33,6 +33,7 @@ def flop_counts(idx: np.ndarray, block_len: np.ndarray, d: int, mode: str) -> di
 
     exact    4d per (valid query, valid key of a selected block)      (QKᵀ and PV)
     virtual  4d per (valid query, unselected block)                   (PISA/PWT)
+             6d per (valid query, unselected block)                   (PWT_ROW: + 2d for w)
              4d per (valid query, valid key of an unselected block)   (LITERAL)
     first    2d² per valid query                                      (A_t H̄ q_t, PISA/PWT)
     prepare  2d² per valid key (H̄ cross term) + 2d·nb² per head for the block scores,
@@ -45,8 +46,8 @@ def flop_counts(idx: np.ndarray, block_len: np.ndarray, d: int, mode: str) -> di
     exact = int((4 * d * rows * sel_tokens).sum())
     unsel_blocks = nb - K_sel
     virtual = first = 0
-    if mode in ("pisa", "pwt"):
-        virtual = int(4 * d * rows.sum() * unsel_blocks * H)
+    if mode in ("pisa", "pwt", "pwt_row"):
+        virtual = int((6 if mode == "pwt_row" else 4) * d * rows.sum() * unsel_blocks * H)
         first = int(2 * d * d * rows.sum() * H)
     elif mode == "literal":
         virtual = int((4 * d * rows * (bl.sum() - sel_tokens)).sum())
@@ -328,6 +329,14 @@ def main():
     ms_perm = timed(lambda: torch.index_select(nat, 1, src, out=cube).masked_fill_(pad, 0))
     del nat, cube
 
+    # PWT with the per-row diagonal w (the pooling ablation), on the same selection
+    pwt_row = None
+    if mode != "pwt_row":
+        fr = flop_counts(idx.cpu().numpy(), bl, d, "pwt_row")
+        ms_row = timed(lambda: pisa.attention_fwd(Q, K, V, st, idx, mask, None, K_sel, "pwt_row", blt, out=O), 3)
+        pwt_row = {"ms_attention": round(ms_row, 4), "attention_flops": fr["attention"],
+                   "tflops": round(fr["attention"] / (ms_row * 1e-3) / 1e12, 2)}
+
     # LITERAL, reported but not held to the dense target
     literal = None
     if mode != "literal":
@@ -400,6 +409,7 @@ def main():
                        "runs": len(cold_step), "flush_bytes": 512 * 2**20},
         "layout_permutation_ms": round(ms_perm, 4),
         "literal": literal,
+        "pwt_row": pwt_row,
         "covariance_routing": routing,
         "rope_selection": rope_leg,
         "flops": fc,

@@ -260,13 +260,14 @@ pisa_status pisa_attention_fwd(pisa_dtype dt, const void* Q, const void* K, cons
   if (K_sel < 0 || K_sel > nb) return fail(PISA_ERR_INVALID_ARG, "K_sel must be in [0, %d] (got %d)", nb, K_sel);
   if (K_sel > 0) PISA_TRY(check_ptr(idx, "idx", false));
   const unsigned base = mode & 15u;
-  if (base > PISA_MODE_LITERAL) return fail(PISA_ERR_INVALID_ARG, "unknown mode %u", base);
+  if (base > PISA_MODE_PWT_ROW) return fail(PISA_ERR_INVALID_ARG, "unknown mode %u", base);
   if (mode & ~(15u | PISA_W_LINEAR | PISA_W_EXP | PISA_W_NOGATE))
     return fail(PISA_ERR_INVALID_ARG, "unknown mode bits 0x%x", mode);
   if ((mode & PISA_W_LINEAR) && (mode & PISA_W_EXP))
     return fail(PISA_ERR_INVALID_ARG, "PISA_W_LINEAR and PISA_W_EXP are exclusive");
   if (base != PISA_MODE_DROP) PISA_TRY(check_ptr(mask, "mask", false));
   if (base == PISA_MODE_PWT) PISA_TRY(check_ptr(wt, "wt", false));
+  if (base == PISA_MODE_PWT_ROW) PISA_TRY(check_ptr(st->ksig2, "st->ksig2", false));
 
   pisa::AttnArgs a{};
   a.Q = Q;
@@ -276,6 +277,7 @@ pisa_status pisa_attention_fwd(pisa_dtype dt, const void* Q, const void* K, cons
   a.idx = idx;
   a.mask = mask;
   a.wt = wt;
+  a.ksig2 = st->ksig2;
   a.O = O;
   a.lse = lse;
   a.H = H;

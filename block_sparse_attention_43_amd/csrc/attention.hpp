@@ -4,7 +4,7 @@
 
 namespace pisa {
 
-enum { MODE_DROP = 0, MODE_PISA = 1, MODE_PWT = 2, MODE_LITERAL = 3 };
+enum { MODE_DROP = 0, MODE_PISA = 1, MODE_PWT = 2, MODE_LITERAL = 3, MODE_PWT_ROW = 4 };
 
 // Lazy rescaling threshold of the online softmax, in log2 units: the running max only
 // moves when a logit exceeds it by more than kTau, so exponentials stay <= 2^kTau and

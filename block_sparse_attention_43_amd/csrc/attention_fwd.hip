@@ -74,12 +74,13 @@ __global__ __launch_bounds__(128) void attention_kernel(AttnArgs a) {
   constexpr int CPRK = D / EPC;             // chunks per K row
   constexpr int CPRV = kB / EPC;            // chunks per Vᵀ row
   constexpr int PF = kB * D / EPC / 128;    // chunks per thread per operand tile
-  constexpr bool VIRT = (MODE == MODE_PISA || MODE == MODE_PWT);
+  constexpr bool VIRT = (MODE == MODE_PISA || MODE == MODE_PWT || MODE == MODE_PWT_ROW);
+  constexpr bool ROWW = MODE == MODE_PWT_ROW;
   constexpr float NEG_INF = -__builtin_huge_valf();
 
   __shared__ __align__(16) T sK[2][kB * LDK];
   __shared__ __align__(16) T sV[2][D * LDV];
-  __shared__ float sBias[2][kB], sInvN[2][kB];
+  __shared__ float sBias[2][kB], sInvN[2][kB], sLnN[ROWW ? 2 : 1][kB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const uint32_t lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -184,10 +185,11 @@ __global__ __launch_bounds__(128) void attention_kernel(AttnArgs a) {
     if (MODE == MODE_PWT) bw_w = wrow[jj];
   };
   // log2-domain bias ln n_j + φ_{i,j}; -inf for selected blocks and the padding beyond nb.
+  // With the per-row w the bias is ln n_j alone and ln n_j is kept for the gate.
   auto store_bias = [&](int buf, int grp) {
     if (tid < kB) {
       const int jj = grp * kB + tid;
-      float b = NEG_INF, invn = 0.f;
+      float b = NEG_INF, invn = 0.f, lnn_k = 0.f;
       if (jj < nb && !((bw_mask >> (jj & 31)) & 1u)) {
         const int nj = min(max(bw_len, 1), kB);
         const float lnn = logf(float(nj));
@@ -199,9 +201,11 @@ __global__ __launch_bounds__(128) void attention_kernel(AttnArgs a) {
         }
         b = (lnn + phi) * kLog2e;
         invn = 1.f / float(nj);
+        lnn_k = lnn;
       }
       sBias[buf][tid] = b;
       sInvN[buf][tid] = invn;
+      if constexpr (ROWW) sLnN[buf][tid] = lnn_k;
     }
   };
 
@@ -233,6 +237,40 @@ __global__ __launch_bounds__(128) void attention_kernel(AttnArgs a) {
 
     // Sᵀ[key][q] for the two 32-key halves of the tile (independent MFMA chains).
     f32x16 s0 = zero16(), s1 = zero16();
+    if constexpr (ROWW) {
+      if (second) {
+        // Per-row diagonal w_{t,j} = ½ Σ_c q_{t,c}² σ²_{j,c} on MFMA (A = σ²_j / 2 rows of
+        // the group's centroids, B = q² of this lane's query), gated and mapped in place;
+        // the score MFMAs below then accumulate onto φ.
+        const int j0 = j_c * kB + feed_row<M>(l32), j1 = j0 + 32;
+        const float* g0 = a.ksig2 + (size_t(h) * nb + min(j0, nb - 1)) * D + KH * g;
+        const float* g1 = a.ksig2 + (size_t(h) * nb + min(j1, nb - 1)) * D + KH * g;
+        const float h0 = j0 < nb ? 0.5f : 0.f, h1 = j1 < nb ? 0.5f : 0.f;
+#pragma unroll 2
+        for (int ks = 0; ks < NKD; ++ks) {
+          float qv[KH], v0[KH], v1[KH];
+          M::unpack(qf[ks], qv);
+#pragma unroll
+          for (int u = 0; u < KH; ++u) {
+            qv[u] *= qv[u];
+            v0[u] = h0 * g0[KI * ks + u];
+            v1[u] = h1 * g1[KI * ks + u];
+          }
+          const AB b = M::pack(qv);
+          s0 = M::mma(M::pack(v0), b, s0);
+          s1 = M::mma(M::pack(v1), b, s1);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float l0 = sLnN[buf][acc_key<M>(0, r, g)], l1 = sLnN[buf][acc_key<M>(1, r, g)];
+          float w0 = s0[r], w1 = s1[r];
+          if (a.gate && w0 > l0) w0 = 0.f;
+          if (a.gate && w1 > l1) w1 = 0.f;
+          s0[r] = a.w_linear ? log1pf(w0) : w0;
+          s1[r] = a.w_linear ? log1pf(w1) : w1;
+        }
+      }
+    }
     {
       const T* kr0 = sKb + feed_row<M>(l32) * LDK + KH * g;
       const T* kr1 = kr0 + 32 * LDK;
@@ -735,6 +773,8 @@ static hipError_t launch_attn_t(int mode, const AttnArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.H) * unsigned(a.nb));
   if (mode == MODE_LITERAL) {
     hipLaunchKernelGGL((attention_kernel<T, D, MODE_LITERAL>), grid, dim3(128), 0, s, a);
+  } else if (mode == MODE_PWT_ROW) {
+    hipLaunchKernelGGL((attention_kernel<T, D, MODE_PWT_ROW>), grid, dim3(128), 0, s, a);
   } else if constexpr (std::is_same<T, float>::value) {   // fp32 DROP / PISA / PWT
     switch (mode) {
       case MODE_DROP: hipLaunchKernelGGL((attention_split_kernel<T, D, MODE_DROP>), grid, dim3(256), 0, s, a); break;
@@ -746,7 +786,7 @@ static hipError_t launch_attn_t(int mode, const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_attention(int bf16, int mode, const AttnArgs& a, hipStream_t s) {
-  if (bf16 && mode != MODE_LITERAL) return launch_attention_frag(mode, a, s);
+  if (bf16 && mode != MODE_LITERAL && mode != MODE_PWT_ROW) return launch_attention_frag(mode, a, s);
   if (bf16) return a.d == 64 ? launch_attn_t<uint16_t, 64>(mode, a, s) : launch_attn_t<uint16_t, 128>(mode, a, s);
   return a.d == 64 ? launch_attn_t<float, 64>(mode, a, s) : launch_attn_t<float, 128>(mode, a, s);
 }

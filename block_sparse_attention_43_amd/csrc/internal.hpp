@@ -94,6 +94,7 @@ struct AttnArgs {
   const int32_t* idx;
   const uint32_t* mask;
   const float* wt;
+  const float* ksig2;  // [H][nb][d] σ²_j (per-row diagonal w only)
   void* O;
   float* lse;
   int H, L, d, nb, nbp, K_sel, nw;

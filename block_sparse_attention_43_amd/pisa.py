@@ -16,13 +16,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpisa.so")
 
 PISA_F32, PISA_BF16 = 0, 1
-MODE_DROP, MODE_PISA, MODE_PWT, MODE_LITERAL = 0, 1, 2, 3
+MODE_DROP, MODE_PISA, MODE_PWT, MODE_LITERAL, MODE_PWT_ROW = 0, 1, 2, 3, 4
 W_LINEAR, W_EXP, W_NOGATE = 1 << 4, 1 << 5, 1 << 6
 STATS_BLOCK_H, STATS_BLOCK_C, STATS_HNORM = 1 << 0, 1 << 1, 1 << 2
 ROUTE_MEAN, ROUTE_COVARIANCE, ROUTE_ERROR = 0, 1, 2
 ROUTES = {"mean": ROUTE_MEAN, "covariance": ROUTE_COVARIANCE, "error": ROUTE_ERROR}
 ROUTE_EPS = 1e-6          # ε of ln(M_j + ε) in covariance-aware scores
-MODES = {"drop": MODE_DROP, "pisa": MODE_PISA, "pwt": MODE_PWT, "literal": MODE_LITERAL}
+MODES = {"drop": MODE_DROP, "pisa": MODE_PISA, "pwt": MODE_PWT, "literal": MODE_LITERAL,
+         "pwt_row": MODE_PWT_ROW}
 B = 64
 
 # Every symbol include/pisa.h declares.

@@ -77,7 +77,11 @@ enum {
   /* Block-wise first order H_j q_t and per-row w = ½ q_tᵀ C_j q_t with weight 1 + w,
      computed from the raw unselected blocks (blog, PWT derivation; PISA paper Eq. (3.2)
      exact first-order variant). Costs about as much as dense attention. */
-  PISA_MODE_LITERAL = 3
+  PISA_MODE_LITERAL = 3,
+  /* PWT with the per-row diagonal w_{t,j} = ½ Σ_c q_{t,c}² σ²_{j,c} in place of the
+     tile-pooled w̃ (blog, PWT section: the ablation of the pooling; each virtual token
+     costs a second d-long product per row). Reads st->ksig2; wt is not used. */
+  PISA_MODE_PWT_ROW = 4
 };
 
 /* Modifier bits of `mode`. */
@@ -236,8 +240,9 @@ pisa_status pisa_select_topk_rope(pisa_dtype dt, const void* Q, const void* Q_pr
  *   N_t = Σ_{j∈S_i} Σ_{n<n_j} e^{q_t·k_{j,n}} v_{j,n} + Σ_{j∉S_i} e^{q_t·k̄_j + φ_{t,j}} ΣV_j
  *         + first order: (Σ_{j∉S_i} e^{q_t·k̄_j + φ_{t,j}}) H̄ q_t      (PISA, PWT)
  *                        Σ_{j∉S_i} e^{q_t·k̄_j + φ_{t,j}} H_j q_t        (LITERAL)
- *   φ = 0 (PISA); φ = w̃_{i,j} (PWT); per-row w = ½ q_tᵀC_j q_t mapped to ln(1 + w)
- *   (LITERAL); w is zeroed when w > ln n_j unless PISA_W_NOGATE. DROP keeps S_i only.
+ *   φ = 0 (PISA); φ = w̃_{i,j} (PWT); φ = ½ Σ_c q_{t,c}² σ²_{j,c} (PWT_ROW); per-row
+ *   w = ½ q_tᵀC_j q_t mapped to ln(1 + w) (LITERAL); w is zeroed when w > ln n_j unless
+ *   PISA_W_NOGATE. DROP keeps S_i only.
  * Inputs: Q, K, V [H][L][d] dtype `dt`; st->packed from pisa_block_stats on the same K, V;
  * idx from pisa_select_topk with the same K_sel; mask (required unless DROP); wt
  * (required for PWT). Outputs: O [H][L][d] dtype `dt`; lse [H][L] float or NULL

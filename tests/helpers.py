@@ -7,7 +7,7 @@ import torch
 
 from block_sparse_attention_43_amd import synth
 
-MODE_NAMES = ["drop", "pisa", "pwt", "literal"]
+MODE_NAMES = ["drop", "pisa", "pwt", "literal", "pwt_row"]
 
 
 def to_device(inp: synth.Inputs):

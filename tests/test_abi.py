@@ -72,6 +72,7 @@ def _stats(pisa, fake=16):
     (dict(K_sel=-1), 1, "K_sel"),
     (dict(K_sel=17), 1, "K_sel"),
     (dict(mode=7), 1, "unknown mode"),
+    (dict(mode=5), 1, "unknown mode"),
     (dict(mode=2 | (1 << 4) | (1 << 5)), 1, "exclusive"),
     (dict(mode=2, wt=None), 1, "wt must not be NULL"),
     (dict(mode=1, mask=None), 1, "mask must not be NULL"),

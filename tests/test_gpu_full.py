@@ -21,8 +21,8 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}
 # (workload, heads checked, tiles per head (None = all), modes)
 PLAN = {
     "tiny": ([0], None, ["drop", "pisa", "pwt", "literal"]),
-    "flux": ([0, 11, 23], None, ["drop", "pisa", "pwt", "literal"]),
-    "wan": ([0, 19, 39], 24, ["pwt", "pisa", "drop", "literal"]),
+    "flux": ([0, 11, 23], None, ["drop", "pisa", "pwt", "literal", "pwt_row"]),
+    "wan": ([0, 19, 39], 24, ["pwt", "pisa", "drop", "literal", "pwt_row"]),
     "hunyuan": ([0, 23], 12, ["pwt", "literal"]),
     "long": ([0], 64, ["pwt"]),
 }
