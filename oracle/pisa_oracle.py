@@ -395,6 +395,127 @@ def dense_attention_head(Q, K, V, B: int, block_len=None) -> dict:
     return dict(O=O, lse=lse)
 
 
+# ----------------------------------------------------------------------------- backward
+def attention_head_backward(Q, K, V, dO, B: int, block_len=None, K_sel: int = 0, mode: str = "pwt",
+                            idx=None, **overrides) -> dict:
+    """Gradients of one head's attention_head output O with respect to Q, K and V for an
+    upstream gradient dO (the loss sum(dO * O)), with the top-K selection and the gate's
+    decisions held fixed (blog, PWT section: sparse fine-tuning backpropagates through the
+    block statistics k̄_j, H̄ and σ²_j while routing stays detached). Modes DROP, PISA and
+    PWT (tile-pooled w̃, global first order).
+
+    With P_{t,k} = e^{x_{t,k} - lse_t} for the exact keys, P_{t,j} = e^{ℓ_{t,j} - lse_t} for
+    the virtual tokens (ℓ = q·k̄_j + φ_{i,j} + ln n_j), Δ_t = dO_t·O_t, v̄_j = ΣV_j / n_j,
+    u_t = H̄ q_t and Ā_t = Σ_j P_{t,j} / n_j, the output is
+        o_t = Σ_k P_{t,k} v_k + Σ_j P_{t,j} v̄_j + Ā_t u_t
+    and the softmax rule gives dx_{t,k} = P_{t,k}(dO_t·v_k - Δ_t),
+    dℓ_{t,j} = P_{t,j}(dO_t·v̄_j + dO_t·u_t / n_j - Δ_t). Then
+        dq_t  = Σ_k dx k_k + Σ_j dℓ k̄_j + Ā_t H̄ᵀ dO_t (+ the pooled-q² term below)
+        dk_k, dv_k (exact keys) = Σ_t dx_{t,k} q_t, Σ_t P_{t,k} dO_t
+        dk̄_j = Σ_t dℓ_{t,j} q_t,  dv̄_j = Σ_t P_{t,j} dO_t,  dH̄ = Σ_t Ā_t dO_t q_tᵀ
+        dw̃_{i,j} = φ'(w̃_{i,j}) Σ_{t in tile i} dℓ_{t,j}   (0 where the gate fired)
+        d\overline{q²}_i = ½ Σ_j dw̃_{i,j} σ²_j,  dσ²_j = ½ Σ_i dw̃_{i,j} \overline{q²}_i
+    and the statistics pass their gradients to the tokens of block j (valid tokens only):
+        dk_i += dk̄_j / n_j + (2/n_j)(k_i - k̄_j)∘dσ²_j + (1/nb) dH̄ᵀ (v_i - v̄_j)
+        dv_i += dv̄_j / n_j + (1/nb) dH̄ (k_i - k̄_j)
+        dq_t += (2/m_i) q_t ∘ d\overline{q²}_i                (m_i valid rows of tile i)
+    Returns dict(dQ, dK, dV) [L_pad, d] (zeros on padded slots), O, lse, idx."""
+    opts = dict(PRESETS[mode])
+    opts.update(overrides)
+    virtual = opts.get("virtual", True)
+    first = opts.get("first", "none")
+    w_kind = opts.get("w_kind", "none")
+    w_map = opts.get("w_map", "exp")
+    guard = opts.get("guard", "gate")
+    if first not in ("none", "global") or w_kind not in ("none", "pooled") or \
+            opts.get("pooling", "sqmean") != "sqmean" or not opts.get("numerator_w", True):
+        raise ValueError("backward covers DROP, PISA and PWT only")
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    L_pad, d = Q.shape
+    rng = block_ranges(L_pad, B, block_len)
+    nb = len(rng)
+    st = block_stats(K, V, B, block_len, per_block=False)
+    fwd = attention_head(Q, K, V, B, block_len, K_sel, mode, idx=idx, stats=st, **overrides)
+    O, lse, idx = fwd["O"], fwd["lse"], fwd["idx"]
+    pq = pool_queries(Q, B, block_len)
+    n = st["n"]
+    vbar = st["vsum"] / n[:, None]
+    hbar = st["hbar"]                                          # H̄[e, c]
+
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    dkbar = np.zeros((nb, d))
+    dvbar = np.zeros((nb, d))
+    dsig2 = np.zeros((nb, d))
+    dqsq = np.zeros((nb, d))
+    dH = np.zeros((d, d))
+    for i in range(nb):
+        s0, m = rng[i]
+        l_t = lse[s0:s0 + m]
+        live = np.isfinite(l_t)
+        if not live.any():
+            continue
+        q, g, o = Q[s0:s0 + m], dO[s0:s0 + m], O[s0:s0 + m]
+        g = np.where(live[:, None], g, 0.0)
+        lt = np.where(live, l_t, 0.0)[:, None]
+        delta = (g * o).sum(axis=1)
+        sel = np.zeros(nb, dtype=bool)
+        sel[idx[i][(idx[i] >= 0) & (idx[i] < nb)]] = True
+        S = np.flatnonzero(sel)
+        dq = np.zeros((m, d))
+        if S.size:
+            tok = np.concatenate([np.arange(rng[j][0], rng[j][0] + rng[j][1]) for j in S])
+            ks, vs = K[tok], V[tok]
+            P = np.exp(q @ ks.T - lt)
+            dx = P * (g @ vs.T - delta[:, None])
+            dq += dx @ ks
+            np.add.at(dK, tok, dx.T @ q)
+            np.add.at(dV, tok, P.T @ g)
+        U = np.flatnonzero(~sel) if virtual else np.zeros(0, dtype=np.int64)
+        if U.size:
+            s = q @ st["kbar"][U].T
+            lnn = np.log(n[U])[None, :]
+            if w_kind == "pooled":
+                w = np.broadcast_to(0.5 * (st["sig2"][U] @ pq["qsq"][i]), s.shape)
+                fired = (w > lnn) if guard == "gate" else np.zeros(s.shape, dtype=bool)
+                if guard not in ("gate", "none"):
+                    raise ValueError("backward takes the gate or no guard")
+                w0 = np.where(fired, 0.0, w)
+                phi = w0 if w_map == "exp" else np.log1p(w0)
+                dphi = np.where(fired, 0.0, 1.0 if w_map == "exp" else 1.0 / (1.0 + w0))
+            else:
+                phi = dphi = np.zeros_like(s)
+            Pv = np.exp(s + phi + lnn - lt)
+            u = q @ hbar.T                                     # u_t = H̄ q_t
+            gu = (g * u).sum(axis=1) if first == "global" else np.zeros(m)
+            dl = Pv * (g @ vbar[U].T + gu[:, None] / n[U][None, :] - delta[:, None])
+            dq += dl @ st["kbar"][U]
+            dkbar[U] += dl.T @ q
+            dvbar[U] += Pv.T @ g
+            if first == "global":
+                abar = (Pv / n[U][None, :]).sum(axis=1)
+                dq += abar[:, None] * (g @ hbar)
+                dH += (abar[:, None] * g).T @ q
+            if w_kind == "pooled":
+                dw = (dphi * dl).sum(axis=0)                   # one value per block, pooled over rows
+                dqsq[i] += 0.5 * (dw @ st["sig2"][U])
+                dsig2[U] += 0.5 * dw[:, None] * pq["qsq"][i][None, :]
+        dQ[s0:s0 + m] += dq
+
+    for i, (s0, m) in enumerate(rng):
+        dQ[s0:s0 + m] += (2.0 / m) * Q[s0:s0 + m] * dqsq[i][None, :]
+    for j, (s0, nj) in enumerate(rng):
+        kd = K[s0:s0 + nj] - st["kbar"][j]
+        vd = V[s0:s0 + nj] - vbar[j]
+        dK[s0:s0 + nj] += dkbar[j] / nj + (2.0 / nj) * kd * dsig2[j] + vd @ dH / nb
+        dV[s0:s0 + nj] += dvbar[j] / nj + kd @ dH.T / nb
+    return dict(dQ=dQ, dK=dK, dV=dV, O=O, lse=lse, idx=idx)
+
+
 # ----------------------------------------------------------------------------- multi-head
 def run(Q, K, V, B: int, block_len=None, K_sel: int = 0, mode: str = "pwt", heads=None,
         tiles=None, idx=None, **overrides) -> dict:

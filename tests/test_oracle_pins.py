@@ -678,3 +678,66 @@ def test_per_row_diagonal_w_reduces_to_pooled_and_to_full_quadratic_form():
     assert np.allclose(c["O"], e["O"], rtol=1e-12, atol=1e-12)
     f = orc.attention_head(Q2, Kd, V, B, None, 2, "pwt")          # pooled differs here
     assert np.abs(f["O"] - c["O"]).max() > 1e-6
+
+
+def _fd_grads(Q, K, V, dO, B, bl, K_sel, mode, idx, eps=1e-6, **kw):
+    def loss(q, k, v):
+        return float((dO * orc.attention_head(q, k, v, B, bl, K_sel, mode, idx=idx, **kw)["O"]).sum())
+    out = []
+    for which in range(3):
+        X = (Q, K, V)[which]
+        fd = np.zeros_like(X)
+        for t in range(X.shape[0]):
+            for c in range(X.shape[1]):
+                args_p = [Q, K, V]
+                args_m = [Q, K, V]
+                Xp, Xm = X.copy(), X.copy()
+                Xp[t, c] += eps
+                Xm[t, c] -= eps
+                args_p[which], args_m[which] = Xp, Xm
+                fd[t, c] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        out.append(fd)
+    return out
+
+
+@pytest.mark.parametrize("mode,kw", [("drop", {}), ("pisa", {}), ("pwt", {}), ("pwt", dict(w_map="linear")),
+                                     ("pwt", dict(guard="none"))])
+def test_backward_matches_finite_differences(mode, kw):
+    """The analytic gradients (selection and gate decisions held fixed) against central
+    differences of the forward definition itself, ragged blocks included; for PWT one
+    block's keys are spread so widely that its w̃ exceeds ln n_j (the gate fires there)."""
+    r = np.random.default_rng(29)
+    B, nb, d = 4, 5, 3
+    bl = np.array([4, 2, 4, 3, 1])
+    Q = r.standard_normal((B * nb, d)) * 0.8
+    K = r.standard_normal((B * nb, d))
+    K[8:12] *= 4.0                                   # block 2: large σ², gated in PWT
+    V = r.standard_normal((B * nb, d))
+    dO = r.standard_normal((B * nb, d))
+    g = orc.attention_head_backward(Q, K, V, dO, B, bl, 2, mode, **kw)
+    if mode == "pwt" and kw.get("guard", "gate") == "gate":
+        st = orc.block_stats(K, V, B, bl, per_block=False)
+        w = orc.pooled_w(orc.pool_queries(Q, B, bl)["qsq"], st["sig2"])
+        assert (w > np.log(st["n"])[None, :]).any() and (w < np.log(st["n"])[None, :]).any()
+    fd = _fd_grads(Q, K, V, dO, B, bl, 2, mode, g["idx"], **kw)
+    for name, a, b in zip(("dQ", "dK", "dV"), (g["dQ"], g["dK"], g["dV"]), fd):
+        assert np.abs(a - b).max() <= 1e-7 * (np.abs(b).max() + 1.0), name
+
+
+def test_backward_with_every_block_selected_is_dense_attention_gradient():
+    """K_sel = nb: every mode is dense softmax attention, whose gradients torch's autograd
+    gives in float64 (a library routine); padded keys and rows excluded."""
+    import torch
+    r = np.random.default_rng(30)
+    B, nb, d = 4, 4, 5
+    bl = np.array([4, 3, 4, 2])
+    ok = (np.arange(B)[None, :] < bl[:, None]).reshape(-1)
+    Q, K, V, dO = (r.standard_normal((B * nb, d)) for _ in range(4))
+    q, k, v = (torch.tensor(x[ok], requires_grad=True) for x in (Q, K, V))
+    o = torch.softmax(q @ k.T, dim=-1) @ v
+    o.backward(torch.tensor(dO[ok]))
+    for mode in ("drop", "pisa", "pwt"):
+        g = orc.attention_head_backward(Q, K, V, dO, B, bl, nb, mode)
+        for a, t in ((g["dQ"], q), (g["dK"], k), (g["dV"], v)):
+            assert np.allclose(a[ok], t.grad.numpy(), rtol=1e-10, atol=1e-12)
+            assert np.all(a[~ok] == 0.0)
