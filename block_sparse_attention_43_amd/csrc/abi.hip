@@ -296,6 +296,96 @@ pisa_status pisa_attention_fwd(pisa_dtype dt, const void* Q, const void* K, cons
   return ok();
 }
 
+size_t pisa_attention_bwd_workspace_bytes(int H, int L, int d, int B, int K_sel) {
+  if (check_shape(H, L, d, B) != PISA_OK || K_sel < 0 || K_sel > L / B) return 0;
+  return pisa::bwd_layout(H, L, d, K_sel).total;
+}
+
+pisa_status pisa_attention_bwd(pisa_dtype dt, const void* Q, const void* K, const void* V,
+                               const pisa_stats* st, const int32_t* idx, const uint32_t* mask,
+                               const float* wt, int H, int L, int d, int B,
+                               const int32_t* block_len, int K_sel, unsigned mode, const float* lse,
+                               const void* dO, float* dQ, float* dK, float* dV, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  PISA_TRY(check_dtype(dt));
+  PISA_TRY(check_shape(H, L, d, B));
+  PISA_TRY(check_ptr(Q, "Q"));
+  PISA_TRY(check_ptr(K, "K"));
+  PISA_TRY(check_ptr(V, "V"));
+  PISA_TRY(check_ptr(dO, "dO"));
+  PISA_TRY(check_ptr(lse, "lse", false));
+  PISA_TRY(check_ptr(dQ, "dQ"));
+  PISA_TRY(check_ptr(dK, "dK"));
+  PISA_TRY(check_ptr(dV, "dV"));
+  PISA_TRY(check_ptr(st, "st", false));
+  PISA_TRY(check_ptr(st->kbar, "st->kbar"));
+  PISA_TRY(check_ptr(st->vsum, "st->vsum"));
+  PISA_TRY(check_ptr(st->ksig2, "st->ksig2"));
+  PISA_TRY(check_ptr(st->hbarT, "st->hbarT"));
+  PISA_TRY(check_ptr(mask, "mask", false));
+  const int nb = L / B;
+  if (K_sel < 0 || K_sel > nb) return fail(PISA_ERR_INVALID_ARG, "K_sel must be in [0, %d] (got %d)", nb, K_sel);
+  if (K_sel > 0) PISA_TRY(check_ptr(idx, "idx", false));
+  const unsigned base = mode & 15u;
+  if (base > PISA_MODE_PWT_ROW) return fail(PISA_ERR_INVALID_ARG, "unknown mode %u", base);
+  if (base == PISA_MODE_LITERAL || base == PISA_MODE_PWT_ROW)
+    return fail(PISA_ERR_UNSUPPORTED, "the backward covers DROP, PISA and PWT");
+  if (mode & ~(15u | PISA_W_LINEAR | PISA_W_EXP | PISA_W_NOGATE))
+    return fail(PISA_ERR_INVALID_ARG, "unknown mode bits 0x%x", mode);
+  if ((mode & PISA_W_LINEAR) && (mode & PISA_W_EXP))
+    return fail(PISA_ERR_INVALID_ARG, "PISA_W_LINEAR and PISA_W_EXP are exclusive");
+  if (base == PISA_MODE_PWT) PISA_TRY(check_ptr(wt, "wt", false));
+  const pisa::BwdLayout w = pisa::bwd_layout(H, L, d, K_sel);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(PISA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", w.total, workspace_bytes);
+  if (!aligned16(workspace)) return fail(PISA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+  char* ws = static_cast<char*>(workspace);
+  pisa::BwdArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.dO = dO;
+  a.lse = lse;
+  a.block_len = block_len;
+  a.idx = idx;
+  a.mask = mask;
+  a.wt = wt;
+  a.kbar = st->kbar;
+  a.vsum = st->vsum;
+  a.ksig2 = st->ksig2;
+  a.hbarT = st->hbarT;
+  a.dQ = dQ;
+  a.dK = dK;
+  a.dV = dV;
+  a.delta = reinterpret_cast<float*>(ws + w.delta);
+  a.gu = reinterpret_cast<float*>(ws + w.gu);
+  a.abar = reinterpret_cast<float*>(ws + w.abar);
+  a.qsq = base == PISA_MODE_PWT ? reinterpret_cast<float*>(ws + w.qsq) : nullptr;
+  a.dwt = reinterpret_cast<float*>(ws + w.dwt);
+  a.dsig2 = reinterpret_cast<float*>(ws + w.dsig2);
+  a.dkbar_part = reinterpret_cast<float*>(ws + w.dkp);
+  a.dvbar_part = reinterpret_cast<float*>(ws + w.dvp);
+  a.dh_part = reinterpret_cast<float*>(ws + w.dhp);
+  a.dh = reinterpret_cast<float*>(ws + w.dh);
+  a.csr_off = reinterpret_cast<int*>(ws + w.off);
+  a.csr_list = reinterpret_cast<int*>(ws + w.list);
+  a.H = H;
+  a.L = L;
+  a.d = d;
+  a.nb = nb;
+  a.nbp = (nb + B - 1) / B * B;
+  a.K_sel = K_sel;
+  a.nw = (nb + 31) / 32;
+  a.nchunk = w.nchunk;
+  a.nhch = w.nhch;
+  a.w_linear = !!(mode & PISA_W_LINEAR);
+  a.gate = !(mode & PISA_W_NOGATE);
+  hipError_t e = pisa::launch_attention_bwd(dt == PISA_BF16, int(base), a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pisa_attention_bwd launch");
+  return ok();
+}
+
 const char* pisa_last_error(void) { return g_err.c_str(); }
 
 const char* pisa_version(void) { return "pisa-mi355x 0.1.0 (gfx950)"; }

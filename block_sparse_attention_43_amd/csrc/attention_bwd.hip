@@ -1,0 +1,828 @@
+// Backward of the piecewise attention (DROP, PISA, PWT) with the selection and the gate's
+// decisions held fixed, the way sparse fine-tuning trains through the block statistics
+// (Sparse Linear Attention blog, PWT section: gradients flow through k̄_j, H_j (here H̄)
+// and σ²_j, the routing is detached).
+//
+// For query t of tile i: P_{t,k} = e^{x_{t,k} - lse_t} (exact keys), P_{t,j} = e^{ℓ_{t,j} - lse_t}
+// (virtual tokens, ℓ = q·k̄_j + φ_{i,j} + ln n_j), Δ_t = dO_t·O_t, u_t = H̄ q_t,
+// Ā_t = Σ_j P_{t,j} / n_j. The softmax rule gives
+//   dx_{t,k} = P_{t,k}(dO_t·v_k - Δ_t),   dℓ_{t,j} = P_{t,j}(dO_t·v̄_j + dO_t·u_t / n_j - Δ_t)
+// and
+//   dq_t = Σ_k dx k_k + Σ_j dℓ k̄_j + Ā_t H̄ᵀ dO_t + (2/m_i) q_t ∘ ½ Σ_j dw̃_{i,j} σ²_j
+//   dk_k, dv_k (exact) = Σ_t dx_{t,k} q_t, Σ_t P_{t,k} dO_t
+//   dk̄_j = Σ_t dℓ q_t, dv̄_j = Σ_t P_{t,j} dO_t, dH̄ = Σ_t Ā_t dO_t q_tᵀ,
+//   dw̃_{i,j} = φ'(w̃_{i,j}) Σ_{t in i} dℓ_{t,j},  dσ²_j = ½ Σ_i dw̃_{i,j} \overline{q²}_i
+// then every token of block j receives
+//   dk += dk̄_j / n_j + (2/n_j)(k - k̄_j) ∘ dσ²_j + (1/nb) dH̄ᵀ (v - v̄_j),
+//   dv += dv̄_j / n_j + (1/nb) dH̄ (k - k̄_j).
+//
+// Kernels, in launch order (all sums in a fixed order: repeated runs are bit-identical):
+//   bwd_rows_kernel      per query tile: dO_t·u_t, the pooled \overline{q²}_i
+//   csr_count/scan/fill  per key block: the query tiles that selected it, ascending
+//   bwd_query_kernel     per query tile: Δ_t = Σ P dP (first pass over its tiles), then dQ
+//                        from the exact and virtual tiles and H̄ᵀ, Ā_t, the tile's dw̃ row
+//   bwd_key_kernel       per key block: dK, dV of its exact keys over the tiles that
+//                        selected it; per centroid group and chunk of query tiles: dk̄, dv̄
+//   bwd_dh_kernel + bwd_dh_reduce_kernel: dH̄
+//   bwd_qsq_kernel       dQ += the pooled-q² term;  bwd_sig_kernel: dσ²_j
+//   bwd_chain_kernel     per key block: the statistics' gradients onto its tokens
+// The 64 x 64 products run on MFMA with operands staged in LDS (bf16 MFMA with fp32
+// accumulation for bf16 inputs; P and dS enter their products in bf16, as the forward
+// pass's P does); scores are computed with the rows fed in the order that lets the
+// accumulators serve directly as the B operand of the following product.
+#include "attention.hpp"
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace pisa {
+
+namespace {
+
+constexpr float NEG_INF = -__builtin_huge_valf();
+constexpr float POS_INF = __builtin_huge_valf();
+
+template <class T>
+__device__ __forceinline__ u32x4 zero_chunk() {
+  return u32x4{0u, 0u, 0u, 0u};
+}
+
+// 64 rows of a row-major [*, D] T matrix into LDS rows (stride LDK) and, if TRANS, into the
+// transposed tile (stride LDT); rows at or past `valid` are written as zeros.
+template <class T, int D, int LDK, int LDT, bool TRANS>
+__device__ __forceinline__ void stage_rows(const T* src, int valid, T* sX, T* sXt, int tid) {
+  constexpr int EPC = 16 / sizeof(T), CPR = D / EPC;
+  for (int c = tid; c < 64 * CPR; c += 256) {
+    const int r = c / CPR, col = (c % CPR) * EPC;
+    const u32x4 v = r < valid ? *reinterpret_cast<const u32x4*>(src + size_t(r) * D + col) : zero_chunk<T>();
+    *reinterpret_cast<u32x4*>(sX + r * LDK + col) = v;
+    if constexpr (TRANS) {
+      const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+      for (int u = 0; u < EPC; ++u) sXt[(col + u) * LDT + r] = e[u];
+    }
+  }
+}
+
+// 64 rows of an fp32 [*, D] matrix (scaled per row) rounded to T, same layout as above.
+template <class T, int D, int LDK, int LDT, bool TRANS, class Scale>
+__device__ __forceinline__ void stage_rows_f32(const float* src, int valid, Scale scale, T* sX, T* sXt, int tid) {
+  constexpr int CPR = D / 4;
+  for (int c = tid; c < 64 * CPR; c += 256) {
+    const int r = c / CPR, col = (c % CPR) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r < valid) {
+      v = *reinterpret_cast<const float4*>(src + size_t(r) * D + col);
+      const float s = scale(r);
+      v.x *= s; v.y *= s; v.z *= s; v.w *= s;
+    }
+    const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const T t = from_f32<T>(f[u]);
+      sX[r * LDK + col + u] = t;
+      if constexpr (TRANS) sXt[(col + u) * LDT + r] = t;
+    }
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------
+// Per query tile: gu_t = dO_t·(H̄ q_t) for valid rows with support (0 otherwise) and, for
+// PWT, the tile's pooled \overline{q²}_i. Thread (row t, quarter) takes
+// a quarter of the output columns e; H̄[e][c] is read as H̄ᵀ[c][e] (fp32).
+template <class T, int D>
+__global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
+  __shared__ float sq[64][D + 1];
+  __shared__ float sHt[D][D + 1];                  // H̄ᵀ[c][e]
+  __shared__ float part[64][4];
+  const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  int m = a.block_len ? a.block_len[i] : kB;
+  m = min(max(m, 1), kB);
+  const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
+  const T* Qt = static_cast<const T*>(a.Q) + row0 * D;
+  const T* Gt = static_cast<const T*>(a.dO) + row0 * D;
+  for (int x = tid; x < 64 * D; x += 256) sq[x / D][x % D] = (x / D) < m ? to_f32(Qt[x]) : 0.f;
+  const float* hT = a.hbarT + size_t(h) * D * D;
+  for (int x = tid; x < D * D; x += 256) sHt[x / D][x % D] = hT[x];
+  __syncthreads();
+  const int t = tid >> 2, qd = tid & 3;
+  constexpr int EQ = D / 4;
+  float gu = 0.f;
+  if (t < m) {
+    for (int e = qd * EQ; e < qd * EQ + EQ; ++e) {
+      const float g = to_f32(Gt[size_t(t) * D + e]);
+      float u = 0.f;
+      for (int c = 0; c < D; ++c) u = fmaf(sHt[c][e], sq[t][c], u);
+      gu = fmaf(g, u, gu);
+    }
+  }
+  part[t][qd] = gu;
+  __syncthreads();
+  if (tid < 64) {
+    const float l = a.lse[row0 + tid];
+    const bool live = tid < m && l > NEG_INF;
+    a.gu[row0 + tid] = live ? (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]) : 0.f;
+  }
+  if (a.qsq && tid < D) {
+    float s = 0.f;
+    for (int r = 0; r < m; ++r) s = fmaf(sq[r][tid], sq[r][tid], s);
+    a.qsq[(size_t(h) * a.nb + i) * D + tid] = s / float(m);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Query tiles that selected key block j (from the membership bitmask), ascending: counts,
+// per-head exclusive scan, fill. One thread per (head, block) for count and fill.
+__global__ __launch_bounds__(256) void csr_count_kernel(BwdArgs a) {
+  const int j = blockIdx.x * 256 + threadIdx.x, h = blockIdx.y;
+  if (j >= a.nb) return;
+  const uint32_t* mh = a.mask + size_t(h) * a.nb * a.nw;
+  int c = 0;
+  for (int i = 0; i < a.nb; ++i) c += (mh[size_t(i) * a.nw + (j >> 5)] >> (j & 31)) & 1u;
+  a.csr_off[size_t(h) * (a.nb + 1) + j + 1] = c;
+}
+
+__global__ __launch_bounds__(256) void csr_scan_kernel(BwdArgs a) {
+  __shared__ int sh[8];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  int* off = a.csr_off + size_t(h) * (a.nb + 1);
+  const int C = (a.nb + 255) / 256, j0 = min(tid * C, a.nb), j1 = min(j0 + C, a.nb);
+  int s = 0;
+  for (int j = j0; j < j1; ++j) s += off[j + 1];
+  int total;
+  int run = block_exclusive_scan_256(s, sh, &total);
+  __syncthreads();
+  const int cap = a.nb * a.K_sel;                  // list capacity (a mask with more bits is cut)
+  for (int j = j0; j < j1; ++j) {
+    const int c = off[j + 1];
+    off[j + 1] = min(run + c, cap);
+    run += c;
+  }
+  if (tid == 0) off[0] = 0;
+}
+
+__global__ __launch_bounds__(256) void csr_fill_kernel(BwdArgs a) {
+  const int j = blockIdx.x * 256 + threadIdx.x, h = blockIdx.y;
+  if (j >= a.nb) return;
+  const uint32_t* mh = a.mask + size_t(h) * a.nb * a.nw;
+  const int* off = a.csr_off + size_t(h) * (a.nb + 1);
+  const int o0 = off[j], len = off[j + 1] - o0;
+  int* out = a.csr_list + size_t(h) * a.nb * a.K_sel + o0;
+  int c = 0;
+  for (int i = 0; i < a.nb && c < len; ++i)
+    if ((mh[size_t(i) * a.nw + (j >> 5)] >> (j & 31)) & 1u) out[c++] = i;
+}
+
+// ---------------------------------------------------------------------------------------
+// Per query tile: dQ over its exact tiles and centroid groups, then + Ā_t H̄ᵀ dO_t.
+// Wave (wk, wq) computes Sᵀ and dPᵀ for key half wk and query half wq (keys fed through
+// feed_row, so the dSᵀ registers are the B operand of dQᵀ += Kᵀ dSᵀ); the two key halves
+// are merged at the end.
+template <class T, int D, int MODE>
+__global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
+  using M = typename MmaFor<T>::type;
+  using AB = typename M::AB;
+  constexpr int KI = M::KI, KH = M::KH;
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int LDK = D + EPC, LDT = kB + EPC;
+  constexpr int NKD = D / KI, NKH = 32 / KI, NET = D / 32;
+  constexpr bool VIRT = MODE != MODE_DROP;
+  constexpr int TK = kB * LDK * int(sizeof(T)), TT = D * LDT * int(sizeof(T));
+  __shared__ __align__(16) char lds[2 * TK + TT];
+  T* sK = reinterpret_cast<T*>(lds);
+  T* sV = reinterpret_cast<T*>(lds + TK);
+  T* sKt = reinterpret_cast<T*>(lds + 2 * TK);
+  __shared__ float sBias[kB], sInvN[kB], sDphi[kB], sDel[2][kB];
+  __shared__ float sDW[kB][kB + 1];              // dSᵀ of a centroid group (PWT), [key][query]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int wk = wave >> 1, wq = wave & 1;
+  const uint32_t lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = int(lin / uint32_t(a.nb)), i = int(lin % uint32_t(a.nb));
+  const int nb = a.nb;
+  int m = a.block_len ? a.block_len[i] : kB;
+  m = min(max(m, 1), kB);
+  const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
+  const int qrow = 32 * wq + l32;
+  const float lse = a.lse[row0 + qrow];
+  const bool qvalid = qrow < m && lse > NEG_INF;
+  const float lse2 = qvalid ? lse * kLog2e : POS_INF;   // P = 0 on rows without support
+  const float gu = a.gu[row0 + qrow];
+  float delta = 0.f;                               // Δ_t = Σ P dP over every tile (first pass)
+
+  const T* Qh = static_cast<const T*>(a.Q) + size_t(h) * a.L * D;
+  const T* Gh = static_cast<const T*>(a.dO) + size_t(h) * a.L * D;
+  const T* Kh = static_cast<const T*>(a.K) + size_t(h) * a.L * D;
+  const T* Vh = static_cast<const T*>(a.V) + size_t(h) * a.L * D;
+  AB qf[NKD], gf[NKD];
+#pragma unroll
+  for (int ks = 0; ks < NKD; ++ks) {
+    qf[ks] = qvalid ? M::load(Qh + (size_t(i) * kB + qrow) * D + KI * ks + KH * g) : M::zero();
+    gf[ks] = qvalid ? M::load(Gh + (size_t(i) * kB + qrow) * D + KI * ks + KH * g) : M::zero();
+  }
+  f32x16 dqt[NET];
+#pragma unroll
+  for (int et = 0; et < NET; ++et) dqt[et] = zero16();
+  float abar = 0.f;
+
+  const int32_t* irow = a.idx + (size_t(h) * nb + i) * a.K_sel;
+  const uint32_t* mrow = a.mask ? a.mask + (size_t(h) * nb + i) * a.nw : nullptr;
+  const float* wrow = a.wt ? a.wt + (size_t(h) * nb + i) * nb : nullptr;
+  const int n1 = a.K_sel, N = n1 + (VIRT ? a.nbp / kB : 0);
+  const int R = 32 * wk + feed_row<M>(l32);       // key row this lane feeds
+
+  // Two passes over the tiles: the first forms Δ_t = dO_t·o_t as Σ P dP in fp32 from the
+  // recomputed P and dP (the definition, instead of the rounded forward output), the
+  // second dS = P (dP - Δ) and dQ.
+  for (int pass = 0; pass < 2; ++pass) {
+  float dsum = 0.f;
+  for (int n = 0; n < N; ++n) {
+    const bool virt = VIRT && n >= n1;
+    int j = 0, nj = 0;
+    if (!virt) {
+      j = irow[n];
+      if (j >= 0 && j < nb) nj = min(max(a.block_len ? a.block_len[j] : kB, 1), kB);
+    } else {
+      j = n - n1;
+    }
+    __syncthreads();                               // previous tile's LDS reads done
+    if (!virt) {
+      if (nj == 0) continue;                       // uniform: out-of-range index, empty block
+      if (pass) stage_rows<T, D, LDK, LDT, true>(Kh + size_t(j) * kB * D, nj, sK, sKt, tid);
+      else stage_rows<T, D, LDK, LDT, false>(Kh + size_t(j) * kB * D, nj, sK, nullptr, tid);
+      stage_rows<T, D, LDK, LDT, false>(Vh + size_t(j) * kB * D, nj, sV, nullptr, tid);
+      if (tid < kB) {
+        sBias[tid] = tid < nj ? 0.f : NEG_INF;
+        sInvN[tid] = 0.f;
+      }
+    } else {
+      const int jb = j * kB, valid = min(kB, nb - jb);
+      const float* kb = a.kbar + (size_t(h) * nb + jb) * D;
+      const float* vs = a.vsum + (size_t(h) * nb + jb) * D;
+      auto one = [](int) { return 1.f; };
+      auto inv = [&](int r) { return 1.f / float(min(max(a.block_len ? a.block_len[jb + r] : kB, 1), kB)); };
+      if (pass) stage_rows_f32<T, D, LDK, LDT, true>(kb, valid, one, sK, sKt, tid);
+      else stage_rows_f32<T, D, LDK, LDT, false>(kb, valid, one, sK, nullptr, tid);
+      stage_rows_f32<T, D, LDK, LDT, false>(vs, valid, inv, sV, nullptr, tid);
+      if (tid < kB) {
+        const int jj = jb + tid;
+        float b = NEG_INF, invn = 0.f, dphi = 0.f;
+        if (jj < nb && !((mrow[jj >> 5] >> (jj & 31)) & 1u)) {
+          const int nn = min(max(a.block_len ? a.block_len[jj] : kB, 1), kB);
+          const float lnn = logf(float(nn));
+          float phi = 0.f;
+          if (MODE == MODE_PWT) {
+            float w = wrow[jj];
+            const bool fired = a.gate && w > lnn;
+            if (fired) w = 0.f;
+            phi = a.w_linear ? log1pf(w) : w;
+            dphi = fired ? 0.f : (a.w_linear ? 1.f / (1.f + w) : 1.f);
+          }
+          b = (lnn + phi) * kLog2e;
+          invn = 1.f / float(nn);
+        }
+        sBias[tid] = b;
+        sInvN[tid] = invn;
+        sDphi[tid] = dphi;
+      }
+    }
+    __syncthreads();
+
+    f32x16 s = zero16(), p = zero16();
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks) {
+      s = M::mma(M::load(sK + R * LDK + KI * ks + KH * g), qf[ks], s);
+      p = M::mma(M::load(sV + R * LDK + KI * ks + KH * g), gf[ks], p);
+    }
+    if (pass == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * wk + acc_key<M>(0, r, g);
+        const float P = fast_exp2(fmaf(s[r], kLog2e, sBias[key]) - lse2);
+        const float dp = virt ? fmaf(gu, sInvN[key], p[r]) : p[r];
+        dsum = fmaf(P, dp, dsum);
+      }
+      continue;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * wk + acc_key<M>(0, r, g);
+      const float P = fast_exp2(fmaf(s[r], kLog2e, sBias[key]) - lse2);
+      float dp = p[r];
+      if (virt) {
+        dp = fmaf(gu, sInvN[key], dp);
+        abar = fmaf(P, sInvN[key], abar);
+      }
+      s[r] = P * (dp - delta);
+    }
+    if (MODE == MODE_PWT && virt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sDW[32 * wk + acc_key<M>(0, r, g)][qrow] = s[r];
+    }
+    // dS enters as hi + lo bf16 parts (its rows sum to ~0, so dQ = Σ dS (k - k̄) cancels and
+    // one rounding of dS would dominate the error); fp32 inputs use one exact product.
+    f32x16 lo;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float hi = to_f32(from_f32<T>(s[r]));
+        lo[r] = s[r] - hi;
+        s[r] = hi;
+      }
+    }
+    static_for<0, NKH>([&](auto ksc) {
+      constexpr int ks = decltype(ksc)::value;
+      const AB b = M::template packv<ks * KH>(s);
+#pragma unroll
+      for (int et = 0; et < NET; ++et) {
+        const AB ka = M::load(sKt + (32 * et + l32) * LDT + 32 * wk + KI * ks + KH * g);
+        dqt[et] = M::mma(ka, b, dqt[et]);
+        if constexpr (sizeof(T) == 2) dqt[et] = M::mma(ka, M::template packv<ks * KH>(lo), dqt[et]);
+      }
+    });
+    if (MODE == MODE_PWT && virt) {
+      __syncthreads();
+      if (tid < kB && j * kB + tid < nb) {
+        float c = 0.f;
+        for (int q = 0; q < kB; ++q) c += sDW[tid][q];
+        a.dwt[(size_t(h) * nb + i) * nb + j * kB + tid] = sDphi[tid] * c;
+      }
+    }
+  }
+  if (pass == 0) {                                 // Δ of this lane's query: both key halves
+    dsum = sum_halves(dsum);
+    if (g == 0) sDel[wk][qrow] = dsum;
+    __syncthreads();
+    delta = qvalid ? sDel[0][qrow] + sDel[1][qrow] : 0.f;
+    if (wk == 0 && g == 0) a.delta[row0 + qrow] = delta;
+  }
+  }
+
+  // Merge the key halves: wave (1, wq) hands its partial dQᵀ and Ā to wave (0, wq).
+  constexpr int XF = (NET * 16 + 1) * 64;          // floats handed over per wave
+  static_assert(2 * XF * 4 <= 2 * TK + TT, "hand-over buffer");
+  __syncthreads();
+  if (wk == 1) {
+    float* mine = reinterpret_cast<float*>(lds) + wq * XF + lane;
+#pragma unroll
+    for (int et = 0; et < NET; ++et)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mine[(et * 16 + r) * 64] = dqt[et][r];
+    mine[NET * 16 * 64] = abar;
+  }
+  __syncthreads();
+  if (wk == 1) return;
+  {
+    const float* other = reinterpret_cast<const float*>(lds) + wq * XF + lane;
+#pragma unroll
+    for (int et = 0; et < NET; ++et)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dqt[et][r] += other[(et * 16 + r) * 64];
+    abar = sum_halves(abar + other[NET * 16 * 64]);
+  }
+  if (VIRT) {
+    // dQᵀ[c][q] += Σ_e H̄ᵀ[c][e] (Ā_q dO_q)[e]: A = H̄ᵀ rows (fp32 → T), B = Ā·dO fragments.
+    const float* hT = a.hbarT + size_t(h) * D * D;
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks) {
+      float gv[KH];
+      M::unpack(gf[ks], gv);
+#pragma unroll
+      for (int u = 0; u < KH; ++u) gv[u] *= abar;
+      const AB b = M::pack(gv);
+#pragma unroll
+      for (int et = 0; et < NET; ++et) {
+        float hv[KH];
+#pragma unroll
+        for (int u = 0; u < KH; ++u) hv[u] = hT[size_t(32 * et + l32) * D + KI * ks + KH * g + u];
+        dqt[et] = M::mma(M::pack(hv), b, dqt[et]);
+      }
+    }
+  }
+  float* dq = a.dQ + (row0 + qrow) * D;
+#pragma unroll
+  for (int et = 0; et < NET; ++et)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[32 * et + acc_row(r, g)] = qvalid ? dqt[et][r] : 0.f;
+  if (g == 0) a.abar[row0 + qrow] = qvalid ? abar : 0.f;
+}
+
+// ---------------------------------------------------------------------------------------
+// Per key block (exact: over the query tiles that selected it) or per centroid group and
+// chunk of query tiles (virtual): dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS. Wave (wq, wk) computes
+// S and dP for query half wq and key half wk (queries fed through feed_row, so P and dS
+// in registers are the B operands); the two query halves are merged at the end.
+template <class T, int D, int MODE, bool GROUP>
+__global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
+  using M = typename MmaFor<T>::type;
+  using AB = typename M::AB;
+  constexpr int KI = M::KI, KH = M::KH;
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int LDK = D + EPC, LDT = kB + EPC;
+  constexpr int NKD = D / KI, NKH = 32 / KI, NET = D / 32;
+  constexpr int TK = kB * LDK * int(sizeof(T)), TT = D * LDT * int(sizeof(T));
+  __shared__ __align__(16) char lds[2 * TK + 2 * TT];
+  T* sQ = reinterpret_cast<T*>(lds);
+  T* sG = reinterpret_cast<T*>(lds + TK);
+  T* sQt = reinterpret_cast<T*>(lds + 2 * TK);
+  T* sGt = reinterpret_cast<T*>(lds + 2 * TK + TT);
+  __shared__ float sL[kB], sD[kB], sU[kB], sBias[kB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int wq = wave >> 1, wk = wave & 1;
+  const int nb = a.nb;
+  const int ngrp = a.nbp / kB;
+  int h, j, chunk = 0;
+  {
+    const uint32_t units = GROUP ? uint32_t(ngrp) * a.nchunk : uint32_t(nb);
+    const uint32_t lin = xcd_remap(blockIdx.x, gridDim.x);
+    h = int(lin / units);
+    const int u = int(lin % units);
+    j = GROUP ? u / a.nchunk : u;
+    chunk = GROUP ? u % a.nchunk : 0;
+  }
+  const int kcol = 32 * wk + l32;                  // this lane's key (column of S)
+  int nj = 0, jj = 0;
+  float invn = 0.f, lnn = 0.f;
+  bool kvalid;
+  if (!GROUP) {
+    nj = min(max(a.block_len ? a.block_len[j] : kB, 1), kB);
+    kvalid = kcol < nj;
+  } else {
+    jj = j * kB + kcol;
+    kvalid = jj < nb;
+    if (kvalid) {
+      const int nn = min(max(a.block_len ? a.block_len[jj] : kB, 1), kB);
+      invn = 1.f / float(nn);
+      lnn = logf(float(nn));
+    }
+  }
+  // K and V rows of this lane's key as B operands (T; centroid groups rounded from fp32).
+  AB kf[NKD], vf[NKD];
+  {
+    const T* Kh = static_cast<const T*>(a.K) + size_t(h) * a.L * D;
+    const T* Vh = static_cast<const T*>(a.V) + size_t(h) * a.L * D;
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks) {
+      if (!kvalid) {
+        kf[ks] = M::zero();
+        vf[ks] = M::zero();
+      } else if (!GROUP) {
+        kf[ks] = M::load(Kh + (size_t(j) * kB + kcol) * D + KI * ks + KH * g);
+        vf[ks] = M::load(Vh + (size_t(j) * kB + kcol) * D + KI * ks + KH * g);
+      } else {
+        float kv[KH], vv[KH];
+        const float* kb = a.kbar + (size_t(h) * nb + jj) * D + KI * ks + KH * g;
+        const float* vs = a.vsum + (size_t(h) * nb + jj) * D + KI * ks + KH * g;
+#pragma unroll
+        for (int u = 0; u < KH; ++u) {
+          kv[u] = to_f32(from_f32<T>(kb[u]));
+          vv[u] = to_f32(from_f32<T>(vs[u] * invn));
+        }
+        kf[ks] = M::pack(kv);
+        vf[ks] = M::pack(vv);
+      }
+    }
+  }
+  f32x16 dvt[NET], dkt[NET];
+#pragma unroll
+  for (int et = 0; et < NET; ++et) dvt[et] = dkt[et] = zero16();
+
+  // Query tiles visited: the CSR list of block j, or chunk `chunk` of all tiles.
+  int t0, t1;
+  const int* list = nullptr;
+  if (!GROUP) {
+    const int* off = a.csr_off + size_t(h) * (nb + 1);
+    t0 = off[j];
+    t1 = off[j + 1];
+    list = a.csr_list + size_t(h) * nb * a.K_sel;
+  } else {
+    const int per = (nb + a.nchunk - 1) / a.nchunk;
+    t0 = min(nb, chunk * per);
+    t1 = min(nb, t0 + per);
+  }
+  const T* Qh = static_cast<const T*>(a.Q) + size_t(h) * a.L * D;
+  const T* Gh = static_cast<const T*>(a.dO) + size_t(h) * a.L * D;
+  const int Rq = 32 * wq + feed_row<M>(l32);       // query row this lane feeds
+
+  for (int x = t0; x < t1; ++x) {
+    const int i = GROUP ? x : list[x];
+    const int m = min(max(a.block_len ? a.block_len[i] : kB, 1), kB);
+    const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
+    __syncthreads();
+    stage_rows<T, D, LDK, LDT, true>(Qh + size_t(i) * kB * D, m, sQ, sQt, tid);
+    stage_rows<T, D, LDK, LDT, true>(Gh + size_t(i) * kB * D, m, sG, sGt, tid);
+    if (tid < kB) {
+      const float l = a.lse[row0 + tid];
+      const bool live = tid < m && l > NEG_INF;
+      sL[tid] = live ? l * kLog2e : POS_INF;
+      sD[tid] = a.delta[row0 + tid];
+      sU[tid] = a.gu[row0 + tid];
+    } else if (GROUP && tid < 2 * kB) {
+      // bias of this lane group's keys for tile i: ln n_j + φ_{i,j}, -inf when selected
+      const int k = tid - kB, jk = j * kB + k;
+      float b = NEG_INF;
+      if (jk < nb) {
+        const uint32_t* mrow = a.mask + (size_t(h) * nb + i) * a.nw;
+        if (!((mrow[jk >> 5] >> (jk & 31)) & 1u)) {
+          const float ln = logf(float(min(max(a.block_len ? a.block_len[jk] : kB, 1), kB)));
+          float phi = 0.f;
+          if (MODE == MODE_PWT) {
+            float w = a.wt[(size_t(h) * nb + i) * nb + jk];
+            if (a.gate && w > ln) w = 0.f;
+            phi = a.w_linear ? log1pf(w) : w;
+          }
+          b = (ln + phi) * kLog2e;
+        }
+      }
+      sBias[k] = b;
+    }
+    __syncthreads();
+
+    f32x16 s = zero16(), p = zero16();
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks) {
+      s = M::mma(M::load(sQ + Rq * LDK + KI * ks + KH * g), kf[ks], s);
+      p = M::mma(M::load(sG + Rq * LDK + KI * ks + KH * g), vf[ks], p);
+    }
+    const float bias = GROUP ? sBias[kcol] : (kvalid ? 0.f : NEG_INF);
+    f32x16 pr;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int q = 32 * wq + acc_key<M>(0, r, g);
+      const float P = fast_exp2(fmaf(s[r], kLog2e, bias) - sL[q]);
+      float dp = p[r];
+      if (GROUP) dp = fmaf(sU[q], invn, dp);
+      pr[r] = P;
+      s[r] = P * (dp - sD[q]);
+    }
+    f32x16 lo;                                     // dS as hi + lo bf16 parts (see bwd_query_kernel)
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float hi = to_f32(from_f32<T>(s[r]));
+        lo[r] = s[r] - hi;
+        s[r] = hi;
+      }
+    }
+    static_for<0, NKH>([&](auto ksc) {
+      constexpr int ks = decltype(ksc)::value;
+      const AB bp = M::template packv<ks * KH>(pr);
+      const AB bs = M::template packv<ks * KH>(s);
+#pragma unroll
+      for (int et = 0; et < NET; ++et) {
+        const int off = (32 * et + l32) * LDT + 32 * wq + KI * ks + KH * g;
+        dvt[et] = M::mma(M::load(sGt + off), bp, dvt[et]);
+        const AB qa = M::load(sQt + off);
+        dkt[et] = M::mma(qa, bs, dkt[et]);
+        if constexpr (sizeof(T) == 2) dkt[et] = M::mma(qa, M::template packv<ks * KH>(lo), dkt[et]);
+      }
+    });
+  }
+  (void)lnn;
+
+  // Merge the query halves: wave (1, wk) hands over to wave (0, wk).
+  constexpr int XF = 2 * NET * 16 * 64;            // floats handed over per wave
+  static_assert(2 * XF * 4 <= 2 * TK + 2 * TT, "hand-over buffer");
+  __syncthreads();
+  if (wq == 1) {
+    float* mine = reinterpret_cast<float*>(lds) + wk * XF + lane;
+#pragma unroll
+    for (int et = 0; et < NET; ++et)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        mine[(et * 16 + r) * 64] = dvt[et][r];
+        mine[((NET + et) * 16 + r) * 64] = dkt[et][r];
+      }
+  }
+  __syncthreads();
+  if (wq == 1) return;
+  const float* other = reinterpret_cast<const float*>(lds) + wk * XF + lane;
+#pragma unroll
+  for (int et = 0; et < NET; ++et)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dvt[et][r] += other[(et * 16 + r) * 64];
+      dkt[et][r] += other[((NET + et) * 16 + r) * 64];
+    }
+  // dVᵀ / dKᵀ accumulators: row e = 32 et + acc_row(r, g), column = this lane's key.
+  float *dk, *dv;
+  if (!GROUP) {
+    const size_t o = (size_t(h) * a.L + size_t(j) * kB + kcol) * D;
+    dk = a.dK + o;
+    dv = a.dV + o;
+  } else {
+    if (!kvalid) return;
+    const size_t o = ((size_t(h) * a.nchunk + chunk) * a.nbp + jj) * D;
+    dk = a.dkbar_part + o;
+    dv = a.dvbar_part + o;
+  }
+#pragma unroll
+  for (int et = 0; et < NET; ++et)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int e = 32 * et + acc_row(r, g);
+      dk[e] = dkt[et][r];
+      dv[e] = dvt[et][r];
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// dH̄[e][c] = Σ_t Ā_t dO_t[e] q_t[c]: per (head, chunk of query tiles) a d x d partial,
+// thread (e-block, c-block) owning EB x EB entries; then a fixed-order reduction.
+template <class T, int D>
+__global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
+  constexpr int EB = D / 16;                       // 16 x 16 thread grid over d x d
+  __shared__ float sg[kB][D + 1], sq[kB][D + 1];
+  const int h = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
+  const int te = tid / 16, tc = tid % 16;
+  const int per = (a.nb + a.nhch - 1) / a.nhch;
+  const int i0 = min(a.nb, ch * per), i1 = min(a.nb, i0 + per);
+  float acc[EB][EB];
+#pragma unroll
+  for (int x = 0; x < EB; ++x)
+#pragma unroll
+    for (int y = 0; y < EB; ++y) acc[x][y] = 0.f;
+  for (int i = i0; i < i1; ++i) {
+    const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
+    __syncthreads();
+    for (int x = tid; x < kB * D; x += 256) {
+      const int r = x / D, c = x % D;
+      const float ab = a.abar[row0 + r];
+      sg[r][c] = ab * to_f32(static_cast<const T*>(a.dO)[(row0 + r) * D + c]);
+      sq[r][c] = ab != 0.f ? to_f32(static_cast<const T*>(a.Q)[(row0 + r) * D + c]) : 0.f;
+    }
+    __syncthreads();
+    for (int r = 0; r < kB; ++r) {
+      float gv[EB], qv[EB];
+#pragma unroll
+      for (int x = 0; x < EB; ++x) {
+        gv[x] = sg[r][te * EB + x];
+        qv[x] = sq[r][tc * EB + x];
+      }
+#pragma unroll
+      for (int x = 0; x < EB; ++x)
+#pragma unroll
+        for (int y = 0; y < EB; ++y) acc[x][y] = fmaf(gv[x], qv[y], acc[x][y]);
+    }
+  }
+  float* out = a.dh_part + (size_t(h) * a.nhch + ch) * D * D;
+#pragma unroll
+  for (int x = 0; x < EB; ++x)
+#pragma unroll
+    for (int y = 0; y < EB; ++y) out[(te * EB + x) * D + tc * EB + y] = acc[x][y];
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dh_reduce_kernel(BwdArgs a) {
+  const int h = blockIdx.y, x = blockIdx.x * 256 + threadIdx.x;
+  if (x >= D * D) return;
+  float s = 0.f;
+  for (int c = 0; c < a.nhch; ++c) s += a.dh_part[(size_t(h) * a.nhch + c) * D * D + x];
+  a.dh[size_t(h) * D * D + x] = s;
+}
+
+// ---------------------------------------------------------------------------------------
+// PWT: dq_t += (2/m_i) q_t ∘ ½ Σ_j dw̃_{i,j} σ²_j (per query tile), and
+// dσ²_j = ½ Σ_i dw̃_{i,j} \overline{q²}_i (per key block).
+template <class T, int D>
+__global__ __launch_bounds__(256) void bwd_qsq_kernel(BwdArgs a) {
+  __shared__ float sdq[D];
+  const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int nb = a.nb;
+  int m = a.block_len ? a.block_len[i] : kB;
+  m = min(max(m, 1), kB);
+  if (tid < D) {
+    const float* dw = a.dwt + (size_t(h) * nb + i) * nb;
+    const float* sg = a.ksig2 + size_t(h) * nb * D + tid;
+    float s = 0.f;
+    for (int j = 0; j < nb; ++j) s = fmaf(dw[j], sg[size_t(j) * D], s);
+    sdq[tid] = s * (1.f / float(m));             // (2/m) · ½ Σ_j dw̃ σ²
+  }
+  __syncthreads();
+  const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
+  for (int x = tid; x < m * D; x += 256) {
+    const int r = x / D, c = x % D;
+    a.dQ[(row0 + r) * D + c] += sdq[c] * to_f32(static_cast<const T*>(a.Q)[(row0 + r) * D + c]);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_sig_kernel(BwdArgs a) {
+  const int x = blockIdx.x * 256 + threadIdx.x, h = blockIdx.y;
+  const int nb = a.nb;
+  if (x >= nb * D) return;
+  const int j = x / D, c = x % D;
+  const float* dw = a.dwt + size_t(h) * nb * nb + j;
+  const float* qs = a.qsq + size_t(h) * nb * D + c;
+  float s = 0.f;
+  for (int i = 0; i < nb; ++i) s = fmaf(dw[size_t(i) * nb], qs[size_t(i) * D], s);
+  a.dsig2[(size_t(h) * nb + j) * D + c] = 0.5f * s;
+}
+
+// ---------------------------------------------------------------------------------------
+// Per key block: the statistics' gradients onto its valid tokens (adds to dK, dV).
+// Thread (token t, quarter) writes a quarter of both rows; dH̄ is staged in LDS.
+template <class T, int D, int MODE>
+__global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a) {
+  __shared__ float sH[D][D + 1];                   // dH̄[e][c] / nb
+  __shared__ float sdk[D], sdv[D], sdsig[D], skb[D], svb[D];
+  const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int nb = a.nb;
+  const int n = min(max(a.block_len ? a.block_len[j] : kB, 1), kB);
+  const float invn = 1.f / float(n), invnb = 1.f / float(nb);
+  constexpr bool VIRT = MODE != MODE_DROP;
+  if (!VIRT) return;
+  for (int x = tid; x < D * D; x += 256) sH[x / D][x % D] = a.dh[size_t(h) * D * D + x] * invnb;
+  if (tid < D) {
+    float dk = 0.f, dv = 0.f;
+    for (int c = 0; c < a.nchunk; ++c) {
+      const size_t o = ((size_t(h) * a.nchunk + c) * a.nbp + j) * D + tid;
+      dk += a.dkbar_part[o];
+      dv += a.dvbar_part[o];
+    }
+    const size_t o = (size_t(h) * nb + j) * D + tid;
+    sdk[tid] = dk * invn;
+    sdv[tid] = dv * invn;
+    sdsig[tid] = MODE == MODE_PWT ? a.dsig2[o] * 2.f * invn : 0.f;
+    skb[tid] = a.kbar[o];
+    svb[tid] = a.vsum[o] * invn;
+  }
+  __syncthreads();
+  const int t = tid >> 2, qd = tid & 3;
+  if (t >= n) return;
+  constexpr int EQ = D / 4;
+  const size_t row = (size_t(h) * a.L + size_t(j) * kB + t) * D;
+  const T* kr = static_cast<const T*>(a.K) + row;
+  const T* vr = static_cast<const T*>(a.V) + row;
+  for (int c = qd * EQ; c < qd * EQ + EQ; ++c) {
+    // dk_c += dk̄_c / n + (2/n)(k_c - k̄_c) dσ²_c + Σ_e dH̄[e][c] (v_e - v̄_e) / nb
+    // dv_c += dv̄_c / n + Σ_e' dH̄[c][e'] (k_e' - k̄_e') / nb
+    float sk = 0.f, sv = 0.f;
+    for (int e = 0; e < D; ++e) {
+      sk = fmaf(sH[e][c], to_f32(vr[e]) - svb[e], sk);
+      sv = fmaf(sH[c][e], to_f32(kr[e]) - skb[e], sv);
+    }
+    a.dK[row + c] += sdk[c] + (to_f32(kr[c]) - skb[c]) * sdsig[c] + sk;
+    a.dV[row + c] += sdv[c] + sv;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+template <class T, int D, int MODE>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
+  const dim3 tiles(a.nb, a.H), blocks((a.nb + 255) / 256, a.H);
+#define PISA_CHECK()                             \
+  do {                                           \
+    hipError_t e_ = hipGetLastError();           \
+    if (e_ != hipSuccess) return e_;             \
+  } while (0)
+  hipLaunchKernelGGL((bwd_rows_kernel<T, D>), tiles, dim3(256), 0, s, a);
+  PISA_CHECK();
+  hipLaunchKernelGGL(csr_count_kernel, blocks, dim3(256), 0, s, a);
+  PISA_CHECK();
+  hipLaunchKernelGGL(csr_scan_kernel, dim3(a.H), dim3(256), 0, s, a);
+  PISA_CHECK();
+  hipLaunchKernelGGL(csr_fill_kernel, blocks, dim3(256), 0, s, a);
+  PISA_CHECK();
+  hipLaunchKernelGGL((bwd_query_kernel<T, D, MODE>), dim3(unsigned(a.H) * unsigned(a.nb)), dim3(256), 0, s, a);
+  PISA_CHECK();
+  hipLaunchKernelGGL((bwd_key_kernel<T, D, MODE, false>), dim3(unsigned(a.H) * unsigned(a.nb)), dim3(256), 0, s, a);
+  PISA_CHECK();
+  if (MODE != MODE_DROP) {
+    const unsigned groups = unsigned(a.nbp / kB) * unsigned(a.nchunk);
+    hipLaunchKernelGGL((bwd_key_kernel<T, D, MODE, true>), dim3(unsigned(a.H) * groups), dim3(256), 0, s, a);
+    PISA_CHECK();
+    hipLaunchKernelGGL((bwd_dh_kernel<T, D>), dim3(a.nhch, a.H), dim3(256), 0, s, a);
+    PISA_CHECK();
+    hipLaunchKernelGGL((bwd_dh_reduce_kernel<D>), dim3((D * D + 255) / 256, a.H), dim3(256), 0, s, a);
+    PISA_CHECK();
+    if (MODE == MODE_PWT) {
+      hipLaunchKernelGGL((bwd_qsq_kernel<T, D>), tiles, dim3(256), 0, s, a);
+      PISA_CHECK();
+      hipLaunchKernelGGL((bwd_sig_kernel<D>), dim3((a.nb * D + 255) / 256, a.H), dim3(256), 0, s, a);
+      PISA_CHECK();
+    }
+    hipLaunchKernelGGL((bwd_chain_kernel<T, D, MODE>), tiles, dim3(256), 0, s, a);
+    PISA_CHECK();
+  }
+#undef PISA_CHECK
+  return hipSuccess;
+}
+
+template <class T, int D>
+static hipError_t launch_bwd_d(int mode, const BwdArgs& a, hipStream_t s) {
+  switch (mode) {
+    case MODE_DROP: return launch_bwd_t<T, D, MODE_DROP>(a, s);
+    case MODE_PISA: return launch_bwd_t<T, D, MODE_PISA>(a, s);
+    default: return launch_bwd_t<T, D, MODE_PWT>(a, s);
+  }
+}
+
+hipError_t launch_attention_bwd(int bf16, int mode, const BwdArgs& a, hipStream_t s) {
+  if (bf16) return a.d == 64 ? launch_bwd_d<uint16_t, 64>(mode, a, s) : launch_bwd_d<uint16_t, 128>(mode, a, s);
+  return a.d == 64 ? launch_bwd_d<float, 64>(mode, a, s) : launch_bwd_d<float, 128>(mode, a, s);
+}
+
+}  // namespace pisa

@@ -30,18 +30,6 @@
 
 namespace pisa {
 
-// Key row (within a 32-key m-tile) that the lane with A-row R loads.
-template <class M>
-__device__ __forceinline__ int feed_row(int R) {
-  const int r = 4 * (R >> 3) + (R & 3), gg = (R >> 2) & 1;
-  return M::KI * (r / M::KH) + M::KH * gg + (r % M::KH);
-}
-// Key (within the 64-key tile) held by accumulator register r of m-tile mt in lane half g.
-template <class M>
-__device__ __forceinline__ int acc_key(int mt, int r, int g) {
-  return 32 * mt + M::KI * (r / M::KH) + M::KH * g + (r % M::KH);
-}
-
 // Running-max update shared by every phase (log2 domain), lazy by kTau.
 template <int NET>
 __device__ __forceinline__ void raise_max(float cand, float& m, float& lsum, float& asum, f32x16 (&acc)[NET]) {

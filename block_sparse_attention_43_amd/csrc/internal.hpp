@@ -103,7 +103,73 @@ struct AttnArgs {
   PackedLayout pl;
 };
 
+// Backward of the attention call (DROP / PISA / PWT); workspace regions as laid out by
+// bwd_layout below.
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* dO;
+  const float* lse;
+  const int32_t* block_len;
+  const int32_t* idx;
+  const uint32_t* mask;
+  const float* wt;
+  const float* kbar;
+  const float* vsum;
+  const float* ksig2;
+  const float* hbarT;
+  float* dQ;
+  float* dK;
+  float* dV;
+  float* delta;      // [H][L]   Δ_t = dO_t·o_t, formed as Σ P dP
+  float* gu;         // [H][L]   dO·(H̄ q)
+  float* abar;       // [H][L]   Ā_t
+  float* qsq;        // [H][nb][d] pooled q² (PWT) or null
+  float* dwt;        // [H][nb][nb] dw̃ (PWT)
+  float* dsig2;      // [H][nb][d]
+  float* dkbar_part; // [H][nchunk][nbp][d]
+  float* dvbar_part; // [H][nchunk][nbp][d]
+  float* dh_part;    // [H][nhch][d][d]
+  float* dh;         // [H][d][d]
+  int* csr_off;      // [H][nb + 1]
+  int* csr_list;     // [H][nb * K_sel]
+  int H, L, d, nb, nbp, K_sel, nw, nchunk, nhch;
+  int w_linear, gate;
+};
+
+struct BwdLayout {
+  size_t delta, gu, abar, qsq, dwt, dsig2, dkp, dvp, dhp, dh, off, list, total;
+  int nchunk, nhch;
+};
+
+inline BwdLayout bwd_layout(int H, int L, int d, int K_sel) {
+  BwdLayout w;
+  const int nb = L / kB, nbp = (nb + kB - 1) / kB * kB, ngrp = nbp / kB;
+  long long c = (1024 + static_cast<long long>(H) * ngrp - 1) / (static_cast<long long>(H) * ngrp);
+  w.nchunk = static_cast<int>(c < 1 ? 1 : (c > nb ? nb : c));
+  long long e = (512 + H - 1) / H;
+  w.nhch = static_cast<int>(e < 1 ? 1 : (e > nb ? nb : e));
+  const size_t f = sizeof(float), Hs = size_t(H);
+  size_t o = 0;
+  w.delta = o; o = align256(o + Hs * L * f);
+  w.gu = o;    o = align256(o + Hs * L * f);
+  w.abar = o;  o = align256(o + Hs * L * f);
+  w.qsq = o;   o = align256(o + Hs * nb * d * f);
+  w.dwt = o;   o = align256(o + Hs * nb * nb * f);
+  w.dsig2 = o; o = align256(o + Hs * nb * d * f);
+  w.dkp = o;   o = align256(o + Hs * w.nchunk * nbp * d * f);
+  w.dvp = o;   o = align256(o + Hs * w.nchunk * nbp * d * f);
+  w.dhp = o;   o = align256(o + Hs * w.nhch * d * d * f);
+  w.dh = o;    o = align256(o + Hs * d * d * f);
+  w.off = o;   o = align256(o + Hs * (nb + 1) * sizeof(int));
+  w.list = o;  o = align256(o + Hs * nb * size_t(K_sel > 0 ? K_sel : 1) * sizeof(int));
+  w.total = o;
+  return w;
+}
+
 hipError_t launch_block_stats(int bf16, const StatsArgs& a, unsigned flags, hipStream_t s);
+hipError_t launch_attention_bwd(int bf16, int mode, const BwdArgs& a, hipStream_t s);
 hipError_t launch_select(int bf16, const SelectArgs& a, hipStream_t s);
 hipError_t launch_attention(int bf16, int mode, const AttnArgs& a, hipStream_t s);
 

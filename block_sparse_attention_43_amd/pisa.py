@@ -30,7 +30,7 @@ B = 64
 EXPORTS = ("pisa_packed_bytes", "pisa_block_stats_workspace_bytes", "pisa_block_stats",
            "pisa_select_workspace_bytes", "pisa_select_topk", "pisa_select_topk_routed",
            "pisa_select_topk_rope",
-           "pisa_attention_fwd",
+           "pisa_attention_fwd", "pisa_attention_bwd_workspace_bytes", "pisa_attention_bwd",
            "pisa_last_error", "pisa_version")
 
 
@@ -86,6 +86,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pisa_attention_fwd.argtypes = [i32, vp, vp, vp, sp, vp, vp, vp, i32, i32, i32, i32, vp, i32,
                                        u32, vp, vp, vp]
     lib.pisa_attention_fwd.restype = i32
+    lib.pisa_attention_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.pisa_attention_bwd_workspace_bytes.restype = sz
+    lib.pisa_attention_bwd.argtypes = [i32, vp, vp, vp, sp, vp, vp, vp, i32, i32, i32, i32, vp, i32, u32,
+                                       vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.pisa_attention_bwd.restype = i32
     lib.pisa_last_error.argtypes = []
     lib.pisa_last_error.restype = ctypes.c_char_p
     lib.pisa_version.argtypes = []
@@ -244,6 +249,27 @@ def attention_fwd(Q, K, V, st: Stats, idx, mask, wt, K_sel: int, mode="pwt", blo
                                   _ptr(mask), _ptr(wt), H, L, d, B, _ptr(block_len), K_sel, m, _ptr(out),
                                   _ptr(lse), _stream(stream)))
     return out, lse
+
+
+def attention_bwd(Q, K, V, st: Stats, idx, mask, wt, K_sel: int, lse, dO, mode="pwt", block_len=None,
+                  out=None, workspace=None, stream=None):
+    """Gradients (dQ, dK, dV) float32 [H, L, d] of sum(dO * O) for the forward call that
+    produced lse with the same arguments (DROP, PISA or PWT)."""
+    lib = load()
+    H, L, d = _shape(Q)
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    if out is None:
+        out = tuple(torch.empty(H, L, d, dtype=torch.float32, device=Q.device) for _ in range(3))
+    dQ, dK, dV = out
+    if workspace is None:
+        need = lib.pisa_attention_bwd_workspace_bytes(H, L, d, B, K_sel)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=Q.device)
+    s = st.struct()
+    _check(lib.pisa_attention_bwd(_dtype_code(Q), _ptr(Q), _ptr(K), _ptr(V), ctypes.byref(s), _ptr(idx),
+                                  _ptr(mask), _ptr(wt), H, L, d, B, _ptr(block_len), K_sel, m, _ptr(lse),
+                                  _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(workspace), workspace.numel(),
+                                  _stream(stream)))
+    return dQ, dK, dV
 
 
 def forward(Q, K, V, K_sel: int, mode="pwt", block_len=None, flags: int = 0, stream=None, route="mean"):

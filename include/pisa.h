@@ -255,6 +255,37 @@ pisa_status pisa_attention_fwd(pisa_dtype dt, const void* Q, const void* K, cons
                                const int32_t* block_len, int K_sel, unsigned mode, void* O,
                                float* lse, void* stream);
 
+/* Workspace bytes of pisa_attention_bwd (0 if unsupported). */
+size_t pisa_attention_bwd_workspace_bytes(int H, int L, int d, int B, int K_sel);
+
+/*
+ * Backward of pisa_attention_fwd for PISA_MODE_DROP, PISA_MODE_PISA and PISA_MODE_PWT (with
+ * the same modifier bits), for sparse fine-tuning (blog, PWT section: gradients flow
+ * through the block statistics k̄_j, H̄ and σ²_j; routing is detached). The selection and
+ * the gate's decisions are held fixed; the loss is sum(dO * O).
+ *   Inputs   Q, K, V, st, idx, mask, wt, block_len, K_sel, mode: as given to the forward
+ *            call (mask is required for every mode and must match idx; st needs kbar, vsum,
+ *            ksig2 and hbarT); lse: that call's output; dO [H][L][d] dtype `dt`.
+ *   Outputs  dQ, dK, dV [H][L][d] float32, overwritten (zeros on padded slots).
+ *   Workspace pisa_attention_bwd_workspace_bytes(H, L, d, B, K_sel) bytes.
+ * With P = e^{logit - lse} for every exact key and virtual token, u_t = H̄ q_t,
+ * Ā_t = Σ_j P_{t,j} / n_j and Δ_t = dO_t·o_t (formed in fp32 as Σ P·dP over every exact key
+ * and virtual token, with dP = dO·v, or dO·v̄_j + dO·u_t / n_j, which is dO·o exactly):
+ *   dq_t  = Σ P(dO·v - Δ) k (exact) + Σ P(dO·v̄_j + dO·u_t / n_j - Δ) k̄_j + Ā_t H̄ᵀ dO_t
+ *           + (2/m_i) q_t ∘ ½ Σ_j dw̃_{i,j} σ²_j                         (PWT)
+ *   dk, dv of exact keys from the same terms; dk̄_j, dv̄_j, dH̄ = Σ_t Ā_t dO_t q_tᵀ and
+ *   dσ²_j = ½ Σ_i dw̃_{i,j} \overline{q²}_i reach the tokens of block j through
+ *   k̄_j, v̄_j = ΣV_j / n_j, H̄ = (1/nb) Σ_j Σ_i v_i (k_i - k̄_j)ᵀ and σ²_j.
+ * Sums are taken in a fixed order (repeated calls are bit-identical). LITERAL and PWT_ROW
+ * give PISA_ERR_UNSUPPORTED.
+ */
+pisa_status pisa_attention_bwd(pisa_dtype dt, const void* Q, const void* K, const void* V,
+                               const pisa_stats* st, const int32_t* idx, const uint32_t* mask,
+                               const float* wt, int H, int L, int d, int B,
+                               const int32_t* block_len, int K_sel, unsigned mode, const float* lse,
+                               const void* dO, float* dQ, float* dK, float* dV, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* pisa_last_error(void);
 
