@@ -329,6 +329,23 @@ def main():
     ms_perm = timed(lambda: torch.index_select(nat, 1, src, out=cube).masked_fill_(pad, 0))
     del nat, cube
 
+    # backward of the timed mode (DROP / PISA / PWT) on the same selection: dQ, dK, dV from dO
+    backward = None
+    if mode in ("drop", "pisa", "pwt"):
+        dO = torch.randn(Q.shape, dtype=torch.float32, device="cuda", generator=torch.Generator(device="cuda").manual_seed(7)).to(Q.dtype)
+        gbuf = tuple(torch.empty(H, L, d, dtype=torch.float32, device="cuda") for _ in range(3))
+        ws_bwd = torch.empty(max(pisa.load().pisa_attention_bwd_workspace_bytes(H, L, d, 64, K_sel), 16),
+                             dtype=torch.uint8, device="cuda")
+        pisa.attention_fwd(Q, K, V, st, idx, mask, wt, K_sel, mode, blt, out=O, lse=lse)
+        ms_bwd = timed(lambda: pisa.attention_bwd(Q, K, V, st, idx, mask, wt, K_sel, lse, dO, mode, blt,
+                                                  out=gbuf, workspace=ws_bwd), 3)
+        fb = flop_counts(idx.cpu().numpy(), bl, d, mode)
+        bflops = int(2.5 * (fb["exact"] + fb["virtual"]) + 2 * fb["first"] + 4 * d * d * int(bl.sum()) * H)
+        backward = {"ms": round(ms_bwd, 4), "algorithmic_flops": bflops,
+                    "tflops": round(bflops / (ms_bwd * 1e-3) / 1e12, 2),
+                    "ratio_to_forward_attention": round(ms_bwd / ms_attn, 2)}
+        del gbuf, ws_bwd, dO
+
     # PWT with the per-row diagonal w (the pooling ablation), on the same selection
     pwt_row = None
     if mode != "pwt_row":
@@ -410,6 +427,7 @@ def main():
         "layout_permutation_ms": round(ms_perm, 4),
         "literal": literal,
         "pwt_row": pwt_row,
+        "backward": backward,
         "covariance_routing": routing,
         "rope_selection": rope_leg,
         "flops": fc,

@@ -46,6 +46,15 @@ __device__ __forceinline__ u32x4 zero_chunk() {
   return u32x4{0u, 0u, 0u, 0u};
 }
 
+// Element (row e, column c) of a transposed [D][64] tile with row stride LDT: the 16-byte
+// chunks of a row are XOR-swizzled by the row's chunk index, so the column-wise stores of
+// the transpose spread over the LDS banks; a chunk stays contiguous for operand reads.
+template <class T, int LDT>
+__device__ __forceinline__ int tix(int e, int c) {
+  constexpr int EPC = 16 / sizeof(T), NCH = 64 / EPC;
+  return e * LDT + ((((c / EPC) ^ ((e / EPC) % NCH)) * EPC) + c % EPC);
+}
+
 // 64 rows of a row-major [*, D] T matrix into LDS rows (stride LDK) and, if TRANS, into the
 // transposed tile (stride LDT); rows at or past `valid` are written as zeros.
 template <class T, int D, int LDK, int LDT, bool TRANS>
@@ -58,7 +67,7 @@ __device__ __forceinline__ void stage_rows(const T* src, int valid, T* sX, T* sX
     if constexpr (TRANS) {
       const T* e = reinterpret_cast<const T*>(&v);
 #pragma unroll
-      for (int u = 0; u < EPC; ++u) sXt[(col + u) * LDT + r] = e[u];
+      for (int u = 0; u < EPC; ++u) sXt[tix<T, LDT>(col + u, r)] = e[u];
     }
   }
 }
@@ -80,7 +89,7 @@ __device__ __forceinline__ void stage_rows_f32(const float* src, int valid, Scal
     for (int u = 0; u < 4; ++u) {
       const T t = from_f32<T>(f[u]);
       sX[r * LDK + col + u] = t;
-      if constexpr (TRANS) sXt[(col + u) * LDT + r] = t;
+      if constexpr (TRANS) sXt[tix<T, LDT>(col + u, r)] = t;
     }
   }
 }
@@ -89,45 +98,54 @@ __device__ __forceinline__ void stage_rows_f32(const float* src, int valid, Scal
 
 // ---------------------------------------------------------------------------------------
 // Per query tile: gu_t = dO_t·(H̄ q_t) for valid rows with support (0 otherwise) and, for
-// PWT, the tile's pooled \overline{q²}_i. Thread (row t, quarter) takes
-// a quarter of the output columns e; H̄[e][c] is read as H̄ᵀ[c][e] (fp32).
+// PWT, the tile's pooled \overline{q²}_i. Uᵀ = H̄ Qᵀ on the fp32 matrix cores (A = H̄ rows
+// read from H̄ᵀ, B = the staged Q rows), so each lane holds one query's column and the
+// dot with dO needs no cross-lane sum; wave w takes query half w & 1 and every other
+// 32-row tile of e.
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
-  __shared__ float sq[64][D + 1];
-  __shared__ float sHt[D][D + 1];                  // H̄ᵀ[c][e]
-  __shared__ float part[64][4];
+  constexpr int NE = D / 32;
+  __shared__ float sq[kB][D + 1], sg[kB][D + 1];
+  __shared__ float part[4][32];
   const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
   int m = a.block_len ? a.block_len[i] : kB;
   m = min(max(m, 1), kB);
   const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
   const T* Qt = static_cast<const T*>(a.Q) + row0 * D;
   const T* Gt = static_cast<const T*>(a.dO) + row0 * D;
-  for (int x = tid; x < 64 * D; x += 256) sq[x / D][x % D] = (x / D) < m ? to_f32(Qt[x]) : 0.f;
-  const float* hT = a.hbarT + size_t(h) * D * D;
-  for (int x = tid; x < D * D; x += 256) sHt[x / D][x % D] = hT[x];
-  __syncthreads();
-  const int t = tid >> 2, qd = tid & 3;
-  constexpr int EQ = D / 4;
-  float gu = 0.f;
-  if (t < m) {
-    for (int e = qd * EQ; e < qd * EQ + EQ; ++e) {
-      const float g = to_f32(Gt[size_t(t) * D + e]);
-      float u = 0.f;
-      for (int c = 0; c < D; ++c) u = fmaf(sHt[c][e], sq[t][c], u);
-      gu = fmaf(g, u, gu);
-    }
+  for (int x = tid; x < kB * D; x += 256) {
+    const bool ok = (x / D) < m;
+    sq[x / D][x % D] = ok ? to_f32(Qt[x]) : 0.f;
+    sg[x / D][x % D] = ok ? to_f32(Gt[x]) : 0.f;
   }
-  part[t][qd] = gu;
   __syncthreads();
-  if (tid < 64) {
-    const float l = a.lse[row0 + tid];
-    const bool live = tid < m && l > NEG_INF;
-    a.gu[row0 + tid] = live ? (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]) : 0.f;
-  }
   if (a.qsq && tid < D) {
     float s = 0.f;
     for (int r = 0; r < m; ++r) s = fmaf(sq[r][tid], sq[r][tid], s);
     a.qsq[(size_t(h) * a.nb + i) * D + tid] = s / float(m);
+  }
+  const float* hT = a.hbarT + size_t(h) * D * D;
+  const int tq = wave & 1, t = 32 * tq + l32;
+  float gu = 0.f;
+  for (int et = wave >> 1; et < NE; et += 2) {
+    f32x16 u = zero16();
+#pragma unroll 8
+    for (int ks = 0; ks < D / 2; ++ks) {
+      const int c = 2 * ks + g;
+      u = __builtin_amdgcn_mfma_f32_32x32x2f32(hT[size_t(c) * D + 32 * et + l32], sq[t][c], u, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) gu = fmaf(sg[t][32 * et + acc_row(r, g)], u[r], gu);
+  }
+  gu = sum_halves(gu);
+  if (g == 0) part[wave][l32] = gu;
+  __syncthreads();
+  if (tid < kB) {
+    const float l = a.lse[row0 + tid];
+    const bool live = tid < m && l > NEG_INF;
+    const int q = tid >> 5, r = tid & 31;
+    a.gu[row0 + tid] = live ? part[q][r] + part[q + 2][r] : 0.f;
   }
 }
 
@@ -235,27 +253,54 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   // Two passes over the tiles: the first forms Δ_t = dO_t·o_t as Σ P dP in fp32 from the
   // recomputed P and dP (the definition, instead of the rounded forward output), the
   // second dS = P (dP - Δ) and dQ.
+  // Exact tiles' K and V rows are loaded into registers one tile ahead (in flight while the
+  // current tile is computed) and written to LDS at the top of their own iteration.
+  constexpr int CPR = D / EPC, CPT = kB * CPR / 256;
+  u32x4 rk[CPT], rv[CPT];
+  auto src = [&](int n, int& j, int& nj) {         // block and valid keys of exact tile n
+    j = irow[n];
+    nj = (j >= 0 && j < nb) ? min(max(a.block_len ? a.block_len[j] : kB, 1), kB) : 0;
+  };
+  auto prefetch = [&](int n) {
+    if (n >= n1) return;
+    int j, nj;
+    src(n, j, nj);
+#pragma unroll
+    for (int p = 0; p < CPT; ++p) {
+      const int c = tid + 256 * p, r = c / CPR, col = (c % CPR) * EPC;
+      const size_t o = (size_t(j) * kB + r) * D + col;
+      rk[p] = r < nj ? *reinterpret_cast<const u32x4*>(Kh + o) : zero_chunk<T>();
+      rv[p] = r < nj ? *reinterpret_cast<const u32x4*>(Vh + o) : zero_chunk<T>();
+    }
+  };
   for (int pass = 0; pass < 2; ++pass) {
   float dsum = 0.f;
+  prefetch(0);
   for (int n = 0; n < N; ++n) {
     const bool virt = VIRT && n >= n1;
     int j = 0, nj = 0;
-    if (!virt) {
-      j = irow[n];
-      if (j >= 0 && j < nb) nj = min(max(a.block_len ? a.block_len[j] : kB, 1), kB);
-    } else {
-      j = n - n1;
-    }
+    if (!virt) src(n, j, nj);
+    else j = n - n1;
     __syncthreads();                               // previous tile's LDS reads done
     if (!virt) {
-      if (nj == 0) continue;                       // uniform: out-of-range index, empty block
-      if (pass) stage_rows<T, D, LDK, LDT, true>(Kh + size_t(j) * kB * D, nj, sK, sKt, tid);
-      else stage_rows<T, D, LDK, LDT, false>(Kh + size_t(j) * kB * D, nj, sK, nullptr, tid);
-      stage_rows<T, D, LDK, LDT, false>(Vh + size_t(j) * kB * D, nj, sV, nullptr, tid);
+      if (nj > 0) {
+#pragma unroll
+        for (int p = 0; p < CPT; ++p) {
+          const int c = tid + 256 * p, r = c / CPR, col = (c % CPR) * EPC;
+          *reinterpret_cast<u32x4*>(sK + r * LDK + col) = rk[p];
+          *reinterpret_cast<u32x4*>(sV + r * LDK + col) = rv[p];
+          if (pass) {
+            const T* e = reinterpret_cast<const T*>(&rk[p]);
+#pragma unroll
+            for (int u = 0; u < EPC; ++u) sKt[tix<T, LDT>(col + u, r)] = e[u];
+          }
+        }
+      }
       if (tid < kB) {
         sBias[tid] = tid < nj ? 0.f : NEG_INF;
         sInvN[tid] = 0.f;
       }
+      prefetch(n + 1);
     } else {
       const int jb = j * kB, valid = min(kB, nb - jb);
       const float* kb = a.kbar + (size_t(h) * nb + jb) * D;
@@ -288,6 +333,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
+    if (!virt && nj == 0) continue;                // uniform: out-of-range index, empty block
 
     f32x16 s = zero16(), p = zero16();
 #pragma unroll
@@ -336,7 +382,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
       const AB b = M::template packv<ks * KH>(s);
 #pragma unroll
       for (int et = 0; et < NET; ++et) {
-        const AB ka = M::load(sKt + (32 * et + l32) * LDT + 32 * wk + KI * ks + KH * g);
+        const AB ka = M::load(sKt + tix<T, LDT>(32 * et + l32, 32 * wk + KI * ks + KH * g));
         dqt[et] = M::mma(ka, b, dqt[et]);
         if constexpr (sizeof(T) == 2) dqt[et] = M::mma(ka, M::template packv<ks * KH>(lo), dqt[et]);
       }
@@ -506,38 +552,79 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   const T* Gh = static_cast<const T*>(a.dO) + size_t(h) * a.L * D;
   const int Rq = 32 * wq + feed_row<M>(l32);       // query row this lane feeds
 
-  for (int x = t0; x < t1; ++x) {
+  // The next query tile's Q and dO rows, row statistics and (centroid groups) bias inputs
+  // are loaded into registers one tile ahead and written to LDS at the top of its iteration.
+  constexpr int CPR = D / EPC, CPT = kB * CPR / 256;
+  u32x4 rq[CPT], rg[CPT];
+  float pl = 0.f, pd = 0.f, pu = 0.f, pw = 0.f;
+  uint32_t pm = 0u;
+  int pn = kB, pmv = kB;
+  auto prefetch = [&](int x) {
+    if (x >= t1) return;
     const int i = GROUP ? x : list[x];
     const int m = min(max(a.block_len ? a.block_len[i] : kB, 1), kB);
+    pmv = m;
+#pragma unroll
+    for (int p = 0; p < CPT; ++p) {
+      const int c = tid + 256 * p, r = c / CPR, col = (c % CPR) * EPC;
+      const size_t o = (size_t(i) * kB + r) * D + col;
+      rq[p] = r < m ? *reinterpret_cast<const u32x4*>(Qh + o) : zero_chunk<T>();
+      rg[p] = r < m ? *reinterpret_cast<const u32x4*>(Gh + o) : zero_chunk<T>();
+    }
     const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
-    __syncthreads();
-    stage_rows<T, D, LDK, LDT, true>(Qh + size_t(i) * kB * D, m, sQ, sQt, tid);
-    stage_rows<T, D, LDK, LDT, true>(Gh + size_t(i) * kB * D, m, sG, sGt, tid);
     if (tid < kB) {
-      const float l = a.lse[row0 + tid];
-      const bool live = tid < m && l > NEG_INF;
-      sL[tid] = live ? l * kLog2e : POS_INF;
-      sD[tid] = a.delta[row0 + tid];
-      sU[tid] = a.gu[row0 + tid];
+      pl = a.lse[row0 + tid];
+      pd = a.delta[row0 + tid];
+      pu = a.gu[row0 + tid];
     } else if (GROUP && tid < 2 * kB) {
-      // bias of this lane group's keys for tile i: ln n_j + φ_{i,j}, -inf when selected
+      const int jk = min(j * kB + tid - kB, nb - 1);
+      pm = a.mask[(size_t(h) * nb + i) * a.nw + (jk >> 5)];
+      pn = a.block_len ? a.block_len[jk] : kB;
+      if (MODE == MODE_PWT) pw = a.wt[(size_t(h) * nb + i) * nb + jk];
+    }
+  };
+  // fp32 at d = 128 has no registers to spare for a tile in flight: load in place.
+  constexpr bool AHEAD = !(sizeof(T) == 4 && D == 128);
+  if (AHEAD) prefetch(t0);
+  for (int x = t0; x < t1; ++x) {
+    if (!AHEAD) prefetch(x);
+    const int m = pmv;
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < CPT; ++p) {
+      const int c = tid + 256 * p, r = c / CPR, col = (c % CPR) * EPC;
+      *reinterpret_cast<u32x4*>(sQ + r * LDK + col) = rq[p];
+      *reinterpret_cast<u32x4*>(sG + r * LDK + col) = rg[p];
+      const T* eq = reinterpret_cast<const T*>(&rq[p]);
+      const T* eg = reinterpret_cast<const T*>(&rg[p]);
+#pragma unroll
+      for (int u = 0; u < EPC; ++u) {
+        sQt[tix<T, LDT>(col + u, r)] = eq[u];
+        sGt[tix<T, LDT>(col + u, r)] = eg[u];
+      }
+    }
+    if (tid < kB) {
+      const bool live = tid < m && pl > NEG_INF;
+      sL[tid] = live ? pl * kLog2e : POS_INF;
+      sD[tid] = pd;
+      sU[tid] = pu;
+    } else if (GROUP && tid < 2 * kB) {
+      // bias of this lane group's keys for the tile: ln n_j + φ_{i,j}, -inf when selected
       const int k = tid - kB, jk = j * kB + k;
       float b = NEG_INF;
-      if (jk < nb) {
-        const uint32_t* mrow = a.mask + (size_t(h) * nb + i) * a.nw;
-        if (!((mrow[jk >> 5] >> (jk & 31)) & 1u)) {
-          const float ln = logf(float(min(max(a.block_len ? a.block_len[jk] : kB, 1), kB)));
-          float phi = 0.f;
-          if (MODE == MODE_PWT) {
-            float w = a.wt[(size_t(h) * nb + i) * nb + jk];
-            if (a.gate && w > ln) w = 0.f;
-            phi = a.w_linear ? log1pf(w) : w;
-          }
-          b = (ln + phi) * kLog2e;
+      if (jk < nb && !((pm >> (jk & 31)) & 1u)) {
+        const float ln = logf(float(min(max(pn, 1), kB)));
+        float phi = 0.f;
+        if (MODE == MODE_PWT) {
+          float w = pw;
+          if (a.gate && w > ln) w = 0.f;
+          phi = a.w_linear ? log1pf(w) : w;
         }
+        b = (ln + phi) * kLog2e;
       }
       sBias[k] = b;
     }
+    if (AHEAD) prefetch(x + 1);
     __syncthreads();
 
     f32x16 s = zero16(), p = zero16();
@@ -572,7 +659,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
       const AB bs = M::template packv<ks * KH>(s);
 #pragma unroll
       for (int et = 0; et < NET; ++et) {
-        const int off = (32 * et + l32) * LDT + 32 * wq + KI * ks + KH * g;
+        const int off = tix<T, LDT>(32 * et + l32, 32 * wq + KI * ks + KH * g);
         dvt[et] = M::mma(M::load(sGt + off), bp, dvt[et]);
         const AB qa = M::load(sQt + off);
         dkt[et] = M::mma(qa, bs, dkt[et]);
@@ -722,18 +809,20 @@ __global__ __launch_bounds__(256) void bwd_sig_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Per key block: the statistics' gradients onto its valid tokens (adds to dK, dV).
-// Thread (token t, quarter) writes a quarter of both rows; dH̄ is staged in LDS.
+// Per key block: the statistics' gradients onto its valid tokens (adds to dK, dV). The two
+// d x d products run on the fp32 matrix cores with dH̄ / nb and the centred tokens staged in
+// LDS: dKᵀ[c][t] += Σ_e dH̄[e][c] (v_t - v̄)[e], dVᵀ[e][t] += Σ_c dH̄[e][c] (k_t - k̄)[c].
 template <class T, int D, int MODE>
 __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a) {
+  constexpr int NE = D / 32;
   __shared__ float sH[D][D + 1];                   // dH̄[e][c] / nb
+  __shared__ float sKd[kB][D + 1], sVd[kB][D + 1]; // k - k̄, v - v̄ (0 on padding)
   __shared__ float sdk[D], sdv[D], sdsig[D], skb[D], svb[D];
   const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int nb = a.nb;
   const int n = min(max(a.block_len ? a.block_len[j] : kB, 1), kB);
   const float invn = 1.f / float(n), invnb = 1.f / float(nb);
-  constexpr bool VIRT = MODE != MODE_DROP;
-  if (!VIRT) return;
   for (int x = tid; x < D * D; x += 256) sH[x / D][x % D] = a.dh[size_t(h) * D * D + x] * invnb;
   if (tid < D) {
     float dk = 0.f, dv = 0.f;
@@ -750,22 +839,37 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a) {
     svb[tid] = a.vsum[o] * invn;
   }
   __syncthreads();
-  const int t = tid >> 2, qd = tid & 3;
-  if (t >= n) return;
-  constexpr int EQ = D / 4;
-  const size_t row = (size_t(h) * a.L + size_t(j) * kB + t) * D;
-  const T* kr = static_cast<const T*>(a.K) + row;
-  const T* vr = static_cast<const T*>(a.V) + row;
-  for (int c = qd * EQ; c < qd * EQ + EQ; ++c) {
-    // dk_c += dk̄_c / n + (2/n)(k_c - k̄_c) dσ²_c + Σ_e dH̄[e][c] (v_e - v̄_e) / nb
-    // dv_c += dv̄_c / n + Σ_e' dH̄[c][e'] (k_e' - k̄_e') / nb
-    float sk = 0.f, sv = 0.f;
-    for (int e = 0; e < D; ++e) {
-      sk = fmaf(sH[e][c], to_f32(vr[e]) - svb[e], sk);
-      sv = fmaf(sH[c][e], to_f32(kr[e]) - skb[e], sv);
+  const size_t row0 = size_t(h) * a.L + size_t(j) * kB;
+  const T* Kb = static_cast<const T*>(a.K) + row0 * D;
+  const T* Vb = static_cast<const T*>(a.V) + row0 * D;
+  for (int x = tid; x < kB * D; x += 256) {
+    const int t = x / D, c = x % D;
+    const bool ok = t < n;
+    sKd[t][c] = ok ? to_f32(Kb[x]) - skb[c] : 0.f;
+    sVd[t][c] = ok ? to_f32(Vb[x]) - svb[c] : 0.f;
+  }
+  __syncthreads();
+  const int tt = wave & 1, t = 32 * tt + l32;
+  const bool tok = t < n;
+  for (int xt = wave >> 1; xt < NE; xt += 2) {
+    f32x16 ak = zero16(), av = zero16();
+#pragma unroll 8
+    for (int ks = 0; ks < D / 2; ++ks) {
+      const int k = 2 * ks + g;
+      // dKᵀ: A(row c = 32 xt + l32, k = e) = dH̄[e][c];  dVᵀ: A(row e = 32 xt + l32, k = c) = dH̄[e][c]
+      ak = __builtin_amdgcn_mfma_f32_32x32x2f32(sH[k][32 * xt + l32], sVd[t][k], ak, 0, 0, 0);
+      av = __builtin_amdgcn_mfma_f32_32x32x2f32(sH[32 * xt + l32][k], sKd[t][k], av, 0, 0, 0);
     }
-    a.dK[row + c] += sdk[c] + (to_f32(kr[c]) - skb[c]) * sdsig[c] + sk;
-    a.dV[row + c] += sdv[c] + sv;
+    if (tok) {
+      float* dk = a.dK + (row0 + t) * D;
+      float* dv = a.dV + (row0 + t) * D;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = 32 * xt + acc_row(r, g);
+        dk[c] += sdk[c] + sKd[t][c] * sdsig[c] + ak[r];
+        dv[c] += sdv[c] + av[r];
+      }
+    }
   }
 }
 
