@@ -19,10 +19,11 @@
 // Kernels, in launch order (all sums in a fixed order: repeated runs are bit-identical):
 //   bwd_rows_kernel      per query tile: dO_t·u_t, the pooled \overline{q²}_i
 //   csr_count/scan/fill  per key block: the query tiles that selected it, ascending
-//   bwd_query_kernel     per query tile: Δ_t = Σ P dP (first pass over its tiles), then dQ
-//                        from the exact and virtual tiles and H̄ᵀ, Ā_t, the tile's dw̃ row
+//   bwd_query_kernel     per query tile, one sweep: Δ_t = Σ P dP and dQ from the exact and
+//                        virtual tiles and H̄ᵀ, Ā_t
 //   bwd_key_kernel       per key block: dK, dV of its exact keys over the tiles that
 //                        selected it; per centroid group and chunk of query tiles: dk̄, dv̄
+//                        and (PWT) dw̃
 //   bwd_dh_kernel + bwd_dh_reduce_kernel: dH̄
 //   bwd_qsq_kernel       dQ += the pooled-q² term;  bwd_sig_kernel: dσ²_j
 //   bwd_chain_kernel     per key block: the statistics' gradients onto its tokens
@@ -195,8 +196,12 @@ __global__ __launch_bounds__(256) void csr_fill_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------------------
 // Per query tile: dQ over its exact tiles and centroid groups, then + Ā_t H̄ᵀ dO_t.
 // Wave (wk, wq) computes Sᵀ and dPᵀ for key half wk and query half wq (keys fed through
-// feed_row, so the dSᵀ registers are the B operand of dQᵀ += Kᵀ dSᵀ); the two key halves
+// feed_row, so registers are the B operands of the products with Kᵀ); the two key halves
 // are merged at the end.
+// One sweep: dQ is linear in Δ, dq_t = Σ P dP k - Δ_t Σ P k, so the sweep accumulates
+// dQ₀ = Kᵀ (P∘dP)ᵀ, kp = Kᵀ Pᵀ and Δ_t = Σ P dP (the definition of dO_t·o_t, in fp32 from
+// the recomputed P and dP) and forms dQ₀ - Δ kp at the end. P∘dP and P enter their products
+// as hi + lo bf16 pairs, so the cancellation in the difference costs no bf16 rounding.
 template <class T, int D, int MODE>
 __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   using M = typename MmaFor<T>::type;
@@ -206,13 +211,13 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   constexpr int LDK = D + EPC, LDT = kB + EPC;
   constexpr int NKD = D / KI, NKH = 32 / KI, NET = D / 32;
   constexpr bool VIRT = MODE != MODE_DROP;
+  constexpr bool SPLIT = sizeof(T) == 2;            // hi + lo operands for bf16
   constexpr int TK = kB * LDK * int(sizeof(T)), TT = D * LDT * int(sizeof(T));
   __shared__ __align__(16) char lds[2 * TK + TT];
   T* sK = reinterpret_cast<T*>(lds);
   T* sV = reinterpret_cast<T*>(lds + TK);
   T* sKt = reinterpret_cast<T*>(lds + 2 * TK);
-  __shared__ float sBias[kB], sInvN[kB], sDphi[kB], sDel[2][kB];
-  __shared__ float sDW[kB][kB + 1];              // dSᵀ of a centroid group (PWT), [key][query]
+  __shared__ float sBias[kB], sInvN[kB], sDel[2][kB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int wk = wave >> 1, wq = wave & 1;
@@ -227,7 +232,6 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   const bool qvalid = qrow < m && lse > NEG_INF;
   const float lse2 = qvalid ? lse * kLog2e : POS_INF;   // P = 0 on rows without support
   const float gu = a.gu[row0 + qrow];
-  float delta = 0.f;                               // Δ_t = Σ P dP over every tile (first pass)
 
   const T* Qh = static_cast<const T*>(a.Q) + size_t(h) * a.L * D;
   const T* Gh = static_cast<const T*>(a.dO) + size_t(h) * a.L * D;
@@ -239,10 +243,10 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
     qf[ks] = qvalid ? M::load(Qh + (size_t(i) * kB + qrow) * D + KI * ks + KH * g) : M::zero();
     gf[ks] = qvalid ? M::load(Gh + (size_t(i) * kB + qrow) * D + KI * ks + KH * g) : M::zero();
   }
-  f32x16 dqt[NET];
+  f32x16 dqt[NET], kpt[NET];
 #pragma unroll
-  for (int et = 0; et < NET; ++et) dqt[et] = zero16();
-  float abar = 0.f;
+  for (int et = 0; et < NET; ++et) dqt[et] = kpt[et] = zero16();
+  float abar = 0.f, dsum = 0.f;
 
   const int32_t* irow = a.idx + (size_t(h) * nb + i) * a.K_sel;
   const uint32_t* mrow = a.mask ? a.mask + (size_t(h) * nb + i) * a.nw : nullptr;
@@ -250,9 +254,6 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   const int n1 = a.K_sel, N = n1 + (VIRT ? a.nbp / kB : 0);
   const int R = 32 * wk + feed_row<M>(l32);       // key row this lane feeds
 
-  // Two passes over the tiles: the first forms Δ_t = dO_t·o_t as Σ P dP in fp32 from the
-  // recomputed P and dP (the definition, instead of the rounded forward output), the
-  // second dS = P (dP - Δ) and dQ.
   // Exact tiles' K and V rows are loaded into registers one tile ahead (in flight while the
   // current tile is computed) and written to LDS at the top of their own iteration.
   constexpr int CPR = D / EPC, CPT = kB * CPR / 256;
@@ -273,8 +274,6 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
       rv[p] = r < nj ? *reinterpret_cast<const u32x4*>(Vh + o) : zero_chunk<T>();
     }
   };
-  for (int pass = 0; pass < 2; ++pass) {
-  float dsum = 0.f;
   prefetch(0);
   for (int n = 0; n < N; ++n) {
     const bool virt = VIRT && n >= n1;
@@ -289,11 +288,9 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
           const int c = tid + 256 * p, r = c / CPR, col = (c % CPR) * EPC;
           *reinterpret_cast<u32x4*>(sK + r * LDK + col) = rk[p];
           *reinterpret_cast<u32x4*>(sV + r * LDK + col) = rv[p];
-          if (pass) {
-            const T* e = reinterpret_cast<const T*>(&rk[p]);
+          const T* e = reinterpret_cast<const T*>(&rk[p]);
 #pragma unroll
-            for (int u = 0; u < EPC; ++u) sKt[tix<T, LDT>(col + u, r)] = e[u];
-          }
+          for (int u = 0; u < EPC; ++u) sKt[tix<T, LDT>(col + u, r)] = e[u];
         }
       }
       if (tid < kB) {
@@ -307,29 +304,25 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
       const float* vs = a.vsum + (size_t(h) * nb + jb) * D;
       auto one = [](int) { return 1.f; };
       auto inv = [&](int r) { return 1.f / float(min(max(a.block_len ? a.block_len[jb + r] : kB, 1), kB)); };
-      if (pass) stage_rows_f32<T, D, LDK, LDT, true>(kb, valid, one, sK, sKt, tid);
-      else stage_rows_f32<T, D, LDK, LDT, false>(kb, valid, one, sK, nullptr, tid);
+      stage_rows_f32<T, D, LDK, LDT, true>(kb, valid, one, sK, sKt, tid);
       stage_rows_f32<T, D, LDK, LDT, false>(vs, valid, inv, sV, nullptr, tid);
       if (tid < kB) {
         const int jj = jb + tid;
-        float b = NEG_INF, invn = 0.f, dphi = 0.f;
+        float b = NEG_INF, invn = 0.f;
         if (jj < nb && !((mrow[jj >> 5] >> (jj & 31)) & 1u)) {
           const int nn = min(max(a.block_len ? a.block_len[jj] : kB, 1), kB);
           const float lnn = logf(float(nn));
           float phi = 0.f;
           if (MODE == MODE_PWT) {
             float w = wrow[jj];
-            const bool fired = a.gate && w > lnn;
-            if (fired) w = 0.f;
+            if (a.gate && w > lnn) w = 0.f;
             phi = a.w_linear ? log1pf(w) : w;
-            dphi = fired ? 0.f : (a.w_linear ? 1.f / (1.f + w) : 1.f);
           }
           b = (lnn + phi) * kLog2e;
           invn = 1.f / float(nn);
         }
         sBias[tid] = b;
         sInvN[tid] = invn;
-        sDphi[tid] = dphi;
       }
     }
     __syncthreads();
@@ -341,16 +334,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
       s = M::mma(M::load(sK + R * LDK + KI * ks + KH * g), qf[ks], s);
       p = M::mma(M::load(sV + R * LDK + KI * ks + KH * g), gf[ks], p);
     }
-    if (pass == 0) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * wk + acc_key<M>(0, r, g);
-        const float P = fast_exp2(fmaf(s[r], kLog2e, sBias[key]) - lse2);
-        const float dp = virt ? fmaf(gu, sInvN[key], p[r]) : p[r];
-        dsum = fmaf(P, dp, dsum);
-      }
-      continue;
-    }
+    f32x16 slo, plo;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = 32 * wk + acc_key<M>(0, r, g);
@@ -360,50 +344,45 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
         dp = fmaf(gu, sInvN[key], dp);
         abar = fmaf(P, sInvN[key], abar);
       }
-      s[r] = P * (dp - delta);
-    }
-    if (MODE == MODE_PWT && virt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sDW[32 * wk + acc_key<M>(0, r, g)][qrow] = s[r];
-    }
-    // dS enters as hi + lo bf16 parts (its rows sum to ~0, so dQ = Σ dS (k - k̄) cancels and
-    // one rounding of dS would dominate the error); fp32 inputs use one exact product.
-    f32x16 lo;
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float hi = to_f32(from_f32<T>(s[r]));
-        lo[r] = s[r] - hi;
-        s[r] = hi;
+      const float pd = P * dp;
+      dsum += pd;
+      s[r] = pd;                                   // P∘dP, then its hi part
+      p[r] = P;                                    // P, then its hi part
+      if constexpr (SPLIT) {
+        const float sh = to_f32(from_f32<T>(pd)), ph = to_f32(from_f32<T>(P));
+        slo[r] = pd - sh;
+        plo[r] = P - ph;
+        s[r] = sh;
+        p[r] = ph;
       }
     }
     static_for<0, NKH>([&](auto ksc) {
       constexpr int ks = decltype(ksc)::value;
-      const AB b = M::template packv<ks * KH>(s);
+      const AB bs = M::template packv<ks * KH>(s);
+      const AB bp = M::template packv<ks * KH>(p);
 #pragma unroll
       for (int et = 0; et < NET; ++et) {
         const AB ka = M::load(sKt + tix<T, LDT>(32 * et + l32, 32 * wk + KI * ks + KH * g));
-        dqt[et] = M::mma(ka, b, dqt[et]);
-        if constexpr (sizeof(T) == 2) dqt[et] = M::mma(ka, M::template packv<ks * KH>(lo), dqt[et]);
+        dqt[et] = M::mma(ka, bs, dqt[et]);
+        kpt[et] = M::mma(ka, bp, kpt[et]);
+        if constexpr (SPLIT) {
+          dqt[et] = M::mma(ka, M::template packv<ks * KH>(slo), dqt[et]);
+          kpt[et] = M::mma(ka, M::template packv<ks * KH>(plo), kpt[et]);
+        }
       }
     });
-    if (MODE == MODE_PWT && virt) {
-      __syncthreads();
-      if (tid < kB && j * kB + tid < nb) {
-        float c = 0.f;
-        for (int q = 0; q < kB; ++q) c += sDW[tid][q];
-        a.dwt[(size_t(h) * nb + i) * nb + j * kB + tid] = sDphi[tid] * c;
-      }
-    }
   }
-  if (pass == 0) {                                 // Δ of this lane's query: both key halves
-    dsum = sum_halves(dsum);
-    if (g == 0) sDel[wk][qrow] = dsum;
-    __syncthreads();
-    delta = qvalid ? sDel[0][qrow] + sDel[1][qrow] : 0.f;
-    if (wk == 0 && g == 0) a.delta[row0 + qrow] = delta;
-  }
-  }
+
+  // Δ of this lane's query over both key halves, then this wave's share dQ₀ - Δ kp.
+  dsum = sum_halves(dsum);
+  if (g == 0) sDel[wk][qrow] = dsum;
+  __syncthreads();
+  const float delta = qvalid ? sDel[0][qrow] + sDel[1][qrow] : 0.f;
+  if (wk == 0 && g == 0) a.delta[row0 + qrow] = delta;
+#pragma unroll
+  for (int et = 0; et < NET; ++et)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqt[et][r] = fmaf(-delta, kpt[et][r], dqt[et][r]);
 
   // Merge the key halves: wave (1, wq) hands its partial dQᵀ and Ā to wave (0, wq).
   constexpr int XF = (NET * 16 + 1) * 64;          // floats handed over per wave
@@ -473,7 +452,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   T* sG = reinterpret_cast<T*>(lds + TK);
   T* sQt = reinterpret_cast<T*>(lds + 2 * TK);
   T* sGt = reinterpret_cast<T*>(lds + 2 * TK + TT);
-  __shared__ float sL[kB], sD[kB], sU[kB], sBias[kB];
+  __shared__ float sL[kB], sD[kB], sU[kB], sBias[kB], sDphi[kB], sCol[2][kB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int wq = wave >> 1, wk = wave & 1;
@@ -611,18 +590,21 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
     } else if (GROUP && tid < 2 * kB) {
       // bias of this lane group's keys for the tile: ln n_j + φ_{i,j}, -inf when selected
       const int k = tid - kB, jk = j * kB + k;
-      float b = NEG_INF;
+      float b = NEG_INF, dphi = 0.f;
       if (jk < nb && !((pm >> (jk & 31)) & 1u)) {
         const float ln = logf(float(min(max(pn, 1), kB)));
         float phi = 0.f;
         if (MODE == MODE_PWT) {
           float w = pw;
-          if (a.gate && w > ln) w = 0.f;
+          const bool fired = a.gate && w > ln;
+          if (fired) w = 0.f;
           phi = a.w_linear ? log1pf(w) : w;
+          dphi = fired ? 0.f : (a.w_linear ? 1.f / (1.f + w) : 1.f);
         }
         b = (ln + phi) * kLog2e;
       }
       sBias[k] = b;
+      sDphi[k] = dphi;
     }
     if (AHEAD) prefetch(x + 1);
     __syncthreads();
@@ -643,6 +625,17 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
       if (GROUP) dp = fmaf(sU[q], invn, dp);
       pr[r] = P;
       s[r] = P * (dp - sD[q]);
+    }
+    if constexpr (GROUP && MODE == MODE_PWT) {
+      // dw̃_{i,j} = φ'(w̃_{i,j}) Σ_{t in tile i} dℓ_{t,j}: column sums of dS over both query halves
+      float cs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cs += s[r];
+      cs = sum_halves(cs);
+      if (g == 0) sCol[wq][kcol] = cs;
+      __syncthreads();
+      if (tid < kB && j * kB + tid < nb)
+        a.dwt[(size_t(h) * nb + x) * nb + j * kB + tid] = sDphi[tid] * (sCol[0][tid] + sCol[1][tid]);
     }
     f32x16 lo;                                     // dS as hi + lo bf16 parts (see bwd_query_kernel)
     if constexpr (sizeof(T) == 2) {
