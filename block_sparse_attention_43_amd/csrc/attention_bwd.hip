@@ -25,7 +25,7 @@
 //                        selected it; per centroid group and chunk of query tiles: dk̄, dv̄
 //                        and (PWT) dw̃
 //   bwd_dh_kernel + bwd_dh_reduce_kernel: dH̄
-//   bwd_qsq_kernel       dQ += the pooled-q² term;  bwd_sig_kernel: dσ²_j
+//   bwd_wprod_kernel     dQ += the pooled-q² term; dσ²_j (products with dw̃)
 //   bwd_chain_kernel     per key block: the statistics' gradients onto its tokens
 // The 64 x 64 products run on MFMA with operands staged in LDS (bf16 MFMA with fp32
 // accumulation for bf16 inputs; P and dS enter their products in bf16, as the forward
@@ -709,21 +709,20 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// dH̄[e][c] = Σ_t Ā_t dO_t[e] q_t[c]: per (head, chunk of query tiles) a d x d partial,
-// thread (e-block, c-block) owning EB x EB entries; then a fixed-order reduction.
+// dH̄[e][c] = Σ_t Ā_t dO_t[e] q_t[c]: per (head, chunk of query tiles) a d x d partial on the
+// fp32 matrix cores (A = (Ā dO)ᵀ, B = Q, contraction over the rows; wave w owns every
+// fourth 32 x 32 output tile), then a fixed-order reduction over the chunks.
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
-  constexpr int EB = D / 16;                       // 16 x 16 thread grid over d x d
+  constexpr int NE = D / 32, NTW = NE * NE / 4;
   __shared__ float sg[kB][D + 1], sq[kB][D + 1];
   const int h = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
-  const int te = tid / 16, tc = tid % 16;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int per = (a.nb + a.nhch - 1) / a.nhch;
   const int i0 = min(a.nb, ch * per), i1 = min(a.nb, i0 + per);
-  float acc[EB][EB];
+  f32x16 acc[NTW];
 #pragma unroll
-  for (int x = 0; x < EB; ++x)
-#pragma unroll
-    for (int y = 0; y < EB; ++y) acc[x][y] = 0.f;
+  for (int u = 0; u < NTW; ++u) acc[u] = zero16();
   for (int i = i0; i < i1; ++i) {
     const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
     __syncthreads();
@@ -734,24 +733,23 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
       sq[r][c] = ab != 0.f ? to_f32(static_cast<const T*>(a.Q)[(row0 + r) * D + c]) : 0.f;
     }
     __syncthreads();
-    for (int r = 0; r < kB; ++r) {
-      float gv[EB], qv[EB];
 #pragma unroll
-      for (int x = 0; x < EB; ++x) {
-        gv[x] = sg[r][te * EB + x];
-        qv[x] = sq[r][tc * EB + x];
+    for (int u = 0; u < NTW; ++u) {
+      const int tile = wave * NTW + u, et = tile / NE, ct = tile % NE;
+#pragma unroll 8
+      for (int ks = 0; ks < kB / 2; ++ks) {
+        const int t = 2 * ks + g;
+        acc[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(sg[t][32 * et + l32], sq[t][32 * ct + l32], acc[u], 0, 0, 0);
       }
-#pragma unroll
-      for (int x = 0; x < EB; ++x)
-#pragma unroll
-        for (int y = 0; y < EB; ++y) acc[x][y] = fmaf(gv[x], qv[y], acc[x][y]);
     }
   }
   float* out = a.dh_part + (size_t(h) * a.nhch + ch) * D * D;
 #pragma unroll
-  for (int x = 0; x < EB; ++x)
+  for (int u = 0; u < NTW; ++u) {
+    const int tile = wave * NTW + u, et = tile / NE, ct = tile % NE;
 #pragma unroll
-    for (int y = 0; y < EB; ++y) out[(te * EB + x) * D + tc * EB + y] = acc[x][y];
+    for (int r = 0; r < 16; ++r) out[(32 * et + acc_row(r, g)) * D + 32 * ct + l32] = acc[u][r];
+  }
 }
 
 template <int D>
@@ -764,42 +762,74 @@ __global__ __launch_bounds__(256) void bwd_dh_reduce_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// PWT: dq_t += (2/m_i) q_t ∘ ½ Σ_j dw̃_{i,j} σ²_j (per query tile), and
-// dσ²_j = ½ Σ_i dw̃_{i,j} \overline{q²}_i (per key block).
-template <class T, int D>
-__global__ __launch_bounds__(256) void bwd_qsq_kernel(BwdArgs a) {
-  __shared__ float sdq[D];
-  const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+// PWT: the two products with dw̃ [nb x nb], on the fp32 matrix cores, one 64-row by d
+// output block per workgroup (4 waves, contraction over 64-wide chunks staged in LDS):
+//   TRANS = false: dqsq_i = ½ Σ_j dw̃_{i,j} σ²_j, then dq_t += (2/m_i) q_t ∘ dqsq_i
+//   TRANS = true:  dσ²_j = ½ Σ_i dw̃_{i,j} \overline{q²}_i
+template <class T, int D, bool TRANS>
+__global__ __launch_bounds__(256) void bwd_wprod_kernel(BwdArgs a) {
+  constexpr int NE = D / 32, NTW = 2 * NE / 4;     // 32 x 32 output tiles per wave
+  __shared__ float sA[kB][kB + 1], sB[kB][D + 1];
+  __shared__ float sOut[kB][D + 1];
+  const int h = blockIdx.y, r0 = blockIdx.x * kB, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int nb = a.nb;
-  int m = a.block_len ? a.block_len[i] : kB;
-  m = min(max(m, 1), kB);
-  if (tid < D) {
-    const float* dw = a.dwt + (size_t(h) * nb + i) * nb;
-    const float* sg = a.ksig2 + size_t(h) * nb * D + tid;
-    float s = 0.f;
-    for (int j = 0; j < nb; ++j) s = fmaf(dw[j], sg[size_t(j) * D], s);
-    sdq[tid] = s * (1.f / float(m));             // (2/m) · ½ Σ_j dw̃ σ²
+  const float* W = a.dwt + size_t(h) * nb * nb;
+  const float* Bm = (TRANS ? a.qsq : a.ksig2) + size_t(h) * nb * D;
+  f32x16 acc[NTW];
+#pragma unroll
+  for (int u = 0; u < NTW; ++u) acc[u] = zero16();
+  for (int k0 = 0; k0 < nb; k0 += kB) {
+    __syncthreads();
+    for (int x = tid; x < kB * kB; x += 256) {     // sA[r][k] = dw̃ (or its transpose), 0 outside
+      const int r = x / kB, k = x % kB, row = r0 + r, col = k0 + k;
+      float v = 0.f;
+      if (row < nb && col < nb) v = TRANS ? W[size_t(col) * nb + row] : W[size_t(row) * nb + col];
+      sA[r][k] = v;
+    }
+    for (int x = tid; x < kB * D; x += 256) {
+      const int k = x / D, c = x % D;
+      sB[k][c] = k0 + k < nb ? Bm[size_t(k0 + k) * D + c] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) {
+      const int tile = wave * NTW + u, rt = tile / NE, ct = tile % NE;
+#pragma unroll 8
+      for (int ks = 0; ks < kB / 2; ++ks) {
+        const int k = 2 * ks + g;
+        acc[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(sA[32 * rt + l32][k], sB[k][32 * ct + l32], acc[u], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NTW; ++u) {
+    const int tile = wave * NTW + u, rt = tile / NE, ct = tile % NE;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sOut[32 * rt + acc_row(r, g)][32 * ct + l32] = 0.5f * acc[u][r];
   }
   __syncthreads();
-  const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
-  for (int x = tid; x < m * D; x += 256) {
-    const int r = x / D, c = x % D;
-    a.dQ[(row0 + r) * D + c] += sdq[c] * to_f32(static_cast<const T*>(a.Q)[(row0 + r) * D + c]);
+  if (TRANS) {
+    for (int x = tid; x < kB * D; x += 256) {
+      const int r = x / D, c = x % D;
+      if (r0 + r < nb) a.dsig2[(size_t(h) * nb + r0 + r) * D + c] = sOut[r][c];
+    }
+  } else {
+    // dq_t += (2/m_i) q_t ∘ dqsq_i for the valid rows of every tile i of this block
+    for (int r = 0; r < kB && r0 + r < nb; ++r) {
+      const int i = r0 + r;
+      const int m = min(max(a.block_len ? a.block_len[i] : kB, 1), kB);
+      const float sc = 2.f / float(m);
+      const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
+      for (int x = tid; x < m * D; x += 256) {
+        const int t = x / D, c = x % D;
+        a.dQ[(row0 + t) * D + c] += sc * sOut[r][c] * to_f32(static_cast<const T*>(a.Q)[(row0 + t) * D + c]);
+      }
+    }
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void bwd_sig_kernel(BwdArgs a) {
-  const int x = blockIdx.x * 256 + threadIdx.x, h = blockIdx.y;
-  const int nb = a.nb;
-  if (x >= nb * D) return;
-  const int j = x / D, c = x % D;
-  const float* dw = a.dwt + size_t(h) * nb * nb + j;
-  const float* qs = a.qsq + size_t(h) * nb * D + c;
-  float s = 0.f;
-  for (int i = 0; i < nb; ++i) s = fmaf(dw[size_t(i) * nb], qs[size_t(i) * D], s);
-  a.dsig2[(size_t(h) * nb + j) * D + c] = 0.5f * s;
-}
+constexpr int CHAIN_G = 8;                         // key blocks per workgroup of bwd_chain_kernel
 
 // ---------------------------------------------------------------------------------------
 // Per key block: the statistics' gradients onto its valid tokens (adds to dK, dV). The two
@@ -811,12 +841,16 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a) {
   __shared__ float sH[D][D + 1];                   // dH̄[e][c] / nb
   __shared__ float sKd[kB][D + 1], sVd[kB][D + 1]; // k - k̄, v - v̄ (0 on padding)
   __shared__ float sdk[D], sdv[D], sdsig[D], skb[D], svb[D];
-  const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int h = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int nb = a.nb;
-  const int n = min(max(a.block_len ? a.block_len[j] : kB, 1), kB);
-  const float invn = 1.f / float(n), invnb = 1.f / float(nb);
+  const float invnb = 1.f / float(nb);
   for (int x = tid; x < D * D; x += 256) sH[x / D][x % D] = a.dh[size_t(h) * D * D + x] * invnb;
+  // CHAIN_G consecutive blocks per workgroup share the staged dH̄.
+  for (int j = blockIdx.x * CHAIN_G; j < min(nb, blockIdx.x * CHAIN_G + CHAIN_G); ++j) {
+  const int n = min(max(a.block_len ? a.block_len[j] : kB, 1), kB);
+  const float invn = 1.f / float(n);
+  __syncthreads();                                 // previous block's reads done
   if (tid < D) {
     float dk = 0.f, dv = 0.f;
     for (int c = 0; c < a.nchunk; ++c) {
@@ -864,6 +898,7 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a) {
       }
     }
   }
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -896,12 +931,13 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((bwd_dh_reduce_kernel<D>), dim3((D * D + 255) / 256, a.H), dim3(256), 0, s, a);
     PISA_CHECK();
     if (MODE == MODE_PWT) {
-      hipLaunchKernelGGL((bwd_qsq_kernel<T, D>), tiles, dim3(256), 0, s, a);
+      const dim3 wgrid((a.nb + kB - 1) / kB, a.H);
+      hipLaunchKernelGGL((bwd_wprod_kernel<T, D, false>), wgrid, dim3(256), 0, s, a);
       PISA_CHECK();
-      hipLaunchKernelGGL((bwd_sig_kernel<D>), dim3((a.nb * D + 255) / 256, a.H), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((bwd_wprod_kernel<T, D, true>), wgrid, dim3(256), 0, s, a);
       PISA_CHECK();
     }
-    hipLaunchKernelGGL((bwd_chain_kernel<T, D, MODE>), tiles, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_chain_kernel<T, D, MODE>), dim3((a.nb + CHAIN_G - 1) / CHAIN_G, a.H), dim3(256), 0, s, a);
     PISA_CHECK();
   }
 #undef PISA_CHECK
