@@ -47,15 +47,6 @@ __device__ __forceinline__ u32x4 zero_chunk() {
   return u32x4{0u, 0u, 0u, 0u};
 }
 
-// Element (row e, column c) of a transposed [D][64] tile with row stride LDT: the 16-byte
-// chunks of a row are XOR-swizzled by the row's chunk index, so the column-wise stores of
-// the transpose spread over the LDS banks; a chunk stays contiguous for operand reads.
-template <class T, int LDT>
-__device__ __forceinline__ int tix(int e, int c) {
-  constexpr int EPC = 16 / sizeof(T), NCH = 64 / EPC;
-  return e * LDT + ((((c / EPC) ^ ((e / EPC) % NCH)) * EPC) + c % EPC);
-}
-
 // 64 rows of a row-major [*, D] T matrix into LDS rows (stride LDK) and, if TRANS, into the
 // transposed tile (stride LDT); rows at or past `valid` are written as zeros.
 template <class T, int D, int LDK, int LDT, bool TRANS>

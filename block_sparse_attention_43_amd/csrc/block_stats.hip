@@ -21,17 +21,23 @@
 namespace pisa {
 
 template <class T, int D, bool PER_BLOCK>
-__global__ __launch_bounds__(256) void block_stats_kernel(StatsArgs a, unsigned flags) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PER_BLOCK ? 1 : 2)))
+void block_stats_kernel(StatsArgs a, unsigned flags) {
   using M = typename MmaFor<T>::type;
   constexpr int KI = M::KI, KH = M::KH;
   constexpr int EPC = 16 / sizeof(T);      // elements per 16-byte chunk
-  constexpr int LDR = D + EPC;             // LDS row stride (elements), padded against bank conflicts
+  constexpr int LDR = D + EPC;             // row stride of the row-major K tile (elements)
+  constexpr int LDT = kB + EPC;            // row stride of the transposed tiles
   constexpr int CPR = D / EPC;             // chunks per token row
   constexpr int CPT = kB * CPR / 256;      // chunks per thread per operand
   constexpr int NT = D / 32;               // 32-wide output tiles per side of d x d
   constexpr int TPW = NT * NT / 4;         // output tiles per wave
+  // K row-major (source of the operand-order K tile) and Kᵀ, Vᵀ (XOR-swizzled, see tix):
+  // the column statistics, the Vᵀ tile and both MFMA operands read 16-byte chunks of the
+  // transposed tiles.
   __shared__ __align__(16) T sK[kB * LDR];
-  __shared__ __align__(16) T sV[kB * LDR];
+  __shared__ __align__(16) T sKt[D * LDT];
+  __shared__ __align__(16) T sVt[D * LDT];
   __shared__ float sKbar[D], sVsum[D];
 
   const int h = blockIdx.y, grp = blockIdx.x;
@@ -74,25 +80,43 @@ __global__ __launch_bounds__(256) void block_stats_kernel(StatsArgs a, unsigned 
 
     __syncthreads();                       // previous block's LDS reads done
 #pragma unroll
-    for (int p = 0; p < CPT; ++p) {        // stage K_j, V_j; rows >= n_j as zeros
+    for (int p = 0; p < CPT; ++p) {        // stage K_j (row-major and transposed), V_jᵀ; rows >= n_j as zeros
       const int c = tid + 256 * p;
       const int row = c / CPR, col = (c % CPR) * EPC;
       const u32x4 z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(sK + row * LDR + col) = row < n ? rk[p] : z;
-      *reinterpret_cast<u32x4*>(sV + row * LDR + col) = row < n ? rv[p] : z;
+      const u32x4 kv = row < n ? rk[p] : z, vv = row < n ? rv[p] : z;
+      *reinterpret_cast<u32x4*>(sK + row * LDR + col) = kv;
+      const T* ek = reinterpret_cast<const T*>(&kv);
+      const T* ev = reinterpret_cast<const T*>(&vv);
+#pragma unroll
+      for (int u = 0; u < EPC; ++u) {
+        sKt[tix<T, LDT>(col + u, row)] = ek[u];
+        sVt[tix<T, LDT>(col + u, row)] = ev[u];
+      }
     }
     if (j + 1 < j1) load_block(j + 1);     // in flight while this block is reduced
     __syncthreads();
 
-    // Column statistics: threads [0, D) own key columns, [128, 128 + D) value columns.
+    // Column statistics: threads [0, D) own key columns, [128, 128 + D) value columns; each
+    // reads its column as 64 / EPC chunks of the transposed tile.
     if (tid < D) {
       float s = 0.f;
-      for (int r = 0; r < kB; ++r) s += to_f32(sK[r * LDR + tid]);
+      for (int q = 0; q < kB / EPC; ++q) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sKt + tix<T, LDT>(tid, q * EPC));
+        const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+        for (int u = 0; u < EPC; ++u) s += to_f32(e[u]);
+      }
       const float mean = s * invn;
       float ss = 0.f;
-      for (int r = 0; r < n; ++r) {
-        const float dv = to_f32(sK[r * LDR + tid]) - mean;
-        ss += dv * dv;
+      for (int q = 0; q < kB / EPC; ++q) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sKt + tix<T, LDT>(tid, q * EPC));
+        const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+        for (int u = 0; u < EPC; ++u) {
+          const float dv = to_f32(e[u]) - mean;
+          ss += q * EPC + u < n ? dv * dv : 0.f;
+        }
       }
       const size_t o = (size_t(h) * a.nb + j) * D + tid;
       a.kbar[o] = mean;
@@ -102,7 +126,13 @@ __global__ __launch_bounds__(256) void block_stats_kernel(StatsArgs a, unsigned 
     } else if (tid >= 128 && tid < 128 + D) {
       const int c = tid - 128;
       float s = 0.f;
-      for (int r = 0; r < kB; ++r) s += to_f32(sV[r * LDR + c]);
+#pragma unroll
+      for (int q = 0; q < kB / EPC; ++q) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sVt + tix<T, LDT>(c, q * EPC));
+        const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+        for (int u = 0; u < EPC; ++u) s += to_f32(e[u]);
+      }
       a.vsum[(size_t(h) * a.nb + j) * D + c] = s;
       sVsum[c] = s;
       vbp[size_t(j / kB) * TE + TL::v(j % kB, c)] = from_f32<T>(s * invn);
@@ -113,10 +143,8 @@ __global__ __launch_bounds__(256) void block_stats_kernel(StatsArgs a, unsigned 
     for (int x = tid; x < TE / EPC; x += 256) {
       int i0 = 0, e = 0;
       TL::vchunk(x, i0, e);
-      __align__(16) T tmp[EPC];
-#pragma unroll
-      for (int u = 0; u < EPC; ++u) tmp[u] = sV[(i0 + u) * LDR + e];
-      *reinterpret_cast<u32x4*>(vt + size_t(j) * TE + x * EPC) = *reinterpret_cast<u32x4*>(tmp);
+      *reinterpret_cast<u32x4*>(vt + size_t(j) * TE + x * EPC) =
+          *reinterpret_cast<const u32x4*>(sVt + tix<T, LDT>(e, i0));
       if constexpr (sizeof(T) == 2) {
         int key = 0, c0 = 0;
         TL::kchunk(x, key, c0);
@@ -134,18 +162,13 @@ __global__ __launch_bounds__(256) void block_stats_kernel(StatsArgs a, unsigned 
     for (int u = 0; u < (PER_BLOCK ? TPW : 1); ++u) blk[u] = zero16();
 #pragma unroll
     for (int ks = 0; ks < kB / KI; ++ks) {
-      float av[KH];
-#pragma unroll
-      for (int u = 0; u < KH; ++u) av[u] = to_f32(sK[(KI * ks + KH * g + u) * LDR + 32 * ct + l32]);
-      const typename M::AB A = M::pack(av);
+      const typename M::AB A = M::load(sKt + tix<T, LDT>(32 * ct + l32, KI * ks + KH * g));
 #pragma unroll
       for (int u = 0; u < TPW; ++u) {
         const int et = (wave * TPW + u) % NT;
-        float bv[KH];
-#pragma unroll
-        for (int q = 0; q < KH; ++q) bv[q] = to_f32(sV[(KI * ks + KH * g + q) * LDR + 32 * et + l32]);
-        if constexpr (PER_BLOCK) blk[u] = M::mma(A, M::pack(bv), blk[u]);
-        else run[u] = M::mma(A, M::pack(bv), run[u]);
+        const typename M::AB Bv = M::load(sVt + tix<T, LDT>(32 * et + l32, KI * ks + KH * g));
+        if constexpr (PER_BLOCK) blk[u] = M::mma(A, Bv, blk[u]);
+        else run[u] = M::mma(A, Bv, run[u]);
       }
     }
 #pragma unroll
@@ -173,17 +196,11 @@ __global__ __launch_bounds__(256) void block_stats_kernel(StatsArgs a, unsigned 
         for (int u = 0; u < TPW; ++u) cb[u] = zero16();
 #pragma unroll
         for (int ks = 0; ks < kB / KI; ++ks) {
-          float av[KH];
-#pragma unroll
-          for (int u = 0; u < KH; ++u) av[u] = to_f32(sK[(KI * ks + KH * g + u) * LDR + 32 * ct + l32]);
-          const typename M::AB A = M::pack(av);
+          const typename M::AB A = M::load(sKt + tix<T, LDT>(32 * ct + l32, KI * ks + KH * g));
 #pragma unroll
           for (int u = 0; u < TPW; ++u) {
             const int et = (wave * TPW + u) % NT;
-            float bv[KH];
-#pragma unroll
-            for (int q = 0; q < KH; ++q) bv[q] = to_f32(sK[(KI * ks + KH * g + q) * LDR + 32 * et + l32]);
-            cb[u] = M::mma(A, M::pack(bv), cb[u]);
+            cb[u] = M::mma(A, M::load(sKt + tix<T, LDT>(32 * et + l32, KI * ks + KH * g)), cb[u]);
           }
         }
 #pragma unroll

@@ -159,6 +159,16 @@ template <int D> struct TileLayout<uint16_t, D> {
   }
 };
 
+// Element (row e, column c) of a transposed [rows][64] LDS tile with row stride LDT: the
+// 16-byte chunks of a row are XOR-swizzled by the row's chunk index, so the column-wise
+// stores of a transpose spread over the LDS banks; a chunk stays contiguous for 16-byte
+// operand reads.
+template <class T, int LDT>
+__device__ __forceinline__ int tix(int e, int c) {
+  constexpr int EPC = 16 / sizeof(T), NCH = 64 / EPC;
+  return e * LDT + ((((c / EPC) ^ ((e / EPC) % NCH)) * EPC) + c % EPC);
+}
+
 // Row index -> accumulator row of the 32x32 output:  row(r, g) = 8*(r/4) + 4*g + r%4.
 __device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 

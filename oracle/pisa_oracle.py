@@ -414,11 +414,11 @@ def attention_head_backward(Q, K, V, dO, B: int, block_len=None, K_sel: int = 0,
         dk_k, dv_k (exact keys) = Σ_t dx_{t,k} q_t, Σ_t P_{t,k} dO_t
         dk̄_j = Σ_t dℓ_{t,j} q_t,  dv̄_j = Σ_t P_{t,j} dO_t,  dH̄ = Σ_t Ā_t dO_t q_tᵀ
         dw̃_{i,j} = φ'(w̃_{i,j}) Σ_{t in tile i} dℓ_{t,j}   (0 where the gate fired)
-        d\overline{q²}_i = ½ Σ_j dw̃_{i,j} σ²_j,  dσ²_j = ½ Σ_i dw̃_{i,j} \overline{q²}_i
+        d\\overline{q²}_i = ½ Σ_j dw̃_{i,j} σ²_j,  dσ²_j = ½ Σ_i dw̃_{i,j} \\overline{q²}_i
     and the statistics pass their gradients to the tokens of block j (valid tokens only):
         dk_i += dk̄_j / n_j + (2/n_j)(k_i - k̄_j)∘dσ²_j + (1/nb) dH̄ᵀ (v_i - v̄_j)
         dv_i += dv̄_j / n_j + (1/nb) dH̄ (k_i - k̄_j)
-        dq_t += (2/m_i) q_t ∘ d\overline{q²}_i                (m_i valid rows of tile i)
+        dq_t += (2/m_i) q_t ∘ d\\overline{q²}_i                (m_i valid rows of tile i)
     Returns dict(dQ, dK, dV) [L_pad, d] (zeros on padded slots), O, lse, idx."""
     opts = dict(PRESETS[mode])
     opts.update(overrides)
