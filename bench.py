@@ -136,6 +136,11 @@ def cpu_baseline(inp, mode: str, heads: int) -> dict:
                       f"(per-head statistics and selection included): {dt:.1f} s", **host}
 
 
+def progress(what: str):
+    """One line per finished leg on stderr (the JSON record alone goes to stdout)."""
+    print(f"[bench] {what}", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,6 +239,7 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
+    progress("inputs on the device")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -268,9 +274,11 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
+    progress("timed steps done")
     ms_exact = timed(lambda: pisa.attention_fwd(Q, K, V, st, idx, mask, None, K_sel, "drop", blt, out=O))
     exact_tflops = fc["exact"] / (ms_exact * 1e-3) / 1e12
 
+    progress("exact branch done")
     # covariance-aware routing, the optional selection rule: its prepare-phase cost (second
     # statistics pass for M_j + routed scores) and how many tiles change their selection
     routing = None
@@ -295,6 +303,7 @@ def main():
         rules["error"] = (idx_r.clone(), mask_r.clone())
         del st_r, idx_r, mask_r, wt_r
 
+    progress("routing leg done")
     # RoPE-aware centroids on rotary workloads: selection cost and how many tiles change
     rope_leg = None
     if cfg.rope and not rope_select:
@@ -308,6 +317,7 @@ def main():
         rules["rope"] = (idx_p.clone(), mask_p.clone())
         del idx_p, mask_p, wt_p
 
+    progress("rope leg done")
     # cold cache: a 512 MiB fill between runs evicts L2 and the Infinity Cache
     flush = torch.empty(512 * 2**20, dtype=torch.uint8, device="cuda")
     cold_step, cold_attn = [], []
@@ -320,6 +330,7 @@ def main():
         cold_attn.append(ev[2].elapsed_time(ev[3]))
     del flush
 
+    progress("cold-cache runs done")
     # step a0, not part of the three calls: natural (t, h, w) order -> padded cube order
     perm = torch.from_numpy(inp.layout.perm.astype(np.int64)).cuda()
     nat = torch.zeros(H, inp.layout.L, d, dtype=Q.dtype, device="cuda")
@@ -329,6 +340,7 @@ def main():
     ms_perm = timed(lambda: torch.index_select(nat, 1, src, out=cube).masked_fill_(pad, 0))
     del nat, cube
 
+    progress("permutation done")
     # backward of the timed mode (DROP / PISA / PWT) on the same selection: dQ, dK, dV from dO
     backward = None
     if mode in ("drop", "pisa", "pwt"):
@@ -346,6 +358,7 @@ def main():
                     "ratio_to_forward_attention": round(ms_bwd / ms_attn, 2)}
         del gbuf, ws_bwd, dO
 
+    progress("backward done")
     # PWT with the per-row diagonal w (the pooling ablation), on the same selection
     pwt_row = None
     if mode != "pwt_row":
@@ -354,6 +367,7 @@ def main():
         pwt_row = {"ms_attention": round(ms_row, 4), "attention_flops": fr["attention"],
                    "tflops": round(fr["attention"] / (ms_row * 1e-3) / 1e12, 2)}
 
+    progress("per-row w done")
     # LITERAL, reported but not held to the dense target
     literal = None
     if mode != "literal":
@@ -362,6 +376,7 @@ def main():
         literal = {"ms_attention": round(ms_lit, 4), "attention_flops": fl["attention"],
                    "tflops": round(fl["attention"] / (ms_lit * 1e-3) / 1e12, 2)}
 
+    progress("LITERAL done")
     dense = {}
     if not args.no_dense:
         idx_all = torch.arange(nb, dtype=torch.int32, device="cuda").expand(H, nb, nb).contiguous()
@@ -394,6 +409,7 @@ def main():
                      dense_best_ms=round(best, 4), speedup_vs_dense=round(best / ms_step, 3))
 
     cpu = None
+    progress("dense and selection recall done")
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, mode, args.cpu_heads)
 
