@@ -76,6 +76,49 @@ def block_ranges(L_pad: int, B: int, block_len=None):
     return [(j * B, int(bl[j])) for j in range(nb)]
 
 
+# ----------------------------------------------------------------------------- layout
+def cube_order(grid, cube=(4, 4, 4)):
+    """Block order of a (T, H, W) latent grid cut into cubes (blog, notation: tokens are cut
+    into blocks of B; video tokens are grouped into 3D cubes): cubes in row-major order over
+    (cube t, cube h, cube w), tokens inside a cube row-major over (dt, dh, dw); a cube cut by
+    the grid's edge keeps its valid tokens first and pads to B slots. Returns (perm, n) with
+    perm[s] = natural row-major index of the token in slot s (-1 for padding) and n[j] the
+    valid tokens of block j."""
+    T, Hh, W = grid
+    ct, ch, cw = cube
+    B = ct * ch * cw
+    perm, n = [], []
+    for a in range((T + ct - 1) // ct):
+        for b in range((Hh + ch - 1) // ch):
+            for c in range((W + cw - 1) // cw):
+                toks = [(t * Hh + h) * W + w
+                        for t in range(a * ct, min(T, a * ct + ct))
+                        for h in range(b * ch, min(Hh, b * ch + ch))
+                        for w in range(c * cw, min(W, c * cw + cw))]
+                n.append(len(toks))
+                perm.extend(toks + [-1] * (B - len(toks)))
+    return np.array(perm, dtype=np.int64), np.array(n, dtype=np.int64)
+
+
+def to_blocks(x: np.ndarray, perm: np.ndarray) -> np.ndarray:
+    """Natural order [..., L, d] -> block order [..., L_pad, d]: slot s holds token perm[s],
+    padding slots hold 0."""
+    perm = np.asarray(perm)
+    out = np.zeros(x.shape[:-2] + (perm.size, x.shape[-1]), dtype=x.dtype)
+    ok = perm >= 0
+    out[..., ok, :] = x[..., perm[ok], :]
+    return out
+
+
+def from_blocks(x: np.ndarray, perm: np.ndarray, L: int) -> np.ndarray:
+    """Block order [..., L_pad, d] -> natural order [..., L, d] (padding slots dropped)."""
+    perm = np.asarray(perm)
+    out = np.zeros(x.shape[:-2] + (L, x.shape[-1]), dtype=x.dtype)
+    ok = perm >= 0
+    out[..., perm[ok], :] = x[..., ok, :]
+    return out
+
+
 # ----------------------------------------------------------------------------- statistics
 def block_stats(K: np.ndarray, V: np.ndarray, B: int, block_len=None, per_block: bool = True) -> dict:
     """Per-block statistics of one head.

@@ -741,3 +741,26 @@ def test_backward_with_every_block_selected_is_dense_attention_gradient():
         for a, t in ((g["dQ"], q), (g["dK"], k), (g["dV"], v)):
             assert np.allclose(a[ok], t.grad.numpy(), rtol=1e-10, atol=1e-12)
             assert np.all(a[~ok] == 0.0)
+
+
+@pytest.mark.parametrize("grid", [(5, 6, 7), (8, 8, 8), (1, 3, 9), (21, 30, 52)])
+def test_cube_order_is_a_padded_bijection(grid):
+    """Every token appears in exactly one slot, each block holds the tokens of one 4x4x4 cube
+    (coordinates within one cube's box), valid tokens come first, and block lengths count
+    them; to_blocks / from_blocks round-trip."""
+    perm, n = orc.cube_order(grid)
+    T, Hh, W = grid
+    L = T * Hh * W
+    assert perm.size == n.size * 64 and n.sum() == L
+    assert np.array_equal(np.sort(perm[perm >= 0]), np.arange(L))
+    for j in range(n.size):
+        blk = perm[j * 64:(j + 1) * 64]
+        assert np.all(blk[:n[j]] >= 0) and np.all(blk[n[j]:] == -1)
+        t, r = np.divmod(blk[:n[j]], Hh * W)
+        h, w = np.divmod(r, W)
+        for c in (t, h, w):
+            assert c.max() // 4 == c.min() // 4
+    x = np.random.default_rng(31).standard_normal((2, L, 3))
+    y = orc.to_blocks(x, perm)
+    assert np.all(y[:, perm < 0] == 0)
+    assert np.array_equal(orc.from_blocks(y, perm, L), x)
