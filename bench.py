@@ -332,12 +332,10 @@ def main():
 
     progress("cold-cache runs done")
     # step a0, not part of the three calls: natural (t, h, w) order -> padded cube order
-    perm = torch.from_numpy(inp.layout.perm.astype(np.int64)).cuda()
+    perm = torch.from_numpy(inp.layout.perm.astype(np.int32)).cuda()
     nat = torch.zeros(H, inp.layout.L, d, dtype=Q.dtype, device="cuda")
     cube = torch.empty_like(Q)
-    src = perm.clamp(min=0)
-    pad = (perm < 0).view(1, -1, 1)
-    ms_perm = timed(lambda: torch.index_select(nat, 1, src, out=cube).masked_fill_(pad, 0))
+    ms_perm = timed(lambda: pisa.layout_to_blocks(nat, perm, out=cube))
     del nat, cube
 
     progress("permutation done")

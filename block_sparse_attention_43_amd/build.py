@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpisa.so")
 SOURCES = ["abi.hip", "block_stats.hip", "select_topk.hip", "attention_fwd.hip", "attention_frag.hip",
-           "attention_bwd.hip"]
+           "attention_bwd.hip", "layout.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU forms are disabled for all device code (hipcc emits them from plain
 # float code otherwise); the host pass warns that it does not know the feature.

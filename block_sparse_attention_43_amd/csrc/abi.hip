@@ -386,6 +386,64 @@ pisa_status pisa_attention_bwd(pisa_dtype dt, const void* Q, const void* K, cons
   return ok();
 }
 
+pisa_status pisa_cube_layout(int T, int Hh, int W, int ct, int ch, int cw, int32_t* perm,
+                             int32_t* block_len, size_t capacity, int* nb_out) {
+  if (T < 1 || Hh < 1 || W < 1 || ct < 1 || ch < 1 || cw < 1)
+    return fail(PISA_ERR_INVALID_ARG, "grid and cube sizes must be >= 1");
+  if (ct * ch * cw != pisa::kB) return fail(PISA_ERR_UNSUPPORTED, "cube must hold B = 64 tokens (got %d)", ct * ch * cw);
+  if (!perm || !block_len || !nb_out) return fail(PISA_ERR_INVALID_ARG, "perm, block_len and nb_out must not be NULL");
+  const long long nt = (T + ct - 1) / ct, nh = (Hh + ch - 1) / ch, nw = (W + cw - 1) / cw;
+  const long long nb = nt * nh * nw;
+  if (static_cast<long long>(T) * Hh * W >= (1LL << 31) || nb > 32768)
+    return fail(PISA_ERR_UNSUPPORTED, "grid too large (%lld blocks)", nb);
+  if (static_cast<size_t>(nb) * pisa::kB > capacity)
+    return fail(PISA_ERR_INVALID_ARG, "perm needs %lld entries (capacity %zu)", nb * pisa::kB, capacity);
+  long long j = 0;
+  for (long long a = 0; a < nt; ++a)
+    for (long long b = 0; b < nh; ++b)
+      for (long long c = 0; c < nw; ++c, ++j) {
+        int n = 0;
+        int32_t* slot = perm + j * pisa::kB;
+        for (int dt = 0; dt < ct; ++dt)
+          for (int dh = 0; dh < ch; ++dh)
+            for (int dw = 0; dw < cw; ++dw) {
+              const long long t = a * ct + dt, h = b * ch + dh, w = c * cw + dw;
+              if (t < T && h < Hh && w < W) slot[n++] = static_cast<int32_t>((t * Hh + h) * W + w);
+            }
+        block_len[j] = n;
+        for (int k = n; k < pisa::kB; ++k) slot[k] = -1;
+      }
+  *nb_out = static_cast<int>(nb);
+  return ok();
+}
+
+static pisa_status layout_call(bool to_blocks, pisa_dtype dt, const void* src, int H, int L_nat, int L_pad,
+                               int d, const int32_t* perm, void* dst, void* stream) {
+  PISA_TRY(check_dtype(dt));
+  if (H < 1 || L_nat < 1 || L_pad < 1 || d < 1) return fail(PISA_ERR_INVALID_ARG, "H, L_nat, L_pad and d must be >= 1");
+  const int row_bytes = d * static_cast<int>(elem_size(dt));
+  if (row_bytes % 16) return fail(PISA_ERR_UNSUPPORTED, "a row must be a multiple of 16 bytes (d = %d)", d);
+  if (static_cast<long long>(H) * L_pad >= (1LL << 31) || static_cast<long long>(L_pad) * (row_bytes / 16) >= (1LL << 40))
+    return fail(PISA_ERR_UNSUPPORTED, "sizes too large");
+  PISA_TRY(check_ptr(src, "src"));
+  PISA_TRY(check_ptr(dst, "dst"));
+  PISA_TRY(check_ptr(perm, "perm", false));
+  hipError_t e = pisa::launch_layout(to_blocks, src, dst, perm, H, L_nat, L_pad, row_bytes,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "layout launch");
+  return ok();
+}
+
+pisa_status pisa_layout_to_blocks(pisa_dtype dt, const void* src, int H, int L_nat, int L_pad, int d,
+                                  const int32_t* perm, void* dst, void* stream) {
+  return layout_call(true, dt, src, H, L_nat, L_pad, d, perm, dst, stream);
+}
+
+pisa_status pisa_layout_from_blocks(pisa_dtype dt, const void* src, int H, int L_nat, int L_pad,
+                                    int d, const int32_t* perm, void* dst, void* stream) {
+  return layout_call(false, dt, src, H, L_nat, L_pad, d, perm, dst, stream);
+}
+
 const char* pisa_last_error(void) { return g_err.c_str(); }
 
 const char* pisa_version(void) { return "pisa-mi355x 0.1.0 (gfx950)"; }

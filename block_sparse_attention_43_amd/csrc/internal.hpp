@@ -169,6 +169,8 @@ inline BwdLayout bwd_layout(int H, int L, int d, int K_sel) {
 }
 
 hipError_t launch_block_stats(int bf16, const StatsArgs& a, unsigned flags, hipStream_t s);
+hipError_t launch_layout(bool to_blocks, const void* src, void* dst, const int32_t* perm, int H, int L_nat,
+                         int L_pad, int row_bytes, hipStream_t s);
 hipError_t launch_attention_bwd(int bf16, int mode, const BwdArgs& a, hipStream_t s);
 hipError_t launch_select(int bf16, const SelectArgs& a, hipStream_t s);
 hipError_t launch_attention(int bf16, int mode, const AttnArgs& a, hipStream_t s);

@@ -31,6 +31,7 @@ EXPORTS = ("pisa_packed_bytes", "pisa_block_stats_workspace_bytes", "pisa_block_
            "pisa_select_workspace_bytes", "pisa_select_topk", "pisa_select_topk_routed",
            "pisa_select_topk_rope",
            "pisa_attention_fwd", "pisa_attention_bwd_workspace_bytes", "pisa_attention_bwd",
+           "pisa_cube_layout", "pisa_layout_to_blocks", "pisa_layout_from_blocks",
            "pisa_last_error", "pisa_version")
 
 
@@ -91,6 +92,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pisa_attention_bwd.argtypes = [i32, vp, vp, vp, sp, vp, vp, vp, i32, i32, i32, i32, vp, i32, u32,
                                        vp, vp, vp, vp, vp, vp, sz, vp]
     lib.pisa_attention_bwd.restype = i32
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lib.pisa_cube_layout.argtypes = [i32, i32, i32, i32, i32, i32, ip, ip, sz, ctypes.POINTER(ctypes.c_int)]
+    lib.pisa_cube_layout.restype = i32
+    for fn in (lib.pisa_layout_to_blocks, lib.pisa_layout_from_blocks):
+        fn.argtypes = [i32, vp, i32, i32, i32, i32, vp, vp, vp]
+        fn.restype = i32
     lib.pisa_last_error.argtypes = []
     lib.pisa_last_error.restype = ctypes.c_char_p
     lib.pisa_version.argtypes = []
@@ -270,6 +277,48 @@ def attention_bwd(Q, K, V, st: Stats, idx, mask, wt, K_sel: int, lse, dO, mode="
                                   _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(workspace), workspace.numel(),
                                   _stream(stream)))
     return dQ, dK, dV
+
+
+def cube_layout(grid, cube=(4, 4, 4)):
+    """Host-side block order of a (T, H, W) grid cut into cubes: (perm int32 [nb*64], -1 for
+    padding slots; block_len int32 [nb]) as numpy arrays."""
+    import numpy as np
+    lib = load()
+    T, Hh, W = grid
+    nb = -(-T // cube[0]) * -(-Hh // cube[1]) * -(-W // cube[2])
+    perm = np.empty(nb * B, dtype=np.int32)
+    bl = np.empty(nb, dtype=np.int32)
+    out = ctypes.c_int(0)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    _check(lib.pisa_cube_layout(T, Hh, W, *cube, perm.ctypes.data_as(ip), bl.ctypes.data_as(ip), perm.size,
+                                ctypes.byref(out)))
+    return perm, bl
+
+
+def layout_to_blocks(x, perm, L_pad: int | None = None, out=None, stream=None):
+    """[H, L_nat, d] natural order -> [H, L_pad, d] block order (perm: device int32 [L_pad])."""
+    lib = load()
+    if x.dim() != 3 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [H, L, d] tensor")
+    H, Ln, d = x.shape
+    Lp = perm.numel() if L_pad is None else L_pad
+    if out is None:
+        out = torch.empty(H, Lp, d, dtype=x.dtype, device=x.device)
+    _check(lib.pisa_layout_to_blocks(_dtype_code(x), _ptr(x), H, Ln, Lp, d, _ptr(perm), _ptr(out), _stream(stream)))
+    return out
+
+
+def layout_from_blocks(x, perm, L_nat: int, out=None, stream=None):
+    """[H, L_pad, d] block order -> [H, L_nat, d] natural order (padding slots dropped)."""
+    lib = load()
+    if x.dim() != 3 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [H, L, d] tensor")
+    H, Lp, d = x.shape
+    if out is None:
+        out = torch.empty(H, L_nat, d, dtype=x.dtype, device=x.device)
+    _check(lib.pisa_layout_from_blocks(_dtype_code(x), _ptr(x), H, L_nat, Lp, d, _ptr(perm), _ptr(out),
+                                       _stream(stream)))
+    return out
 
 
 def forward(Q, K, V, K_sel: int, mode="pwt", block_len=None, flags: int = 0, stream=None, route="mean"):

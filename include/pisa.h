@@ -286,6 +286,34 @@ pisa_status pisa_attention_bwd(pisa_dtype dt, const void* Q, const void* K, cons
                                const void* dO, float* dQ, float* dK, float* dV, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/*
+ * Layout step (blog "Sparse Linear Attention", notation: tokens are cut into blocks of B;
+ * video latents are grouped into 3D cubes). Block order is the layout every other call
+ * takes.
+ *
+ * pisa_cube_layout (host only, no GPU work): the block order of a T x Hh x W latent grid
+ * (natural order row-major over (t, h, w)) cut into ct x ch x cw cubes of B = ct*ch*cw
+ * tokens: cubes row-major over their (t, h, w) indices, tokens inside a cube row-major,
+ * a cube cut by the grid's edge keeps its valid tokens first and is padded to B slots.
+ *   perm       HOST int32 [nb * B] out: natural index of the token in each slot, -1 = padding
+ *   block_len  HOST int32 [nb] out: valid tokens per block (n_j)
+ *   capacity   entries of perm available; nb * B must fit (nb = product of ceil(grid/cube))
+ * Returns PISA_OK and writes *nb_out, or an error (sizes, capacity).
+ *
+ * pisa_layout_to_blocks: dst[h][s] = perm[s] >= 0 ? src[h][perm[s]] : 0
+ *   src [H][L_nat][d], dst [H][L_pad][d] dtype `dt`; perm DEVICE int32 [L_pad].
+ * pisa_layout_from_blocks: dst[h][perm[s]] = src[h][s] for the slots with perm[s] >= 0
+ *   src [H][L_pad][d], dst [H][L_nat][d]; perm must map the valid slots one-to-one onto
+ *   [0, L_nat) (pisa_cube_layout's does); entries outside [0, L_nat) are skipped.
+ * Both are stream-ordered copies (HBM-bound); src and dst must not overlap.
+ */
+pisa_status pisa_cube_layout(int T, int Hh, int W, int ct, int ch, int cw, int32_t* perm,
+                             int32_t* block_len, size_t capacity, int* nb_out);
+pisa_status pisa_layout_to_blocks(pisa_dtype dt, const void* src, int H, int L_nat, int L_pad, int d,
+                                  const int32_t* perm, void* dst, void* stream);
+pisa_status pisa_layout_from_blocks(pisa_dtype dt, const void* src, int H, int L_nat, int L_pad,
+                                    int d, const int32_t* perm, void* dst, void* stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* pisa_last_error(void);
 
