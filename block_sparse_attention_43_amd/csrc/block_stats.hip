@@ -269,10 +269,10 @@ template <class T, int D>
 __global__ __launch_bounds__(256) void heterogeneity_kernel(StatsArgs a) {
   using M = typename MmaFor<T>::type;
   constexpr int KI = M::KI, KH = M::KH;
-  constexpr int EPC = 16 / sizeof(T), LDR = D + EPC, CPR = D / EPC, CPT = kB * CPR / 256;
+  constexpr int EPC = 16 / sizeof(T), LDT = kB + EPC, CPR = D / EPC, CPT = kB * CPR / 256;
   constexpr int NT = D / 32, TPW = NT * NT / 4;
-  __shared__ __align__(16) T sK[kB * LDR];
-  __shared__ __align__(16) T sV[kB * LDR];
+  __shared__ __align__(16) T sKt[D * LDT];      // K_jᵀ, V_jᵀ, XOR-swizzled (see tix)
+  __shared__ __align__(16) T sVt[D * LDT];
   __shared__ float sKbar[D], sVsum[D], sPart[4];
 
   const int h = blockIdx.y, j0 = blockIdx.x * a.G, j1 = min(a.nb, j0 + a.G);
@@ -308,8 +308,14 @@ __global__ __launch_bounds__(256) void heterogeneity_kernel(StatsArgs a) {
     for (int p = 0; p < CPT; ++p) {
       const int c = tid + 256 * p, row = c / CPR, col = (c % CPR) * EPC;
       const u32x4 z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(sK + row * LDR + col) = row < n ? rk[p] : z;
-      *reinterpret_cast<u32x4*>(sV + row * LDR + col) = row < n ? rv[p] : z;
+      const u32x4 kv = row < n ? rk[p] : z, vv = row < n ? rv[p] : z;
+      const T* ek = reinterpret_cast<const T*>(&kv);
+      const T* ev = reinterpret_cast<const T*>(&vv);
+#pragma unroll
+      for (int u = 0; u < EPC; ++u) {
+        sKt[tix<T, LDT>(col + u, row)] = ek[u];
+        sVt[tix<T, LDT>(col + u, row)] = ev[u];
+      }
     }
     const size_t o = (size_t(h) * a.nb + j) * D;
     if (tid < D) sKbar[tid] = a.kbar[o + tid];
@@ -322,17 +328,11 @@ __global__ __launch_bounds__(256) void heterogeneity_kernel(StatsArgs a) {
     for (int u = 0; u < TPW; ++u) blk[u] = zero16();
 #pragma unroll
     for (int ks = 0; ks < kB / KI; ++ks) {
-      float av[KH];
-#pragma unroll
-      for (int u = 0; u < KH; ++u) av[u] = to_f32(sK[(KI * ks + KH * g + u) * LDR + 32 * ct + l32]);
-      const typename M::AB A = M::pack(av);
+      const typename M::AB A = M::load(sKt + tix<T, LDT>(32 * ct + l32, KI * ks + KH * g));
 #pragma unroll
       for (int u = 0; u < TPW; ++u) {
         const int et = (wave * TPW + u) % NT;
-        float bv[KH];
-#pragma unroll
-        for (int q = 0; q < KH; ++q) bv[q] = to_f32(sV[(KI * ks + KH * g + q) * LDR + 32 * et + l32]);
-        blk[u] = M::mma(A, M::pack(bv), blk[u]);
+        blk[u] = M::mma(A, M::load(sVt + tix<T, LDT>(32 * et + l32, KI * ks + KH * g)), blk[u]);
       }
     }
     float ss = 0.f;
