@@ -47,24 +47,9 @@ __device__ __forceinline__ u32x4 zero_chunk() {
   return u32x4{0u, 0u, 0u, 0u};
 }
 
-// 64 rows of a row-major [*, D] T matrix into LDS rows (stride LDK) and, if TRANS, into the
-// transposed tile (stride LDT); rows at or past `valid` are written as zeros.
-template <class T, int D, int LDK, int LDT, bool TRANS>
-__device__ __forceinline__ void stage_rows(const T* src, int valid, T* sX, T* sXt, int tid) {
-  constexpr int EPC = 16 / sizeof(T), CPR = D / EPC;
-  for (int c = tid; c < 64 * CPR; c += 256) {
-    const int r = c / CPR, col = (c % CPR) * EPC;
-    const u32x4 v = r < valid ? *reinterpret_cast<const u32x4*>(src + size_t(r) * D + col) : zero_chunk<T>();
-    *reinterpret_cast<u32x4*>(sX + r * LDK + col) = v;
-    if constexpr (TRANS) {
-      const T* e = reinterpret_cast<const T*>(&v);
-#pragma unroll
-      for (int u = 0; u < EPC; ++u) sXt[tix<T, LDT>(col + u, r)] = e[u];
-    }
-  }
-}
-
-// 64 rows of an fp32 [*, D] matrix (scaled per row) rounded to T, same layout as above.
+// 64 rows of an fp32 [*, D] matrix (scaled per row) rounded to T, into LDS rows (stride LDK)
+// and, if TRANS, into the transposed tile (stride LDT, swizzled); rows at or past `valid`
+// are written as zeros.
 template <class T, int D, int LDK, int LDT, bool TRANS, class Scale>
 __device__ __forceinline__ void stage_rows_f32(const float* src, int valid, Scale scale, T* sX, T* sXt, int tid) {
   constexpr int CPR = D / 4;
