@@ -260,6 +260,19 @@ def main():
     value = fc["total"] / (ms_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[cfg.dtype]
     attn_tflops = fc["attention"] / (ms_attn * 1e-3) / 1e12
+    # the two prepare calls are HBM-bound: bytes they move by design per call
+    es = 2 if cfg.dtype == "bf16" else 4
+    nbp = (nb + 63) // 64 * 64
+    stats_bytes = (2 * H * L * d * es                        # read K, V
+                   + (2 if es == 2 else 1) * H * L * d * es  # write Vᵀ (+ operand-order K for bf16)
+                   + 3 * H * nb * d * 4 + 2 * H * nbp * d * es + H * d * d * (4 + es))
+    sel_bytes = (H * L * d * es + 2 * H * nb * d * 4 * 2     # read Q; write q̄, mean(q²), read them back
+                 + 2 * H * nb * d * 4                        # read k̄, σ²
+                 + H * nb * nb * 4 * (3 if wt is not None else 2)  # scores (write + read), w̃
+                 + H * nb * (K_sel + (nb + 31) // 32) * 4)   # idx, mask
+    prepare = {k: {"bytes": int(b), "gbs": round(b / (ms * 1e-3) / 1e9, 1),
+                   "frac_of_hbm": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+               for k, b, ms in (("pisa_block_stats", stats_bytes, ms_stats), ("pisa_select_topk", sel_bytes, ms_sel))}
     traffic = load_traffic(args.config)
 
     # exact branch alone: DROP on the same selection (phase 1 only)
@@ -433,6 +446,7 @@ def main():
         "ms_select": round(ms_sel, 4),
         "ms_attention": round(ms_attn, 4),
         "frac_of_peak_total": round(value / peak, 4),
+        "prepare_hbm": prepare,
         "exact_branch": {"ms": round(ms_exact, 4), "tflops": round(exact_tflops, 2),
                          "frac": round(exact_tflops / peak, 4)},
         "cold_cache": {"ms_per_step": round(float(np.median(cold_step)), 4),
