@@ -357,7 +357,8 @@ def main():
     if mode in ("drop", "pisa", "pwt"):
         dO = torch.randn(Q.shape, dtype=torch.float32, device="cuda", generator=torch.Generator(device="cuda").manual_seed(7)).to(Q.dtype)
         gbuf = tuple(torch.empty(H, L, d, dtype=torch.float32, device="cuda") for _ in range(3))
-        ws_bwd = torch.empty(max(pisa.load().pisa_attention_bwd_workspace_bytes(H, L, d, 64, K_sel), 16),
+        ws_bwd = torch.empty(max(pisa.load().pisa_attention_bwd_workspace_bytes(1 if cfg.dtype == "bf16" else 0, H, L, d,
+                                                                                64, K_sel), 16),
                              dtype=torch.uint8, device="cuda")
         pisa.attention_fwd(Q, K, V, st, idx, mask, wt, K_sel, mode, blt, out=O, lse=lse)
         ms_bwd = timed(lambda: pisa.attention_bwd(Q, K, V, st, idx, mask, wt, K_sel, lse, dO, mode, blt,

@@ -296,9 +296,9 @@ pisa_status pisa_attention_fwd(pisa_dtype dt, const void* Q, const void* K, cons
   return ok();
 }
 
-size_t pisa_attention_bwd_workspace_bytes(int H, int L, int d, int B, int K_sel) {
-  if (check_shape(H, L, d, B) != PISA_OK || K_sel < 0 || K_sel > L / B) return 0;
-  return pisa::bwd_layout(H, L, d, K_sel).total;
+size_t pisa_attention_bwd_workspace_bytes(pisa_dtype dt, int H, int L, int d, int B, int K_sel) {
+  if (check_dtype(dt) != PISA_OK || check_shape(H, L, d, B) != PISA_OK || K_sel < 0 || K_sel > L / B) return 0;
+  return pisa::bwd_layout(elem_size(dt), H, L, d, K_sel).total;
 }
 
 pisa_status pisa_attention_bwd(pisa_dtype dt, const void* Q, const void* K, const void* V,
@@ -335,7 +335,7 @@ pisa_status pisa_attention_bwd(pisa_dtype dt, const void* Q, const void* K, cons
   if ((mode & PISA_W_LINEAR) && (mode & PISA_W_EXP))
     return fail(PISA_ERR_INVALID_ARG, "PISA_W_LINEAR and PISA_W_EXP are exclusive");
   if (base == PISA_MODE_PWT) PISA_TRY(check_ptr(wt, "wt", false));
-  const pisa::BwdLayout w = pisa::bwd_layout(H, L, d, K_sel);
+  const pisa::BwdLayout w = pisa::bwd_layout(elem_size(dt), H, L, d, K_sel);
   if (!workspace || workspace_bytes < w.total)
     return fail(PISA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", w.total, workspace_bytes);
   if (!aligned16(workspace)) return fail(PISA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
@@ -370,6 +370,12 @@ pisa_status pisa_attention_bwd(pisa_dtype dt, const void* Q, const void* K, cons
   a.dh = reinterpret_cast<float*>(ws + w.dh);
   a.csr_off = reinterpret_cast<int*>(ws + w.off);
   a.csr_list = reinterpret_cast<int*>(ws + w.list);
+  a.kt = ws + w.kt;
+  a.kbr = ws + w.kbr;
+  a.kbt = ws + w.kbt;
+  a.vbr = ws + w.vbr;
+  a.vbias = reinterpret_cast<float*>(ws + w.vbias);
+  a.vinvn = reinterpret_cast<float*>(ws + w.vinvn);
   a.H = H;
   a.L = L;
   a.d = d;

@@ -47,28 +47,80 @@ __device__ __forceinline__ u32x4 zero_chunk() {
   return u32x4{0u, 0u, 0u, 0u};
 }
 
-// 64 rows of an fp32 [*, D] matrix (scaled per row) rounded to T, into LDS rows (stride LDK)
-// and, if TRANS, into the transposed tile (stride LDT, swizzled); rows at or past `valid`
-// are written as zeros.
-template <class T, int D, int LDK, int LDT, bool TRANS, class Scale>
-__device__ __forceinline__ void stage_rows_f32(const float* src, int valid, Scale scale, T* sX, T* sXt, int tid) {
-  constexpr int CPR = D / 4;
-  for (int c = tid; c < 64 * CPR; c += 256) {
-    const int r = c / CPR, col = (c % CPR) * 4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (r < valid) {
-      v = *reinterpret_cast<const float4*>(src + size_t(r) * D + col);
-      const float s = scale(r);
-      v.x *= s; v.y *= s; v.z *= s; v.w *= s;
-    }
-    const float f[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const T t = from_f32<T>(f[u]);
-      sX[r * LDK + col + u] = t;
-      if constexpr (TRANS) sXt[tix<T, LDT>(col + u, r)] = t;
-    }
-  }
+// Workgroup barrier that waits for this wave's LDS operations and for all but its newest VM
+// vector memory loads (direct loads of tiles issued later than the one about to be read).
+// __syncthreads would also drain those: its release fence covers the direct loads' LDS
+// writes. The "memory" clobber keeps the compiler from moving memory accesses across it.
+template <int VM>
+__device__ __forceinline__ void barrier_vm() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | 0x70);   // vmcnt(VM) expcnt(7) lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// LDS address (offset in the workgroup's LDS) of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char*)(p)));
+}
+
+// Reads of LDS that direct loads fill, written as inline asm whose block also waits for
+// them: the compiler does not track which LDS object a direct load writes and would make
+// any LDS read it sees wait for every direct load still in flight. Outputs are
+// early-clobber, so no destination shares a register with an address still to be used.
+template <int OFF>
+__device__ __forceinline__ void lds_read4x16(u32x4 (&o)[4], const uint32_t (&ad)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%8\n\t"
+      "ds_read_b128 %1, %5 offset:%8\n\t"
+      "ds_read_b128 %2, %6 offset:%8\n\t"
+      "ds_read_b128 %3, %7 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void lds_read8x16(u32x4 (&o)[8], const uint32_t (&ad)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%16\n\t"
+      "ds_read_b128 %1, %9 offset:%16\n\t"
+      "ds_read_b128 %2, %10 offset:%16\n\t"
+      "ds_read_b128 %3, %11 offset:%16\n\t"
+      "ds_read_b128 %4, %12 offset:%16\n\t"
+      "ds_read_b128 %5, %13 offset:%16\n\t"
+      "ds_read_b128 %6, %14 offset:%16\n\t"
+      "ds_read_b128 %7, %15 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]),
+        "i"(OFF));
+}
+template <int N, int OFF>
+__device__ __forceinline__ void lds_read_x16(u32x4 (&o)[N], const uint32_t (&ad)[N]) {
+  static_assert(N == 4 || N == 8, "read block size");
+  if constexpr (N == 4) lds_read4x16<OFF>(o, ad);
+  else lds_read8x16<OFF>(o, ad);
+}
+// Eight 16-byte reads at one address plus the offsets O0..O7.
+template <int O0, int O1, int O2, int O3, int O4, int O5, int O6, int O7>
+__device__ __forceinline__ void lds_read8_at(u32x4 (&o)[8], uint32_t ad) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%9\n\t"
+      "ds_read_b128 %1, %8 offset:%10\n\t"
+      "ds_read_b128 %2, %8 offset:%11\n\t"
+      "ds_read_b128 %3, %8 offset:%12\n\t"
+      "ds_read_b128 %4, %8 offset:%13\n\t"
+      "ds_read_b128 %5, %8 offset:%14\n\t"
+      "ds_read_b128 %6, %8 offset:%15\n\t"
+      "ds_read_b128 %7, %8 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(ad), "i"(O0), "i"(O1), "i"(O2), "i"(O3), "i"(O4), "i"(O5), "i"(O6), "i"(O7));
+}
+__device__ __forceinline__ uint32_t lds_read_u32(uint32_t ad) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(ad));
+  return v;
 }
 
 }  // namespace
@@ -127,6 +179,87 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Operand tiles of the dQ sweep that are not rows of the inputs, rounded to the input type
+// as the forward's centroid tiles are, zeros past the valid rows: z = 0, key block i: Kᵀ
+// [d][64]; z = 1, centroid group i: k̄ rows [64][d], k̄ᵀ [d][64] and v̄ = ΣV / n rows [64][d].
+// The sweep moves them, with K and V themselves, into LDS by direct loads.
+template <class T, int D>
+__global__ __launch_bounds__(256) void bwd_pack_kernel(BwdArgs a) {
+  constexpr int EPC = 16 / sizeof(T), LDT = kB + EPC, CPR = D / EPC, CPT = kB / EPC;
+  constexpr size_t TE = size_t(kB) * D;
+  __shared__ __align__(16) T sXt[D * LDT];
+  const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int nb = a.nb, ngrp = a.nbp / kB;
+  T* out;
+  if (blockIdx.z == 0) {
+    const int valid = min(max(a.block_len ? a.block_len[i] : kB, 1), kB);
+    const T* src = static_cast<const T*>(a.K) + (size_t(h) * a.L + size_t(i) * kB) * D;
+    for (int c = tid; c < kB * CPR; c += 256) {
+      const int r = c / CPR, col = (c % CPR) * EPC;
+      const u32x4 v = r < valid ? *reinterpret_cast<const u32x4*>(src + size_t(r) * D + col) : zero_chunk<T>();
+      const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+      for (int u = 0; u < EPC; ++u) sXt[tix<T, LDT>(col + u, r)] = e[u];
+    }
+    out = reinterpret_cast<T*>(a.kt) + (size_t(h) * nb + i) * TE;
+  } else {
+    if (i >= ngrp) return;
+    const int j0 = i * kB, valid = min(kB, nb - j0);
+    const size_t to = (size_t(h) * ngrp + i) * TE;
+    T* kr = reinterpret_cast<T*>(a.kbr) + to;
+    T* vr = reinterpret_cast<T*>(a.vbr) + to;
+    for (int x = tid; x < kB * D; x += 256) {
+      const int r = x / D, c = x % D;
+      float fk = 0.f, fv = 0.f;
+      if (r < valid) {
+        const size_t o = (size_t(h) * nb + j0 + r) * D + c;
+        fk = a.kbar[o];
+        fv = a.vsum[o] * (1.f / float(min(max(a.block_len ? a.block_len[j0 + r] : kB, 1), kB)));
+      }
+      const T tk = from_f32<T>(fk);
+      kr[x] = tk;
+      vr[x] = from_f32<T>(fv);
+      sXt[tix<T, LDT>(c, r)] = tk;
+    }
+    out = reinterpret_cast<T*>(a.kbt) + to;
+  }
+  __syncthreads();
+  for (int c = tid; c < D * CPT; c += 256) {
+    const int e = c / CPT, k0 = (c % CPT) * EPC;
+    *reinterpret_cast<u32x4*>(out + e * kB + k0) = *reinterpret_cast<const u32x4*>(&sXt[tix<T, LDT>(e, k0)]);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Log2-domain bias of every virtual token of query tile i, (ln n_j + φ_ij) log2 e, -inf for
+// the selected blocks and the padding past nb (φ as in the forward: gated w̃, or ln(1 + w̃));
+// and, once, 1 / n_j (0 past nb).
+template <int MODE>
+__global__ __launch_bounds__(256) void bwd_bias_kernel(BwdArgs a) {
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  const int i = blockIdx.x, h = blockIdx.y, nb = a.nb;
+  const uint32_t* mrow = a.mask + (size_t(h) * nb + i) * a.nw;
+  const float* wrow = MODE == MODE_PWT ? a.wt + (size_t(h) * nb + i) * nb : nullptr;
+  float* out = a.vbias + (size_t(h) * nb + i) * a.nbp;
+  for (int jj = threadIdx.x; jj < a.nbp; jj += 256) {
+    const int nn = jj < nb ? min(max(a.block_len ? a.block_len[jj] : kB, 1), kB) : 0;
+    float b = NEG_INF;
+    if (jj < nb && !((mrow[jj >> 5] >> (jj & 31)) & 1u)) {
+      const float lnn = logf(float(nn));
+      float phi = 0.f;
+      if (MODE == MODE_PWT) {
+        float w = wrow[jj];
+        if (a.gate && w > lnn) w = 0.f;
+        phi = a.w_linear ? log1pf(w) : w;
+      }
+      b = (lnn + phi) * kLog2e;
+    }
+    out[jj] = b;
+    if (h == 0 && i == 0) a.vinvn[jj] = nn > 0 ? 1.f / float(nn) : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Query tiles that selected key block j (from the membership bitmask), ascending: counts,
 // per-head exclusive scan, fill. One thread per (head, block) for count and fill.
 __global__ __launch_bounds__(256) void csr_count_kernel(BwdArgs a) {
@@ -178,28 +311,43 @@ __global__ __launch_bounds__(256) void csr_fill_kernel(BwdArgs a) {
 // dQ₀ = Kᵀ (P∘dP)ᵀ, kp = Kᵀ Pᵀ and Δ_t = Σ P dP (the definition of dO_t·o_t, in fp32 from
 // the recomputed P and dP) and forms dQ₀ - Δ kp at the end. P∘dP and P enter their products
 // as hi + lo bf16 pairs, so the cancellation in the difference costs no bf16 rounding.
+// Each tile's operands (K or k̄ rows, V or v̄ rows, Kᵀ or k̄ᵀ, and a virtual tile's biases
+// and 1 / n_j) arrive by direct global->LDS loads into a ring of NST stages, NST - 1 tiles
+// ahead of use, each stage its own LDS object (so the compiler sees that reading one stage
+// does not wait for the loads landing in another); tiles are swizzled rows (SwizzledTile).
 template <class T, int D, int MODE>
 __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   using M = typename MmaFor<T>::type;
   using AB = typename M::AB;
   constexpr int KI = M::KI, KH = M::KH;
-  constexpr int EPC = 16 / sizeof(T);
-  constexpr int LDK = D + EPC, LDT = kB + EPC;
+  constexpr int ES = sizeof(T);
   constexpr int NKD = D / KI, NKH = 32 / KI, NET = D / 32;
   constexpr bool VIRT = MODE != MODE_DROP;
   constexpr bool SPLIT = sizeof(T) == 2;            // hi + lo operands for bf16
-  constexpr int TK = kB * LDK * int(sizeof(T)), TT = D * LDT * int(sizeof(T));
-  __shared__ __align__(16) char lds[2 * TK + TT];
-  T* sK = reinterpret_cast<T*>(lds);
-  T* sV = reinterpret_cast<T*>(lds + TK);
-  T* sKt = reinterpret_cast<T*>(lds + 2 * TK);
-  __shared__ float sBias[kB], sInvN[kB], sDel[2][kB];
+  constexpr int KROW = D * ES, TROW = kB * ES;      // bytes per key row; per Kᵀ row
+  constexpr int TB = kB * KROW;                     // bytes per operand tile
+  constexpr int DPW = TB / 4096;                    // 1 KB direct loads per wave and operand
+  constexpr int RB = 3 * TB;                        // stage offset of the 4 x 64-float rows
+  constexpr int SB = RB + 4 * kB * 4;               // bytes per stage
+  constexpr int BUDGET = 152 * 1024;
+  constexpr int NST = 3 * SB <= BUDGET ? 3 : (2 * SB <= BUDGET ? 2 : 1);
+  constexpr int PT = 3 * DPW + 1;                   // direct loads per wave and tile
+  constexpr int DCH = 256;                          // descriptor chunk (exact tiles)
+  using KT = SwizzledTile<KROW>;
+  using TT = SwizzledTile<TROW>;
+  static_assert(DPW >= 1 && TB % 4096 == 0, "tile shape");
+  __shared__ __align__(1024) char sS0[SB];
+  __shared__ __align__(1024) char sS1[NST > 1 ? SB : 16];
+  __shared__ __align__(1024) char sS2[NST > 2 ? SB : 16];
+  __shared__ float sDel[2][kB];
+  __shared__ uint32_t sDesc[2][DCH];                // exact tile -> block | valid keys << 16
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // kept scalar
   const int wk = wave >> 1, wq = wave & 1;
   const uint32_t lin = xcd_remap(blockIdx.x, gridDim.x);
   const int h = int(lin / uint32_t(a.nb)), i = int(lin % uint32_t(a.nb));
-  const int nb = a.nb;
+  const int nb = a.nb, ngrp = a.nbp / kB;
   int m = a.block_len ? a.block_len[i] : kB;
   m = min(max(m, 1), kB);
   const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
@@ -211,8 +359,6 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
 
   const T* Qh = static_cast<const T*>(a.Q) + size_t(h) * a.L * D;
   const T* Gh = static_cast<const T*>(a.dO) + size_t(h) * a.L * D;
-  const T* Kh = static_cast<const T*>(a.K) + size_t(h) * a.L * D;
-  const T* Vh = static_cast<const T*>(a.V) + size_t(h) * a.L * D;
   AB qf[NKD], gf[NKD];
 #pragma unroll
   for (int ks = 0; ks < NKD; ++ks) {
@@ -224,101 +370,168 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   for (int et = 0; et < NET; ++et) dqt[et] = kpt[et] = zero16();
   float abar = 0.f, dsum = 0.f;
 
+  // Let the fragment loads land before the first direct loads are issued, so that later
+  // waits for those (counted from the newest) never have to cover them.
+  __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
+
   const int32_t* irow = a.idx + (size_t(h) * nb + i) * a.K_sel;
-  const uint32_t* mrow = a.mask ? a.mask + (size_t(h) * nb + i) * a.nw : nullptr;
-  const float* wrow = a.wt ? a.wt + (size_t(h) * nb + i) * nb : nullptr;
-  const int n1 = a.K_sel, N = n1 + (VIRT ? a.nbp / kB : 0);
+  const int n1 = a.K_sel, N = n1 + (VIRT ? ngrp : 0);
   const int R = 32 * wk + feed_row<M>(l32);       // key row this lane feeds
 
-  // Exact tiles' K and V rows are loaded into registers one tile ahead (in flight while the
-  // current tile is computed) and written to LDS at the top of their own iteration.
-  constexpr int CPR = D / EPC, CPT = kB * CPR / 256;
-  u32x4 rk[CPT], rv[CPT];
-  auto src = [&](int n, int& j, int& nj) {         // block and valid keys of exact tile n
-    j = irow[n];
-    nj = (j >= 0 && j < nb) ? min(max(a.block_len ? a.block_len[j] : kB, 1), kB) : 0;
-  };
-  auto prefetch = [&](int n) {
-    if (n >= n1) return;
-    int j, nj;
-    src(n, j, nj);
-#pragma unroll
-    for (int p = 0; p < CPT; ++p) {
-      const int c = tid + 256 * p, r = c / CPR, col = (c % CPR) * EPC;
-      const size_t o = (size_t(j) * kB + r) * D + col;
-      rk[p] = r < nj ? *reinterpret_cast<const u32x4*>(Kh + o) : zero_chunk<T>();
-      rv[p] = r < nj ? *reinterpret_cast<const u32x4*>(Vh + o) : zero_chunk<T>();
+  auto fill_desc = [&](int chunk) {
+    for (int e = tid; e < DCH; e += 256) {
+      const int n = chunk * DCH + e;
+      uint32_t d = 0u;
+      if (n < n1) {
+        const int j = irow[n];
+        if (j >= 0 && j < nb) d = uint32_t(j) | (uint32_t(min(max(a.block_len ? a.block_len[j] : kB, 1), kB)) << 16);
+      }
+      sDesc[chunk & 1][e] = d;
     }
   };
-  prefetch(0);
-  for (int n = 0; n < N; ++n) {
-    const bool virt = VIRT && n >= n1;
-    int j = 0, nj = 0;
-    if (!virt) src(n, j, nj);
-    else j = n - n1;
-    __syncthreads();                               // previous tile's LDS reads done
-    if (!virt) {
-      if (nj > 0) {
-#pragma unroll
-        for (int p = 0; p < CPT; ++p) {
-          const int c = tid + 256 * p, r = c / CPR, col = (c % CPR) * EPC;
-          *reinterpret_cast<u32x4*>(sK + r * LDK + col) = rk[p];
-          *reinterpret_cast<u32x4*>(sV + r * LDK + col) = rv[p];
-          const T* e = reinterpret_cast<const T*>(&rk[p]);
-#pragma unroll
-          for (int u = 0; u < EPC; ++u) sKt[tix<T, LDT>(col + u, r)] = e[u];
-        }
-      }
-      if (tid < kB) {
-        sBias[tid] = tid < nj ? 0.f : NEG_INF;
-        sInvN[tid] = 0.f;
-      }
-      prefetch(n + 1);
-    } else {
-      const int jb = j * kB, valid = min(kB, nb - jb);
-      const float* kb = a.kbar + (size_t(h) * nb + jb) * D;
-      const float* vs = a.vsum + (size_t(h) * nb + jb) * D;
-      auto one = [](int) { return 1.f; };
-      auto inv = [&](int r) { return 1.f / float(min(max(a.block_len ? a.block_len[jb + r] : kB, 1), kB)); };
-      stage_rows_f32<T, D, LDK, LDT, true>(kb, valid, one, sK, sKt, tid);
-      stage_rows_f32<T, D, LDK, LDT, false>(vs, valid, inv, sV, nullptr, tid);
-      if (tid < kB) {
-        const int jj = jb + tid;
-        float b = NEG_INF, invn = 0.f;
-        if (jj < nb && !((mrow[jj >> 5] >> (jj & 31)) & 1u)) {
-          const int nn = min(max(a.block_len ? a.block_len[jj] : kB, 1), kB);
-          const float lnn = logf(float(nn));
-          float phi = 0.f;
-          if (MODE == MODE_PWT) {
-            float w = wrow[jj];
-            if (a.gate && w > lnn) w = 0.f;
-            phi = a.w_linear ? log1pf(w) : w;
-          }
-          b = (lnn + phi) * kLog2e;
-          invn = 1.f / float(nn);
-        }
-        sBias[tid] = b;
-        sInvN[tid] = invn;
-      }
-    }
-    __syncthreads();
-    if (!virt && nj == 0) continue;                // uniform: out-of-range index, empty block
+  auto desc = [&](int t) -> uint32_t {
+    return __builtin_amdgcn_readfirstlane(lds_read_u32(lds_addr(&sDesc[(t / DCH) & 1][t % DCH])));
+  };
 
+  // Per-lane source offsets inside a tile of the 16-byte chunk each direct load of this
+  // lane fills (swizzled order), for the row tiles (rows of KROW bytes) and Kᵀ tiles.
+  int koff[DPW], krow[DPW], toff[DPW];
+#pragma unroll
+  for (int u = 0; u < DPW; ++u) {
+    const int b = (wave * DPW + u) * 1024 + lane * 16;
+    const int rk = b / KROW, rt = b / TROW;
+    krow[u] = rk;
+    koff[u] = rk * KROW + ((((b % KROW) >> 4) ^ KT::swz(rk)) << 4);
+    toff[u] = rt * TROW + ((((b % TROW) >> 4) ^ TT::swz(rt)) << 4);
+  }
+  // Direct loads of tile t into stage S. Rows of an exact block past its valid count are
+  // loaded from row 0 instead (finite values; their keys are masked). Wave 0 loads a
+  // virtual tile's biases, wave 1 its 1 / n_j; every wave issues the same PT loads.
+  const char* Kb = reinterpret_cast<const char*>(static_cast<const T*>(a.K) + size_t(h) * a.L * D);
+  const char* Vb = reinterpret_cast<const char*>(static_cast<const T*>(a.V) + size_t(h) * a.L * D);
+  auto issue = [&](int t, auto sc) {
+    constexpr int S = decltype(sc)::value;
+    char* st = S == 0 ? sS0 : (S == 1 ? sS1 : sS2);
+    const char *pk, *pv, *pt, *pr;
+    int nrows;
+    if (VIRT && t >= n1) {
+      const size_t go = (size_t(h) * ngrp + (t - n1)) * TB;
+      pk = a.kbr + go;
+      pv = a.vbr + go;
+      pt = a.kbt + go;
+      nrows = kB;
+      pr = wave == 0 ? reinterpret_cast<const char*>(a.vbias + (size_t(h) * nb + i) * a.nbp + (t - n1) * kB)
+                     : reinterpret_cast<const char*>(a.vinvn + (t - n1) * kB);
+    } else {
+      const uint32_t d = desc(t);
+      const int j = int(d & 0xFFFFu);
+      nrows = int(d >> 16);
+      pk = Kb + size_t(j) * TB;
+      pv = Vb + size_t(j) * TB;
+      pt = a.kt + (size_t(h) * nb + j) * TB;
+      pr = reinterpret_cast<const char*>(a.vinvn ? a.vinvn : a.lse);   // unused values
+    }
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(pk, TB), rv = make_rsrc(pv, TB), rt = make_rsrc(pt, TB);
+#pragma unroll
+    for (int u = 0; u < DPW; ++u) {
+      const int ko = krow[u] < nrows ? koff[u] : koff[u] - krow[u] * KROW;
+      buf_dma16(rk, ko, 0, st + (wave * DPW + u) * 1024);
+      buf_dma16(rv, ko, 0, st + TB + (wave * DPW + u) * 1024);
+      buf_dma16(rt, toff[u], 0, st + 2 * TB + (wave * DPW + u) * 1024);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(pr, kB * 4), (__attribute__((address_space(3))) void*)(st + RB + wave * kB * 4),
+                                             4, lane * 4, 0, 0, 0);
+  };
+
+  // LDS byte offsets inside a stage of this lane's operand fragments: K (and V, one tile
+  // further) rows for the scores, Kᵀ rows for dQ₀ and kp, and this lane's first bias.
+  constexpr int NT = NET * NKH;
+  uint32_t kad[NKD], tad[NT];
+#pragma unroll
+  for (int ks = 0; ks < NKD; ++ks) kad[ks] = KT::offset(R, (KI * ks + KH * g) * ES);
+#pragma unroll
+  for (int et = 0; et < NET; ++et)
+#pragma unroll
+    for (int ks = 0; ks < NKH; ++ks)
+      tad[et * NKH + ks] = 2 * TB + TT::offset(32 * et + l32, (32 * wk + KI * ks + KH * g) * ES);
+  const int key0 = 32 * wk + acc_key<M>(0, 0, g);
+
+  // One tile from stage S: Sᵀ, dPᵀ, P and P∘dP (hi + lo), dQ₀ and kp.
+  auto compute = [&](int t, auto sc) {
+    constexpr int S = decltype(sc)::value;
+    const char* sk = S == 0 ? sS0 : (S == 1 ? sS1 : sS2);
+    const bool virt = VIRT && t >= n1;
+    const int nj = virt ? kB : int(desc(t) >> 16);
+    if (nj == 0) return;                           // uniform: out-of-range index
+    // bf16 operands are read ahead into registers; fp32 ones (four times as many
+    // registers) where the products use them.
+    constexpr int NA = SPLIT ? NKD : 1, NTA = SPLIT ? NT : 1;
+    AB ka[NA], va[NA], ta[NTA];
+    float bias[16], invn[16];
+    if constexpr (SPLIT) {
+      // bf16: every operand in three blocks of 16-byte reads, the rows' biases in a fourth.
+      static_assert(NKD == 4 || NKD == 8, "fragments per block");
+      const uint32_t base = lds_addr(sk);
+      uint32_t ad[NKD], adt[NT];
+      u32x4 rk[NKD], rv[NKD], rt[NT];
+#pragma unroll
+      for (int ks = 0; ks < NKD; ++ks) ad[ks] = base + kad[ks];
+#pragma unroll
+      for (int x = 0; x < NT; ++x) adt[x] = base + tad[x];
+      lds_read_x16<NKD, 0>(rk, ad);
+      lds_read_x16<NKD, TB>(rv, ad);
+      lds_read_x16<NT, 0>(rt, adt);
+#pragma unroll
+      for (int ks = 0; ks < NKD; ++ks) {
+        ka[ks] = __builtin_bit_cast(AB, rk[ks]);
+        va[ks] = __builtin_bit_cast(AB, rv[ks]);
+      }
+#pragma unroll
+      for (int x = 0; x < NT; ++x) ta[x] = __builtin_bit_cast(AB, rt[x]);
+      if (virt) {
+        // keys key0 + {0..7, 16..23}: biases at +0, +64 bytes, 1 / n_j one row (256 bytes) on
+        u32x4 rb[8];
+        lds_read8_at<0, 16, 64, 80, 256, 272, 320, 336>(rb, base + RB + key0 * 4);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          bias[r] = __uint_as_float(rb[(r >> 3) * 2 + ((r >> 2) & 1)][r & 3]);
+          invn[r] = __uint_as_float(rb[4 + (r >> 3) * 2 + ((r >> 2) & 1)][r & 3]);
+        }
+      }
+    } else {
+      const float* sbias = reinterpret_cast<const float*>(sk + RB);
+      if (virt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * wk + acc_key<M>(0, r, g);
+          bias[r] = sbias[key];
+          invn[r] = sbias[kB + key];
+        }
+      }
+    }
+    if (!virt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        bias[r] = 32 * wk + acc_key<M>(0, r, g) < nj ? 0.f : NEG_INF;
+        invn[r] = 0.f;
+      }
+    }
+    auto kfrag = [&](int ks) { return SPLIT ? ka[ks % NA] : M::load(reinterpret_cast<const T*>(sk + kad[ks])); };
+    auto vfrag = [&](int ks) { return SPLIT ? va[ks % NA] : M::load(reinterpret_cast<const T*>(sk + TB + kad[ks])); };
     f32x16 s = zero16(), p = zero16();
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks) {
-      s = M::mma(M::load(sK + R * LDK + KI * ks + KH * g), qf[ks], s);
-      p = M::mma(M::load(sV + R * LDK + KI * ks + KH * g), gf[ks], p);
+      s = M::mma(kfrag(ks), qf[ks], s);
+      p = M::mma(vfrag(ks), gf[ks], p);
     }
     f32x16 slo, plo;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = 32 * wk + acc_key<M>(0, r, g);
-      const float P = fast_exp2(fmaf(s[r], kLog2e, sBias[key]) - lse2);
+      const float P = fast_exp2(fmaf(s[r], kLog2e, bias[r]) - lse2);
       float dp = p[r];
       if (virt) {
-        dp = fmaf(gu, sInvN[key], dp);
-        abar = fmaf(P, sInvN[key], abar);
+        dp = fmaf(gu, invn[r], dp);
+        abar = fmaf(P, invn[r], abar);
       }
       const float pd = P * dp;
       dsum += pd;
@@ -338,12 +551,41 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
       const AB bp = M::template packv<ks * KH>(p);
 #pragma unroll
       for (int et = 0; et < NET; ++et) {
-        const AB ka = M::load(sKt + tix<T, LDT>(32 * et + l32, 32 * wk + KI * ks + KH * g));
-        dqt[et] = M::mma(ka, bs, dqt[et]);
-        kpt[et] = M::mma(ka, bp, kpt[et]);
+        const AB kt = SPLIT ? ta[(et * NKH + ks) % NTA] : M::load(reinterpret_cast<const T*>(sk + tad[et * NKH + ks]));
+        dqt[et] = M::mma(kt, bs, dqt[et]);
+        kpt[et] = M::mma(kt, bp, kpt[et]);
         if constexpr (SPLIT) {
-          dqt[et] = M::mma(ka, M::template packv<ks * KH>(slo), dqt[et]);
-          kpt[et] = M::mma(ka, M::template packv<ks * KH>(plo), kpt[et]);
+          dqt[et] = M::mma(kt, M::template packv<ks * KH>(slo), dqt[et]);
+          kpt[et] = M::mma(kt, M::template packv<ks * KH>(plo), kpt[et]);
+        }
+      }
+    });
+  };
+
+  if (n1 > 0) fill_desc(0);
+  if (n1 > DCH) fill_desc(1);
+  __syncthreads();
+  // Prologue: tiles [0, NST - 1) in flight (tile 0 with a single stage).
+  static_for<0, (NST > 1 ? NST - 1 : 1)>([&](auto sc) {
+    if (decltype(sc)::value < N) issue(decltype(sc)::value, sc);
+  });
+  // NST tiles per iteration so every stage index is static.
+  for (int n = 0; n < N; n += NST) {
+    static_for<0, NST>([&](auto sc) {
+      constexpr int S = decltype(sc)::value;
+      const int t = n + S;
+      if (t < N) {
+        // This wave's loads of tile t have landed once at most the loads of the tiles
+        // issued after it (NST - 2 of them, fewer at the end) are outstanding; after the
+        // barrier everyone's have, and the stage of tile t - 1 is free.
+        if (NST == 3 && t + 1 < N) barrier_vm<PT>();
+        else barrier_vm<0>();
+        if (t % DCH == 0 && t >= DCH && t + DCH < n1) fill_desc(t / DCH + 1);
+        if (NST > 1 && t + NST - 1 < N) issue(t + NST - 1, std::integral_constant<int, (S + NST - 1) % NST>{});
+        compute(t, sc);
+        if (NST == 1) {
+          __syncthreads();
+          if (t + 1 < N) issue(t + 1, sc);
         }
       }
     });
@@ -362,10 +604,9 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
 
   // Merge the key halves: wave (1, wq) hands its partial dQᵀ and Ā to wave (0, wq).
   constexpr int XF = (NET * 16 + 1) * 64;          // floats handed over per wave
-  static_assert(2 * XF * 4 <= 2 * TK + TT, "hand-over buffer");
-  __syncthreads();
+  static_assert(2 * XF * 4 <= SB, "hand-over buffer");
   if (wk == 1) {
-    float* mine = reinterpret_cast<float*>(lds) + wq * XF + lane;
+    float* mine = reinterpret_cast<float*>(sS0) + wq * XF + lane;
 #pragma unroll
     for (int et = 0; et < NET; ++et)
 #pragma unroll
@@ -375,7 +616,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   __syncthreads();
   if (wk == 1) return;
   {
-    const float* other = reinterpret_cast<const float*>(lds) + wq * XF + lane;
+    const float* other = reinterpret_cast<const float*>(sS0) + wq * XF + lane;
 #pragma unroll
     for (int et = 0; et < NET; ++et)
 #pragma unroll
@@ -888,6 +1129,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   } while (0)
   hipLaunchKernelGGL((bwd_rows_kernel<T, D>), tiles, dim3(256), 0, s, a);
   PISA_CHECK();
+  hipLaunchKernelGGL((bwd_pack_kernel<T, D>), dim3(a.nb, a.H, MODE == MODE_DROP ? 1 : 2), dim3(256), 0, s, a);
+  PISA_CHECK();
+  if (MODE != MODE_DROP) {
+    hipLaunchKernelGGL((bwd_bias_kernel<MODE>), dim3(a.nb, a.H), dim3(256), 0, s, a);
+    PISA_CHECK();
+  }
   hipLaunchKernelGGL(csr_count_kernel, blocks, dim3(256), 0, s, a);
   PISA_CHECK();
   hipLaunchKernelGGL(csr_scan_kernel, dim3(a.H), dim3(256), 0, s, a);

@@ -134,16 +134,25 @@ struct BwdArgs {
   float* dh;         // [H][d][d]
   int* csr_off;      // [H][nb + 1]
   int* csr_list;     // [H][nb * K_sel]
+  // Operand tiles of the dQ sweep in the input type (written by bwd_pack_kernel), 64 x d or
+  // d x 64 row-major, zeros past the valid rows: [H][nb] block tiles, [H][nbp/64] groups
+  char* kt;          // Kᵀ of each key block
+  char* kbr;         // k̄ rows of each centroid group
+  char* kbt;         // k̄ᵀ of each centroid group
+  char* vbr;         // v̄ = ΣV / n rows of each centroid group
+  float* vbias;      // [H][nb][nbp] log2-domain bias of each virtual token (-inf: excluded)
+  float* vinvn;      // [nbp] 1 / n_j (0 past nb)
   int H, L, d, nb, nbp, K_sel, nw, nchunk, nhch;
   int w_linear, gate;
 };
 
 struct BwdLayout {
-  size_t delta, gu, abar, qsq, dwt, dsig2, dkp, dvp, dhp, dh, off, list, total;
+  size_t delta, gu, abar, qsq, dwt, dsig2, dkp, dvp, dhp, dh, off, list;
+  size_t kt, kbr, kbt, vbr, vbias, vinvn, total;
   int nchunk, nhch;
 };
 
-inline BwdLayout bwd_layout(int H, int L, int d, int K_sel) {
+inline BwdLayout bwd_layout(size_t elem, int H, int L, int d, int K_sel) {
   BwdLayout w;
   const int nb = L / kB, nbp = (nb + kB - 1) / kB * kB, ngrp = nbp / kB;
   long long c = (1024 + static_cast<long long>(H) * ngrp - 1) / (static_cast<long long>(H) * ngrp);
@@ -164,6 +173,13 @@ inline BwdLayout bwd_layout(int H, int L, int d, int K_sel) {
   w.dh = o;    o = align256(o + Hs * d * d * f);
   w.off = o;   o = align256(o + Hs * (nb + 1) * sizeof(int));
   w.list = o;  o = align256(o + Hs * nb * size_t(K_sel > 0 ? K_sel : 1) * sizeof(int));
+  const size_t tiles = Hs * nb * kB * d * elem, groups = Hs * (nbp / kB) * kB * d * elem;
+  w.kt = o;    o = align256(o + tiles);
+  w.kbr = o;   o = align256(o + groups);
+  w.kbt = o;   o = align256(o + groups);
+  w.vbr = o;   o = align256(o + groups);
+  w.vbias = o; o = align256(o + Hs * nb * nbp * f);
+  w.vinvn = o; o = align256(o + size_t(nbp) * f);
   w.total = o;
   return w;
 }

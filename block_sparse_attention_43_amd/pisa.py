@@ -87,7 +87,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pisa_attention_fwd.argtypes = [i32, vp, vp, vp, sp, vp, vp, vp, i32, i32, i32, i32, vp, i32,
                                        u32, vp, vp, vp]
     lib.pisa_attention_fwd.restype = i32
-    lib.pisa_attention_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.pisa_attention_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.pisa_attention_bwd_workspace_bytes.restype = sz
     lib.pisa_attention_bwd.argtypes = [i32, vp, vp, vp, sp, vp, vp, vp, i32, i32, i32, i32, vp, i32, u32,
                                        vp, vp, vp, vp, vp, vp, sz, vp]
@@ -269,7 +269,7 @@ def attention_bwd(Q, K, V, st: Stats, idx, mask, wt, K_sel: int, lse, dO, mode="
         out = tuple(torch.empty(H, L, d, dtype=torch.float32, device=Q.device) for _ in range(3))
     dQ, dK, dV = out
     if workspace is None:
-        need = lib.pisa_attention_bwd_workspace_bytes(H, L, d, B, K_sel)
+        need = lib.pisa_attention_bwd_workspace_bytes(_dtype_code(Q), H, L, d, B, K_sel)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=Q.device)
     s = st.struct()
     _check(lib.pisa_attention_bwd(_dtype_code(Q), _ptr(Q), _ptr(K), _ptr(V), ctypes.byref(s), _ptr(idx),

@@ -256,7 +256,7 @@ pisa_status pisa_attention_fwd(pisa_dtype dt, const void* Q, const void* K, cons
                                float* lse, void* stream);
 
 /* Workspace bytes of pisa_attention_bwd (0 if unsupported). */
-size_t pisa_attention_bwd_workspace_bytes(int H, int L, int d, int B, int K_sel);
+size_t pisa_attention_bwd_workspace_bytes(pisa_dtype dt, int H, int L, int d, int B, int K_sel);
 
 /*
  * Backward of pisa_attention_fwd for PISA_MODE_DROP, PISA_MODE_PISA and PISA_MODE_PWT (with
@@ -267,7 +267,7 @@ size_t pisa_attention_bwd_workspace_bytes(int H, int L, int d, int B, int K_sel)
  *            call (mask is required for every mode and must match idx; st needs kbar, vsum,
  *            ksig2 and hbarT); lse: that call's output; dO [H][L][d] dtype `dt`.
  *   Outputs  dQ, dK, dV [H][L][d] float32, overwritten (zeros on padded slots).
- *   Workspace pisa_attention_bwd_workspace_bytes(H, L, d, B, K_sel) bytes.
+ *   Workspace pisa_attention_bwd_workspace_bytes(dt, H, L, d, B, K_sel) bytes.
  * With P = e^{logit - lse} for every exact key and virtual token, u_t = H̄ q_t,
  * Ā_t = Σ_j P_{t,j} / n_j and Δ_t = dO_t·o_t (formed in fp32 as Σ P·dP over every exact key
  * and virtual token, with dP = dO·v, or dO·v̄_j + dO·u_t / n_j, which is dO·o exactly):

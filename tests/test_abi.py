@@ -169,8 +169,8 @@ def test_backward_argument_errors(lib, case, status, msg):
     r = lib.pisa_attention_bwd(1, 16, 16, 16, ctypes.byref(st), 16, a["mask"], a["wt"], 1, 1024, 64, 64, None, 4,
                                a["mode"], a["lse"], 16, 16, 16, 16, 16, a["ws"], None)
     assert r == status and msg in lib.pisa_last_error().decode()
-    assert lib.pisa_attention_bwd_workspace_bytes(1, 1024, 64, 64, 4) > 0
-    assert lib.pisa_attention_bwd_workspace_bytes(1, 1024, 64, 64, 17) == 0
+    assert lib.pisa_attention_bwd_workspace_bytes(1, 1, 1024, 64, 64, 4) > 0
+    assert lib.pisa_attention_bwd_workspace_bytes(1, 1, 1024, 64, 64, 17) == 0
 
 
 @pytest.mark.parametrize("grid", [(5, 6, 7), (8, 8, 8), (1, 3, 9), (21, 30, 52), (30, 48, 80)])
