@@ -374,7 +374,10 @@ pisa_status pisa_attention_bwd(pisa_dtype dt, const void* Q, const void* K, cons
   a.kbr = ws + w.kbr;
   a.kbt = ws + w.kbt;
   a.vbr = ws + w.vbr;
+  a.qt = ws + w.qt;
+  a.gt = ws + w.gt;
   a.vbias = reinterpret_cast<float*>(ws + w.vbias);
+  a.vdphi = reinterpret_cast<float*>(ws + w.vdphi);
   a.vinvn = reinterpret_cast<float*>(ws + w.vinvn);
   a.H = H;
   a.L = L;

@@ -117,6 +117,14 @@ __device__ __forceinline__ void lds_read8_at(u32x4 (&o)[8], uint32_t ad) {
       : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
       : "v"(ad), "i"(O0), "i"(O1), "i"(O2), "i"(O3), "i"(O4), "i"(O5), "i"(O6), "i"(O7));
 }
+__device__ __forceinline__ void lds_write_u32(uint32_t ad, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(ad), "v"(v) : "memory");
+}
+// Barrier after this wave's LDS operations, leaving its vector memory loads in flight.
+__device__ __forceinline__ void barrier_lgkm() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);              // vmcnt(63) expcnt(7) lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
 __device__ __forceinline__ uint32_t lds_read_u32(uint32_t ad) {
   uint32_t v;
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(ad));
@@ -179,10 +187,11 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Operand tiles of the dQ sweep that are not rows of the inputs, rounded to the input type
-// as the forward's centroid tiles are, zeros past the valid rows: z = 0, key block i: Kᵀ
-// [d][64]; z = 1, centroid group i: k̄ rows [64][d], k̄ᵀ [d][64] and v̄ = ΣV / n rows [64][d].
-// The sweep moves them, with K and V themselves, into LDS by direct loads.
+// Operand tiles of the sweeps that are not rows of the inputs, in the input type (centroid
+// tiles rounded from fp32 as the forward's are), zeros past the valid rows: z = 0, block i:
+// Kᵀ [d][64]; z = 1, query tile i: Qᵀ and dOᵀ; z = 2, centroid group i: k̄ rows [64][d],
+// k̄ᵀ [d][64] and v̄ = ΣV / n rows [64][d]. The sweeps move them, with the rows of Q, K, V
+// and dO themselves, into LDS by direct loads.
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_pack_kernel(BwdArgs a) {
   constexpr int EPC = 16 / sizeof(T), LDT = kB + EPC, CPR = D / EPC, CPT = kB / EPC;
@@ -190,10 +199,8 @@ __global__ __launch_bounds__(256) void bwd_pack_kernel(BwdArgs a) {
   __shared__ __align__(16) T sXt[D * LDT];
   const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int nb = a.nb, ngrp = a.nbp / kB;
-  T* out;
-  if (blockIdx.z == 0) {
-    const int valid = min(max(a.block_len ? a.block_len[i] : kB, 1), kB);
-    const T* src = static_cast<const T*>(a.K) + (size_t(h) * a.L + size_t(i) * kB) * D;
+  // Transpose of the valid rows of a 64-row block of src into sXt.
+  auto stage_t = [&](const T* src, int valid) {
     for (int c = tid; c < kB * CPR; c += 256) {
       const int r = c / CPR, col = (c % CPR) * EPC;
       const u32x4 v = r < valid ? *reinterpret_cast<const u32x4*>(src + size_t(r) * D + col) : zero_chunk<T>();
@@ -201,7 +208,28 @@ __global__ __launch_bounds__(256) void bwd_pack_kernel(BwdArgs a) {
 #pragma unroll
       for (int u = 0; u < EPC; ++u) sXt[tix<T, LDT>(col + u, r)] = e[u];
     }
-    out = reinterpret_cast<T*>(a.kt) + (size_t(h) * nb + i) * TE;
+  };
+  auto write_t = [&](T* out) {
+    for (int c = tid; c < D * CPT; c += 256) {
+      const int e = c / CPT, k0 = (c % CPT) * EPC;
+      *reinterpret_cast<u32x4*>(out + e * kB + k0) = *reinterpret_cast<const u32x4*>(&sXt[tix<T, LDT>(e, k0)]);
+    }
+  };
+  T* out;
+  if (blockIdx.z < 2) {
+    const int valid = min(max(a.block_len ? a.block_len[i] : kB, 1), kB);
+    const size_t row0 = (size_t(h) * a.L + size_t(i) * kB) * D, to = (size_t(h) * nb + i) * TE;
+    if (blockIdx.z == 0) {
+      stage_t(static_cast<const T*>(a.K) + row0, valid);
+      out = reinterpret_cast<T*>(a.kt) + to;
+    } else {
+      stage_t(static_cast<const T*>(a.Q) + row0, valid);
+      __syncthreads();
+      write_t(reinterpret_cast<T*>(a.qt) + to);
+      __syncthreads();
+      stage_t(static_cast<const T*>(a.dO) + row0, valid);
+      out = reinterpret_cast<T*>(a.gt) + to;
+    }
   } else {
     if (i >= ngrp) return;
     const int j0 = i * kB, valid = min(kB, nb - j0);
@@ -224,16 +252,13 @@ __global__ __launch_bounds__(256) void bwd_pack_kernel(BwdArgs a) {
     out = reinterpret_cast<T*>(a.kbt) + to;
   }
   __syncthreads();
-  for (int c = tid; c < D * CPT; c += 256) {
-    const int e = c / CPT, k0 = (c % CPT) * EPC;
-    *reinterpret_cast<u32x4*>(out + e * kB + k0) = *reinterpret_cast<const u32x4*>(&sXt[tix<T, LDT>(e, k0)]);
-  }
+  write_t(out);
 }
 
 // ---------------------------------------------------------------------------------------
 // Log2-domain bias of every virtual token of query tile i, (ln n_j + φ_ij) log2 e, -inf for
-// the selected blocks and the padding past nb (φ as in the forward: gated w̃, or ln(1 + w̃));
-// and, once, 1 / n_j (0 past nb).
+// the selected blocks and the padding past nb (φ as in the forward: gated w̃, or ln(1 + w̃)),
+// with φ'(w̃) (0 where excluded or gated, and for PISA); and, once, 1 / n_j (0 past nb).
 template <int MODE>
 __global__ __launch_bounds__(256) void bwd_bias_kernel(BwdArgs a) {
   constexpr float NEG_INF = -__builtin_huge_valf();
@@ -243,18 +268,21 @@ __global__ __launch_bounds__(256) void bwd_bias_kernel(BwdArgs a) {
   float* out = a.vbias + (size_t(h) * nb + i) * a.nbp;
   for (int jj = threadIdx.x; jj < a.nbp; jj += 256) {
     const int nn = jj < nb ? min(max(a.block_len ? a.block_len[jj] : kB, 1), kB) : 0;
-    float b = NEG_INF;
+    float b = NEG_INF, dphi = 0.f;
     if (jj < nb && !((mrow[jj >> 5] >> (jj & 31)) & 1u)) {
       const float lnn = logf(float(nn));
       float phi = 0.f;
       if (MODE == MODE_PWT) {
         float w = wrow[jj];
-        if (a.gate && w > lnn) w = 0.f;
+        const bool fired = a.gate && w > lnn;
+        if (fired) w = 0.f;
         phi = a.w_linear ? log1pf(w) : w;
+        dphi = fired ? 0.f : (a.w_linear ? 1.f / (1.f + w) : 1.f);
       }
       b = (lnn + phi) * kLog2e;
     }
     out[jj] = b;
+    a.vdphi[(size_t(h) * nb + i) * a.nbp + jj] = dphi;
     if (h == 0 && i == 0) a.vinvn[jj] = nn > 0 ? 1.f / float(nn) : 0.f;
   }
 }
@@ -655,23 +683,36 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
 // chunk of query tiles (virtual): dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS. Wave (wq, wk) computes
 // S and dP for query half wq and key half wk (queries fed through feed_row, so P and dS
 // in registers are the B operands); the two query halves are merged at the end.
+// Each query tile's Q and dO rows, Qᵀ and dOᵀ, row statistics and (centroid groups) the
+// tile's biases and φ' arrive by direct loads into a ring of NST stages, read through
+// inline-asm blocks (bf16) as in bwd_query_kernel.
 template <class T, int D, int MODE, bool GROUP>
 __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   using M = typename MmaFor<T>::type;
   using AB = typename M::AB;
   constexpr int KI = M::KI, KH = M::KH;
-  constexpr int EPC = 16 / sizeof(T);
-  constexpr int LDK = D + EPC, LDT = kB + EPC;
-  constexpr int NKD = D / KI, NKH = 32 / KI, NET = D / 32;
-  constexpr int TK = kB * LDK * int(sizeof(T)), TT = D * LDT * int(sizeof(T));
-  __shared__ __align__(16) char lds[2 * TK + 2 * TT];
-  T* sQ = reinterpret_cast<T*>(lds);
-  T* sG = reinterpret_cast<T*>(lds + TK);
-  T* sQt = reinterpret_cast<T*>(lds + 2 * TK);
-  T* sGt = reinterpret_cast<T*>(lds + 2 * TK + TT);
-  __shared__ float sL[kB], sD[kB], sU[kB], sBias[kB], sDphi[kB], sCol[2][kB];
+  constexpr int ES = sizeof(T);
+  constexpr int NKD = D / KI, NKH = 32 / KI, NET = D / 32, NT = NET * NKH;
+  constexpr bool SPLIT = sizeof(T) == 2;
+  constexpr int KROW = D * ES, TROW = kB * ES, TB = kB * KROW;
+  constexpr int DPW = TB / 4096;                    // 1 KB direct loads per wave and operand
+  constexpr int RB = 4 * TB;                        // rows: lse, Δ, gu, bias, φ', 3 unused
+  constexpr int SB = RB + 8 * kB * 4;               // bytes per stage
+  constexpr int BUDGET = 152 * 1024;
+  constexpr int NST = 3 * SB <= BUDGET ? 3 : (2 * SB <= BUDGET ? 2 : 1);
+  constexpr int PT = 4 * DPW + 2;                   // direct loads per wave and tile
+  constexpr int DCH = 256;
+  using KT = SwizzledTile<KROW>;
+  using TT = SwizzledTile<TROW>;
+  static_assert(DPW >= 1 && TB % 4096 == 0, "tile shape");
+  __shared__ __align__(1024) char sS0[SB];
+  __shared__ __align__(1024) char sS1[NST > 1 ? SB : 16];
+  __shared__ __align__(1024) char sS2[NST > 2 ? SB : 16];
+  __shared__ float sCol[2][kB];
+  __shared__ uint32_t sDesc[2][DCH];                // tile -> query tile | valid rows << 16
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // kept scalar
   const int wq = wave >> 1, wk = wave & 1;
   const int nb = a.nb;
   const int ngrp = a.nbp / kB;
@@ -686,7 +727,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   }
   const int kcol = 32 * wk + l32;                  // this lane's key (column of S)
   int nj = 0, jj = 0;
-  float invn = 0.f, lnn = 0.f;
+  float invn = 0.f;
   bool kvalid;
   if (!GROUP) {
     nj = min(max(a.block_len ? a.block_len[j] : kB, 1), kB);
@@ -694,11 +735,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   } else {
     jj = j * kB + kcol;
     kvalid = jj < nb;
-    if (kvalid) {
-      const int nn = min(max(a.block_len ? a.block_len[jj] : kB, 1), kB);
-      invn = 1.f / float(nn);
-      lnn = logf(float(nn));
-    }
+    if (kvalid) invn = 1.f / float(min(max(a.block_len ? a.block_len[jj] : kB, 1), kB));
   }
   // K and V rows of this lane's key as B operands (T; centroid groups rounded from fp32).
   AB kf[NKD], vf[NKD];
@@ -744,123 +781,199 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
     t0 = min(nb, chunk * per);
     t1 = min(nb, t0 + per);
   }
-  const T* Qh = static_cast<const T*>(a.Q) + size_t(h) * a.L * D;
-  const T* Gh = static_cast<const T*>(a.dO) + size_t(h) * a.L * D;
-  const int Rq = 32 * wq + feed_row<M>(l32);       // query row this lane feeds
+  const int N = t1 - t0;
+  // Let the operand loads land before the first direct loads are issued, so that later
+  // waits for those (counted from the newest) never have to cover them.
+  __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
 
-  // The next query tile's Q and dO rows, row statistics and (centroid groups) bias inputs
-  // are loaded into registers one tile ahead and written to LDS at the top of its iteration.
-  constexpr int CPR = D / EPC, CPT = kB * CPR / 256;
-  u32x4 rq[CPT], rg[CPT];
-  float pl = 0.f, pd = 0.f, pu = 0.f, pw = 0.f;
-  uint32_t pm = 0u;
-  int pn = kB, pmv = kB;
-  auto prefetch = [&](int x) {
-    if (x >= t1) return;
-    const int i = GROUP ? x : list[x];
-    const int m = min(max(a.block_len ? a.block_len[i] : kB, 1), kB);
-    pmv = m;
-#pragma unroll
-    for (int p = 0; p < CPT; ++p) {
-      const int c = tid + 256 * p, r = c / CPR, col = (c % CPR) * EPC;
-      const size_t o = (size_t(i) * kB + r) * D + col;
-      rq[p] = r < m ? *reinterpret_cast<const u32x4*>(Qh + o) : zero_chunk<T>();
-      rg[p] = r < m ? *reinterpret_cast<const u32x4*>(Gh + o) : zero_chunk<T>();
-    }
-    const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
-    if (tid < kB) {
-      pl = a.lse[row0 + tid];
-      pd = a.delta[row0 + tid];
-      pu = a.gu[row0 + tid];
-    } else if (GROUP && tid < 2 * kB) {
-      const int jk = min(j * kB + tid - kB, nb - 1);
-      pm = a.mask[(size_t(h) * nb + i) * a.nw + (jk >> 5)];
-      pn = a.block_len ? a.block_len[jk] : kB;
-      if (MODE == MODE_PWT) pw = a.wt[(size_t(h) * nb + i) * nb + jk];
+  auto fill_desc = [&](int c) {
+    for (int e = tid; e < DCH; e += 256) {
+      const int n = c * DCH + e;
+      uint32_t d = 0u;
+      if (n < N) {
+        const int i = GROUP ? t0 + n : list[t0 + n];
+        d = uint32_t(i) | (uint32_t(min(max(a.block_len ? a.block_len[i] : kB, 1), kB)) << 16);
+      }
+      sDesc[c & 1][e] = d;
     }
   };
-  // fp32 at d = 128 has no registers to spare for a tile in flight: load in place.
-  constexpr bool AHEAD = !(sizeof(T) == 4 && D == 128);
-  if (AHEAD) prefetch(t0);
-  for (int x = t0; x < t1; ++x) {
-    if (!AHEAD) prefetch(x);
-    const int m = pmv;
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < CPT; ++p) {
-      const int c = tid + 256 * p, r = c / CPR, col = (c % CPR) * EPC;
-      *reinterpret_cast<u32x4*>(sQ + r * LDK + col) = rq[p];
-      *reinterpret_cast<u32x4*>(sG + r * LDK + col) = rg[p];
-      const T* eq = reinterpret_cast<const T*>(&rq[p]);
-      const T* eg = reinterpret_cast<const T*>(&rg[p]);
-#pragma unroll
-      for (int u = 0; u < EPC; ++u) {
-        sQt[tix<T, LDT>(col + u, r)] = eq[u];
-        sGt[tix<T, LDT>(col + u, r)] = eg[u];
-      }
-    }
-    if (tid < kB) {
-      const bool live = tid < m && pl > NEG_INF;
-      sL[tid] = live ? pl * kLog2e : POS_INF;
-      sD[tid] = pd;
-      sU[tid] = pu;
-    } else if (GROUP && tid < 2 * kB) {
-      // bias of this lane group's keys for the tile: ln n_j + φ_{i,j}, -inf when selected
-      const int k = tid - kB, jk = j * kB + k;
-      float b = NEG_INF, dphi = 0.f;
-      if (jk < nb && !((pm >> (jk & 31)) & 1u)) {
-        const float ln = logf(float(min(max(pn, 1), kB)));
-        float phi = 0.f;
-        if (MODE == MODE_PWT) {
-          float w = pw;
-          const bool fired = a.gate && w > ln;
-          if (fired) w = 0.f;
-          phi = a.w_linear ? log1pf(w) : w;
-          dphi = fired ? 0.f : (a.w_linear ? 1.f / (1.f + w) : 1.f);
-        }
-        b = (ln + phi) * kLog2e;
-      }
-      sBias[k] = b;
-      sDphi[k] = dphi;
-    }
-    if (AHEAD) prefetch(x + 1);
-    __syncthreads();
+  auto desc = [&](int n) -> uint32_t {
+    return __builtin_amdgcn_readfirstlane(lds_read_u32(lds_addr(&sDesc[(n / DCH) & 1][n % DCH])));
+  };
 
+  // Per-lane source offsets (swizzled order) of the chunks this lane's direct loads fill.
+  int roff[DPW], rrow[DPW], toff[DPW];
+#pragma unroll
+  for (int u = 0; u < DPW; ++u) {
+    const int b = (wave * DPW + u) * 1024 + lane * 16;
+    const int rk = b / KROW, rt = b / TROW;
+    rrow[u] = rk;
+    roff[u] = rk * KROW + ((((b % KROW) >> 4) ^ KT::swz(rk)) << 4);
+    toff[u] = rt * TROW + ((((b % TROW) >> 4) ^ TT::swz(rt)) << 4);
+  }
+  const char* Qb = reinterpret_cast<const char*>(static_cast<const T*>(a.Q) + size_t(h) * a.L * D);
+  const char* Gb = reinterpret_cast<const char*>(static_cast<const T*>(a.dO) + size_t(h) * a.L * D);
+  // Direct loads of tile n into stage S. Query rows past the tile's valid count are loaded
+  // from row 0 (finite values; those queries get P = 0). Every wave issues PT loads: its
+  // share of the four tiles and two 256-byte rows (wave 0: lse, Δ; wave 1: gu, bias;
+  // wave 2: φ'; the others repeat the lse row into unused slots).
+  auto issue = [&](int n, auto sc) {
+    constexpr int S = decltype(sc)::value;
+    char* st = S == 0 ? sS0 : (S == 1 ? sS1 : sS2);
+    const uint32_t d = desc(n);
+    const int i = int(d & 0xFFFFu), m = int(d >> 16);
+    const size_t rowb = size_t(h) * a.L + size_t(i) * kB;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qb + size_t(i) * TB, TB), rg = make_rsrc(Gb + size_t(i) * TB, TB);
+    const __amdgpu_buffer_rsrc_t rqt = make_rsrc(a.qt + (size_t(h) * nb + i) * TB, TB);
+    const __amdgpu_buffer_rsrc_t rgt = make_rsrc(a.gt + (size_t(h) * nb + i) * TB, TB);
+#pragma unroll
+    for (int u = 0; u < DPW; ++u) {
+      const int ro = rrow[u] < m ? roff[u] : roff[u] - rrow[u] * KROW;
+      const int lb = (wave * DPW + u) * 1024;
+      buf_dma16(rq, ro, 0, st + lb);
+      buf_dma16(rg, ro, 0, st + TB + lb);
+      buf_dma16(rqt, toff[u], 0, st + 2 * TB + lb);
+      buf_dma16(rgt, toff[u], 0, st + 3 * TB + lb);
+    }
+    const float* lse_row = a.lse + rowb;
+    const float* r0 = lse_row;
+    const float* r1 = lse_row;
+    if (wave == 0) {
+      r1 = a.delta + rowb;
+    } else if (wave == 1) {
+      r0 = a.gu + rowb;
+      if (GROUP) r1 = a.vbias + (size_t(h) * nb + i) * a.nbp + j * kB;
+    } else if (wave == 2) {
+      if (GROUP && MODE == MODE_PWT) r0 = a.vdphi + (size_t(h) * nb + i) * a.nbp + j * kB;
+    }
+    auto row_dma = [&](const float* src, int slot) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(src, kB * 4),
+                                               (__attribute__((address_space(3))) void*)(st + RB + slot * kB * 4),
+                                               4, lane * 4, 0, 0, 0);
+    };
+    row_dma(r0, 2 * wave);
+    row_dma(r1, 2 * wave + 1);
+  };
+
+  // LDS byte offsets inside a stage of this lane's operand fragments and first query.
+  uint32_t rad[NKD], tad[NT];
+  const int Rq = 32 * wq + feed_row<M>(l32);       // query row this lane feeds
+#pragma unroll
+  for (int ks = 0; ks < NKD; ++ks) rad[ks] = KT::offset(Rq, (KI * ks + KH * g) * ES);
+#pragma unroll
+  for (int et = 0; et < NET; ++et)
+#pragma unroll
+    for (int ks = 0; ks < NKH; ++ks)
+      tad[et * NKH + ks] = TT::offset(32 * et + l32, (32 * wq + KI * ks + KH * g) * ES);
+  const int q0 = 32 * wq + acc_key<M>(0, 0, g);
+
+  auto compute = [&](int n, auto sc) {
+    constexpr int S = decltype(sc)::value;
+    const char* sk = S == 0 ? sS0 : (S == 1 ? sS1 : sS2);
+    const int m = int(desc(n) >> 16);
+    constexpr int NA = SPLIT ? NKD : 1, NTA = SPLIT ? NT : 1;
+    AB qa[NA], ga[NA], qta[NTA], gta[NTA];
+    float lse[16], del[16], gu[16], bias, dphi = 0.f;
+    const uint32_t base = lds_addr(sk);
+    if constexpr (SPLIT) {
+      static_assert(NKD == 4 || NKD == 8, "fragments per block");
+      uint32_t ad[NKD];
+      u32x4 r4[NKD], rv[NKD];
+#pragma unroll
+      for (int ks = 0; ks < NKD; ++ks) ad[ks] = base + rad[ks];
+      lds_read_x16<NKD, 0>(r4, ad);
+      lds_read_x16<NKD, TB>(rv, ad);
+#pragma unroll
+      for (int ks = 0; ks < NKD; ++ks) {
+        qa[ks] = __builtin_bit_cast(AB, r4[ks]);
+        ga[ks] = __builtin_bit_cast(AB, rv[ks]);
+      }
+      // queries q0 + {0..7, 16..23} of the lse, Δ and gu rows
+      u32x4 rb[8], rc[8];
+      lds_read8_at<0, 16, 64, 80, 256, 272, 320, 336>(rb, base + RB + q0 * 4);
+      lds_read8_at<512, 528, 576, 592, 768, 784, 1024, 1040>(rc, base + RB + q0 * 4);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = (r >> 3) * 2 + ((r >> 2) & 1);
+        lse[r] = __uint_as_float(rb[v][r & 3]);
+        del[r] = __uint_as_float(rb[4 + v][r & 3]);
+        gu[r] = __uint_as_float(rc[v][r & 3]);
+      }
+      // this lane's key: bias (slot 3) and φ' (slot 4), read above at q0-relative offsets
+      // would not cover it; read them directly.
+      bias = GROUP ? __uint_as_float(lds_read_u32(base + RB + 3 * kB * 4 + kcol * 4)) : 0.f;
+      if (GROUP && MODE == MODE_PWT) dphi = __uint_as_float(lds_read_u32(base + RB + 4 * kB * 4 + kcol * 4));
+    } else {
+      const float* rows = reinterpret_cast<const float*>(sk + RB);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = 32 * wq + acc_key<M>(0, r, g);
+        lse[r] = rows[q];
+        del[r] = rows[kB + q];
+        gu[r] = rows[2 * kB + q];
+      }
+      bias = GROUP ? rows[3 * kB + kcol] : 0.f;
+      if (GROUP && MODE == MODE_PWT) dphi = rows[4 * kB + kcol];
+    }
+    (void)dphi;
+    if (!GROUP) bias = kvalid ? 0.f : NEG_INF;
+    auto qfrag = [&](int ks) { return SPLIT ? qa[ks % NA] : M::load(reinterpret_cast<const T*>(sk + rad[ks])); };
+    auto gfrag = [&](int ks) { return SPLIT ? ga[ks % NA] : M::load(reinterpret_cast<const T*>(sk + TB + rad[ks])); };
     f32x16 s = zero16(), p = zero16();
 #pragma unroll
     for (int ks = 0; ks < NKD; ++ks) {
-      s = M::mma(M::load(sQ + Rq * LDK + KI * ks + KH * g), kf[ks], s);
-      p = M::mma(M::load(sG + Rq * LDK + KI * ks + KH * g), vf[ks], p);
+      s = M::mma(qfrag(ks), kf[ks], s);
+      p = M::mma(gfrag(ks), vf[ks], p);
     }
-    const float bias = GROUP ? sBias[kcol] : (kvalid ? 0.f : NEG_INF);
     f32x16 pr;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int q = 32 * wq + acc_key<M>(0, r, g);
-      const float P = fast_exp2(fmaf(s[r], kLog2e, bias) - sL[q]);
+      const float L2 = (q < m && lse[r] > NEG_INF) ? lse[r] * kLog2e : POS_INF;
+      const float P = fast_exp2(fmaf(s[r], kLog2e, bias) - L2);
       float dp = p[r];
-      if (GROUP) dp = fmaf(sU[q], invn, dp);
+      if (GROUP) dp = fmaf(gu[r], invn, dp);
       pr[r] = P;
-      s[r] = P * (dp - sD[q]);
+      s[r] = P * (dp - del[r]);
     }
     if constexpr (GROUP && MODE == MODE_PWT) {
-      // dw̃_{i,j} = φ'(w̃_{i,j}) Σ_{t in tile i} dℓ_{t,j}: column sums of dS over both query halves
+      // dw̃_{i,j} = φ'(w̃_{i,j}) Σ_{t in tile i} dℓ_{t,j}: column sums of dS over both query
+      // halves, exchanged through LDS (asm accesses and a barrier that keeps the ring's
+      // loads in flight).
       float cs = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) cs += s[r];
       cs = sum_halves(cs);
-      if (g == 0) sCol[wq][kcol] = cs;
-      __syncthreads();
-      if (tid < kB && j * kB + tid < nb)
-        a.dwt[(size_t(h) * nb + x) * nb + j * kB + tid] = sDphi[tid] * (sCol[0][tid] + sCol[1][tid]);
+      if (g == 0) lds_write_u32(lds_addr(&sCol[wq][kcol]), __float_as_uint(cs));
+      barrier_lgkm();
+      if (wave == 0) {
+        const float c0 = __uint_as_float(lds_read_u32(lds_addr(&sCol[0][lane])));
+        const float c1 = __uint_as_float(lds_read_u32(lds_addr(&sCol[1][lane])));
+        const float dph = SPLIT ? __uint_as_float(lds_read_u32(base + RB + 4 * kB * 4 + lane * 4))
+                                : reinterpret_cast<const float*>(sk + RB)[4 * kB + lane];
+        const int x = GROUP ? t0 + n : 0;
+        if (j * kB + lane < nb) a.dwt[(size_t(h) * nb + x) * nb + j * kB + lane] = dph * (c0 + c1);
+      }
     }
     f32x16 lo;                                     // dS as hi + lo bf16 parts (see bwd_query_kernel)
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (SPLIT) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float hi = to_f32(from_f32<T>(s[r]));
         lo[r] = s[r] - hi;
         s[r] = hi;
+      }
+      // Qᵀ and dOᵀ fragments, read once the score operands are dead
+      uint32_t adt[NT];
+      u32x4 rt[NT], ru[NT];
+#pragma unroll
+      for (int x = 0; x < NT; ++x) adt[x] = base + 2 * TB + tad[x];
+      lds_read_x16<NT, 0>(rt, adt);
+      lds_read_x16<NT, TB>(ru, adt);
+#pragma unroll
+      for (int x = 0; x < NT; ++x) {
+        qta[x] = __builtin_bit_cast(AB, rt[x]);
+        gta[x] = __builtin_bit_cast(AB, ru[x]);
       }
     }
     static_for<0, NKH>([&](auto ksc) {
@@ -869,22 +982,50 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
       const AB bs = M::template packv<ks * KH>(s);
 #pragma unroll
       for (int et = 0; et < NET; ++et) {
-        const int off = tix<T, LDT>(32 * et + l32, 32 * wq + KI * ks + KH * g);
-        dvt[et] = M::mma(M::load(sGt + off), bp, dvt[et]);
-        const AB qa = M::load(sQt + off);
-        dkt[et] = M::mma(qa, bs, dkt[et]);
-        if constexpr (sizeof(T) == 2) dkt[et] = M::mma(qa, M::template packv<ks * KH>(lo), dkt[et]);
+        const int x = et * NKH + ks;
+        const AB ga_t = SPLIT ? gta[x % NTA] : M::load(reinterpret_cast<const T*>(sk + 3 * TB + tad[x]));
+        const AB qa_t = SPLIT ? qta[x % NTA] : M::load(reinterpret_cast<const T*>(sk + 2 * TB + tad[x]));
+        dvt[et] = M::mma(ga_t, bp, dvt[et]);
+        dkt[et] = M::mma(qa_t, bs, dkt[et]);
+        if constexpr (SPLIT) dkt[et] = M::mma(qa_t, M::template packv<ks * KH>(lo), dkt[et]);
+      }
+    });
+  };
+
+  if (N > 0) fill_desc(0);
+  if (N > DCH) fill_desc(1);
+  __syncthreads();
+  // Prologue: tiles [0, NST - 1) in flight (tile 0 with a single stage).
+  static_for<0, (NST > 1 ? NST - 1 : 1)>([&](auto sc) {
+    if (decltype(sc)::value < N) issue(decltype(sc)::value, sc);
+  });
+  for (int n0 = 0; n0 < N; n0 += NST) {
+    static_for<0, NST>([&](auto sc) {
+      constexpr int S = decltype(sc)::value;
+      const int n = n0 + S;
+      if (n < N) {
+        // Tile n has landed once at most the loads issued after it are outstanding (the
+        // next tile's, and a dw̃ store); after the barrier everyone's have, and the stage
+        // of tile n - 1 is free.
+        if (NST == 3 && n + 1 < N) barrier_vm<PT>();
+        else barrier_vm<0>();
+        if (n % DCH == 0 && n >= DCH && n + DCH < N) fill_desc(n / DCH + 1);
+        if (NST > 1 && n + NST - 1 < N) issue(n + NST - 1, std::integral_constant<int, (S + NST - 1) % NST>{});
+        compute(n, sc);
+        if (NST == 1) {
+          __syncthreads();
+          if (n + 1 < N) issue(n + 1, sc);
+        }
       }
     });
   }
-  (void)lnn;
 
   // Merge the query halves: wave (1, wk) hands over to wave (0, wk).
   constexpr int XF = 2 * NET * 16 * 64;            // floats handed over per wave
-  static_assert(2 * XF * 4 <= 2 * TK + 2 * TT, "hand-over buffer");
+  static_assert(2 * XF * 4 <= SB, "hand-over buffer");
   __syncthreads();
   if (wq == 1) {
-    float* mine = reinterpret_cast<float*>(lds) + wk * XF + lane;
+    float* mine = reinterpret_cast<float*>(sS0) + wk * XF + lane;
 #pragma unroll
     for (int et = 0; et < NET; ++et)
 #pragma unroll
@@ -895,7 +1036,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   }
   __syncthreads();
   if (wq == 1) return;
-  const float* other = reinterpret_cast<const float*>(lds) + wk * XF + lane;
+  const float* other = reinterpret_cast<const float*>(sS0) + wk * XF + lane;
 #pragma unroll
   for (int et = 0; et < NET; ++et)
 #pragma unroll
@@ -1129,7 +1270,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   } while (0)
   hipLaunchKernelGGL((bwd_rows_kernel<T, D>), tiles, dim3(256), 0, s, a);
   PISA_CHECK();
-  hipLaunchKernelGGL((bwd_pack_kernel<T, D>), dim3(a.nb, a.H, MODE == MODE_DROP ? 1 : 2), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bwd_pack_kernel<T, D>), dim3(a.nb, a.H, MODE == MODE_DROP ? 2 : 3), dim3(256), 0, s, a);
   PISA_CHECK();
   if (MODE != MODE_DROP) {
     hipLaunchKernelGGL((bwd_bias_kernel<MODE>), dim3(a.nb, a.H), dim3(256), 0, s, a);

@@ -140,7 +140,10 @@ struct BwdArgs {
   char* kbr;         // k̄ rows of each centroid group
   char* kbt;         // k̄ᵀ of each centroid group
   char* vbr;         // v̄ = ΣV / n rows of each centroid group
+  char* qt;          // Qᵀ of each query tile
+  char* gt;          // dOᵀ of each query tile
   float* vbias;      // [H][nb][nbp] log2-domain bias of each virtual token (-inf: excluded)
+  float* vdphi;      // [H][nb][nbp] φ'(w̃) of each virtual token (0: excluded or gated)
   float* vinvn;      // [nbp] 1 / n_j (0 past nb)
   int H, L, d, nb, nbp, K_sel, nw, nchunk, nhch;
   int w_linear, gate;
@@ -148,7 +151,7 @@ struct BwdArgs {
 
 struct BwdLayout {
   size_t delta, gu, abar, qsq, dwt, dsig2, dkp, dvp, dhp, dh, off, list;
-  size_t kt, kbr, kbt, vbr, vbias, vinvn, total;
+  size_t kt, kbr, kbt, vbr, qt, gt, vbias, vdphi, vinvn, total;
   int nchunk, nhch;
 };
 
@@ -178,7 +181,10 @@ inline BwdLayout bwd_layout(size_t elem, int H, int L, int d, int K_sel) {
   w.kbr = o;   o = align256(o + groups);
   w.kbt = o;   o = align256(o + groups);
   w.vbr = o;   o = align256(o + groups);
+  w.qt = o;    o = align256(o + tiles);
+  w.gt = o;    o = align256(o + tiles);
   w.vbias = o; o = align256(o + Hs * nb * nbp * f);
+  w.vdphi = o; o = align256(o + Hs * nb * nbp * f);
   w.vinvn = o; o = align256(o + size_t(nbp) * f);
   w.total = o;
   return w;
