@@ -364,6 +364,7 @@ pisa_status pisa_attention_bwd(pisa_dtype dt, const void* Q, const void* K, cons
   a.qsq = base == PISA_MODE_PWT ? reinterpret_cast<float*>(ws + w.qsq) : nullptr;
   a.dwt = reinterpret_cast<float*>(ws + w.dwt);
   a.dsig2 = reinterpret_cast<float*>(ws + w.dsig2);
+  a.dqsq = reinterpret_cast<float*>(ws + w.dqsq);
   a.dkbar_part = reinterpret_cast<float*>(ws + w.dkp);
   a.dvbar_part = reinterpret_cast<float*>(ws + w.dvp);
   a.dh_part = reinterpret_cast<float*>(ws + w.dhp);

@@ -25,7 +25,8 @@
 //                        selected it; per centroid group and chunk of query tiles: dk̄, dv̄
 //                        and (PWT) dw̃
 //   bwd_dh_kernel + bwd_dh_reduce_kernel: dH̄
-//   bwd_wprod_kernel     dQ += the pooled-q² term; dσ²_j (products with dw̃)
+//   bwd_wprod_kernel     the products with dw̃: dqsq_i and dσ²_j
+//   bwd_qsq_kernel       dQ += the pooled-q² term
 //   bwd_chain_kernel     per key block: the statistics' gradients onto its tokens
 // The 64 x 64 products run on MFMA with operands staged in LDS (bf16 MFMA with fp32
 // accumulation for bf16 inputs; P and dS enter their products in bf16, as the forward
@@ -139,50 +140,129 @@ __device__ __forceinline__ uint32_t lds_read_u32(uint32_t ad) {
 // read from H̄ᵀ, B = the staged Q rows), so each lane holds one query's column and the
 // dot with dO needs no cross-lane sum; wave w takes query half w & 1 and every other
 // 32-row tile of e.
+// bf16 inputs: ROWS_G query tiles per workgroup share H̄ staged once in LDS as hi + lo bf16
+// parts; u = H̄ q on bf16 MFMA (q exact in bf16, so the products lose nothing), gu = dO·u.
+constexpr int ROWS_G = 8;
+template <int D>
+__device__ __forceinline__ void rows_bf16(const BwdArgs& a) {
+  constexpr int NE = D / 32, NKD = D / 16, LDH = D + 8;
+  __shared__ __align__(16) uint16_t sHh[D * LDH], sHl[D * LDH];
+  __shared__ float part[4][32];
+  const int h = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const float* hT = a.hbarT + size_t(h) * D * D;
+  for (int x = tid; x < D * D; x += 256) {         // H̄[e][c] = H̄ᵀ[c][e]
+    const int c = x / D, e = x % D;
+    const float f = hT[x];
+    const uint16_t hi = from_f32<uint16_t>(f);
+    sHh[e * LDH + c] = hi;
+    sHl[e * LDH + c] = from_f32<uint16_t>(f - to_f32(hi));
+  }
+  __syncthreads();
+  const uint16_t* Qh = static_cast<const uint16_t*>(a.Q);
+  const uint16_t* Gh = static_cast<const uint16_t*>(a.dO);
+  const int tq = wave & 1, t = 32 * tq + l32;
+  for (int i = blockIdx.x * ROWS_G; i < min(a.nb, blockIdx.x * ROWS_G + ROWS_G); ++i) {
+    const int m = min(max(a.block_len ? a.block_len[i] : kB, 1), kB);
+    const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
+    if (a.qsq && tid < D) {
+      float s = 0.f;
+#pragma unroll 8
+      for (int r = 0; r < m; ++r) {
+        const float q = to_f32(Qh[(row0 + r) * D + tid]);
+        s = fmaf(q, q, s);
+      }
+      a.qsq[(size_t(h) * a.nb + i) * D + tid] = s / float(m);
+    }
+    bf16x8 qf[NKD];
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks)
+      qf[ks] = t < m ? *reinterpret_cast<const bf16x8*>(Qh + (row0 + t) * D + 16 * ks + 8 * g) : MmaBF16::zero();
+    float gu = 0.f;
+    for (int et = wave >> 1; et < NE; et += 2) {
+      f32x16 u = zero16();
+      const uint16_t* hr = sHh + (32 * et + l32) * LDH + 8 * g;
+      const uint16_t* lr = sHl + (32 * et + l32) * LDH + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < NKD; ++ks) {
+        u = MmaBF16::mma(*reinterpret_cast<const bf16x8*>(hr + 16 * ks), qf[ks], u);
+        u = MmaBF16::mma(*reinterpret_cast<const bf16x8*>(lr + 16 * ks), qf[ks], u);
+      }
+      if (t < m) {
+        // dO[t][e] for e = 32 et + acc_row(r, g): four runs of four
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const uint2 w = *reinterpret_cast<const uint2*>(Gh + (row0 + t) * D + 32 * et + 8 * q4 + 4 * g);
+          const float d0 = __uint_as_float(w.x << 16), d1 = __uint_as_float(w.x & 0xFFFF0000u);
+          const float d2 = __uint_as_float(w.y << 16), d3 = __uint_as_float(w.y & 0xFFFF0000u);
+          gu = fmaf(d0, u[4 * q4 + 0], gu);
+          gu = fmaf(d1, u[4 * q4 + 1], gu);
+          gu = fmaf(d2, u[4 * q4 + 2], gu);
+          gu = fmaf(d3, u[4 * q4 + 3], gu);
+        }
+      }
+    }
+    gu = sum_halves(gu);
+    __syncthreads();                               // previous tile's part[] read
+    if (g == 0) part[wave][l32] = gu;
+    __syncthreads();
+    if (tid < kB) {
+      const float l = a.lse[row0 + tid];
+      const bool live = tid < m && l > NEG_INF;
+      const int q = tid >> 5, r = tid & 31;
+      a.gu[row0 + tid] = live ? part[q][r] + part[q + 2][r] : 0.f;
+    }
+  }
+}
+
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
-  constexpr int NE = D / 32;
-  __shared__ float sq[kB][D + 1], sg[kB][D + 1];
-  __shared__ float part[4][32];
-  const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
-  int m = a.block_len ? a.block_len[i] : kB;
-  m = min(max(m, 1), kB);
-  const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
-  const T* Qt = static_cast<const T*>(a.Q) + row0 * D;
-  const T* Gt = static_cast<const T*>(a.dO) + row0 * D;
-  for (int x = tid; x < kB * D; x += 256) {
-    const bool ok = (x / D) < m;
-    sq[x / D][x % D] = ok ? to_f32(Qt[x]) : 0.f;
-    sg[x / D][x % D] = ok ? to_f32(Gt[x]) : 0.f;
-  }
-  __syncthreads();
-  if (a.qsq && tid < D) {
-    float s = 0.f;
-    for (int r = 0; r < m; ++r) s = fmaf(sq[r][tid], sq[r][tid], s);
-    a.qsq[(size_t(h) * a.nb + i) * D + tid] = s / float(m);
-  }
-  const float* hT = a.hbarT + size_t(h) * D * D;
-  const int tq = wave & 1, t = 32 * tq + l32;
-  float gu = 0.f;
-  for (int et = wave >> 1; et < NE; et += 2) {
-    f32x16 u = zero16();
-#pragma unroll 8
-    for (int ks = 0; ks < D / 2; ++ks) {
-      const int c = 2 * ks + g;
-      u = __builtin_amdgcn_mfma_f32_32x32x2f32(hT[size_t(c) * D + 32 * et + l32], sq[t][c], u, 0, 0, 0);
+  if constexpr (sizeof(T) == 2) {
+    rows_bf16<D>(a);
+  } else {
+    constexpr int NE = D / 32;
+    __shared__ float sq[kB][D + 1], sg[kB][D + 1];
+    __shared__ float part[4][32];
+    const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+    int m = a.block_len ? a.block_len[i] : kB;
+    m = min(max(m, 1), kB);
+    const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
+    const T* Qt = static_cast<const T*>(a.Q) + row0 * D;
+    const T* Gt = static_cast<const T*>(a.dO) + row0 * D;
+    for (int x = tid; x < kB * D; x += 256) {
+      const bool ok = (x / D) < m;
+      sq[x / D][x % D] = ok ? to_f32(Qt[x]) : 0.f;
+      sg[x / D][x % D] = ok ? to_f32(Gt[x]) : 0.f;
     }
+    __syncthreads();
+    if (a.qsq && tid < D) {
+      float s = 0.f;
+      for (int r = 0; r < m; ++r) s = fmaf(sq[r][tid], sq[r][tid], s);
+      a.qsq[(size_t(h) * a.nb + i) * D + tid] = s / float(m);
+    }
+    const float* hT = a.hbarT + size_t(h) * D * D;
+    const int tq = wave & 1, t = 32 * tq + l32;
+    float gu = 0.f;
+    for (int et = wave >> 1; et < NE; et += 2) {
+      f32x16 u = zero16();
+#pragma unroll 8
+      for (int ks = 0; ks < D / 2; ++ks) {
+        const int c = 2 * ks + g;
+        u = __builtin_amdgcn_mfma_f32_32x32x2f32(hT[size_t(c) * D + 32 * et + l32], sq[t][c], u, 0, 0, 0);
+      }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) gu = fmaf(sg[t][32 * et + acc_row(r, g)], u[r], gu);
-  }
-  gu = sum_halves(gu);
-  if (g == 0) part[wave][l32] = gu;
-  __syncthreads();
-  if (tid < kB) {
-    const float l = a.lse[row0 + tid];
-    const bool live = tid < m && l > NEG_INF;
-    const int q = tid >> 5, r = tid & 31;
-    a.gu[row0 + tid] = live ? part[q][r] + part[q + 2][r] : 0.f;
+      for (int r = 0; r < 16; ++r) gu = fmaf(sg[t][32 * et + acc_row(r, g)], u[r], gu);
+    }
+    gu = sum_halves(gu);
+    if (g == 0) part[wave][l32] = gu;
+    __syncthreads();
+    if (tid < kB) {
+      const float l = a.lse[row0 + tid];
+      const bool live = tid < m && l > NEG_INF;
+      const int q = tid >> 5, r = tid & 31;
+      a.gu[row0 + tid] = live ? part[q][r] + part[q + 2][r] : 0.f;
+    }
   }
 }
 
@@ -875,6 +955,37 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
     AB qa[NA], ga[NA], qta[NTA], gta[NTA];
     float lse[16], del[16], gu[16], bias, dphi = 0.f;
     const uint32_t base = lds_addr(sk);
+    // Row statistics of this lane's queries q0 + {0..7, 16..23} (lse, Δ, gu) and this
+    // lane's key's bias and φ'. Centroid groups read them while the score products run
+    // (fenced there, measured faster); exact blocks before them.
+    auto read_rows = [&]() {
+      if constexpr (SPLIT) {
+        u32x4 rb[8], rc[8];
+        lds_read8_at<0, 16, 64, 80, 256, 272, 320, 336>(rb, base + RB + q0 * 4);
+        lds_read8_at<512, 528, 576, 592, 768, 784, 1024, 1040>(rc, base + RB + q0 * 4);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int v = (r >> 3) * 2 + ((r >> 2) & 1);
+          lse[r] = __uint_as_float(rb[v][r & 3]);
+          del[r] = __uint_as_float(rb[4 + v][r & 3]);
+          gu[r] = __uint_as_float(rc[v][r & 3]);
+        }
+        bias = GROUP ? __uint_as_float(lds_read_u32(base + RB + 3 * kB * 4 + kcol * 4)) : 0.f;
+        if (GROUP && MODE == MODE_PWT) dphi = __uint_as_float(lds_read_u32(base + RB + 4 * kB * 4 + kcol * 4));
+      } else {
+        const float* rows = reinterpret_cast<const float*>(sk + RB);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = 32 * wq + acc_key<M>(0, r, g);
+          lse[r] = rows[q];
+          del[r] = rows[kB + q];
+          gu[r] = rows[2 * kB + q];
+        }
+        bias = GROUP ? rows[3 * kB + kcol] : 0.f;
+        if (GROUP && MODE == MODE_PWT) dphi = rows[4 * kB + kcol];
+      }
+    };
+    constexpr bool LATE = SPLIT && GROUP;
     if constexpr (SPLIT) {
       static_assert(NKD == 4 || NKD == 8, "fragments per block");
       uint32_t ad[NKD];
@@ -888,7 +999,18 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
         qa[ks] = __builtin_bit_cast(AB, r4[ks]);
         ga[ks] = __builtin_bit_cast(AB, rv[ks]);
       }
-      // queries q0 + {0..7, 16..23} of the lse, Δ and gu rows
+    }
+    if constexpr (!LATE) read_rows();
+    auto qfrag = [&](int ks) { return SPLIT ? qa[ks % NA] : M::load(reinterpret_cast<const T*>(sk + rad[ks])); };
+    auto gfrag = [&](int ks) { return SPLIT ? ga[ks % NA] : M::load(reinterpret_cast<const T*>(sk + TB + rad[ks])); };
+    f32x16 s = zero16(), p = zero16();
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks) {
+      s = M::mma(qfrag(ks), kf[ks], s);
+      p = M::mma(gfrag(ks), vf[ks], p);
+    }
+    if constexpr (LATE) {
+      __builtin_amdgcn_sched_barrier(0);
       u32x4 rb[8], rc[8];
       lds_read8_at<0, 16, 64, 80, 256, 272, 320, 336>(rb, base + RB + q0 * 4);
       lds_read8_at<512, 528, 576, 592, 768, 784, 1024, 1040>(rc, base + RB + q0 * 4);
@@ -899,32 +1021,12 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
         del[r] = __uint_as_float(rb[4 + v][r & 3]);
         gu[r] = __uint_as_float(rc[v][r & 3]);
       }
-      // this lane's key: bias (slot 3) and φ' (slot 4), read above at q0-relative offsets
-      // would not cover it; read them directly.
-      bias = GROUP ? __uint_as_float(lds_read_u32(base + RB + 3 * kB * 4 + kcol * 4)) : 0.f;
-      if (GROUP && MODE == MODE_PWT) dphi = __uint_as_float(lds_read_u32(base + RB + 4 * kB * 4 + kcol * 4));
-    } else {
-      const float* rows = reinterpret_cast<const float*>(sk + RB);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = 32 * wq + acc_key<M>(0, r, g);
-        lse[r] = rows[q];
-        del[r] = rows[kB + q];
-        gu[r] = rows[2 * kB + q];
-      }
-      bias = GROUP ? rows[3 * kB + kcol] : 0.f;
-      if (GROUP && MODE == MODE_PWT) dphi = rows[4 * kB + kcol];
+      bias = __uint_as_float(lds_read_u32(base + RB + 3 * kB * 4 + kcol * 4));
+      if (MODE == MODE_PWT) dphi = __uint_as_float(lds_read_u32(base + RB + 4 * kB * 4 + kcol * 4));
+      __builtin_amdgcn_sched_barrier(0);
     }
     (void)dphi;
     if (!GROUP) bias = kvalid ? 0.f : NEG_INF;
-    auto qfrag = [&](int ks) { return SPLIT ? qa[ks % NA] : M::load(reinterpret_cast<const T*>(sk + rad[ks])); };
-    auto gfrag = [&](int ks) { return SPLIT ? ga[ks % NA] : M::load(reinterpret_cast<const T*>(sk + TB + rad[ks])); };
-    f32x16 s = zero16(), p = zero16();
-#pragma unroll
-    for (int ks = 0; ks < NKD; ++ks) {
-      s = M::mma(qfrag(ks), kf[ks], s);
-      p = M::mma(gfrag(ks), vf[ks], p);
-    }
     f32x16 pr;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -1070,43 +1172,128 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
 // dH̄[e][c] = Σ_t Ā_t dO_t[e] q_t[c]: per (head, chunk of query tiles) a d x d partial on the
 // fp32 matrix cores (A = (Ā dO)ᵀ, B = Q, contraction over the rows; wave w owns every
 // fourth 32 x 32 output tile), then a fixed-order reduction over the chunks.
-template <class T, int D>
-__global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
-  constexpr int NE = D / 32, NTW = NE * NE / 4;
-  __shared__ float sg[kB][D + 1], sq[kB][D + 1];
+// bf16 inputs: bf16 MFMA over the packed dOᵀ and Qᵀ tiles, the contraction over the tile's
+// 64 rows; A = (Ā dO)ᵀ formed in fp32 and entered as hi + lo bf16 parts, B = Qᵀ (exact), so
+// the sums lose nothing to the bf16 operands. Operands come straight from global memory,
+// the next tile's in flight while the current one is multiplied.
+template <int D>
+__device__ __forceinline__ void dh_bf16(const BwdArgs& a) {
+  constexpr int NE = D / 32, NTW = NE * NE / 4, NKS = kB / 16;
+  constexpr int NA = 1, NB = NTW;                  // one A row tile and NTW column tiles per wave
+  static_assert(NTW <= NE && NE % NTW == 0, "wave tiling");
   const int h = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int per = (a.nb + a.nhch - 1) / a.nhch;
   const int i0 = min(a.nb, ch * per), i1 = min(a.nb, i0 + per);
-  f32x16 acc[NTW];
+  // output tiles of this wave: (et, ct) = (ea + x, cb + y), x < NA, y < NB
+  const int ea = (wave * NTW) / NE, cb = (wave * NTW) % NE;
+  f32x16 acc[NA][NB];
 #pragma unroll
-  for (int u = 0; u < NTW; ++u) acc[u] = zero16();
-  for (int i = i0; i < i1; ++i) {
-    const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
-    __syncthreads();
-    for (int x = tid; x < kB * D; x += 256) {
-      const int r = x / D, c = x % D;
-      const float ab = a.abar[row0 + r];
-      sg[r][c] = ab * to_f32(static_cast<const T*>(a.dO)[(row0 + r) * D + c]);
-      sq[r][c] = ab != 0.f ? to_f32(static_cast<const T*>(a.Q)[(row0 + r) * D + c]) : 0.f;
+  for (int x = 0; x < NA; ++x)
+#pragma unroll
+    for (int y = 0; y < NB; ++y) acc[x][y] = zero16();
+  const size_t TE = size_t(kB) * D;
+  const uint16_t* gt = reinterpret_cast<const uint16_t*>(a.gt) + size_t(h) * a.nb * TE;
+  const uint16_t* qt = reinterpret_cast<const uint16_t*>(a.qt) + size_t(h) * a.nb * TE;
+  u32x4 ga[2][NKS][NA], qb[2][NKS][NB];
+  float4 ab[2][NKS][2];
+  auto load = [&](int i, int buf) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int t = 16 * ks + 8 * g;
+#pragma unroll
+      for (int x = 0; x < NA; ++x)
+        ga[buf][ks][x] = *reinterpret_cast<const u32x4*>(gt + size_t(i) * TE + size_t(32 * (ea + x) + l32) * kB + t);
+#pragma unroll
+      for (int y = 0; y < NB; ++y)
+        qb[buf][ks][y] = *reinterpret_cast<const u32x4*>(qt + size_t(i) * TE + size_t(32 * (cb + y) + l32) * kB + t);
+      const float4* ap = reinterpret_cast<const float4*>(a.abar + size_t(h) * a.L + size_t(i) * kB + t);
+      ab[buf][ks][0] = ap[0];
+      ab[buf][ks][1] = ap[1];
     }
-    __syncthreads();
+  };
+  if (i0 < i1) load(i0, 0);
+  for (int i = i0; i < i1; i += 2) {
+    static_for<0, 2>([&](auto bc) {
+      constexpr int B = decltype(bc)::value;
+      if (i + B < i1) {
+        if (i + B + 1 < i1) load(i + B + 1, B ^ 1);
 #pragma unroll
-    for (int u = 0; u < NTW; ++u) {
-      const int tile = wave * NTW + u, et = tile / NE, ct = tile % NE;
-#pragma unroll 8
-      for (int ks = 0; ks < kB / 2; ++ks) {
-        const int t = 2 * ks + g;
-        acc[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(sg[t][32 * et + l32], sq[t][32 * ct + l32], acc[u], 0, 0, 0);
+        for (int ks = 0; ks < NKS; ++ks) {
+          const float av[8] = {ab[B][ks][0].x, ab[B][ks][0].y, ab[B][ks][0].z, ab[B][ks][0].w,
+                               ab[B][ks][1].x, ab[B][ks][1].y, ab[B][ks][1].z, ab[B][ks][1].w};
+#pragma unroll
+          for (int x = 0; x < NA; ++x) {
+            const uint16_t* gv = reinterpret_cast<const uint16_t*>(&ga[B][ks][x]);
+            float hi[8], lo[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const float f = av[u] * to_f32(gv[u]);
+              hi[u] = to_f32(from_f32<uint16_t>(f));
+              lo[u] = f - hi[u];
+            }
+            const bf16x8 ah = MmaBF16::pack(hi), al = MmaBF16::pack(lo);
+#pragma unroll
+            for (int y = 0; y < NB; ++y) {
+              const bf16x8 bq = __builtin_bit_cast(bf16x8, qb[B][ks][y]);
+              acc[x][y] = MmaBF16::mma(ah, bq, acc[x][y]);
+              acc[x][y] = MmaBF16::mma(al, bq, acc[x][y]);
+            }
+          }
+        }
       }
-    }
+    });
   }
   float* out = a.dh_part + (size_t(h) * a.nhch + ch) * D * D;
 #pragma unroll
-  for (int u = 0; u < NTW; ++u) {
-    const int tile = wave * NTW + u, et = tile / NE, ct = tile % NE;
+  for (int x = 0; x < NA; ++x)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) out[(32 * et + acc_row(r, g)) * D + 32 * ct + l32] = acc[u][r];
+    for (int y = 0; y < NB; ++y)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) out[(32 * (ea + x) + acc_row(r, g)) * D + 32 * (cb + y) + l32] = acc[x][y][r];
+}
+
+template <class T, int D>
+__global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
+  if constexpr (sizeof(T) == 2) {
+    dh_bf16<D>(a);
+  } else {
+    constexpr int NE = D / 32, NTW = NE * NE / 4;
+    __shared__ float sg[kB][D + 1], sq[kB][D + 1];
+    const int h = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+    const int per = (a.nb + a.nhch - 1) / a.nhch;
+    const int i0 = min(a.nb, ch * per), i1 = min(a.nb, i0 + per);
+    f32x16 acc[NTW];
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) acc[u] = zero16();
+    for (int i = i0; i < i1; ++i) {
+      const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
+      __syncthreads();
+      for (int x = tid; x < kB * D; x += 256) {
+        const int r = x / D, c = x % D;
+        const float ab = a.abar[row0 + r];
+        sg[r][c] = ab * to_f32(static_cast<const T*>(a.dO)[(row0 + r) * D + c]);
+        sq[r][c] = ab != 0.f ? to_f32(static_cast<const T*>(a.Q)[(row0 + r) * D + c]) : 0.f;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < NTW; ++u) {
+        const int tile = wave * NTW + u, et = tile / NE, ct = tile % NE;
+#pragma unroll 8
+        for (int ks = 0; ks < kB / 2; ++ks) {
+          const int t = 2 * ks + g;
+          acc[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(sg[t][32 * et + l32], sq[t][32 * ct + l32], acc[u], 0, 0, 0);
+        }
+      }
+    }
+    float* out = a.dh_part + (size_t(h) * a.nhch + ch) * D * D;
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) {
+      const int tile = wave * NTW + u, et = tile / NE, ct = tile % NE;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) out[(32 * et + acc_row(r, g)) * D + 32 * ct + l32] = acc[u][r];
+    }
   }
 }
 
@@ -1122,7 +1309,7 @@ __global__ __launch_bounds__(256) void bwd_dh_reduce_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------------------
 // PWT: the two products with dw̃ [nb x nb], on the fp32 matrix cores, one 64-row by d
 // output block per workgroup (4 waves, contraction over 64-wide chunks staged in LDS):
-//   TRANS = false: dqsq_i = ½ Σ_j dw̃_{i,j} σ²_j, then dq_t += (2/m_i) q_t ∘ dqsq_i
+//   TRANS = false: dqsq_i = ½ Σ_j dw̃_{i,j} σ²_j (applied to dQ by bwd_qsq_kernel)
 //   TRANS = true:  dσ²_j = ½ Σ_i dw̃_{i,j} \overline{q²}_i
 template <class T, int D, bool TRANS>
 __global__ __launch_bounds__(256) void bwd_wprod_kernel(BwdArgs a) {
@@ -1167,24 +1354,46 @@ __global__ __launch_bounds__(256) void bwd_wprod_kernel(BwdArgs a) {
     for (int r = 0; r < 16; ++r) sOut[32 * rt + acc_row(r, g)][32 * ct + l32] = 0.5f * acc[u][r];
   }
   __syncthreads();
-  if (TRANS) {
-    for (int x = tid; x < kB * D; x += 256) {
-      const int r = x / D, c = x % D;
-      if (r0 + r < nb) a.dsig2[(size_t(h) * nb + r0 + r) * D + c] = sOut[r][c];
-    }
-  } else {
-    // dq_t += (2/m_i) q_t ∘ dqsq_i for the valid rows of every tile i of this block
-    for (int r = 0; r < kB && r0 + r < nb; ++r) {
-      const int i = r0 + r;
-      const int m = min(max(a.block_len ? a.block_len[i] : kB, 1), kB);
-      const float sc = 2.f / float(m);
-      const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
-      for (int x = tid; x < m * D; x += 256) {
-        const int t = x / D, c = x % D;
-        a.dQ[(row0 + t) * D + c] += sc * sOut[r][c] * to_f32(static_cast<const T*>(a.Q)[(row0 + t) * D + c]);
-      }
-    }
+  float* out = TRANS ? a.dsig2 : a.dqsq;
+  for (int x = tid; x < kB * D; x += 256) {
+    const int r = x / D, c = x % D;
+    if (r0 + r < nb) out[(size_t(h) * nb + r0 + r) * D + c] = sOut[r][c];
   }
+}
+
+// dq_t += (2/m_i) q_t ∘ dqsq_i on the valid rows of every query tile (PWT), four elements
+// per thread.
+template <class T, int D>
+__global__ __launch_bounds__(256) void bwd_qsq_kernel(BwdArgs a) {
+  const size_t x = (size_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  const size_t total = size_t(a.H) * a.L * D;
+  if (x >= total) return;
+  const size_t row = x / D;                        // h * L + token
+  const int c = int(x % D);
+  const int h = int(row / size_t(a.L)), tok = int(row % size_t(a.L));
+  const int i = tok / kB, r = tok % kB;
+  const int m = min(max(a.block_len ? a.block_len[i] : kB, 1), kB);
+  if (r >= m) return;
+  const float sc = 2.f / float(m);
+  const float4 w = *reinterpret_cast<const float4*>(a.dqsq + (size_t(h) * a.nb + i) * D + c);
+  float q[4];
+  if constexpr (sizeof(T) == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.Q) + x);
+    q[0] = __uint_as_float(v.x << 16);
+    q[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    q[2] = __uint_as_float(v.y << 16);
+    q[3] = __uint_as_float(v.y & 0xFFFF0000u);
+  } else {
+    const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(a.Q) + x);
+    q[0] = v.x; q[1] = v.y; q[2] = v.z; q[3] = v.w;
+  }
+  float4* dq = reinterpret_cast<float4*>(a.dQ + x);
+  float4 d = *dq;
+  d.x += sc * w.x * q[0];
+  d.y += sc * w.y * q[1];
+  d.z += sc * w.z * q[2];
+  d.w += sc * w.w * q[3];
+  *dq = d;
 }
 
 constexpr int CHAIN_G = 8;                         // key blocks per workgroup of bwd_chain_kernel
@@ -1192,7 +1401,8 @@ constexpr int CHAIN_G = 8;                         // key blocks per workgroup o
 // ---------------------------------------------------------------------------------------
 // Per key block: the statistics' gradients onto its valid tokens (adds to dK, dV). The two
 // d x d products run on the fp32 matrix cores with dH̄ / nb and the centred tokens staged in
-// LDS: dKᵀ[c][t] += Σ_e dH̄[e][c] (v_t - v̄)[e], dVᵀ[e][t] += Σ_c dH̄[e][c] (k_t - k̄)[c].
+// LDS: dK[t][c] += Σ_e (v_t - v̄)[e] dH̄[e][c], dV[t][e] += Σ_c (k_t - k̄)[c] dH̄[e][c]; the
+// output columns run along the lanes, so the updates of dK and dV are row-contiguous.
 template <class T, int D, int MODE>
 __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a) {
   constexpr int NE = D / 32;
@@ -1234,26 +1444,37 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a) {
     sVd[t][c] = ok ? to_f32(Vb[x]) - svb[c] : 0.f;
   }
   __syncthreads();
-  const int tt = wave & 1, t = 32 * tt + l32;
-  const bool tok = t < n;
+  // wave: token half tt (rows 32 tt + [0, 32)), output column tiles xt = wave / 2, + 2
+  const int tt = wave & 1;
   for (int xt = wave >> 1; xt < NE; xt += 2) {
     f32x16 ak = zero16(), av = zero16();
+    const int col = 32 * xt + l32;
 #pragma unroll 8
     for (int ks = 0; ks < D / 2; ++ks) {
       const int k = 2 * ks + g;
-      // dKᵀ: A(row c = 32 xt + l32, k = e) = dH̄[e][c];  dVᵀ: A(row e = 32 xt + l32, k = c) = dH̄[e][c]
-      ak = __builtin_amdgcn_mfma_f32_32x32x2f32(sH[k][32 * xt + l32], sVd[t][k], ak, 0, 0, 0);
-      av = __builtin_amdgcn_mfma_f32_32x32x2f32(sH[32 * xt + l32][k], sKd[t][k], av, 0, 0, 0);
+      // dK: A(row t, k = e) = (v - v̄)[t][e], B(k = e, col c) = dH̄[e][c]
+      // dV: A(row t, k = c) = (k - k̄)[t][c], B(k = c, col e) = dH̄[e][c]
+      ak = __builtin_amdgcn_mfma_f32_32x32x2f32(sVd[32 * tt + l32][k], sH[k][col], ak, 0, 0, 0);
+      av = __builtin_amdgcn_mfma_f32_32x32x2f32(sKd[32 * tt + l32][k], sH[col][k], av, 0, 0, 0);
     }
-    if (tok) {
-      float* dk = a.dK + (row0 + t) * D;
-      float* dv = a.dV + (row0 + t) * D;
+    const float dkc = sdk[col], dvc = sdv[col], dsc = sdsig[col];
+    // Branch-free, so all 32 loads of the update are in flight together; padding rows
+    // (zeros from the key sweep) receive + 0.
+    float xk[16], xv[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c = 32 * xt + acc_row(r, g);
-        dk[c] += sdk[c] + sKd[t][c] * sdsig[c] + ak[r];
-        dv[c] += sdv[c] + av[r];
-      }
+    for (int r = 0; r < 16; ++r) {
+      const size_t o = (row0 + 32 * tt + acc_row(r, g)) * D + col;
+      xk[r] = a.dK[o];
+      xv[r] = a.dV[o];
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = 32 * tt + acc_row(r, g);
+      const bool on = t < n;
+      const size_t o = (row0 + t) * D + col;
+      const float uk = xk[r] + (dkc + sKd[t][col] * dsc + ak[r]), uv = xv[r] + (dvc + av[r]);
+      a.dK[o] = on ? uk : xk[r];
+      a.dV[o] = on ? uv : xv[r];
     }
   }
   }
@@ -1268,7 +1489,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
     hipError_t e_ = hipGetLastError();           \
     if (e_ != hipSuccess) return e_;             \
   } while (0)
-  hipLaunchKernelGGL((bwd_rows_kernel<T, D>), tiles, dim3(256), 0, s, a);
+  const dim3 rows_grid(sizeof(T) == 2 ? unsigned((a.nb + ROWS_G - 1) / ROWS_G) : unsigned(a.nb), unsigned(a.H));
+  hipLaunchKernelGGL((bwd_rows_kernel<T, D>), rows_grid, dim3(256), 0, s, a);
   PISA_CHECK();
   hipLaunchKernelGGL((bwd_pack_kernel<T, D>), dim3(a.nb, a.H, MODE == MODE_DROP ? 2 : 3), dim3(256), 0, s, a);
   PISA_CHECK();
@@ -1297,6 +1519,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
     if (MODE == MODE_PWT) {
       const dim3 wgrid((a.nb + kB - 1) / kB, a.H);
       hipLaunchKernelGGL((bwd_wprod_kernel<T, D, false>), wgrid, dim3(256), 0, s, a);
+      PISA_CHECK();
+      const size_t quads = size_t(a.H) * a.L * D / 4;
+      hipLaunchKernelGGL((bwd_qsq_kernel<T, D>), dim3(unsigned((quads + 255) / 256)), dim3(256), 0, s, a);
       PISA_CHECK();
       hipLaunchKernelGGL((bwd_wprod_kernel<T, D, true>), wgrid, dim3(256), 0, s, a);
       PISA_CHECK();

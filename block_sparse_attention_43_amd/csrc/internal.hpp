@@ -128,6 +128,7 @@ struct BwdArgs {
   float* qsq;        // [H][nb][d] pooled q² (PWT) or null
   float* dwt;        // [H][nb][nb] dw̃ (PWT)
   float* dsig2;      // [H][nb][d]
+  float* dqsq;       // [H][nb][d] ½ Σ_j dw̃_{i,j} σ²_j (PWT)
   float* dkbar_part; // [H][nchunk][nbp][d]
   float* dvbar_part; // [H][nchunk][nbp][d]
   float* dh_part;    // [H][nhch][d][d]
@@ -150,7 +151,7 @@ struct BwdArgs {
 };
 
 struct BwdLayout {
-  size_t delta, gu, abar, qsq, dwt, dsig2, dkp, dvp, dhp, dh, off, list;
+  size_t delta, gu, abar, qsq, dwt, dsig2, dqsq, dkp, dvp, dhp, dh, off, list;
   size_t kt, kbr, kbt, vbr, qt, gt, vbias, vdphi, vinvn, total;
   int nchunk, nhch;
 };
@@ -170,6 +171,7 @@ inline BwdLayout bwd_layout(size_t elem, int H, int L, int d, int K_sel) {
   w.qsq = o;   o = align256(o + Hs * nb * d * f);
   w.dwt = o;   o = align256(o + Hs * nb * nb * f);
   w.dsig2 = o; o = align256(o + Hs * nb * d * f);
+  w.dqsq = o;  o = align256(o + Hs * nb * d * f);
   w.dkp = o;   o = align256(o + Hs * w.nchunk * nbp * d * f);
   w.dvp = o;   o = align256(o + Hs * w.nchunk * nbp * d * f);
   w.dhp = o;   o = align256(o + Hs * w.nhch * d * d * f);
