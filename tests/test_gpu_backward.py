@@ -127,3 +127,16 @@ def test_backward_full_wan(gpu_lib):
     got = _gpu_backward(gpu_lib, inp, K_sel, "pwt", sel, w, dO)
     worst = _check(inp, K_sel, "pwt", sel, got, dO, heads=[0])
     print(f"wan pwt head 0: worst rel-L2 of dQ, dK, dV {worst:.2e}")
+
+
+@pytest.mark.timeout(900)
+def test_backward_long_tile_lists(gpu_lib):
+    """More than 512 tiles on every list (K_sel = 515 of nb = 520): the query sweep's and the
+    key sweep's tile descriptors are staged 256 at a time, so both refill mid-loop."""
+    inp = synth.random_blocks(107, H=1, nb=520, d=64, dtype="bf16", smooth=2.0)
+    K_sel = 515
+    sel, w = oracle_selection(inp, K_sel)
+    dO = _dO(inp, 153)
+    got = _gpu_backward(gpu_lib, inp, K_sel, "pwt", sel, w, dO)
+    worst = _check(inp, K_sel, "pwt", sel, got, dO)
+    print(f"nb=520 K_sel=515 pwt: worst rel-L2 of dQ, dK, dV {worst:.2e}")
