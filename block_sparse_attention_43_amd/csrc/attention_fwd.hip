@@ -68,6 +68,9 @@ __global__ __launch_bounds__(128) void attention_kernel(AttnArgs a) {
 
   __shared__ __align__(16) T sK[2][kB * LDK];
   __shared__ __align__(16) T sV[2][D * LDV];
+  // σ²_j / 2 of a centroid group (per-row w, bf16; the fp32 tiles leave no LDS for it)
+  constexpr bool SIG_LDS = ROWW && sizeof(T) == 2;
+  __shared__ __align__(16) T sS[SIG_LDS ? kB * LDK : 1];
   __shared__ float sBias[2][kB], sInvN[2][kB], sLnN[ROWW ? 2 : 1][kB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
@@ -229,24 +232,51 @@ __global__ __launch_bounds__(128) void attention_kernel(AttnArgs a) {
       if (second) {
         // Per-row diagonal w_{t,j} = ½ Σ_c q_{t,c}² σ²_{j,c} on MFMA (A = σ²_j / 2 rows of
         // the group's centroids, B = q² of this lane's query), gated and mapped in place;
-        // the score MFMAs below then accumulate onto φ.
-        const int j0 = j_c * kB + feed_row<M>(l32), j1 = j0 + 32;
-        const float* g0 = a.ksig2 + (size_t(h) * nb + min(j0, nb - 1)) * D + KH * g;
-        const float* g1 = a.ksig2 + (size_t(h) * nb + min(j1, nb - 1)) * D + KH * g;
-        const float h0 = j0 < nb ? 0.5f : 0.f, h1 = j1 < nb ? 0.5f : 0.f;
-#pragma unroll 2
-        for (int ks = 0; ks < NKD; ++ks) {
-          float qv[KH], v0[KH], v1[KH];
-          M::unpack(qf[ks], qv);
-#pragma unroll
-          for (int u = 0; u < KH; ++u) {
-            qv[u] *= qv[u];
-            v0[u] = h0 * g0[KI * ks + u];
-            v1[u] = h1 * g1[KI * ks + u];
+        // the score MFMAs below then accumulate onto φ. The group's σ²/2 rows are staged
+        // in LDS first (one coalesced load; zeros past nb), rounded to T as the operand.
+        if constexpr (SIG_LDS) {
+          __syncthreads();                           // previous group's sS reads done
+          for (int c = tid; c < kB * D / 4; c += 128) {
+            const int r = c / (D / 4), col = (c % (D / 4)) * 4, jj = j_c * kB + r;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (jj < nb) v = *reinterpret_cast<const float4*>(a.ksig2 + (size_t(h) * nb + jj) * D + col);
+            sS[r * LDK + col + 0] = from_f32<T>(0.5f * v.x);
+            sS[r * LDK + col + 1] = from_f32<T>(0.5f * v.y);
+            sS[r * LDK + col + 2] = from_f32<T>(0.5f * v.z);
+            sS[r * LDK + col + 3] = from_f32<T>(0.5f * v.w);
           }
-          const AB b = M::pack(qv);
-          s0 = M::mma(M::pack(v0), b, s0);
-          s1 = M::mma(M::pack(v1), b, s1);
+          __syncthreads();
+          const T* sr0 = sS + feed_row<M>(l32) * LDK + KH * g;
+          const T* sr1 = sr0 + 32 * LDK;
+#pragma unroll
+          for (int ks = 0; ks < NKD; ++ks) {
+            float qv[KH];
+            M::unpack(qf[ks], qv);
+#pragma unroll
+            for (int u = 0; u < KH; ++u) qv[u] *= qv[u];
+            const AB b = M::pack(qv);
+            s0 = M::mma(M::load(sr0 + KI * ks), b, s0);
+            s1 = M::mma(M::load(sr1 + KI * ks), b, s1);
+          }
+        } else {
+          const int j0 = j_c * kB + feed_row<M>(l32), j1 = j0 + 32;
+          const float* g0 = a.ksig2 + (size_t(h) * nb + min(j0, nb - 1)) * D + KH * g;
+          const float* g1 = a.ksig2 + (size_t(h) * nb + min(j1, nb - 1)) * D + KH * g;
+          const float h0 = j0 < nb ? 0.5f : 0.f, h1 = j1 < nb ? 0.5f : 0.f;
+#pragma unroll 2
+          for (int ks = 0; ks < NKD; ++ks) {
+            float qv[KH], v0[KH], v1[KH];
+            M::unpack(qf[ks], qv);
+#pragma unroll
+            for (int u = 0; u < KH; ++u) {
+              qv[u] *= qv[u];
+              v0[u] = h0 * g0[KI * ks + u];
+              v1[u] = h1 * g1[KI * ks + u];
+            }
+            const AB b = M::pack(qv);
+            s0 = M::mma(M::pack(v0), b, s0);
+            s1 = M::mma(M::pack(v1), b, s1);
+          }
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -377,14 +407,34 @@ __global__ __launch_bounds__(128) void attention_kernel(AttnArgs a) {
 
   const float lt = sum_halves(lsum);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const size_t orow = size_t(h) * a.L + size_t(i) * kB + qrow;
+  float lse_out = (qvalid && lt > 0.f) ? m * kLn2 + logf(lt) : NEG_INF;
+  // Merge with a pass over the other keys whose normalised output and lse are in O and lse
+  // (per-row w: the exact tiles ran first in the register-streamed kernel). Softmax over
+  // the union: weights e^{lse_x - M} of the two normalised outputs.
+  float w_own = 1.f, w_prev = 0.f;
+  if (ROWW && a.merge) {
+    const float lp = a.lse[orow], M = fmaxf(lp, lse_out);
+    w_prev = M > NEG_INF && lp > NEG_INF ? expf(lp - M) : 0.f;
+    w_own = M > NEG_INF && lse_out > NEG_INF ? expf(lse_out - M) : 0.f;
+    const float den = w_prev + w_own;
+    lse_out = den > 0.f ? M + logf(den) : NEG_INF;
+    const float id = den > 0.f ? 1.f / den : 0.f;
+    w_prev *= id;
+    w_own *= id;
+  }
   T* sO = sK[0];
+  const T* Oprev = static_cast<const T*>(a.O) + orow * D;
 #pragma unroll
   for (int et = 0; et < NET; ++et)
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      sO[qrow * LDK + 32 * et + acc_row(r, g)] = from_f32<T>(qvalid ? acc[et][r] * inv : 0.f);
-  if (a.lse && g == 0)
-    a.lse[size_t(h) * a.L + size_t(i) * kB + qrow] = (qvalid && lt > 0.f) ? m * kLn2 + logf(lt) : NEG_INF;
+    for (int r = 0; r < 16; ++r) {
+      const int e = 32 * et + acc_row(r, g);
+      float o = acc[et][r] * inv;
+      if (ROWW && a.merge) o = w_own * o + w_prev * to_f32(Oprev[e]);
+      sO[qrow * LDK + e] = from_f32<T>(qvalid ? o : 0.f);
+    }
+  if (a.lse && g == 0) a.lse[orow] = lse_out;
   __syncthreads();
   T* Oh = static_cast<T*>(a.O) + (size_t(h) * a.L + size_t(i) * kB) * D;
 #pragma unroll
@@ -762,7 +812,20 @@ static hipError_t launch_attn_t(int mode, const AttnArgs& a, hipStream_t s) {
   if (mode == MODE_LITERAL) {
     hipLaunchKernelGGL((attention_kernel<T, D, MODE_LITERAL>), grid, dim3(128), 0, s, a);
   } else if (mode == MODE_PWT_ROW) {
-    hipLaunchKernelGGL((attention_kernel<T, D, MODE_PWT_ROW>), grid, dim3(128), 0, s, a);
+    if (a.lse) {
+      // Two passes: the exact tiles as DROP in the fast kernel (writes O, lse), then the
+      // virtual tokens with the per-row w, merged into O and lse.
+      if constexpr (std::is_same<T, float>::value)
+        hipLaunchKernelGGL((attention_split_kernel<T, D, MODE_DROP>), grid, dim3(256), 0, s, a);
+      else
+        launch_attention_frag(MODE_DROP, a, s);
+      AttnArgs v = a;
+      v.K_sel = 0;
+      v.merge = 1;
+      hipLaunchKernelGGL((attention_kernel<T, D, MODE_PWT_ROW>), grid, dim3(128), 0, s, v);
+    } else {
+      hipLaunchKernelGGL((attention_kernel<T, D, MODE_PWT_ROW>), grid, dim3(128), 0, s, a);
+    }
   } else if constexpr (std::is_same<T, float>::value) {   // fp32 DROP / PISA / PWT
     switch (mode) {
       case MODE_DROP: hipLaunchKernelGGL((attention_split_kernel<T, D, MODE_DROP>), grid, dim3(256), 0, s, a); break;

@@ -100,6 +100,7 @@ struct AttnArgs {
   int H, L, d, nb, nbp, K_sel, nw;
   int w_linear;    // phi(w) = ln(1 + w) instead of w
   int gate;        // zero w when w > ln n_j
+  int merge;       // O, lse already hold another pass over other keys: combine with it
   PackedLayout pl;
 };
 

@@ -16,7 +16,8 @@ import torch
 from block_sparse_attention_43_amd import synth
 from oracle import pisa_oracle as orc
 from helpers import (CASES, MODE_NAMES, check_selection, gpu_attention_on, gpu_run, mask_to_sets,
-                     oracle_selection, rel_l2, small_case, to_device, valid_rows)
+                     oracle_selection, rel_l2, selection_to_device, small_case, to_device,
+                     valid_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -258,3 +259,29 @@ def test_late_logits_far_above_the_first_unit(gpu_lib, mode):
     print(f"{mode}: rel-L2 {err:.2e}, max |lse diff| {lse_err:.2e}")
     assert err <= TOL_SAME_SEL["bf16"]
     assert lse_err < 5e-2
+
+
+@pytest.mark.parametrize("case", ["bf16_d128_ragged", "f32_d64_ragged_nb130", "bf16_nb70"])
+def test_pwt_row_single_pass(gpu_lib, case):
+    """PWT_ROW without lse runs in one pass (no hand-over buffer); with lse it runs the
+    selected blocks and the virtual tokens separately and merges them. Both against the
+    oracle, and against each other."""
+    pisa = gpu_lib
+    inp, K_sel = _case(case)
+    sel, w = oracle_selection(inp, K_sel)
+    Q, K, V, blt = to_device(inp)
+    st = pisa.block_stats(K, V, blt)
+    di, dm, dw = selection_to_device(sel, w, inp.nb)
+    O1, none = pisa.attention_fwd(Q, K, V, st, di, dm, None, K_sel, "pwt_row", blt, want_lse=False)
+    O2, lse2 = pisa.attention_fwd(Q, K, V, st, di, dm, None, K_sel, "pwt_row", blt)
+    torch.cuda.synchronize()
+    assert none is None
+    o1, o2 = (O.float().cpu().numpy().astype(np.float64) for O in (O1, O2))
+    ok = valid_rows(inp)
+    for h in range(inp.H):
+        ref = _oracle(inp, h, "pwt_row", K_sel, idx=sel[h])
+        e1, e2 = rel_l2(o1[h][ok], ref["O"][ok]), rel_l2(o2[h][ok], ref["O"][ok])
+        print(f"{case} h{h}: single pass {e1:.2e}, two passes {e2:.2e}")
+        assert e1 <= TOL_SAME_SEL[inp.cfg.dtype] and e2 <= TOL_SAME_SEL[inp.cfg.dtype]
+        assert np.all(o1[h][~ok] == 0) and np.all(o2[h][~ok] == 0)
+        assert rel_l2(o1[h][ok], o2[h][ok]) <= (1e-5 if inp.cfg.dtype == "f32" else 1e-2)
