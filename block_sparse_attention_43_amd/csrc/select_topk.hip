@@ -146,7 +146,10 @@ __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
   constexpr int CPR = D / 4, NCH = 64 * CPR / 256;
   __shared__ __align__(16) float sA[64 * RS], sB[64 * RS];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
-  const int h = blockIdx.z, i0 = blockIdx.y * 64, j0 = blockIdx.x * 64, nb = a.nb;
+  // Workgroups are dealt round-robin to the XCDs: remap so that the tiles of one head run
+  // on one XCD and read its centroids from that XCD's L2.
+  const uint32_t nt = gridDim.x, lin = xcd_remap(blockIdx.x + nt * (blockIdx.y + nt * blockIdx.z), nt * nt * gridDim.z);
+  const int h = int(lin / (nt * nt)), i0 = int(lin / nt % nt) * 64, j0 = int(lin % nt) * 64, nb = a.nb;
   const int wi = (wave >> 1) * 32, wj = (wave & 1) * 32;
   const int col = j0 + wj + c;
   auto product = [&](const float* A, const float* B) {
@@ -303,6 +306,122 @@ __global__ __launch_bounds__(256) void topk_kernel(SelectArgs a) {
   }
 }
 
+// Inclusive scan over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// One wave per (query tile, head), four rows per workgroup, for nb <= 64 P: lane l owns
+// block indices [l P, l P + P), so index order is lane order and the tie rule is a lane
+// prefix. The same radix select as topk_kernel with wave-private histograms in LDS and
+// wave scans instead of block barriers.
+template <int P>
+__global__ __launch_bounds__(256) void topk_wave_kernel(SelectArgs a) {
+  __shared__ int hist[4][256];
+  __shared__ uint32_t smask[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nb = a.nb, K = a.K_sel;
+  const int row_id = blockIdx.x * 4 + wave;          // h * nb + i
+  if (row_id >= a.H * nb) return;                     // whole waves leave together
+  const float* row = a.scores + size_t(row_id) * nb;
+  const int base = lane * P;
+  int* hw = hist[wave];
+
+  uint32_t key[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) key[p] = (base + p < nb) ? order_key(row[base + p]) : 0u;
+
+  uint32_t Tk = 0u;
+  int take_eq = 0;
+  const bool all = K >= nb;
+  if (K > 0 && !all) {
+    uint32_t prefix = 0u, pmask = 0u;
+    int rem = K;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hw[4 * lane + q] = 0;
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+        if (base + p < nb && (key[p] & pmask) == prefix) atomicAdd(&hw[(key[p] >> shift) & 255u], 1);
+      // lane l takes digits 255 - 4l .. 252 - 4l (high digits first)
+      int c[4], own = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        c[q] = hw[255 - 4 * lane - q];
+        own += c[q];
+      }
+      const int incl = wave_inclusive_scan(own);
+      int excl = incl - own;
+      // the lane whose digits reach rem finds the digit; broadcast it
+      int dg = -1, rm = 0;
+      if (excl < rem && incl >= rem) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (dg < 0 && excl + c[q] >= rem) {
+            dg = 255 - 4 * lane - q;
+            rm = rem - excl;
+          }
+          excl += c[q];
+        }
+      }
+      const uint64_t who = __ballot(dg >= 0);
+      const int src = __ffsll(static_cast<unsigned long long>(who)) - 1;
+      dg = __shfl(dg, src, 64);
+      rm = __shfl(rm, src, 64);
+      prefix |= uint32_t(dg) << shift;
+      pmask |= 0xFFu << shift;
+      rem = rm;
+    }
+    Tk = prefix;
+    take_eq = rem;
+  }
+
+  int eq_local = 0;
+#pragma unroll
+  for (int p = 0; p < P; ++p) eq_local += (base + p < nb && key[p] == Tk) ? 1 : 0;
+  const int eq_start = wave_inclusive_scan(eq_local) - eq_local;
+  auto selected = [&](int p, int& eqc) -> bool {
+    if (base + p >= nb) return false;
+    if (all) return true;
+    if (K == 0) return false;
+    if (key[p] > Tk) return true;
+    if (key[p] == Tk) return eqc++ < take_eq;
+    return false;
+  };
+  int cnt = 0;
+  {
+    int eqc = eq_start;
+#pragma unroll
+    for (int p = 0; p < P; ++p) cnt += selected(p, eqc) ? 1 : 0;
+  }
+  int pos = wave_inclusive_scan(cnt) - cnt;
+  int32_t* out = a.idx + size_t(row_id) * K;
+  uint32_t* sm = smask[wave];
+  if (a.mask) sm[lane] = 0u;
+  {
+    int eqc = eq_start;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      if (selected(p, eqc)) {
+        if (pos < K) out[pos] = base + p;   // bound holds by construction; kept as a guard
+        ++pos;
+        if (a.mask) atomicOr(&sm[(base + p) >> 5], 1u << ((base + p) & 31));
+      }
+    }
+  }
+  if (a.mask) {
+    uint32_t* mo = a.mask + size_t(row_id) * a.nw;
+    if (lane < a.nw) mo[lane] = sm[lane];
+  }
+}
+
 template <class T, int D>
 static hipError_t launch_select_t(const SelectArgs& a, hipStream_t s) {
   hipError_t e = hipSuccess;
@@ -320,6 +439,16 @@ static hipError_t launch_select_t(const SelectArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((score_kernel<D>), dim3(nt, nt, a.H), dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.nb <= 64 * 32) {
+    const int pw = (a.nb + 63) / 64;
+    const dim3 gw(unsigned((size_t(a.H) * a.nb + 3) / 4));
+    if (pw <= 4) hipLaunchKernelGGL((topk_wave_kernel<4>), gw, dim3(256), 0, s, a);
+    else if (pw <= 8) hipLaunchKernelGGL((topk_wave_kernel<8>), gw, dim3(256), 0, s, a);
+    else if (pw <= 12) hipLaunchKernelGGL((topk_wave_kernel<12>), gw, dim3(256), 0, s, a);
+    else if (pw <= 16) hipLaunchKernelGGL((topk_wave_kernel<16>), gw, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((topk_wave_kernel<32>), gw, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const int per = (a.nb + 255) / 256;
   const dim3 g(a.nb, a.H);
   if (per <= 1) hipLaunchKernelGGL((topk_kernel<1>), g, dim3(256), 0, s, a);
