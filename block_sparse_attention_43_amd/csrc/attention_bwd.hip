@@ -1399,84 +1399,197 @@ __global__ __launch_bounds__(256) void bwd_qsq_kernel(BwdArgs a) {
 constexpr int CHAIN_G = 8;                         // key blocks per workgroup of bwd_chain_kernel
 
 // ---------------------------------------------------------------------------------------
+// bf16 inputs: G = dH̄ / nb staged once per workgroup as hi + lo bf16 parts, in both
+// orientations; the products run on bf16 MFMA with the token rows (exact in bf16) as A
+// operands straight from memory, and the block means enter as per-block vectors:
+//   dK[t][c] += Σ_e v_t[e] G[e][c] - (v̄ᵀ G)[c],   dV[t][e] += Σ_c k_t[c] G[e][c] - (G k̄)[e].
+template <int D, int MODE>
+__device__ __forceinline__ void chain_bf16(const BwdArgs& a) {
+  constexpr int NE = D / 32, NKD = D / 16, LDG = D + 8, CT = NE / 2;
+  __shared__ __align__(16) uint16_t sGh[D * LDG], sGl[D * LDG];   // G[e][c]
+  __shared__ __align__(16) uint16_t sTh[D * LDG], sTl[D * LDG];   // Gᵀ[c][e]
+  __shared__ float sdk[D], sdv[D], sdsig[D], skb[D], svb[D], scv[D], sck[D];
+  const int h = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int nb = a.nb;
+  const float invnb = 1.f / float(nb);
+  for (int x = tid; x < D * D; x += 256) {
+    const int e = x / D, c = x % D;
+    const float f = a.dh[size_t(h) * D * D + x] * invnb;
+    const uint16_t hi = from_f32<uint16_t>(f), lo = from_f32<uint16_t>(f - to_f32(hi));
+    sGh[e * LDG + c] = hi;
+    sGl[e * LDG + c] = lo;
+    sTh[c * LDG + e] = hi;
+    sTl[c * LDG + e] = lo;
+  }
+  const uint16_t* Kb = static_cast<const uint16_t*>(a.K);
+  const uint16_t* Vb = static_cast<const uint16_t*>(a.V);
+  const int tt = wave & 1, cp = wave >> 1;          // token half; column tiles cp CT .. cp CT + CT - 1
+  const int t = 32 * tt + l32;                      // A row of this lane
+  for (int j = blockIdx.x * CHAIN_G; j < min(nb, blockIdx.x * CHAIN_G + CHAIN_G); ++j) {
+    const int n = min(max(a.block_len ? a.block_len[j] : kB, 1), kB);
+    const float invn = 1.f / float(n);
+    const size_t row0 = size_t(h) * a.L + size_t(j) * kB;
+    __syncthreads();                                // G staged; previous block's vectors read
+    if (tid < D) {
+      float dk = 0.f, dv = 0.f;
+      for (int c = 0; c < a.nchunk; ++c) {
+        const size_t o = ((size_t(h) * a.nchunk + c) * a.nbp + j) * D + tid;
+        dk += a.dkbar_part[o];
+        dv += a.dvbar_part[o];
+      }
+      const size_t o = (size_t(h) * nb + j) * D + tid;
+      sdk[tid] = dk * invn;
+      sdv[tid] = dv * invn;
+      sdsig[tid] = MODE == MODE_PWT ? a.dsig2[o] * 2.f * invn : 0.f;
+      skb[tid] = a.kbar[o];
+      svb[tid] = a.vsum[o] * invn;
+    }
+    // this lane's token rows as A operands (zeros on padding rows)
+    bf16x8 va[NKD], ka[NKD];
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks) {
+      const size_t o = (row0 + t) * D + 16 * ks + 8 * g;
+      va[ks] = t < n ? *reinterpret_cast<const bf16x8*>(Vb + o) : MmaBF16::zero();
+      ka[ks] = t < n ? *reinterpret_cast<const bf16x8*>(Kb + o) : MmaBF16::zero();
+    }
+    __syncthreads();
+    if (tid < D) {                                  // (v̄ᵀ G)[c]
+      float sv = 0.f;
+      for (int e = 0; e < D; ++e) sv = fmaf(svb[e], to_f32(sGh[e * LDG + tid]) + to_f32(sGl[e * LDG + tid]), sv);
+      scv[tid] = sv;
+    } else if (tid >= 128 && tid < 128 + D) {       // (G k̄)[e]
+      const int e = tid - 128;
+      float sk = 0.f;
+      for (int c = 0; c < D; ++c) sk = fmaf(to_f32(sTh[c * LDG + e]) + to_f32(sTl[c * LDG + e]), skb[c], sk);
+      sck[e] = sk;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < CT; ++u) {
+      const int col = 32 * (cp * CT + u) + l32;
+      f32x16 ak = zero16(), av = zero16();
+#pragma unroll
+      for (int ks = 0; ks < NKD; ++ks) {
+        const int kk = 16 * ks + 8 * g;
+        // dK: B(k = e, col c) = G[e][c] = Gᵀ[c][e];  dV: B(k = c, col e) = G[e][c]
+        const bf16x8 th = *reinterpret_cast<const bf16x8*>(sTh + col * LDG + kk);
+        const bf16x8 tl = *reinterpret_cast<const bf16x8*>(sTl + col * LDG + kk);
+        const bf16x8 gh = *reinterpret_cast<const bf16x8*>(sGh + col * LDG + kk);
+        const bf16x8 gl = *reinterpret_cast<const bf16x8*>(sGl + col * LDG + kk);
+        ak = MmaBF16::mma(va[ks], th, ak);
+        ak = MmaBF16::mma(va[ks], tl, ak);
+        av = MmaBF16::mma(ka[ks], gh, av);
+        av = MmaBF16::mma(ka[ks], gl, av);
+      }
+      const float dkc = sdk[col], dvc = sdv[col], dsc = sdsig[col], kbc = skb[col];
+      const float cvc = scv[col], ckc = sck[col];
+      // Branch-free, so all loads of the update are in flight together; padding rows
+      // (zeros from the key sweep) are written back unchanged.
+      float xk[16], xv[16], kt[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const size_t o = (row0 + 32 * tt + acc_row(r, g)) * D + col;
+        xk[r] = a.dK[o];
+        xv[r] = a.dV[o];
+        kt[r] = to_f32(Kb[o]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tr = 32 * tt + acc_row(r, g);
+        const size_t o = (row0 + tr) * D + col;
+        const float uk = xk[r] + (dkc + (kt[r] - kbc) * dsc + (ak[r] - cvc));
+        const float uv = xv[r] + (dvc + (av[r] - ckc));
+        a.dK[o] = tr < n ? uk : xk[r];
+        a.dV[o] = tr < n ? uv : xv[r];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Per key block: the statistics' gradients onto its valid tokens (adds to dK, dV). The two
 // d x d products run on the fp32 matrix cores with dH̄ / nb and the centred tokens staged in
 // LDS: dK[t][c] += Σ_e (v_t - v̄)[e] dH̄[e][c], dV[t][e] += Σ_c (k_t - k̄)[c] dH̄[e][c]; the
 // output columns run along the lanes, so the updates of dK and dV are row-contiguous.
 template <class T, int D, int MODE>
 __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs a) {
-  constexpr int NE = D / 32;
-  __shared__ float sH[D][D + 1];                   // dH̄[e][c] / nb
-  __shared__ float sKd[kB][D + 1], sVd[kB][D + 1]; // k - k̄, v - v̄ (0 on padding)
-  __shared__ float sdk[D], sdv[D], sdsig[D], skb[D], svb[D];
-  const int h = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
-  const int nb = a.nb;
-  const float invnb = 1.f / float(nb);
-  for (int x = tid; x < D * D; x += 256) sH[x / D][x % D] = a.dh[size_t(h) * D * D + x] * invnb;
-  // CHAIN_G consecutive blocks per workgroup share the staged dH̄.
-  for (int j = blockIdx.x * CHAIN_G; j < min(nb, blockIdx.x * CHAIN_G + CHAIN_G); ++j) {
-  const int n = min(max(a.block_len ? a.block_len[j] : kB, 1), kB);
-  const float invn = 1.f / float(n);
-  __syncthreads();                                 // previous block's reads done
-  if (tid < D) {
-    float dk = 0.f, dv = 0.f;
-    for (int c = 0; c < a.nchunk; ++c) {
-      const size_t o = ((size_t(h) * a.nchunk + c) * a.nbp + j) * D + tid;
-      dk += a.dkbar_part[o];
-      dv += a.dvbar_part[o];
+  if constexpr (sizeof(T) == 2) {
+    chain_bf16<D, MODE>(a);
+  } else {
+    constexpr int NE = D / 32;
+    __shared__ float sH[D][D + 1];                   // dH̄[e][c] / nb
+    __shared__ float sKd[kB][D + 1], sVd[kB][D + 1]; // k - k̄, v - v̄ (0 on padding)
+    __shared__ float sdk[D], sdv[D], sdsig[D], skb[D], svb[D];
+    const int h = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+    const int nb = a.nb;
+    const float invnb = 1.f / float(nb);
+    for (int x = tid; x < D * D; x += 256) sH[x / D][x % D] = a.dh[size_t(h) * D * D + x] * invnb;
+    // CHAIN_G consecutive blocks per workgroup share the staged dH̄.
+    for (int j = blockIdx.x * CHAIN_G; j < min(nb, blockIdx.x * CHAIN_G + CHAIN_G); ++j) {
+    const int n = min(max(a.block_len ? a.block_len[j] : kB, 1), kB);
+    const float invn = 1.f / float(n);
+    __syncthreads();                                 // previous block's reads done
+    if (tid < D) {
+      float dk = 0.f, dv = 0.f;
+      for (int c = 0; c < a.nchunk; ++c) {
+        const size_t o = ((size_t(h) * a.nchunk + c) * a.nbp + j) * D + tid;
+        dk += a.dkbar_part[o];
+        dv += a.dvbar_part[o];
+      }
+      const size_t o = (size_t(h) * nb + j) * D + tid;
+      sdk[tid] = dk * invn;
+      sdv[tid] = dv * invn;
+      sdsig[tid] = MODE == MODE_PWT ? a.dsig2[o] * 2.f * invn : 0.f;
+      skb[tid] = a.kbar[o];
+      svb[tid] = a.vsum[o] * invn;
     }
-    const size_t o = (size_t(h) * nb + j) * D + tid;
-    sdk[tid] = dk * invn;
-    sdv[tid] = dv * invn;
-    sdsig[tid] = MODE == MODE_PWT ? a.dsig2[o] * 2.f * invn : 0.f;
-    skb[tid] = a.kbar[o];
-    svb[tid] = a.vsum[o] * invn;
-  }
-  __syncthreads();
-  const size_t row0 = size_t(h) * a.L + size_t(j) * kB;
-  const T* Kb = static_cast<const T*>(a.K) + row0 * D;
-  const T* Vb = static_cast<const T*>(a.V) + row0 * D;
-  for (int x = tid; x < kB * D; x += 256) {
-    const int t = x / D, c = x % D;
-    const bool ok = t < n;
-    sKd[t][c] = ok ? to_f32(Kb[x]) - skb[c] : 0.f;
-    sVd[t][c] = ok ? to_f32(Vb[x]) - svb[c] : 0.f;
-  }
-  __syncthreads();
-  // wave: token half tt (rows 32 tt + [0, 32)), output column tiles xt = wave / 2, + 2
-  const int tt = wave & 1;
-  for (int xt = wave >> 1; xt < NE; xt += 2) {
-    f32x16 ak = zero16(), av = zero16();
-    const int col = 32 * xt + l32;
+    __syncthreads();
+    const size_t row0 = size_t(h) * a.L + size_t(j) * kB;
+    const T* Kb = static_cast<const T*>(a.K) + row0 * D;
+    const T* Vb = static_cast<const T*>(a.V) + row0 * D;
+    for (int x = tid; x < kB * D; x += 256) {
+      const int t = x / D, c = x % D;
+      const bool ok = t < n;
+      sKd[t][c] = ok ? to_f32(Kb[x]) - skb[c] : 0.f;
+      sVd[t][c] = ok ? to_f32(Vb[x]) - svb[c] : 0.f;
+    }
+    __syncthreads();
+    // wave: token half tt (rows 32 tt + [0, 32)), output column tiles xt = wave / 2, + 2
+    const int tt = wave & 1;
+    for (int xt = wave >> 1; xt < NE; xt += 2) {
+      f32x16 ak = zero16(), av = zero16();
+      const int col = 32 * xt + l32;
 #pragma unroll 8
-    for (int ks = 0; ks < D / 2; ++ks) {
-      const int k = 2 * ks + g;
-      // dK: A(row t, k = e) = (v - v̄)[t][e], B(k = e, col c) = dH̄[e][c]
-      // dV: A(row t, k = c) = (k - k̄)[t][c], B(k = c, col e) = dH̄[e][c]
-      ak = __builtin_amdgcn_mfma_f32_32x32x2f32(sVd[32 * tt + l32][k], sH[k][col], ak, 0, 0, 0);
-      av = __builtin_amdgcn_mfma_f32_32x32x2f32(sKd[32 * tt + l32][k], sH[col][k], av, 0, 0, 0);
-    }
-    const float dkc = sdk[col], dvc = sdv[col], dsc = sdsig[col];
-    // Branch-free, so all 32 loads of the update are in flight together; padding rows
-    // (zeros from the key sweep) receive + 0.
-    float xk[16], xv[16];
+      for (int ks = 0; ks < D / 2; ++ks) {
+        const int k = 2 * ks + g;
+        // dK: A(row t, k = e) = (v - v̄)[t][e], B(k = e, col c) = dH̄[e][c]
+        // dV: A(row t, k = c) = (k - k̄)[t][c], B(k = c, col e) = dH̄[e][c]
+        ak = __builtin_amdgcn_mfma_f32_32x32x2f32(sVd[32 * tt + l32][k], sH[k][col], ak, 0, 0, 0);
+        av = __builtin_amdgcn_mfma_f32_32x32x2f32(sKd[32 * tt + l32][k], sH[col][k], av, 0, 0, 0);
+      }
+      const float dkc = sdk[col], dvc = sdv[col], dsc = sdsig[col];
+      // Branch-free, so all 32 loads of the update are in flight together; padding rows
+      // (zeros from the key sweep) receive + 0.
+      float xk[16], xv[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const size_t o = (row0 + 32 * tt + acc_row(r, g)) * D + col;
-      xk[r] = a.dK[o];
-      xv[r] = a.dV[o];
-    }
+      for (int r = 0; r < 16; ++r) {
+        const size_t o = (row0 + 32 * tt + acc_row(r, g)) * D + col;
+        xk[r] = a.dK[o];
+        xv[r] = a.dV[o];
+      }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = 32 * tt + acc_row(r, g);
-      const bool on = t < n;
-      const size_t o = (row0 + t) * D + col;
-      const float uk = xk[r] + (dkc + sKd[t][col] * dsc + ak[r]), uv = xv[r] + (dvc + av[r]);
-      a.dK[o] = on ? uk : xk[r];
-      a.dV[o] = on ? uv : xv[r];
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * tt + acc_row(r, g);
+        const bool on = t < n;
+        const size_t o = (row0 + t) * D + col;
+        const float uk = xk[r] + (dkc + sKd[t][col] * dsc + ak[r]), uv = xv[r] + (dvc + av[r]);
+        a.dK[o] = on ? uk : xk[r];
+        a.dV[o] = on ? uv : xv[r];
+      }
     }
-  }
+    }
   }
 }
 
