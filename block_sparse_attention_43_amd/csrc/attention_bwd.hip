@@ -1010,6 +1010,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
       p = M::mma(gfrag(ks), vf[ks], p);
     }
     if constexpr (LATE) {
+      // read_rows written out: through the lambda this instance spills (measured)
       __builtin_amdgcn_sched_barrier(0);
       u32x4 rb[8], rc[8];
       lds_read8_at<0, 16, 64, 80, 256, 272, 320, 336>(rb, base + RB + q0 * 4);
