@@ -27,5 +27,7 @@ __device__ __forceinline__ int acc_key(int mt, int r, int g) {
 
 // bf16 DROP / PISA / PWT: register-streamed kernel over operand-order tiles.
 hipError_t launch_attention_frag(int mode, const AttnArgs& a, hipStream_t s);
+// bf16 PWT_ROW: virtual tokens with the per-row w, merged into O / lse of a DROP pass.
+hipError_t launch_virtual_row(const AttnArgs& a, hipStream_t s);
 
 }  // namespace pisa

@@ -815,14 +815,16 @@ static hipError_t launch_attn_t(int mode, const AttnArgs& a, hipStream_t s) {
     if (a.lse) {
       // Two passes: the exact tiles as DROP in the fast kernel (writes O, lse), then the
       // virtual tokens with the per-row w, merged into O and lse.
-      if constexpr (std::is_same<T, float>::value)
+      if constexpr (std::is_same<T, float>::value) {
         hipLaunchKernelGGL((attention_split_kernel<T, D, MODE_DROP>), grid, dim3(256), 0, s, a);
-      else
+        AttnArgs v = a;
+        v.K_sel = 0;
+        v.merge = 1;
+        hipLaunchKernelGGL((attention_kernel<T, D, MODE_PWT_ROW>), grid, dim3(128), 0, s, v);
+      } else {
         launch_attention_frag(MODE_DROP, a, s);
-      AttnArgs v = a;
-      v.K_sel = 0;
-      v.merge = 1;
-      hipLaunchKernelGGL((attention_kernel<T, D, MODE_PWT_ROW>), grid, dim3(128), 0, s, v);
+        launch_virtual_row(a, s);
+      }
     } else {
       hipLaunchKernelGGL((attention_kernel<T, D, MODE_PWT_ROW>), grid, dim3(128), 0, s, a);
     }
