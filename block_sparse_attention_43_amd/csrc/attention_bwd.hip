@@ -43,6 +43,8 @@ namespace {
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr float POS_INF = __builtin_huge_valf();
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 template <class T>
 __device__ __forceinline__ u32x4 zero_chunk() {
   return u32x4{0u, 0u, 0u, 0u};
@@ -117,6 +119,25 @@ __device__ __forceinline__ void lds_read8_at(u32x4 (&o)[8], uint32_t ad) {
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
       : "v"(ad), "i"(O0), "i"(O1), "i"(O2), "i"(O3), "i"(O4), "i"(O5), "i"(O6), "i"(O7));
+}
+// Eight LDS transpose reads (ds_read_b64_tr_b16, gfx950): within each group of 16 lanes,
+// lane 4a + b receives element b of the 8-byte rows addressed by lanes a, a + 4, a + 8 and
+// a + 12 of the group; if lane 4u + a addresses row r0 + u at column c0 + 4a of a bf16 tile,
+// lane t gets rows r0 .. r0 + 3 of column c0 + t, i.e. a transposed operand from row-major
+// data. Waits for its reads like the blocks above.
+__device__ __forceinline__ void lds_read8_tr16(u32x2 (&o)[8], const uint32_t (&ad)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]));
 }
 __device__ __forceinline__ void lds_write_u32(uint32_t ad, uint32_t v) {
   asm volatile("ds_write_b32 %0, %1" ::"v"(ad), "v"(v) : "memory");
@@ -776,11 +797,14 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   constexpr bool SPLIT = sizeof(T) == 2;
   constexpr int KROW = D * ES, TROW = kB * ES, TB = kB * KROW;
   constexpr int DPW = TB / 4096;                    // 1 KB direct loads per wave and operand
-  constexpr int RB = 4 * TB;                        // rows: lse, Δ, gu, bias, φ', 3 unused
+  // Stage: Q and dO rows, for fp32 also Qᵀ and dOᵀ (bf16 forms the transposed operands
+  // from the rows with LDS transpose reads), then the rows lse, Δ, gu, bias, φ', 3 unused.
+  constexpr int NTILE = SPLIT ? 2 : 4;
+  constexpr int RB = NTILE * TB;
   constexpr int SB = RB + 8 * kB * 4;               // bytes per stage
   constexpr int BUDGET = 152 * 1024;
   constexpr int NST = 3 * SB <= BUDGET ? 3 : (2 * SB <= BUDGET ? 2 : 1);
-  constexpr int PT = 4 * DPW + 2;                   // direct loads per wave and tile
+  constexpr int PT = NTILE * DPW + 2;               // direct loads per wave and tile
   constexpr int DCH = 256;
   using KT = SwizzledTile<KROW>;
   using TT = SwizzledTile<TROW>;
@@ -912,8 +936,10 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
       const int lb = (wave * DPW + u) * 1024;
       buf_dma16(rq, ro, 0, st + lb);
       buf_dma16(rg, ro, 0, st + TB + lb);
-      buf_dma16(rqt, toff[u], 0, st + 2 * TB + lb);
-      buf_dma16(rgt, toff[u], 0, st + 3 * TB + lb);
+      if constexpr (!SPLIT) {
+        buf_dma16(rqt, toff[u], 0, st + 2 * TB + lb);
+        buf_dma16(rgt, toff[u], 0, st + 3 * TB + lb);
+      }
     }
     const float* lse_row = a.lse + rowb;
     const float* r0 = lse_row;
@@ -946,6 +972,9 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
     for (int ks = 0; ks < NKH; ++ks)
       tad[et * NKH + ks] = TT::offset(32 * et + l32, (32 * wq + KI * ks + KH * g) * ES);
   const int q0 = 32 * wq + acc_key<M>(0, 0, g);
+  // transpose reads: lane 16 G + 4 u + a addresses query row 32 wq + 8 (G / 2) + u (+ the
+  // fragment's k offset) at column 16 (G % 2) + 4 a (+ the fragment's column tile)
+  const int trow = 32 * wq + 8 * (lane >> 5) + ((lane & 15) >> 2), tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   auto compute = [&](int n, auto sc) {
     constexpr int S = decltype(sc)::value;
@@ -1066,17 +1095,30 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
         lo[r] = s[r] - hi;
         s[r] = hi;
       }
-      // Qᵀ and dOᵀ fragments, read once the score operands are dead
-      uint32_t adt[NT];
-      u32x4 rt[NT], ru[NT];
+      // Qᵀ and dOᵀ fragments from the Q and dO rows by transpose reads, once the score
+      // operands are dead: fragment x = (et, ks) is two reads (rows +0..3, +4..7).
+      static_assert(2 * NT % 8 == 0, "transpose read blocks");
 #pragma unroll
-      for (int x = 0; x < NT; ++x) adt[x] = base + 2 * TB + tad[x];
-      lds_read_x16<NT, 0>(rt, adt);
-      lds_read_x16<NT, TB>(ru, adt);
+      for (int op = 0; op < 2; ++op) {
 #pragma unroll
-      for (int x = 0; x < NT; ++x) {
-        qta[x] = __builtin_bit_cast(AB, rt[x]);
-        gta[x] = __builtin_bit_cast(AB, ru[x]);
+        for (int b8 = 0; b8 < 2 * NT / 8; ++b8) {
+          uint32_t ad[8];
+          u32x2 o[8];
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            const int y = 8 * b8 + v, x = y >> 1, rr = y & 1;
+            const int et = x / NKH, ks = x % NKH;
+            ad[v] = base + op * TB + KT::offset(trow + KI * ks + 4 * rr, (32 * et + tcol) * ES);
+          }
+          lds_read8_tr16(o, ad);
+#pragma unroll
+          for (int v = 0; v < 8; v += 2) {
+            const int x = (8 * b8 + v) >> 1;
+            const AB f = __builtin_bit_cast(AB, u32x4{o[v][0], o[v][1], o[v + 1][0], o[v + 1][1]});
+            if (op == 0) qta[x] = f;
+            else gta[x] = f;
+          }
+        }
       }
     }
     static_for<0, NKH>([&](auto ksc) {
@@ -1125,10 +1167,12 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
 
   // Merge the query halves: wave (1, wk) hands over to wave (0, wk).
   constexpr int XF = 2 * NET * 16 * 64;            // floats handed over per wave
-  static_assert(2 * XF * 4 <= SB, "hand-over buffer");
+  // one stage array per handing wave (or both in the single stage)
+  static_assert(NST >= 2 ? XF * 4 <= SB : 2 * XF * 4 <= SB, "hand-over buffer");
+  char* const hbuf = NST >= 2 ? (wk ? sS1 : sS0) : sS0 + wk * XF * 4;
   __syncthreads();
   if (wq == 1) {
-    float* mine = reinterpret_cast<float*>(sS0) + wk * XF + lane;
+    float* mine = reinterpret_cast<float*>(hbuf) + lane;
 #pragma unroll
     for (int et = 0; et < NET; ++et)
 #pragma unroll
@@ -1139,7 +1183,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   }
   __syncthreads();
   if (wq == 1) return;
-  const float* other = reinterpret_cast<const float*>(sS0) + wk * XF + lane;
+  const float* other = reinterpret_cast<const float*>(hbuf) + lane;
 #pragma unroll
   for (int et = 0; et < NET; ++et)
 #pragma unroll
