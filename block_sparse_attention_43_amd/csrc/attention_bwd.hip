@@ -288,11 +288,12 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Operand tiles of the sweeps that are not rows of the inputs, in the input type (centroid
-// tiles rounded from fp32 as the forward's are), zeros past the valid rows: z = 0, block i:
-// Kᵀ [d][64]; z = 1, query tile i: Qᵀ and dOᵀ; z = 2, centroid group i: k̄ rows [64][d],
-// k̄ᵀ [d][64] and v̄ = ΣV / n rows [64][d]. The sweeps move them, with the rows of Q, K, V
-// and dO themselves, into LDS by direct loads.
+// Operand tiles that are not rows of the inputs, in the input type (centroid tiles rounded
+// from fp32 as the forward's are), zeros past the valid rows: kind 0, block i: Kᵀ [d][64];
+// kind 1, query tile i: Qᵀ and dOᵀ; kind 2, centroid group i: k̄ rows [64][d], k̄ᵀ [d][64]
+// and v̄ = ΣV / n rows [64][d]. The sweeps move them, with the rows of Q, K, V and dO
+// themselves, into LDS by direct loads; the bf16 sweeps form the transposed operands from
+// rows with LDS transpose reads and use kind 1 only for dH̄.
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_pack_kernel(BwdArgs a) {
   constexpr int EPC = 16 / sizeof(T), LDT = kB + EPC, CPR = D / EPC, CPT = kB / EPC;
@@ -316,11 +317,13 @@ __global__ __launch_bounds__(256) void bwd_pack_kernel(BwdArgs a) {
       *reinterpret_cast<u32x4*>(out + e * kB + k0) = *reinterpret_cast<const u32x4*>(&sXt[tix<T, LDT>(e, k0)]);
     }
   };
+  // bf16 forms Kᵀ and k̄ᵀ operands with LDS transpose reads: its launch starts at z = 1
+  const int kind = int(blockIdx.z) + (sizeof(T) == 2 ? 1 : 0);
   T* out;
-  if (blockIdx.z < 2) {
+  if (kind < 2) {
     const int valid = min(max(a.block_len ? a.block_len[i] : kB, 1), kB);
     const size_t row0 = (size_t(h) * a.L + size_t(i) * kB) * D, to = (size_t(h) * nb + i) * TE;
-    if (blockIdx.z == 0) {
+    if (kind == 0) {
       stage_t(static_cast<const T*>(a.K) + row0, valid);
       out = reinterpret_cast<T*>(a.kt) + to;
     } else {
@@ -456,11 +459,14 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   constexpr int KROW = D * ES, TROW = kB * ES;      // bytes per key row; per Kᵀ row
   constexpr int TB = kB * KROW;                     // bytes per operand tile
   constexpr int DPW = TB / 4096;                    // 1 KB direct loads per wave and operand
-  constexpr int RB = 3 * TB;                        // stage offset of the 4 x 64-float rows
+  // Stage: K (or k̄) rows, V (or v̄) rows, for fp32 also Kᵀ (bf16 forms the transposed
+  // operand from the rows with LDS transpose reads), then 4 x 64-float rows.
+  constexpr int NTILE = SPLIT ? 2 : 3;
+  constexpr int RB = NTILE * TB;
   constexpr int SB = RB + 4 * kB * 4;               // bytes per stage
   constexpr int BUDGET = 152 * 1024;
   constexpr int NST = 3 * SB <= BUDGET ? 3 : (2 * SB <= BUDGET ? 2 : 1);
-  constexpr int PT = 3 * DPW + 1;                   // direct loads per wave and tile
+  constexpr int PT = NTILE * DPW + 1;               // direct loads per wave and tile
   constexpr int DCH = 256;                          // descriptor chunk (exact tiles)
   using KT = SwizzledTile<KROW>;
   using TT = SwizzledTile<TROW>;
@@ -566,7 +572,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
       const int ko = krow[u] < nrows ? koff[u] : koff[u] - krow[u] * KROW;
       buf_dma16(rk, ko, 0, st + (wave * DPW + u) * 1024);
       buf_dma16(rv, ko, 0, st + TB + (wave * DPW + u) * 1024);
-      buf_dma16(rt, toff[u], 0, st + 2 * TB + (wave * DPW + u) * 1024);
+      if constexpr (!SPLIT) buf_dma16(rt, toff[u], 0, st + 2 * TB + (wave * DPW + u) * 1024);
     }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(pr, kB * 4), (__attribute__((address_space(3))) void*)(st + RB + wave * kB * 4),
                                              4, lane * 4, 0, 0, 0);
@@ -584,6 +590,9 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
     for (int ks = 0; ks < NKH; ++ks)
       tad[et * NKH + ks] = 2 * TB + TT::offset(32 * et + l32, (32 * wk + KI * ks + KH * g) * ES);
   const int key0 = 32 * wk + acc_key<M>(0, 0, g);
+  // transpose reads: lane 16 G + 4 u + a addresses key row 32 wk + 8 (G / 2) + u (+ the
+  // fragment's k offset) at column 16 (G % 2) + 4 a (+ the fragment's column tile)
+  const int trow = 32 * wk + 8 * (lane >> 5) + ((lane & 15) >> 2), tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   // One tile from stage S: Sᵀ, dPᵀ, P and P∘dP (hi + lo), dQ₀ and kp.
   auto compute = [&](int t, auto sc) {
@@ -601,22 +610,35 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
       // bf16: every operand in three blocks of 16-byte reads, the rows' biases in a fourth.
       static_assert(NKD == 4 || NKD == 8, "fragments per block");
       const uint32_t base = lds_addr(sk);
-      uint32_t ad[NKD], adt[NT];
-      u32x4 rk[NKD], rv[NKD], rt[NT];
+      uint32_t ad[NKD];
+      u32x4 rk[NKD], rv[NKD];
 #pragma unroll
       for (int ks = 0; ks < NKD; ++ks) ad[ks] = base + kad[ks];
-#pragma unroll
-      for (int x = 0; x < NT; ++x) adt[x] = base + tad[x];
       lds_read_x16<NKD, 0>(rk, ad);
       lds_read_x16<NKD, TB>(rv, ad);
-      lds_read_x16<NT, 0>(rt, adt);
 #pragma unroll
       for (int ks = 0; ks < NKD; ++ks) {
         ka[ks] = __builtin_bit_cast(AB, rk[ks]);
         va[ks] = __builtin_bit_cast(AB, rv[ks]);
       }
+      // Kᵀ fragments from the K rows by transpose reads: fragment x = (et, ks) is two
+      // reads (keys +0..3, +4..7 of its k range).
+      static_assert(2 * NT % 8 == 0, "transpose read blocks");
 #pragma unroll
-      for (int x = 0; x < NT; ++x) ta[x] = __builtin_bit_cast(AB, rt[x]);
+      for (int b8 = 0; b8 < 2 * NT / 8; ++b8) {
+        uint32_t adr[8];
+        u32x2 o[8];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const int y = 8 * b8 + v, x = y >> 1, rr = y & 1;
+          const int et = x / NKH, ks = x % NKH;
+          adr[v] = base + KT::offset(trow + KI * ks + 4 * rr, (32 * et + tcol) * ES);
+        }
+        lds_read8_tr16(o, adr);
+#pragma unroll
+        for (int v = 0; v < 8; v += 2)
+          ta[(8 * b8 + v) >> 1] = __builtin_bit_cast(AB, u32x4{o[v][0], o[v][1], o[v + 1][0], o[v + 1][1]});
+      }
       if (virt) {
         // keys key0 + {0..7, 16..23}: biases at +0, +64 bytes, 1 / n_j one row (256 bytes) on
         u32x4 rb[8];
@@ -1650,8 +1672,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const dim3 rows_grid(sizeof(T) == 2 ? unsigned((a.nb + ROWS_G - 1) / ROWS_G) : unsigned(a.nb), unsigned(a.H));
   hipLaunchKernelGGL((bwd_rows_kernel<T, D>), rows_grid, dim3(256), 0, s, a);
   PISA_CHECK();
-  hipLaunchKernelGGL((bwd_pack_kernel<T, D>), dim3(a.nb, a.H, MODE == MODE_DROP ? 2 : 3), dim3(256), 0, s, a);
-  PISA_CHECK();
+  // Kinds of packed tiles read: fp32 Kᵀ (0) and Qᵀ, dOᵀ (1, key sweep); bf16 Qᵀ, dOᵀ for
+  // dH̄ only (not in DROP); centroid groups (2) unless DROP.
+  {
+    const unsigned kinds = sizeof(T) == 2 ? (MODE == MODE_DROP ? 0u : 2u) : (MODE == MODE_DROP ? 2u : 3u);
+    if (kinds > 0) {
+      hipLaunchKernelGGL((bwd_pack_kernel<T, D>), dim3(a.nb, a.H, kinds), dim3(256), 0, s, a);
+      PISA_CHECK();
+    }
+  }
   if (MODE != MODE_DROP) {
     hipLaunchKernelGGL((bwd_bias_kernel<MODE>), dim3(a.nb, a.H), dim3(256), 0, s, a);
     PISA_CHECK();
