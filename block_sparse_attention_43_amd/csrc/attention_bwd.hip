@@ -465,7 +465,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   constexpr int RB = NTILE * TB;
   constexpr int SB = RB + 4 * kB * 4;               // bytes per stage
   constexpr int BUDGET = 152 * 1024;
-  constexpr int NST = 3 * SB <= BUDGET ? 3 : (2 * SB <= BUDGET ? 2 : 1);
+  constexpr int NST = 4 * SB <= BUDGET ? 4 : (3 * SB <= BUDGET ? 3 : (2 * SB <= BUDGET ? 2 : 1));
   constexpr int PT = NTILE * DPW + 1;               // direct loads per wave and tile
   constexpr int DCH = 256;                          // descriptor chunk (exact tiles)
   using KT = SwizzledTile<KROW>;
@@ -474,6 +474,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   __shared__ __align__(1024) char sS0[SB];
   __shared__ __align__(1024) char sS1[NST > 1 ? SB : 16];
   __shared__ __align__(1024) char sS2[NST > 2 ? SB : 16];
+  __shared__ __align__(1024) char sS3[NST > 3 ? SB : 16];
   __shared__ float sDel[2][kB];
   __shared__ uint32_t sDesc[2][DCH];                // exact tile -> block | valid keys << 16
 
@@ -546,7 +547,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   const char* Vb = reinterpret_cast<const char*>(static_cast<const T*>(a.V) + size_t(h) * a.L * D);
   auto issue = [&](int t, auto sc) {
     constexpr int S = decltype(sc)::value;
-    char* st = S == 0 ? sS0 : (S == 1 ? sS1 : sS2);
+    char* st = S == 0 ? sS0 : (S == 1 ? sS1 : (S == 2 ? sS2 : sS3));
     const char *pk, *pv, *pt, *pr;
     int nrows;
     if (VIRT && t >= n1) {
@@ -597,7 +598,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   // One tile from stage S: Sᵀ, dPᵀ, P and P∘dP (hi + lo), dQ₀ and kp.
   auto compute = [&](int t, auto sc) {
     constexpr int S = decltype(sc)::value;
-    const char* sk = S == 0 ? sS0 : (S == 1 ? sS1 : sS2);
+    const char* sk = S == 0 ? sS0 : (S == 1 ? sS1 : (S == 2 ? sS2 : sS3));
     const bool virt = VIRT && t >= n1;
     const int nj = virt ? kB : int(desc(t) >> 16);
     if (nj == 0) return;                           // uniform: out-of-range index
@@ -729,8 +730,16 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
         // This wave's loads of tile t have landed once at most the loads of the tiles
         // issued after it (NST - 2 of them, fewer at the end) are outstanding; after the
         // barrier everyone's have, and the stage of tile t - 1 is free.
-        if (NST == 3 && t + 1 < N) barrier_vm<PT>();
-        else barrier_vm<0>();
+        if constexpr (NST >= 4) {
+          if (t + 2 < N) barrier_vm<2 * PT>();
+          else if (t + 1 < N) barrier_vm<PT>();
+          else barrier_vm<0>();
+        } else if constexpr (NST == 3) {
+          if (t + 1 < N) barrier_vm<PT>();
+          else barrier_vm<0>();
+        } else {
+          barrier_vm<0>();
+        }
         if (t % DCH == 0 && t >= DCH && t + DCH < n1) fill_desc(t / DCH + 1);
         if (NST > 1 && t + NST - 1 < N) issue(t + NST - 1, std::integral_constant<int, (S + NST - 1) % NST>{});
         compute(t, sc);
@@ -825,7 +834,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   constexpr int RB = NTILE * TB;
   constexpr int SB = RB + 8 * kB * 4;               // bytes per stage
   constexpr int BUDGET = 152 * 1024;
-  constexpr int NST = 3 * SB <= BUDGET ? 3 : (2 * SB <= BUDGET ? 2 : 1);
+  constexpr int NST = 4 * SB <= BUDGET ? 4 : (3 * SB <= BUDGET ? 3 : (2 * SB <= BUDGET ? 2 : 1));
   constexpr int PT = NTILE * DPW + 2;               // direct loads per wave and tile
   constexpr int DCH = 256;
   using KT = SwizzledTile<KROW>;
@@ -834,6 +843,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   __shared__ __align__(1024) char sS0[SB];
   __shared__ __align__(1024) char sS1[NST > 1 ? SB : 16];
   __shared__ __align__(1024) char sS2[NST > 2 ? SB : 16];
+  __shared__ __align__(1024) char sS3[NST > 3 ? SB : 16];
   __shared__ float sCol[2][kB];
   __shared__ uint32_t sDesc[2][DCH];                // tile -> query tile | valid rows << 16
 
@@ -945,7 +955,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   // wave 2: φ'; the others repeat the lse row into unused slots).
   auto issue = [&](int n, auto sc) {
     constexpr int S = decltype(sc)::value;
-    char* st = S == 0 ? sS0 : (S == 1 ? sS1 : sS2);
+    char* st = S == 0 ? sS0 : (S == 1 ? sS1 : (S == 2 ? sS2 : sS3));
     const uint32_t d = desc(n);
     const int i = int(d & 0xFFFFu), m = int(d >> 16);
     const size_t rowb = size_t(h) * a.L + size_t(i) * kB;
@@ -1000,7 +1010,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
 
   auto compute = [&](int n, auto sc) {
     constexpr int S = decltype(sc)::value;
-    const char* sk = S == 0 ? sS0 : (S == 1 ? sS1 : sS2);
+    const char* sk = S == 0 ? sS0 : (S == 1 ? sS1 : (S == 2 ? sS2 : sS3));
     const int m = int(desc(n) >> 16);
     constexpr int NA = SPLIT ? NKD : 1, NTA = SPLIT ? NT : 1;
     AB qa[NA], ga[NA], qta[NTA], gta[NTA];
@@ -1174,8 +1184,16 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
         // Tile n has landed once at most the loads issued after it are outstanding (the
         // next tile's, and a dw̃ store); after the barrier everyone's have, and the stage
         // of tile n - 1 is free.
-        if (NST == 3 && n + 1 < N) barrier_vm<PT>();
-        else barrier_vm<0>();
+        if constexpr (NST >= 4) {
+          if (n + 2 < N) barrier_vm<2 * PT>();
+          else if (n + 1 < N) barrier_vm<PT>();
+          else barrier_vm<0>();
+        } else if constexpr (NST == 3) {
+          if (n + 1 < N) barrier_vm<PT>();
+          else barrier_vm<0>();
+        } else {
+          barrier_vm<0>();
+        }
         if (n % DCH == 0 && n >= DCH && n + DCH < N) fill_desc(n / DCH + 1);
         if (NST > 1 && n + NST - 1 < N) issue(n + NST - 1, std::integral_constant<int, (S + NST - 1) % NST>{});
         compute(n, sc);
