@@ -285,3 +285,44 @@ def test_pwt_row_single_pass(gpu_lib, case):
         assert e1 <= TOL_SAME_SEL[inp.cfg.dtype] and e2 <= TOL_SAME_SEL[inp.cfg.dtype]
         assert np.all(o1[h][~ok] == 0) and np.all(o2[h][~ok] == 0)
         assert rel_l2(o1[h][ok], o2[h][ok]) <= (1e-5 if inp.cfg.dtype == "f32" else 1e-2)
+
+
+@pytest.mark.parametrize("bits,kw", [("W_LINEAR", dict(w_map="linear")), ("W_NOGATE", dict(guard="none"))])
+def test_pwt_row_mode_bits_bf16(gpu_lib, bits, kw):
+    """The bf16 per-row-w pass (virtual tokens in their own kernel, merged with the DROP
+    pass) under both mode bits, against the oracle on the same selection."""
+    inp, K_sel = _case("bf16_d128_ragged")
+    sel, w = oracle_selection(inp, K_sel)
+    g = gpu_attention_on(gpu_lib, inp, K_sel, "pwt_row", sel, w, mode_bits=getattr(gpu_lib, bits))
+    ok = valid_rows(inp)
+    for h in range(inp.H):
+        ref = _oracle(inp, h, "pwt_row", K_sel, idx=sel[h], **kw)
+        err = rel_l2(g["O"][h][ok], ref["O"][ok])
+        print(f"pwt_row {bits} h{h}: rel-L2 {err:.2e}")
+        assert err <= TOL_SAME_SEL["bf16"]
+        assert np.abs(g["lse"][h][ok] - ref["lse"][ok]).max() < 2e-2
+
+
+@pytest.mark.parametrize("gate", [True, False])
+def test_pwt_row_gate_fires_bf16(gpu_lib, gate):
+    """Blocks with widely spread keys, so that the per-row w exceeds ln n_j for many rows:
+    the gate decides the output (the gated and ungated oracles differ by ~80 %); the bf16
+    per-row-w pass must follow the oracle either way."""
+    inp = synth.random_blocks(153, H=1, nb=8, d=128, dtype="bf16", block_len=[64, 64, 40, 64, 64, 64, 17, 64])
+    ok = valid_rows(inp)
+    k = synth.bf16_bits_to_f32(inp.K)
+    k[0, 2 * 64:3 * 64] *= 6.0
+    k[0, 5 * 64:6 * 64] *= 6.0
+    k[:, ~ok, :] = 0.0
+    inp.K[...] = synth.f32_to_bf16_bits(k)
+    K_sel = 3
+    sel, w = oracle_selection(inp, K_sel)
+    bits = 0 if gate else gpu_lib.W_NOGATE
+    g = gpu_attention_on(gpu_lib, inp, K_sel, "pwt_row", sel, w, mode_bits=bits)
+    kw = {} if gate else dict(guard="none")
+    ref = _oracle(inp, 0, "pwt_row", K_sel, idx=sel[0], **kw)
+    other = _oracle(inp, 0, "pwt_row", K_sel, idx=sel[0], **({"guard": "none"} if gate else {}))
+    assert rel_l2(other["O"][ok], ref["O"][ok]) > 0.1           # the gate matters here
+    err = rel_l2(g["O"][0][ok], ref["O"][ok])
+    print(f"pwt_row gate={gate}: rel-L2 {err:.2e}")
+    assert err <= TOL_SAME_SEL["bf16"]
