@@ -361,11 +361,14 @@ def main():
                                                                                 64, K_sel), 16),
                              dtype=torch.uint8, device="cuda")
         pisa.attention_fwd(Q, K, V, st, idx, mask, wt, K_sel, mode, blt, out=O, lse=lse)
+        # with the forward output (Δ = dO·O read), as a training step has it; and without
         ms_bwd = timed(lambda: pisa.attention_bwd(Q, K, V, st, idx, mask, wt, K_sel, lse, dO, mode, blt,
-                                                  out=gbuf, workspace=ws_bwd), 3)
+                                                  out=gbuf, workspace=ws_bwd, O=O), 3)
+        ms_bwd_no_o = timed(lambda: pisa.attention_bwd(Q, K, V, st, idx, mask, wt, K_sel, lse, dO, mode, blt,
+                                                       out=gbuf, workspace=ws_bwd), 3)
         fb = flop_counts(idx.cpu().numpy(), bl, d, mode)
         bflops = int(2.5 * (fb["exact"] + fb["virtual"]) + 2 * fb["first"] + 4 * d * d * int(bl.sum()) * H)
-        backward = {"ms": round(ms_bwd, 4), "algorithmic_flops": bflops,
+        backward = {"ms": round(ms_bwd, 4), "ms_without_o": round(ms_bwd_no_o, 4), "algorithmic_flops": bflops,
                     "tflops": round(bflops / (ms_bwd * 1e-3) / 1e12, 2),
                     "ratio_to_forward_attention": round(ms_bwd / ms_attn, 2)}
         del gbuf, ws_bwd, dO

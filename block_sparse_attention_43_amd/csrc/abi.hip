@@ -305,14 +305,15 @@ pisa_status pisa_attention_bwd(pisa_dtype dt, const void* Q, const void* K, cons
                                const pisa_stats* st, const int32_t* idx, const uint32_t* mask,
                                const float* wt, int H, int L, int d, int B,
                                const int32_t* block_len, int K_sel, unsigned mode, const float* lse,
-                               const void* dO, float* dQ, float* dK, float* dV, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               const void* O, const void* dO, float* dQ, float* dK, float* dV,
+                               void* workspace, size_t workspace_bytes, void* stream) {
   PISA_TRY(check_dtype(dt));
   PISA_TRY(check_shape(H, L, d, B));
   PISA_TRY(check_ptr(Q, "Q"));
   PISA_TRY(check_ptr(K, "K"));
   PISA_TRY(check_ptr(V, "V"));
   PISA_TRY(check_ptr(dO, "dO"));
+  if (O) PISA_TRY(check_ptr(O, "O"));
   PISA_TRY(check_ptr(lse, "lse", false));
   PISA_TRY(check_ptr(dQ, "dQ"));
   PISA_TRY(check_ptr(dK, "dK"));
@@ -346,6 +347,7 @@ pisa_status pisa_attention_bwd(pisa_dtype dt, const void* Q, const void* K, cons
   a.K = K;
   a.V = V;
   a.dO = dO;
+  a.O = O;
   a.lse = lse;
   a.block_len = block_len;
   a.idx = idx;

@@ -18,9 +18,11 @@
 //
 // Kernels, in launch order (all sums in a fixed order: repeated runs are bit-identical):
 //   bwd_rows_kernel      per query tile: dO_t·u_t, the pooled \overline{q²}_i
+//   bwd_delta_kernel     (forward output given) Δ_O = dO_t·O_t per row, corrected to Δ_t
+//                        in the dQ sweep
 //   csr_count/scan/fill  per key block: the query tiles that selected it, ascending
-//   bwd_query_kernel     per query tile, one sweep: Δ_t = Σ P dP and dQ from the exact and
-//                        virtual tiles and H̄ᵀ, Ā_t
+//   bwd_query_kernel     per query tile, one sweep: dQ from the exact and virtual tiles and
+//                        H̄ᵀ, Ā_t, and (no forward output given) Δ_t = Σ P dP
 //   bwd_key_kernel       per key block: dK, dV of its exact keys over the tiles that
 //                        selected it; per centroid group and chunk of query tiles: dk̄, dv̄
 //                        and (PWT) dw̃
@@ -435,19 +437,61 @@ __global__ __launch_bounds__(256) void csr_fill_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Δ_t = dO_t·O_t from the forward output, in fp32, for rows with support (valid slot,
+// finite lse); 0 elsewhere, as the single-sweep form writes it. LPR lanes per row, each
+// one 16-byte chunk of O and of dO, summed across the row's lanes.
+template <class T, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
+  constexpr int EPL = 16 / int(sizeof(T)), LPR = D / EPL, RPB = 256 / LPR;
+  static_assert(LPR >= 1 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "lanes per row");
+  const size_t rows = size_t(a.H) * a.L;
+  const size_t r = size_t(blockIdx.x) * RPB + threadIdx.x / LPR;
+  const int c = int(threadIdx.x % LPR);
+  float s = 0.f;
+  bool live = false;
+  if (r < rows) {
+    const int t = int(r % size_t(a.L)), blk = t / kB;
+    const int m = min(max(a.block_len ? a.block_len[blk] : kB, 1), kB);
+    live = (t % kB) < m && a.lse[r] > NEG_INF;
+    if (live) {
+      const size_t off = r * D + size_t(c) * EPL;
+      const u32x4 vo = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.O) + off);
+      const u32x4 vg = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dO) + off);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (sizeof(T) == 2) {
+          s = fmaf(__uint_as_float(vo[k] << 16), __uint_as_float(vg[k] << 16), s);
+          s = fmaf(__uint_as_float(vo[k] & 0xFFFF0000u), __uint_as_float(vg[k] & 0xFFFF0000u), s);
+        } else {
+          s = fmaf(__uint_as_float(vo[k]), __uint_as_float(vg[k]), s);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = LPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (r < rows && c == 0) a.delta[r] = live ? s : 0.f;
+}
+
+// ---------------------------------------------------------------------------------------
 // Per query tile: dQ over its exact tiles and centroid groups, then + Ā_t H̄ᵀ dO_t.
 // Wave (wk, wq) computes Sᵀ and dPᵀ for key half wk and query half wq (keys fed through
 // feed_row, so registers are the B operands of the products with Kᵀ); the two key halves
 // are merged at the end.
-// One sweep: dQ is linear in Δ, dq_t = Σ P dP k - Δ_t Σ P k, so the sweep accumulates
-// dQ₀ = Kᵀ (P∘dP)ᵀ, kp = Kᵀ Pᵀ and Δ_t = Σ P dP (the definition of dO_t·o_t, in fp32 from
-// the recomputed P and dP) and forms dQ₀ - Δ kp at the end. P∘dP and P enter their products
-// as hi + lo bf16 pairs, so the cancellation in the difference costs no bf16 rounding.
+// DIR (Δ_O = dO·O from bwd_delta_kernel): dS = P∘(dP - Δ_O) and P enter one product each
+// with Kᵀ, in the input type, and the sweep sums ε = Σ dS in fp32 (= Δ - Δ_O: O's
+// rounding, which Σ P k would otherwise amplify), then forms dQ = Kᵀ dSᵀ - ε kp and hands
+// Δ = Δ_O + ε to the key sweep.
+// Otherwise one sweep without Δ: dQ is linear in Δ, dq_t = Σ P dP k - Δ_t Σ P k, so the
+// sweep accumulates dQ₀ = Kᵀ (P∘dP)ᵀ, kp = Kᵀ Pᵀ and Δ_t = Σ P dP (the definition of
+// dO_t·o_t, in fp32 from the recomputed P and dP) and forms dQ₀ - Δ kp at the end. P∘dP
+// and P enter their products as hi + lo bf16 pairs, so the cancellation in the difference
+// costs no bf16 rounding.
 // Each tile's operands (K or k̄ rows, V or v̄ rows, Kᵀ or k̄ᵀ, and a virtual tile's biases
 // and 1 / n_j) arrive by direct global->LDS loads into a ring of NST stages, NST - 1 tiles
 // ahead of use, each stage its own LDS object (so the compiler sees that reading one stage
 // does not wait for the loads landing in another); tiles are swizzled rows (SwizzledTile).
-template <class T, int D, int MODE>
+template <class T, int D, int MODE, bool DIR>
 __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   using M = typename MmaFor<T>::type;
   using AB = typename M::AB;
@@ -492,6 +536,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   const bool qvalid = qrow < m && lse > NEG_INF;
   const float lse2 = qvalid ? lse * kLog2e : POS_INF;   // P = 0 on rows without support
   const float gu = a.gu[row0 + qrow];
+  const float dl = DIR && qvalid ? a.delta[row0 + qrow] : 0.f;
 
   const T* Qh = static_cast<const T*>(a.Q) + size_t(h) * a.L * D;
   const T* Gh = static_cast<const T*>(a.dO) + size_t(h) * a.L * D;
@@ -685,6 +730,13 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
         dp = fmaf(gu, invn[r], dp);
         abar = fmaf(P, invn[r], abar);
       }
+      if constexpr (DIR) {
+        const float ds = P * (dp - dl);
+        dsum += ds;                                // ε
+        s[r] = ds;
+        p[r] = P;
+        continue;
+      }
       const float pd = P * dp;
       dsum += pd;
       s[r] = pd;                                   // P∘dP, then its hi part
@@ -700,13 +752,12 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
     static_for<0, NKH>([&](auto ksc) {
       constexpr int ks = decltype(ksc)::value;
       const AB bs = M::template packv<ks * KH>(s);
-      const AB bp = M::template packv<ks * KH>(p);
 #pragma unroll
       for (int et = 0; et < NET; ++et) {
         const AB kt = SPLIT ? ta[(et * NKH + ks) % NTA] : M::load(reinterpret_cast<const T*>(sk + tad[et * NKH + ks]));
         dqt[et] = M::mma(kt, bs, dqt[et]);
-        kpt[et] = M::mma(kt, bp, kpt[et]);
-        if constexpr (SPLIT) {
+        kpt[et] = M::mma(kt, M::template packv<ks * KH>(p), kpt[et]);
+        if constexpr (SPLIT && !DIR) {
           dqt[et] = M::mma(kt, M::template packv<ks * KH>(slo), dqt[et]);
           kpt[et] = M::mma(kt, M::template packv<ks * KH>(plo), kpt[et]);
         }
@@ -751,12 +802,13 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
     });
   }
 
-  // Δ of this lane's query over both key halves, then this wave's share dQ₀ - Δ kp.
+  // Δ (DIR: ε) of this lane's query over both key halves, then this wave's share of
+  // dQ₀ - Δ kp (DIR: Kᵀ dSᵀ - ε kp); Δ (DIR: Δ_O + ε) for the key sweep.
   dsum = sum_halves(dsum);
   if (g == 0) sDel[wk][qrow] = dsum;
   __syncthreads();
   const float delta = qvalid ? sDel[0][qrow] + sDel[1][qrow] : 0.f;
-  if (wk == 0 && g == 0) a.delta[row0 + qrow] = delta;
+  if (wk == 0 && g == 0) a.delta[row0 + qrow] = qvalid ? dl + delta : 0.f;
 #pragma unroll
   for (int et = 0; et < NET; ++et)
 #pragma unroll
@@ -1709,7 +1761,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   PISA_CHECK();
   hipLaunchKernelGGL(csr_fill_kernel, blocks, dim3(256), 0, s, a);
   PISA_CHECK();
-  hipLaunchKernelGGL((bwd_query_kernel<T, D, MODE>), dim3(unsigned(a.H) * unsigned(a.nb)), dim3(256), 0, s, a);
+  if (a.O) {
+    constexpr unsigned RPB = 256u / (D * sizeof(T) / 16u);
+    const size_t rows = size_t(a.H) * size_t(a.L);
+    hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3(unsigned((rows + RPB - 1) / RPB)), dim3(256), 0, s, a);
+    PISA_CHECK();
+    hipLaunchKernelGGL((bwd_query_kernel<T, D, MODE, true>), dim3(unsigned(a.H) * unsigned(a.nb)), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((bwd_query_kernel<T, D, MODE, false>), dim3(unsigned(a.H) * unsigned(a.nb)), dim3(256), 0, s, a);
+  }
   PISA_CHECK();
   hipLaunchKernelGGL((bwd_key_kernel<T, D, MODE, false>), dim3(unsigned(a.H) * unsigned(a.nb)), dim3(256), 0, s, a);
   PISA_CHECK();

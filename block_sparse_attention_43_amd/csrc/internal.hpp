@@ -111,6 +111,7 @@ struct BwdArgs {
   const void* K;
   const void* V;
   const void* dO;
+  const void* O;     // [H][L][d] the forward output, or null (Δ then formed in the dQ sweep)
   const float* lse;
   const int32_t* block_len;
   const int32_t* idx;
@@ -123,7 +124,7 @@ struct BwdArgs {
   float* dQ;
   float* dK;
   float* dV;
-  float* delta;      // [H][L]   Δ_t = dO_t·o_t, formed as Σ P dP
+  float* delta;      // [H][L]   Δ_t = dO_t·o_t: dO·O from O, else formed as Σ P dP
   float* gu;         // [H][L]   dO·(H̄ q)
   float* abar;       // [H][L]   Ā_t
   float* qsq;        // [H][nb][d] pooled q² (PWT) or null

@@ -90,7 +90,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pisa_attention_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.pisa_attention_bwd_workspace_bytes.restype = sz
     lib.pisa_attention_bwd.argtypes = [i32, vp, vp, vp, sp, vp, vp, vp, i32, i32, i32, i32, vp, i32, u32,
-                                       vp, vp, vp, vp, vp, vp, sz, vp]
+                                       vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.pisa_attention_bwd.restype = i32
     ip = ctypes.POINTER(ctypes.c_int32)
     lib.pisa_cube_layout.argtypes = [i32, i32, i32, i32, i32, i32, ip, ip, sz, ctypes.POINTER(ctypes.c_int)]
@@ -259,9 +259,10 @@ def attention_fwd(Q, K, V, st: Stats, idx, mask, wt, K_sel: int, mode="pwt", blo
 
 
 def attention_bwd(Q, K, V, st: Stats, idx, mask, wt, K_sel: int, lse, dO, mode="pwt", block_len=None,
-                  out=None, workspace=None, stream=None):
+                  out=None, workspace=None, stream=None, O=None):
     """Gradients (dQ, dK, dV) float32 [H, L, d] of sum(dO * O) for the forward call that
-    produced lse with the same arguments (DROP, PISA or PWT)."""
+    produced lse with the same arguments (DROP, PISA or PWT). Passing that call's output O
+    lets Δ = dO·O be read instead of formed in the dQ sweep (half its products)."""
     lib = load()
     H, L, d = _shape(Q)
     m = MODES[mode] if isinstance(mode, str) else int(mode)
@@ -274,7 +275,7 @@ def attention_bwd(Q, K, V, st: Stats, idx, mask, wt, K_sel: int, lse, dO, mode="
     s = st.struct()
     _check(lib.pisa_attention_bwd(_dtype_code(Q), _ptr(Q), _ptr(K), _ptr(V), ctypes.byref(s), _ptr(idx),
                                   _ptr(mask), _ptr(wt), H, L, d, B, _ptr(block_len), K_sel, m, _ptr(lse),
-                                  _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(workspace), workspace.numel(),
+                                  _ptr(O), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(workspace), workspace.numel(),
                                   _stream(stream)))
     return dQ, dK, dV
 

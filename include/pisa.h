@@ -269,11 +269,16 @@ size_t pisa_attention_bwd_workspace_bytes(pisa_dtype dt, int H, int L, int d, in
  *   Inputs   Q, K, V, st, idx, mask, wt, block_len, K_sel, mode: as given to the forward
  *            call (mask is required for every mode and must match idx; st needs kbar, vsum,
  *            ksig2 and hbarT); lse: that call's output; dO [H][L][d] dtype `dt`.
+ *            O [H][L][d] dtype `dt`: that call's output, or NULL (see Δ below).
  *   Outputs  dQ, dK, dV [H][L][d] float32, overwritten (zeros on padded slots).
  *   Workspace pisa_attention_bwd_workspace_bytes(dt, H, L, d, B, K_sel) bytes.
  * With P = e^{logit - lse} for every exact key and virtual token, u_t = H̄ q_t,
- * Ā_t = Σ_j P_{t,j} / n_j and Δ_t = dO_t·o_t (formed in fp32 as Σ P·dP over every exact key
- * and virtual token, with dP = dO·v, or dO·v̄_j + dO·u_t / n_j, which is dO·o exactly):
+ * Ā_t = Σ_j P_{t,j} / n_j and Δ_t = dO_t·o_t. With O given, Δ_O = dO·O in fp32, and dS =
+ * P(dP - Δ_O) and P enter the dQ products in the input type (two products per tile); the
+ * fp32 sum ε = Σ dS = Δ - Δ_O then removes O's rounding (dq -= ε Σ P k, Δ = Δ_O + ε). With O NULL,
+ * Δ is formed in fp32 as Σ P·dP over every exact key and virtual token (dP = dO·v, or
+ * dO·v̄_j + dO·u_t / n_j, which is dO·o exactly) in the same sweep, and dQ as
+ * Σ P dP k - Δ Σ P k with hi + lo operand pairs (four products per tile; no rounding of O):
  *   dq_t  = Σ P(dO·v - Δ) k (exact) + Σ P(dO·v̄_j + dO·u_t / n_j - Δ) k̄_j + Ā_t H̄ᵀ dO_t
  *           + (2/m_i) q_t ∘ ½ Σ_j dw̃_{i,j} σ²_j                         (PWT)
  *   dk, dv of exact keys from the same terms; dk̄_j, dv̄_j, dH̄ = Σ_t Ā_t dO_t q_tᵀ and
@@ -286,8 +291,8 @@ pisa_status pisa_attention_bwd(pisa_dtype dt, const void* Q, const void* K, cons
                                const pisa_stats* st, const int32_t* idx, const uint32_t* mask,
                                const float* wt, int H, int L, int d, int B,
                                const int32_t* block_len, int K_sel, unsigned mode, const float* lse,
-                               const void* dO, float* dQ, float* dK, float* dV, void* workspace,
-                               size_t workspace_bytes, void* stream);
+                               const void* O, const void* dO, float* dQ, float* dK, float* dV,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Layout step (blog "Sparse Linear Attention", notation: tokens are cut into blocks of B;

@@ -167,7 +167,7 @@ def test_backward_argument_errors(lib, case, status, msg):
     a = dict(mode=2, mask=16, wt=16, lse=16, ws=1 << 30)
     a.update(case)
     r = lib.pisa_attention_bwd(1, 16, 16, 16, ctypes.byref(st), 16, a["mask"], a["wt"], 1, 1024, 64, 64, None, 4,
-                               a["mode"], a["lse"], 16, 16, 16, 16, 16, a["ws"], None)
+                               a["mode"], a["lse"], None, 16, 16, 16, 16, 16, a["ws"], None)
     assert r == status and msg in lib.pisa_last_error().decode()
     assert lib.pisa_attention_bwd_workspace_bytes(1, 1, 1024, 64, 64, 4) > 0
     assert lib.pisa_attention_bwd_workspace_bytes(1, 1, 1024, 64, 64, 17) == 0
