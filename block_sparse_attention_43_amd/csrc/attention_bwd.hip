@@ -1171,14 +1171,9 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
         if (j * kB + lane < nb) a.dwt[(size_t(h) * nb + x) * nb + j * kB + lane] = dph * (c0 + c1);
       }
     }
-    f32x16 lo;                                     // dS as hi + lo bf16 parts (see bwd_query_kernel)
+    // dS enters dKᵀ in the input type, as P enters dVᵀ: Σ_t dS q_t has no cancellation
+    // that would amplify its rounding (unlike Σ_k dS k in the dQ sweep).
     if constexpr (SPLIT) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float hi = to_f32(from_f32<T>(s[r]));
-        lo[r] = s[r] - hi;
-        s[r] = hi;
-      }
       // Qᵀ and dOᵀ fragments from the Q and dO rows by transpose reads, once the score
       // operands are dead: fragment x = (et, ks) is two reads (rows +0..3, +4..7).
       static_assert(2 * NT % 8 == 0, "transpose read blocks");
@@ -1216,7 +1211,6 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
         const AB qa_t = SPLIT ? qta[x % NTA] : M::load(reinterpret_cast<const T*>(sk + 2 * TB + tad[x]));
         dvt[et] = M::mma(ga_t, bp, dvt[et]);
         dkt[et] = M::mma(qa_t, bs, dkt[et]);
-        if constexpr (SPLIT) dkt[et] = M::mma(qa_t, M::template packv<ks * KH>(lo), dkt[et]);
       }
     });
   };

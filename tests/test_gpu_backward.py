@@ -4,8 +4,8 @@ are pinned to central differences of the forward definition.
 Both sides take the oracle's selection and PWT weights (the GPU forward runs on them too,
 so lse comes from the GPU), and the same seeded dO. Bars: rel-L2 of dQ, dK, dV over valid
 slots <= 1e-4 for fp32 inputs and <= 2e-2 for bf16 inputs (P enters dV in bf16 as in the
-forward pass; dS enters dK as a hi + lo bf16 pair, and dQ as one too when the forward output
-is not passed, in bf16 when it is); padded slots exactly 0. `with_o` passes the forward
+forward pass, and so does dS into dK; dS enters dQ as a hi + lo bf16 pair when the forward
+output is not passed, in bf16 when it is); padded slots exactly 0. `with_o` passes the forward
 output O, so the dQ sweep starts from Δ_O = dO·O and corrects O's bf16 rounding with the
 fp32 sum of dS (without that correction bf16 dQ misses the bar: rel-L2 ~2.4e-2 on
 bf16_d128_ragged, from Δ_O's error times the keys' common mean).
