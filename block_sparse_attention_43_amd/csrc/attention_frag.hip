@@ -676,8 +676,8 @@ hipError_t launch_attention_frag(int mode, const AttnArgs& a, hipStream_t s) {
 // every 64-centroid group for both query halves, with its own running max, and the halves
 // merge at the end. Centroid and v̄ᵀ fragments come in MFMA operand order from the
 // statistics pass (packed tiles), σ²/2 fragments are formed from σ² in the same row order,
-// so no operand goes through LDS; a group's loads are issued before the previous group's
-// arithmetic.
+// so no operand goes through LDS; a group's centroid and v̄ᵀ fragments are loaded into
+// their registers as soon as the previous group's last product has read them.
 template <int D>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void virtual_row_kernel(AttnArgs a) {
@@ -722,13 +722,18 @@ void virtual_row_kernel(AttnArgs a) {
   bf16x8 kb[NKD], sg[NKD], vb[NVF];
   uint32_t mword = 0u;
   int blen[16];
-  auto load_group = [&](int grp) {
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbh, uint32_t(ngrp) * TB), rv = make_rsrc(vbh, uint32_t(ngrp) * TB);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbh, uint32_t(ngrp) * TB), rv = make_rsrc(vbh, uint32_t(ngrp) * TB);
+  auto load_k = [&](int grp) {
     const int off = grp * TB + kh * HB + lane * 16;
 #pragma unroll
     for (int f = 0; f < NKD; ++f) kb[f] = ld_frag(rk, off + f * 1024, 0);
+  };
+  auto load_v = [&](int grp) {
+    const int off = grp * TB + kh * HB + lane * 16;
 #pragma unroll
     for (int f = 0; f < NVF; ++f) vb[f] = ld_frag(rv, off + f * 1024, 0);
+  };
+  auto load_group = [&](int grp) {
     const int jr = grp * kB + 32 * kh + key_of_row(l32);       // this lane's A row
     const float* sr = sig + size_t(min(jr, nb - 1)) * D + 8 * g;
     const float hv = jr < nb ? 0.5f : 0.f;
@@ -749,6 +754,8 @@ void virtual_row_kernel(AttnArgs a) {
     }
   };
 
+  load_k(0);
+  load_v(0);
   for (int grp = 0; grp < ngrp; ++grp) {
     load_group(grp);
     const int jw = grp * kB + 32 * kh;
@@ -774,6 +781,7 @@ void virtual_row_kernel(AttnArgs a) {
         s = MmaBF16::mma(kb[ks], qf[u][ks], s);
         w = MmaBF16::mma(sg[ks], MmaBF16::pack(qv), w);
       }
+      if (u == 1 && grp + 1 < ngrp) load_k(grp + 1);
       float t[16], rmx = NEG_INF;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -809,6 +817,7 @@ void virtual_row_kernel(AttnArgs a) {
 #pragma unroll
         for (int et = 0; et < NET; ++et) acc[et][u] = MmaBF16::mma(vb[2 * et + ks], pb, acc[et][u]);
       }
+      if (u == 1 && grp + 1 < ngrp) load_v(grp + 1);
     }
   }
 
