@@ -652,8 +652,11 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
     constexpr int NA = SPLIT ? NKD : 1, NTA = SPLIT ? NT : 1;
     AB ka[NA], va[NA], ta[NTA];
     float bias[16], invn[16];
+    f32x16 s = zero16(), p = zero16();
     if constexpr (SPLIT) {
       // bf16: every operand in three blocks of 16-byte reads, the rows' biases in a fourth.
+      // DIR: the V rows are read while the Sᵀ products run, the Kᵀ fragments and biases
+      // while the dPᵀ products run (the fences keep the products between the read blocks).
       static_assert(NKD == 4 || NKD == 8, "fragments per block");
       const uint32_t base = lds_addr(sk);
       uint32_t ad[NKD];
@@ -661,11 +664,21 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < NKD; ++ks) ad[ks] = base + kad[ks];
       lds_read_x16<NKD, 0>(rk, ad);
-      lds_read_x16<NKD, TB>(rv, ad);
+      if constexpr (DIR) {
 #pragma unroll
-      for (int ks = 0; ks < NKD; ++ks) {
-        ka[ks] = __builtin_bit_cast(AB, rk[ks]);
-        va[ks] = __builtin_bit_cast(AB, rv[ks]);
+        for (int ks = 0; ks < NKD; ++ks) s = M::mma(__builtin_bit_cast(AB, rk[ks]), qf[ks], s);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_read_x16<NKD, TB>(rv, ad);
+#pragma unroll
+        for (int ks = 0; ks < NKD; ++ks) p = M::mma(__builtin_bit_cast(AB, rv[ks]), gf[ks], p);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        lds_read_x16<NKD, TB>(rv, ad);
+#pragma unroll
+        for (int ks = 0; ks < NKD; ++ks) {
+          ka[ks] = __builtin_bit_cast(AB, rk[ks]);
+          va[ks] = __builtin_bit_cast(AB, rv[ks]);
+        }
       }
       // Kᵀ fragments from the K rows by transpose reads: fragment x = (et, ks) is two
       // reads (keys +0..3, +4..7 of its k range).
@@ -713,13 +726,12 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
         invn[r] = 0.f;
       }
     }
-    auto kfrag = [&](int ks) { return SPLIT ? ka[ks % NA] : M::load(reinterpret_cast<const T*>(sk + kad[ks])); };
-    auto vfrag = [&](int ks) { return SPLIT ? va[ks % NA] : M::load(reinterpret_cast<const T*>(sk + TB + kad[ks])); };
-    f32x16 s = zero16(), p = zero16();
+    if constexpr (!(SPLIT && DIR)) {
 #pragma unroll
-    for (int ks = 0; ks < NKD; ++ks) {
-      s = M::mma(kfrag(ks), qf[ks], s);
-      p = M::mma(vfrag(ks), gf[ks], p);
+      for (int ks = 0; ks < NKD; ++ks) {
+        s = M::mma(SPLIT ? ka[ks % NA] : M::load(reinterpret_cast<const T*>(sk + kad[ks])), qf[ks], s);
+        p = M::mma(SPLIT ? va[ks % NA] : M::load(reinterpret_cast<const T*>(sk + TB + kad[ks])), gf[ks], p);
+      }
     }
     f32x16 slo, plo;
 #pragma unroll
