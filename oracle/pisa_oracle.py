@@ -379,7 +379,7 @@ def attention_head(Q, K, V, B: int, block_len=None, K_sel: int = 0, mode: str = 
             w = np.zeros_like(s)
         elif w_kind == "pooled":
             pool = pq["qsq"][i] if pooling == "sqmean" else pq["qbar_sq"][i]
-            w = np.broadcast_to(0.5 * (st["sig2"][U] @ pool), s.shape)
+            w = np.broadcast_to(pooled_w(pool[None, :], st["sig2"][U])[0], s.shape)
         elif w_kind == "rowdiag":
             w = 0.5 * (q ** 2) @ st["sig2"][U].T
         elif w_kind == "row":
@@ -559,24 +559,7 @@ def attention_head_backward(Q, K, V, dO, B: int, block_len=None, K_sel: int = 0,
     return dict(dQ=dQ, dK=dK, dV=dV, O=O, lse=lse, idx=idx)
 
 
-# ----------------------------------------------------------------------------- multi-head
-def run(Q, K, V, B: int, block_len=None, K_sel: int = 0, mode: str = "pwt", heads=None,
-        tiles=None, idx=None, **overrides) -> dict:
-    """Every head of [H, L_pad, d] float64 inputs; ``idx`` may be [H, nb, K_sel]."""
-    H = Q.shape[0]
-    hs = range(H) if heads is None else heads
-    O = np.zeros(Q.shape)
-    lse = np.full(Q.shape[:2], -np.inf)
-    sel = {}
-    for h in hs:
-        r = attention_head(Q[h], K[h], V[h], B, block_len, K_sel, mode,
-                           idx=None if idx is None else idx[h], tiles=tiles, **overrides)
-        O[h] = r["O"]
-        lse[h] = r["lse"]
-        sel[h] = r["idx"]
-    return dict(O=O, lse=lse, idx=sel)
-
-
+# ----------------------------------------------------------------------------- second-order matrix
 def pooled_w(qsq: np.ndarray, sig2: np.ndarray) -> np.ndarray:
     """w̃_{i,j} = ½ sum_c \\overline{q²}_{i,c} σ²_{j,c}, the [query tile x key block] matrix
     of the diagonal + pooled second-order term (blog, PWT section), before the gate."""

@@ -214,6 +214,48 @@ def test_pooling_is_square_then_mean():
     assert abs(lse_bad[0] - (math.log(2) + q @ c)) < 1e-14
 
 
+def test_pooled_w_hand_computed():
+    """w̃ for one tile of rows a = (1, 2), b = (3, -2) and one block of keys k̄ ± δ with
+    δ = (1, 3), worked by hand (blog, PWT section: ½ Σ_c mean_tile(q_c²) σ²_{j,c}).
+    mean(q²) = ((1 + 9)/2, (4 + 4)/2) = (5, 4); σ² = δ² = (1, 9); w̃ = ½ (5·1 + 4·9) = 20.5.
+    Pooling q̄² instead would give ½ (4·1 + 0·9) = 2, a dropped ½ gives 41."""
+    Q = np.array([[1.0, 2.0], [3.0, -2.0]])
+    kbar, delta = np.array([0.25, -0.5]), np.array([1.0, 3.0])
+    K = np.stack([kbar + delta, kbar - delta])
+    st = orc.block_stats(K, np.zeros((2, 2)), 2)
+    pq = orc.pool_queries(Q, 2)
+    w = orc.pooled_w(pq["qsq"], st["sig2"])
+    assert w.shape == (1, 1)
+    assert w[0, 0] == 20.5
+    # the PWT logit of that block, seen by row a: q·k̄ + ln 2 + w̃ (gate off: 20.5 > ln 2)
+    lse = orc.attention_head(Q, K, np.ones((2, 2)), 2, None, 0, "pwt", guard="none")["lse"]
+    assert abs(lse[0] - (Q[0] @ kbar + math.log(2) + 20.5)) < 1e-12
+
+
+def test_pooled_w_brute_force_loops():
+    """Rectangular case (3 tiles, 5 blocks, ragged) against plain loops over the
+    definition: w̃_{i,j} = ½ Σ_c [(1/m_i) Σ_t q_{t,c}²] [(1/n_j) Σ_k (k_{k,c} - k̄_{j,c})²]."""
+    r = np.random.default_rng(17)
+    B, d = 4, 3
+    bl = np.array([4, 2, 3, 4, 1])
+    Q = r.standard_normal((B * 5, d))
+    K = r.standard_normal((B * 5, d))
+    st = orc.block_stats(K, np.zeros_like(K), B, bl)
+    pq = orc.pool_queries(Q, B, bl)
+    tiles = [0, 2, 3]
+    w = orc.pooled_w(pq["qsq"][tiles], st["sig2"])
+    assert w.shape == (3, 5)
+    for a, i in enumerate(tiles):
+        for j in range(5):
+            tot = 0.0
+            for c in range(d):
+                msq = sum(Q[i * B + t, c] ** 2 for t in range(bl[i])) / bl[i]
+                mean = sum(K[j * B + k, c] for k in range(bl[j])) / bl[j]
+                var = sum((K[j * B + k, c] - mean) ** 2 for k in range(bl[j])) / bl[j]
+                tot += msq * var
+            assert abs(w[a, j] - 0.5 * tot) < 1e-12
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_constant_values_give_constant_output(mode):
     """Softmax output is a weighted mean: V ≡ u gives o = u exactly, which requires the
