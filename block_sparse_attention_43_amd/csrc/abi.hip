@@ -75,8 +75,10 @@ pisa_status select_impl(pisa_dtype dt, const void* Q, const void* Q_pre, const v
   PISA_TRY(check_shape(H, L, d, B));
   if (!rope || wt) PISA_TRY(check_ptr(Q, "Q"));
   PISA_TRY(check_ptr(st, "st", false));
+  if (route > PISA_ROUTE_ERROR) return fail(PISA_ERR_INVALID_ARG, "unknown route %u", route);
   if (!rope) PISA_TRY(check_ptr(st->kbar, "st->kbar"));
-  if (wt) PISA_TRY(check_ptr(st->ksig2, "st->ksig2"));
+  // The predicted-error route reads σ² for w̃ whether or not w̃ is written out.
+  if (wt || route == PISA_ROUTE_ERROR) PISA_TRY(check_ptr(st->ksig2, "st->ksig2"));
   if (rope) {
     PISA_TRY(check_ptr(Q_pre, "Q_pre"));
     PISA_TRY(check_ptr(K_pre, "K_pre"));
@@ -95,7 +97,6 @@ pisa_status select_impl(pisa_dtype dt, const void* Q, const void* Q_pre, const v
     if (rope->pairs != PISA_ROPE_ADJACENT && rope->pairs != PISA_ROPE_HALF)
       return fail(PISA_ERR_INVALID_ARG, "unknown rope->pairs %d", rope->pairs);
   }
-  if (route > PISA_ROUTE_ERROR) return fail(PISA_ERR_INVALID_ARG, "unknown route %u", route);
   if (route != PISA_ROUTE_MEAN) {
     PISA_TRY(check_ptr(st->hnorm, "st->hnorm", false));
     if (!(eps > 0.f) || eps > 3.0e38f) return fail(PISA_ERR_INVALID_ARG, "eps must be finite and > 0 (got %g)", double(eps));

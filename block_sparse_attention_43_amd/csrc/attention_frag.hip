@@ -647,8 +647,9 @@ template <int D, int MODE>
 static hipError_t launch_frag_m(const AttnArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.H) * unsigned(a.nb));
   hipLaunchKernelGGL((attention_frag_kernel<D, MODE, 2>), grid, dim3(128), 0, s, a);
-  // Without block lengths every query tile is full and the second launch would be empty.
-  if (a.block_len) hipLaunchKernelGGL((attention_frag_kernel<D, MODE, 1>), grid, dim3(128), 0, s, a);
+  // The tile counts come from the statistics call's tile order on the device, so the
+  // short-tile launch always runs; its workgroups leave at once when there are none.
+  hipLaunchKernelGGL((attention_frag_kernel<D, MODE, 1>), grid, dim3(128), 0, s, a);
   return hipGetLastError();
 }
 

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libpisa.so")
 
 PISA_F32, PISA_BF16 = 0, 1
 MODE_DROP, MODE_PISA, MODE_PWT, MODE_LITERAL, MODE_PWT_ROW = 0, 1, 2, 3, 4
-W_LINEAR, W_EXP, W_NOGATE = 1 << 4, 1 << 5, 1 << 6
+W_LINEAR, W_NOGATE, W_EXP = 1 << 4, 1 << 5, 1 << 6
 STATS_BLOCK_H, STATS_BLOCK_C, STATS_HNORM = 1 << 0, 1 << 1, 1 << 2
 ROUTE_MEAN, ROUTE_COVARIANCE, ROUTE_ERROR = 0, 1, 2
 ROUTES = {"mean": ROUTE_MEAN, "covariance": ROUTE_COVARIANCE, "error": ROUTE_ERROR}
@@ -128,6 +128,16 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _keep(stream, *tensors):
+    """Buffers the binding allocated on the current stream but hands to work on another
+    stream: tell the caching allocator not to reuse them before that stream is done."""
+    if stream is None or stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def _shape(Q: torch.Tensor):
     if Q.dim() != 3 or not Q.is_contiguous():
         raise ValueError("tensors must be contiguous [H, L, d]")
@@ -179,6 +189,9 @@ def block_stats(K, V, block_len=None, flags: int = 0, out: Stats | None = None, 
     need = lib.pisa_block_stats_workspace_bytes(H, L, d, B)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=K.device)
+        _keep(stream, workspace)
+    if out is None:
+        _keep(stream, st.kbar, st.vsum, st.ksig2, st.hbarT, st.packed, st.hblk, st.cblk, st.hnorm)
     s = st.struct()
     _check(lib.pisa_block_stats(_dtype_code(K), _ptr(K), _ptr(V), H, L, d, B, _ptr(block_len), flags,
                                 ctypes.byref(s), _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -198,11 +211,13 @@ def select_topk(Q, st: Stats, K_sel: int, block_len=None, want_wt: bool = True, 
         idx = torch.empty(H, nb, max(K_sel, 1), dtype=torch.int32, device=Q.device)[:, :, :K_sel]
         mask = torch.empty(H, nb, nw, dtype=torch.int32, device=Q.device) if want_mask else None
         wt = torch.empty(H, nb, nb, dtype=torch.float32, device=Q.device) if want_wt else None
+        _keep(stream, idx, mask, wt)
     else:
         idx, mask, wt = out
     need = lib.pisa_select_workspace_bytes(H, L, d, B)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+        _keep(stream, workspace)
     r = ROUTES[route] if isinstance(route, str) else int(route)
     s = st.struct()
     _check(lib.pisa_select_topk_routed(_dtype_code(Q), _ptr(Q), ctypes.byref(s), H, L, d, B,
@@ -225,6 +240,7 @@ def select_topk_rope(Q, Q_pre, K_pre, pos, widths, base: float, st: Stats, K_sel
         idx = torch.empty(H, nb, max(K_sel, 1), dtype=torch.int32, device=Q_pre.device)[:, :, :K_sel]
         mask = torch.empty(H, nb, nw, dtype=torch.int32, device=Q_pre.device) if want_mask else None
         wt = torch.empty(H, nb, nb, dtype=torch.float32, device=Q_pre.device) if want_wt else None
+        _keep(stream, idx, mask, wt)
     else:
         idx, mask, wt = out
     if pos.dtype != torch.float32 or not pos.is_contiguous() or pos.shape[0] != L:
@@ -234,6 +250,7 @@ def select_topk_rope(Q, Q_pre, K_pre, pos, widths, base: float, st: Stats, K_sel
     if workspace is None:
         workspace = torch.empty(lib.pisa_select_workspace_bytes(H, L, d, B), dtype=torch.uint8,
                                 device=Q_pre.device)
+        _keep(stream, workspace)
     s = st.struct()
     _check(lib.pisa_select_topk_rope(_dtype_code(Q_pre), _ptr(Q), _ptr(Q_pre), _ptr(K_pre), _ptr(pos),
                                      ctypes.byref(rope), ctypes.byref(s), H, L, d, B, _ptr(block_len), K_sel,
@@ -249,8 +266,10 @@ def attention_fwd(Q, K, V, st: Stats, idx, mask, wt, K_sel: int, mode="pwt", blo
     m = MODES[mode] if isinstance(mode, str) else int(mode)
     if out is None:
         out = torch.empty_like(Q)
+        _keep(stream, out)
     if lse is None and want_lse:
         lse = torch.empty(H, L, dtype=torch.float32, device=Q.device)
+        _keep(stream, lse)
     s = st.struct()
     _check(lib.pisa_attention_fwd(_dtype_code(Q), _ptr(Q), _ptr(K), _ptr(V), ctypes.byref(s), _ptr(idx),
                                   _ptr(mask), _ptr(wt), H, L, d, B, _ptr(block_len), K_sel, m, _ptr(out),
@@ -268,10 +287,12 @@ def attention_bwd(Q, K, V, st: Stats, idx, mask, wt, K_sel: int, lse, dO, mode="
     m = MODES[mode] if isinstance(mode, str) else int(mode)
     if out is None:
         out = tuple(torch.empty(H, L, d, dtype=torch.float32, device=Q.device) for _ in range(3))
+        _keep(stream, *out)
     dQ, dK, dV = out
     if workspace is None:
         need = lib.pisa_attention_bwd_workspace_bytes(_dtype_code(Q), H, L, d, B, K_sel)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=Q.device)
+        _keep(stream, workspace)
     s = st.struct()
     _check(lib.pisa_attention_bwd(_dtype_code(Q), _ptr(Q), _ptr(K), _ptr(V), ctypes.byref(s), _ptr(idx),
                                   _ptr(mask), _ptr(wt), H, L, d, B, _ptr(block_len), K_sel, m, _ptr(lse),
@@ -305,6 +326,7 @@ def layout_to_blocks(x, perm, L_pad: int | None = None, out=None, stream=None):
     Lp = perm.numel() if L_pad is None else L_pad
     if out is None:
         out = torch.empty(H, Lp, d, dtype=x.dtype, device=x.device)
+        _keep(stream, out)
     _check(lib.pisa_layout_to_blocks(_dtype_code(x), _ptr(x), H, Ln, Lp, d, _ptr(perm), _ptr(out), _stream(stream)))
     return out
 
@@ -317,6 +339,7 @@ def layout_from_blocks(x, perm, L_nat: int, out=None, stream=None):
     H, Lp, d = x.shape
     if out is None:
         out = torch.empty(H, L_nat, d, dtype=x.dtype, device=x.device)
+        _keep(stream, out)
     _check(lib.pisa_layout_from_blocks(_dtype_code(x), _ptr(x), H, L_nat, Lp, d, _ptr(perm), _ptr(out),
                                        _stream(stream)))
     return out

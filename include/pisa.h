@@ -87,8 +87,9 @@ enum {
 /* Modifier bits of `mode`. */
 enum {
   PISA_W_LINEAR = 1u << 4,  /* φ(w) = ln(1 + w) (the 1 + w form); default for LITERAL */
-  PISA_W_EXP = 1u << 5,     /* φ(w) = w (the e^w form); default for PWT */
-  PISA_W_NOGATE = 1u << 6   /* disable the validity gate (w > ln n_j => w = 0) */
+  PISA_W_NOGATE = 1u << 5,  /* disable the validity gate (w > ln n_j => w = 0) */
+  PISA_W_EXP = 1u << 6      /* φ(w) = w (the e^w form); default for PWT, needed only to
+                               switch LITERAL to it */
 };
 
 /* Flags of pisa_block_stats. */
@@ -243,8 +244,9 @@ pisa_status pisa_select_topk_rope(pisa_dtype dt, const void* Q, const void* Q_pr
  *   φ = 0 (PISA); φ = w̃_{i,j} (PWT); φ = ½ Σ_c q_{t,c}² σ²_{j,c} (PWT_ROW); per-row
  *   w = ½ q_tᵀC_j q_t mapped to ln(1 + w) (LITERAL); w is zeroed when w > ln n_j unless
  *   PISA_W_NOGATE. DROP keeps S_i only.
- * Inputs: Q, K, V [H][L][d] dtype `dt`; st->packed from pisa_block_stats on the same K, V;
- * idx from pisa_select_topk with the same K_sel; mask (required unless DROP); wt
+ * Inputs: Q, K, V [H][L][d] dtype `dt`; st->packed from pisa_block_stats on the same K, V
+ * and the same block_len (the packed tile order holds each query tile's row count from
+ * that call); idx from pisa_select_topk with the same K_sel; mask (required unless DROP); wt
  * (required for PWT). Outputs: O [H][L][d] dtype `dt`; lse [H][L] float or NULL
  * (natural-log log-sum-exp of every row's logits, -inf for padded rows and rows with no
  * support). Out-of-range entries of idx are treated as empty blocks.

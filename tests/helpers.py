@@ -124,8 +124,9 @@ def check_selection(gpu_idx: np.ndarray, scores: np.ndarray, K_sel: int, rtol: f
     """GPU selection (fp32 scores) against fp64 oracle scores (``scores`` row r belongs
     to tile rows[r]). Where the gap between the
     K_sel-th and the next score exceeds the fp32 rounding bound the sets must be equal;
-    inside the bound any choice among the near-tied blocks is valid (and counted).
-    Returns (n_exact_tiles, n_near_tie_tiles, min_gap)."""
+    inside the bound any choice among the near-tied blocks is valid (and counted), except
+    at an exact tie of the fp64 scores (gap 0), where the lower-index rule decides and
+    the sets must be equal. Returns (n_exact_tiles, n_near_tie_tiles, min_gap)."""
     nq, nb = scores.shape
     rows = range(nq) if rows is None else rows
     exact = near = 0
@@ -144,8 +145,8 @@ def check_selection(gpu_idx: np.ndarray, scores: np.ndarray, K_sel: int, rtol: f
         tol = rtol * (np.abs(s).max() + 1e-30)
         gap = kth - nxt
         min_gap = min(min_gap, gap)
-        if gap > tol:
-            assert got == want, f"tile {i}: selection differs with gap {gap:.3e} > tol {tol:.3e}"
+        if gap > tol or gap == 0.0:
+            assert got == want, f"tile {i}: selection differs with gap {gap:.3e} (tol {tol:.3e})"
             exact += 1
         else:
             lo = nxt - tol

@@ -23,8 +23,8 @@ PLAN = {
     "tiny": ([0], None, ["drop", "pisa", "pwt", "literal"]),
     "flux": ([0, 11, 23], None, ["drop", "pisa", "pwt", "literal", "pwt_row"]),
     "wan": ([0, 19, 39], 24, ["pwt", "pisa", "drop", "literal", "pwt_row"]),
-    "hunyuan": ([0, 23], 12, ["pwt", "literal"]),
-    "long": ([0], 64, ["pwt"]),
+    "hunyuan": ([0, 23], 12, ["pwt", "pisa", "drop", "literal", "pwt_row"]),
+    "long": ([0], 64, ["pwt", "pisa", "drop"]),
 }
 
 
