@@ -3,10 +3,16 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "internal.hpp"
 #include "pisa.h"
+
+// Fixed scratch of pisa_block_stats_noalloc: the H̄ partials. Every GPU the library runs
+// on holds its own copy for the life of the process; host code uses the per-device
+// address from hipGetSymbolAddress (stats_scratch below), never the array's name.
+static __device__ __align__(256) char scratch[PISA_STATS_SCRATCH_BYTES];
 
 namespace {
 
@@ -145,6 +151,76 @@ pisa_status select_impl(pisa_dtype dt, const void* Q, const void* Q_pre, const v
   return ok();
 }
 
+// Checks shared by both statistics entry points.
+pisa_status stats_checks(pisa_dtype dt, const void* K, const void* V, int H, int L, int d, int B,
+                         unsigned flags, const pisa_stats* out) {
+  PISA_TRY(check_dtype(dt));
+  PISA_TRY(check_shape(H, L, d, B));
+  PISA_TRY(check_ptr(K, "K"));
+  PISA_TRY(check_ptr(V, "V"));
+  PISA_TRY(check_ptr(out, "out", false));
+  if (flags & ~7u) return fail(PISA_ERR_INVALID_ARG, "unknown stats flags 0x%x", flags);
+  PISA_TRY(check_ptr(out->kbar, "out->kbar"));
+  PISA_TRY(check_ptr(out->vsum, "out->vsum"));
+  PISA_TRY(check_ptr(out->ksig2, "out->ksig2"));
+  PISA_TRY(check_ptr(out->hbarT, "out->hbarT"));
+  PISA_TRY(check_ptr(out->packed, "out->packed"));
+  if (flags & PISA_STATS_BLOCK_H) PISA_TRY(check_ptr(out->hblk, "out->hblk"));
+  if (flags & PISA_STATS_BLOCK_C) PISA_TRY(check_ptr(out->cblk, "out->cblk"));
+  if (flags & PISA_STATS_HNORM) PISA_TRY(check_ptr(out->hnorm, "out->hnorm", false));
+  return PISA_OK;
+}
+
+pisa_status stats_launch(pisa_dtype dt, const void* K, const void* V, int H, int L, int d,
+                         const int32_t* block_len, unsigned flags, const pisa_stats* out,
+                         float* part, int G, void* stream) {
+  pisa::StatsArgs a{};
+  a.K = K;
+  a.V = V;
+  a.block_len = block_len;
+  a.kbar = out->kbar;
+  a.vsum = out->vsum;
+  a.ksig2 = out->ksig2;
+  a.hbarT = out->hbarT;
+  a.hblk = out->hblk;
+  a.cblk = out->cblk;
+  a.hnorm = out->hnorm;
+  a.packed = static_cast<char*>(out->packed);
+  a.part = part;
+  a.H = H;
+  a.L = L;
+  a.d = d;
+  a.pl = pisa::packed_layout(elem_size(dt), H, L, d);
+  a.nb = a.pl.nb;
+  a.nbp = a.pl.nbp;
+  a.G = G;
+  a.ngroups = (a.nb + a.G - 1) / a.G;
+  hipError_t e = pisa::launch_block_stats(dt == PISA_BF16, a, flags, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pisa_block_stats launch");
+  return ok();
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, looked up once per device with that device current.
+pisa_status stats_scratch(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PISA_ERR_UNSUPPORTED, "device %d beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<float*>(g_scratch_ptr[dev]);
+  return PISA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -166,49 +242,32 @@ pisa_status pisa_block_stats(pisa_dtype dt, const void* K, const void* V, int H,
                              int B, const int32_t* block_len, unsigned flags,
                              const pisa_stats* out, void* workspace, size_t workspace_bytes,
                              void* stream) {
-  PISA_TRY(check_dtype(dt));
-  PISA_TRY(check_shape(H, L, d, B));
-  PISA_TRY(check_ptr(K, "K"));
-  PISA_TRY(check_ptr(V, "V"));
-  PISA_TRY(check_ptr(out, "out", false));
-  if (flags & ~7u) return fail(PISA_ERR_INVALID_ARG, "unknown stats flags 0x%x", flags);
-  PISA_TRY(check_ptr(out->kbar, "out->kbar"));
-  PISA_TRY(check_ptr(out->vsum, "out->vsum"));
-  PISA_TRY(check_ptr(out->ksig2, "out->ksig2"));
-  PISA_TRY(check_ptr(out->hbarT, "out->hbarT"));
-  PISA_TRY(check_ptr(out->packed, "out->packed"));
-  if (flags & PISA_STATS_BLOCK_H) PISA_TRY(check_ptr(out->hblk, "out->hblk"));
-  if (flags & PISA_STATS_BLOCK_C) PISA_TRY(check_ptr(out->cblk, "out->cblk"));
-  if (flags & PISA_STATS_HNORM) PISA_TRY(check_ptr(out->hnorm, "out->hnorm", false));
+  PISA_TRY(stats_checks(dt, K, V, H, L, d, B, flags, out));
   const size_t need = pisa_block_stats_workspace_bytes(H, L, d, B);
   if (!workspace || workspace_bytes < need)
     return fail(PISA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   if (!aligned16(workspace)) return fail(PISA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return stats_launch(dt, K, V, H, L, d, block_len, flags, out, static_cast<float*>(workspace),
+                      pisa::stats_group(H, L / B), stream);
+}
 
-  pisa::StatsArgs a{};
-  a.K = K;
-  a.V = V;
-  a.block_len = block_len;
-  a.kbar = out->kbar;
-  a.vsum = out->vsum;
-  a.ksig2 = out->ksig2;
-  a.hbarT = out->hbarT;
-  a.hblk = out->hblk;
-  a.cblk = out->cblk;
-  a.hnorm = out->hnorm;
-  a.packed = static_cast<char*>(out->packed);
-  a.part = static_cast<float*>(workspace);
-  a.H = H;
-  a.L = L;
-  a.d = d;
-  a.pl = pisa::packed_layout(elem_size(dt), H, L, d);
-  a.nb = a.pl.nb;
-  a.nbp = a.pl.nbp;
-  a.G = pisa::stats_group(H, a.nb);
-  a.ngroups = (a.nb + a.G - 1) / a.G;
-  hipError_t e = pisa::launch_block_stats(dt == PISA_BF16, a, flags, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "pisa_block_stats launch");
-  return ok();
+pisa_status pisa_block_stats_noalloc(pisa_dtype dt, const void* K, const void* V, int H, int L,
+                                     int d, int B, const int32_t* block_len, unsigned flags,
+                                     const pisa_stats* out, void* stream) {
+  PISA_TRY(stats_checks(dt, K, V, H, L, d, B, flags, out));
+  // One d x d fp32 partial of H̄ per (head, group of G blocks). The default grouping is
+  // kept when its partials fit the scratch; otherwise G grows until they do.
+  const size_t per = size_t(d) * d * sizeof(float);
+  const size_t fit = PISA_STATS_SCRATCH_BYTES / (per * size_t(H));    // groups per head that fit
+  if (fit < 1)
+    return fail(PISA_ERR_WORKSPACE, "pisa_block_stats_noalloc: H = %d heads of d = %d need %zu scratch bytes "
+                "(the fixed scratch holds %zu)", H, d, per * size_t(H), size_t(PISA_STATS_SCRATCH_BYTES));
+  const int nb = L / B;
+  int G = pisa::stats_group(H, nb);
+  if (size_t((nb + G - 1) / G) > fit) G = int((size_t(nb) + fit - 1) / fit);
+  float* part = nullptr;
+  PISA_TRY(stats_scratch(&part));
+  return stats_launch(dt, K, V, H, L, d, block_len, flags, out, part, G, stream);
 }
 
 size_t pisa_select_workspace_bytes(int H, int L, int d, int B) {

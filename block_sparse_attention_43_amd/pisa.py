@@ -28,6 +28,7 @@ B = 64
 
 # Every symbol include/pisa.h declares.
 EXPORTS = ("pisa_packed_bytes", "pisa_block_stats_workspace_bytes", "pisa_block_stats",
+           "pisa_block_stats_noalloc",
            "pisa_select_workspace_bytes", "pisa_select_topk", "pisa_select_topk_routed",
            "pisa_select_topk_rope",
            "pisa_attention_fwd", "pisa_attention_bwd_workspace_bytes", "pisa_attention_bwd",
@@ -76,6 +77,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pisa_select_workspace_bytes.restype = sz
     lib.pisa_block_stats.argtypes = [i32, vp, vp, i32, i32, i32, i32, vp, u32, sp, vp, sz, vp]
     lib.pisa_block_stats.restype = i32
+    lib.pisa_block_stats_noalloc.argtypes = [i32, vp, vp, i32, i32, i32, i32, vp, u32, sp, vp]
+    lib.pisa_block_stats_noalloc.restype = i32
     lib.pisa_select_topk.argtypes = [i32, vp, sp, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.pisa_select_topk.restype = i32
     lib.pisa_select_topk_routed.argtypes = [i32, vp, sp, i32, i32, i32, i32, vp, i32, u32, ctypes.c_float,
@@ -196,6 +199,20 @@ def block_stats(K, V, block_len=None, flags: int = 0, out: Stats | None = None, 
     _check(lib.pisa_block_stats(_dtype_code(K), _ptr(K), _ptr(V), H, L, d, B, _ptr(block_len), flags,
                                 ctypes.byref(s), _ptr(workspace), workspace.numel(), _stream(stream)))
     return st
+
+
+STATS_SCRATCH_BYTES = 64 << 20     # PISA_STATS_SCRATCH_BYTES
+
+
+def block_stats_noalloc(K, V, block_len, out: Stats, flags: int = 0, stream=None) -> Stats:
+    """pisa_block_stats_noalloc: the statistics into caller-allocated ``out``, with the
+    H̄ partials in the library's fixed device scratch (no allocation in the call)."""
+    lib = load()
+    H, L, d = _shape(K)
+    s = out.struct()
+    _check(lib.pisa_block_stats_noalloc(_dtype_code(K), _ptr(K), _ptr(V), H, L, d, B, _ptr(block_len), flags,
+                                        ctypes.byref(s), _stream(stream)))
+    return out
 
 
 def select_topk(Q, st: Stats, K_sel: int, block_len=None, want_wt: bool = True, want_mask: bool = True,

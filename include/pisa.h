@@ -155,6 +155,25 @@ pisa_status pisa_block_stats(pisa_dtype dt, const void* K, const void* V, int H,
                              const pisa_stats* out, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* Size of the fixed device scratch of pisa_block_stats_noalloc (64 MiB per GPU). */
+#define PISA_STATS_SCRATCH_BYTES (64u << 20)
+
+/*
+ * pisa_block_stats for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments, results
+ * and errors as pisa_block_stats without the workspace: the fp32 partial sums of H̄ live
+ * in a fixed PISA_STATS_SCRATCH_BYTES array in device memory that every GPU the library
+ * runs on holds until the process ends. The call allocates nothing. When the default
+ * grouping of blocks would need more partials than fit, blocks are grouped more coarsely
+ * (H̄ may then differ from pisa_block_stats in the last bits); more than
+ * PISA_STATS_SCRATCH_BYTES / (4 d²) heads (1024 at d = 128) give PISA_ERR_WORKSPACE.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (other
+ * streams, other threads) race and must be ordered by the caller.
+ */
+pisa_status pisa_block_stats_noalloc(pisa_dtype dt, const void* K, const void* V, int H, int L,
+                                     int d, int B, const int32_t* block_len, unsigned flags,
+                                     const pisa_stats* out, void* stream);
+
 /* Workspace bytes of pisa_select_topk, pisa_select_topk_routed and pisa_select_topk_rope
  * (pooled queries, rotated key centroids and the fp32 score matrix). */
 size_t pisa_select_workspace_bytes(int H, int L, int d, int B);
