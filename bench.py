@@ -56,16 +56,27 @@ def flop_counts(idx: np.ndarray, block_len: np.ndarray, d: int, mode: str) -> di
                 attention=exact + virtual + first, total=exact + virtual + first + prepare)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the sources of the bf16 attention kernels (the measured kernel)."""
+def kernel_source_hash(dtype: str = "bf16") -> str:
+    """Hash of the sources of the measured attention kernel: the register-streamed kernel
+    for bf16 inputs, the LDS-staged one (attention_split_kernel) for fp32."""
     h = hashlib.sha256()
-    for name in ("attention_frag.hip", "common.hpp", "attention.hpp"):
+    main = "attention_frag.hip" if dtype == "bf16" else "attention_fwd.hip"
+    for name in (main, "common.hpp", "attention.hpp"):
         with open(os.path.join(ROOT, "block_sparse_attention_43_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
+def _large_splits(H: int, nb: int) -> int:
+    """Key splits of the selection over rows of more than 2048 blocks (as the library
+    picks them: enough workgroups of 128 rows to fill the GPU, at most 16)."""
+    nrg, tiles, ks = (nb + 127) // 128, (nb + 31) // 32, 1
+    while ks < 16 and nrg * H * ks < 2048 and tiles // (2 * ks) >= 4:
+        ks *= 2
+    return ks
+
+
+def load_traffic(workload: str, dtype: str):
     """HBM bytes per attention launch measured with rocprofv3 counters, if they were taken
     on the current kernel source (profiles/attention_fwd_<workload>_traffic.json)."""
     p = os.path.join(ROOT, "profiles", f"attention_fwd_{workload}_traffic.json")
@@ -73,7 +84,7 @@ def load_traffic(workload: str):
         return None
     with open(p) as f:
         rec = json.load(f)
-    if rec.get("kernel_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_sha256_16") != kernel_source_hash(dtype):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -197,7 +208,7 @@ def main():
             pisa.attention_fwd(Q, K, V, st, idx, mask, wt, K_sel, mode, blt, out=O)
         torch.cuda.synchronize()
         print(json.dumps({"traffic_driver": cfg.name, "mode": mode, "copy_bytes": 512 * 2**20,
-                          "kernel_sha256_16": kernel_source_hash()}))
+                          "kernel_sha256_16": kernel_source_hash(cfg.dtype)}))
         return
 
     # every buffer allocated once, outside the timed region
@@ -266,14 +277,21 @@ def main():
     stats_bytes = (2 * H * L * d * es                        # read K, V
                    + (2 if es == 2 else 1) * H * L * d * es  # write Vᵀ (+ operand-order K for bf16)
                    + 3 * H * nb * d * 4 + 2 * H * nbp * d * es + H * d * d * (4 + es))
+    nw = (nb + 31) // 32
     sel_bytes = (H * L * d * es + 2 * H * nb * d * 4 * 2     # read Q; write q̄, mean(q²), read them back
                  + 2 * H * nb * d * 4                        # read k̄, σ²
-                 + H * nb * nb * 4 * (3 if wt is not None else 2)  # scores (write + read), w̃
-                 + H * nb * (K_sel + (nb + 31) // 32) * 4)   # idx, mask
+                 + H * nb * (K_sel + nw) * 4                 # idx, mask
+                 + (H * nb * nb * 4 if wt is not None else 0))   # w̃
+    if nb <= 2048:
+        sel_bytes += 2 * H * nb * nb * 4                     # score rows written and read back
+    else:
+        # recomputed scores: per row the bin counts of every key split (written, read) and
+        # the mask words written twice and read once
+        sel_bytes += H * nb * (2 * 512 * _large_splits(H, nb) + 2 * nw * 4)
     prepare = {k: {"bytes": int(b), "gbs": round(b / (ms * 1e-3) / 1e9, 1),
                    "frac_of_hbm": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
                for k, b, ms in (("pisa_block_stats", stats_bytes, ms_stats), ("pisa_select_topk", sel_bytes, ms_sel))}
-    traffic = load_traffic(args.config)
+    traffic = load_traffic(args.config, cfg.dtype)
 
     # exact branch alone: DROP on the same selection (phase 1 only)
     def timed(fn, n=5):
@@ -466,8 +484,9 @@ def main():
         **dense,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4), "traffic": traffic,
-                     "kernel": "pisa_attention_fwd: attention_frag_kernel, one launch for query "
-                               "tiles of more than 32 rows and one for the rest",
+                     "kernel": ("pisa_attention_fwd: attention_frag_kernel, one launch for query "
+                                "tiles of more than 32 rows and one for the rest" if cfg.dtype == "bf16" else
+                                "pisa_attention_fwd: attention_split_kernel (fp32 inputs), one launch"),
                      "algorithmic_flops_per_launch": fc["attention"]},
         "cpu_baseline": cpu,
     }
