@@ -425,6 +425,23 @@ def main():
             pisa.attention_fwd(Q, K, V, st, idx_x, mask_x, None, K_sel, "drop", blt, out=O, lse=lse_sel)
             recall[name_r] = round(float(torch.exp(lse_sel - lse_all)[:, valid].mean().item()), 5)
         dense["selection_mass_recall"] = recall
+        if backward is not None:
+            # dense backward baseline: DROP with every block selected (the same kernels as the
+            # sparse backward), forward output given; forward + backward against the step's
+            mask_all = torch.zeros(H, nb, (nb + 31) // 32 * 32, dtype=torch.bool)
+            mask_all[:, :, :nb] = True
+            mask_all = torch.from_numpy(np.packbits(mask_all.numpy(), axis=-1, bitorder="little")
+                                        .view(np.int32).reshape(H, nb, -1).copy()).cuda()
+            dO = torch.randn(Q.shape, dtype=torch.float32, device="cuda",
+                             generator=torch.Generator(device="cuda").manual_seed(7)).to(Q.dtype)
+            gbuf = tuple(torch.empty(H, L, d, dtype=torch.float32, device="cuda") for _ in range(3))
+            ws_bd = torch.empty(max(pisa.load().pisa_attention_bwd_workspace_bytes(
+                1 if cfg.dtype == "bf16" else 0, H, L, d, 64, nb), 16), dtype=torch.uint8, device="cuda")
+            pisa.attention_fwd(Q, K, V, st, idx_all, mask_all, None, nb, "drop", blt, out=O, lse=lse_all)
+            ms_bwd_dense = timed(lambda: pisa.attention_bwd(Q, K, V, st, idx_all, mask_all, None, nb, lse_all, dO,
+                                                            "drop", blt, out=gbuf, workspace=ws_bd, O=O), 1)
+            dense["dense_backward_ms"] = round(ms_bwd_dense, 4)
+            del gbuf, ws_bd, dO, mask_all
         del idx_all, lse_all, lse_sel
         ok = torch.from_numpy(inp.layout.perm >= 0).cuda()
         q = Q[:, ok].unsqueeze(0).contiguous()
@@ -440,6 +457,10 @@ def main():
         dense.update(dense_ours_ms=round(ms_drop_all, 4),
                      dense_sdpa_ms=None if ms_sdpa is None else round(ms_sdpa, 4),
                      dense_best_ms=round(best, 4), speedup_vs_dense=round(best / ms_step, 3))
+        if "dense_backward_ms" in dense:
+            # forward + backward: the dense pair against the sparse step and its backward
+            dense["fwd_bwd_speedup_vs_dense"] = round((best + dense["dense_backward_ms"])
+                                                      / (ms_step + backward["ms"]), 3)
 
     cpu = None
     progress("dense and selection recall done")

@@ -132,14 +132,29 @@ pisa_status select_impl(pisa_dtype dt, const void* Q, const void* Q_pre, const v
     a.rope_base = rope->base;
   }
   a.block_len = block_len;
-  a.qbar = static_cast<float*>(workspace);
-  a.qsq = a.qbar + size_t(H) * nb * d;
-  a.krot = a.qsq + size_t(H) * nb * d;
-  a.scores = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                      pisa::align256(3 * size_t(H) * nb * d * sizeof(float)));
+  const pisa::SelectLayout wl = pisa::select_layout(H, nb, d);
+  char* ws = static_cast<char*>(workspace);
+  a.qbar = reinterpret_cast<float*>(ws + wl.qbar);
+  a.qsq = reinterpret_cast<float*>(ws + wl.qsq);
+  a.krot = reinterpret_cast<float*>(ws + wl.krot);
   a.wt = wt;
   a.idx = idx;
   a.mask = mask;
+  a.stile = reinterpret_cast<float*>(ws + wl.stile);
+  if (nb <= pisa::kSmallNb) {
+    a.scores = reinterpret_cast<float*>(ws + wl.scores);
+  } else {
+    a.ktile = reinterpret_cast<float*>(ws + wl.ktile);
+    a.lhist = reinterpret_cast<uint32_t*>(ws + wl.lhist);
+    a.lstate = reinterpret_cast<int4*>(ws + wl.lstate);
+    a.lcoff = reinterpret_cast<int*>(ws + wl.lcoff);
+    a.lcand = reinterpret_cast<uint2*>(ws + wl.lcand);
+    a.lkpart = reinterpret_cast<float4*>(ws + wl.lkpart);
+    a.lover = reinterpret_cast<int*>(ws + wl.lover);
+    a.lks = wl.lks;
+    a.lnkp = wl.lnkp;
+    if (!a.mask) a.mask = reinterpret_cast<uint32_t*>(ws + wl.lmask);
+  }
   a.H = H;
   a.L = L;
   a.d = d;
@@ -272,8 +287,7 @@ pisa_status pisa_block_stats_noalloc(pisa_dtype dt, const void* K, const void* V
 
 size_t pisa_select_workspace_bytes(int H, int L, int d, int B) {
   if (check_shape(H, L, d, B) != PISA_OK) return 0;
-  const size_t nb = size_t(L / B);
-  return pisa::align256(3 * size_t(H) * nb * d * sizeof(float)) + size_t(H) * nb * nb * sizeof(float);
+  return pisa::select_layout(H, L / B, d).total;
 }
 
 pisa_status pisa_select_topk_routed(pisa_dtype dt, const void* Q, const pisa_stats* st, int H,

@@ -79,12 +79,70 @@ struct SelectArgs {
   const int32_t* block_len;
   float* qbar;     // [H][nb][d]   workspace
   float* qsq;      // [H][nb][d]   workspace
-  float* scores;   // [H][nb][nb]  workspace
+  float* scores;   // [H][nb][nb]  workspace (nb <= kSmallNb only)
   float* wt;       // [H][nb][nb]  or null
   int32_t* idx;    // [H][nb][K_sel]
-  uint32_t* mask;  // [H][nb][nw]  or null
+  uint32_t* mask;  // [H][nb][nw]  or null (the caller's, else workspace for nb > kSmallNb)
   int H, L, d, nb, K_sel, nw;
+  // nb > kSmallNb: histogram-threshold selection without the score matrix (workspace)
+  uint32_t* lhist;  // [H][nb][lks][kLBins / 2] per key split, bin counts as u16 pairs
+  int4* lstate;     // [H][nb] threshold bin b*, blocks still needed from it, its count, overflow
+  int* lcoff;       // [H][nb][lks] first list slot of each key split's candidates
+  uint2* lcand;     // [H][nb][kLCap] candidates: order key, block index (ascending index)
+  float4* lkpart;   // [H][lnkp] max |k̄_j|, min and max key bias, max σ²_{j,c} per 256 blocks
+  int* lover;       // [1 + H nb] rows whose threshold bin overflowed the list: count, rows
+  int lks, lnkp;
+  // fp32 rows in the tiled order of the score products (tile_rows in select_topk.hip):
+  // float4 ((h·tiles + t)·(d/8) + u)·64 + lane = row 32 t + lane % 32, columns
+  // (lane / 32)·d/2 + 4u .. + 3, so each 16-byte load of a wave reads 1 KB in one piece.
+  float* ktile;     // [H][tiles][d/8][64] float4: k̄ (or the turned key centroids)
+  float* stile;     // [H][tiles][d/8][64] float4: σ²
 };
+
+// Selection over many key blocks: rows of at most kSmallNb blocks keep the whole score
+// row in registers; longer rows go through a linear-bin histogram of the recomputed scores.
+constexpr int kSmallNb = 2048;
+constexpr int kLBins = 256;   // linear bins per row
+constexpr int kLCap = 256;    // candidates kept per row (threshold bin)
+constexpr int kLRows = 128;   // query tiles per workgroup of the score passes
+constexpr int kMaxNb = 32768; // longest row the selection handles (128 KB of fp32 in LDS)
+
+struct SelectLayout {
+  size_t qbar, qsq, krot, stile, ktile, scores, lhist, lstate, lcoff, lcand, lkpart, lover, lmask, total;
+  int lks, lnkp;
+};
+
+inline SelectLayout select_layout(int H, int nb, int d) {
+  SelectLayout w{};
+  const size_t Hs = size_t(H), f = sizeof(float), hnd = Hs * nb * d * f;
+  const size_t tiled = Hs * ((size_t(nb) + 31) / 32) * 32 * d * f;
+  size_t o = 0;
+  w.qbar = o; o += hnd;
+  w.qsq = o;  o += hnd;
+  w.krot = o; o = align256(o + hnd);
+  w.stile = o; o = align256(o + tiled);
+  if (nb <= kSmallNb) {
+    w.scores = o; o = align256(o + Hs * nb * nb * f);
+    w.total = o;
+    return w;
+  }
+  const int nrg = (nb + kLRows - 1) / kLRows, tiles = (nb + 31) / 32;
+  int ks = 1;
+  while (ks < 16 && static_cast<long long>(nrg) * H * ks < 2048 && tiles / (2 * ks) >= 4) ks *= 2;
+  w.lks = ks;
+  w.lnkp = (nb + 255) / 256;
+  const size_t nw = size_t(tiles);
+  w.ktile = o;  o = align256(o + tiled);
+  w.lhist = o;  o = align256(o + Hs * nb * ks * (kLBins / 2) * 4);
+  w.lstate = o; o = align256(o + Hs * nb * 16);
+  w.lcoff = o;  o = align256(o + Hs * nb * ks * 4);
+  w.lcand = o;  o = align256(o + Hs * nb * kLCap * 8);
+  w.lkpart = o; o = align256(o + Hs * w.lnkp * 16);
+  w.lover = o;  o = align256(o + (1 + Hs * nb) * 4);
+  w.lmask = o;  o = align256(o + Hs * nb * nw * 4);
+  w.total = o;
+  return w;
+}
 
 struct AttnArgs {
   const void* Q;
@@ -199,6 +257,9 @@ hipError_t launch_layout(bool to_blocks, const void* src, void* dst, const int32
                          int L_pad, int row_bytes, hipStream_t s);
 hipError_t launch_attention_bwd(int bf16, int mode, const BwdArgs& a, hipStream_t s);
 hipError_t launch_select(int bf16, const SelectArgs& a, hipStream_t s);
+hipError_t launch_select_large(const SelectArgs& a, hipStream_t s);
+hipError_t launch_pooled_w(const SelectArgs& a, hipStream_t s);
+hipError_t launch_tile_rows(const float* src, float* dst, int H, int nb, int d, hipStream_t s);
 hipError_t launch_attention(int bf16, int mode, const AttnArgs& a, hipStream_t s);
 
 }  // namespace pisa

@@ -4,9 +4,8 @@
 // q̄_i = mean of the valid rows of query tile i, \overline{q²}_i = mean of their squares
 // (PISA paper Fig. 3 prepare phase; Sparse Linear Attention blog, PWT section: square
 // first, then average). Scores s_{i,j} = q̄_i·k̄_j (MoBA-style block-mean scoring,
-// blog Sparse Attention section) and w̃_{i,j} = ½ Σ_c \overline{q²}_{i,c} σ²_{j,c}, the
-// [query block x key block] matrix that PWT computes once before the attention kernel.
-// S_i keeps the K_sel largest scores, ties to the lower block index, emitted in
+// blog Sparse Attention section); the matrix w̃_{i,j} = ½ Σ_c \overline{q²}_{i,c} σ²_{j,c}
+// that PWT reads in the attention call is written by pooled_w.hip. S_i keeps the K_sel largest scores, ties to the lower block index, emitted in
 // ascending block order plus a bitmask of the selected blocks. Covariance-aware routing
 // (PISA paper §3.3, Eq. (7)) adds ln(M_j + eps) of the block heterogeneity to every score
 // of key block j; the row softmax of Eq. (7) keeps the order, so the top-K is taken on
@@ -14,11 +13,13 @@
 // section: mass times heterogeneity) adds w̃_{i,j} + ln n_j on top.
 //
 // Scores are fp32 (matrix-core fp32 products and sums) with one fixed summation order per
-// element, so identical centroids score identically. Top-K is an exact radix select on
-// order-preserving 32-bit keys held in registers (256 threads, up to 128 keys each), with
-// the tie rule resolved by block-wide prefix counts in index order.
+// element, so identical centroids score identically. Rows of at most kSmallNb blocks are
+// stored and radix-selected here (order-preserving 32-bit keys in registers, the tie rule
+// by prefix counts in index order); longer rows go to select_large.hip, which recomputes
+// the scores instead of storing them.
 #include "common.hpp"
 #include "internal.hpp"
+#include "select_common.hpp"
 
 namespace pisa {
 
@@ -133,9 +134,9 @@ __global__ __launch_bounds__(256) void rope_pool_kernel(SelectArgs a) {
   }
 }
 
-// S = Q̄ K̄ᵀ and W = ½ Q̄² Σ²ᵀ per head on the fp32 matrix cores: a 64x64 output tile per
-// workgroup, each of its four waves a 32x32 quarter (v_mfma_f32_32x32x2f32 over the head
-// dimension). The 64 query and 64 key rows are staged in LDS with coalesced 16-byte loads.
+// S = Q̄ K̄ᵀ per head (plus W = ½ Q̄² Σ²ᵀ for the predicted-error route) on the fp32
+// matrix cores: a 64x64 output tile per workgroup, each of its four waves a 32x32 quarter
+// (v_mfma_f32_32x32x2f32 over the head dimension). The 64 query and 64 key rows are staged in LDS with coalesced 16-byte loads.
 // MFMA step m pairs column m (lane half 0) with column m + D/2 (lane half 1), so each
 // lane reads one contiguous half row per operand. Every output element is accumulated
 // in the same order whatever its position, so identical centroids score identically.
@@ -186,11 +187,10 @@ __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
     }
   };
   f32x16 w = zero16();
-  if (a.wt || a.route == 2) {
+  if (a.route == 2) {                        // predicted-error route: w̃ enters the score
     w = product(a.qsq, a.ksig2);
 #pragma unroll
     for (int r = 0; r < 16; ++r) w[r] *= 0.5f;
-    if (a.wt) store(a.wt, w);
   }
   f32x16 s = product(a.qbar, a.rope_axes ? a.krot : a.kbar);
   if (a.route != 0 && col < nb) {
@@ -204,12 +204,6 @@ __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
     for (int r = 0; r < 16; ++r) s[r] = (a.route == 2 ? s[r] + w[r] : s[r]) + bias;
   }
   store(a.scores, s);
-}
-
-__device__ __forceinline__ uint32_t order_key(float s) {
-  s = s + 0.0f;                                   // -0 -> +0 so equal scores tie
-  const uint32_t u = __float_as_uint(s);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 // One workgroup per (query tile, head). Thread t owns block indices [t*P, t*P + P).
@@ -304,17 +298,6 @@ __global__ __launch_bounds__(256) void topk_kernel(SelectArgs a) {
     uint32_t* mo = a.mask + (size_t(h) * nb + i) * a.nw;
     for (int w = tid; w < a.nw; w += 256) mo[w] = smask[w];
   }
-}
-
-// Inclusive scan over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_inclusive_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  return x;
 }
 
 // One wave per (query tile, head), four rows per workgroup, for nb <= 64 P: lane l owns
@@ -422,6 +405,29 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(SelectArgs a) {
   }
 }
 
+// fp32 [H][nb][D] rows into the tiled order of the score products (SelectArgs::ktile):
+// float4 ((h·tiles + t)·(D/8) + u)·64 + lane is row 32 t + lane % 32, columns
+// (lane / 32)·D/2 + 4u .. + 3, zeros past nb. Writes are coalesced; the source is small.
+template <int D>
+__global__ __launch_bounds__(256) void tile_rows_kernel(const float* src, float* dst, int nb) {
+  constexpr int U = D / 8;
+  const int t = blockIdx.x, h = blockIdx.y, tiles = gridDim.x;
+  float4* out = reinterpret_cast<float4*>(dst) + (size_t(h) * tiles + t) * U * 64;
+  for (int e = threadIdx.x; e < U * 64; e += 256) {
+    const int u = e / 64, lane = e % 64, row = 32 * t + (lane & 31), col = (lane >> 5) * (D / 2) + 4 * u;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row < nb) v = *reinterpret_cast<const float4*>(src + (size_t(h) * nb + row) * D + col);
+    out[e] = v;
+  }
+}
+
+hipError_t launch_tile_rows(const float* src, float* dst, int H, int nb, int d, hipStream_t s) {
+  const dim3 g((nb + 31) / 32, H);
+  if (d == 64) hipLaunchKernelGGL((tile_rows_kernel<64>), g, dim3(256), 0, s, src, dst, nb);
+  else hipLaunchKernelGGL((tile_rows_kernel<128>), g, dim3(256), 0, s, src, dst, nb);
+  return hipGetLastError();
+}
+
 template <class T, int D>
 static hipError_t launch_select_t(const SelectArgs& a, hipStream_t s) {
   hipError_t e = hipSuccess;
@@ -435,7 +441,19 @@ static hipError_t launch_select_t(const SelectArgs& a, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  const bool large = a.nb > kSmallNb;
+  if (a.wt || (large && a.route == 2)) {     // σ² in the tiled order of the products
+    e = launch_tile_rows(a.ksig2, a.stile, a.H, a.nb, D, s);
+    if (e != hipSuccess) return e;
+  }
+  e = launch_pooled_w(a, s);                 // w̃ (when asked for), after the pooled q²
+  if (e != hipSuccess) return e;
   const int nt = (a.nb + 63) / 64;
+  if (large) {                               // no score matrix: recomputed scores
+    e = launch_tile_rows(a.rope_axes ? a.krot : a.kbar, a.ktile, a.H, a.nb, D, s);
+    if (e != hipSuccess) return e;
+    return launch_select_large(a, s);
+  }
   hipLaunchKernelGGL((score_kernel<D>), dim3(nt, nt, a.H), dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

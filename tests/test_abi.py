@@ -53,6 +53,10 @@ def test_workspace_and_packed_sizes(lib):
     assert lib.pisa_packed_bytes(0, H, L, d, 64) > packed          # fp32 is larger
     assert lib.pisa_select_workspace_bytes(H, L, d, 64) >= H * nb * nb * 4
     assert lib.pisa_block_stats_workspace_bytes(H, L, d, 64) >= H * d * d * 4
+    # rows of more than 2048 key blocks keep no score matrix: at nb = 20480 the selection
+    # workspace is the pooled queries plus per-row bins and lists, far below nb² fp32
+    big = lib.pisa_select_workspace_bytes(1, 20480 * 64, d, 64)
+    assert 3 * 20480 * d * 4 < big < 20480 * 20480 * 4 // 4
     for bad in [(0, L, d, 64), (H, L + 1, d, 64), (H, L, 96, 64), (H, L, d, 32)]:
         assert lib.pisa_block_stats_workspace_bytes(*bad) == 0
         assert lib.pisa_select_workspace_bytes(*bad) == 0
