@@ -810,7 +810,14 @@ template <class T, int D>
 static hipError_t launch_attn_t(int mode, const AttnArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.H) * unsigned(a.nb));
   if (mode == MODE_LITERAL) {
-    hipLaunchKernelGGL((attention_kernel<T, D, MODE_LITERAL>), grid, dim3(128), 0, s, a);
+    if (!std::is_same<T, float>::value && a.lse) {
+      // bf16 with lse given: the selected blocks as DROP in the fast kernel (writes O,
+      // lse), then the unselected blocks in their literal form, merged into O and lse.
+      launch_attention_frag(MODE_DROP, a, s);
+      launch_literal_rest(a, s);
+    } else {
+      hipLaunchKernelGGL((attention_kernel<T, D, MODE_LITERAL>), grid, dim3(128), 0, s, a);
+    }
   } else if (mode == MODE_PWT_ROW) {
     if (a.lse) {
       // Two passes: the exact tiles as DROP in the fast kernel (writes O, lse), then the

@@ -259,6 +259,9 @@ hipError_t launch_attention_bwd(int bf16, int mode, const BwdArgs& a, hipStream_
 hipError_t launch_select(int bf16, const SelectArgs& a, hipStream_t s);
 hipError_t launch_select_large(const SelectArgs& a, hipStream_t s);
 hipError_t launch_pooled_w(const SelectArgs& a, hipStream_t s);
+// bf16 LITERAL, second pass: the unselected blocks in block-wise form, merged into the
+// O / lse of a DROP pass over the selected blocks (attention_literal.hip).
+hipError_t launch_literal_rest(const AttnArgs& a, hipStream_t s);
 hipError_t launch_tile_rows(const float* src, float* dst, int H, int nb, int d, hipStream_t s);
 hipError_t launch_attention(int bf16, int mode, const AttnArgs& a, hipStream_t s);
 
