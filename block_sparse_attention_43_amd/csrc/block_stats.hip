@@ -232,15 +232,26 @@ void block_stats_kernel(StatsArgs a, unsigned flags) {
 // Fixed-order reduction of the per-workgroup partials into H̄ᵀ (fp32) and H̄[e][c]
 // (storage type); also zeroes the padding rows of the packed centroid / mean-value
 // tiles beyond nb so the attention kernel reads finite zeros there.
+//
+// Workgroup = 16 elements of H̄; thread (sub, xi) sums the group partials q ≡ sub (mod 16)
+// of element xi in increasing q, and the 16 partial sums are added in sub order: a fixed
+// order, so reruns are bit-identical, with 16 times the parallelism and 1/16 the chain
+// length of one sum per element (the long sequences have a thousand partials per head).
 template <class T, int D>
 __global__ __launch_bounds__(256) void hbar_reduce_kernel(StatsArgs a) {
-  const int h = blockIdx.y;
-  const int x = blockIdx.x * 256 + threadIdx.x;
-  if (x >= D * D) return;
-  const int c = x / D, e = x % D;
-  const float* part = a.part + size_t(h) * a.ngroups * D * D;
+  __shared__ float red[16][17];
+  const int h = blockIdx.y, tid = threadIdx.x, xi = tid & 15, sub = tid >> 4;
+  const int x = blockIdx.x * 16 + xi;
+  const float* part = a.part + size_t(h) * a.ngroups * D * D + x;
+  float ps = 0.f;
+  for (int q = sub; q < a.ngroups; q += 16) ps += part[size_t(q) * D * D];
+  red[sub][xi] = ps;
+  __syncthreads();
+  if (sub != 0) return;
   float s = 0.f;
-  for (int q = 0; q < a.ngroups; ++q) s += part[size_t(q) * D * D + x];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) s += red[k][xi];
+  const int c = x / D, e = x % D;
   const float hb = s / float(a.nb);
   a.hbarT[size_t(h) * D * D + x] = hb;
   T* hbp = reinterpret_cast<T*>(a.packed + a.pl.hbar) + size_t(h) * D * D;
@@ -378,7 +389,7 @@ __global__ __launch_bounds__(256) void tile_order_kernel(StatsArgs a) {
 
 template <class T, int D>
 static hipError_t launch_stats_t(const StatsArgs& a, unsigned flags, hipStream_t s) {
-  dim3 g1(a.ngroups, a.H), g2((D * D + 255) / 256, a.H);
+  dim3 g1(a.ngroups, a.H), g2(D * D / 16, a.H);
   if (flags & 3u) hipLaunchKernelGGL((block_stats_kernel<T, D, true>), g1, dim3(256), 0, s, a, flags);
   else hipLaunchKernelGGL((block_stats_kernel<T, D, false>), g1, dim3(256), 0, s, a, flags);
   hipError_t e = hipGetLastError();
