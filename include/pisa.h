@@ -269,9 +269,11 @@ pisa_status pisa_select_topk_rope(pisa_dtype dt, const void* Q, const void* Q_pr
  * (required for PWT). Outputs: O [H][L][d] dtype `dt`; lse [H][L] float or NULL
  * (natural-log log-sum-exp of every row's logits, -inf for padded rows and rows with no
  * support). Out-of-range entries of idx are treated as empty blocks.
- * PWT_ROW with lse given runs in two passes that use lse as the hand-over: the selected
- * blocks as DROP (O and lse written), then the virtual tokens, merged into O and lse; with
- * lse NULL it runs in a single (slower) pass. Both give the same result up to rounding.
+ * PWT_ROW, and LITERAL for PISA_BF16, with lse given run in two passes that use lse as
+ * the hand-over: the selected blocks as DROP (O and lse written), then the virtual tokens
+ * (PWT_ROW) or the unselected blocks in their literal form (LITERAL), merged into O and
+ * lse; with lse NULL (or fp32 LITERAL) they run in a single (slower) pass. Both give the
+ * same result up to rounding.
  */
 pisa_status pisa_attention_fwd(pisa_dtype dt, const void* Q, const void* K, const void* V,
                                const pisa_stats* st, const int32_t* idx, const uint32_t* mask,
