@@ -445,7 +445,7 @@ def attention_head_backward(Q, K, V, dO, B: int, block_len=None, K_sel: int = 0,
     upstream gradient dO (the loss sum(dO * O)), with the top-K selection and the gate's
     decisions held fixed (blog, PWT section: sparse fine-tuning backpropagates through the
     block statistics k̄_j, H̄ and σ²_j while routing stays detached). Modes DROP, PISA and
-    PWT (tile-pooled w̃, global first order).
+    PWT (tile-pooled w̃, global first order), PWT_ROW and LITERAL (below).
 
     With P_{t,k} = e^{x_{t,k} - lse_t} for the exact keys, P_{t,j} = e^{ℓ_{t,j} - lse_t} for
     the virtual tokens (ℓ = q·k̄_j + φ_{i,j} + ln n_j), Δ_t = dO_t·O_t, v̄_j = ΣV_j / n_j,
@@ -462,6 +462,20 @@ def attention_head_backward(Q, K, V, dO, B: int, block_len=None, K_sel: int = 0,
         dk_i += dk̄_j / n_j + (2/n_j)(k_i - k̄_j)∘dσ²_j + (1/nb) dH̄ᵀ (v_i - v̄_j)
         dv_i += dv̄_j / n_j + (1/nb) dH̄ (k_i - k̄_j)
         dq_t += (2/m_i) q_t ∘ d\\overline{q²}_i                (m_i valid rows of tile i)
+
+    PWT with the per-row diagonal w_{t,j} = ½ Σ_c q_{t,c}² σ²_{j,c} (PWT_ROW) differs only in
+    w: dw_{t,j} = φ'(w_{t,j}) dℓ_{t,j} per row, so dq_t += q_t ∘ Σ_j dw_{t,j} σ²_j and
+    dσ²_j = ½ Σ_t dw_{t,j} q_t² replace the pooled terms.
+
+    LITERAL (block-wise first order and per-row w_{t,j} = ½ q_tᵀ C_j q_t, PISA paper Eq.
+    (3.2) with the blog's PWT weight): the unselected block j adds â_{t,j}(ΣV_j + H_j q_t) to
+    o_t and n_j â_{t,j} to the denominator, â = e^{q·k̄_j + φ_{t,j} - lse_t}. Then
+        dℓ_{t,j} = â (dO_t·ΣV_j + dO_t·H_j q_t) - n_j â Δ_t      (log-weight s + φ)
+        dq_t += dℓ k̄_j + φ' dℓ C_j q_t + â H_jᵀ dO_t
+        dk̄_j = Σ_t dℓ q_t,  dΣV_j = Σ_t â dO_t,  dH_j = Σ_t â dO_t q_tᵀ,
+        dC_j = ½ Σ_t φ' dℓ q_t q_tᵀ
+    and block j's tokens receive, besides dk̄_j / n_j and dΣV_j,
+        dk_i += dH_jᵀ (v_i - v̄_j) + (1/n_j)(dC_j + dC_jᵀ)(k_i - k̄_j),  dv_i += dH_j (k_i - k̄_j).
     Returns dict(dQ, dK, dV) [L_pad, d] (zeros on padded slots), O, lse, idx."""
     opts = dict(PRESETS[mode])
     opts.update(overrides)
@@ -470,9 +484,12 @@ def attention_head_backward(Q, K, V, dO, B: int, block_len=None, K_sel: int = 0,
     w_kind = opts.get("w_kind", "none")
     w_map = opts.get("w_map", "exp")
     guard = opts.get("guard", "gate")
-    if first not in ("none", "global") or w_kind not in ("none", "pooled") or \
+    literal = first == "block" and w_kind == "row"
+    if not (literal or (first in ("none", "global") and w_kind in ("none", "pooled", "rowdiag"))) or \
             opts.get("pooling", "sqmean") != "sqmean" or not opts.get("numerator_w", True):
-        raise ValueError("backward covers DROP, PISA and PWT only")
+        raise ValueError("backward covers DROP, PISA, PWT, PWT_ROW and LITERAL")
+    if guard not in ("gate", "none"):
+        raise ValueError("backward takes the gate or no guard")
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
@@ -480,7 +497,7 @@ def attention_head_backward(Q, K, V, dO, B: int, block_len=None, K_sel: int = 0,
     L_pad, d = Q.shape
     rng = block_ranges(L_pad, B, block_len)
     nb = len(rng)
-    st = block_stats(K, V, B, block_len, per_block=False)
+    st = block_stats(K, V, B, block_len, per_block=literal)
     fwd = attention_head(Q, K, V, B, block_len, K_sel, mode, idx=idx, stats=st, **overrides)
     O, lse, idx = fwd["O"], fwd["lse"], fwd["idx"]
     pq = pool_queries(Q, B, block_len)
@@ -496,6 +513,8 @@ def attention_head_backward(Q, K, V, dO, B: int, block_len=None, K_sel: int = 0,
     dsig2 = np.zeros((nb, d))
     dqsq = np.zeros((nb, d))
     dH = np.zeros((d, d))
+    dHb = np.zeros((nb, d, d)) if literal else None            # dH_j[e, c]
+    dCb = np.zeros((nb, d, d)) if literal else None
     for i in range(nb):
         s0, m = rng[i]
         l_t = lse[s0:s0 + m]
@@ -522,23 +541,44 @@ def attention_head_backward(Q, K, V, dO, B: int, block_len=None, K_sel: int = 0,
         if U.size:
             s = q @ st["kbar"][U].T
             lnn = np.log(n[U])[None, :]
-            if w_kind == "pooled":
+            if w_kind == "none":
+                w = np.zeros_like(s)
+            elif w_kind == "pooled":
                 w = np.broadcast_to(0.5 * (st["sig2"][U] @ pq["qsq"][i]), s.shape)
+            elif w_kind == "rowdiag":
+                w = 0.5 * (q ** 2) @ st["sig2"][U].T
+            else:                                              # row: ½ q_tᵀ C_j q_t
+                w = 0.5 * np.einsum("tc,jce,te->tj", q, st["C"][U], q)
+            if w_kind == "none":
+                phi = dphi = np.zeros_like(s)
+            else:
                 fired = (w > lnn) if guard == "gate" else np.zeros(s.shape, dtype=bool)
-                if guard not in ("gate", "none"):
-                    raise ValueError("backward takes the gate or no guard")
                 w0 = np.where(fired, 0.0, w)
                 phi = w0 if w_map == "exp" else np.log1p(w0)
                 dphi = np.where(fired, 0.0, 1.0 if w_map == "exp" else 1.0 / (1.0 + w0))
-            else:
-                phi = dphi = np.zeros_like(s)
             Pv = np.exp(s + phi + lnn - lt)
-            u = q @ hbar.T                                     # u_t = H̄ q_t
-            gu = (g * u).sum(axis=1) if first == "global" else np.zeros(m)
-            dl = Pv * (g @ vbar[U].T + gu[:, None] / n[U][None, :] - delta[:, None])
+            if literal:                                        # H_j q_t per block, [m, |U|, d]
+                hq = np.einsum("jec,tc->tje", st["H"][U], q)
+                gh = np.einsum("te,tje->tj", g, hq)
+                dl = Pv * (g @ vbar[U].T + gh / n[U][None, :] - delta[:, None])
+            else:
+                u = q @ hbar.T                                 # u_t = H̄ q_t
+                gu = (g * u).sum(axis=1) if first == "global" else np.zeros(m)
+                dl = Pv * (g @ vbar[U].T + gu[:, None] / n[U][None, :] - delta[:, None])
             dq += dl @ st["kbar"][U]
             dkbar[U] += dl.T @ q
             dvbar[U] += Pv.T @ g
+            if literal:
+                ahat = Pv / n[U][None, :]                      # e^{s + φ - lse}
+                dw = dphi * dl
+                dq += np.einsum("tj,jce,te->tc", dw, st["C"][U], q)
+                dq += np.einsum("tj,jec,te->tc", ahat, st["H"][U], g)
+                dHb[U] += np.einsum("tj,te,tc->jec", ahat, g, q)
+                dCb[U] += 0.5 * np.einsum("tj,tc,te->jce", dw, q, q)
+            if w_kind == "rowdiag":
+                dw = dphi * dl
+                dq += q * (dw @ st["sig2"][U])
+                dsig2[U] += 0.5 * dw.T @ (q ** 2)
             if first == "global":
                 abar = (Pv / n[U][None, :]).sum(axis=1)
                 dq += abar[:, None] * (g @ hbar)
@@ -556,6 +596,9 @@ def attention_head_backward(Q, K, V, dO, B: int, block_len=None, K_sel: int = 0,
         vd = V[s0:s0 + nj] - vbar[j]
         dK[s0:s0 + nj] += dkbar[j] / nj + (2.0 / nj) * kd * dsig2[j] + vd @ dH / nb
         dV[s0:s0 + nj] += dvbar[j] / nj + kd @ dH.T / nb
+        if literal:
+            dK[s0:s0 + nj] += vd @ dHb[j] + kd @ (dCb[j] + dCb[j].T) / nj
+            dV[s0:s0 + nj] += kd @ dHb[j].T
     return dict(dQ=dQ, dK=dK, dV=dV, O=O, lse=lse, idx=idx)
 
 

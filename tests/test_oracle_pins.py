@@ -743,11 +743,14 @@ def _fd_grads(Q, K, V, dO, B, bl, K_sel, mode, idx, eps=1e-6, **kw):
 
 
 @pytest.mark.parametrize("mode,kw", [("drop", {}), ("pisa", {}), ("pwt", {}), ("pwt", dict(w_map="linear")),
-                                     ("pwt", dict(guard="none"))])
+                                     ("pwt", dict(guard="none")), ("pwt_row", {}), ("pwt_row", dict(w_map="linear")),
+                                     ("pwt_row", dict(guard="none")), ("literal", {}), ("literal", dict(w_map="exp")),
+                                     ("literal", dict(guard="none"))])
 def test_backward_matches_finite_differences(mode, kw):
     """The analytic gradients (selection and gate decisions held fixed) against central
-    differences of the forward definition itself, ragged blocks included; for PWT one
-    block's keys are spread so widely that its w̃ exceeds ln n_j (the gate fires there)."""
+    differences of the forward definition itself, ragged blocks included; one block's keys
+    are spread so widely that its w exceeds ln n_j for some rows or tiles (the gate fires
+    there) while other pairs stay below it."""
     r = np.random.default_rng(29)
     B, nb, d = 4, 5, 3
     bl = np.array([4, 2, 4, 3, 1])
@@ -757,9 +760,14 @@ def test_backward_matches_finite_differences(mode, kw):
     V = r.standard_normal((B * nb, d))
     dO = r.standard_normal((B * nb, d))
     g = orc.attention_head_backward(Q, K, V, dO, B, bl, 2, mode, **kw)
-    if mode == "pwt" and kw.get("guard", "gate") == "gate":
-        st = orc.block_stats(K, V, B, bl, per_block=False)
-        w = orc.pooled_w(orc.pool_queries(Q, B, bl)["qsq"], st["sig2"])
+    if mode != "drop" and mode != "pisa" and kw.get("guard", "gate") == "gate":
+        st = orc.block_stats(K, V, B, bl, per_block=True)
+        if mode == "pwt":
+            w = orc.pooled_w(orc.pool_queries(Q, B, bl)["qsq"], st["sig2"])
+        elif mode == "pwt_row":
+            w = 0.5 * (Q ** 2) @ st["sig2"].T
+        else:
+            w = 0.5 * np.einsum("tc,jce,te->tj", Q, st["C"], Q)
         assert (w > np.log(st["n"])[None, :]).any() and (w < np.log(st["n"])[None, :]).any()
     fd = _fd_grads(Q, K, V, dO, B, bl, 2, mode, g["idx"], **kw)
     for name, a, b in zip(("dQ", "dK", "dV"), (g["dQ"], g["dK"], g["dV"]), fd):
@@ -778,7 +786,7 @@ def test_backward_with_every_block_selected_is_dense_attention_gradient():
     q, k, v = (torch.tensor(x[ok], requires_grad=True) for x in (Q, K, V))
     o = torch.softmax(q @ k.T, dim=-1) @ v
     o.backward(torch.tensor(dO[ok]))
-    for mode in ("drop", "pisa", "pwt"):
+    for mode in ("drop", "pisa", "pwt", "pwt_row", "literal"):
         g = orc.attention_head_backward(Q, K, V, dO, B, bl, nb, mode)
         for a, t in ((g["dQ"], q), (g["dK"], k), (g["dV"], v)):
             assert np.allclose(a[ok], t.grad.numpy(), rtol=1e-10, atol=1e-12)
