@@ -256,6 +256,10 @@ hipError_t launch_block_stats(int bf16, const StatsArgs& a, unsigned flags, hipS
 hipError_t launch_layout(bool to_blocks, const void* src, void* dst, const int32_t* perm, int H, int L_nat,
                          int L_pad, int row_bytes, hipStream_t s);
 hipError_t launch_attention_bwd(int bf16, int mode, const BwdArgs& a, hipStream_t s);
+// bf16 LITERAL backward: Δ, dQ and dK / dV sweeps over every (query tile, key block) pair
+// (attention_bwd_literal.hip); reads Q, K, V, dO, lse, mask, block_len; writes delta, dQ,
+// dK, dV.
+hipError_t launch_literal_bwd(const BwdArgs& a, hipStream_t s);
 hipError_t launch_select(int bf16, const SelectArgs& a, hipStream_t s);
 hipError_t launch_select_large(const SelectArgs& a, hipStream_t s);
 hipError_t launch_pooled_w(const SelectArgs& a, hipStream_t s);

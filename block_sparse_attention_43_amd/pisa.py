@@ -297,8 +297,9 @@ def attention_fwd(Q, K, V, st: Stats, idx, mask, wt, K_sel: int, mode="pwt", blo
 def attention_bwd(Q, K, V, st: Stats, idx, mask, wt, K_sel: int, lse, dO, mode="pwt", block_len=None,
                   out=None, workspace=None, stream=None, O=None):
     """Gradients (dQ, dK, dV) float32 [H, L, d] of sum(dO * O) for the forward call that
-    produced lse with the same arguments (DROP, PISA or PWT). Passing that call's output O
-    lets Δ = dO·O be read instead of formed in the dQ sweep (half its products)."""
+    produced lse with the same arguments (DROP, PISA, PWT, or LITERAL for bf16 inputs).
+    Passing that call's output O lets Δ = dO·O be read instead of formed in the dQ sweep
+    (half its products); LITERAL always forms Δ itself."""
     lib = load()
     H, L, d = _shape(Q)
     m = MODES[mode] if isinstance(mode, str) else int(mode)

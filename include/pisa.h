@@ -285,10 +285,11 @@ pisa_status pisa_attention_fwd(pisa_dtype dt, const void* Q, const void* K, cons
 size_t pisa_attention_bwd_workspace_bytes(pisa_dtype dt, int H, int L, int d, int B, int K_sel);
 
 /*
- * Backward of pisa_attention_fwd for PISA_MODE_DROP, PISA_MODE_PISA and PISA_MODE_PWT (with
- * the same modifier bits), for sparse fine-tuning (blog, PWT section: gradients flow
- * through the block statistics k̄_j, H̄ and σ²_j; routing is detached). The selection and
- * the gate's decisions are held fixed; the loss is sum(dO * O).
+ * Backward of pisa_attention_fwd for PISA_MODE_DROP, PISA_MODE_PISA, PISA_MODE_PWT and (bf16)
+ * PISA_MODE_LITERAL (with the same modifier bits), for sparse fine-tuning (blog, PWT
+ * section: gradients flow through the block statistics k̄_j, H̄ and σ²_j; routing is
+ * detached). The selection and the gate's decisions are held fixed; the loss is
+ * sum(dO * O).
  *   Inputs   Q, K, V, st, idx, mask, wt, block_len, K_sel, mode: as given to the forward
  *            call (mask is required for every mode and must match idx; st needs kbar, vsum,
  *            ksig2 and hbarT); lse: that call's output; dO [H][L][d] dtype `dt`.
@@ -307,8 +308,17 @@ size_t pisa_attention_bwd_workspace_bytes(pisa_dtype dt, int H, int L, int d, in
  *   dk, dv of exact keys from the same terms; dk̄_j, dv̄_j, dH̄ = Σ_t Ā_t dO_t q_tᵀ and
  *   dσ²_j = ½ Σ_i dw̃_{i,j} \overline{q²}_i reach the tokens of block j through
  *   k̄_j, v̄_j = ΣV_j / n_j, H̄ = (1/nb) Σ_j Σ_i v_i (k_i - k̄_j)ᵀ and σ²_j.
- * Sums are taken in a fixed order (repeated calls are bit-identical). LITERAL and PWT_ROW
- * give PISA_ERR_UNSUPPORTED.
+ * PISA_MODE_LITERAL (bf16 inputs; the PISA paper's Eq. (3.2) block-wise first order with the
+ * blog's per-row w = ½ qᵀC_j q, PWT section): every unselected block j enters as
+ * E (1 + y_n) v_n over its valid keys n, with x_n = q·k_n, s̄ = mean x, y_n = x_n - s̄,
+ * w = ½ mean y², φ(w) as in the forward, E = e^{s̄ + φ - lse}; then
+ *   dx_n = E dO·v_n + dw y_n / n_j - mean_m(...) + dℓ / n_j,  dℓ = E (Σ_n (1 + y_n) dO·v_n - n_j Δ),
+ *   dw = φ'(w) dℓ, and dq = Σ dx k, dk = Σ dx q, dv = Σ (P or E (1 + y)) dO over every
+ *   (query tile, key block) pair. Δ is formed in fp32 by a first sweep over all pairs (O is
+ *   not read), so this backward costs about three dense score sweeps. fp32 inputs give
+ *   PISA_ERR_UNSUPPORTED for LITERAL.
+ * Sums are taken in a fixed order (repeated calls are bit-identical). PWT_ROW gives
+ * PISA_ERR_UNSUPPORTED.
  */
 pisa_status pisa_attention_bwd(pisa_dtype dt, const void* Q, const void* K, const void* V,
                                const pisa_stats* st, const int32_t* idx, const uint32_t* mask,

@@ -186,8 +186,8 @@ def test_rope_select_argument_errors(lib, rope, msg):
 
 
 @pytest.mark.parametrize("case,status,msg", [
-    (dict(mode=3), 2, "DROP, PISA and PWT"),
-    (dict(mode=4), 2, "DROP, PISA and PWT"),
+    (dict(mode=3, dt=0), 2, "LITERAL backward takes bf16"),
+    (dict(mode=4), 2, "DROP, PISA, PWT and LITERAL"),
     (dict(mode=9), 1, "unknown mode"),
     (dict(mask=None), 1, "mask must not be NULL"),
     (dict(wt=None), 1, "wt must not be NULL"),
@@ -197,9 +197,9 @@ def test_rope_select_argument_errors(lib, rope, msg):
 def test_backward_argument_errors(lib, case, status, msg):
     from block_sparse_attention_43_amd import pisa
     st = _stats(pisa)
-    a = dict(mode=2, mask=16, wt=16, lse=16, ws=1 << 30)
+    a = dict(mode=2, mask=16, wt=16, lse=16, ws=1 << 30, dt=1)
     a.update(case)
-    r = lib.pisa_attention_bwd(1, 16, 16, 16, ctypes.byref(st), 16, a["mask"], a["wt"], 1, 1024, 64, 64, None, 4,
+    r = lib.pisa_attention_bwd(a["dt"], 16, 16, 16, ctypes.byref(st), 16, a["mask"], a["wt"], 1, 1024, 64, 64, None, 4,
                                a["mode"], a["lse"], None, 16, 16, 16, 16, 16, a["ws"], None)
     assert r == status and msg in lib.pisa_last_error().decode()
     assert lib.pisa_attention_bwd_workspace_bytes(1, 1, 1024, 64, 64, 4) > 0
