@@ -491,6 +491,19 @@ def main():
             dense["fwd_bwd_speedup_vs_dense"] = round((best + dense["dense_backward_ms"])
                                                       / (ms_step + backward["ms"]), 3)
 
+    # yardstick for the matrix-core fraction: the vendor library's bf16 GEMM on this card
+    calibration = None
+    if cfg.dtype == "bf16" and not args.no_dense:
+        ga = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+        gb = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+        gc = torch.empty_like(ga)
+        ms_gemm = timed(lambda: torch.matmul(ga, gb, out=gc), n=20)
+        g_tflops = 2 * 8192 ** 3 / (ms_gemm * 1e-3) / 1e12
+        calibration = {"gemm": "torch.matmul bf16 8192x8192x8192 (vendor library)", "ms": round(ms_gemm, 4),
+                       "tflops": round(g_tflops, 2), "frac": round(g_tflops / peak, 4),
+                       "exact_branch_vs_gemm": round(exact_tflops / g_tflops, 4)}
+        del ga, gb, gc
+
     cpu = None
     progress("dense and selection recall done")
     if not args.no_cpu_baseline:
@@ -533,6 +546,7 @@ def main():
         "rope_selection": rope_leg,
         "flops": fc,
         **dense,
+        "gemm_calibration": calibration,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4), "traffic": traffic,
                      "kernel": ("pisa_attention_fwd: attention_frag_kernel, one launch for query "
