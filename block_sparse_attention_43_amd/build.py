@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpisa.so")
-SOURCES = ["abi.hip", "block_stats.hip", "select_topk.hip", "select_large.hip", "pooled_w.hip", "attention_fwd.hip", "attention_frag.hip",
+SOURCES = ["abi.hip", "block_stats.hip", "select_topk.hip", "select_large.hip", "pooled_w.hip", "attention_fwd.hip", "attention_frag.hip", "attention_row.hip",
            "attention_literal.hip", "attention_bwd.hip", "attention_bwd_literal.hip", "layout.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU forms are disabled for all device code (hipcc emits them from plain
@@ -46,6 +46,7 @@ def _run(cmd):
 # Per-source extra flags. The register-streamed attention kernel keeps its MFMA results
 # in VGPRs (the VALU reads every score tile); operands still come from AGPRs.
 EXTRA = {"attention_frag.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
+         "attention_row.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
          "attention_literal.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"]}
 
 

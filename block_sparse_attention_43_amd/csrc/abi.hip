@@ -403,9 +403,8 @@ pisa_status pisa_attention_bwd(pisa_dtype dt, const void* Q, const void* K, cons
   if (K_sel > 0) PISA_TRY(check_ptr(idx, "idx", false));
   const unsigned base = mode & 15u;
   if (base > PISA_MODE_PWT_ROW) return fail(PISA_ERR_INVALID_ARG, "unknown mode %u", base);
-  if (base == PISA_MODE_PWT_ROW) return fail(PISA_ERR_UNSUPPORTED, "the backward covers DROP, PISA, PWT and LITERAL");
-  if (base == PISA_MODE_LITERAL && dt != PISA_BF16)
-    return fail(PISA_ERR_UNSUPPORTED, "the LITERAL backward takes bf16 inputs");
+  if ((base == PISA_MODE_LITERAL || base == PISA_MODE_PWT_ROW) && dt != PISA_BF16)
+    return fail(PISA_ERR_UNSUPPORTED, "the LITERAL and PWT_ROW backward takes bf16 inputs");
   if (mode & ~(15u | PISA_W_LINEAR | PISA_W_EXP | PISA_W_NOGATE))
     return fail(PISA_ERR_INVALID_ARG, "unknown mode bits 0x%x", mode);
   if ((mode & PISA_W_LINEAR) && (mode & PISA_W_EXP))
@@ -439,6 +438,8 @@ pisa_status pisa_attention_bwd(pisa_dtype dt, const void* Q, const void* K, cons
   a.gu = reinterpret_cast<float*>(ws + w.gu);
   a.abar = reinterpret_cast<float*>(ws + w.abar);
   a.qsq = base == PISA_MODE_PWT ? reinterpret_cast<float*>(ws + w.qsq) : nullptr;
+  // LITERAL / PWT_ROW take the pooled-q² region (H nb d >= H L floats) for the renormalised lse
+  a.lse2 = base == PISA_MODE_LITERAL || base == PISA_MODE_PWT_ROW ? reinterpret_cast<float*>(ws + w.qsq) : nullptr;
   a.dwt = reinterpret_cast<float*>(ws + w.dwt);
   a.dsig2 = reinterpret_cast<float*>(ws + w.dsig2);
   a.dqsq = reinterpret_cast<float*>(ws + w.dqsq);
@@ -468,9 +469,10 @@ pisa_status pisa_attention_bwd(pisa_dtype dt, const void* Q, const void* K, cons
   a.nhch = w.nhch;
   a.w_linear = base == PISA_MODE_LITERAL ? !(mode & PISA_W_EXP) : !!(mode & PISA_W_LINEAR);
   a.gate = !(mode & PISA_W_NOGATE);
-  hipError_t e = base == PISA_MODE_LITERAL
-                     ? pisa::launch_literal_bwd(a, static_cast<hipStream_t>(stream))
-                     : pisa::launch_attention_bwd(dt == PISA_BF16, int(base), a, static_cast<hipStream_t>(stream));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = base == PISA_MODE_LITERAL   ? pisa::launch_literal_bwd(a, hs)
+                 : base == PISA_MODE_PWT_ROW ? pisa::launch_rowdiag_bwd(a, hs)
+                                             : pisa::launch_attention_bwd(dt == PISA_BF16, int(base), a, hs);
   if (e != hipSuccess) return hip_fail(e, "pisa_attention_bwd launch");
   return ok();
 }

@@ -1813,6 +1813,35 @@ static hipError_t launch_bwd_d(int mode, const BwdArgs& a, hipStream_t s) {
   }
 }
 
+// Pieces shared with the PWT_ROW backward (attention_bwd_literal.hip): dO·(H̄ q) per row,
+// and after its sweeps dH̄ from Ā and the statistics' gradients onto the tokens (with dσ²).
+hipError_t launch_bwd_rows(const BwdArgs& a, hipStream_t s) {
+  const dim3 grid(unsigned((a.nb + ROWS_G - 1) / ROWS_G), unsigned(a.H));
+  if (a.d == 64) hipLaunchKernelGGL((bwd_rows_kernel<uint16_t, 64>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((bwd_rows_kernel<uint16_t, 128>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd_stats_tail_d(const BwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_pack_kernel<uint16_t, D>), dim3(a.nb, a.H, 1), dim3(256), 0, s, a);   // Qᵀ, dOᵀ for dH̄
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dh_kernel<uint16_t, D>), dim3(a.nhch, a.H), dim3(256), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dh_reduce_kernel<D>), dim3((D * D + 255) / 256, a.H), dim3(256), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_chain_kernel<uint16_t, D, MODE_PWT>), dim3((a.nb + CHAIN_G - 1) / CHAIN_G, a.H), dim3(256),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_stats_tail(const BwdArgs& a, hipStream_t s) {
+  return a.d == 64 ? launch_bwd_stats_tail_d<64>(a, s) : launch_bwd_stats_tail_d<128>(a, s);
+}
+
 hipError_t launch_attention_bwd(int bf16, int mode, const BwdArgs& a, hipStream_t s) {
   if (bf16) return a.d == 64 ? launch_bwd_d<uint16_t, 64>(mode, a, s) : launch_bwd_d<uint16_t, 128>(mode, a, s);
   return a.d == 64 ? launch_bwd_d<float, 64>(mode, a, s) : launch_bwd_d<float, 128>(mode, a, s);

@@ -86,8 +86,9 @@ __device__ __forceinline__ void quarter_product(const uint16_t* X, const uint16_
 }
 
 // Per-row pass of one (query row, 16-key part): the gradient of the scores (dx) and the dV
-// weights of keys [16 p, 16 p + 16), or (DELTA) only this part's share of Δ. Sums over
-// the block's 64 keys combine the four parts of the row (lanes 4 q .. 4 q + 3).
+// weights of keys [16 p, 16 p + 16), or (DELTA) only this part's share of Σ P dO·v (returned)
+// and of the softmax mass Σ P (added to mass). Sums over the block's 64 keys combine the
+// four parts of the row (lanes 4 q .. 4 q + 3).
 struct RowIn {
   float lse, delta;
   int nj;                                // valid keys of the block
@@ -102,15 +103,18 @@ __device__ __forceinline__ float sum4(float v) {
 }
 
 template <bool DELTA>
-__device__ __forceinline__ float row_pass(const float* x, const float* av, const RowIn& in, int p, float* dx, float* wv) {
+__device__ __forceinline__ float row_pass(const float* x, const float* av, const RowIn& in, int p, float* dx, float* wv,
+                                          float& mass) {
   float part = 0.f;
   if (in.sel) {
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const bool ok = in.live && 16 * p + u < in.nj;
       const float P = ok ? __expf(x[u] - in.lse) : 0.f;
-      if constexpr (DELTA) part = fmaf(P, av[u], part);
-      else {
+      if constexpr (DELTA) {
+        part = fmaf(P, av[u], part);
+        mass += P;
+      } else {
         dx[u] = P * (av[u] - in.delta);
         wv[u] = P;
       }
@@ -136,7 +140,10 @@ __device__ __forceinline__ float row_pass(const float* x, const float* av, const
   const float phi = in.linear ? log1pf(w) : w;
   const float dphi = fired ? 0.f : (in.linear ? 1.f / (1.f + w) : 1.f);
   const float E = in.live ? __expf(sbar + phi - in.lse) : 0.f;
-  if constexpr (DELTA) return (p == 0) ? E * t : 0.f;
+  if constexpr (DELTA) {
+    if (p == 0) mass += float(in.nj) * E;
+    return (p == 0) ? E * t : 0.f;
+  }
   const float dl = E * (t - float(in.nj) * in.delta), dw = dl * dphi;
   float sdy = 0.f;
 #pragma unroll
@@ -157,7 +164,9 @@ __device__ __forceinline__ float row_pass(const float* x, const float* av, const
 }  // namespace
 
 // PASS 0: Δ of every row of query tile i; PASS 1: its dQ. One workgroup per (head, tile).
-template <int D, int PASS>
+// SEL: the selected blocks only (their exact terms), for PWT_ROW, whose unselected blocks
+// are virtual tokens handled by rowdiag_bwd_query_kernel.
+template <int D, int PASS, bool SEL>
 __global__ __launch_bounds__(256) void literal_bwd_query_kernel(BwdArgs a) {
   constexpr int RS = LitLds<D>::RS, NT = D / 64;
   __shared__ __align__(16) uint16_t sQ[kB * RS], sG[kB * RS], sK[kB * RS], sV[kB * RS];
@@ -181,16 +190,18 @@ __global__ __launch_bounds__(256) void literal_bwd_query_kernel(BwdArgs a) {
   stage_rows<D>(sQ, Qb, mi);
   stage_rows<D>(sG, Gb, mi);
   if (tid < kB) {
-    sLse[tid] = tid < mi ? a.lse[row0 + tid] : kNegInf;
+    sLse[tid] = tid < mi ? (PASS ? a.lse2 : a.lse)[row0 + tid] : kNegInf;
     sDelta[tid] = PASS ? a.delta[row0 + tid] : 0.f;
   }
+  __syncthreads();
   const int q = tid >> 2, p = tid & 3;
   f32x16 acc[NT];
 #pragma unroll
   for (int u = 0; u < NT; ++u) acc[u] = zero16();
-  float dpart = 0.f;
+  float dpart = 0.f, mpart = 0.f;
 
   for (int j = 0; j < nb; ++j) {
+    if (SEL && !((mrow[j >> 5] >> (j & 31)) & 1u)) continue;   // the same for the whole workgroup
     const int nj = rows_of(j);
     __syncthreads();                     // previous step's tiles consumed
     stage_rows<D>(sK, Kh + size_t(j) * kB * D, nj);
@@ -215,9 +226,9 @@ __global__ __launch_bounds__(256) void literal_bwd_query_kernel(BwdArgs a) {
       av[u] = sA[q * kSS + 16 * p + u];
     }
     if constexpr (PASS == 0) {
-      dpart += row_pass<true>(x, av, in, p, dx, wv);
+      dpart += row_pass<true>(x, av, in, p, dx, wv, mpart);
     } else {
-      row_pass<false>(x, av, in, p, dx, wv);
+      row_pass<false>(x, av, in, p, dx, wv, mpart);
       bf16x8 lo, hi;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -240,8 +251,21 @@ __global__ __launch_bounds__(256) void literal_bwd_query_kernel(BwdArgs a) {
     }
   }
   if constexpr (PASS == 0) {
-    const float d = sum4(dpart);
-    if (p == 0) a.delta[row0 + q] = (q < mi && sLse[q] > kNegInf) ? d : 0.f;
+    // The forward normalised with the row sums of its bf16 P, so these fp32 P sum to
+    // 1 + O(2^-9), and that offset, times the keys' common mean, would reach dQ: the later
+    // sweeps take lse' = lse + ln Σ P and Δ = Σ P dO·v / Σ P, so their P sum to 1.
+    // SEL leaves the raw sums (Δ part in delta, mass in lse2) for the virtual tokens' sweep.
+    const float d = sum4(dpart), m = sum4(mpart);
+    const bool live = q < mi && sLse[q] > kNegInf;
+    if (p == 0) {
+      if (SEL) {
+        a.delta[row0 + q] = live ? d : 0.f;
+        a.lse2[row0 + q] = live ? m : 0.f;
+      } else {
+        a.delta[row0 + q] = live ? d / m : 0.f;
+        a.lse2[row0 + q] = live ? sLse[q] + logf(m) : kNegInf;
+      }
+    }
   } else {
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
@@ -255,8 +279,9 @@ __global__ __launch_bounds__(256) void literal_bwd_query_kernel(BwdArgs a) {
   }
 }
 
-// dK and dV of key block j over every query tile. One workgroup per (head, block).
-template <int D>
+// dK and dV of key block j over every query tile (SEL: over the tiles that selected it).
+// One workgroup per (head, block).
+template <int D, bool SEL>
 __global__ __launch_bounds__(256) void literal_bwd_key_kernel(BwdArgs a) {
   constexpr int RS = LitLds<D>::RS, NT = D / 64;
   __shared__ __align__(16) uint16_t sK[kB * RS], sV[kB * RS], sQ[kB * RS], sG[kB * RS];
@@ -283,6 +308,7 @@ __global__ __launch_bounds__(256) void literal_bwd_key_kernel(BwdArgs a) {
   for (int u = 0; u < NT; ++u) ak[u] = av_[u] = zero16();
 
   for (int i = 0; i < nb; ++i) {
+    if (SEL && !((mh[size_t(i) * a.nw + (j >> 5)] >> (j & 31)) & 1u)) continue;
     const int mi = rows_of(i);
     const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
     __syncthreads();
@@ -291,7 +317,7 @@ __global__ __launch_bounds__(256) void literal_bwd_key_kernel(BwdArgs a) {
     stage_cols<D>(sQT, Qh + size_t(i) * kB * D, mi);
     stage_cols<D>(sGT, Gh + size_t(i) * kB * D, mi);
     if (tid < kB) {
-      sLse[tid] = tid < mi ? a.lse[row0 + tid] : kNegInf;
+      sLse[tid] = tid < mi ? a.lse2[row0 + tid] : kNegInf;
       sDelta[tid] = tid < mi ? a.delta[row0 + tid] : 0.f;
     }
     __syncthreads();
@@ -312,7 +338,8 @@ __global__ __launch_bounds__(256) void literal_bwd_key_kernel(BwdArgs a) {
       x[u] = sS[q * kSS + 16 * p + u];
       avv[u] = sA[q * kSS + 16 * p + u];
     }
-    row_pass<false>(x, avv, in, p, dx, wv);
+    float unused = 0.f;
+    row_pass<false>(x, avv, in, p, dx, wv, unused);
     // transposed: [key][query]
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
@@ -347,16 +374,424 @@ __global__ __launch_bounds__(256) void literal_bwd_key_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// PWT_ROW: the virtual tokens with the per-row w_{t,j} = ½ Σ_c q_{t,c}² σ²_{j,c} (Sparse
+// Linear Attention blog, PWT section). For query t and unselected block j:
+//   P = e^{q·k̄_j + ln n_j + φ(w) - lse_t},  dℓ = P (dO·v̄_j + dO·(H̄ q_t) / n_j - Δ_t),
+//   dw = φ'(w) dℓ,  Ā_t = Σ_j P / n_j,
+//   dq_t += Σ_j dℓ k̄_j + q_t ∘ Σ_j dw σ²_j + Ā_t H̄ᵀ dO_t,
+//   dk̄_j = Σ_t dℓ q_t,  dv̄_j = Σ_t P dO_t,  dσ²_j = ½ Σ_t dw q_t²,
+// the statistics' gradients then reaching the tokens as for PWT. The selected blocks' exact
+// terms come from the LITERAL kernels above restricted to the selection.
+//
+// The virtual kernels keep the 32 x 32 score quarters in registers: the rows of the
+// product's A operand are fed in the permuted order that makes accumulator registers
+// [8 ks, 8 ks + 8) the B operand of k-step ks of the next product (feed_row), so the
+// softmax terms go from one MFMA to the next without LDS. Centroid, v̄ and σ² rows are the
+// fp32 statistics rounded to bf16; w enters the exponent and decides the gate, so it is
+// formed from hi + lo parts of q² and ½ σ² (three products, within ~2^-16 of fp32), as in
+// the forward's virtual_row_kernel.
+
+namespace {
+
+// Rows of centroid group gi (k̄, v̄ = ΣV / n, ½ σ² as hi + lo parts) as bf16 [64][D] tiles,
+// zeros past nb; with T also k̄ᵀ and σ²ᵀ as [D][72] tiles.
+template <int D, bool T>
+__device__ __forceinline__ void stage_group(uint16_t* kb, uint16_t* vb, uint16_t* s2, uint16_t* s2lo, uint16_t* kbt,
+                                            uint16_t* s2t, const BwdArgs& a, int h, int gi) {
+  constexpr int RS = LitLds<D>::RS, CPR = D / 8;
+  for (int x = threadIdx.x; x < kB * CPR; x += 256) {
+    const int r = x / CPR, col = (x % CPR) * 8, j = gi * kB + r;
+    float k8[8], v8[8], s8[8];
+    if (j < a.nb) {
+      const size_t o = (size_t(h) * a.nb + j) * D + col;
+      const float inv = 1.f / float(min(max(a.block_len ? a.block_len[j] : kB, 1), kB));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        k8[u] = a.kbar[o + u];
+        v8[u] = a.vsum[o + u] * inv;
+        s8[u] = a.ksig2[o + u];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) k8[u] = v8[u] = s8[u] = 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      kb[r * RS + col + u] = f32_to_bf16(k8[u]);
+      vb[r * RS + col + u] = f32_to_bf16(v8[u]);
+      const uint16_t hs = f32_to_bf16(0.5f * s8[u]);
+      s2[r * RS + col + u] = hs;
+      s2lo[r * RS + col + u] = f32_to_bf16(0.5f * s8[u] - bf16_to_f32(hs));
+      if constexpr (T) {
+        kbt[(col + u) * kTS + r] = f32_to_bf16(k8[u]);
+        s2t[(col + u) * kTS + r] = f32_to_bf16(s8[u]);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ bf16x8 square8(bf16x8 v) {
+  bf16x8 r;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const float f = static_cast<float>(v[u]);
+    r[u] = static_cast<__bf16>(f * f);
+  }
+  return r;
+}
+
+// q² of bf16 q as hi + lo bf16 parts (together exact to 2^-16 relative).
+__device__ __forceinline__ void square8_split(bf16x8 v, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const float f = static_cast<float>(v[u]) * static_cast<float>(v[u]);
+    hi[u] = static_cast<__bf16>(f);
+    lo[u] = static_cast<__bf16>(f - static_cast<float>(hi[u]));
+  }
+}
+
+// φ and φ' of a gated w (the forward's rule), and the virtual token's log-weight offset.
+struct PhiOut {
+  float phi, dphi;
+};
+__device__ __forceinline__ PhiOut phi_of(float w, float lnn, int gate, int linear) {
+  const bool fired = gate && w > lnn;
+  if (fired) w = 0.f;
+  return {linear ? log1pf(w) : w, fired ? 0.f : (linear ? 1.f / (1.f + w) : 1.f)};
+}
+
+}  // namespace
+
+// Per query tile: PASS 0 adds the virtual tokens' share of Δ_t; PASS 1 adds their share of
+// dQ (without Ā H̄ᵀ dO) and writes Ā_t. Wave (kh, x): centroids [32 kh, +32) of each group
+// against queries [32 x, +32), Sᵀ, (dO V̄ᵀ)ᵀ and Wᵀ in registers; dQᵀ of the wave's queries
+// summed over its centroid half, the halves added at the end.
+template <int D, int PASS>
+__global__ __launch_bounds__(256) void rowdiag_bwd_query_kernel(BwdArgs a) {
+  constexpr int RS = LitLds<D>::RS, NE = D / 32, NKD = D / 16;
+  __shared__ __align__(16) uint16_t sQ[kB * RS], sG[kB * RS];
+  __shared__ __align__(16) uint16_t sGrp[4 * kB * RS];              // k̄, v̄, ½σ² hi, lo rows; then hand-over
+  __shared__ __align__(16) uint16_t sKbT[PASS ? D * kTS : 8], sS2T[PASS ? D * kTS : 8];
+  __shared__ float sRow[3][kB], sLnn[kB], sInv[kB], sRed[2][kB];
+  __shared__ int sEx[kB];
+  uint16_t *sKb = sGrp, *sVb = sGrp + kB * RS, *sS2 = sGrp + 2 * kB * RS, *sS2l = sGrp + 3 * kB * RS;
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int wave = tid >> 6, kh = wave & 1, x = wave >> 1;
+  const int nb = a.nb, h = int(blockIdx.x) / nb, i = int(blockIdx.x) % nb, ngrp = a.nbp / kB;
+  auto rows_of = [&](int b) { return a.block_len ? min(max(a.block_len[b], 1), kB) : kB; };
+  const int mi = rows_of(i);
+  const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
+  stage_rows<D>(sQ, static_cast<const uint16_t*>(a.Q) + row0 * D, mi);
+  stage_rows<D>(sG, static_cast<const uint16_t*>(a.dO) + row0 * D, mi);
+  if (tid < kB) {
+    sRow[0][tid] = tid < mi ? (PASS ? a.lse2 : a.lse)[row0 + tid] : kNegInf;
+    sRow[1][tid] = PASS ? a.delta[row0 + tid] : 0.f;
+    sRow[2][tid] = a.gu[row0 + tid];
+  }
+  __syncthreads();
+  const int t = 32 * x + c;                                        // this lane's query
+  const float lse_t = sRow[0][t], delta_t = sRow[1][t], gu_t = sRow[2][t];
+  const bool live = t < mi && lse_t > kNegInf;
+  const uint32_t* mrow = a.mask + (size_t(h) * nb + i) * a.nw;
+  const int fr = 32 * kh + feed_row<MmaBF16>(c);                   // centroid row fed by this lane
+  f32x16 dq[NE], dqw[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) dq[e] = dqw[e] = zero16();
+  float dpart = 0.f, mpart = 0.f, apart = 0.f;
+
+  for (int gi = 0; gi < ngrp; ++gi) {
+    __syncthreads();                                               // previous group's tiles read
+    stage_group<D, PASS == 1>(sKb, sVb, sS2, sS2l, sKbT, sS2T, a, h, gi);
+    if (tid < kB) {
+      const int j = gi * kB + tid;
+      const bool in = j < nb;
+      const int n = in ? rows_of(j) : 1;
+      sLnn[tid] = __logf(float(n));
+      sInv[tid] = 1.f / float(n);
+      sEx[tid] = !in || ((mrow[j >> 5] >> (j & 31)) & 1u);
+    }
+    __syncthreads();
+    f32x16 S = zero16(), A = zero16(), W = zero16();
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks) {
+      const int k0 = 16 * ks + 8 * g;
+      const bf16x8 q = lds8(sQ + t * RS + k0);
+      bf16x8 qh, ql;
+      square8_split(q, qh, ql);
+      const bf16x8 sh = lds8(sS2 + fr * RS + k0);
+      S = MmaBF16::mma(lds8(sKb + fr * RS + k0), q, S);
+      A = MmaBF16::mma(lds8(sVb + fr * RS + k0), lds8(sG + t * RS + k0), A);
+      W = MmaBF16::mma(sh, ql, W);
+      W = MmaBF16::mma(lds8(sS2l + fr * RS + k0), qh, W);
+      W = MmaBF16::mma(sh, qh, W);
+    }
+    bf16x8 dlb[2], dwb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int jl = 32 * kh + 16 * (r >> 3) + 8 * g + (r & 7);    // centroid of register r
+      const bool ok = live && !sEx[jl];
+      const float lnn = sLnn[jl], inv = sInv[jl];
+      const PhiOut ph = phi_of(W[r], lnn, a.gate, a.w_linear);
+      const float P = ok ? __expf(S[r] + lnn + ph.phi - lse_t) : 0.f;
+      const float dpv = fmaf(gu_t, inv, A[r]);
+      if constexpr (PASS == 0) {
+        dpart = fmaf(P, dpv, dpart);
+        mpart += P;
+      } else {
+        const float dl = P * (dpv - delta_t);
+        apart = fmaf(P, inv, apart);
+        dlb[r >> 3][r & 7] = static_cast<__bf16>(dl);
+        dwb[r >> 3][r & 7] = static_cast<__bf16>(dl * ph.dphi);
+      }
+    }
+    if constexpr (PASS == 1) {
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int k0 = 32 * kh + 16 * ks + 8 * g;
+          dq[e] = MmaBF16::mma(lds8(sKbT + (32 * e + c) * kTS + k0), dlb[ks], dq[e]);
+          dqw[e] = MmaBF16::mma(lds8(sS2T + (32 * e + c) * kTS + k0), dwb[ks], dqw[e]);
+        }
+    }
+  }
+
+  __syncthreads();                                                 // group tiles no longer read
+  if constexpr (PASS == 0) {
+    // add the selected blocks' sums (left by the exact sweep) and renormalise (see there)
+    const float v = sum_halves(dpart), m = sum_halves(mpart);
+    if (kh == 1 && g == 0) {
+      sRed[0][t] = v;
+      sRed[1][t] = m;
+    }
+    __syncthreads();
+    if (kh == 0 && g == 0) {
+      const float dt = a.delta[row0 + t] + v + sRed[0][t], mt = a.lse2[row0 + t] + m + sRed[1][t];
+      a.delta[row0 + t] = live ? dt / mt : 0.f;
+      a.lse2[row0 + t] = live ? lse_t + logf(mt) : kNegInf;
+    }
+  } else {
+    const float v = sum_halves(apart);
+    if (kh == 1 && g == 0) sRed[1][t] = v;
+    // this wave's share of dQ[t][d]: Σ dℓ k̄ + q ∘ Σ dw σ²
+    float* hand = reinterpret_cast<float*>(sGrp);                  // [x][e][r][lane] of the kh = 1 waves
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * e + acc_row(r, g);
+        const float cv = fmaf(bf16_to_f32(sQ[t * RS + d]), dqw[e][r], dq[e][r]);
+        if (kh == 1) hand[((x * NE + e) * 16 + r) * 64 + lane] = cv;
+        else dq[e][r] = cv;
+      }
+    __syncthreads();
+    if (kh == 0) {
+      if (g == 0) a.abar[row0 + t] = live ? v + sRed[1][t] : 0.f;
+      if (t < mi) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const size_t o = (row0 + t) * D + 32 * e + acc_row(r, g);
+            a.dQ[o] += dq[e][r] + hand[((x * NE + e) * 16 + r) * 64 + lane];
+          }
+      }
+    }
+  }
+}
+
+// dQ += Ā_t H̄ᵀ dO_t for every row: vᵀ = H̄ᵀ dOᵀ on bf16 MFMA with H̄ᵀ as hi + lo bf16 parts
+// (dO exact in bf16). One workgroup per (head, 8 query tiles); wave w takes query half w & 1
+// and every other 32-row tile of d.
+template <int D>
+__global__ __launch_bounds__(256) void rowdiag_bwd_hterm_kernel(BwdArgs a) {
+  constexpr int RS = LitLds<D>::RS, NE = D / 32, NKD = D / 16, TG = 8;
+  __shared__ __align__(16) uint16_t sHh[D * RS], sHl[D * RS];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31, wave = tid >> 6;
+  const int h = blockIdx.y, nb = a.nb;
+  const float* hT = a.hbarT + size_t(h) * D * D;
+  for (int e = tid; e < D * D; e += 256) {                         // H̄ᵀ[c][e'] row-major
+    const float f = hT[e];
+    const uint16_t hi = f32_to_bf16(f);
+    sHh[(e / D) * RS + e % D] = hi;
+    sHl[(e / D) * RS + e % D] = f32_to_bf16(f - bf16_to_f32(hi));
+  }
+  __syncthreads();
+  const uint16_t* Gh = static_cast<const uint16_t*>(a.dO);
+  for (int i = blockIdx.x * TG; i < min(nb, blockIdx.x * TG + TG); ++i) {
+    const int mi = a.block_len ? min(max(a.block_len[i], 1), kB) : kB;
+    const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
+    const int t = 32 * (wave & 1) + c;
+    bf16x8 gf[NKD];
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks)
+      gf[ks] = t < mi ? lds8(Gh + (row0 + t) * D + 16 * ks + 8 * g) : MmaBF16::zero();
+    const float ab = t < mi ? a.abar[row0 + t] : 0.f;
+    for (int e = wave >> 1; e < NE; e += 2) {
+      f32x16 v = zero16();
+#pragma unroll
+      for (int ks = 0; ks < NKD; ++ks) {
+        const int k0 = 16 * ks + 8 * g;
+        v = MmaBF16::mma(lds8(sHh + (32 * e + c) * RS + k0), gf[ks], v);
+        v = MmaBF16::mma(lds8(sHl + (32 * e + c) * RS + k0), gf[ks], v);
+      }
+      if (t < mi && ab != 0.f) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a.dQ[(row0 + t) * D + 32 * e + acc_row(r, g)] += ab * v[r];
+      }
+    }
+  }
+}
+
+// Per centroid group (every query tile): dk̄_j = Σ_t dℓ q_t, dv̄_j = Σ_t P dO_t and
+// dσ²_j = ½ Σ_t dw q_t² of its unselected pairs. Wave (kh, x): centroids [32 kh, +32) (one per
+// lane) against queries [32 x, +32) (fed permuted, so the registers are the B operands of
+// the products with Qᵀ, dOᵀ and (q²)ᵀ); the two query halves are added at the end.
+template <int D>
+__global__ __launch_bounds__(256) void rowdiag_bwd_key_kernel(BwdArgs a) {
+  constexpr int RS = LitLds<D>::RS, NE = D / 32, NKD = D / 16;
+  __shared__ __align__(16) uint16_t sGrp[4 * kB * RS];
+  __shared__ __align__(16) uint16_t sBuf[2 * kB * RS + 2 * D * kTS];   // Q, dO rows, Qᵀ, dOᵀ; then hand-over
+  __shared__ float sRow[3][kB];
+  uint16_t *sKb = sGrp, *sVb = sGrp + kB * RS, *sS2 = sGrp + 2 * kB * RS, *sS2l = sGrp + 3 * kB * RS;
+  uint16_t *sQ = sBuf, *sG = sBuf + kB * RS, *sQT = sBuf + 2 * kB * RS, *sGT = sQT + D * kTS;
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int wave = tid >> 6, kh = wave & 1, x = wave >> 1;
+  const int nb = a.nb, ngrp = a.nbp / kB, h = int(blockIdx.x) / ngrp, gi = int(blockIdx.x) % ngrp;
+  auto rows_of = [&](int b) { return a.block_len ? min(max(a.block_len[b], 1), kB) : kB; };
+  stage_group<D, false>(sKb, sVb, sS2, sS2l, nullptr, nullptr, a, h, gi);
+  const int jl = 32 * kh + c, j = gi * kB + jl;                    // this lane's centroid
+  const bool inj = j < nb;
+  const float nj = float(inj ? rows_of(j) : 1), lnn = __logf(nj), inv = 1.f / nj;
+  const int fr = 32 * x + feed_row<MmaBF16>(c);                    // query row fed by this lane
+  const uint32_t* mh = a.mask + size_t(h) * nb * a.nw;
+  f32x16 dkb[NE], dvb[NE], dsg[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) dkb[e] = dvb[e] = dsg[e] = zero16();
+
+  for (int i = 0; i < nb; ++i) {
+    const int mi = rows_of(i);
+    const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
+    __syncthreads();
+    const uint16_t* Qb = static_cast<const uint16_t*>(a.Q) + row0 * D;
+    const uint16_t* Gb = static_cast<const uint16_t*>(a.dO) + row0 * D;
+    stage_rows<D>(sQ, Qb, mi);
+    stage_rows<D>(sG, Gb, mi);
+    stage_cols<D>(sQT, Qb, mi);
+    stage_cols<D>(sGT, Gb, mi);
+    if (tid < kB) {
+      sRow[0][tid] = tid < mi ? a.lse2[row0 + tid] : kNegInf;
+      sRow[1][tid] = a.delta[row0 + tid];
+      sRow[2][tid] = a.gu[row0 + tid];
+    }
+    __syncthreads();
+    const bool ex = !inj || ((mh[size_t(i) * a.nw + (j >> 5)] >> (j & 31)) & 1u);
+    f32x16 S = zero16(), A = zero16(), W = zero16();
+#pragma unroll
+    for (int ks = 0; ks < NKD; ++ks) {
+      const int k0 = 16 * ks + 8 * g;
+      const bf16x8 q = lds8(sQ + fr * RS + k0);
+      bf16x8 qh, ql;
+      square8_split(q, qh, ql);
+      const bf16x8 sh = lds8(sS2 + jl * RS + k0);
+      S = MmaBF16::mma(q, lds8(sKb + jl * RS + k0), S);
+      A = MmaBF16::mma(lds8(sG + fr * RS + k0), lds8(sVb + jl * RS + k0), A);
+      W = MmaBF16::mma(ql, sh, W);
+      W = MmaBF16::mma(qh, lds8(sS2l + jl * RS + k0), W);
+      W = MmaBF16::mma(qh, sh, W);
+    }
+    bf16x8 pb[2], dlb[2], dwb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tq = 32 * x + 16 * (r >> 3) + 8 * g + (r & 7);     // query of register r
+      const float lse = sRow[0][tq];
+      const bool ok = !ex && tq < mi && lse > kNegInf;
+      const PhiOut ph = phi_of(W[r], lnn, a.gate, a.w_linear);
+      const float P = ok ? __expf(S[r] + lnn + ph.phi - lse) : 0.f;
+      const float dl = P * (fmaf(sRow[2][tq], inv, A[r]) - sRow[1][tq]);
+      pb[r >> 3][r & 7] = static_cast<__bf16>(P);
+      dlb[r >> 3][r & 7] = static_cast<__bf16>(dl);
+      dwb[r >> 3][r & 7] = static_cast<__bf16>(dl * ph.dphi);
+    }
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int k0 = 32 * x + 16 * ks + 8 * g;
+        const bf16x8 qt = lds8(sQT + (32 * e + c) * kTS + k0);
+        dkb[e] = MmaBF16::mma(qt, dlb[ks], dkb[e]);
+        dvb[e] = MmaBF16::mma(lds8(sGT + (32 * e + c) * kTS + k0), pb[ks], dvb[e]);
+        dsg[e] = MmaBF16::mma(square8(qt), dwb[ks], dsg[e]);
+      }
+  }
+
+  // add the query halves (x = 1 hands over through LDS, one quantity at a time) and write
+  float* hand = reinterpret_cast<float*>(sBuf);                    // [kh][e][r][lane]
+  const size_t ob = (size_t(h) * nb + min(j, nb - 1)) * D;
+  const size_t op = (size_t(h) * a.nbp + j) * D;                   // chunk 0 of the partial sums
+  auto combine = [&](f32x16 (&v)[NE], auto store) {
+    __syncthreads();
+    if (x == 1) {
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) hand[((kh * NE + e) * 16 + r) * 64 + lane] = v[e][r];
+    }
+    __syncthreads();
+    if (x == 0 && inj) {
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) store(32 * e + acc_row(r, g), v[e][r] + hand[((kh * NE + e) * 16 + r) * 64 + lane]);
+    }
+  };
+  combine(dkb, [&](int d, float val) { a.dkbar_part[op + d] = val; });
+  combine(dvb, [&](int d, float val) { a.dvbar_part[op + d] = val; });
+  combine(dsg, [&](int d, float val) { a.dsig2[ob + d] = 0.5f * val; });
+}
+
+template <int D>
+static hipError_t launch_rowdiag_bwd_d(const BwdArgs& a0, hipStream_t s) {
+  BwdArgs a = a0;
+  a.nchunk = 1;                          // one partial sum per centroid (rowdiag_bwd_key_kernel)
+  a.qsq = nullptr;
+  const dim3 tiles(unsigned(a.H) * unsigned(a.nb)), groups(unsigned(a.H) * unsigned(a.nbp / kB));
+#define PISA_LAUNCH(...)                       \
+  do {                                         \
+    hipLaunchKernelGGL(__VA_ARGS__);           \
+    hipError_t e_ = hipGetLastError();         \
+    if (e_ != hipSuccess) return e_;           \
+  } while (0)
+  hipError_t e = launch_bwd_rows(a, s);
+  if (e != hipSuccess) return e;
+  PISA_LAUNCH((literal_bwd_query_kernel<D, 0, true>), tiles, dim3(256), 0, s, a);
+  PISA_LAUNCH((rowdiag_bwd_query_kernel<D, 0>), tiles, dim3(256), 0, s, a);
+  PISA_LAUNCH((literal_bwd_query_kernel<D, 1, true>), tiles, dim3(256), 0, s, a);
+  PISA_LAUNCH((rowdiag_bwd_query_kernel<D, 1>), tiles, dim3(256), 0, s, a);
+  PISA_LAUNCH((rowdiag_bwd_hterm_kernel<D>), dim3((a.nb + 7) / 8, a.H), dim3(256), 0, s, a);
+  PISA_LAUNCH((literal_bwd_key_kernel<D, true>), tiles, dim3(256), 0, s, a);
+  PISA_LAUNCH((rowdiag_bwd_key_kernel<D>), groups, dim3(256), 0, s, a);
+#undef PISA_LAUNCH
+  return launch_bwd_stats_tail(a, s);
+}
+
+hipError_t launch_rowdiag_bwd(const BwdArgs& a, hipStream_t s) {
+  return a.d == 64 ? launch_rowdiag_bwd_d<64>(a, s) : launch_rowdiag_bwd_d<128>(a, s);
+}
+
 template <int D>
 static hipError_t launch_literal_bwd_d(const BwdArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.H) * unsigned(a.nb));
-  hipLaunchKernelGGL((literal_bwd_query_kernel<D, 0>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((literal_bwd_query_kernel<D, 0, false>), grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((literal_bwd_query_kernel<D, 1>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((literal_bwd_query_kernel<D, 1, false>), grid, dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((literal_bwd_key_kernel<D>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((literal_bwd_key_kernel<D, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -183,6 +183,7 @@ struct BwdArgs {
   float* dK;
   float* dV;
   float* delta;      // [H][L]   Δ_t = dO_t·o_t: dO·O from O, else formed as Σ P dP
+  float* lse2;       // [H][L]   LITERAL / PWT_ROW: lse + ln Σ P (the sweeps' P then sum to 1)
   float* gu;         // [H][L]   dO·(H̄ q)
   float* abar;       // [H][L]   Ā_t
   float* qsq;        // [H][nb][d] pooled q² (PWT) or null
@@ -260,6 +261,11 @@ hipError_t launch_attention_bwd(int bf16, int mode, const BwdArgs& a, hipStream_
 // (attention_bwd_literal.hip); reads Q, K, V, dO, lse, mask, block_len; writes delta, dQ,
 // dK, dV.
 hipError_t launch_literal_bwd(const BwdArgs& a, hipStream_t s);
+// bf16 PWT_ROW backward (attention_bwd_literal.hip), and the pieces of attention_bwd.hip it
+// shares: gu = dO·(H̄ q) per row; dH̄ from Ā, then the statistics' gradients onto the tokens.
+hipError_t launch_rowdiag_bwd(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_rows(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_stats_tail(const BwdArgs& a, hipStream_t s);
 hipError_t launch_select(int bf16, const SelectArgs& a, hipStream_t s);
 hipError_t launch_select_large(const SelectArgs& a, hipStream_t s);
 hipError_t launch_pooled_w(const SelectArgs& a, hipStream_t s);

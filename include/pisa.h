@@ -286,7 +286,7 @@ size_t pisa_attention_bwd_workspace_bytes(pisa_dtype dt, int H, int L, int d, in
 
 /*
  * Backward of pisa_attention_fwd for PISA_MODE_DROP, PISA_MODE_PISA, PISA_MODE_PWT and (bf16)
- * PISA_MODE_LITERAL (with the same modifier bits), for sparse fine-tuning (blog, PWT
+ * PISA_MODE_LITERAL and PISA_MODE_PWT_ROW (with the same modifier bits), for sparse fine-tuning (blog, PWT
  * section: gradients flow through the block statistics k̄_j, H̄ and σ²_j; routing is
  * detached). The selection and the gate's decisions are held fixed; the loss is
  * sum(dO * O).
@@ -315,10 +315,15 @@ size_t pisa_attention_bwd_workspace_bytes(pisa_dtype dt, int H, int L, int d, in
  *   dx_n = E dO·v_n + dw y_n / n_j - mean_m(...) + dℓ / n_j,  dℓ = E (Σ_n (1 + y_n) dO·v_n - n_j Δ),
  *   dw = φ'(w) dℓ, and dq = Σ dx k, dk = Σ dx q, dv = Σ (P or E (1 + y)) dO over every
  *   (query tile, key block) pair. Δ is formed in fp32 by a first sweep over all pairs (O is
- *   not read), so this backward costs about three dense score sweeps. fp32 inputs give
- *   PISA_ERR_UNSUPPORTED for LITERAL.
- * Sums are taken in a fixed order (repeated calls are bit-identical). PWT_ROW gives
- * PISA_ERR_UNSUPPORTED.
+ *   not read), so this backward costs about three dense score sweeps.
+ * PISA_MODE_PWT_ROW (bf16 inputs; w_{t,j} = ½ Σ_c q_{t,c}² σ²_{j,c} per row): as PWT with
+ *   dw_{t,j} = φ'(w_{t,j}) dℓ_{t,j} per row, so dq_t gains q_t ∘ Σ_j dw σ²_j and
+ *   dσ²_j = ½ Σ_t dw q_t² (in place of the pooled terms); the selected blocks' exact terms,
+ *   Δ and Ā as above.
+ * For LITERAL and PWT_ROW the Δ sweep also sums P and the later sweeps use lse + ln Σ P (the
+ * forward normalised with sums of its bf16 P; the common mean of the keys would amplify
+ * the 2^-9 offset in dq). fp32 inputs give PISA_ERR_UNSUPPORTED for these two modes.
+ * Sums are taken in a fixed order (repeated calls are bit-identical).
  */
 pisa_status pisa_attention_bwd(pisa_dtype dt, const void* Q, const void* K, const void* V,
                                const pisa_stats* st, const int32_t* idx, const uint32_t* mask,

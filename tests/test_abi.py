@@ -186,8 +186,8 @@ def test_rope_select_argument_errors(lib, rope, msg):
 
 
 @pytest.mark.parametrize("case,status,msg", [
-    (dict(mode=3, dt=0), 2, "LITERAL backward takes bf16"),
-    (dict(mode=4), 2, "DROP, PISA, PWT and LITERAL"),
+    (dict(mode=3, dt=0), 2, "PWT_ROW backward takes bf16"),
+    (dict(mode=4, dt=0), 2, "PWT_ROW backward takes bf16"),
     (dict(mode=9), 1, "unknown mode"),
     (dict(mask=None), 1, "mask must not be NULL"),
     (dict(wt=None), 1, "wt must not be NULL"),
