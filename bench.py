@@ -419,6 +419,20 @@ def main():
         del gbuf, ws_bwd, dO
 
     progress("backward done")
+    def row_backward_ms(name):
+        """One backward call of LITERAL or PWT_ROW (bf16) on the step's selection, after its
+        forward call; one warm-up call and one timed call."""
+        g = torch.randn(Q.shape, dtype=torch.float32, device="cuda",
+                        generator=torch.Generator(device="cuda").manual_seed(7)).to(Q.dtype)
+        bufs = tuple(torch.empty(H, L, d, dtype=torch.float32, device="cuda") for _ in range(3))
+        ws_r = torch.empty(pisa.load().pisa_attention_bwd_workspace_bytes(1, H, L, d, 64, K_sel),
+                           dtype=torch.uint8, device="cuda")
+        pisa.attention_fwd(Q, K, V, st, idx, mask, None, K_sel, name, blt, out=O, lse=lse)
+        ms_r = timed(lambda: pisa.attention_bwd(Q, K, V, st, idx, mask, None, K_sel, lse, g, name, blt,
+                                                out=bufs, workspace=ws_r), 1)
+        del g, bufs, ws_r
+        return ms_r
+
     # PWT with the per-row diagonal w (the pooling ablation), on the same selection
     pwt_row = None
     if mode != "pwt_row":
@@ -426,6 +440,8 @@ def main():
         ms_row = timed(lambda: pisa.attention_fwd(Q, K, V, st, idx, mask, None, K_sel, "pwt_row", blt, out=O), 3)
         pwt_row = {"ms_attention": round(ms_row, 4), "attention_flops": fr["attention"],
                    "tflops": round(fr["attention"] / (ms_row * 1e-3) / 1e12, 2)}
+        if cfg.dtype == "bf16" and nb <= 2048:
+            pwt_row["backward_ms"] = round(row_backward_ms("pwt_row"), 4)
 
     progress("per-row w done")
     # LITERAL, reported but not held to the dense target
@@ -435,6 +451,10 @@ def main():
         ms_lit = timed(lambda: pisa.attention_fwd(Q, K, V, st, idx, mask, None, K_sel, "literal", blt, out=O), 3)
         literal = {"ms_attention": round(ms_lit, 4), "attention_flops": fl["attention"],
                    "tflops": round(fl["attention"] / (ms_lit * 1e-3) / 1e12, 2)}
+        # its backward sweeps every (query tile, key block) pair three times: timed where that
+        # stays within seconds
+        if cfg.dtype == "bf16" and nb * nb * H <= 2 * 10 ** 7:
+            literal["backward_ms"] = round(row_backward_ms("literal"), 4)
 
     progress("LITERAL done")
     dense = {}

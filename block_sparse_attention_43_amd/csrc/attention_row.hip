@@ -37,6 +37,7 @@ void virtual_row_kernel(AttnArgs a) {
   constexpr float NEG_INF = -__builtin_huge_valf();
   __shared__ __align__(16) float sX[2 * NET * 16 * 64 + 6 * 64];   // hand-over, then output staging
   __shared__ float sW[kB];                                          // weight of the DROP pass per row
+  __shared__ __align__(16) bf16x8 sSgl[2][D / 16][64];              // lo parts of σ²/2, per wave and lane
 
   const int lane = threadIdx.x & 63, g = lane >> 5, l32 = lane & 31;
   const int kh = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -70,7 +71,7 @@ void virtual_row_kernel(AttnArgs a) {
 
   // Operands of group grp for this wave's key half: centroid and σ²/2 fragments (A of the
   // score and w products; lane 32 g + R holds centroid key_of_row(R)), v̄ᵀ fragments.
-  bf16x8 kb[NKD], sg[NKD], sgl[NKD], vb[NVF];   // σ²/2 as hi (sg) + lo (sgl) parts
+  bf16x8 kb[NKD], sg[NKD], vb[NVF];             // σ²/2 as hi (sg) + lo (in LDS: registers are full) parts
   uint32_t mword = 0u;
   int blen[16];
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbh, uint32_t(ngrp) * TB), rv = make_rsrc(vbh, uint32_t(ngrp) * TB);
@@ -94,8 +95,10 @@ void virtual_row_kernel(AttnArgs a) {
       const float4 x1 = *reinterpret_cast<const float4*>(sr + 16 * f + 4);
       const float v[8] = {hv * x0.x, hv * x0.y, hv * x0.z, hv * x0.w, hv * x1.x, hv * x1.y, hv * x1.z, hv * x1.w};
       sg[f] = MmaBF16::pack(v);
+      bf16x8 lo;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sgl[f][e] = static_cast<__bf16>(v[e] - static_cast<float>(sg[f][e]));
+      for (int e = 0; e < 8; ++e) lo[e] = static_cast<__bf16>(v[e] - static_cast<float>(sg[f][e]));
+      sSgl[kh][f][lane] = lo;
     }
     // keys of this lane's score registers: 16 (r / 8) + 8 g + r % 8 of the half
     const int jw = grp * kB + 32 * kh;
@@ -142,7 +145,7 @@ void virtual_row_kernel(AttnArgs a) {
         }
         s = MmaBF16::mma(kb[ks], qf[u][ks], s);
         w = MmaBF16::mma(sg[ks], q2l, w);
-        w = MmaBF16::mma(sgl[ks], q2h, w);
+        w = MmaBF16::mma(sSgl[kh][ks][lane], q2h, w);
         w = MmaBF16::mma(sg[ks], q2h, w);
       }
       if (u == 1 && grp + 1 < ngrp) load_k(grp + 1);
