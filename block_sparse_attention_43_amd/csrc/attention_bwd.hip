@@ -819,8 +819,9 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   dsum = sum_halves(dsum);
   if (g == 0) sDel[wk][qrow] = dsum;
   __syncthreads();
-  const float delta = qvalid ? sDel[0][qrow] + sDel[1][qrow] : 0.f;
-  if (wk == 0 && g == 0) a.delta[row0 + qrow] = qvalid ? dl + delta : 0.f;
+  // (DIR with a final Δ, a.delta_final: dS already used the row's Δ; no correction)
+  const float delta = qvalid && !(DIR && a.delta_final) ? sDel[0][qrow] + sDel[1][qrow] : 0.f;
+  if (wk == 0 && g == 0 && !(DIR && a.delta_final)) a.delta[row0 + qrow] = qvalid ? dl + delta : 0.f;
 #pragma unroll
   for (int et = 0; et < NET; ++et)
 #pragma unroll
@@ -1840,6 +1841,25 @@ static hipError_t launch_bwd_stats_tail_d(const BwdArgs& a, hipStream_t s) {
 
 hipError_t launch_bwd_stats_tail(const BwdArgs& a, hipStream_t s) {
   return a.d == 64 ? launch_bwd_stats_tail_d<64>(a, s) : launch_bwd_stats_tail_d<128>(a, s);
+}
+
+template <int D>
+static hipError_t launch_bwd_exact_sweeps_d(const BwdArgs& a, hipStream_t s) {
+  const dim3 tiles(unsigned(a.H) * unsigned(a.nb)), blocks((a.nb + 255) / 256, a.H);
+  hipLaunchKernelGGL((bwd_query_kernel<uint16_t, D, MODE_DROP, true>), tiles, dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(csr_count_kernel, blocks, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(csr_scan_kernel, dim3(a.H), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(csr_fill_kernel, blocks, dim3(256), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_key_kernel<uint16_t, D, MODE_DROP, false>), tiles, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_exact_sweeps(const BwdArgs& a, hipStream_t s) {
+  return a.d == 64 ? launch_bwd_exact_sweeps_d<64>(a, s) : launch_bwd_exact_sweeps_d<128>(a, s);
 }
 
 hipError_t launch_attention_bwd(int bf16, int mode, const BwdArgs& a, hipStream_t s) {

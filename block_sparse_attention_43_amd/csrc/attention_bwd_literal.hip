@@ -164,7 +164,7 @@ __device__ __forceinline__ float row_pass(const float* x, const float* av, const
 }  // namespace
 
 // PASS 0: Δ of every row of query tile i; PASS 1: its dQ. One workgroup per (head, tile).
-// SEL: the selected blocks only (their exact terms), for PWT_ROW, whose unselected blocks
+// SEL (PASS 0 only): the selected blocks' sums alone, for PWT_ROW, whose unselected blocks
 // are virtual tokens handled by rowdiag_bwd_query_kernel.
 template <int D, int PASS, bool SEL>
 __global__ __launch_bounds__(256) void literal_bwd_query_kernel(BwdArgs a) {
@@ -279,9 +279,8 @@ __global__ __launch_bounds__(256) void literal_bwd_query_kernel(BwdArgs a) {
   }
 }
 
-// dK and dV of key block j over every query tile (SEL: over the tiles that selected it).
-// One workgroup per (head, block).
-template <int D, bool SEL>
+// dK and dV of key block j over every query tile. One workgroup per (head, block).
+template <int D>
 __global__ __launch_bounds__(256) void literal_bwd_key_kernel(BwdArgs a) {
   constexpr int RS = LitLds<D>::RS, NT = D / 64;
   __shared__ __align__(16) uint16_t sK[kB * RS], sV[kB * RS], sQ[kB * RS], sG[kB * RS];
@@ -308,7 +307,6 @@ __global__ __launch_bounds__(256) void literal_bwd_key_kernel(BwdArgs a) {
   for (int u = 0; u < NT; ++u) ak[u] = av_[u] = zero16();
 
   for (int i = 0; i < nb; ++i) {
-    if (SEL && !((mh[size_t(i) * a.nw + (j >> 5)] >> (j & 31)) & 1u)) continue;
     const int mi = rows_of(i);
     const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
     __syncthreads();
@@ -381,8 +379,9 @@ __global__ __launch_bounds__(256) void literal_bwd_key_kernel(BwdArgs a) {
 //   dw = φ'(w) dℓ,  Ā_t = Σ_j P / n_j,
 //   dq_t += Σ_j dℓ k̄_j + q_t ∘ Σ_j dw σ²_j + Ā_t H̄ᵀ dO_t,
 //   dk̄_j = Σ_t dℓ q_t,  dv̄_j = Σ_t P dO_t,  dσ²_j = ½ Σ_t dw q_t²,
-// the statistics' gradients then reaching the tokens as for PWT. The selected blocks' exact
-// terms come from the LITERAL kernels above restricted to the selection.
+// the statistics' gradients then reaching the tokens as for PWT. The selected blocks' Δ and
+// softmax mass come from the LITERAL query kernel restricted to the selection; their dQ,
+// dK and dV from the PWT backward's exact sweeps, given the final Δ and lse + ln Σ P.
 //
 // The virtual kernels keep the 32 x 32 score quarters in registers: the rows of the
 // product's A operand are fed in the permuted order that makes accumulator registers
@@ -769,10 +768,17 @@ static hipError_t launch_rowdiag_bwd_d(const BwdArgs& a0, hipStream_t s) {
   if (e != hipSuccess) return e;
   PISA_LAUNCH((literal_bwd_query_kernel<D, 0, true>), tiles, dim3(256), 0, s, a);
   PISA_LAUNCH((rowdiag_bwd_query_kernel<D, 0>), tiles, dim3(256), 0, s, a);
-  PISA_LAUNCH((literal_bwd_query_kernel<D, 1, true>), tiles, dim3(256), 0, s, a);
+  {
+    // the selected keys' dQ and dK, dV: the PWT backward's exact sweeps, with the final Δ
+    // and the renormalised lse
+    BwdArgs b = a;
+    b.lse = a.lse2;
+    b.delta_final = 1;
+    e = launch_bwd_exact_sweeps(b, s);
+    if (e != hipSuccess) return e;
+  }
   PISA_LAUNCH((rowdiag_bwd_query_kernel<D, 1>), tiles, dim3(256), 0, s, a);
   PISA_LAUNCH((rowdiag_bwd_hterm_kernel<D>), dim3((a.nb + 7) / 8, a.H), dim3(256), 0, s, a);
-  PISA_LAUNCH((literal_bwd_key_kernel<D, true>), tiles, dim3(256), 0, s, a);
   PISA_LAUNCH((rowdiag_bwd_key_kernel<D>), groups, dim3(256), 0, s, a);
 #undef PISA_LAUNCH
   return launch_bwd_stats_tail(a, s);
@@ -791,7 +797,7 @@ static hipError_t launch_literal_bwd_d(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((literal_bwd_query_kernel<D, 1, false>), grid, dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((literal_bwd_key_kernel<D, false>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((literal_bwd_key_kernel<D>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -209,6 +209,8 @@ struct BwdArgs {
   float* vinvn;      // [nbp] 1 / n_j (0 past nb)
   int H, L, d, nb, nbp, K_sel, nw, nchunk, nhch;
   int w_linear, gate;
+  int delta_final;   // Δ in delta is final (taken over every term of the row): the exact dQ
+                     // sweep given O uses it as is, with no ε correction and no write-back
 };
 
 struct BwdLayout {
@@ -266,6 +268,10 @@ hipError_t launch_literal_bwd(const BwdArgs& a, hipStream_t s);
 hipError_t launch_rowdiag_bwd(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_rows(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_stats_tail(const BwdArgs& a, hipStream_t s);
+// The PWT backward's exact sweeps (DROP instances, bf16) with a.delta final and a.lse the
+// row normaliser: dQ of the selected keys, then the key-block lists and dK, dV of the
+// selected keys.
+hipError_t launch_bwd_exact_sweeps(const BwdArgs& a, hipStream_t s);
 hipError_t launch_select(int bf16, const SelectArgs& a, hipStream_t s);
 hipError_t launch_select_large(const SelectArgs& a, hipStream_t s);
 hipError_t launch_pooled_w(const SelectArgs& a, hipStream_t s);
