@@ -118,3 +118,40 @@ def test_backward_gate_fires_and_reruns_are_identical(gpu_lib, name):
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
     _check(inp, K_sel, sel, a, dO, name=name)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("workload,name", [("flux", "literal"), ("flux", "pwt_row"), ("wan", "pwt_row")])
+def test_backward_full_size(gpu_lib, workload, name):
+    """Full-size workloads on the oracle's selection for every head, head 0 against the
+    oracle's gradients (LITERAL's oracle, with per-block H_j and C_j, is only run on the
+    Flux-like workload: on the Wan-like one it would take the CPU too long)."""
+    inp = synth.make(workload)
+    K_sel = inp.K_sel
+    sel, w = oracle_selection(inp, K_sel)
+    print(f"{name} backward {workload} full size", flush=True)
+    dO = _dO(inp, 165)
+    got = _run(gpu_lib, inp, K_sel, sel, w, dO, name=name)
+    ok = valid_rows(inp)
+    dO64 = synth.to_float64(dO, "bf16")
+    ref = orc.attention_head_backward(inp.f64("Q", 0), inp.f64("K", 0), inp.f64("V", 0), dO64[0], 64,
+                                      inp.layout.block_len, K_sel, name, idx=sel[0])
+    for which, g, r in zip(("dQ", "dK", "dV"), got, (ref["dQ"], ref["dK"], ref["dV"])):
+        e = rel_l2(g[0][ok], r[ok])
+        assert np.all(g[0][~ok] == 0), which
+        assert e <= TOL, (workload, name, which, e)
+        print(f"{workload} {name} head 0 {which}: rel-L2 {e:.2e}")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["literal", "pwt_row"])
+def test_backward_long_tile_lists(gpu_lib, name):
+    """Nearly every block selected (K_sel = 515 of nb = 520): the exact sweeps' tile
+    descriptors are staged in chunks and refill mid-loop."""
+    inp = synth.random_blocks(107, H=1, nb=520, d=64, dtype="bf16", smooth=2.0)
+    K_sel = 515
+    sel, w = oracle_selection(inp, K_sel)
+    print(f"{name} backward nb=520 K_sel=515", flush=True)
+    dO = _dO(inp, 166)
+    got = _run(gpu_lib, inp, K_sel, sel, w, dO, name=name)
+    _check(inp, K_sel, sel, got, dO, name=name)
