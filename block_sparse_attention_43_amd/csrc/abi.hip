@@ -144,11 +144,14 @@ pisa_status select_impl(pisa_dtype dt, const void* Q, const void* Q_pre, const v
   if (nb <= pisa::kSmallNb) {
     a.scores = reinterpret_cast<float*>(ws + wl.scores);
   } else {
-    a.ktile = reinterpret_cast<float*>(ws + wl.ktile);
+    a.khl = reinterpret_cast<uint4*>(ws + wl.khl);
+    a.shl = reinterpret_cast<uint4*>(ws + wl.shl);
     a.lhist = reinterpret_cast<uint32_t*>(ws + wl.lhist);
     a.lstate = reinterpret_cast<int4*>(ws + wl.lstate);
     a.lcoff = reinterpret_cast<int*>(ws + wl.lcoff);
-    a.lcand = reinterpret_cast<uint2*>(ws + wl.lcand);
+    a.lcnt = reinterpret_cast<int*>(ws + wl.lcnt);
+    a.lcand = reinterpret_cast<uint32_t*>(ws + wl.lcand);
+    a.lparam = reinterpret_cast<float4*>(ws + wl.lparam);
     a.lkpart = reinterpret_cast<float4*>(ws + wl.lkpart);
     a.lover = reinterpret_cast<int*>(ws + wl.lover);
     a.lks = wl.lks;

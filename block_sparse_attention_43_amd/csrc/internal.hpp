@@ -86,29 +86,37 @@ struct SelectArgs {
   int H, L, d, nb, K_sel, nw;
   // nb > kSmallNb: histogram-threshold selection without the score matrix (workspace)
   uint32_t* lhist;  // [H][nb][lks][kLBins / 2] per key split, bin counts as u16 pairs
-  int4* lstate;     // [H][nb] threshold bin b*, blocks still needed from it, its count, overflow
-  int* lcoff;       // [H][nb][lks] first list slot of each key split's candidates
-  uint2* lcand;     // [H][nb][kLCap] candidates: order key, block index (ascending index)
+  int4* lstate;     // [H][nb] threshold bin b*, -, list length, sent to the fallback
+  int* lcoff;       // [H][nb][lks] first list slot of each key split's slice
+  int* lcnt;        // [H][nb][lks] near scores each key split found
+  uint32_t* lcand;  // [H][nb][kLCap] near block indices (ascending within the list)
+  float4* lparam;   // [H][nb] bin origin, bin scale, margin 2ε per row
   float4* lkpart;   // [H][lnkp] max |k̄_j|, min and max key bias, max σ²_{j,c} per 256 blocks
-  int* lover;       // [1 + H nb] rows whose threshold bin overflowed the list: count, rows
+  int* lover;       // [1 + H nb] rows for the fallback: count, rows
   int lks, lnkp;
-  // fp32 rows in the tiled order of the score products (tile_rows in select_topk.hip):
+  // bf16 hi / lo operands of the approximate score products (select_large.hip): 16-byte
+  // unit ((h·tiles + t)·2 + part)·(d/16)·64 + u·64 + lane = part of row 32 t + lane % 32,
+  // columns (lane / 32)·d/2 + 8u .. + 7, so each 16-byte load of a wave reads 1 KB.
+  uint4* khl;       // k̄ (or the turned key centroids)
+  uint4* shl;       // σ² (predicted-error route)
+  // fp32 σ² rows in the tiled order of the w̃ products (tile_rows in select_topk.hip):
   // float4 ((h·tiles + t)·(d/8) + u)·64 + lane = row 32 t + lane % 32, columns
-  // (lane / 32)·d/2 + 4u .. + 3, so each 16-byte load of a wave reads 1 KB in one piece.
-  float* ktile;     // [H][tiles][d/8][64] float4: k̄ (or the turned key centroids)
-  float* stile;     // [H][tiles][d/8][64] float4: σ²
+  // (lane / 32)·d/2 + 4u .. + 3.
+  float* stile;
 };
 
 // Selection over many key blocks: rows of at most kSmallNb blocks keep the whole score
 // row in registers; longer rows go through a linear-bin histogram of the recomputed scores.
 constexpr int kSmallNb = 2048;
 constexpr int kLBins = 256;   // linear bins per row
-constexpr int kLCap = 256;    // candidates kept per row (threshold bin)
+constexpr int kLCap = 1024;   // list slots per row (scores near the threshold bin)
+constexpr int kMaxKs = 16;    // key splits of the score passes, at most
 constexpr int kLRows = 128;   // query tiles per workgroup of the score passes
 constexpr int kMaxNb = 32768; // longest row the selection handles (128 KB of fp32 in LDS)
 
 struct SelectLayout {
-  size_t qbar, qsq, krot, stile, ktile, scores, lhist, lstate, lcoff, lcand, lkpart, lover, lmask, total;
+  size_t qbar, qsq, krot, stile, khl, shl, scores, lhist, lstate, lcoff, lcnt, lcand, lparam, lkpart, lover, lmask,
+      total;
   int lks, lnkp;
 };
 
@@ -128,15 +136,18 @@ inline SelectLayout select_layout(int H, int nb, int d) {
   }
   const int nrg = (nb + kLRows - 1) / kLRows, tiles = (nb + 31) / 32;
   int ks = 1;
-  while (ks < 16 && static_cast<long long>(nrg) * H * ks < 2048 && tiles / (2 * ks) >= 4) ks *= 2;
+  while (ks < kMaxKs && static_cast<long long>(nrg) * H * ks < 2048 && tiles / (2 * ks) >= 4) ks *= 2;
   w.lks = ks;
   w.lnkp = (nb + 255) / 256;
   const size_t nw = size_t(tiles);
-  w.ktile = o;  o = align256(o + tiled);
+  w.khl = o;    o = align256(o + tiled);
+  w.shl = o;    o = align256(o + tiled);
   w.lhist = o;  o = align256(o + Hs * nb * ks * (kLBins / 2) * 4);
   w.lstate = o; o = align256(o + Hs * nb * 16);
   w.lcoff = o;  o = align256(o + Hs * nb * ks * 4);
-  w.lcand = o;  o = align256(o + Hs * nb * kLCap * 8);
+  w.lcnt = o;   o = align256(o + Hs * nb * ks * 4);
+  w.lcand = o;  o = align256(o + Hs * nb * kLCap * 4);
+  w.lparam = o; o = align256(o + Hs * nb * 16);
   w.lkpart = o; o = align256(o + Hs * w.lnkp * 16);
   w.lover = o;  o = align256(o + (1 + Hs * nb) * 4);
   w.lmask = o;  o = align256(o + Hs * nb * nw * 4);

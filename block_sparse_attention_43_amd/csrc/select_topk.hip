@@ -405,7 +405,7 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(SelectArgs a) {
   }
 }
 
-// fp32 [H][nb][D] rows into the tiled order of the score products (SelectArgs::ktile):
+// fp32 [H][nb][D] rows into the tiled order of the w̃ products (SelectArgs::stile):
 // float4 ((h·tiles + t)·(D/8) + u)·64 + lane is row 32 t + lane % 32, columns
 // (lane / 32)·D/2 + 4u .. + 3, zeros past nb. Writes are coalesced; the source is small.
 template <int D>
@@ -441,19 +441,14 @@ static hipError_t launch_select_t(const SelectArgs& a, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const bool large = a.nb > kSmallNb;
-  if (a.wt || (large && a.route == 2)) {     // σ² in the tiled order of the products
+  if (a.wt) {                                // σ² in the tiled order of the w̃ products
     e = launch_tile_rows(a.ksig2, a.stile, a.H, a.nb, D, s);
     if (e != hipSuccess) return e;
   }
   e = launch_pooled_w(a, s);                 // w̃ (when asked for), after the pooled q²
   if (e != hipSuccess) return e;
   const int nt = (a.nb + 63) / 64;
-  if (large) {                               // no score matrix: recomputed scores
-    e = launch_tile_rows(a.rope_axes ? a.krot : a.kbar, a.ktile, a.H, a.nb, D, s);
-    if (e != hipSuccess) return e;
-    return launch_select_large(a, s);
-  }
+  if (a.nb > kSmallNb) return launch_select_large(a, s);   // no score matrix: recomputed scores
   hipLaunchKernelGGL((score_kernel<D>), dim3(nt, nt, a.H), dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
