@@ -813,8 +813,9 @@ static hipError_t launch_attn_t(int mode, const AttnArgs& a, hipStream_t s) {
     if (!std::is_same<T, float>::value && a.lse) {
       // bf16 with lse given: the selected blocks as DROP in the fast kernel (writes O,
       // lse), then the unselected blocks in their literal form, merged into O and lse.
-      launch_attention_frag(MODE_DROP, a, s);
-      launch_literal_rest(a, s);
+      const hipError_t e = launch_attention_frag(MODE_DROP, a, s);
+      if (e != hipSuccess) return e;
+      return launch_literal_rest(a, s);
     } else {
       hipLaunchKernelGGL((attention_kernel<T, D, MODE_LITERAL>), grid, dim3(128), 0, s, a);
     }
@@ -829,8 +830,9 @@ static hipError_t launch_attn_t(int mode, const AttnArgs& a, hipStream_t s) {
         v.merge = 1;
         hipLaunchKernelGGL((attention_kernel<T, D, MODE_PWT_ROW>), grid, dim3(128), 0, s, v);
       } else {
-        launch_attention_frag(MODE_DROP, a, s);
-        launch_virtual_row(a, s);
+        const hipError_t e = launch_attention_frag(MODE_DROP, a, s);
+        if (e != hipSuccess) return e;
+        return launch_virtual_row(a, s);
       }
     } else {
       hipLaunchKernelGGL((attention_kernel<T, D, MODE_PWT_ROW>), grid, dim3(128), 0, s, a);
