@@ -144,12 +144,13 @@ void attention_frag_kernel(AttnArgs a) {
   int N = n1 + (VIRT ? ngrp : 0);        // all tiles of this wave
   int dbase = 0;
   auto block_keys = [&](int j) -> int { return a.block_len ? min(max(a.block_len[j], 1), kB) : kB; };
-  auto build_list = [&]() -> int {       // compact table; returns its length
+  // jf: this lane's entry of the first 64, loaded by the caller ahead of other work.
+  auto build_list = [&](int jf) -> int {  // compact table; returns its length
     const uint64_t below = (uint64_t(1) << lane) - 1u;
     int written = 0, ragged = 0;
     for (int s0 = 0; s0 < a.K_sel; s0 += 64) {
       const int e = s0 + lane;
-      const int j = e < a.K_sel ? irow[e] : -1;
+      const int j = s0 == 0 ? jf : e < a.K_sel ? irow[e] : -1;
       const bool valid = j >= 0 && j < nb;
       const int v = valid ? block_keys(j) : 0;
       const bool rag = valid && v <= 32;
@@ -467,9 +468,16 @@ void attention_frag_kernel(AttnArgs a) {
       // scores of unit 0, issued as the loading steps of tiles -NS .. -1 would issue them
       // (the loop's memory waits then hold from its first step on). Vᵀ stage NS - 1 and
       // P of "unit -1" are zero, so step 0's PV adds nothing.
+      // The first chunk of the selection is loaded before the first virtual rows are
+      // filled (their rows depend on the virtual index only), so the two memory
+      // latencies overlap.
+      const int jf = compact && lane < a.K_sel ? irow[lane] : -1;
+      if constexpr (VIRT) {
+        if (ngrp > 0) vfill(n1, min(VH, ngrp));
+      }
       if (a.K_sel > 0) {
         if (compact) {
-          n1 = build_list();
+          n1 = build_list(jf);
           N = n1 + (VIRT ? ngrp : 0);
         } else {
           fill(0);
@@ -478,7 +486,6 @@ void attention_frag_kernel(AttnArgs a) {
       }
       if (N == 0) break;
       if constexpr (VIRT) {
-        if (N > n1) vfill(n1, min(VH, N - n1));
         if (N > n1 + VH) vfill(n1 + VH, min(VH, N - n1 - VH));
       }
       pb[1][0] = pb[1][1] = bf16x8{};

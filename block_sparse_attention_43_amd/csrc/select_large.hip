@@ -737,8 +737,8 @@ __global__ __launch_bounds__(256) void lresolve_kernel(SelectArgs a) {
 }
 
 // Rows sent to the fallback: the whole row's exact scores into LDS (one block per thread
-// in turn), radix-selected by the workgroup as select_topk.hip's topk_kernel does from a
-// stored row.
+// in turn), radix-selected by the workgroup: four 8-bit passes over order-preserving keys,
+// lower index first at equal keys.
 template <int D, int ROUTE>
 __global__ __launch_bounds__(256) void lfallback_kernel(SelectArgs a) {
   constexpr int P = kMaxNb / 256;

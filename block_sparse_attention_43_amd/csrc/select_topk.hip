@@ -206,108 +206,31 @@ __global__ __launch_bounds__(256) void score_kernel(SelectArgs a) {
   store(a.scores, s);
 }
 
-// One workgroup per (query tile, head). Thread t owns block indices [t*P, t*P + P).
-template <int P>
-__global__ __launch_bounds__(256) void topk_kernel(SelectArgs a) {
-  __shared__ int hist[256];
-  __shared__ int scan_sh[8];
-  __shared__ uint32_t s_digit;
-  __shared__ int s_rem;
-  __shared__ uint32_t smask[1024];
-  const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int nb = a.nb, K = a.K_sel;
-  const float* row = a.scores + (size_t(h) * nb + i) * nb;
-  const int base = tid * P;
-
-  uint32_t key[P];
-#pragma unroll
-  for (int p = 0; p < P; ++p) key[p] = (base + p < nb) ? order_key(row[base + p]) : 0u;
-
-  // Threshold key T (the K-th largest) and how many keys equal to T are taken.
-  uint32_t T = 0u;
-  int take_eq = 0;
-  bool all = (K >= nb);
-  if (K > 0 && !all) {
-    uint32_t prefix = 0u, pmask = 0u;
-    int rem = K;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      hist[tid] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int p = 0; p < P; ++p)
-        if (base + p < nb && (key[p] & pmask) == prefix) atomicAdd(&hist[(key[p] >> shift) & 255u], 1);
-      __syncthreads();
-      const int b = 255 - tid;                 // scan from the highest digit down
-      const int v = hist[b];
-      int tot;
-      const int excl = block_exclusive_scan_256(v, scan_sh, &tot);
-      if (excl < rem && excl + v >= rem) {
-        s_digit = uint32_t(b);
-        s_rem = rem - excl;
-      }
-      __syncthreads();
-      prefix |= s_digit << shift;
-      pmask |= 0xFFu << shift;
-      rem = s_rem;
-      __syncthreads();
-    }
-    T = prefix;
-    take_eq = rem;
-  }
-
-  // Selected flags in index order: key > T, or key == T among the first take_eq such.
-  int eq_local = 0;
-#pragma unroll
-  for (int p = 0; p < P; ++p) eq_local += (base + p < nb && key[p] == T) ? 1 : 0;
-  int tot;
-  const int eq_start = block_exclusive_scan_256(eq_local, scan_sh, &tot);
-  auto selected = [&](int p, int& eqc) -> bool {
-    if (base + p >= nb) return false;
-    if (all) return true;
-    if (K == 0) return false;
-    if (key[p] > T) return true;
-    if (key[p] == T) return eqc++ < take_eq;
-    return false;
-  };
-  int cnt = 0;
-  {
-    int eqc = eq_start;
-#pragma unroll
-    for (int p = 0; p < P; ++p) cnt += selected(p, eqc) ? 1 : 0;
-  }
-  int pos = block_exclusive_scan_256(cnt, scan_sh, &tot);
-  int32_t* out = a.idx + (size_t(h) * nb + i) * K;
-  if (a.mask) {
-    for (int w = tid; w < a.nw; w += 256) smask[w] = 0u;
-    __syncthreads();
-  }
-  {
-    int eqc = eq_start;
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      if (selected(p, eqc)) {
-        if (pos < K) out[pos] = base + p;   // bound holds by construction; kept as a guard
-        ++pos;
-        if (a.mask) atomicOr(&smask[(base + p) >> 5], 1u << ((base + p) & 31));
-      }
-    }
-  }
-  if (a.mask) {
-    __syncthreads();
-    uint32_t* mo = a.mask + (size_t(h) * nb + i) * a.nw;
-    for (int w = tid; w < a.nw; w += 256) mo[w] = smask[w];
-  }
-}
-
 // One wave per (query tile, head), four rows per workgroup, for nb <= 64 P: lane l owns
 // block indices [l P, l P + P), so index order is lane order and the tie rule is a lane
-// prefix. The same radix select as topk_kernel with wave-private histograms in LDS and
-// wave scans instead of block barriers.
+// prefix.
+//
+// The row reaches the lanes through LDS: the wave reads it with coalesced 16-byte loads
+// into a per-wave buffer padded by one word every 32 (a lane's P words then sit in
+// distinct banks) and each lane takes its own range from there.
+//
+// Selection is exact in two stages. First, 256 linear bins over the row's value range
+// [lo, hi]: bin(x) = min(255, ⌊(x - lo)·256 / (hi - lo)⌋) in fp32, a non-decreasing
+// function of x, so every key in a higher bin is at least every key in a lower one and
+// equal scores share a bin; the histogram gives the bin b* that holds the K-th largest
+// score and how many of the K fall in it. Scores spread over many bins, so the LDS
+// counters see little contention (an 8-bit radix digit of the raw key puts most of a
+// row's scores in a handful of exponent digits). Second, the 4-pass 8-bit radix select
+// on order-preserving keys, over the keys of bin b* only, fixes the threshold key and how
+// many keys equal to it are taken, lowest indices first. A row whose range is not finite
+// puts every key in bin 0, which is the plain radix select.
 template <int P>
 __global__ __launch_bounds__(256) void topk_wave_kernel(SelectArgs a) {
-  __shared__ int hist[4][256];
+  constexpr int NBIN = 256;
+  constexpr int RW = 64 * P + 2 * P;         // padded row words per wave (one pad word per 32)
+  __shared__ int hist[4][NBIN];
   __shared__ uint32_t smask[4][64];
+  __shared__ float srow[4][RW];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nb = a.nb, K = a.K_sel;
   const int row_id = blockIdx.x * 4 + wave;          // h * nb + i
@@ -315,49 +238,101 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(SelectArgs a) {
   const float* row = a.scores + size_t(row_id) * nb;
   const int base = lane * P;
   int* hw = hist[wave];
+  float* rs = srow[wave];
+  auto pad = [](int e) { return e + (e >> 5); };
+
+  // Coalesced staging: 16-byte chunks where the row allows (rows start at a multiple of
+  // nb floats, so only nb % 4 == 0 keeps every chunk aligned), single words otherwise.
+  if ((nb & 3) == 0) {
+    for (int c = lane; 4 * c < nb; c += 64) {
+      const float4 v = *reinterpret_cast<const float4*>(row + 4 * c);
+      rs[pad(4 * c)] = v.x; rs[pad(4 * c + 1)] = v.y; rs[pad(4 * c + 2)] = v.z; rs[pad(4 * c + 3)] = v.w;
+    }
+  } else {
+    for (int e = lane; e < nb; e += 64) rs[pad(e)] = row[e];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   uint32_t key[P];
+  float x[P];
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
-  for (int p = 0; p < P; ++p) key[p] = (base + p < nb) ? order_key(row[base + p]) : 0u;
+  for (int p = 0; p < P; ++p) {
+    const bool v = base + p < nb;
+    x[p] = v ? rs[pad(base + p)] + 0.0f : 0.f;      // -0 -> +0 so equal scores tie
+    key[p] = v ? order_key(x[p]) : 0u;
+    if (v) {
+      kmin = min(kmin, key[p]);
+      kmax = max(kmax, key[p]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), o, 64)));
+    kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), o, 64)));
+  }
+  auto key_value = [](uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k); };
+  const float lo = key_value(kmin), hi = key_value(kmax);
+  const float span = hi - lo;
+  const float scale = float(NBIN) / span;
+  const bool lin = __builtin_isfinite(lo) && __builtin_isfinite(hi) && span > 0.f && __builtin_isfinite(span) &&
+                   __builtin_isfinite(scale) && scale > 0.f;
+  int bn[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) bn[p] = lin ? min(NBIN - 1, int((x[p] - lo) * scale)) : 0;
 
+  // Finds the digit (0..255, high first) whose count reaches rem; returns it and the rank
+  // left within it. Lane l holds the counts of digits 255 - 4l .. 252 - 4l.
+  auto find_digit = [&](int rem, int& rm) -> int {
+    int c[4], own = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c[q] = hw[255 - 4 * lane - q];
+      own += c[q];
+    }
+    const int incl = wave_inclusive_scan(own);
+    int excl = incl - own;
+    int dg = -1, r = 0;
+    if (excl < rem && incl >= rem) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (dg < 0 && excl + c[q] >= rem) {
+          dg = 255 - 4 * lane - q;
+          r = rem - excl;
+        }
+        excl += c[q];
+      }
+    }
+    const uint64_t who = __ballot(dg >= 0);
+    const int src = __ffsll(static_cast<unsigned long long>(who)) - 1;
+    rm = __shfl(r, src, 64);
+    return __shfl(dg, src, 64);
+  };
+
+  int bstar = -1;                               // threshold bin; keys above it are all taken
   uint32_t Tk = 0u;
   int take_eq = 0;
   const bool all = K >= nb;
   if (K > 0 && !all) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hw[4 * lane + q] = 0;
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      if (base + p < nb) atomicAdd(&hw[bn[p]], 1);
+    int rem = 0;
+    bstar = find_digit(K, rem);
     uint32_t prefix = 0u, pmask = 0u;
-    int rem = K;
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
 #pragma unroll
       for (int q = 0; q < 4; ++q) hw[4 * lane + q] = 0;
 #pragma unroll
       for (int p = 0; p < P; ++p)
-        if (base + p < nb && (key[p] & pmask) == prefix) atomicAdd(&hw[(key[p] >> shift) & 255u], 1);
-      // lane l takes digits 255 - 4l .. 252 - 4l (high digits first)
-      int c[4], own = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        c[q] = hw[255 - 4 * lane - q];
-        own += c[q];
-      }
-      const int incl = wave_inclusive_scan(own);
-      int excl = incl - own;
-      // the lane whose digits reach rem finds the digit; broadcast it
-      int dg = -1, rm = 0;
-      if (excl < rem && incl >= rem) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (dg < 0 && excl + c[q] >= rem) {
-            dg = 255 - 4 * lane - q;
-            rm = rem - excl;
-          }
-          excl += c[q];
-        }
-      }
-      const uint64_t who = __ballot(dg >= 0);
-      const int src = __ffsll(static_cast<unsigned long long>(who)) - 1;
-      dg = __shfl(dg, src, 64);
-      rm = __shfl(rm, src, 64);
+        if (base + p < nb && bn[p] == bstar && (key[p] & pmask) == prefix) atomicAdd(&hw[(key[p] >> shift) & 255u], 1);
+      int rm = 0;
+      const int dg = find_digit(rem, rm);
       prefix |= uint32_t(dg) << shift;
       pmask |= 0xFFu << shift;
       rem = rm;
@@ -366,14 +341,18 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(SelectArgs a) {
     take_eq = rem;
   }
 
+  // Taken: every key of a bin above b*; in b*, keys above Tk and the first take_eq keys
+  // equal to Tk in index order.
   int eq_local = 0;
 #pragma unroll
-  for (int p = 0; p < P; ++p) eq_local += (base + p < nb && key[p] == Tk) ? 1 : 0;
+  for (int p = 0; p < P; ++p) eq_local += (base + p < nb && bn[p] == bstar && key[p] == Tk) ? 1 : 0;
   const int eq_start = wave_inclusive_scan(eq_local) - eq_local;
   auto selected = [&](int p, int& eqc) -> bool {
     if (base + p >= nb) return false;
     if (all) return true;
     if (K == 0) return false;
+    if (bn[p] > bstar) return true;
+    if (bn[p] < bstar) return false;
     if (key[p] > Tk) return true;
     if (key[p] == Tk) return eqc++ < take_eq;
     return false;
@@ -452,26 +431,14 @@ static hipError_t launch_select_t(const SelectArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((score_kernel<D>), dim3(nt, nt, a.H), dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.nb <= 64 * 32) {
-    const int pw = (a.nb + 63) / 64;
-    const dim3 gw(unsigned((size_t(a.H) * a.nb + 3) / 4));
-    if (pw <= 4) hipLaunchKernelGGL((topk_wave_kernel<4>), gw, dim3(256), 0, s, a);
-    else if (pw <= 8) hipLaunchKernelGGL((topk_wave_kernel<8>), gw, dim3(256), 0, s, a);
-    else if (pw <= 12) hipLaunchKernelGGL((topk_wave_kernel<12>), gw, dim3(256), 0, s, a);
-    else if (pw <= 16) hipLaunchKernelGGL((topk_wave_kernel<16>), gw, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((topk_wave_kernel<32>), gw, dim3(256), 0, s, a);
-    return hipGetLastError();
-  }
-  const int per = (a.nb + 255) / 256;
-  const dim3 g(a.nb, a.H);
-  if (per <= 1) hipLaunchKernelGGL((topk_kernel<1>), g, dim3(256), 0, s, a);
-  else if (per <= 2) hipLaunchKernelGGL((topk_kernel<2>), g, dim3(256), 0, s, a);
-  else if (per <= 4) hipLaunchKernelGGL((topk_kernel<4>), g, dim3(256), 0, s, a);
-  else if (per <= 8) hipLaunchKernelGGL((topk_kernel<8>), g, dim3(256), 0, s, a);
-  else if (per <= 16) hipLaunchKernelGGL((topk_kernel<16>), g, dim3(256), 0, s, a);
-  else if (per <= 32) hipLaunchKernelGGL((topk_kernel<32>), g, dim3(256), 0, s, a);
-  else if (per <= 64) hipLaunchKernelGGL((topk_kernel<64>), g, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((topk_kernel<128>), g, dim3(256), 0, s, a);
+  static_assert(kSmallNb <= 64 * 32, "one wave per row covers every stored row");
+  const int pw = (a.nb + 63) / 64;
+  const dim3 gw(unsigned((size_t(a.H) * a.nb + 3) / 4));
+  if (pw <= 4) hipLaunchKernelGGL((topk_wave_kernel<4>), gw, dim3(256), 0, s, a);
+  else if (pw <= 8) hipLaunchKernelGGL((topk_wave_kernel<8>), gw, dim3(256), 0, s, a);
+  else if (pw <= 12) hipLaunchKernelGGL((topk_wave_kernel<12>), gw, dim3(256), 0, s, a);
+  else if (pw <= 16) hipLaunchKernelGGL((topk_wave_kernel<16>), gw, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((topk_wave_kernel<32>), gw, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
