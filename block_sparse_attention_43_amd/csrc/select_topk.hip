@@ -23,51 +23,60 @@
 
 namespace pisa {
 
+// One wave per query tile, four tiles per workgroup. Lane l reads 16-byte chunk l % CPR of
+// rows l / CPR + RPL·p (RPL = 64 / CPR rows per wave-wide load, all loads issued before
+// any sum), so each load instruction covers RPL whole rows; the lanes holding the same
+// chunk then add their column sums and sums of squares with lane exchanges, in a fixed
+// order. No LDS and no workgroup barrier.
 template <class T, int D>
 __global__ __launch_bounds__(256) void pool_kernel(SelectArgs a) {
-  // Thread t reads 16-byte chunks (EPC columns) of rows t / CPR + RG * p; column sums and
-  // sums of squares are reduced over the RG row groups through LDS.
   constexpr int EPC = 16 / sizeof(T);
   constexpr int CPR = D / EPC;             // chunks per row
-  constexpr int RG = 256 / CPR;            // row groups
-  __shared__ float s1[RG][D], s2[RG][D];
-  const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  static_assert(CPR <= 64 && 64 % CPR == 0, "a row fits one wave-wide load");
+  constexpr int RPL = 64 / CPR;            // rows per wave-wide load
+  constexpr int NL = kB / RPL;             // loads per lane
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = blockIdx.x * 4 + wave, h = blockIdx.y;
+  if (i >= a.nb) return;                   // whole waves leave together
   int n = a.block_len ? a.block_len[i] : kB;
   n = min(max(n, 1), kB);
-  const int ch = tid % CPR, rg = tid / CPR;
+  const int ch = lane % CPR, r0 = lane / CPR;
   const T* Qt = static_cast<const T*>(a.Q) + (size_t(h) * a.L + size_t(i) * kB) * D;
+  u32x4 v[NL];
+#pragma unroll
+  for (int p = 0; p < NL; ++p) {
+    const int r = r0 + RPL * p;
+    v[p] = r < n ? *reinterpret_cast<const u32x4*>(Qt + size_t(r) * D + ch * EPC) : u32x4{0u, 0u, 0u, 0u};
+  }
   float sum[EPC], sq[EPC];
 #pragma unroll
   for (int u = 0; u < EPC; ++u) sum[u] = sq[u] = 0.f;
 #pragma unroll
-  for (int p = 0; p < kB / RG; ++p) {
-    const int r = rg + RG * p;
-    if (r < n) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(Qt + size_t(r) * D + ch * EPC);
-      const T* e = reinterpret_cast<const T*>(&v);
+  for (int p = 0; p < NL; ++p) {
+    const T* e = reinterpret_cast<const T*>(&v[p]);
 #pragma unroll
-      for (int u = 0; u < EPC; ++u) {
-        const float x = to_f32(e[u]);
-        sum[u] += x;
-        sq[u] += x * x;
-      }
+    for (int u = 0; u < EPC; ++u) {
+      const float x = to_f32(e[u]);
+      sum[u] += x;
+      sq[u] += x * x;
     }
   }
 #pragma unroll
-  for (int u = 0; u < EPC; ++u) {
-    s1[rg][ch * EPC + u] = sum[u];
-    s2[rg][ch * EPC + u] = sq[u];
-  }
-  __syncthreads();
-  if (tid < D) {
-    float t1 = 0.f, t2 = 0.f;
-    for (int q = 0; q < RG; ++q) {
-      t1 += s1[q][tid];
-      t2 += s2[q][tid];
+  for (int o = CPR; o < 64; o <<= 1)
+#pragma unroll
+    for (int u = 0; u < EPC; ++u) {
+      sum[u] += __shfl_xor(sum[u], o, 64);
+      sq[u] += __shfl_xor(sq[u], o, 64);
     }
+  if (lane < CPR) {
     const float invn = 1.f / float(n);
-    a.qbar[(size_t(h) * a.nb + i) * D + tid] = t1 * invn;
-    a.qsq[(size_t(h) * a.nb + i) * D + tid] = t2 * invn;
+    float* qb = a.qbar + (size_t(h) * a.nb + i) * D + ch * EPC;
+    float* qs = a.qsq + (size_t(h) * a.nb + i) * D + ch * EPC;
+#pragma unroll
+    for (int u = 0; u < EPC; u += 4) {
+      *reinterpret_cast<float4*>(qb + u) = make_float4(sum[u] * invn, sum[u + 1] * invn, sum[u + 2] * invn, sum[u + 3] * invn);
+      *reinterpret_cast<float4*>(qs + u) = make_float4(sq[u] * invn, sq[u + 1] * invn, sq[u + 2] * invn, sq[u + 3] * invn);
+    }
   }
 }
 
@@ -243,13 +252,29 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(SelectArgs a) {
 
   // Coalesced staging: 16-byte chunks where the row allows (rows start at a multiple of
   // nb floats, so only nb % 4 == 0 keeps every chunk aligned), single words otherwise.
+  // All loads are issued before the first LDS write, so one memory latency covers the row.
   if ((nb & 3) == 0) {
-    for (int c = lane; 4 * c < nb; c += 64) {
-      const float4 v = *reinterpret_cast<const float4*>(row + 4 * c);
-      rs[pad(4 * c)] = v.x; rs[pad(4 * c + 1)] = v.y; rs[pad(4 * c + 2)] = v.z; rs[pad(4 * c + 3)] = v.w;
+    constexpr int NC = (P + 3) / 4;                 // 16-byte chunks per lane
+    float4 v[NC];
+#pragma unroll
+    for (int q = 0; q < NC; ++q) {
+      const int c = min(lane + 64 * q, nb / 4 - 1);  // clamped in bounds; the extra chunks are not stored
+      v[q] = *reinterpret_cast<const float4*>(row + 4 * c);
+    }
+#pragma unroll
+    for (int q = 0; q < NC; ++q) {
+      const int c = lane + 64 * q;
+      if (4 * c < nb) {
+        rs[pad(4 * c)] = v[q].x; rs[pad(4 * c + 1)] = v[q].y; rs[pad(4 * c + 2)] = v[q].z; rs[pad(4 * c + 3)] = v[q].w;
+      }
     }
   } else {
-    for (int e = lane; e < nb; e += 64) rs[pad(e)] = row[e];
+    float v[P];
+#pragma unroll
+    for (int q = 0; q < P; ++q) v[q] = row[min(lane + 64 * q, nb - 1)];
+#pragma unroll
+    for (int q = 0; q < P; ++q)
+      if (lane + 64 * q < nb) rs[pad(lane + 64 * q)] = v[q];
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -411,7 +436,7 @@ template <class T, int D>
 static hipError_t launch_select_t(const SelectArgs& a, hipStream_t s) {
   hipError_t e = hipSuccess;
   if (a.rope_axes == 0 || a.wt) {            // RoPE-aware scores read Q only for w̃
-    hipLaunchKernelGGL((pool_kernel<T, D>), dim3(a.nb, a.H), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((pool_kernel<T, D>), dim3((a.nb + 3) / 4, a.H), dim3(256), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
