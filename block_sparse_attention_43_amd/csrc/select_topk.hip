@@ -348,19 +348,52 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(SelectArgs a) {
       if (base + p < nb) atomicAdd(&hw[bn[p]], 1);
     int rem = 0;
     bstar = find_digit(K, rem);
-    uint32_t prefix = 0u, pmask = 0u;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
+    // The keys of bin b* (usually a few dozen) are gathered into the wave's LDS buffer,
+    // which the row no longer needs, at most CM per lane; the radix passes then visit
+    // those instead of all P keys of every lane. A larger bin keeps the keys in place.
+    constexpr int CM = 4;
+    int cl = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) hw[4 * lane + q] = 0;
+    for (int p = 0; p < P; ++p) cl += (base + p < nb && bn[p] == bstar) ? 1 : 0;
+    const int cincl = wave_inclusive_scan(cl);
+    const int ctot = __shfl(cincl, 63, 64);
+    uint32_t prefix = 0u, pmask = 0u;
+    auto radix = [&](auto count_keys) {
+      for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hw[4 * lane + q] = 0;
+        count_keys(shift, pmask, prefix);
+        int rm = 0;
+        const int dg = find_digit(rem, rm);
+        prefix |= uint32_t(dg) << shift;
+        pmask |= 0xFFu << shift;
+        rem = rm;
+      }
+    };
+    if (ctot <= 64 * CM) {
+      uint32_t* cbuf = reinterpret_cast<uint32_t*>(rs);
+      int w = cincl - cl;
 #pragma unroll
       for (int p = 0; p < P; ++p)
-        if (base + p < nb && bn[p] == bstar && (key[p] & pmask) == prefix) atomicAdd(&hw[(key[p] >> shift) & 255u], 1);
-      int rm = 0;
-      const int dg = find_digit(rem, rm);
-      prefix |= uint32_t(dg) << shift;
-      pmask |= 0xFFu << shift;
-      rem = rm;
+        if (base + p < nb && bn[p] == bstar) cbuf[w++] = key[p];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      uint32_t ck[CM];
+#pragma unroll
+      for (int m = 0; m < CM; ++m) ck[m] = lane + 64 * m < ctot ? cbuf[lane + 64 * m] : 0u;
+      radix([&](int shift, uint32_t pm, uint32_t pf) {
+#pragma unroll
+        for (int m = 0; m < CM; ++m)
+          if (lane + 64 * m < ctot && (ck[m] & pm) == pf) atomicAdd(&hw[(ck[m] >> shift) & 255u], 1);
+      });
+    } else {
+      radix([&](int shift, uint32_t pm, uint32_t pf) {
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+          if (base + p < nb && bn[p] == bstar && (key[p] & pm) == pf) atomicAdd(&hw[(key[p] >> shift) & 255u], 1);
+      });
     }
     Tk = prefix;
     take_eq = rem;
