@@ -8,8 +8,10 @@ copy of block 2m) and K_sel is odd, so in every query tile the K_sel-th and the 
 score are tied exactly; integer data adds many more ties elsewhere. The selection must
 then equal the oracle's bit for bit (blog "Sparse Linear Attention", Sparse Attention
 section: top-K over block-mean scores; ties to the lower index is this repository's
-reading). One case runs the one-wave-per-row top-K (nb <= 2048), one the
-workgroup-per-row top-K (nb > 2048).
+reading). One case runs the top-K over stored score rows (nb <= 2048), one the selection
+without a score matrix (nb > 2048). Two more stored-row cases give the top-K degenerate
+value ranges: every score equal (no range to bin), and one block scoring far above the
+rest (every other score in one bin, more of them than the bin's gathered list holds).
 """
 import numpy as np
 import pytest
@@ -59,3 +61,34 @@ def test_exact_ties_go_to_the_lower_index(gpu_lib, nb, H, dtype, K_sel):
         for i in range(nb):
             assert set(np.flatnonzero(sets[h, i])) == set(got[h, i])
     assert n_tied == H * nb, "every tile's boundary must fall inside an exact tie"
+
+
+@pytest.mark.parametrize("case", ["all_equal", "one_far_above"])
+def test_stored_row_topk_degenerate_ranges(gpu_lib, case):
+    pisa = gpu_lib
+    nb, H, d, K_sel = 300, 1, 64, 30
+    rng = np.random.default_rng(77)
+    Q = rng.integers(0, 3, size=(H, nb * 64, d)).astype(np.float32)      # q̄ >= 0
+    if case == "all_equal":
+        K = np.ones((H, nb * 64, d), np.float32)
+    else:
+        K = rng.integers(-2, 3, size=(H, nb * 64, d)).astype(np.float32)
+        K[:, 7 * 64:8 * 64] = 40.0
+    V = rng.standard_normal((H, nb * 64, d)).astype(np.float32)
+    print(f"degenerate top-K case {case}", flush=True)
+    dev = [torch.from_numpy(x).cuda() for x in (Q, K, V)]
+    st = pisa.block_stats(dev[1], dev[2], None)
+    idx, mask, _ = pisa.select_topk(dev[0], st, K_sel, None, want_wt=False)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy().astype(np.int64)[0]
+    ost = orc.block_stats(K[0].astype(np.float64), V[0].astype(np.float64), 64, None, per_block=False)
+    s = orc.block_scores(orc.pool_queries(Q[0].astype(np.float64), 64, None)["qbar"], ost["kbar"])
+    want = orc.select_topk(s, K_sel)
+    assert (got == want).all()
+    if case == "all_equal":
+        assert (got == np.arange(K_sel)[None, :]).all()
+    else:
+        assert (got == 7).any(axis=1).all()
+    sets = mask_to_sets(mask.cpu().numpy().view(np.uint32), nb)
+    for i in range(nb):
+        assert set(np.flatnonzero(sets[0, i])) == set(got[i])
