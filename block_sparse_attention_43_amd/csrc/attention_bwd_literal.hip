@@ -56,15 +56,39 @@ __device__ __forceinline__ void stage_rows(uint16_t* dst, const uint16_t* src, i
   }
 }
 
-// The transpose of the same block: dst[c][r] (row stride 72), zero for rows r >= nv.
+// The same staging split in two, so that the next tile's loads run during the current
+// tile's products: load_rows takes this thread's 16-byte chunks of rows [0, nv) (zeros
+// past nv; every load is in bounds, the block being 64 rows of a padded tensor);
+// put_rows writes them as stage_rows does, put_cols as the transpose dst[c][r] (row
+// stride 72).
 template <int D>
-__device__ __forceinline__ void stage_cols(uint16_t* dst, const uint16_t* src, int nv) {
-  constexpr int CPR = D / 8;
-  for (int c = threadIdx.x; c < kB * CPR; c += 256) {
-    const int r = c / CPR, col = (c % CPR) * 8;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (r < nv) v = *reinterpret_cast<const u32x4*>(src + size_t(r) * D + col);
-    const uint16_t* e = reinterpret_cast<const uint16_t*>(&v);
+struct RowRegs {
+  static constexpr int CPR = D / 8, N = kB * CPR / 256;
+  u32x4 v[N];
+};
+template <int D>
+__device__ __forceinline__ void load_rows(RowRegs<D>& t, const uint16_t* src, int nv) {
+#pragma unroll
+  for (int k = 0; k < RowRegs<D>::N; ++k) {
+    const int c = threadIdx.x + 256 * k, r = c / RowRegs<D>::CPR, col = (c % RowRegs<D>::CPR) * 8;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src + size_t(r) * D + col);
+    t.v[k] = r < nv ? v : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+template <int D>
+__device__ __forceinline__ void put_rows(uint16_t* dst, const RowRegs<D>& t) {
+#pragma unroll
+  for (int k = 0; k < RowRegs<D>::N; ++k) {
+    const int c = threadIdx.x + 256 * k, r = c / RowRegs<D>::CPR, col = (c % RowRegs<D>::CPR) * 8;
+    *reinterpret_cast<u32x4*>(dst + r * LitLds<D>::RS + col) = t.v[k];
+  }
+}
+template <int D>
+__device__ __forceinline__ void put_cols(uint16_t* dst, const RowRegs<D>& t) {
+#pragma unroll
+  for (int k = 0; k < RowRegs<D>::N; ++k) {
+    const int c = threadIdx.x + 256 * k, r = c / RowRegs<D>::CPR, col = (c % RowRegs<D>::CPR) * 8;
+    const uint16_t* e = reinterpret_cast<const uint16_t*>(&t.v[k]);
 #pragma unroll
     for (int u = 0; u < 8; ++u) dst[(col + u) * kTS + r] = e[u];
   }
@@ -200,13 +224,31 @@ __global__ __launch_bounds__(256) void literal_bwd_query_kernel(BwdArgs a) {
   for (int u = 0; u < NT; ++u) acc[u] = zero16();
   float dpart = 0.f, mpart = 0.f;
 
-  for (int j = 0; j < nb; ++j) {
-    if (SEL && !((mrow[j >> 5] >> (j & 31)) & 1u)) continue;   // the same for the whole workgroup
+  // Blocks visited (SEL: the selected ones only; the same for the whole workgroup); each
+  // block's K and V rows are loaded while the previous block's products run.
+  auto next_block = [&](int b) {
+    ++b;
+    if (SEL)
+      while (b < nb && !((mrow[b >> 5] >> (b & 31)) & 1u)) ++b;
+    return b;
+  };
+  RowRegs<D> kr, vr;
+  int jn = next_block(-1);
+  if (jn < nb) {
+    load_rows<D>(kr, Kh + size_t(jn) * kB * D, rows_of(jn));
+    load_rows<D>(vr, Vh + size_t(jn) * kB * D, rows_of(jn));
+  }
+  for (int j = jn; j < nb; j = jn) {
     const int nj = rows_of(j);
+    jn = next_block(j);
     __syncthreads();                     // previous step's tiles consumed
-    stage_rows<D>(sK, Kh + size_t(j) * kB * D, nj);
-    stage_rows<D>(sV, Vh + size_t(j) * kB * D, nj);
-    if constexpr (PASS == 1) stage_cols<D>(sKT, Kh + size_t(j) * kB * D, nj);
+    put_rows<D>(sK, kr);
+    put_rows<D>(sV, vr);
+    if constexpr (PASS == 1) put_cols<D>(sKT, kr);
+    if (jn < nb) {
+      load_rows<D>(kr, Kh + size_t(jn) * kB * D, rows_of(jn));
+      load_rows<D>(vr, Vh + size_t(jn) * kB * D, rows_of(jn));
+    }
     __syncthreads();
     quarter_product<D>(sQ, sK, sS, qh, kh);
     quarter_product<D>(sG, sV, sA, qh, kh);
@@ -306,17 +348,26 @@ __global__ __launch_bounds__(256) void literal_bwd_key_kernel(BwdArgs a) {
 #pragma unroll
   for (int u = 0; u < NT; ++u) ak[u] = av_[u] = zero16();
 
+  // Each query tile's Q and dO rows are loaded once, while the previous tile's products
+  // run, and written to LDS both row-major and transposed.
+  RowRegs<D> qr, gr;
+  load_rows<D>(qr, Qh, rows_of(0));
+  load_rows<D>(gr, Gh, rows_of(0));
   for (int i = 0; i < nb; ++i) {
     const int mi = rows_of(i);
     const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
     __syncthreads();
-    stage_rows<D>(sQ, Qh + size_t(i) * kB * D, mi);
-    stage_rows<D>(sG, Gh + size_t(i) * kB * D, mi);
-    stage_cols<D>(sQT, Qh + size_t(i) * kB * D, mi);
-    stage_cols<D>(sGT, Gh + size_t(i) * kB * D, mi);
+    put_rows<D>(sQ, qr);
+    put_rows<D>(sG, gr);
+    put_cols<D>(sQT, qr);
+    put_cols<D>(sGT, gr);
     if (tid < kB) {
       sLse[tid] = tid < mi ? a.lse2[row0 + tid] : kNegInf;
       sDelta[tid] = tid < mi ? a.delta[row0 + tid] : 0.f;
+    }
+    if (i + 1 < nb) {
+      load_rows<D>(qr, Qh + size_t(i + 1) * kB * D, rows_of(i + 1));
+      load_rows<D>(gr, Gh + size_t(i + 1) * kB * D, rows_of(i + 1));
     }
     __syncthreads();
     quarter_product<D>(sQ, sK, sS, qh, kh);
@@ -671,16 +722,23 @@ __global__ __launch_bounds__(256) void rowdiag_bwd_key_kernel(BwdArgs a) {
 #pragma unroll
   for (int e = 0; e < NE; ++e) dkb[e] = dvb[e] = dsg[e] = zero16();
 
+  // Each query tile's Q and dO rows are loaded once, while the previous tile's products
+  // run, and written to LDS both row-major and transposed.
+  RowRegs<D> qr, gr;
+  load_rows<D>(qr, static_cast<const uint16_t*>(a.Q) + size_t(h) * a.L * D, rows_of(0));
+  load_rows<D>(gr, static_cast<const uint16_t*>(a.dO) + size_t(h) * a.L * D, rows_of(0));
   for (int i = 0; i < nb; ++i) {
     const int mi = rows_of(i);
     const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
     __syncthreads();
-    const uint16_t* Qb = static_cast<const uint16_t*>(a.Q) + row0 * D;
-    const uint16_t* Gb = static_cast<const uint16_t*>(a.dO) + row0 * D;
-    stage_rows<D>(sQ, Qb, mi);
-    stage_rows<D>(sG, Gb, mi);
-    stage_cols<D>(sQT, Qb, mi);
-    stage_cols<D>(sGT, Gb, mi);
+    put_rows<D>(sQ, qr);
+    put_rows<D>(sG, gr);
+    put_cols<D>(sQT, qr);
+    put_cols<D>(sGT, gr);
+    if (i + 1 < nb) {
+      load_rows<D>(qr, static_cast<const uint16_t*>(a.Q) + (row0 + kB) * D, rows_of(i + 1));
+      load_rows<D>(gr, static_cast<const uint16_t*>(a.dO) + (row0 + kB) * D, rows_of(i + 1));
+    }
     if (tid < kB) {
       sRow[0][tid] = tid < mi ? a.lse2[row0 + tid] : kNegInf;
       sRow[1][tid] = a.delta[row0 + tid];
