@@ -350,25 +350,32 @@ __global__ __launch_bounds__(256) void literal_bwd_key_kernel(BwdArgs a) {
 
   // Each query tile's Q and dO rows are loaded once, while the previous tile's products
   // run, and written to LDS both row-major and transposed.
+  // The tile's row statistics (lse, Δ; threads below kB) travel with its rows.
   RowRegs<D> qr, gr;
-  load_rows<D>(qr, Qh, rows_of(0));
-  load_rows<D>(gr, Gh, rows_of(0));
+  float rl = 0.f, rd = 0.f;
+  auto load_tile = [&](int t) {
+    const int mt = rows_of(t);
+    load_rows<D>(qr, Qh + size_t(t) * kB * D, mt);
+    load_rows<D>(gr, Gh + size_t(t) * kB * D, mt);
+    if (tid < kB) {
+      const size_t r = size_t(h) * a.L + size_t(t) * kB + tid;
+      rl = tid < mt ? a.lse2[r] : kNegInf;
+      rd = tid < mt ? a.delta[r] : 0.f;
+    }
+  };
+  load_tile(0);
   for (int i = 0; i < nb; ++i) {
     const int mi = rows_of(i);
-    const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
     __syncthreads();
     put_rows<D>(sQ, qr);
     put_rows<D>(sG, gr);
     put_cols<D>(sQT, qr);
     put_cols<D>(sGT, gr);
     if (tid < kB) {
-      sLse[tid] = tid < mi ? a.lse2[row0 + tid] : kNegInf;
-      sDelta[tid] = tid < mi ? a.delta[row0 + tid] : 0.f;
+      sLse[tid] = rl;
+      sDelta[tid] = rd;
     }
-    if (i + 1 < nb) {
-      load_rows<D>(qr, Qh + size_t(i + 1) * kB * D, rows_of(i + 1));
-      load_rows<D>(gr, Gh + size_t(i + 1) * kB * D, rows_of(i + 1));
-    }
+    if (i + 1 < nb) load_tile(i + 1);
     __syncthreads();
     quarter_product<D>(sQ, sK, sS, qh, kh);
     quarter_product<D>(sG, sV, sA, qh, kh);
@@ -724,26 +731,34 @@ __global__ __launch_bounds__(256) void rowdiag_bwd_key_kernel(BwdArgs a) {
 
   // Each query tile's Q and dO rows are loaded once, while the previous tile's products
   // run, and written to LDS both row-major and transposed.
+  // The tile's row statistics (lse, Δ, dO·u; threads below kB) travel with its rows.
   RowRegs<D> qr, gr;
-  load_rows<D>(qr, static_cast<const uint16_t*>(a.Q) + size_t(h) * a.L * D, rows_of(0));
-  load_rows<D>(gr, static_cast<const uint16_t*>(a.dO) + size_t(h) * a.L * D, rows_of(0));
+  float r0v = 0.f, r1v = 0.f, r2v = 0.f;
+  auto load_tile = [&](int t) {
+    const int mt = rows_of(t);
+    const size_t rt = size_t(h) * a.L + size_t(t) * kB;
+    load_rows<D>(qr, static_cast<const uint16_t*>(a.Q) + rt * D, mt);
+    load_rows<D>(gr, static_cast<const uint16_t*>(a.dO) + rt * D, mt);
+    if (tid < kB) {
+      r0v = tid < mt ? a.lse2[rt + tid] : kNegInf;
+      r1v = a.delta[rt + tid];
+      r2v = a.gu[rt + tid];
+    }
+  };
+  load_tile(0);
   for (int i = 0; i < nb; ++i) {
     const int mi = rows_of(i);
-    const size_t row0 = size_t(h) * a.L + size_t(i) * kB;
     __syncthreads();
     put_rows<D>(sQ, qr);
     put_rows<D>(sG, gr);
     put_cols<D>(sQT, qr);
     put_cols<D>(sGT, gr);
-    if (i + 1 < nb) {
-      load_rows<D>(qr, static_cast<const uint16_t*>(a.Q) + (row0 + kB) * D, rows_of(i + 1));
-      load_rows<D>(gr, static_cast<const uint16_t*>(a.dO) + (row0 + kB) * D, rows_of(i + 1));
-    }
     if (tid < kB) {
-      sRow[0][tid] = tid < mi ? a.lse2[row0 + tid] : kNegInf;
-      sRow[1][tid] = a.delta[row0 + tid];
-      sRow[2][tid] = a.gu[row0 + tid];
+      sRow[0][tid] = r0v;
+      sRow[1][tid] = r1v;
+      sRow[2][tid] = r2v;
     }
+    if (i + 1 < nb) load_tile(i + 1);
     __syncthreads();
     const bool ex = !inj || ((mh[size_t(i) * a.nw + (j >> 5)] >> (j & 31)) & 1u);
     f32x16 S = zero16(), A = zero16(), W = zero16();
