@@ -14,9 +14,10 @@
 //
 // Scores are fp32 (matrix-core fp32 products and sums) with one fixed summation order per
 // element, so identical centroids score identically. Rows of at most kSmallNb blocks are
-// stored and radix-selected here (order-preserving 32-bit keys in registers, the tie rule
-// by prefix counts in index order); longer rows go to select_large.hip, which recomputes
-// the scores instead of storing them.
+// stored and selected here (linear bins over the row's range, then a radix select on
+// order-preserving 32-bit keys within the threshold bin, the tie rule by prefix counts in
+// index order); longer rows go to select_large.hip, which recomputes the scores instead
+// of storing them.
 #include "common.hpp"
 #include "internal.hpp"
 #include "select_common.hpp"
