@@ -36,6 +36,13 @@ constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kSS = kB + 1;              // fp32 row stride of the score tiles (odd: no conflicts)
 constexpr int kTS = kB + 8;              // bf16 row stride of 64-wide tiles (16-byte rows, spread banks)
 
+// Offset of element k (< 64) within row `row` of a transposed tile written by put_cols:
+// groups of eight are XOR-swizzled by row / 8, so the eight rows one thread writes per
+// 16-byte chunk (rows eight apart between neighbouring threads) fall in different banks;
+// a reader of eight consecutive k from k0 (a multiple of 8) gets them contiguous at
+// tpos(row, k0).
+__device__ __forceinline__ int tpos(int row, int k) { return k ^ (((row >> 3) & 7) << 3); }
+
 template <int D>
 struct LitLds {
   static constexpr int RS = D + 8;       // bf16 row stride of [64][D] tiles
@@ -59,7 +66,7 @@ __device__ __forceinline__ void stage_rows(uint16_t* dst, const uint16_t* src, i
 // The same staging split in two, so that the next tile's loads run during the current
 // tile's products: load_rows takes this thread's 16-byte chunks of rows [0, nv) (zeros
 // past nv; every load is in bounds, the block being 64 rows of a padded tensor);
-// put_rows writes them as stage_rows does, put_cols as the transpose dst[c][r] (row
+// put_rows writes them as stage_rows does, put_cols as the transpose dst[c][tpos(c, r)] (row
 // stride 72).
 template <int D>
 struct RowRegs {
@@ -90,7 +97,7 @@ __device__ __forceinline__ void put_cols(uint16_t* dst, const RowRegs<D>& t) {
     const int c = threadIdx.x + 256 * k, r = c / RowRegs<D>::CPR, col = (c % RowRegs<D>::CPR) * 8;
     const uint16_t* e = reinterpret_cast<const uint16_t*>(&t.v[k]);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) dst[(col + u) * kTS + r] = e[u];
+    for (int u = 0; u < 8; ++u) dst[(col + u) * kTS + tpos(col + u, r)] = e[u];
   }
 }
 
@@ -287,7 +294,7 @@ __global__ __launch_bounds__(256) void literal_bwd_query_kernel(BwdArgs a) {
 #pragma unroll
         for (int ks = 0; ks < kB / 16; ++ks)
           acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(sDX + (32 * qh + c) * kTS + 16 * ks + 8 * g),
-                                                           lds8(sKT + (32 * dt + c) * kTS + 16 * ks + 8 * g),
+                                                           lds8(sKT + (32 * dt + c) * kTS + tpos(32 * dt + c, 16 * ks + 8 * g)),
                                                            acc[u], 0, 0, 0);
       }
     }
@@ -410,10 +417,10 @@ __global__ __launch_bounds__(256) void literal_bwd_key_kernel(BwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < kB / 16; ++ks) {
         ak[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(sDXT + (32 * kh + c) * kTS + 16 * ks + 8 * g),
-                                                        lds8(sQT + (32 * dt + c) * kTS + 16 * ks + 8 * g),
+                                                        lds8(sQT + (32 * dt + c) * kTS + tpos(32 * dt + c, 16 * ks + 8 * g)),
                                                         ak[u], 0, 0, 0);
         av_[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds8(sWT + (32 * kh + c) * kTS + 16 * ks + 8 * g),
-                                                         lds8(sGT + (32 * dt + c) * kTS + 16 * ks + 8 * g),
+                                                         lds8(sGT + (32 * dt + c) * kTS + tpos(32 * dt + c, 16 * ks + 8 * g)),
                                                          av_[u], 0, 0, 0);
       }
     }
@@ -793,9 +800,9 @@ __global__ __launch_bounds__(256) void rowdiag_bwd_key_kernel(BwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int k0 = 32 * x + 16 * ks + 8 * g;
-        const bf16x8 qt = lds8(sQT + (32 * e + c) * kTS + k0);
+        const bf16x8 qt = lds8(sQT + (32 * e + c) * kTS + tpos(32 * e + c, k0));
         dkb[e] = MmaBF16::mma(qt, dlb[ks], dkb[e]);
-        dvb[e] = MmaBF16::mma(lds8(sGT + (32 * e + c) * kTS + k0), pb[ks], dvb[e]);
+        dvb[e] = MmaBF16::mma(lds8(sGT + (32 * e + c) * kTS + tpos(32 * e + c, k0)), pb[ks], dvb[e]);
         dsg[e] = MmaBF16::mma(square8(qt), dwb[ks], dsg[e]);
       }
   }
